@@ -1,0 +1,389 @@
+"""Pins for the CPU oracle: checks against what the pages and mathematics fix.
+
+None of these retypes the oracle's formulas.  Each pin compares the oracle with
+something independent of it: the pages' stated invariant (naive and absorb give
+identical outputs, page "Naive vs Absorb Attention Implementations in
+DeepSeek-V3", FAQ on whether switching changes the output), hand-worked closed
+forms (tests/golden/hand_worked.json), library routines (torch's
+scaled_dot_product_attention and rms_norm on the CPU), scalar brute-force loops,
+and identities of softmax and of the split merge.  The mutation tests at the end
+plant a plausible mistake in the oracle (on the CPU) and check that some pin fails.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import bruteforce as BF
+from oracle import mla_oracle as O
+from mla_latent_kv_absorb_amd.workloads import (ATTN_CONFIGS, EXPAND_CONFIGS, AttnConfig,
+                                                 make_attn_inputs, make_expand_inputs)
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_worked.json")
+
+
+def rel_err(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.abs(a - b).max() / max(np.abs(b).max(), 1e-300))
+
+
+def small_cfg(**kw):
+    base = dict(name="t", dtype="f32", batch=2, seqlen_q=1, n_heads=3, kv_lora_rank=8,
+                qk_rope_head_dim=4, qk_nope_head_dim=5, v_head_dim=6, end_pos=7, cache_len=9,
+                cache_batch=3, wkv_b_var=1.0 / 8, seed=11)
+    base.update(kw)
+    return AttnConfig(**base)
+
+
+def run(route, cfg, x, dtype=np.float64, **kw):
+    f = O.absorb_attention if route == "absorb" else O.naive_attention
+    return f(x["q_nope"], x["q_pe"], x["kv_cache"], x["pe_cache"], x["wkv_b"], cfg.end_pos,
+             cfg.softmax_scale, cfg.v_head_dim, dtype=dtype, **kw)
+
+
+def wuv_rows(wkv_b, H, Dn, Dv, h):
+    """W_UV[h] picked by explicit row numbers of wkv_b (rows h*(Dn+Dv)+Dn .. +Dv-1)."""
+    return np.stack([np.asarray(wkv_b[h * (Dn + Dv) + Dn + e], np.float64) for e in range(Dv)])
+
+
+# ----------------------------------------------------------------------------- pins as functions
+# Each returns the worst relative error it sees; the mutation tests reuse them.
+
+CASES = [
+    small_cfg(),
+    small_cfg(seqlen_q=3, end_pos=7, seed=12),            # causal chunk
+    small_cfg(seqlen_q=7, end_pos=7, seed=13),            # chunk covering the whole prefix
+    small_cfg(batch=1, n_heads=2, end_pos=1, seed=14),    # a single cached token
+]
+
+
+def pin_naive_equals_absorb():
+    worst = 0.0
+    for cfg in CASES + [ATTN_CONFIGS["tiny_f32"]]:
+        x = make_attn_inputs(cfg)
+        worst = max(worst, rel_err(run("absorb", cfg, x), run("naive", cfg, x)))
+    return worst
+
+
+def pin_golden():
+    g = json.load(open(GOLDEN))
+    worst = 0.0
+    for key in ("absorb_decode", "absorb_chunk", "absorb_scaled_two_heads"):
+        c = g[key]
+        q_nope = np.array(c["q_nope"])
+        H, Dn = q_nope.shape[2], q_nope.shape[3]
+        Dv = np.array(c["wkv_b"]).shape[0] // H - Dn
+        out = O.absorb_attention(q_nope, np.array(c["q_pe"]), np.array(c["kv_cache"]),
+                                 np.array(c["pe_cache"]), np.array(c["wkv_b"]), c["end_pos"],
+                                 c["softmax_scale"], Dv)
+        worst = max(worst, rel_err(out, np.array(c["expected_out"])))
+    e = g["expand"]
+    k, v = O.expand_kv(np.array(e["c_kv"]), np.array(e["rms_w"]), np.array(e["wkv_b"]), 2, 1, 1, e["eps"])
+    worst = max(worst, rel_err(k, np.array(e["expected_k_nope"])), rel_err(v, np.array(e["expected_v"])))
+    return worst
+
+
+def pin_softmax_rows():
+    worst = 0.0
+    for cfg in CASES:
+        x = make_attn_inputs(cfg)
+        _, inter = run("absorb", cfg, x, return_intermediates=True)
+        p = inter["p"]
+        worst = max(worst, float(np.abs(p.sum(-1) - 1.0).max()))
+        vis = O.allowed_positions(cfg.seqlen_q, cfg.end_pos)
+        # positions later than the query's own must carry no weight; brute-force visibility
+        for s in range(cfg.seqlen_q):
+            last = cfg.end_pos - cfg.seqlen_q + s
+            worst = max(worst, float(np.abs(p[:, s, :, last + 1:]).max(initial=0.0)))
+            worst = max(worst, 0.0 if vis[s].sum() == last + 1 else 1.0)
+    return worst
+
+
+def pin_constant_cache():
+    """kv[b,t] = c and pe[b,t] = r for all t: every score is equal per row, so out = W_UV[h] c."""
+    cfg = small_cfg(seqlen_q=2, end_pos=6)
+    x = make_attn_inputs(cfg)
+    rng = np.random.default_rng(5)
+    c = rng.standard_normal((cfg.cache_batch, cfg.kv_lora_rank))
+    r = rng.standard_normal((cfg.cache_batch, cfg.qk_rope_head_dim))
+    x["kv_cache"] = np.repeat(c[:, None, :], cfg.cache_len, axis=1)
+    x["pe_cache"] = np.repeat(r[:, None, :], cfg.cache_len, axis=1)
+    out = run("absorb", cfg, x)
+    worst = 0.0
+    for b in range(cfg.batch):
+        for h in range(cfg.n_heads):
+            expect = wuv_rows(x["wkv_b"], cfg.n_heads, cfg.qk_nope_head_dim, cfg.v_head_dim, h) @ c[b]
+            for s in range(cfg.seqlen_q):
+                worst = max(worst, rel_err(out[b, s, h], expect))
+    return worst
+
+
+def pin_single_position():
+    """end_pos = 1: the only visible position gets probability 1, so out = W_UV[h] kv[b,0]."""
+    cfg = small_cfg(end_pos=1)
+    x = make_attn_inputs(cfg)
+    out = run("absorb", cfg, x)
+    worst = 0.0
+    for b in range(cfg.batch):
+        for h in range(cfg.n_heads):
+            expect = wuv_rows(x["wkv_b"], cfg.n_heads, cfg.qk_nope_head_dim, cfg.v_head_dim, h) @ \
+                np.asarray(x["kv_cache"][b, 0], np.float64)
+            worst = max(worst, rel_err(out[b, 0, h], expect))
+    return worst
+
+
+def pin_zero_query():
+    """q = 0: all visible scores are 0, p is uniform, out = W_UV[h] * mean of the visible kv rows."""
+    cfg = small_cfg(seqlen_q=3, end_pos=7)
+    x = make_attn_inputs(cfg)
+    x["q_nope"] = np.zeros_like(x["q_nope"])
+    x["q_pe"] = np.zeros_like(x["q_pe"])
+    out = run("absorb", cfg, x)
+    worst = 0.0
+    for b in range(cfg.batch):
+        for s in range(cfg.seqlen_q):
+            last = cfg.end_pos - cfg.seqlen_q + s
+            mean = np.asarray(x["kv_cache"][b, :last + 1], np.float64).mean(axis=0)
+            for h in range(cfg.n_heads):
+                expect = wuv_rows(x["wkv_b"], cfg.n_heads, cfg.qk_nope_head_dim, cfg.v_head_dim, h) @ mean
+                worst = max(worst, rel_err(out[b, s, h], expect))
+    return worst
+
+
+def pin_rope_shift_invariance():
+    """pe rows identical over t: the rope term adds the same constant to every score of a row,
+    which softmax cancels, so the output does not depend on q_pe."""
+    cfg = small_cfg(seqlen_q=2)
+    x = make_attn_inputs(cfg)
+    x["pe_cache"] = np.repeat(x["pe_cache"][:, :1, :], cfg.cache_len, axis=1)
+    a = run("absorb", cfg, x)
+    x2 = dict(x)
+    x2["q_pe"] = np.random.default_rng(9).standard_normal(x["q_pe"].shape) * 3.0
+    return rel_err(run("absorb", cfg, x2), a)
+
+
+def pin_torch_sdpa():
+    """Naive-route q, k, v through torch's scaled_dot_product_attention (CPU, fp64, causal
+    boolean mask) equal the oracle's output."""
+    worst = 0.0
+    for cfg in CASES:
+        x = make_attn_inputs(cfg)
+        out, inter = run("naive", cfg, x, return_intermediates=True)
+        q = np.concatenate([x["q_nope"], x["q_pe"]], -1).astype(np.float64)
+        qt = torch.from_numpy(q).permute(0, 2, 1, 3).contiguous()                    # [B,H,S,D]
+        kt = torch.from_numpy(np.ascontiguousarray(inter["k"])).permute(0, 2, 1, 3).contiguous()
+        vt = torch.from_numpy(np.ascontiguousarray(inter["v"])).permute(0, 2, 1, 3).contiguous()
+        start = cfg.end_pos - cfg.seqlen_q
+        mask = torch.tensor([[t <= start + s for t in range(cfg.end_pos)] for s in range(cfg.seqlen_q)])
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask,
+                                                               scale=cfg.softmax_scale)
+        worst = max(worst, rel_err(out, ref.permute(0, 2, 1, 3).numpy()))
+    return worst
+
+
+def pin_bruteforce():
+    worst = 0.0
+    for cfg in [ATTN_CONFIGS["tiny_f32"], small_cfg(batch=1, seqlen_q=3, n_heads=2, end_pos=8, seed=21)]:
+        x = make_attn_inputs(cfg)
+        bf = BF.attention_loops(x["q_nope"].tolist(), x["q_pe"].tolist(), x["kv_cache"].tolist(),
+                                x["pe_cache"].tolist(), x["wkv_b"].tolist(), cfg.end_pos,
+                                cfg.softmax_scale, cfg.v_head_dim)
+        worst = max(worst, rel_err(run("absorb", cfg, x), np.array(bf)))
+    return worst
+
+
+def pin_chunk_rows_are_decodes():
+    """Row s of a causal chunk equals a decode call whose end_pos is the row's position + 1."""
+    cfg = small_cfg(seqlen_q=4, end_pos=7)
+    x = make_attn_inputs(cfg)
+    chunk = run("absorb", cfg, x)
+    worst = 0.0
+    for s in range(cfg.seqlen_q):
+        dcfg = cfg.replace(seqlen_q=1, end_pos=cfg.start_pos + s + 1)
+        xd = dict(x, q_nope=x["q_nope"][:, s:s + 1], q_pe=x["q_pe"][:, s:s + 1])
+        worst = max(worst, rel_err(chunk[:, s:s + 1], run("absorb", dcfg, xd)))
+    return worst
+
+
+def pin_split_merge():
+    """Any partition of [0, end_pos) merged with the online-softmax rule gives the unsplit o_lat,
+    including one-token splits and splits that are fully masked for some rows."""
+    cfg = small_cfg(seqlen_q=3, end_pos=9, cache_len=9)
+    x = make_attn_inputs(cfg)
+    _, inter = run("absorb", cfg, x, return_intermediates=True)
+    worst = 0.0
+    for cuts in ([0, 9], [0, 1, 2, 3, 9], [0, 4, 5, 9], [0, 6, 7, 8, 9], [0, 3, 3, 9]):
+        parts = [O.attention_partial(inter["q_lat"], x["q_pe"], x["kv_cache"], x["pe_cache"],
+                                     cfg.end_pos, cfg.softmax_scale, a, b) for a, b in zip(cuts, cuts[1:])]
+        worst = max(worst, rel_err(O.merge_partials(parts), inter["o_lat"]))
+    return worst
+
+
+def pin_rms_norm():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((5, 16)) * 3.0
+    w = 1.0 + 0.1 * rng.standard_normal(16)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(x), (16,), torch.from_numpy(w), eps=1e-6).numpy()
+    worst = rel_err(O.rms_norm(x, w, 1e-6), ref)
+    # one-hot row a*e_j with unit weight: n = a e_j / sqrt(a^2/C + eps)
+    C, a, eps = 16, 2.5, 1e-3
+    for j in (0, 7, 15):
+        xo = np.zeros((1, C))
+        xo[0, j] = a
+        expect = np.zeros((1, C))
+        expect[0, j] = a / math.sqrt(a * a / C + eps)
+        worst = max(worst, rel_err(O.rms_norm(xo, np.ones(C), eps), expect))
+    return worst
+
+
+def pin_expand():
+    """Expansion against scalar loops, and against the naive route's own K/V materialisation
+    for kv = RMSNorm(c_kv) (the two pages describe the same up-projection)."""
+    cfg = EXPAND_CONFIGS["tiny_f32"].replace(n_tokens=6, n_heads=2, kv_lora_rank=8, qk_nope_head_dim=3,
+                                            v_head_dim=5, seed=17)
+    x = make_expand_inputs(cfg)
+    k, v = O.expand_kv(x["c_kv"], x["rms_w"], x["wkv_b"], cfg.n_heads, cfg.qk_nope_head_dim,
+                       cfg.v_head_dim, cfg.eps)
+    kb, vb = BF.expand_loops(x["c_kv"].tolist(), x["rms_w"].tolist(), x["wkv_b"].tolist(), cfg.n_heads,
+                             cfg.qk_nope_head_dim, cfg.v_head_dim, cfg.eps)
+    worst = max(rel_err(k, np.array(kb)), rel_err(v, np.array(vb)))
+    n = O.rms_norm(x["c_kv"], x["rms_w"], cfg.eps)
+    kn, vn = O.naive_kv(n[None], x["wkv_b"], 1, cfg.n_tokens, cfg.n_heads, cfg.qk_nope_head_dim,
+                        cfg.v_head_dim)
+    worst = max(worst, rel_err(k, kn[0].transpose(1, 0, 2)), rel_err(v, vn[0].transpose(1, 0, 2)))
+    return worst
+
+
+PINS = {
+    "naive_equals_absorb": (pin_naive_equals_absorb, 1e-12),
+    "golden": (pin_golden, 1e-12),
+    "softmax_rows": (pin_softmax_rows, 1e-12),
+    "constant_cache": (pin_constant_cache, 1e-12),
+    "single_position": (pin_single_position, 1e-12),
+    "zero_query": (pin_zero_query, 1e-12),
+    "rope_shift_invariance": (pin_rope_shift_invariance, 1e-12),
+    "torch_sdpa": (pin_torch_sdpa, 1e-12),
+    "bruteforce": (pin_bruteforce, 1e-12),
+    "chunk_rows_are_decodes": (pin_chunk_rows_are_decodes, 1e-12),
+    "split_merge": (pin_split_merge, 1e-12),
+    "rms_norm": (pin_rms_norm, 1e-12),
+    "expand": (pin_expand, 1e-12),
+}
+
+
+@pytest.mark.parametrize("name", list(PINS))
+def test_pin(name):
+    fn, tol = PINS[name]
+    err = fn()
+    assert err <= tol, f"pin {name}: error {err:.3e} > {tol:.1e}"
+
+
+def test_naive_equals_absorb_fp32():
+    """The stated invariant at fp32 on the tiny workload: agreement within 1e-5 of max|ref|."""
+    cfg = ATTN_CONFIGS["tiny_f32"]
+    x = make_attn_inputs(cfg)
+    a = run("absorb", cfg, x, dtype=np.float32)
+    n = run("naive", cfg, x, dtype=np.float32)
+    assert a.dtype == np.float32 and n.dtype == np.float32
+    assert rel_err(a, n) <= 1e-5
+
+
+def test_rows_match_full():
+    cfg = small_cfg(seqlen_q=3, end_pos=7)
+    x = make_attn_inputs(cfg)
+    full = run("absorb", cfg, x)
+    rows = [(0, 0, 0), (1, 2, 2), (0, 1, 1), (1, 0, 2)]
+    sel = O.absorb_attention_rows(x["q_nope"], x["q_pe"], x["kv_cache"], x["pe_cache"], x["wkv_b"],
+                                  cfg.end_pos, cfg.softmax_scale, cfg.v_head_dim, rows)
+    assert rel_err(sel, np.stack([full[b, s, h] for b, s, h in rows])) <= 1e-13
+
+
+# ----------------------------------------------------------------------------- planted mistakes
+
+def _failing_pins():
+    bad = []
+    for name, (fn, tol) in PINS.items():
+        try:
+            err = fn()
+        except Exception:
+            err = float("inf")
+        if not (err <= tol):
+            bad.append(name)
+    return bad
+
+
+def _swap_split(wkv_b, n_heads, qk_nope_head_dim, v_head_dim):
+    C = wkv_b.shape[1]
+    per_head = wkv_b.reshape(n_heads, qk_nope_head_dim + v_head_dim, C)
+    return per_head[:, v_head_dim:, :], per_head[:, :v_head_dim, :]
+
+
+def _off_by_one_mask(seqlen_q, end_pos):
+    start_pos = end_pos - seqlen_q
+    return np.arange(end_pos)[None, :] < (start_pos + np.arange(seqlen_q))[:, None] + (seqlen_q == 1)
+
+
+def _softmax_no_max(scores, allowed):
+    e = np.where(allowed, np.exp(scores), 0.0)
+    return e / e.sum(axis=-2, keepdims=True)
+
+
+def _rms_eps_outside(x, w, eps, dtype=np.float64):
+    x, w = np.asarray(x, dtype), np.asarray(w, dtype)
+    return x / (np.sqrt(np.mean(x * x, axis=-1, keepdims=True)) + eps) * w
+
+
+def _merge_forgets_weight(parts):
+    ms = np.stack([p[0] for p in parts])
+    M = ms.max(axis=0)
+    num, den = 0.0, 0.0
+    for m, l, o in parts:
+        w = np.where(np.isfinite(m), np.exp(np.where(np.isfinite(m), m - M, 0.0)), 0.0)
+        num = num + w[..., None] * o
+        den = den + l
+    return num / den[..., None]
+
+
+_orig_absorb = O.absorb_attention
+_orig_expand = O.expand_kv
+
+
+def _absorb_without_rope(q_nope, q_pe, *a, **kw):
+    return _orig_absorb(q_nope, np.zeros_like(np.asarray(q_pe)), *a, **kw)
+
+
+def _absorb_transposed_heads(*a, **kw):
+    r = _orig_absorb(*a, **kw)
+    if kw.get("return_intermediates"):
+        return r[0][:, :, ::-1], r[1]
+    return r[:, :, ::-1]
+
+
+def _expand_swapped(c_kv, rms_w, wkv_b, n_heads, qk_nope_head_dim, v_head_dim, eps, dtype=np.float64):
+    n = O.rms_norm(c_kv, rms_w, eps, dtype)
+    y = np.matmul(n, np.asarray(wkv_b, dtype).T).reshape(n.shape[0], n_heads, -1).transpose(1, 0, 2)
+    return y[..., v_head_dim:], y[..., :v_head_dim]
+
+
+MUTATIONS = {
+    "swap_uk_uv": ("split_wkv_b", _swap_split),
+    "mask_off_by_one": ("allowed_positions", _off_by_one_mask),
+    "softmax_wrong_axis": ("masked_softmax", _softmax_no_max),
+    "rms_eps_outside_sqrt": ("rms_norm", _rms_eps_outside),
+    "merge_forgets_weight": ("merge_partials", _merge_forgets_weight),
+    "absorb_drops_rope": ("absorb_attention", _absorb_without_rope),
+    "absorb_reverses_heads": ("absorb_attention", _absorb_transposed_heads),
+    "expand_split_swapped": ("expand_kv", _expand_swapped),
+}
+
+
+@pytest.mark.parametrize("mutation", list(MUTATIONS))
+def test_planted_mistake_is_caught(mutation, monkeypatch):
+    attr, fn = MUTATIONS[mutation]
+    monkeypatch.setattr(O, attr, fn)
+    bad = _failing_pins()
+    assert bad, f"planted mistake {mutation} passed every pin"
