@@ -1,0 +1,148 @@
+/*
+ * mla_absorb.h -- C ABI of the MI355X (gfx950) MLA absorb-attention library.
+ *
+ * Two operations, each a set of HIP kernels enqueued on a caller stream:
+ *
+ *   mla_absorb_attn  DeepSeek-V3 Multi-Head Latent Attention in "absorb" form, as the page
+ *                    "Naive vs Absorb Attention Implementations in DeepSeek-V3" describes it
+ *                    (sections "Absorb Implementation Cache Design" and "Absorb Path
+ *                    Execution"): the no-rope query is absorbed through each head's W_UK
+ *                    slice of wkv_b into the kv_lora_rank latent space, scored against the
+ *                    compressed kv_cache plus the separate pe_cache, softmax-normalised over
+ *                    the cached positions, summed over kv_cache in latent space, and
+ *                    projected out through each head's W_UV slice.
+ *
+ *   mla_expand_kv    "Latent KV expansion with split" (kernelindex.com, operation 064):
+ *                    RMSNorm over the latent, the wkv_b projection to
+ *                    n_heads * (qk_nope_head_dim + v_head_dim), then reshape, transpose and
+ *                    split into head-major K_nope and V (the naive path's keys and values).
+ *
+ * Conventions shared by every entry point
+ *   - Data pointers are DEVICE pointers (hipMalloc'd or torch CUDA tensors) on the current HIP
+ *     device; the caller owns every buffer, including the workspace.  The library keeps no
+ *     pointer after a call returns and never modifies inputs.
+ *   - All tensors are dense, row-major (innermost index contiguous) and of one element type:
+ *     MLA_DTYPE_F32 (float) or MLA_DTYPE_BF16 (bfloat16 stored as uint16).  Every pointer must
+ *     be 16-byte aligned.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL means the default stream); results
+ *     are valid once the stream has synchronised.  Calls on one stream are ordered; concurrent
+ *     calls on different streams must not share a workspace.
+ *   - Every argument is validated before any HIP call: a failing call returns a negative status,
+ *     enqueues nothing and sets a thread-local message (mla_last_error).  Launch failures return
+ *     MLA_ERR_HIP.  Nothing aborts and no C++ exception crosses the ABI.
+ *   - Accumulation, softmax and normalisation run in fp32; bf16 outputs are rounded to nearest
+ *     even.
+ */
+#ifndef MLA_ABSORB_H
+#define MLA_ABSORB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------------------------- */
+#define MLA_OK 0
+#define MLA_ERR_NULL (-1)        /* a required pointer is NULL                                 */
+#define MLA_ERR_SHAPE (-2)       /* a size is not positive, or sizes disagree                  */
+#define MLA_ERR_DTYPE (-3)       /* unknown element type                                       */
+#define MLA_ERR_RANGE (-4)       /* end_pos / batch beyond the cache capacity, S > end_pos     */
+#define MLA_ERR_ALIGN (-5)       /* a pointer is not 16-byte aligned                           */
+#define MLA_ERR_WORKSPACE (-6)   /* workspace missing or smaller than the size query returns   */
+#define MLA_ERR_HIP (-7)         /* a HIP runtime call or kernel launch failed                 */
+#define MLA_ERR_UNSUPPORTED (-8) /* option or shape the requested kernel path cannot run       */
+
+/* ---- element types ------------------------------------------------------------------------ */
+#define MLA_DTYPE_F32 0
+#define MLA_DTYPE_BF16 1
+
+/* ---- kernel paths (mla_attn_options.path) --------------------------------------------------- */
+#define MLA_PATH_AUTO 0    /* matrix-core kernels when the shape allows, else the plain path   */
+#define MLA_PATH_PLAIN 1   /* plain vector-ALU kernels: any shape, fp32 or bf16 (slow)          */
+#define MLA_PATH_MFMA 2    /* bf16 matrix-core kernels only; MLA_ERR_UNSUPPORTED otherwise      */
+
+/* Sizes of one absorb-attention call (names follow DeepSeek-V3's ModelArgs). */
+typedef struct mla_attn_shape {
+  int64_t batch;            /* B   sequences attended: rows [0, B) of the caches               */
+  int64_t seqlen_q;         /* S   new query tokens per sequence (1 = decode)                  */
+  int64_t n_heads;          /* H                                                                */
+  int64_t kv_lora_rank;     /* C   latent width                                                 */
+  int64_t qk_rope_head_dim; /* R   rope width of q_pe and pe_cache                              */
+  int64_t qk_nope_head_dim; /* Dn  no-rope query width (rows of W_UK per head)                  */
+  int64_t v_head_dim;       /* Dv  value width (rows of W_UV per head)                          */
+  int64_t cache_batch;      /* Bmax rows allocated in kv_cache / pe_cache (>= B)                */
+  int64_t cache_len;        /* Tmax positions allocated per cache row (>= end_pos)              */
+} mla_attn_shape;
+
+/* Optional knobs of mla_absorb_attn; pass NULL for the defaults (all zero). */
+typedef struct mla_attn_options {
+  int32_t num_splits; /* 0: the planner chooses; n > 0: split [0, end_pos) into n ranges        */
+  int32_t path;       /* MLA_PATH_*                                                             */
+} mla_attn_options;
+
+/*
+ * Bytes of device workspace mla_absorb_attn needs for this shape, end_pos, dtype and options
+ * (the absorbed query and the per-split softmax partials).  Returns 0 when the arguments are
+ * invalid (the same checks as mla_absorb_attn; see mla_last_error).
+ */
+size_t mla_absorb_attn_workspace_size(const mla_attn_shape *shape, int64_t end_pos, int32_t dtype,
+                                      const mla_attn_options *options);
+
+/*
+ * Absorb-form MLA attention ("Naive vs Absorb Attention Implementations in DeepSeek-V3",
+ * section "Absorb Path Execution").
+ *
+ *   q_nope    [B, S, H, Dn]                 no-rope query
+ *   q_pe      [B, S, H, R]                  rope query (already rotated)
+ *   kv_cache  [Bmax, Tmax, C]               compressed latent per cached position (already
+ *                                           normalised; this call does no RMSNorm)
+ *   pe_cache  [Bmax, Tmax, R]               rope key per cached position, shared by all heads
+ *   wkv_b     [H * (Dn + Dv), C]            Linear weight; head h owns rows h*(Dn+Dv) ..
+ *                                           (h+1)*(Dn+Dv)-1, the first Dn being W_UK[h] and the
+ *                                           last Dv being W_UV[h]
+ *   end_pos   attend to cache positions [0, end_pos) of rows [0, B)
+ *   softmax_scale  multiplies (q_lat . kv + q_pe . pe) before the softmax
+ *   out       [B, S, H, Dv]                 written; must not alias any input or the workspace
+ *
+ * With S > 1 the S query tokens sit at positions end_pos - S .. end_pos - 1 and query s sees
+ * cache positions t <= end_pos - S + s (causal within the chunk); the caller has already
+ * written their kv/pe rows.  Requires 1 <= S <= end_pos <= Tmax and 1 <= B <= Bmax.
+ * workspace: at least mla_absorb_attn_workspace_size(...) bytes of device memory (may be NULL
+ * when that size is 0).  Returns MLA_OK or a negative MLA_ERR_* status.
+ */
+int32_t mla_absorb_attn(const void *q_nope, const void *q_pe, const void *kv_cache,
+                        const void *pe_cache, const void *wkv_b, int64_t end_pos,
+                        float softmax_scale, void *out, const mla_attn_shape *shape,
+                        int32_t dtype, const mla_attn_options *options, void *workspace,
+                        size_t workspace_bytes, void *stream);
+
+/*
+ * Latent KV expansion with split (kernelindex.com operation 064).
+ *
+ *   c_kv    [T, C]                 raw compressed latent of T tokens
+ *   rms_w   [C]                    RMSNorm weight
+ *   wkv_b   [H * (Dn + Dv), C]     Linear weight, rows laid out as in mla_absorb_attn
+ *   k_nope  [H, T, Dn]             written: k_nope[h,t,:] = rows h*(Dn+Dv) .. +Dn-1 of
+ *                                  wkv_b applied to n[t]
+ *   v       [H, T, Dv]             written: the next Dv rows applied to n[t]
+ * where n[t,:] = c_kv[t,:] / sqrt(mean_c c_kv[t,c]^2 + eps) * rms_w.  No workspace.
+ * k_nope and v must not alias the inputs or each other.  Returns MLA_OK or MLA_ERR_*.
+ */
+int32_t mla_expand_kv(const void *c_kv, const void *rms_w, const void *wkv_b, void *k_nope,
+                      void *v, int64_t n_tokens, int64_t n_heads, int64_t kv_lora_rank,
+                      int64_t qk_nope_head_dim, int64_t v_head_dim, float eps, int32_t dtype,
+                      int32_t path, void *stream);
+
+/* Static text for a status code (never NULL). */
+const char *mla_strerror(int32_t status);
+
+/* Thread-local detail of the most recent failing call on this thread ("" if none). */
+const char *mla_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_ABSORB_H */

@@ -1,0 +1,183 @@
+"""Thin ctypes binding over libmla_absorb.so (declared in include/mla_absorb.h).
+
+Argument marshalling only: shapes are read off torch tensors, outputs and workspace
+are allocated with torch on the tensors' device, the call goes to the caller's
+current HIP stream, and every step of the computation runs in the library's HIP
+kernels.  There is no fallback: if the library cannot be loaded, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmla_absorb.so")
+
+MLA_OK = 0
+MLA_ERR_NULL = -1
+MLA_ERR_SHAPE = -2
+MLA_ERR_DTYPE = -3
+MLA_ERR_RANGE = -4
+MLA_ERR_ALIGN = -5
+MLA_ERR_WORKSPACE = -6
+MLA_ERR_HIP = -7
+MLA_ERR_UNSUPPORTED = -8
+
+MLA_DTYPE_F32 = 0
+MLA_DTYPE_BF16 = 1
+
+PATHS = {"auto": 0, "plain": 1, "mfma": 2}
+
+EXPORTED = ("mla_absorb_attn", "mla_absorb_attn_workspace_size", "mla_expand_kv", "mla_strerror",
+            "mla_last_error")
+
+
+class AttnShape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in (
+        "batch", "seqlen_q", "n_heads", "kv_lora_rank", "qk_rope_head_dim", "qk_nope_head_dim",
+        "v_head_dim", "cache_batch", "cache_len")]
+
+
+class AttnOptions(ctypes.Structure):
+    _fields_ = [("num_splits", ctypes.c_int32), ("path", ctypes.c_int32)]
+
+
+class MLAError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{strerror(status)} ({status}): {detail}")
+        self.status = status
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library once; raise if it is missing (nothing here falls back to another path)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m mla_latent_kv_absorb_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    lib.mla_absorb_attn.argtypes = [vp, vp, vp, vp, vp, i64, ctypes.c_float, vp, ctypes.POINTER(AttnShape), i32,
+                                    ctypes.POINTER(AttnOptions), vp, sz, vp]
+    lib.mla_absorb_attn.restype = i32
+    lib.mla_absorb_attn_workspace_size.argtypes = [ctypes.POINTER(AttnShape), i64, i32, ctypes.POINTER(AttnOptions)]
+    lib.mla_absorb_attn_workspace_size.restype = sz
+    lib.mla_expand_kv.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float, i32, i32, vp]
+    lib.mla_expand_kv.restype = i32
+    lib.mla_strerror.argtypes = [i32]
+    lib.mla_strerror.restype = ctypes.c_char_p
+    lib.mla_last_error.argtypes = []
+    lib.mla_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def strerror(status: int) -> str:
+    return load().mla_strerror(status).decode()
+
+
+def last_error() -> str:
+    return load().mla_last_error().decode()
+
+
+def _check(status: int) -> None:
+    if status != MLA_OK:
+        raise MLAError(status, last_error())
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.float32:
+        return MLA_DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return MLA_DTYPE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _stream_handle(device) -> Optional[int]:
+    import torch
+
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _require_device(*ts) -> None:
+    dev = ts[0].device
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must live on a GPU device")
+        if t.device != dev:
+            raise ValueError("all tensors must be on the same device")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+        if t.dtype != ts[0].dtype:
+            raise ValueError("all tensors must share one dtype")
+
+
+def attn_shape(q_nope, q_pe, kv_cache, wkv_b) -> AttnShape:
+    B, S, H, Dn = q_nope.shape
+    R = q_pe.shape[-1]
+    Bmax, Tmax, C = kv_cache.shape
+    if wkv_b.shape[0] % H:
+        raise ValueError("wkv_b rows must be a multiple of n_heads")
+    Dv = wkv_b.shape[0] // H - Dn
+    return AttnShape(B, S, H, C, R, Dn, Dv, Bmax, Tmax)
+
+
+def absorb_attn_workspace_size(shape: AttnShape, end_pos: int, dtype: int, num_splits: int = 0,
+                               path: str = "auto") -> int:
+    lib = load()
+    opt = AttnOptions(num_splits, PATHS[path])
+    n = lib.mla_absorb_attn_workspace_size(ctypes.byref(shape), end_pos, dtype, ctypes.byref(opt))
+    if n == 0 and last_error():
+        raise MLAError(MLA_ERR_SHAPE, last_error())
+    return int(n)
+
+
+def absorb_attn(q_nope, q_pe, kv_cache, pe_cache, wkv_b, end_pos: int, softmax_scale: float, out=None, *,
+                num_splits: int = 0, path: str = "auto", workspace=None):
+    """MLA attention in absorb form on torch GPU tensors; returns out [B, S, H, Dv]."""
+    import torch
+
+    lib = load()
+    _require_device(q_nope, q_pe, kv_cache, pe_cache, wkv_b)
+    shape = attn_shape(q_nope, q_pe, kv_cache, wkv_b)
+    dt = _dtype_code(q_nope)
+    if out is None:
+        out = torch.empty((shape.batch, shape.seqlen_q, shape.n_heads, shape.v_head_dim), dtype=q_nope.dtype,
+                          device=q_nope.device)
+    _require_device(q_nope, out)
+    opt = AttnOptions(num_splits, PATHS[path])
+    need = absorb_attn_workspace_size(shape, end_pos, dt, num_splits, path)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q_nope.device)
+    rc = lib.mla_absorb_attn(q_nope.data_ptr(), q_pe.data_ptr(), kv_cache.data_ptr(), pe_cache.data_ptr(),
+                             wkv_b.data_ptr(), end_pos, softmax_scale, out.data_ptr(), ctypes.byref(shape), dt,
+                             ctypes.byref(opt), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                             _stream_handle(q_nope.device))
+    _check(rc)
+    return out
+
+
+def expand_kv(c_kv, rms_w, wkv_b, n_heads: int, qk_nope_head_dim: int, v_head_dim: int, eps: float = 1e-6,
+              k_nope=None, v=None, *, path: str = "auto") -> Tuple["object", "object"]:
+    """Latent KV expansion with split; returns (k_nope [H, T, Dn], v [H, T, Dv])."""
+    import torch
+
+    lib = load()
+    _require_device(c_kv, rms_w, wkv_b)
+    T, C = c_kv.shape
+    if k_nope is None:
+        k_nope = torch.empty((n_heads, T, qk_nope_head_dim), dtype=c_kv.dtype, device=c_kv.device)
+    if v is None:
+        v = torch.empty((n_heads, T, v_head_dim), dtype=c_kv.dtype, device=c_kv.device)
+    _require_device(c_kv, k_nope, v)
+    rc = lib.mla_expand_kv(c_kv.data_ptr(), rms_w.data_ptr(), wkv_b.data_ptr(), k_nope.data_ptr(), v.data_ptr(),
+                           T, n_heads, C, qk_nope_head_dim, v_head_dim, eps, _dtype_code(c_kv), PATHS[path],
+                           _stream_handle(c_kv.device))
+    _check(rc)
+    return k_nope, v

@@ -1,0 +1,47 @@
+// Internal interface between the C-ABI layer (mla_api.cpp) and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+// One validated absorb-attention call.  Rows are the B*S*H query rows in (b, s, h) order.
+struct AttnCall {
+  int64_t B, S, H, C, R, Dn, Dv, Bmax, Tmax;
+  int64_t end_pos;
+  float scale;
+  int32_t dtype;      // MLA_DTYPE_*
+  int32_t splits;     // ranges the positions [0, end_pos) are cut into
+  int64_t split_len;  // positions per range (the last may be shorter or empty)
+  const void *q_nope, *q_pe, *kv, *pe, *wkv_b;
+  void *out;
+  void *ws;           // workspace (layout chosen by the path's workspace function)
+  hipStream_t stream;
+};
+
+struct ExpandCall {
+  int64_t T, H, C, Dn, Dv;
+  float eps;
+  int32_t dtype;
+  const void *c_kv, *rms_w, *wkv_b;
+  void *k_nope, *v;
+  hipStream_t stream;
+};
+
+// ---- plain vector-ALU path (any shape, fp32 or bf16) -------------------------------------------
+size_t plain_attn_workspace(const AttnCall &c);
+int32_t plain_attn_splits(const AttnCall &c);
+hipError_t plain_absorb_attn(const AttnCall &c);
+hipError_t plain_expand_kv(const ExpandCall &c);
+
+// ---- matrix-core path (bf16, shapes accepted by mfma_attn_supported) ---------------------------
+bool mfma_attn_supported(const AttnCall &c, const char **why);
+size_t mfma_attn_workspace(const AttnCall &c);
+int32_t mfma_attn_splits(const AttnCall &c, int num_cus);
+hipError_t mfma_absorb_attn(const AttnCall &c);
+
+bool mfma_expand_supported(const ExpandCall &c, const char **why);
+hipError_t mfma_expand_kv(const ExpandCall &c);
+
+}  // namespace mla

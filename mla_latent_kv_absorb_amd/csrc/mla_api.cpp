@@ -1,0 +1,220 @@
+// C-ABI layer: argument validation, split planning and dispatch to the kernel paths.
+// Every check runs before the first HIP call, so a rejected call enqueues nothing.
+#include <hip/hip_runtime.h>
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/mla_absorb.h"
+#include "launch.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int32_t fail(int32_t status, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+void clear_error() { g_last_error[0] = '\0'; }
+
+bool misaligned(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+size_t elem_size(int32_t dtype) { return dtype == MLA_DTYPE_F32 ? 4 : 2; }
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+  const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+  return pa < pb + nb && pb < pa + na;
+}
+
+// Shape, dtype and option checks shared by the size query and the call.  Fills `c` (without
+// pointers) and picks the kernel path.  Makes no HIP call: the plan depends only on the
+// arguments, so the size query and the call always agree.
+int32_t plan_attn(const mla_attn_shape *shape, int64_t end_pos, int32_t dtype,
+                  const mla_attn_options *options, mla::AttnCall &c, bool &use_mfma) {
+  if (!shape) return fail(MLA_ERR_NULL, "shape is NULL");
+  if (dtype != MLA_DTYPE_F32 && dtype != MLA_DTYPE_BF16) return fail(MLA_ERR_DTYPE, "unknown dtype %d", dtype);
+  const mla_attn_shape &s = *shape;
+  const int64_t dims[] = {s.batch, s.seqlen_q, s.n_heads, s.kv_lora_rank, s.qk_rope_head_dim,
+                          s.qk_nope_head_dim, s.v_head_dim, s.cache_batch, s.cache_len};
+  const char *names[] = {"batch", "seqlen_q", "n_heads", "kv_lora_rank", "qk_rope_head_dim",
+                         "qk_nope_head_dim", "v_head_dim", "cache_batch", "cache_len"};
+  for (int i = 0; i < 9; ++i)
+    if (dims[i] <= 0 || dims[i] > (int64_t(1) << 31))
+      return fail(MLA_ERR_SHAPE, "%s = %lld is out of range", names[i], (long long)dims[i]);
+  if (s.batch > s.cache_batch)
+    return fail(MLA_ERR_RANGE, "batch %lld exceeds cache_batch %lld", (long long)s.batch, (long long)s.cache_batch);
+  if (end_pos < 1 || end_pos > s.cache_len)
+    return fail(MLA_ERR_RANGE, "end_pos %lld outside [1, cache_len=%lld]", (long long)end_pos, (long long)s.cache_len);
+  if (s.seqlen_q > end_pos)
+    return fail(MLA_ERR_RANGE, "seqlen_q %lld exceeds end_pos %lld", (long long)s.seqlen_q, (long long)end_pos);
+  const int64_t rows = s.batch * s.seqlen_q * s.n_heads;
+  if (rows > (int64_t(1) << 31) / 4)
+    return fail(MLA_ERR_SHAPE, "batch*seqlen_q*n_heads = %lld is too large", (long long)rows);
+  // every row of every tensor must start on a 16-byte boundary
+  const int64_t ealign = 16 / int64_t(elem_size(dtype));
+  if (s.kv_lora_rank % ealign || s.qk_rope_head_dim % ealign || s.qk_nope_head_dim % ealign ||
+      s.v_head_dim % ealign)
+    return fail(MLA_ERR_ALIGN, "kv_lora_rank, qk_rope_head_dim, qk_nope_head_dim and v_head_dim must be "
+                               "multiples of %lld elements (16-byte rows)", (long long)ealign);
+
+  mla_attn_options opt = {0, MLA_PATH_AUTO};
+  if (options) opt = *options;
+  if (opt.num_splits < 0 || opt.num_splits > 4096)
+    return fail(MLA_ERR_SHAPE, "num_splits %d outside [0, 4096]", opt.num_splits);
+  if (opt.path != MLA_PATH_AUTO && opt.path != MLA_PATH_PLAIN && opt.path != MLA_PATH_MFMA)
+    return fail(MLA_ERR_UNSUPPORTED, "unknown path %d", opt.path);
+
+  c = mla::AttnCall{};
+  c.B = s.batch; c.S = s.seqlen_q; c.H = s.n_heads; c.C = s.kv_lora_rank; c.R = s.qk_rope_head_dim;
+  c.Dn = s.qk_nope_head_dim; c.Dv = s.v_head_dim; c.Bmax = s.cache_batch; c.Tmax = s.cache_len;
+  c.end_pos = end_pos; c.dtype = dtype;
+
+  use_mfma = false;
+  if (opt.path != MLA_PATH_PLAIN) {
+    const char *why = "";
+    const bool ok = mla::mfma_attn_supported(c, &why);
+    if (opt.path == MLA_PATH_MFMA && !ok) return fail(MLA_ERR_UNSUPPORTED, "matrix-core path: %s", why);
+    use_mfma = ok;
+  }
+  if (opt.num_splits > 0) {
+    c.splits = opt.num_splits;
+  } else {
+    c.splits = use_mfma ? mla::mfma_attn_splits(c, 256) : mla::plain_attn_splits(c);
+  }
+  if (c.splits > end_pos) c.splits = int32_t(end_pos);
+  c.split_len = (end_pos + c.splits - 1) / c.splits;
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *mla_strerror(int32_t status) {
+  switch (status) {
+    case MLA_OK: return "success";
+    case MLA_ERR_NULL: return "a required pointer is NULL";
+    case MLA_ERR_SHAPE: return "invalid or inconsistent sizes";
+    case MLA_ERR_DTYPE: return "unknown element type";
+    case MLA_ERR_RANGE: return "end_pos/batch outside the cache capacity or seqlen_q > end_pos";
+    case MLA_ERR_ALIGN: return "pointer or row not 16-byte aligned";
+    case MLA_ERR_WORKSPACE: return "workspace missing or too small";
+    case MLA_ERR_HIP: return "HIP runtime or kernel launch failure";
+    case MLA_ERR_UNSUPPORTED: return "unsupported option or shape for the requested kernel path";
+    default: return "unknown status";
+  }
+}
+
+const char *mla_last_error(void) { return g_last_error; }
+
+size_t mla_absorb_attn_workspace_size(const mla_attn_shape *shape, int64_t end_pos, int32_t dtype,
+                                      const mla_attn_options *options) {
+  clear_error();
+  mla::AttnCall c;
+  bool use_mfma = false;
+  if (plan_attn(shape, end_pos, dtype, options, c, use_mfma) != MLA_OK) return 0;
+  return use_mfma ? mla::mfma_attn_workspace(c) : mla::plain_attn_workspace(c);
+}
+
+int32_t mla_absorb_attn(const void *q_nope, const void *q_pe, const void *kv_cache, const void *pe_cache,
+                        const void *wkv_b, int64_t end_pos, float softmax_scale, void *out,
+                        const mla_attn_shape *shape, int32_t dtype, const mla_attn_options *options,
+                        void *workspace, size_t workspace_bytes, void *stream) {
+  clear_error();
+  mla::AttnCall c;
+  bool use_mfma = false;
+  int32_t rc = plan_attn(shape, end_pos, dtype, options, c, use_mfma);
+  if (rc != MLA_OK) return rc;
+  const void *ptrs[] = {q_nope, q_pe, kv_cache, pe_cache, wkv_b, out};
+  const char *names[] = {"q_nope", "q_pe", "kv_cache", "pe_cache", "wkv_b", "out"};
+  for (int i = 0; i < 6; ++i) {
+    if (!ptrs[i]) return fail(MLA_ERR_NULL, "%s is NULL", names[i]);
+    if (misaligned(ptrs[i])) return fail(MLA_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
+  }
+  if (!(softmax_scale == softmax_scale) || softmax_scale <= 0.f || softmax_scale > 1e30f)
+    return fail(MLA_ERR_SHAPE, "softmax_scale must be a positive finite number");
+  const size_t es = elem_size(dtype);
+  const size_t rows = size_t(c.B * c.S * c.H);
+  const size_t bytes_in[] = {rows * size_t(c.Dn) * es, rows * size_t(c.R) * es,
+                             size_t(c.Bmax * c.Tmax * c.C) * es, size_t(c.Bmax * c.Tmax * c.R) * es,
+                             size_t(c.H * (c.Dn + c.Dv) * c.C) * es};
+  const size_t out_bytes = rows * size_t(c.Dv) * es;
+  for (int i = 0; i < 5; ++i)
+    if (overlaps(out, out_bytes, ptrs[i], bytes_in[i])) return fail(MLA_ERR_SHAPE, "out overlaps %s", names[i]);
+  const size_t need = use_mfma ? mla::mfma_attn_workspace(c) : mla::plain_attn_workspace(c);
+  if (need > 0) {
+    if (!workspace) return fail(MLA_ERR_WORKSPACE, "workspace is NULL but %zu bytes are needed", need);
+    if (workspace_bytes < need)
+      return fail(MLA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+    if (misaligned(workspace)) return fail(MLA_ERR_ALIGN, "workspace is not 16-byte aligned");
+    if (overlaps(workspace, need, out, out_bytes)) return fail(MLA_ERR_WORKSPACE, "workspace overlaps out");
+    for (int i = 0; i < 5; ++i)
+      if (overlaps(workspace, need, ptrs[i], bytes_in[i]))
+        return fail(MLA_ERR_WORKSPACE, "workspace overlaps %s", names[i]);
+  }
+  c.scale = softmax_scale;
+  c.q_nope = q_nope; c.q_pe = q_pe; c.kv = kv_cache; c.pe = pe_cache; c.wkv_b = wkv_b;
+  c.out = out; c.ws = workspace; c.stream = static_cast<hipStream_t>(stream);
+  if (use_mfma && c.splits == 0) c.splits = 1;
+  hipError_t e = use_mfma ? mla::mfma_absorb_attn(c) : mla::plain_absorb_attn(c);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return MLA_OK;
+}
+
+int32_t mla_expand_kv(const void *c_kv, const void *rms_w, const void *wkv_b, void *k_nope, void *v,
+                      int64_t n_tokens, int64_t n_heads, int64_t kv_lora_rank, int64_t qk_nope_head_dim,
+                      int64_t v_head_dim, float eps, int32_t dtype, int32_t path, void *stream) {
+  clear_error();
+  if (dtype != MLA_DTYPE_F32 && dtype != MLA_DTYPE_BF16) return fail(MLA_ERR_DTYPE, "unknown dtype %d", dtype);
+  const int64_t dims[] = {n_tokens, n_heads, kv_lora_rank, qk_nope_head_dim, v_head_dim};
+  const char *dnames[] = {"n_tokens", "n_heads", "kv_lora_rank", "qk_nope_head_dim", "v_head_dim"};
+  for (int i = 0; i < 5; ++i)
+    if (dims[i] <= 0 || dims[i] > (int64_t(1) << 31))
+      return fail(MLA_ERR_SHAPE, "%s = %lld is out of range", dnames[i], (long long)dims[i]);
+  const int64_t ealign = 16 / int64_t(elem_size(dtype));
+  if (kv_lora_rank % ealign || qk_nope_head_dim % ealign || v_head_dim % ealign)
+    return fail(MLA_ERR_ALIGN, "kv_lora_rank, qk_nope_head_dim and v_head_dim must be multiples of %lld "
+                               "elements (16-byte rows)", (long long)ealign);
+  if (n_heads * (qk_nope_head_dim + v_head_dim) > (int64_t(1) << 31))
+    return fail(MLA_ERR_SHAPE, "n_heads * (qk_nope_head_dim + v_head_dim) is too large");
+  if (!(eps >= 0.f) || eps > 1e30f) return fail(MLA_ERR_SHAPE, "eps must be finite and >= 0");
+  if (path != MLA_PATH_AUTO && path != MLA_PATH_PLAIN && path != MLA_PATH_MFMA)
+    return fail(MLA_ERR_UNSUPPORTED, "unknown path %d", path);
+  const void *ptrs[] = {c_kv, rms_w, wkv_b, k_nope, v};
+  const char *names[] = {"c_kv", "rms_w", "wkv_b", "k_nope", "v"};
+  for (int i = 0; i < 5; ++i) {
+    if (!ptrs[i]) return fail(MLA_ERR_NULL, "%s is NULL", names[i]);
+    if (misaligned(ptrs[i])) return fail(MLA_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
+  }
+  const size_t es = elem_size(dtype);
+  const size_t sizes[] = {size_t(n_tokens * kv_lora_rank) * es, size_t(kv_lora_rank) * es,
+                          size_t(n_heads * (qk_nope_head_dim + v_head_dim) * kv_lora_rank) * es,
+                          size_t(n_heads * n_tokens * qk_nope_head_dim) * es,
+                          size_t(n_heads * n_tokens * v_head_dim) * es};
+  for (int o = 3; o < 5; ++o)
+    for (int i = 0; i < 5; ++i)
+      if (i != o && overlaps(ptrs[o], sizes[o], ptrs[i], sizes[i]))
+        return fail(MLA_ERR_SHAPE, "%s overlaps %s", names[o], names[i]);
+  mla::ExpandCall e{};
+  e.T = n_tokens; e.H = n_heads; e.C = kv_lora_rank; e.Dn = qk_nope_head_dim; e.Dv = v_head_dim;
+  e.eps = eps; e.dtype = dtype; e.c_kv = c_kv; e.rms_w = rms_w; e.wkv_b = wkv_b; e.k_nope = k_nope; e.v = v;
+  e.stream = static_cast<hipStream_t>(stream);
+  bool use_mfma = false;
+  if (path != MLA_PATH_PLAIN) {
+    const char *why = "";
+    const bool ok = mla::mfma_expand_supported(e, &why);
+    if (path == MLA_PATH_MFMA && !ok) return fail(MLA_ERR_UNSUPPORTED, "matrix-core path: %s", why);
+    use_mfma = ok;
+  }
+  hipError_t err = use_mfma ? mla::mfma_expand_kv(e) : mla::plain_expand_kv(e);
+  if (err != hipSuccess) return fail(MLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+  return MLA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,210 @@
+// Plain vector-ALU kernels: any shape, fp32 or bf16 storage, fp32 arithmetic.
+//
+// They compute the same absorb-form attention and latent expansion as the matrix-core kernels
+// (page "Naive vs Absorb Attention Implementations in DeepSeek-V3", section "Absorb Path
+// Execution"; kernelindex op 064 "Latent KV expansion with split"), one output element per
+// thread with no tiling, and serve the fp32 workloads and shapes the matrix-core kernels do not
+// take.
+#include "common.h"
+#include "launch.h"
+#include "../../include/mla_absorb.h"
+
+namespace mla {
+namespace {
+
+constexpr int kThreads = 256;
+
+// q_lat[row, c] = sum_d q_nope[row, d] * W_UK[h, d, c]   (h = row % H)
+template <typename T>
+__global__ void __launch_bounds__(kThreads)
+plain_absorb_q_kernel(const T *__restrict__ q_nope, const T *__restrict__ wkv_b,
+                      float *__restrict__ q_lat, int64_t H, int64_t C, int64_t Dn, int64_t Dv) {
+  const int64_t row = blockIdx.x;
+  const int64_t c = int64_t(blockIdx.y) * kThreads + threadIdx.x;
+  if (c >= C) return;
+  const int64_t h = row % H;
+  const T *q = q_nope + row * Dn;
+  const T *w = wkv_b + h * (Dn + Dv) * C + c;
+  float acc = 0.f;
+  for (int64_t d = 0; d < Dn; ++d) acc = fmaf(Elem<T>::load(q, d), Elem<T>::load(w, d * C), acc);
+  q_lat[row * C + c] = acc;
+}
+
+// One block per (row, split): online softmax over the split's visible positions.
+// Writes m (largest scaled score, -inf if none visible), l (sum of exp(score - m)) and
+// o[c] = sum exp(score - m) * kv[t, c].
+template <typename T>
+__global__ void __launch_bounds__(kThreads)
+plain_attn_partial_kernel(const float *__restrict__ q_lat, const T *__restrict__ q_pe,
+                          const T *__restrict__ kv, const T *__restrict__ pe,
+                          float *__restrict__ part_ml, float *__restrict__ part_o, AttnCall a) {
+  extern __shared__ float sm[];
+  float *sq = sm;             // C   absorbed query
+  float *sqp = sq + a.C;      // R   rope query
+  float *so = sqp + a.R;      // C   running weighted sum
+  float *sp = so + a.C;       // kThreads probabilities of the current chunk
+  float *red = sp + kThreads; // 16
+
+  const int64_t row = blockIdx.x;
+  const int split = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int64_t b = row / (a.S * a.H);
+  const int64_t s = (row / a.H) % a.S;
+  const int64_t last = a.end_pos - a.S + s;  // last visible position of this query
+  const int64_t t0 = int64_t(split) * a.split_len;
+  int64_t t1 = t0 + a.split_len;
+  if (t1 > a.end_pos) t1 = a.end_pos;
+  if (t1 > last + 1) t1 = last + 1;
+
+  for (int64_t c = tid; c < a.C; c += kThreads) { sq[c] = q_lat[row * a.C + c]; so[c] = 0.f; }
+  for (int64_t r = tid; r < a.R; r += kThreads) sqp[r] = Elem<T>::load(q_pe, row * a.R + r);
+  __syncthreads();
+
+  const T *kvb = kv + b * a.Tmax * a.C;
+  const T *peb = pe + b * a.Tmax * a.R;
+  float m = -INFINITY, l = 0.f;
+  for (int64_t tc = t0; tc < t1; tc += kThreads) {
+    const int n = int((t1 - tc) < kThreads ? (t1 - tc) : kThreads);
+    float sc = -INFINITY;
+    if (tid < n) {
+      const int64_t t = tc + tid;
+      float acc = 0.f;
+      for (int64_t c = 0; c < a.C; ++c) acc = fmaf(sq[c], Elem<T>::load(kvb, t * a.C + c), acc);
+      for (int64_t r = 0; r < a.R; ++r) acc = fmaf(sqp[r], Elem<T>::load(peb, t * a.R + r), acc);
+      sc = acc * a.scale;
+    }
+    const float m_new = fmaxf(m, block_max(sc, red));
+    const float p = (tid < n) ? expf(sc - m_new) : 0.f;
+    sp[tid] = p;
+    const float alpha = (m == -INFINITY) ? 0.f : expf(m - m_new);
+    l = l * alpha + block_sum(p, red);  // block_sum synchronises, so sp is visible below
+    for (int64_t c = tid; c < a.C; c += kThreads) {
+      float acc = so[c] * alpha;
+      for (int j = 0; j < n; ++j) acc = fmaf(sp[j], Elem<T>::load(kvb, (tc + j) * a.C + c), acc);
+      so[c] = acc;
+    }
+    m = m_new;
+    __syncthreads();
+  }
+  const int64_t idx = row * a.splits + split;
+  if (tid == 0) { part_ml[2 * idx] = m; part_ml[2 * idx + 1] = l; }
+  for (int64_t c = tid; c < a.C; c += kThreads) part_o[idx * a.C + c] = so[c];
+}
+
+// One block per row: merge the split partials into o_lat, then out = W_UV[h] o_lat.
+template <typename T>
+__global__ void __launch_bounds__(kThreads)
+plain_merge_upproj_kernel(const float *__restrict__ part_ml, const float *__restrict__ part_o,
+                          const T *__restrict__ wkv_b, T *__restrict__ out, AttnCall a) {
+  extern __shared__ float sm[];
+  float *so = sm;  // C
+  const int64_t row = blockIdx.x;
+  const int64_t h = row % a.H;
+  const int tid = threadIdx.x;
+  const float *ml = part_ml + 2 * row * a.splits;
+  float M = -INFINITY;
+  for (int i = 0; i < a.splits; ++i) M = fmaxf(M, ml[2 * i]);
+  float den = 0.f;
+  for (int i = 0; i < a.splits; ++i)
+    if (ml[2 * i] != -INFINITY) den += expf(ml[2 * i] - M) * ml[2 * i + 1];
+  const float inv = 1.f / den;
+  for (int64_t c = tid; c < a.C; c += kThreads) {
+    float acc = 0.f;
+    for (int i = 0; i < a.splits; ++i)
+      if (ml[2 * i] != -INFINITY) acc = fmaf(expf(ml[2 * i] - M), part_o[(row * a.splits + i) * a.C + c], acc);
+    so[c] = acc * inv;
+  }
+  __syncthreads();
+  const T *wuv = wkv_b + (h * (a.Dn + a.Dv) + a.Dn) * a.C;
+  for (int64_t e = tid; e < a.Dv; e += kThreads) {
+    float acc = 0.f;
+    for (int64_t c = 0; c < a.C; ++c) acc = fmaf(so[c], Elem<T>::load(wuv, e * a.C + c), acc);
+    Elem<T>::store(static_cast<T *>(a.out), row * a.Dv + e, acc);
+  }
+}
+
+// One block per (token, 256 output features): RMSNorm of the token's latent, then the
+// projection; feature j of head h = j / (Dn+Dv) goes to k_nope or v by its offset in the head.
+template <typename T>
+__global__ void __launch_bounds__(kThreads)
+plain_expand_kernel(const T *__restrict__ c_kv, const T *__restrict__ rms_w, const T *__restrict__ wkv_b,
+                    T *__restrict__ k_nope, T *__restrict__ v, ExpandCall e) {
+  extern __shared__ float sm[];
+  float *sn = sm;           // C
+  float *red = sn + e.C;    // 16
+  const int64_t t = blockIdx.x;
+  const int tid = threadIdx.x;
+  float ss = 0.f;
+  for (int64_t c = tid; c < e.C; c += kThreads) {
+    const float x = Elem<T>::load(c_kv, t * e.C + c);
+    sn[c] = x;
+    ss = fmaf(x, x, ss);
+  }
+  ss = block_sum(ss, red);
+  const float inv = 1.f / sqrtf(ss / float(e.C) + e.eps);
+  for (int64_t c = tid; c < e.C; c += kThreads) sn[c] = sn[c] * inv * Elem<T>::load(rms_w, c);
+  __syncthreads();
+  const int64_t per_head = e.Dn + e.Dv;
+  const int64_t j = int64_t(blockIdx.y) * kThreads + tid;
+  if (j >= e.H * per_head) return;
+  float acc = 0.f;
+  for (int64_t c = 0; c < e.C; ++c) acc = fmaf(sn[c], Elem<T>::load(wkv_b, j * e.C + c), acc);
+  const int64_t h = j / per_head, jj = j % per_head;
+  if (jj < e.Dn) Elem<T>::store(k_nope, (h * e.T + t) * e.Dn + jj, acc);
+  else Elem<T>::store(v, (h * e.T + t) * e.Dv + (jj - e.Dn), acc);
+}
+
+template <typename T>
+hipError_t run_attn(const AttnCall &a) {
+  const int64_t rows = a.B * a.S * a.H;
+  float *q_lat = static_cast<float *>(a.ws);
+  float *part_ml = q_lat + rows * a.C;
+  float *part_o = part_ml + 2 * rows * a.splits;
+  const T *q_nope = static_cast<const T *>(a.q_nope);
+  plain_absorb_q_kernel<T><<<dim3(unsigned(rows), unsigned((a.C + kThreads - 1) / kThreads)), kThreads, 0,
+                             a.stream>>>(q_nope, static_cast<const T *>(a.wkv_b), q_lat, a.H, a.C, a.Dn, a.Dv);
+  const size_t sm_attn = sizeof(float) * size_t(2 * a.C + a.R + kThreads + 16);
+  plain_attn_partial_kernel<T><<<dim3(unsigned(rows), unsigned(a.splits)), kThreads, sm_attn, a.stream>>>(
+      q_lat, static_cast<const T *>(a.q_pe), static_cast<const T *>(a.kv), static_cast<const T *>(a.pe),
+      part_ml, part_o, a);
+  plain_merge_upproj_kernel<T><<<dim3(unsigned(rows)), kThreads, sizeof(float) * size_t(a.C), a.stream>>>(
+      part_ml, part_o, static_cast<const T *>(a.wkv_b), static_cast<T *>(a.out), a);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t run_expand(const ExpandCall &e) {
+  const int64_t feats = e.H * (e.Dn + e.Dv);
+  plain_expand_kernel<T><<<dim3(unsigned(e.T), unsigned((feats + kThreads - 1) / kThreads)), kThreads,
+                           sizeof(float) * size_t(e.C + 16), e.stream>>>(
+      static_cast<const T *>(e.c_kv), static_cast<const T *>(e.rms_w), static_cast<const T *>(e.wkv_b),
+      static_cast<T *>(e.k_nope), static_cast<T *>(e.v), e);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int32_t plain_attn_splits(const AttnCall &c) {
+  // Enough blocks to spread over the chip, but never fewer than 256 positions per split.
+  const int64_t rows = c.B * c.S * c.H;
+  int64_t splits = (2048 + rows - 1) / rows;
+  const int64_t max_by_len = (c.end_pos + 255) / 256;
+  if (splits > max_by_len) splits = max_by_len;
+  if (splits < 1) splits = 1;
+  return int32_t(splits);
+}
+
+size_t plain_attn_workspace(const AttnCall &c) {
+  const size_t rows = size_t(c.B * c.S * c.H);
+  return sizeof(float) * (rows * size_t(c.C) + rows * size_t(c.splits) * (2 + size_t(c.C)));
+}
+
+hipError_t plain_absorb_attn(const AttnCall &c) {
+  return c.dtype == MLA_DTYPE_F32 ? run_attn<float>(c) : run_attn<uint16_t>(c);
+}
+
+hipError_t plain_expand_kv(const ExpandCall &e) {
+  return e.dtype == MLA_DTYPE_F32 ? run_expand<float>(e) : run_expand<uint16_t>(e);
+}
+
+}  // namespace mla

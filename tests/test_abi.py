@@ -1,0 +1,149 @@
+"""C-ABI checks that need no GPU: the library loads, exports what include/mla_absorb.h declares,
+and rejects bad arguments before any HIP call (so these calls never touch a device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mla_latent_kv_absorb_amd import binding as B
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "mla_absorb.h")
+
+# Fake, 16-byte-aligned device addresses.  Every call below fails validation before any kernel
+# could be enqueued, so they are never dereferenced.
+P = [0x7f0000000000 + i * 0x100000000 for i in range(8)]
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        import __graft_entry__
+
+        __graft_entry__.build()
+    return B.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:char\s*\*|size_t|int32_t)\s*\**\s*(mla_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_binding_names():
+    assert declared_functions() == sorted(B.EXPORTED)
+
+
+def test_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_strerror_covers_codes(lib):
+    for code in range(0, -9, -1):
+        assert B.strerror(code) and B.strerror(code) != "unknown status"
+    assert B.strerror(-99) == "unknown status"
+
+
+def shape(**kw):
+    d = dict(batch=2, seqlen_q=1, n_heads=128, kv_lora_rank=512, qk_rope_head_dim=64, qk_nope_head_dim=128,
+             v_head_dim=128, cache_batch=2, cache_len=4096)
+    d.update(kw)
+    return B.AttnShape(*[d[f] for f, _ in B.AttnShape._fields_])
+
+
+def call_attn(lib, s, end_pos=4096, dtype=B.MLA_DTYPE_BF16, ptrs=None, ws=P[7], ws_bytes=1 << 40, scale=0.07,
+              opt=None):
+    p = list(P[:6]) if ptrs is None else ptrs
+    o = ctypes.byref(opt) if opt is not None else None
+    return lib.mla_absorb_attn(p[0], p[1], p[2], p[3], p[4], end_pos, scale, p[5], ctypes.byref(s), dtype, o, ws,
+                               ws_bytes, None)
+
+
+def test_workspace_size_query(lib):
+    n = B.absorb_attn_workspace_size(shape(), 4096, B.MLA_DTYPE_BF16)
+    assert n > 0
+    n32 = B.absorb_attn_workspace_size(shape(n_heads=4, kv_lora_rank=64, qk_rope_head_dim=16, qk_nope_head_dim=32,
+                                             v_head_dim=32, batch=1, cache_batch=1, cache_len=128), 128,
+                                       B.MLA_DTYPE_F32)
+    assert n32 > 0
+    bad = lib.mla_absorb_attn_workspace_size(ctypes.byref(shape(batch=3)), 4096, B.MLA_DTYPE_BF16, None)
+    assert bad == 0 and "batch" in B.last_error()
+
+
+@pytest.mark.parametrize("kw,end_pos,code,needle", [
+    (dict(batch=3), 4096, B.MLA_ERR_RANGE, "batch"),
+    ({}, 4097, B.MLA_ERR_RANGE, "end_pos"),
+    ({}, 0, B.MLA_ERR_RANGE, "end_pos"),
+    (dict(seqlen_q=5), 4, B.MLA_ERR_RANGE, "seqlen_q"),
+    (dict(n_heads=0), 4096, B.MLA_ERR_SHAPE, "n_heads"),
+    (dict(kv_lora_rank=-1), 4096, B.MLA_ERR_SHAPE, "kv_lora_rank"),
+    (dict(kv_lora_rank=500), 4096, B.MLA_ERR_ALIGN, "multiples"),
+])
+def test_attn_shape_errors(lib, kw, end_pos, code, needle):
+    assert call_attn(lib, shape(**kw), end_pos=end_pos) == code
+    assert needle in B.last_error()
+
+
+def test_attn_pointer_errors(lib):
+    s = shape()
+    for i in range(6):
+        p = list(P[:6])
+        p[i] = None
+        assert call_attn(lib, s, ptrs=p) == B.MLA_ERR_NULL
+        p[i] = P[i] + 2
+        assert call_attn(lib, s, ptrs=p) == B.MLA_ERR_ALIGN
+    assert lib.mla_absorb_attn(*P[:5], 4096, 0.07, P[5], None, B.MLA_DTYPE_BF16, None, P[7], 1 << 40,
+                               None) == B.MLA_ERR_NULL
+
+
+def test_attn_dtype_scale_and_options(lib):
+    s = shape()
+    assert call_attn(lib, s, dtype=7) == B.MLA_ERR_DTYPE
+    assert call_attn(lib, s, scale=0.0) == B.MLA_ERR_SHAPE
+    assert call_attn(lib, s, scale=float("nan")) == B.MLA_ERR_SHAPE
+    assert call_attn(lib, s, opt=B.AttnOptions(-1, 0)) == B.MLA_ERR_SHAPE
+    assert call_attn(lib, s, opt=B.AttnOptions(0, 9)) == B.MLA_ERR_UNSUPPORTED
+    fp32 = shape(n_heads=4, kv_lora_rank=64, qk_rope_head_dim=16, qk_nope_head_dim=32, v_head_dim=32)
+    assert call_attn(lib, fp32, dtype=B.MLA_DTYPE_F32, end_pos=128,
+                     opt=B.AttnOptions(0, B.PATHS["mfma"])) == B.MLA_ERR_UNSUPPORTED
+
+
+def test_attn_workspace_errors(lib):
+    s = shape()
+    need = B.absorb_attn_workspace_size(s, 4096, B.MLA_DTYPE_BF16)
+    assert call_attn(lib, s, ws=None) == B.MLA_ERR_WORKSPACE
+    assert call_attn(lib, s, ws_bytes=need - 1) == B.MLA_ERR_WORKSPACE
+    assert call_attn(lib, s, ws=P[7] + 8) == B.MLA_ERR_ALIGN
+    # workspace on top of kv_cache
+    assert call_attn(lib, s, ws=P[2] + 4096) == B.MLA_ERR_WORKSPACE
+
+
+def test_attn_out_alias(lib):
+    p = list(P[:6])
+    p[5] = P[2] + 1024  # out inside kv_cache
+    assert call_attn(lib, shape(), ptrs=p) == B.MLA_ERR_SHAPE
+    assert "overlaps" in B.last_error()
+
+
+def call_expand(lib, T=64, H=128, C=512, Dn=128, Dv=128, eps=1e-6, dtype=B.MLA_DTYPE_BF16, ptrs=None, path=0):
+    p = list(P[:5]) if ptrs is None else ptrs
+    return lib.mla_expand_kv(p[0], p[1], p[2], p[3], p[4], T, H, C, Dn, Dv, eps, dtype, path, None)
+
+
+def test_expand_errors(lib):
+    assert call_expand(lib, T=0) == B.MLA_ERR_SHAPE
+    assert call_expand(lib, C=511) == B.MLA_ERR_ALIGN
+    assert call_expand(lib, dtype=3) == B.MLA_ERR_DTYPE
+    assert call_expand(lib, eps=-1.0) == B.MLA_ERR_SHAPE
+    assert call_expand(lib, path=5) == B.MLA_ERR_UNSUPPORTED
+    for i in range(5):
+        p = list(P[:5])
+        p[i] = None
+        assert call_expand(lib, ptrs=p) == B.MLA_ERR_NULL
+        p[i] = P[i] + 4
+        assert call_expand(lib, ptrs=p) == B.MLA_ERR_ALIGN
+    p = list(P[:5])
+    p[4] = P[3] + 64  # v inside k_nope
+    assert call_expand(lib, ptrs=p) == B.MLA_ERR_SHAPE
+    assert call_expand(lib, dtype=B.MLA_DTYPE_F32, C=64, H=4, Dn=32, Dv=32, path=B.PATHS["mfma"]) == \
+        B.MLA_ERR_UNSUPPORTED

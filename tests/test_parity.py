@@ -1,0 +1,136 @@
+"""GPU parity: the HIP path (through the C-ABI) against the CPU oracle on the same seeded inputs.
+
+Bar: max|gpu - ref| <= 1e-5 * max|ref| for fp32 workloads and <= 2e-2 * max|ref| for bf16
+workloads, no NaN/Inf anywhere; outputs are NaN-poisoned before each call so an element the
+kernels never write fails the check.
+"""
+import numpy as np
+import pytest
+import torch
+
+from mla_latent_kv_absorb_amd.workloads import (ATTN_CONFIGS, EXPAND_CONFIGS, make_attn_inputs,
+                                                 make_expand_inputs)
+from oracle import mla_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+
+
+def tdtype(cfg):
+    return torch.float32 if cfg.dtype == "f32" else torch.bfloat16
+
+
+def to_dev(x, cfg):
+    return {k: torch.from_numpy(v).to("cuda").to(tdtype(cfg)) for k, v in x.items()}
+
+
+def check(gpu, ref, tol, what):
+    g = gpu.float().cpu().double().numpy() if isinstance(gpu, torch.Tensor) else gpu
+    assert np.isfinite(g).all(), f"{what}: {int((~np.isfinite(g)).sum())} non-finite outputs"
+    err = np.abs(g - ref)
+    scale = np.abs(ref).max()
+    worst = float(err.max() / scale)
+    loc = np.unravel_index(int(err.argmax()), err.shape)
+    print(f"{what}: max rel err {worst:.3e} at {loc}, mean abs err {err.mean():.3e}, max|ref| {scale:.3e}")
+    assert worst <= tol, f"{what}: max abs err {err.max():.3e} = {worst:.3e} * max|ref| at {loc} > {tol}"
+
+
+def run_attn(lib, cfg, t, path="auto", splits=0):
+    out = torch.full((cfg.batch, cfg.seqlen_q, cfg.n_heads, cfg.v_head_dim), float("nan"), dtype=tdtype(cfg),
+                     device="cuda")
+    lib.absorb_attn(t["q_nope"], t["q_pe"], t["kv_cache"], t["pe_cache"], t["wkv_b"], cfg.end_pos, cfg.softmax_scale,
+                    out, num_splits=splits, path=path)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_attn(cfg, x):
+    return O.absorb_attention(x["q_nope"], x["q_pe"], x["kv_cache"], x["pe_cache"], x["wkv_b"], cfg.end_pos,
+                              cfg.softmax_scale, cfg.v_head_dim)
+
+
+def dsv3_small(**kw):
+    base = dict(batch=2, cache_batch=3, end_pos=300, cache_len=320)
+    base.update(kw)
+    return ATTN_CONFIGS["dsv3_decode"].replace(**base)
+
+
+# --------------------------------------------------------------------------------- tiny fp32
+
+@pytest.mark.parametrize("path", ["plain", "auto"])
+def test_tiny_f32_absorb_and_naive(gpu_lib, path):
+    cfg = ATTN_CONFIGS["tiny_f32"]
+    x = make_attn_inputs(cfg)
+    out = run_attn(gpu_lib, cfg, to_dev(x, cfg), path=path)
+    check(out, oracle_attn(cfg, x), TOL["f32"], f"tiny_f32 {path} vs absorb oracle")
+    naive = O.naive_attention(x["q_nope"], x["q_pe"], x["kv_cache"], x["pe_cache"], x["wkv_b"], cfg.end_pos,
+                              cfg.softmax_scale, cfg.v_head_dim)
+    check(out, naive, TOL["f32"], f"tiny_f32 {path} vs naive oracle")
+
+
+@pytest.mark.parametrize("splits", [1, 3, 128])
+def test_tiny_f32_splits(gpu_lib, splits):
+    cfg = ATTN_CONFIGS["tiny_f32"]
+    x = make_attn_inputs(cfg)
+    out = run_attn(gpu_lib, cfg, to_dev(x, cfg), path="plain", splits=splits)
+    check(out, oracle_attn(cfg, x), TOL["f32"], f"tiny_f32 splits={splits}")
+
+
+def test_tiny_f32_chunk(gpu_lib):
+    cfg = ATTN_CONFIGS["tiny_f32"].replace(seqlen_q=9, end_pos=100)
+    x = make_attn_inputs(cfg)
+    out = run_attn(gpu_lib, cfg, to_dev(x, cfg))
+    check(out, oracle_attn(cfg, x), TOL["f32"], "tiny_f32 causal chunk S=9")
+
+
+@pytest.mark.parametrize("path", ["plain", "auto"])
+def test_tiny_f32_expand(gpu_lib, path):
+    cfg = EXPAND_CONFIGS["tiny_f32"]
+    x = make_expand_inputs(cfg)
+    t = to_dev(x, cfg)
+    k = torch.full((cfg.n_heads, cfg.n_tokens, cfg.qk_nope_head_dim), float("nan"), device="cuda")
+    v = torch.full((cfg.n_heads, cfg.n_tokens, cfg.v_head_dim), float("nan"), device="cuda")
+    gpu_lib.expand_kv(t["c_kv"], t["rms_w"], t["wkv_b"], cfg.n_heads, cfg.qk_nope_head_dim, cfg.v_head_dim, cfg.eps,
+                      k, v, path=path)
+    torch.cuda.synchronize()
+    kr, vr = O.expand_kv(x["c_kv"], x["rms_w"], x["wkv_b"], cfg.n_heads, cfg.qk_nope_head_dim, cfg.v_head_dim,
+                         cfg.eps)
+    check(k, kr, TOL["f32"], "tiny_f32 expand K_nope")
+    check(v, vr, TOL["f32"], "tiny_f32 expand V")
+
+
+# --------------------------------------------------------------------------------- bf16, DSV3 heads, small
+
+@pytest.mark.parametrize("path", ["plain", "auto"])
+@pytest.mark.parametrize("end_pos", [1, 37, 300])
+def test_bf16_decode_small(gpu_lib, path, end_pos):
+    cfg = dsv3_small(end_pos=end_pos)
+    x = make_attn_inputs(cfg)
+    out = run_attn(gpu_lib, cfg, to_dev(x, cfg), path=path)
+    check(out, oracle_attn(cfg, x), TOL["bf16"], f"bf16 decode B=2 T={end_pos} {path}")
+
+
+@pytest.mark.parametrize("path", ["plain", "auto"])
+def test_bf16_chunk_small(gpu_lib, path):
+    cfg = dsv3_small(seqlen_q=5, end_pos=200, batch=1, cache_batch=1)
+    x = make_attn_inputs(cfg)
+    out = run_attn(gpu_lib, cfg, to_dev(x, cfg), path=path)
+    check(out, oracle_attn(cfg, x), TOL["bf16"], f"bf16 chunk S=5 T=200 {path}")
+
+
+@pytest.mark.parametrize("path", ["plain", "auto"])
+def test_bf16_expand_small(gpu_lib, path):
+    cfg = EXPAND_CONFIGS["dsv3_expand"].replace(n_tokens=200)
+    x = make_expand_inputs(cfg)
+    t = to_dev(x, cfg)
+    k = torch.full((cfg.n_heads, cfg.n_tokens, cfg.qk_nope_head_dim), float("nan"), dtype=torch.bfloat16,
+                   device="cuda")
+    v = torch.full_like(k, float("nan"))
+    gpu_lib.expand_kv(t["c_kv"], t["rms_w"], t["wkv_b"], cfg.n_heads, cfg.qk_nope_head_dim, cfg.v_head_dim, cfg.eps,
+                      k, v, path=path)
+    torch.cuda.synchronize()
+    kr, vr = O.expand_kv(x["c_kv"], x["rms_w"], x["wkv_b"], cfg.n_heads, cfg.qk_nope_head_dim, cfg.v_head_dim,
+                         cfg.eps)
+    check(k, kr, TOL["bf16"], f"bf16 expand T=200 K_nope {path}")
+    check(v, vr, TOL["bf16"], f"bf16 expand T=200 V {path}")
