@@ -10,17 +10,14 @@ namespace mla {
 // bf16 is carried as its 16-bit pattern.  Widening is exact (shift into the high half).
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
 
-// Round-to-nearest-even narrowing (inputs here are finite; NaN is kept a NaN).
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
-}
+// Round-to-nearest-even narrowing; gfx950 does it in hardware (v_cvt_pk_bf16_f32).
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 // Two floats -> packed pair of bf16 (low half = a).
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return uint32_t(f32_to_bf16(a)) | (uint32_t(f32_to_bf16(b)) << 16);
+  const bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // Element access for the two storage types used by the plain kernels.

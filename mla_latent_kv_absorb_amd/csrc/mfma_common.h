@@ -1,0 +1,100 @@
+// Matrix-core (MFMA) building blocks for gfx950.
+//
+// v_mfma_f32_32x32x16_bf16 computes D[32x32] += A[32x16] * B[16x32] per wavefront:
+//   A operand: lane l holds A[l % 32][8 * (l / 32) + j], j = 0..7   (8 bf16 = 16 bytes)
+//   B operand: lane l holds B[8 * (l / 32) + j][l % 32]
+//   D:         lane l, register r holds D[8 * (r / 4) + 4 * (l / 32) + r % 4][l % 32]
+// Any consistent assignment of the 16 contraction indices to (l / 32, j) gives the same
+// result, so A and B only have to agree with each other.
+//
+// ds_read_b64_tr_b16 (gfx950 transposing LDS read): within each group of 16 lanes, source lane s
+// reads 4 consecutive 16-bit elements at its own address, and destination lane i receives in slot
+// j the element i % 4 of source lane 4 * j + i / 4.  If source lane s points at row
+// (r0 + s / 4), column (c0 + 4 * (s % 4)) of a row-major tile, destination lane i receives column
+// c0 + i of rows r0 .. r0 + 3: a 4x16 block read out transposed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+
+#define MLA_LDS __attribute__((address_space(3)))
+
+__device__ __forceinline__ f32x16 mfma32(const u32x4 &a, const u32x4 &b, const f32x16 &c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
+}
+
+__device__ __forceinline__ u32x4 lds_read16(const unsigned char *base, uint32_t byte_off) {
+  return *(const MLA_LDS u32x4 *)(base + byte_off);
+}
+
+__device__ __forceinline__ void lds_write16(unsigned char *base, uint32_t byte_off, const u32x4 &v) {
+  *(MLA_LDS u32x4 *)(base + byte_off) = v;
+}
+
+__device__ __forceinline__ void lds_write8(unsigned char *base, uint32_t byte_off, const u32x2 &v) {
+  *(MLA_LDS u32x2 *)(base + byte_off) = v;
+}
+
+// Two transposing reads (rows r0..r0+3 then r0+4..r0+7) packed into one 8-element operand.
+__device__ __forceinline__ u32x4 lds_read_tr_pair(const unsigned char *base, uint32_t off0, uint32_t off1) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS s16x4 *)(base + off0));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS s16x4 *)(base + off1));
+  const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+  return u32x4{l2[0], l2[1], h2[0], h2[1]};
+}
+
+// ---- buffer resources: 128-bit descriptor in SGPRs + 32-bit per-lane byte offset ---------------
+// Reads past `bytes` return zero and writes past it are dropped (raw buffer, stride 0).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, int(bytes), 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+__device__ __forceinline__ void buf_store16(rsrc_t r, const u32x4 &v, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, soff, 0);
+}
+__device__ __forceinline__ void buf_store8(rsrc_t r, const u32x2 &v, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, voff, soff, 0);
+}
+// 16 bytes per lane from a buffer straight into LDS: lane l's bytes land at lds_base + 16 * l
+// (lds_base is wavefront-uniform and goes through M0).
+__device__ __forceinline__ void buf_load16_lds(rsrc_t r, unsigned char *lds_base, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (MLA_LDS void *)(lds_base), 16, voff, soff, 0, 0);
+}
+
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Accumulator access.  MFMA results live in AGPRs; reading them through an explicit
+// v_accvgpr_read pins each move to its use, so the compiler does not copy a whole accumulator
+// array into VGPRs at once (which forces spills of everything else that is live).  Both helpers
+// are plain register moves.
+__device__ __forceinline__ float agpr_read(float x) {
+  float r;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(r) : "a"(x));
+  return r;
+}
+__device__ __forceinline__ float agpr_write(float x) {
+  float r;
+  asm volatile("v_accvgpr_write_b32 %0, %1" : "=a"(r) : "v"(x));
+  return r;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace mla

@@ -102,7 +102,7 @@ def test_tiny_f32_expand(gpu_lib, path):
 
 # --------------------------------------------------------------------------------- bf16, DSV3 heads, small
 
-@pytest.mark.parametrize("path", ["plain", "auto"])
+@pytest.mark.parametrize("path", ["plain", "mfma"])
 @pytest.mark.parametrize("end_pos", [1, 37, 300])
 def test_bf16_decode_small(gpu_lib, path, end_pos):
     cfg = dsv3_small(end_pos=end_pos)
@@ -111,7 +111,7 @@ def test_bf16_decode_small(gpu_lib, path, end_pos):
     check(out, oracle_attn(cfg, x), TOL["bf16"], f"bf16 decode B=2 T={end_pos} {path}")
 
 
-@pytest.mark.parametrize("path", ["plain", "auto"])
+@pytest.mark.parametrize("path", ["plain", "mfma"])
 def test_bf16_chunk_small(gpu_lib, path):
     cfg = dsv3_small(seqlen_q=5, end_pos=200, batch=1, cache_batch=1)
     x = make_attn_inputs(cfg)
@@ -119,7 +119,7 @@ def test_bf16_chunk_small(gpu_lib, path):
     check(out, oracle_attn(cfg, x), TOL["bf16"], f"bf16 chunk S=5 T=200 {path}")
 
 
-@pytest.mark.parametrize("path", ["plain", "auto"])
+@pytest.mark.parametrize("path", ["plain", "mfma"])
 def test_bf16_expand_small(gpu_lib, path):
     cfg = EXPAND_CONFIGS["dsv3_expand"].replace(n_tokens=200)
     x = make_expand_inputs(cfg)
@@ -134,3 +134,107 @@ def test_bf16_expand_small(gpu_lib, path):
                          cfg.eps)
     check(k, kr, TOL["bf16"], f"bf16 expand T=200 K_nope {path}")
     check(v, vr, TOL["bf16"], f"bf16 expand T=200 V {path}")
+
+
+# --------------------------------------------------------------------------------- matrix-core path
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 7, 64])
+def test_mfma_forced_splits(gpu_lib, splits):
+    cfg = dsv3_small(end_pos=1000, cache_len=1024)
+    x = make_attn_inputs(cfg)
+    out = run_attn(gpu_lib, cfg, to_dev(x, cfg), path="mfma", splits=splits)
+    check(out, oracle_attn(cfg, x), TOL["bf16"], f"mfma decode T=1000 splits={splits}")
+
+
+@pytest.mark.parametrize("kw", [
+    dict(n_heads=16, seqlen_q=3, end_pos=130),     # 48 query rows: one partial row block
+    dict(n_heads=128, seqlen_q=3, end_pos=97),     # 384 rows: three row blocks, causal
+    dict(n_heads=64, seqlen_q=64, end_pos=64),     # chunk covering the whole prefix
+    dict(n_heads=128, seqlen_q=1, end_pos=65),     # one position past a tile boundary
+])
+def test_mfma_shapes(gpu_lib, kw):
+    cfg = dsv3_small(batch=2, cache_batch=2, cache_len=max(160, kw["end_pos"]), **kw)
+    x = make_attn_inputs(cfg)
+    out = run_attn(gpu_lib, cfg, to_dev(x, cfg), path="mfma")
+    check(out, oracle_attn(cfg, x), TOL["bf16"], f"mfma {kw}")
+
+
+def test_mfma_repeatable_bitwise(gpu_lib):
+    cfg = dsv3_small(end_pos=777, cache_len=800)
+    x = make_attn_inputs(cfg)
+    t = to_dev(x, cfg)
+    a = run_attn(gpu_lib, cfg, t, path="mfma", splits=5)
+    b = run_attn(gpu_lib, cfg, t, path="mfma", splits=5)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_mfma_larger_than_tile_max_shift(gpu_lib):
+    """A row whose scores grow along the cache forces the running maximum to move by far more
+    than the lazy-rescale threshold several times inside one split."""
+    cfg = dsv3_small(batch=1, cache_batch=1, end_pos=512, cache_len=512)
+    x = make_attn_inputs(cfg)
+    ramp = np.linspace(0.0, 6.0, cfg.cache_len, dtype=np.float32)[None, :, None]
+    x["pe_cache"] = (x["pe_cache"] * 0.1 + ramp).astype(np.float32)
+    x["q_pe"] = np.abs(x["q_pe"]) * 2.0 + 1.0
+    from mla_latent_kv_absorb_amd.workloads import round_to_bf16
+    x = {k: round_to_bf16(v) for k, v in x.items()}
+    out = run_attn(gpu_lib, cfg, to_dev(x, cfg), path="mfma", splits=1)
+    check(out, oracle_attn(cfg, x), TOL["bf16"], "mfma growing scores")
+
+
+def sample_rows(cfg, n, seed):
+    rng = np.random.default_rng(seed)
+    rows = {(0, 0, 0), (cfg.batch - 1, cfg.seqlen_q - 1, cfg.n_heads - 1), (0, cfg.seqlen_q - 1, 0),
+            (cfg.batch - 1, 0, cfg.n_heads // 2)}
+    while len(rows) < n:
+        rows.add((int(rng.integers(cfg.batch)), int(rng.integers(cfg.seqlen_q)), int(rng.integers(cfg.n_heads))))
+    return sorted(rows)
+
+
+@pytest.mark.parametrize("name", ["dsv3_decode", "long_decode", "chunk_prefill"])
+def test_full_size_attention(gpu_lib, name):
+    cfg = ATTN_CONFIGS[name]
+    print(f"full-size {name}: B={cfg.batch} S={cfg.seqlen_q} T={cfg.end_pos}", flush=True)
+    x = make_attn_inputs(cfg)
+    out = run_attn(gpu_lib, cfg, to_dev(x, cfg))
+    assert torch.isfinite(out).all(), "non-finite outputs"
+    rows = sample_rows(cfg, 48, 7)
+    ref = O.absorb_attention_rows(x["q_nope"], x["q_pe"], x["kv_cache"], x["pe_cache"], x["wkv_b"], cfg.end_pos,
+                                  cfg.softmax_scale, cfg.v_head_dim, rows)
+    g = out.float().cpu().double().numpy()
+    got = np.stack([g[b, s, h] for b, s, h in rows])
+    check(got, ref, TOL["bf16"], f"{name} sampled rows")
+
+
+def test_full_size_expand(gpu_lib):
+    cfg = EXPAND_CONFIGS["dsv3_expand"]
+    x = make_expand_inputs(cfg)
+    t = to_dev(x, cfg)
+    k = torch.full((cfg.n_heads, cfg.n_tokens, cfg.qk_nope_head_dim), float("nan"), dtype=torch.bfloat16,
+                   device="cuda")
+    v = torch.full_like(k, float("nan"))
+    gpu_lib.expand_kv(t["c_kv"], t["rms_w"], t["wkv_b"], cfg.n_heads, cfg.qk_nope_head_dim, cfg.v_head_dim, cfg.eps,
+                      k, v)
+    torch.cuda.synchronize()
+    assert torch.isfinite(k).all() and torch.isfinite(v).all()
+    rng = np.random.default_rng(11)
+    toks = np.unique(np.concatenate([[0, 255, 256, cfg.n_tokens - 1], rng.integers(0, cfg.n_tokens, 60)]))
+    kr, vr = O.expand_kv(x["c_kv"][toks], x["rms_w"], x["wkv_b"], cfg.n_heads, cfg.qk_nope_head_dim,
+                         cfg.v_head_dim, cfg.eps)
+    idx = torch.from_numpy(toks).cuda()
+    check(k[:, idx], kr, TOL["bf16"], "dsv3_expand K_nope sampled tokens")
+    check(v[:, idx], vr, TOL["bf16"], "dsv3_expand V sampled tokens")
+
+
+@pytest.mark.parametrize("T", [1, 100, 257, 1000])
+def test_mfma_expand_ragged(gpu_lib, T):
+    cfg = EXPAND_CONFIGS["dsv3_expand"].replace(n_tokens=T, n_heads=4)
+    x = make_expand_inputs(cfg)
+    t = to_dev(x, cfg)
+    k, v = gpu_lib.expand_kv(t["c_kv"], t["rms_w"], t["wkv_b"], cfg.n_heads, cfg.qk_nope_head_dim, cfg.v_head_dim,
+                             cfg.eps, path="mfma")
+    torch.cuda.synchronize()
+    kr, vr = O.expand_kv(x["c_kv"], x["rms_w"], x["wkv_b"], cfg.n_heads, cfg.qk_nope_head_dim, cfg.v_head_dim,
+                         cfg.eps)
+    check(k, kr, TOL["bf16"], f"mfma expand T={T} K_nope")
+    check(v, vr, TOL["bf16"], f"mfma expand T={T} V")
