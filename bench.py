@@ -1,0 +1,278 @@
+"""Benchmark: MLA absorb decode on one MI355X, DeepSeek-V3 decode shape.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dsv3_decode]
+                    [--no-extras] [--no-cpu-baseline]
+
+A step is one absorb-attention decode call (query absorption through W_UK, split-KV attention
+over kv_cache + pe_cache, merge and W_UV projection) over one batch: 32 sequences x 4096 cached
+positions x 128 heads, bf16.  Inputs are seeded synthetic tensors drawn on the GPU with the
+workload's shapes and distributions (q, caches ~N(0,1); wkv_b ~N(0,1/512)).  To measure HBM rather
+than the 256 MB Infinity Cache, the timed steps rotate over several complete input sets (about
+750 MB in all), so each step's operands were last touched three steps earlier.
+
+Prints ONE JSON line.  `value` is microseconds per step (lower is better).  `roofline` reports
+the dominant kernel (the attention kernel) against HBM bandwidth: algorithmic bytes per launch
+(the kv and pe cache rows it must read plus the rope query) over its average duration, measured
+with HIP events recorded around that kernel on its stream during the timed steps.
+`cpu_baseline` times the CPU oracle (NumPy, float64) on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2516.6
+METRIC = "MLA absorb decode µs/step, HBM GB/s & MFMA TFLOP/s as % of roofline"
+
+
+def attn_work(cfg):
+    """Algorithmic bytes and FLOPs of one absorb-attention call (caches [:B, :end_pos], wkv_b, q, out)."""
+    B, S, H = cfg.batch, cfg.seqlen_q, cfg.n_heads
+    C, R, Dn, Dv, T = cfg.kv_lora_rank, cfg.qk_rope_head_dim, cfg.qk_nope_head_dim, cfg.v_head_dim, cfg.end_pos
+    e = 2  # bf16
+    cache = B * T * (C + R) * e
+    weights = H * (Dn + Dv) * C * e
+    q = B * S * H * (Dn + R) * e
+    out = B * S * H * Dv * e
+    start = T - S
+    pairs = sum(start + s + 1 for s in range(S))  # visible (query, position) pairs per (b, h)
+    flops = 2 * B * S * H * Dn * C + 2 * B * H * pairs * (C + R) + 2 * B * H * pairs * C + 2 * B * S * H * C * Dv
+    return {"bytes": cache + weights + q + out, "flops": flops, "cache_bytes": cache,
+            "attn_kernel_bytes": cache + B * S * H * R * e}
+
+
+def expand_work(cfg):
+    T, H, C, Dn, Dv = cfg.n_tokens, cfg.n_heads, cfg.kv_lora_rank, cfg.qk_nope_head_dim, cfg.v_head_dim
+    e = 2
+    return {"bytes": T * C * e + C * e + H * (Dn + Dv) * C * e + H * T * (Dn + Dv) * e,
+            "flops": 2 * T * C * H * (Dn + Dv)}
+
+
+def gpu_inputs(cfg, seed, torch):
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+
+    def draw(shape, std):
+        return (torch.randn(shape, generator=g, device="cuda", dtype=torch.float32) * std).to(torch.bfloat16)
+
+    B, S, H = cfg.batch, cfg.seqlen_q, cfg.n_heads
+    return {
+        "q_nope": draw((B, S, H, cfg.qk_nope_head_dim), 1.0),
+        "q_pe": draw((B, S, H, cfg.qk_rope_head_dim), 1.0),
+        "kv_cache": draw((cfg.cache_batch, cfg.cache_len, cfg.kv_lora_rank), 1.0),
+        "pe_cache": draw((cfg.cache_batch, cfg.cache_len, cfg.qk_rope_head_dim), 1.0),
+        "wkv_b": draw((H * (cfg.qk_nope_head_dim + cfg.v_head_dim), cfg.kv_lora_rank), math.sqrt(cfg.wkv_b_var)),
+    }
+
+
+def time_attn(cfg, steps, warmup, sets, torch, binding, seed=1, timed_kernels=0b010):
+    """Returns (us_per_step, wall_us_per_step, per-kernel timing dict)."""
+    inputs = [gpu_inputs(cfg, seed + 1000 * i, torch) for i in range(sets)]
+    out = torch.empty((cfg.batch, cfg.seqlen_q, cfg.n_heads, cfg.v_head_dim), dtype=torch.bfloat16, device="cuda")
+    shape = binding.attn_shape(inputs[0]["q_nope"], inputs[0]["q_pe"], inputs[0]["kv_cache"], inputs[0]["wkv_b"])
+    need = binding.absorb_attn_workspace_size(shape, cfg.end_pos, binding.MLA_DTYPE_BF16)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        x = inputs[i % sets]
+        binding.absorb_attn(x["q_nope"], x["q_pe"], x["kv_cache"], x["pe_cache"], x["wkv_b"], cfg.end_pos,
+                            cfg.softmax_scale, out, workspace=ws)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    binding.timing_enable(timed_kernels)
+    binding.timing_collect()  # drop anything recorded before the timed region
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(steps):
+        step(warmup + i)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e6 / steps
+    kt = binding.timing_collect()
+    binding.timing_enable(0)
+    del inputs
+    torch.cuda.empty_cache()
+    return e0.elapsed_time(e1) * 1000.0 / steps, wall, kt
+
+
+def time_expand(cfg, steps, warmup, torch, binding, seed=4):
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    x = torch.randn((cfg.n_tokens, cfg.kv_lora_rank), generator=g, device="cuda").to(torch.bfloat16)
+    w = (1.0 + math.sqrt(cfg.rms_w_var) * torch.randn((cfg.kv_lora_rank,), generator=g, device="cuda")).to(torch.bfloat16)
+    wk = (torch.randn((cfg.n_heads * (cfg.qk_nope_head_dim + cfg.v_head_dim), cfg.kv_lora_rank), generator=g,
+                      device="cuda") * math.sqrt(cfg.wkv_b_var)).to(torch.bfloat16)
+    k = torch.empty((cfg.n_heads, cfg.n_tokens, cfg.qk_nope_head_dim), dtype=torch.bfloat16, device="cuda")
+    v = torch.empty((cfg.n_heads, cfg.n_tokens, cfg.v_head_dim), dtype=torch.bfloat16, device="cuda")
+    for _ in range(warmup):
+        binding.expand_kv(x, w, wk, cfg.n_heads, cfg.qk_nope_head_dim, cfg.v_head_dim, cfg.eps, k, v)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        binding.expand_kv(x, w, wk, cfg.n_heads, cfg.qk_nope_head_dim, cfg.v_head_dim, cfg.eps, k, v)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1000.0 / steps
+
+
+def cpu_baseline(cfg, budget_s=12.0):
+    """The CPU oracle (absorb route, float64 NumPy) on the first sequences of the workload.
+
+    Scaled to microseconds per full step; `cores` is the thread count the BLAS library used."""
+    import numpy as np
+
+    from mla_latent_kv_absorb_amd.workloads import make_attn_inputs
+    from oracle import mla_oracle as O
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    n_seq = 4
+    sub = cfg.replace(batch=n_seq, cache_batch=n_seq)
+    x = make_attn_inputs(sub, seed=cfg.seed)
+    reps, elapsed = 0, 0.0
+    t0 = time.perf_counter()
+    while elapsed < budget_s or reps < 2:
+        O.absorb_attention(x["q_nope"], x["q_pe"], x["kv_cache"], x["pe_cache"], x["wkv_b"], cfg.end_pos,
+                           cfg.softmax_scale, cfg.v_head_dim)
+        reps += 1
+        elapsed = time.perf_counter() - t0
+        if reps >= 500:
+            break
+    per_call = elapsed / reps
+    us_per_step = per_call * 1e6 * cfg.batch / n_seq
+    return {"value": round(us_per_step, 1), "unit": "us/step", "cores": int(threads), "kind": "oracle",
+            "sample": f"absorb route, float64, {n_seq} of {cfg.batch} sequences (same shapes otherwise), "
+                      f"{reps} calls in {elapsed:.1f} s, scaled by {cfg.batch}/{n_seq}",
+            "host_cpus": os.cpu_count()}
+
+
+def traffic_for(kernel_src, name):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they match this source."""
+    path = os.path.join(ROOT, "profiles", f"{name}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+        sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
+        if rec.get("source_sha256") != sha:
+            return None
+        return rec.get("traffic_bytes")
+    except Exception:
+        return None
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="dsv3_decode")
+    ap.add_argument("--sets", type=int, default=4, help="input sets rotated over (cold Infinity Cache)")
+    ap.add_argument("--no-extras", action="store_true", help="skip timing the other workloads")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from mla_latent_kv_absorb_amd import binding
+    from mla_latent_kv_absorb_amd.workloads import ATTN_CONFIGS, EXPAND_CONFIGS
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    binding.load()  # fails loudly if the HIP library is not built
+    torch.cuda.set_device(0)
+
+    cfg = ATTN_CONFIGS[args.workload]
+    work = attn_work(cfg)
+    us, wall_us, kt = time_attn(cfg, args.steps, args.warmup, args.sets, torch, binding)
+    gbs = work["bytes"] / (us * 1e-6) / 1e9
+    tflops = work["flops"] / (us * 1e-6) / 1e12
+
+    attn = kt.get("attn")
+    roofline = None
+    if attn:
+        kb = work["attn_kernel_bytes"]
+        ach = kb / (attn["avg_us"] * 1e-6) / 1e9
+        src = os.path.join(ROOT, "mla_latent_kv_absorb_amd", "csrc", "absorb_mfma.hip")
+        roofline = {"kernel": "attn_kernel", "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic_for(src, "attn_kernel"),
+                    "algorithmic_bytes": kb, "avg_us": round(attn["avg_us"], 2), "launches": attn["launches"]}
+
+    line = {
+        "metric": METRIC,
+        "value": round(us, 2),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us / 1000.0, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": cfg.batch, "seqlen_q": cfg.seqlen_q, "n_heads": cfg.n_heads,
+                   "kv_lora_rank": cfg.kv_lora_rank, "qk_rope_head_dim": cfg.qk_rope_head_dim,
+                   "qk_nope_head_dim": cfg.qk_nope_head_dim, "v_head_dim": cfg.v_head_dim,
+                   "end_pos": cfg.end_pos, "input_sets_rotated": args.sets},
+        "gbps": round(gbs, 1),
+        "tflops": round(tflops, 2),
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+        "algorithmic_bytes": work["bytes"],
+        "algorithmic_flops": work["flops"],
+        "wall_us_per_step": round(wall_us, 2),
+        "roofline": roofline,
+    }
+
+    if not args.no_extras:
+        extras = {}
+        for name in ("long_decode", "chunk_prefill"):
+            c = ATTN_CONFIGS[name]
+            w = attn_work(c)
+            steps = 10 if name == "chunk_prefill" else 30
+            u, _, k = time_attn(c, steps, 3, 2 if name == "chunk_prefill" else args.sets, torch, binding,
+                                seed=c.seed, timed_kernels=0b111)
+            extras[name] = {"us_per_step": round(u, 2), "gbps": round(w["bytes"] / (u * 1e-6) / 1e9, 1),
+                            "tflops": round(w["flops"] / (u * 1e-6) / 1e12, 2),
+                            "kernels_us": {n: round(v["avg_us"], 2) for n, v in k.items()}}
+        ec = EXPAND_CONFIGS["dsv3_expand"]
+        u = time_expand(ec, 20, 3, torch, binding)
+        w = expand_work(ec)
+        extras["dsv3_expand"] = {"us_per_step": round(u, 2), "gbps": round(w["bytes"] / (u * 1e-6) / 1e9, 1),
+                                 "tflops": round(w["flops"] / (u * 1e-6) / 1e12, 2),
+                                 "mfma_frac": round(w["flops"] / (u * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+        line["extras"] = extras
+
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(cfg)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

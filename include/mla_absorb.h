@@ -135,6 +135,25 @@ int32_t mla_expand_kv(const void *c_kv, const void *rms_w, const void *wkv_b, vo
                       int64_t qk_nope_head_dim, int64_t v_head_dim, float eps, int32_t dtype,
                       int32_t path, void *stream);
 
+/* ---- kernel timing (benchmark instrumentation) ----------------------------------------------
+ * While a kernel's bit is set in the mask given to mla_timing_enable (bit k = kernel id k), every
+ * launch of it from this thread is bracketed by a pair of HIP events recorded on the launch
+ * stream.  mla_timing_collect waits for the recorded events and returns, per kernel id, the
+ * number of launches and their summed duration in milliseconds since the previous collect, then
+ * forgets them.  The library owns the events.  Returns MLA_OK, or MLA_ERR_HIP if an event call
+ * failed (the affected launches are then missing from the totals). */
+#define MLA_KERNEL_ABSORB_Q 0     /* query absorption through W_UK            */
+#define MLA_KERNEL_ATTN 1         /* split-KV scores, softmax, latent sum      */
+#define MLA_KERNEL_MERGE_UPPROJ 2 /* split merge and W_UV projection           */
+#define MLA_KERNEL_EXPAND 3       /* RMSNorm + projection + head-major split   */
+#define MLA_KERNEL_PLAIN 4        /* any kernel of the plain vector-ALU path   */
+#define MLA_NUM_KERNELS 5
+
+int32_t mla_timing_enable(uint32_t kernel_mask);
+int32_t mla_timing_collect(int32_t launches[MLA_NUM_KERNELS], double ms[MLA_NUM_KERNELS]);
+/* Short name of a kernel id ("" for an unknown id). */
+const char *mla_kernel_name(int32_t kernel_id);
+
 /* Static text for a status code (never NULL). */
 const char *mla_strerror(int32_t status);
 

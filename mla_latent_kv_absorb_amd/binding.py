@@ -30,7 +30,9 @@ MLA_DTYPE_BF16 = 1
 PATHS = {"auto": 0, "plain": 1, "mfma": 2}
 
 EXPORTED = ("mla_absorb_attn", "mla_absorb_attn_workspace_size", "mla_expand_kv", "mla_strerror",
-            "mla_last_error")
+            "mla_last_error", "mla_timing_enable", "mla_timing_collect", "mla_kernel_name")
+
+NUM_KERNELS = 5  # MLA_NUM_KERNELS
 
 
 class AttnShape(ctypes.Structure):
@@ -72,6 +74,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_strerror.restype = ctypes.c_char_p
     lib.mla_last_error.argtypes = []
     lib.mla_last_error.restype = ctypes.c_char_p
+    lib.mla_timing_enable.argtypes = [ctypes.c_uint32]
+    lib.mla_timing_enable.restype = i32
+    lib.mla_timing_collect.argtypes = [ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_double)]
+    lib.mla_timing_collect.restype = i32
+    lib.mla_kernel_name.argtypes = [i32]
+    lib.mla_kernel_name.restype = ctypes.c_char_p
     _lib = lib
     return lib
 
@@ -82,6 +90,23 @@ def strerror(status: int) -> str:
 
 def last_error() -> str:
     return load().mla_last_error().decode()
+
+
+def timing_enable(kernel_mask: int) -> None:
+    """Record HIP events around the kernels whose id bit is set (0 turns timing off)."""
+    load().mla_timing_enable(kernel_mask)
+
+
+def timing_collect() -> dict:
+    """{kernel name: {"launches": n, "avg_us": mean duration}} since the previous collect."""
+    lib = load()
+    launches = (ctypes.c_int32 * NUM_KERNELS)()
+    ms = (ctypes.c_double * NUM_KERNELS)()
+    rc = lib.mla_timing_collect(launches, ms)
+    if rc != MLA_OK:
+        raise MLAError(rc, "kernel timing events failed")
+    return {lib.mla_kernel_name(i).decode(): {"launches": launches[i], "avg_us": ms[i] * 1000.0 / launches[i]}
+            for i in range(NUM_KERNELS) if launches[i]}
 
 
 def _check(status: int) -> None:

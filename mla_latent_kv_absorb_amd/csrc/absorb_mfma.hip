@@ -345,6 +345,7 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(AbsorbQArgs a) {
 // ------------------------------------------------------------------------------------------------
 // Merge the split partials of 32 rows of one head into o_lat (bf16, LDS), then
 // out[row, e] = sum_c o_lat[row, c] * W_UV[h][e][c]; wave w produces e in [32 w, 32 w + 32).
+// The merge weights are w_i = exp2(m_i - M) / sum_i exp2(m_i - M) l_i (zero for an empty split).
 struct MergeArgs {
   const float *part_ml;
   const uint16_t *part_o;
@@ -355,6 +356,7 @@ struct MergeArgs {
 
 __global__ void __launch_bounds__(256) merge_upproj_kernel(MergeArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char ol[32 * kC * 2];  // 32 KB
+  __shared__ float row_max[32], row_inv[32];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int l32 = lane & 31, g = lane >> 5;
@@ -365,51 +367,87 @@ __global__ void __launch_bounds__(256) merge_upproj_kernel(MergeArgs a) {
   // W_UV[h] rows e = 32 wave + l32 as the B operand: lane holds W[e][16 ks + 8 g .. +7]
   u32x4 wf[32];
   {
-    const uint16_t *wr = a.wkv_b + (int64_t(h) * (kDn + kDv) + kDn + 32 * wave + l32) * kC + 8 * g;
+    const rsrc_t wres = make_rsrc(a.wkv_b + (int64_t(h) * (kDn + kDv) + kDn) * kC, kDv * kC * 2);
+    const uint32_t voff = uint32_t(32 * wave + l32) * (kC * 2) + 16 * g;
 #pragma unroll
-    for (int ks = 0; ks < 32; ++ks) wf[ks] = *reinterpret_cast<const u32x4 *>(wr + 16 * ks);
+    for (int ks = 0; ks < 32; ++ks) wf[ks] = buf_load16(wres, voff, ks * 32);
   }
 
-  const int tr = threadIdx.x >> 3;  // row this thread merges
-  const int tq = threadIdx.x & 7;   // its chunk phase
+  const int ch = threadIdx.x & 63;  // 16-byte chunk of the latent this thread merges
+  const int r0 = threadIdx.x >> 6;  // rows r0, r0 + 4, ..., r0 + 28
+  const int64_t stride_row = int64_t(a.H) * a.splits;  // partial rows between consecutive m
   for (int rb = rb0; rb < min(nrb, rb0 + a.row_blocks_per_wg); ++rb) {
-    const int m = rb * 32 + tr;
-    const bool ok = m < a.M;
-    const int64_t grow = int64_t(m) * a.H + h;
-    // weights exp2(m_i - M) / sum_i exp2(m_i - M) l_i, computed by the 8 threads of a row
-    float wmax = -INFINITY;
-    if (ok)
-      for (int i = 0; i < a.splits; ++i) wmax = fmaxf(wmax, a.part_ml[2 * (grow * a.splits + i)]);
-    float den = 0.f;
-    if (ok)
-      for (int i = tq; i < a.splits; i += 8) {
-        const float mi = a.part_ml[2 * (grow * a.splits + i)];
-        if (mi != -INFINITY) den += fast_exp2(mi - wmax) * a.part_ml[2 * (grow * a.splits + i) + 1];
+    // ---- per-row maximum and 1 / denominator (8 threads per row share the splits)
+    {
+      const int r = threadIdx.x >> 3, q = threadIdx.x & 7;
+      const int m = rb * 32 + r;
+      const float *ml = a.part_ml + 2 * ((int64_t(m) * a.H + h) * a.splits);
+      float mx = -INFINITY;
+      if (m < a.M)
+        for (int i = q; i < a.splits; i += 8) mx = fmaxf(mx, ml[2 * i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 4, 64));
+      float den = 0.f;
+      if (m < a.M)
+        for (int i = q; i < a.splits; i += 8) {
+          const float mi = ml[2 * i];
+          if (mi != -INFINITY) den += fast_exp2(mi - mx) * ml[2 * i + 1];
+        }
+      den += __shfl_xor(den, 1, 64);
+      den += __shfl_xor(den, 2, 64);
+      den += __shfl_xor(den, 4, 64);
+      if (q == 0) {
+        row_max[r] = mx;
+        row_inv[r] = (m < a.M && den > 0.f) ? 1.f / den : 0.f;
       }
-    den += __shfl_xor(den, 1, 64);
-    den += __shfl_xor(den, 2, 64);
-    den += __shfl_xor(den, 4, 64);
-    const float inv = ok ? 1.f / den : 0.f;
-    // chunks tq, tq+8, ... of the row (64 chunks of 8 columns)
-    for (int cq = tq; cq < kC / 8; cq += 8) {
-      float o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (ok) {
-        for (int i = 0; i < a.splits; ++i) {
-          const int64_t idx = grow * a.splits + i;
-          const float mi = a.part_ml[2 * idx];
-          if (mi == -INFINITY) continue;
-          const float wi = fast_exp2(mi - wmax) * inv;
-          const u32x4 v = *reinterpret_cast<const u32x4 *>(a.part_o + idx * kC + cq * 8);
+    }
+    __syncthreads();
+    // ---- o_lat[row][chunk] = sum_i w_i o_i[row][chunk]; the 8 rows of a thread load in parallel
+    {
+      float acc[8][8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[k][e] = 0.f;
+      float mx[8], inv[8];
+      uint32_t base[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int r = r0 + 4 * k;
+        const int m = min(rb * 32 + r, a.M - 1);
+        mx[k] = row_max[r];
+        inv[k] = row_inv[r];
+        base[k] = uint32_t((int64_t(m) * a.H + h) * a.splits) * (kC * 2) + ch * 16;
+      }
+      const rsrc_t pres = make_rsrc(a.part_o, 0xffffffffu);
+      const float *mlb = a.part_ml;
+      for (int i = 0; i < a.splits; ++i) {
+        u32x4 v[8];
+        float wgt[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          v[k] = buf_load16(pres, base[k], uint32_t(i) * (kC * 2));
+          const int m = min(rb * 32 + r0 + 4 * k, a.M - 1);
+          const float mi = mlb[2 * ((int64_t(m) * a.H + h) * a.splits + i)];
+          wgt[k] = (mi == -INFINITY) ? 0.f : fast_exp2(mi - mx[k]) * inv[k];
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            o[2 * e] = fmaf(wi, __uint_as_float(v[e] << 16), o[2 * e]);
-            o[2 * e + 1] = fmaf(wi, __uint_as_float(v[e] & 0xffff0000u), o[2 * e + 1]);
+            acc[k][2 * e] = fmaf(wgt[k], __uint_as_float(v[k][e] << 16), acc[k][2 * e]);
+            acc[k][2 * e + 1] = fmaf(wgt[k], __uint_as_float(v[k][e] & 0xffff0000u), acc[k][2 * e + 1]);
           }
-        }
       }
-      const u32x4 pk{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7])};
-      const int pos = (cq & ~7) | ((cq & 7) ^ (tr & 7));
-      *reinterpret_cast<u32x4 *>(ol + tr * (kC * 2) + pos * 16) = pk;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int r = r0 + 4 * k;
+        const u32x4 pk{pack_bf16x2(acc[k][0], acc[k][1]), pack_bf16x2(acc[k][2], acc[k][3]),
+                       pack_bf16x2(acc[k][4], acc[k][5]), pack_bf16x2(acc[k][6], acc[k][7])};
+        const int pos = (ch & ~7) | ((ch & 7) ^ (r & 7));
+        lds_write16(ol, uint32_t(r) * (kC * 2) + pos * 16, pk);
+      }
     }
     __syncthreads();
     f32x16 d = f32x16{};
@@ -419,14 +457,15 @@ __global__ void __launch_bounds__(256) merge_upproj_kernel(MergeArgs a) {
       const u32x4 af = lds_read16(ol, l32 * (kC * 2) + ((q & ~7) | ((q & 7) ^ (l32 & 7))) * 16);
       d = mfma32(af, wf[ks], d);
     }
-    __syncthreads();
     // D[row][e]: lane holds e = 32 wave + l32, rows 8 (r/4) + 4 g + r % 4
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int mm = rb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
       if (mm < a.M) a.out[(int64_t(mm) * a.H + h) * kDv + 32 * wave + l32] = f32_to_bf16(d[r]);
     }
+    __syncthreads();  // row_max / row_inv / ol are rewritten by the next row block
   }
+  (void)stride_row;
 }
 
 }  // namespace
@@ -455,6 +494,15 @@ int32_t mfma_attn_splits(const AttnCall &c, int num_cus) {
   return int32_t(splits);
 }
 
+bool mfma_attn_plan_ok(const AttnCall &c, const char **why) {
+  // split partials are addressed with 32-bit byte offsets
+  if (c.B * c.S * c.H * int64_t(c.splits) * kC * 2 >= (int64_t(1) << 32)) {
+    *why = "batch * seqlen_q * n_heads * num_splits too large for the split partials";
+    return false;
+  }
+  return true;
+}
+
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 size_t mfma_attn_workspace(const AttnCall &c) {
@@ -473,8 +521,10 @@ hipError_t mfma_absorb_attn(const AttnCall &c) {
 
   AbsorbQArgs qa{static_cast<const uint16_t *>(c.q_nope), static_cast<const uint16_t *>(c.wkv_b), q_lat, int32_t(c.H), M, 4};
   const int nrb = (M + 31) / 32;
+  timing_begin(MLA_KERNEL_ABSORB_Q, c.stream);
   absorb_q_kernel<<<dim3(unsigned(c.H), kC / 128, unsigned((nrb + qa.row_blocks_per_wg - 1) / qa.row_blocks_per_wg)), 256,
                     0, c.stream>>>(qa);
+  timing_end(MLA_KERNEL_ABSORB_Q, c.stream);
 
   AttnArgs aa{};
   aa.q_lat = q_lat;
@@ -493,12 +543,16 @@ hipError_t mfma_absorb_attn(const AttnCall &c) {
   aa.row_blocks = int32_t((c.S * c.H + kRowsWG - 1) / kRowsWG);
   aa.scale_log2 = c.scale * kLog2e;
   const int64_t nwg = c.B * int64_t(aa.splits) * aa.row_blocks;
+  timing_begin(MLA_KERNEL_ATTN, c.stream);
   attn_kernel<<<dim3(unsigned(nwg)), 256, 0, c.stream>>>(aa);
+  timing_end(MLA_KERNEL_ATTN, c.stream);
 
   MergeArgs ma{part_ml, part_o, static_cast<const uint16_t *>(c.wkv_b), static_cast<uint16_t *>(c.out), int32_t(c.H), M,
                c.splits, 8};
+  timing_begin(MLA_KERNEL_MERGE_UPPROJ, c.stream);
   merge_upproj_kernel<<<dim3(unsigned(c.H), unsigned((nrb + ma.row_blocks_per_wg - 1) / ma.row_blocks_per_wg)), 256, 0,
                         c.stream>>>(ma);
+  timing_end(MLA_KERNEL_MERGE_UPPROJ, c.stream);
   return hipGetLastError();
 }
 

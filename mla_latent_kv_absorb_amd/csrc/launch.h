@@ -29,6 +29,10 @@ struct ExpandCall {
   hipStream_t stream;
 };
 
+// ---- benchmark instrumentation (no-ops unless enabled for the kernel id) ----------------------
+void timing_begin(int kernel_id, hipStream_t stream);
+void timing_end(int kernel_id, hipStream_t stream);
+
 // ---- plain vector-ALU path (any shape, fp32 or bf16) -------------------------------------------
 size_t plain_attn_workspace(const AttnCall &c);
 int32_t plain_attn_splits(const AttnCall &c);
@@ -39,6 +43,7 @@ hipError_t plain_expand_kv(const ExpandCall &c);
 bool mfma_attn_supported(const AttnCall &c, const char **why);
 size_t mfma_attn_workspace(const AttnCall &c);
 int32_t mfma_attn_splits(const AttnCall &c, int num_cus);
+bool mfma_attn_plan_ok(const AttnCall &c, const char **why);  // limits that depend on the split count
 hipError_t mfma_absorb_attn(const AttnCall &c);
 
 bool mfma_expand_supported(const ExpandCall &c, const char **why);

@@ -89,6 +89,18 @@ int32_t plan_attn(const mla_attn_shape *shape, int64_t end_pos, int32_t dtype,
   }
   if (c.splits > end_pos) c.splits = int32_t(end_pos);
   c.split_len = (end_pos + c.splits - 1) / c.splits;
+  if (use_mfma) {
+    const char *why = "";
+    if (!mla::mfma_attn_plan_ok(c, &why)) {
+      if (opt.path == MLA_PATH_MFMA) return fail(MLA_ERR_UNSUPPORTED, "matrix-core path: %s", why);
+      use_mfma = false;
+      if (opt.num_splits == 0) {
+        c.splits = mla::plain_attn_splits(c);
+        if (c.splits > end_pos) c.splits = int32_t(end_pos);
+        c.split_len = (end_pos + c.splits - 1) / c.splits;
+      }
+    }
+  }
   return MLA_OK;
 }
 

@@ -161,6 +161,7 @@ hipError_t run_attn(const AttnCall &a) {
   float *part_ml = q_lat + rows * a.C;
   float *part_o = part_ml + 2 * rows * a.splits;
   const T *q_nope = static_cast<const T *>(a.q_nope);
+  timing_begin(MLA_KERNEL_PLAIN, a.stream);
   plain_absorb_q_kernel<T><<<dim3(unsigned(rows), unsigned((a.C + kThreads - 1) / kThreads)), kThreads, 0,
                              a.stream>>>(q_nope, static_cast<const T *>(a.wkv_b), q_lat, a.H, a.C, a.Dn, a.Dv);
   const size_t sm_attn = sizeof(float) * size_t(2 * a.C + a.R + kThreads + 16);
@@ -169,16 +170,19 @@ hipError_t run_attn(const AttnCall &a) {
       part_ml, part_o, a);
   plain_merge_upproj_kernel<T><<<dim3(unsigned(rows)), kThreads, sizeof(float) * size_t(a.C), a.stream>>>(
       part_ml, part_o, static_cast<const T *>(a.wkv_b), static_cast<T *>(a.out), a);
+  timing_end(MLA_KERNEL_PLAIN, a.stream);
   return hipGetLastError();
 }
 
 template <typename T>
 hipError_t run_expand(const ExpandCall &e) {
   const int64_t feats = e.H * (e.Dn + e.Dv);
+  timing_begin(MLA_KERNEL_PLAIN, e.stream);
   plain_expand_kernel<T><<<dim3(unsigned(e.T), unsigned((feats + kThreads - 1) / kThreads)), kThreads,
                            sizeof(float) * size_t(e.C + 16), e.stream>>>(
       static_cast<const T *>(e.c_kv), static_cast<const T *>(e.rms_w), static_cast<const T *>(e.wkv_b),
       static_cast<T *>(e.k_nope), static_cast<T *>(e.v), e);
+  timing_end(MLA_KERNEL_PLAIN, e.stream);
   return hipGetLastError();
 }
 
