@@ -188,6 +188,9 @@ def main():
     ap.add_argument("--sets", type=int, default=4, help="input sets rotated over (cold Infinity Cache)")
     ap.add_argument("--no-extras", action="store_true", help="skip timing the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB, --steps times (reference "
+                         "kernel of known size for scaling the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -207,9 +210,21 @@ def main():
     binding.load()  # fails loudly if the HIP library is not built
     torch.cuda.set_device(0)
 
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20)
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "dispatches": args.steps}))
+        return
+
     cfg = ATTN_CONFIGS[args.workload]
     work = attn_work(cfg)
     us, wall_us, kt = time_attn(cfg, args.steps, args.warmup, args.sets, torch, binding)
+    # per-kernel averages of the same workload in a separate, fully instrumented pass
+    _, _, kt_all = time_attn(cfg, 20, 3, args.sets, torch, binding, timed_kernels=0b1111)
     gbs = work["bytes"] / (us * 1e-6) / 1e9
     tflops = work["flops"] / (us * 1e-6) / 1e12
 
@@ -248,6 +263,7 @@ def main():
         "algorithmic_flops": work["flops"],
         "wall_us_per_step": round(wall_us, 2),
         "roofline": roofline,
+        "kernels_us": {n: round(v["avg_us"], 2) for n, v in kt_all.items()},
     }
 
     if not args.no_extras:
@@ -257,7 +273,7 @@ def main():
             w = attn_work(c)
             steps = 10 if name == "chunk_prefill" else 30
             u, _, k = time_attn(c, steps, 3, 2 if name == "chunk_prefill" else args.sets, torch, binding,
-                                seed=c.seed, timed_kernels=0b111)
+                                seed=c.seed, timed_kernels=0b1111)
             extras[name] = {"us_per_step": round(u, 2), "gbps": round(w["bytes"] / (u * 1e-6) / 1e9, 1),
                             "tflops": round(w["flops"] / (u * 1e-6) / 1e12, 2),
                             "kernels_us": {n: round(v["avg_us"], 2) for n, v in k.items()}}

@@ -3,13 +3,14 @@
 // fp32 accumulation.
 //
 // The computation is the absorb path of the page "Naive vs Absorb Attention Implementations in
-// DeepSeek-V3" (section "Absorb Path Execution"), run as three kernels:
-//   1. absorb_q_kernel       q_lat[row, :] = q_nope[row, :] . W_UK[h]            (query absorption)
-//   2. attn_kernel           per (sequence, 128-row block, position split): scores against
-//                            kv_cache (512) and pe_cache (64) as one 576-deep contraction, online
-//                            softmax, probability-weighted sum over kv_cache in latent space
-//   3. merge_upproj_kernel   merge the split partials (rescaled by exp2(m_i - M)), then project
-//                            out through W_UV[h]
+// DeepSeek-V3" (section "Absorb Path Execution"), run as up to four kernels:
+//   1. absorb_q_kernel   q_lat[row, :] = q_nope[row, :] . W_UK[h]            (query absorption)
+//   2. attn_kernel       per (sequence, 128-row block, position split): scores against kv_cache
+//                        (512) and pe_cache (64) as one 576-deep contraction, online softmax,
+//                        probability-weighted sum over kv_cache in latent space
+//   3. merge_kernel      combine the split partials (rescaled by exp2(m_i - M)); skipped when
+//                        there is a single split
+//   4. upproj_kernel     project out through W_UV[h]
 // Rows are the B*S*H query rows in (b, s, h) order.  Every kv/pe row of a split is read from HBM
 // once per 128-row block and shared through LDS by all of the block's heads.
 #include "common.h"
@@ -24,19 +25,26 @@ constexpr int kC = 512;        // kv_lora_rank
 constexpr int kR = 64;         // qk_rope_head_dim
 constexpr int kDn = 128;       // qk_nope_head_dim
 constexpr int kDv = 128;       // v_head_dim
-constexpr int kTile = 64;      // cached positions per LDS tile (two 32-position MFMA blocks)
+constexpr int kTile = 32;      // cached positions per LDS tile (one 32-position MFMA block)
+constexpr int kStages = 4;     // tiles in LDS: three in flight while one is consumed
 constexpr int kRowsWG = 128;   // query rows per attention workgroup (4 waves x 32)
-constexpr int kKvTileBytes = kTile * kC * 2;              // 64 KB
-constexpr int kPeTileBytes = kTile * kR * 2;              // 8 KB
-constexpr int kStageBytes = kKvTileBytes + kPeTileBytes;  // 72 KB; two stages fill 144 KB of LDS
+constexpr int kKvTileBytes = kTile * kC * 2;              // 32 KB
+constexpr int kPeTileBytes = kTile * kR * 2;              // 4 KB
+constexpr int kStageBytes = kKvTileBytes + kPeTileBytes;  // 36 KB; four stages fill 144 KB of LDS
+constexpr int kLoadsPerTile = kTile * (kC + kR) * 2 / 16 / 256;  // 16-byte DMA loads per thread per tile (9)
 constexpr float kLog2e = 1.4426950408889634f;
 
-// XOR swizzle of 16-byte chunks inside a tile row (applied within aligned groups of 8 chunks).
-// It makes both LDS read patterns conflict-free: the score read, where lanes 0..7 touch rows
-// rho(0..7) = {0,1,2,3,8,9,10,11} at one chunk, and the transposing read, where each group of 16
-// lanes touches 4 consecutive rows at one 32-byte chunk pair.
-__device__ __forceinline__ int tile_swz(int row) { return ((row & 3) << 1) | ((row >> 3) & 1); }
-__device__ __forceinline__ int swz_chunk(int chunk, int row) { return (chunk & ~7) | ((chunk & 7) ^ tile_swz(row)); }
+// LDS on gfx950 has 64 four-byte banks; a ds_read_b128 is serviced 16 lanes at a time and a
+// (transposing) 8-byte read 32 lanes at a time.  kv tile rows are 1 KB, so every row starts on
+// bank 0; 16-byte chunks are XOR-swizzled inside aligned groups of 16 (256 bytes) by
+// F(row) = ((row & 3) << 2) | ((row >> 2) & 3):
+//   - score read: 16 lanes read one chunk of rows r0..r0+15 -> F is a bijection on row & 15;
+//   - P.V transposing read: 32 lanes read chunks 4k..4k+3 of rows r0..r0+3 -> the high two bits
+//     of F are row & 3, so the four rows land on four different 64-byte quarters.
+// pe rows are 128 bytes (two per bank period); their 8 chunks are XOR-swizzled by (row >> 1) & 7.
+__device__ __forceinline__ int kv_swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+__device__ __forceinline__ int swz_chunk(int chunk, int row) { return (chunk & ~15) | ((chunk & 15) ^ kv_swz(row)); }
+__device__ __forceinline__ int pe_swz(int row) { return (row >> 1) & 7; }
 
 // The score MFMA's output row i is fed from tile row rho(i) (bits 2 and 3 swapped).  With that
 // order, registers 0..7 of lane l hold positions 8*(l/32) + 0..7 and registers 8..15 hold
@@ -50,7 +58,8 @@ struct AttnArgs {
   const uint16_t *kv;      // [Bmax, Tmax, 512]
   const uint16_t *pe;      // [Bmax, Tmax, 64]
   float *part_ml;          // [rows, splits, 2]   (max in log2 units, sum)
-  uint16_t *part_o;        // [rows, splits, 512] (unnormalised, relative to the max)
+  uint16_t *part_o;        // [rows, splits, 512] (unnormalised, relative to the max; with one
+                           // split: normalised, i.e. o_lat)
   int64_t Tmax;
   int32_t S, H, SH;        // SH = S * H rows per sequence
   int32_t end_pos, splits, split_len, row_blocks;
@@ -65,7 +74,7 @@ constexpr float kRescale = 8.f;
 
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 attn_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kStageBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kStages * kStageBytes];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int l32 = lane & 31, g = lane >> 5;
@@ -84,10 +93,13 @@ attn_kernel(AttnArgs a) {
   const int t_begin = split * a.split_len;
   const int t_split_end = min(t_begin + a.split_len, a.end_pos);
   const int row_end = row_ok ? min(t_split_end, a.end_pos - a.S + s + 1) : t_begin;
-  // positions the whole workgroup needs: up to the last visible position of its last row
-  // (integer division runs on the vector ALU, so the uniform results are re-scalarised)
-  const int last_row = min(a.SH - 1, rb * kRowsWG + kRowsWG - 1);
+  // Positions the workgroup needs (up to the last visible one of its last row), and the prefix
+  // visible to all of its rows (tiles inside it need no mask).  Integer division runs on the
+  // vector ALU, so the uniform results are re-scalarised.
+  const int first_row = rb * kRowsWG;
+  const int last_row = min(a.SH - 1, first_row + kRowsWG - 1);
   const int wg_end = __builtin_amdgcn_readfirstlane(min(t_split_end, a.end_pos - a.S + last_row / a.H + 1));
+  const int wg_full = __builtin_amdgcn_readfirstlane(min(t_split_end, a.end_pos - a.S + first_row / a.H + 1));
   const int ntiles = __builtin_amdgcn_readfirstlane(wg_end > t_begin ? (wg_end - t_begin + kTile - 1) / kTile : 0);
 
   // Absorbed query as the score B operand: lane holds q[row][16 ks + 8 g .. +7].
@@ -101,34 +113,28 @@ attn_kernel(AttnArgs a) {
     for (int ks = 0; ks < 4; ++ks) qf[32 + ks] = row_ok ? *reinterpret_cast<const u32x4 *>(pr + 16 * ks) : u32x4{0, 0, 0, 0};
   }
 
-  // DMA geometry.  kv: wave w moves tile rows 16w..16w+15, one 1 KB row per instruction; the
-  // lane's 16-byte chunk position is `lane` and it fetches source chunk swz_chunk(lane, row).
-  // pe: each instruction moves 8 rows of 128 bytes.  Rows past the last needed position repeat
-  // the last one (valid data, masked in the softmax).
+  // DMA geometry.  kv: wave w moves tile rows 8w..8w+7, one 1 KB row per instruction; lane l owns
+  // chunk position l and fetches source chunk swz_chunk(l, row).  pe: wave w moves rows
+  // 8w..8w+7 (128 bytes each) in one instruction.  Rows past the last needed position repeat the
+  // last one (valid data, masked in the softmax).
   const rsrc_t kvres = make_rsrc(a.kv + int64_t(b) * a.Tmax * kC, uint32_t(a.Tmax) * (kC * 2));
   const rsrc_t peres = make_rsrc(a.pe + int64_t(b) * a.Tmax * kR, uint32_t(a.Tmax) * (kR * 2));
-  // the swizzle depends on row bits 0, 1 and 3 only, so row 16w + i uses the pattern of row i
-  uint32_t kv_voff[16];
+  uint32_t kv_voff[8];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) kv_voff[i] = uint32_t(swz_chunk(lane, i)) * 16;
-  uint32_t pe_voff[2];  // pe rows 8 (2w + i) + lane / 8: bit 3 of the row is i
-#pragma unroll
-  for (int i = 0; i < 2; ++i) pe_voff[i] = uint32_t((lane & 7) ^ tile_swz(8 * i + (lane >> 3))) * 16;
+  for (int i = 0; i < 8; ++i) kv_voff[i] = uint32_t(swz_chunk(lane, 8 * (wave & 1) + i)) * 16;
+  const int pe_row = wave * 8 + (lane >> 3);
+  const uint32_t pe_voff = uint32_t((lane & 7) ^ pe_swz(pe_row)) * 16;
   auto issue = [&](int j) {
-    unsigned char *st = smem + (j & 1) * kStageBytes;
+    unsigned char *st = smem + (j % kStages) * kStageBytes;
     const int t0 = t_begin + j * kTile;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int t = min(t0 + wave * 16 + i, wg_end - 1);  // wavefront-uniform
-      buf_load16_lds(kvres, st + (wave * 16 + i) * (kC * 2), kv_voff[i], uint32_t(t) * (kC * 2));
+    for (int i = 0; i < 8; ++i) {
+      const int t = min(t0 + wave * 8 + i, wg_end - 1);  // wavefront-uniform
+      buf_load16_lds(kvres, st + (wave * 8 + i) * (kC * 2), kv_voff[i], uint32_t(t) * (kC * 2));
     }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int row = (wave * 2 + i) * 8 + (lane >> 3);
-      const int tp = min(t0 + row, wg_end - 1);
-      buf_load16_lds(peres, st + kKvTileBytes + (wave * 2 + i) * 1024, pe_voff[i] + uint32_t(tp - t0) * (kR * 2),
-                     uint32_t(t0) * (kR * 2));
-    }
+    const int tp = min(t0 + pe_row, wg_end - 1);
+    buf_load16_lds(peres, st + kKvTileBytes + wave * 8 * (kR * 2), pe_voff + uint32_t(tp - t0) * (kR * 2),
+                   uint32_t(t0) * (kR * 2));
   };
 
   f32x16 acc[16];
@@ -136,147 +142,162 @@ attn_kernel(AttnArgs a) {
   for (int i = 0; i < 16; ++i) acc[i] = f32x16{};
   float m_ref = -INFINITY, lsum = 0.f;
 
-  // score A-operand reads: tile row rho(l32), chunk 2 ks + g (swizzled)
+  // score A-operand reads: tile row rho(l32), chunk 2 ks + g
   const int arow = rho(l32);
-  const int afz = tile_swz(arow);
-  uint32_t sc_off[4];
+  uint32_t sc_off[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) sc_off[i] = uint32_t(arow) * (kC * 2) + uint32_t((2 * i + g) ^ afz) * 16;
-  const uint32_t pe_off0 = kKvTileBytes + uint32_t(arow) * (kR * 2);
-  // P.V A-operand (transposing) reads: rows 16 ks + 8 g + s16/4 (+4), chunk 4 cb + 2 chalf + (s16&3)/2
+  for (int i = 0; i < 8; ++i) sc_off[i] = uint32_t(arow) * (kC * 2) + uint32_t((2 * i + g) ^ kv_swz(arow)) * 16;
+  uint32_t pe_off[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pe_off[i] = kKvTileBytes + uint32_t(arow) * (kR * 2) + uint32_t((2 * i + g) ^ pe_swz(arow)) * 16;
+  // P.V A-operand (transposing) reads: source lane s16 of a 16-lane group reads row
+  // 16 ks + 8 g + 4 h + s16 / 4, chunk 4 cb + 2 chalf + (s16 & 3) / 2, half (s16 & 1).
   const int s16 = lane & 15, chalf = (lane >> 4) & 1;
-  uint32_t tr_off[2][2];  // [cb & 1][ks]
+  uint32_t tr_off[4][2];  // [cb & 3][h]; + 16 KB for ks = 1, + 256 B per (cb >> 2)
 #pragma unroll
-  for (int par = 0; par < 2; ++par)
+  for (int c4 = 0; c4 < 4; ++c4)
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int row0 = 16 * ks + 8 * g + (s16 >> 2);
-      const int chunk = 4 * par + 2 * chalf + ((s16 & 3) >> 1);
-      tr_off[par][ks] = uint32_t(row0) * (kC * 2) + uint32_t(swz_chunk(chunk, row0)) * 16 + (s16 & 1) * 8;
+    for (int h = 0; h < 2; ++h) {
+      const int row0 = 8 * g + 4 * h + (s16 >> 2);
+      const int chunk = 4 * c4 + 2 * chalf + ((s16 & 3) >> 1);
+      tr_off[c4][h] = uint32_t(row0) * (kC * 2) + uint32_t(swz_chunk(chunk, row0)) * 16 + (s16 & 1) * 8;
     }
 
-  if (ntiles > 0) issue(0);
+  for (int j = 0; j < kStages - 1 && j < ntiles; ++j) issue(j);
 
 #pragma unroll 1
   for (int j = 0; j < ntiles; ++j) {
-    // Only tile j's DMA is outstanding here.  A bare s_barrier follows: a __syncthreads() fence
-    // would add nothing, and issuing tile j+1 inside the branch below lets the compiler's own LDS
-    // DMA wait before the first LDS read resolve to "all but tile j+1".
-    wait_vmcnt<0>();
+    // Tiles j+1 and j+2 may still be in flight; a bare s_barrier follows (a __syncthreads() fence
+    // would also wait for them).
+    const int ahead = min(ntiles - 1 - j, kStages - 2);
+    if (ahead >= 2) wait_vmcnt<2 * kLoadsPerTile>();
+    else if (ahead == 1) wait_vmcnt<kLoadsPerTile>();
+    else wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
-    if (j + 1 < ntiles) issue(j + 1);
+    if (j + kStages - 1 < ntiles) issue(j + kStages - 1);
 
-    const unsigned char *st = smem + (j & 1) * kStageBytes;
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int t0 = t_begin + j * kTile + 32 * half;
-      const uint32_t hb = uint32_t(half) * 32 * (kC * 2);
+    const unsigned char *st = smem + (j % kStages) * kStageBytes;
+    const int t0 = t_begin + j * kTile;
 
-      // ---- scores S^T[position][row] over the 576-wide concatenation of kv and pe
-      f32x16 sacc = f32x16{};
-      {
-        u32x4 fr[2][4];
+    // ---- scores S^T[position][row] over the 576-wide concatenation of kv and pe
+    f32x16 sacc = f32x16{};
+    {
+      u32x4 fr[2][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) fr[0][i] = lds_read16(st, hb + sc_off[i]);
+      for (int i = 0; i < 4; ++i) fr[0][i] = lds_read16(st, sc_off[i]);
 #pragma unroll
-        for (int grp = 0; grp < 9; ++grp) {
-          const int cur = grp & 1;
-          if (grp + 1 < 8) {
+      for (int grp = 0; grp < 9; ++grp) {
+        const int cur = grp & 1;
+        if (grp + 1 < 8) {
+          const int k0 = 4 * (grp + 1);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) fr[cur ^ 1][i] = lds_read16(st, hb + sc_off[i] + (grp + 1) * 128);
-          } else if (grp + 1 == 8) {
+          for (int i = 0; i < 4; ++i) fr[cur ^ 1][i] = lds_read16(st, sc_off[(k0 + i) & 7] + ((k0 + i) >> 3) * 256);
+        } else if (grp + 1 == 8) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              fr[cur ^ 1][i] = lds_read16(st, pe_off0 + uint32_t(half) * 32 * (kR * 2) + uint32_t((2 * i + g) ^ afz) * 16);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) sacc = mfma32(fr[cur][i], qf[4 * grp + i], sacc);
-          __builtin_amdgcn_sched_barrier(0);
+          for (int i = 0; i < 4; ++i) fr[cur ^ 1][i] = lds_read16(st, pe_off[i]);
         }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sacc = mfma32(fr[cur][i], qf[4 * grp + i], sacc);
+        __builtin_amdgcn_sched_barrier(0);
       }
+    }
 
-      // ---- online softmax (log2 domain); register r holds position 16*(r/8) + 8*g + r%8
-      float x[16];
-      float mloc = -INFINITY;
+    // ---- online softmax (log2 domain); register r holds position 16*(r/8) + 8*g + r%8
+    const bool masked = t0 + kTile > wg_full;  // wavefront-uniform
+    float mloc = -INFINITY;
+    if (masked) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int t = t0 + 16 * (r >> 3) + 8 * g + (r & 7);
-        x[r] = (t < row_end) ? sacc[r] * a.scale_log2 : -INFINITY;
-        mloc = fmaxf(mloc, x[r]);
+        if (t >= row_end) sacc[r] = -INFINITY;
       }
-      const float mrow = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-      if (m_ref == -INFINITY) {
-        m_ref = mrow;  // first visible positions: nothing accumulated yet
-      } else if (mrow > m_ref + kRescale) {
-        const float alpha = fast_exp2(m_ref - mrow);
-        lsum *= alpha;
-        m_ref = mrow;
+    }
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
+    for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sacc[r]);
+    const float mrow = fmaxf(mloc, __shfl_xor(mloc, 32, 64)) * a.scale_log2;  // scale > 0
+    if (m_ref == -INFINITY) {
+      m_ref = mrow;  // first visible positions: nothing accumulated yet
+    } else if (mrow > m_ref + kRescale) {
+      const float alpha = fast_exp2(m_ref - mrow);
+      lsum *= alpha;
+      m_ref = mrow;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc[i][r] = agpr_write(agpr_read(acc[i][r]) * alpha);
+      for (int i = 0; i < 16; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][r] = agpr_write(agpr_read(acc[i][r]) * alpha);
+    }
+    const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+    float psum = 0.f;
+    u32x4 pb[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float p[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        p[r] = fast_exp2(fmaf(sacc[8 * h + r], a.scale_log2, -m_use));
+        psum += p[r];
       }
-      const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
-      float psum = 0.f;
-      u32x4 pb[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        float p[8];
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          p[r] = fast_exp2(x[8 * h + r] - m_use);
-          psum += p[r];
-        }
-        pb[h] = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                      pack_bf16x2(p[6], p[7])};
-      }
-      lsum += psum;
+      pb[h] = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                    pack_bf16x2(p[6], p[7])};
+    }
+    lsum += psum;
 
-      // ---- O^T[c][row] += KV^T[c][position] . P^T[position][row]
-      {
-        u32x4 fr[2][2];
+    // ---- O^T[c][row] += KV^T[c][position] . P^T[position][row]
+    {
+      u32x4 fr[2][2];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-          fr[0][ks] = lds_read_tr_pair(st, hb + tr_off[0][ks], hb + tr_off[0][ks] + 4 * (kC * 2));
+      for (int ks = 0; ks < 2; ++ks) fr[0][ks] = lds_read_tr_pair(st, tr_off[0][0] + ks * 16384, tr_off[0][1] + ks * 16384);
 #pragma unroll
-        for (int cb = 0; cb < 16; ++cb) {
-          const int cur = cb & 1;
-          if (cb + 1 < 16) {
-            const uint32_t base = hb + uint32_t((cb + 1) >> 1) * 128;
+      for (int cb = 0; cb < 16; ++cb) {
+        const int cur = cb & 1;
+        if (cb + 1 < 16) {
+          const int n = cb + 1;
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-              fr[cur ^ 1][ks] = lds_read_tr_pair(st, base + tr_off[(cb + 1) & 1][ks],
-                                                 base + tr_off[(cb + 1) & 1][ks] + 4 * (kC * 2));
-          }
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks) acc[cb] = mfma32(fr[cur][ks], pb[ks], acc[cb]);
-          __builtin_amdgcn_sched_barrier(0);
+          for (int ks = 0; ks < 2; ++ks)
+            fr[cur ^ 1][ks] = lds_read_tr_pair(st, tr_off[n & 3][0] + (n >> 2) * 256 + ks * 16384,
+                                               tr_off[n & 3][1] + (n >> 2) * 256 + ks * 16384);
         }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) acc[cb] = mfma32(fr[cur][ks], pb[ks], acc[cb]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
 
-  // ---- partial state of this split (max in log2 units, sum, unnormalised o)
+  // ---- partial state of this split: max (log2 units), sum, unnormalised o.  o goes through LDS
+  // so that every global store writes one whole 1 KB row.
   lsum += __shfl_xor(lsum, 32, 64);
-  if (row_ok) {
-    const int64_t idx = grow * a.splits + split;
-    if (g == 0) {
-      a.part_ml[2 * idx] = m_ref;
-      a.part_ml[2 * idx + 1] = lsum;
-    }
-    uint16_t *po = a.part_o + idx * kC + 4 * g;
+  // with a single split the result is final: normalise here and skip the merge
+  const float oscale = (a.splits == 1 && lsum > 0.f) ? 1.f / lsum : 1.f;
+  wait_vmcnt<0>();
+  __syncthreads();  // every wave is done with the tiles
+  unsigned char *stage = smem + wave * (32 * kC * 2);  // this wave's 32 rows
 #pragma unroll
-    for (int cb = 0; cb < 16; ++cb) {
+  for (int cb = 0; cb < 16; ++cb) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const u32x2 v{pack_bf16x2(agpr_read(acc[cb][4 * q]), agpr_read(acc[cb][4 * q + 1])),
-                      pack_bf16x2(agpr_read(acc[cb][4 * q + 2]), agpr_read(acc[cb][4 * q + 3]))};
-        *reinterpret_cast<u32x2 *>(po + 32 * cb + 8 * q) = v;
-      }
+    for (int q = 0; q < 4; ++q) {
+      const u32x2 v{pack_bf16x2(agpr_read(acc[cb][4 * q]) * oscale, agpr_read(acc[cb][4 * q + 1]) * oscale),
+                    pack_bf16x2(agpr_read(acc[cb][4 * q + 2]) * oscale, agpr_read(acc[cb][4 * q + 3]) * oscale)};
+      const int chunk = 4 * cb + q;
+      lds_write8(stage, uint32_t(l32) * (kC * 2) + uint32_t((chunk & ~15) | ((chunk & 15) ^ (l32 & 15))) * 16 + 8 * g, v);
     }
   }
+  if (row_ok && g == 0) {
+    const int64_t idx = grow * a.splits + split;
+    a.part_ml[2 * idx] = m_ref;
+    a.part_ml[2 * idx + 1] = lsum;
+  }
+  // same wavefront wrote these rows; LDS operations of one wavefront complete in order
+  const int rows_here = min(32, a.SH - (first_row + wave * 32));
+  const uint32_t rd_lane = uint32_t((lane & ~15) | ((lane & 15))) * 16;
+  for (int r = 0; r < rows_here; ++r) {
+    const u32x4 v = lds_read16(stage, uint32_t(r) * (kC * 2) + uint32_t((lane & ~15) | ((lane & 15) ^ (r & 15))) * 16);
+    const int64_t idx = (int64_t(b) * a.SH + first_row + wave * 32 + r) * a.splits + split;
+    *reinterpret_cast<u32x4 *>(a.part_o + idx * kC + lane * 8) = v;
+  }
+  (void)rd_lane;
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -291,7 +312,10 @@ struct AbsorbQArgs {
   int32_t row_blocks_per_wg;
 };
 
-__device__ __forceinline__ int w_swz(int row) { return (row & 3) << 1; }
+// W_UK tile rows are 256 bytes (one bank period, 16 chunks).  The transposing read touches 4
+// consecutive rows x 4 chunks per 32 lanes; XOR-ing the chunk with (row & 3) << 2 puts the four
+// rows in different 64-byte quarters.
+__device__ __forceinline__ int w_swz(int row) { return (row & 3) << 2; }
 
 __global__ void __launch_bounds__(256) absorb_q_kernel(AbsorbQArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char wt[kDn * 128 * 2];  // 32 KB
@@ -305,7 +329,7 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(AbsorbQArgs a) {
   // stage W_UK[h][0:128][c0:c0+128]: each wave instruction moves 4 rows of 256 bytes; within it the
   // lane's row is lane / 16 and its chunk position lane % 16 (source chunk swizzled by the row)
   const rsrc_t wres = make_rsrc(a.wkv_b + int64_t(h) * (kDn + kDv) * kC, kDn * kC * 2);
-  const uint32_t w_voff = uint32_t(lane >> 4) * (kC * 2) + uint32_t((lane & 15) ^ (((lane >> 4) & 3) << 1)) * 16;
+  const uint32_t w_voff = uint32_t(lane >> 4) * (kC * 2) + uint32_t((lane & 15) ^ w_swz(lane >> 4)) * 16;
 #pragma unroll
   for (int i = 0; i < 8; ++i)
     buf_load16_lds(wres, wt + (wave * 8 + i) * 1024, w_voff, uint32_t((wave * 8 + i) * 4) * (kC * 2) + c0 * 2);
@@ -325,8 +349,8 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(AbsorbQArgs a) {
       const int row0 = 16 * ks + 8 * g + (s16 >> 2);
       const int chunk = 4 * wave + 2 * chalf + ((s16 & 3) >> 1);
       const int within = (s16 & 1) * 8;
-      const uint32_t off0 = row0 * 256 + ((chunk & ~7) | ((chunk & 7) ^ w_swz(row0))) * 16 + within;
-      const uint32_t off1 = (row0 + 4) * 256 + ((chunk & ~7) | ((chunk & 7) ^ w_swz(row0 + 4))) * 16 + within;
+      const uint32_t off0 = row0 * 256 + (chunk ^ w_swz(row0)) * 16 + within;
+      const uint32_t off1 = (row0 + 4) * 256 + (chunk ^ w_swz(row0 + 4)) * 16 + within;
       const u32x4 af = lds_read_tr_pair(wt, off0, off1);
       d = mfma32(af, bf, d);
     }
@@ -343,129 +367,117 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(AbsorbQArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------------
-// Merge the split partials of 32 rows of one head into o_lat (bf16, LDS), then
-// out[row, e] = sum_c o_lat[row, c] * W_UV[h][e][c]; wave w produces e in [32 w, 32 w + 32).
-// The merge weights are w_i = exp2(m_i - M) / sum_i exp2(m_i - M) l_i (zero for an empty split).
+// Split merge: o_lat[row, :] = sum_i w_i o_i[row, :] with w_i = exp2(m_i - M) / sum_i exp2(m_i - M) l_i
+// (zero for a split that saw no position).  One thread per (row, 16-byte chunk); its split loads
+// are independent, so the whole grid keeps them in flight together.
 struct MergeArgs {
-  const float *part_ml;
-  const uint16_t *part_o;
-  const uint16_t *wkv_b;
-  uint16_t *out;           // [rows, 128]
-  int32_t H, M, splits, row_blocks_per_wg;
+  const float *part_ml;    // [rows, splits, 2]
+  const uint16_t *part_o;  // [rows, splits, 512]
+  uint16_t *o_lat;         // [rows, 512]
+  int64_t rows;
+  int32_t splits;
 };
 
-__global__ void __launch_bounds__(256) merge_upproj_kernel(MergeArgs a) {
+__global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
+  const int64_t gid = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t row = gid >> 6;
+  const int ch = int(gid & 63);
+  if (row >= a.rows) return;
+  const float *ml = a.part_ml + 2 * row * a.splits;
+  float M = -INFINITY;
+  for (int i = 0; i < a.splits; ++i) M = fmaxf(M, ml[2 * i]);
+  float den = 0.f;
+  for (int i = 0; i < a.splits; ++i)
+    if (ml[2 * i] != -INFINITY) den += fast_exp2(ml[2 * i] - M) * ml[2 * i + 1];
+  const float inv = 1.f / den;  // every row sees at least one position
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  const uint16_t *po = a.part_o + row * a.splits * kC + ch * 8;
+  int i = 0;
+  for (; i + 8 <= a.splits; i += 8) {
+    u32x4 v[8];
+    float w[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      v[k] = *reinterpret_cast<const u32x4 *>(po + int64_t(i + k) * kC);
+      const float mi = ml[2 * (i + k)];
+      w[k] = (mi == -INFINITY) ? 0.f : fast_exp2(mi - M) * inv;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] = fmaf(w[k], __uint_as_float(v[k][e] << 16), acc[2 * e]);
+        acc[2 * e + 1] = fmaf(w[k], __uint_as_float(v[k][e] & 0xffff0000u), acc[2 * e + 1]);
+      }
+  }
+  for (; i < a.splits; ++i) {
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(po + int64_t(i) * kC);
+    const float mi = ml[2 * i];
+    const float w = (mi == -INFINITY) ? 0.f : fast_exp2(mi - M) * inv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[2 * e] = fmaf(w, __uint_as_float(v[e] << 16), acc[2 * e]);
+      acc[2 * e + 1] = fmaf(w, __uint_as_float(v[e] & 0xffff0000u), acc[2 * e + 1]);
+    }
+  }
+  const u32x4 pk{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
+                 pack_bf16x2(acc[6], acc[7])};
+  *reinterpret_cast<u32x4 *>(a.o_lat + row * kC + ch * 8) = pk;
+}
+
+// ------------------------------------------------------------------------------------------------
+// out[row, e] = sum_c o_lat[row, c] * W_UV[h][e][c] for the rows of head h.  Two waves per
+// workgroup, each owning 32 of the workgroup's 64 output columns e; the W_UV rows stay in
+// registers while the workgroup walks its 32-row blocks (o_lat rows staged in LDS).
+struct UpprojArgs {
+  const uint16_t *o_lat;   // [rows, 512], row = m * H + h
+  const uint16_t *wkv_b;
+  uint16_t *out;           // [rows, 128]
+  int32_t H, M, row_blocks_per_wg;
+};
+
+__global__ void __launch_bounds__(128) upproj_kernel(UpprojArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char ol[32 * kC * 2];  // 32 KB
-  __shared__ float row_max[32], row_inv[32];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int l32 = lane & 31, g = lane >> 5;
   const int h = blockIdx.x;
-  const int rb0 = blockIdx.y * a.row_blocks_per_wg;
+  const int e0 = blockIdx.y * 64 + 32 * wave;
+  const int rb0 = blockIdx.z * a.row_blocks_per_wg;
   const int nrb = (a.M + 31) / 32;
 
-  // W_UV[h] rows e = 32 wave + l32 as the B operand: lane holds W[e][16 ks + 8 g .. +7]
+  // W_UV[h] rows e0 + l32 as the B operand: lane holds W[e][16 ks + 8 g .. +7]
   u32x4 wf[32];
   {
     const rsrc_t wres = make_rsrc(a.wkv_b + (int64_t(h) * (kDn + kDv) + kDn) * kC, kDv * kC * 2);
-    const uint32_t voff = uint32_t(32 * wave + l32) * (kC * 2) + 16 * g;
+    const uint32_t voff = uint32_t(e0 + l32) * (kC * 2) + 16 * g;
 #pragma unroll
     for (int ks = 0; ks < 32; ++ks) wf[ks] = buf_load16(wres, voff, ks * 32);
   }
-
-  const int ch = threadIdx.x & 63;  // 16-byte chunk of the latent this thread merges
-  const int r0 = threadIdx.x >> 6;  // rows r0, r0 + 4, ..., r0 + 28
-  const int64_t stride_row = int64_t(a.H) * a.splits;  // partial rows between consecutive m
   for (int rb = rb0; rb < min(nrb, rb0 + a.row_blocks_per_wg); ++rb) {
-    // ---- per-row maximum and 1 / denominator (8 threads per row share the splits)
-    {
-      const int r = threadIdx.x >> 3, q = threadIdx.x & 7;
-      const int m = rb * 32 + r;
-      const float *ml = a.part_ml + 2 * ((int64_t(m) * a.H + h) * a.splits);
-      float mx = -INFINITY;
-      if (m < a.M)
-        for (int i = q; i < a.splits; i += 8) mx = fmaxf(mx, ml[2 * i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 4, 64));
-      float den = 0.f;
-      if (m < a.M)
-        for (int i = q; i < a.splits; i += 8) {
-          const float mi = ml[2 * i];
-          if (mi != -INFINITY) den += fast_exp2(mi - mx) * ml[2 * i + 1];
-        }
-      den += __shfl_xor(den, 1, 64);
-      den += __shfl_xor(den, 2, 64);
-      den += __shfl_xor(den, 4, 64);
-      if (q == 0) {
-        row_max[r] = mx;
-        row_inv[r] = (m < a.M && den > 0.f) ? 1.f / den : 0.f;
-      }
-    }
-    __syncthreads();
-    // ---- o_lat[row][chunk] = sum_i w_i o_i[row][chunk]; the 8 rows of a thread load in parallel
-    {
-      float acc[8][8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[k][e] = 0.f;
-      float mx[8], inv[8];
-      uint32_t base[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int r = r0 + 4 * k;
-        const int m = min(rb * 32 + r, a.M - 1);
-        mx[k] = row_max[r];
-        inv[k] = row_inv[r];
-        base[k] = uint32_t((int64_t(m) * a.H + h) * a.splits) * (kC * 2) + ch * 16;
-      }
-      const rsrc_t pres = make_rsrc(a.part_o, 0xffffffffu);
-      const float *mlb = a.part_ml;
-      for (int i = 0; i < a.splits; ++i) {
-        u32x4 v[8];
-        float wgt[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          v[k] = buf_load16(pres, base[k], uint32_t(i) * (kC * 2));
-          const int m = min(rb * 32 + r0 + 4 * k, a.M - 1);
-          const float mi = mlb[2 * ((int64_t(m) * a.H + h) * a.splits + i)];
-          wgt[k] = (mi == -INFINITY) ? 0.f : fast_exp2(mi - mx[k]) * inv[k];
-        }
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            acc[k][2 * e] = fmaf(wgt[k], __uint_as_float(v[k][e] << 16), acc[k][2 * e]);
-            acc[k][2 * e + 1] = fmaf(wgt[k], __uint_as_float(v[k][e] & 0xffff0000u), acc[k][2 * e + 1]);
-          }
-      }
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int r = r0 + 4 * k;
-        const u32x4 pk{pack_bf16x2(acc[k][0], acc[k][1]), pack_bf16x2(acc[k][2], acc[k][3]),
-                       pack_bf16x2(acc[k][4], acc[k][5]), pack_bf16x2(acc[k][6], acc[k][7])};
-        const int pos = (ch & ~7) | ((ch & 7) ^ (r & 7));
-        lds_write16(ol, uint32_t(r) * (kC * 2) + pos * 16, pk);
-      }
+    // stage 32 o_lat rows: wave w copies rows w, w+2, ...; lane = 16-byte chunk (swizzled by row)
+#pragma unroll 4
+    for (int r = wave; r < 32; r += 2) {
+      const int m = min(rb * 32 + r, a.M - 1);
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(a.o_lat + (int64_t(m) * a.H + h) * kC + lane * 8);
+      lds_write16(ol, uint32_t(r) * (kC * 2) + uint32_t((lane & ~15) | ((lane & 15) ^ (r & 15))) * 16, v);
     }
     __syncthreads();
     f32x16 d = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < 32; ++ks) {
       const int q = 2 * ks + g;
-      const u32x4 af = lds_read16(ol, l32 * (kC * 2) + ((q & ~7) | ((q & 7) ^ (l32 & 7))) * 16);
+      const u32x4 af = lds_read16(ol, uint32_t(l32) * (kC * 2) + uint32_t((q & ~15) | ((q & 15) ^ (l32 & 15))) * 16);
       d = mfma32(af, wf[ks], d);
     }
-    // D[row][e]: lane holds e = 32 wave + l32, rows 8 (r/4) + 4 g + r % 4
+    __syncthreads();  // ol is rewritten by the next row block
+    // D[row][e]: lane holds e = e0 + l32, rows 8 (r/4) + 4 g + r % 4
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int mm = rb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-      if (mm < a.M) a.out[(int64_t(mm) * a.H + h) * kDv + 32 * wave + l32] = f32_to_bf16(d[r]);
+      if (mm < a.M) a.out[(int64_t(mm) * a.H + h) * kDv + e0 + l32] = f32_to_bf16(d[r]);
     }
-    __syncthreads();  // row_max / row_inv / ol are rewritten by the next row block
   }
-  (void)stride_row;
 }
 
 }  // namespace
@@ -547,12 +559,20 @@ hipError_t mfma_absorb_attn(const AttnCall &c) {
   attn_kernel<<<dim3(unsigned(nwg)), 256, 0, c.stream>>>(aa);
   timing_end(MLA_KERNEL_ATTN, c.stream);
 
-  MergeArgs ma{part_ml, part_o, static_cast<const uint16_t *>(c.wkv_b), static_cast<uint16_t *>(c.out), int32_t(c.H), M,
-               c.splits, 8};
-  timing_begin(MLA_KERNEL_MERGE_UPPROJ, c.stream);
-  merge_upproj_kernel<<<dim3(unsigned(c.H), unsigned((nrb + ma.row_blocks_per_wg - 1) / ma.row_blocks_per_wg)), 256, 0,
-                        c.stream>>>(ma);
-  timing_end(MLA_KERNEL_MERGE_UPPROJ, c.stream);
+  // split merge (skipped with one split: the attention epilogue then writes o_lat itself)
+  uint16_t *o_lat = part_o;
+  if (c.splits > 1) {
+    o_lat = q_lat;  // q_lat is dead once the attention kernel has run
+    MergeArgs ma{part_ml, part_o, o_lat, rows, c.splits};
+    timing_begin(MLA_KERNEL_MERGE, c.stream);
+    merge_kernel<<<dim3(unsigned((rows * 64 + 255) / 256)), 256, 0, c.stream>>>(ma);
+    timing_end(MLA_KERNEL_MERGE, c.stream);
+  }
+  UpprojArgs ua{o_lat, static_cast<const uint16_t *>(c.wkv_b), static_cast<uint16_t *>(c.out), int32_t(c.H), M, 8};
+  timing_begin(MLA_KERNEL_UPPROJ, c.stream);
+  upproj_kernel<<<dim3(unsigned(c.H), 2, unsigned((nrb + ua.row_blocks_per_wg - 1) / ua.row_blocks_per_wg)), 128, 0,
+                  c.stream>>>(ua);
+  timing_end(MLA_KERNEL_UPPROJ, c.stream);
   return hipGetLastError();
 }
 

@@ -39,8 +39,12 @@ struct ExpandArgs {
   float eps;
 };
 
+// Operand tiles have 128-byte rows (8 chunks of 16 bytes): two rows per 64-bank period.  A
+// ds_read_b128 serves 16 lanes = 16 consecutive rows at once, so chunks are XOR-swizzled by
+// (row >> 1) & 7: rows of equal parity then use eight different chunk slots.
+__device__ __forceinline__ int op_swz(int row) { return (row >> 1) & 7; }
 __device__ __forceinline__ uint32_t tile_off(int row, int chunk) {
-  return uint32_t(row) * (kKC * 2) + uint32_t(chunk ^ (row & 7)) * 16;
+  return uint32_t(row) * (kKC * 2) + uint32_t(chunk ^ op_swz(row)) * 16;
 }
 
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -56,11 +60,14 @@ expand_kernel(ExpandArgs a) {
   const int wt = wave & 1;   // token half of this wave
   const int wj = wave >> 1;  // 0: K_nope features, 1: V features
 
-  // W rows of this head; each wave instruction moves 8 rows x 128 bytes.  Within such a block the
-  // lane's row is lane / 8 and its chunk position lane % 8, so the per-lane offset is loop
-  // invariant: (lane / 8) * 1024 + ((lane % 8) ^ (lane / 8)) * 16.
+  // W rows of this head; each wave instruction moves 8 rows x 128 bytes.  Within instruction i
+  // the lane's row is 8 (8 wave + i) + lane / 8 and its chunk position lane % 8, so the source
+  // chunk (lane % 8) ^ op_swz(row) depends only on the lane and the parity of i.
   const rsrc_t wres = make_rsrc(a.wkv_b + int64_t(h) * (kDn + kDv) * kC, (kDn + kDv) * kC * 2);
-  const uint32_t w_lane_off = uint32_t(lane >> 3) * (kC * 2) + uint32_t((lane & 7) ^ (lane >> 3)) * 16;
+  uint32_t w_lane_off[2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par)
+    w_lane_off[par] = uint32_t(lane >> 3) * (kC * 2) + uint32_t((lane & 7) ^ op_swz(8 * par + (lane >> 3))) * 16;
   // c_kv staging: thread owns rows srow + 32 i and chunk schunk of every stage; rows past T read 0
   const int srow = threadIdx.x >> 3, schunk = threadIdx.x & 7;
   const rsrc_t xres = make_rsrc(a.c_kv + int64_t(t0) * kC, uint32_t(min(kTT, a.T - t0)) * (kC * 2));
@@ -73,13 +80,13 @@ expand_kernel(ExpandArgs a) {
     unsigned char *dst = smem + buf * kStage + wave * 8 * 1024;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      buf_load16_lds(wres, dst + i * 1024, w_lane_off, uint32_t((wave * 8 + i) * 8 * (kC * 2) + kc * (kKC * 2)));
+      buf_load16_lds(wres, dst + i * 1024, w_lane_off[i & 1], uint32_t((wave * 8 + i) * 8 * (kC * 2) + kc * (kKC * 2)));
   };
   auto load_x = [&](int kc) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) xr[i] = buf_load16(xres, x_lane_off, uint32_t(i * 32 * (kC * 2) + kc * (kKC * 2)));
   };
-  const uint32_t st_off0 = uint32_t(srow) * (kKC * 2) + uint32_t(schunk ^ (srow & 7)) * 16;  // row srow + 32 i: same swizzle
+  const uint32_t st_off0 = tile_off(srow, schunk);  // rows srow + 32 i share the swizzle
   auto store_x = [&](int kc, int buf) {
     const u32x4 wv = buf_load16(rwres, schunk * 16, kc * (kKC * 2));
     float w[8];
@@ -107,10 +114,10 @@ expand_kernel(ExpandArgs a) {
     }
   };
 
-  // operand reads: row base + ((q ^ (row & 7)) * 16), and row & 7 == l32 & 7 for every operand row
+  // operand reads: every operand row is 32 k + l32 (+ a multiple of 32), so it shares the swizzle of l32
   uint32_t rd_off[4];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) rd_off[ks] = uint32_t(l32) * (kKC * 2) + uint32_t((2 * ks + g) ^ (l32 & 7)) * 16;
+  for (int ks = 0; ks < 4; ++ks) rd_off[ks] = tile_off(l32, 2 * ks + g);
   const uint32_t a_base = uint32_t(wj * 128) * (kKC * 2);
   const uint32_t b_base = kStageHalf + uint32_t(wt * 128) * (kKC * 2);
 
