@@ -137,8 +137,10 @@ int32_t mla_expand_kv(const void *c_kv, const void *rms_w, const void *wkv_b, vo
 
 /* ---- kernel timing (benchmark instrumentation) ----------------------------------------------
  * While a kernel's bit is set in the mask given to mla_timing_enable (bit k = kernel id k), every
- * launch of it from this thread is bracketed by a pair of HIP events recorded on the launch
- * stream.  mla_timing_collect waits for the recorded events and returns, per kernel id, the
+ * launch of it from this thread carries a pair of HIP events on the launch stream.  A single
+ * matrix-core kernel is launched with hipExtLaunchKernel, whose events take the dispatch's own
+ * start and end times; the plain path's kernels are bracketed together by events recorded
+ * before and after them.  mla_timing_collect waits for the recorded events and returns, per kernel id, the
  * number of launches and their summed duration in milliseconds since the previous collect, then
  * forgets them.  The library owns the events.  Returns MLA_OK, or MLA_ERR_HIP if an event call
  * failed (the affected launches are then missing from the totals). */

@@ -163,29 +163,49 @@ def absorb_attn_workspace_size(shape: AttnShape, end_pos: int, dtype: int, num_s
     return int(n)
 
 
+class AbsorbAttnCall:
+    """One absorb-attention call with its arguments marshalled once.
+
+    The tensors are validated and their pointers, the shape descriptor and the workspace are
+    fixed at construction, together with the HIP stream that is current then; every call of the
+    object re-issues mla_absorb_attn with them (for loops that run the same step over and over
+    on the same buffers).  The object keeps the tensors alive.
+    """
+
+    def __init__(self, q_nope, q_pe, kv_cache, pe_cache, wkv_b, end_pos: int, softmax_scale: float, out=None, *,
+                 num_splits: int = 0, path: str = "auto", workspace=None):
+        import torch
+
+        lib = load()
+        _require_device(q_nope, q_pe, kv_cache, pe_cache, wkv_b)
+        shape = attn_shape(q_nope, q_pe, kv_cache, wkv_b)
+        dt = _dtype_code(q_nope)
+        if out is None:
+            out = torch.empty((shape.batch, shape.seqlen_q, shape.n_heads, shape.v_head_dim), dtype=q_nope.dtype,
+                              device=q_nope.device)
+        _require_device(q_nope, out)
+        opt = AttnOptions(num_splits, PATHS[path])
+        need = absorb_attn_workspace_size(shape, end_pos, dt, num_splits, path)
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q_nope.device)
+        self.out = out
+        self._keep = (q_nope, q_pe, kv_cache, pe_cache, wkv_b, out, workspace, shape, opt)
+        self._fn = lib.mla_absorb_attn
+        self._args = (q_nope.data_ptr(), q_pe.data_ptr(), kv_cache.data_ptr(), pe_cache.data_ptr(), wkv_b.data_ptr(),
+                      end_pos, softmax_scale, out.data_ptr(), ctypes.byref(shape), dt, ctypes.byref(opt),
+                      workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                      _stream_handle(q_nope.device))
+
+    def __call__(self):
+        _check(self._fn(*self._args))
+        return self.out
+
+
 def absorb_attn(q_nope, q_pe, kv_cache, pe_cache, wkv_b, end_pos: int, softmax_scale: float, out=None, *,
                 num_splits: int = 0, path: str = "auto", workspace=None):
     """MLA attention in absorb form on torch GPU tensors; returns out [B, S, H, Dv]."""
-    import torch
-
-    lib = load()
-    _require_device(q_nope, q_pe, kv_cache, pe_cache, wkv_b)
-    shape = attn_shape(q_nope, q_pe, kv_cache, wkv_b)
-    dt = _dtype_code(q_nope)
-    if out is None:
-        out = torch.empty((shape.batch, shape.seqlen_q, shape.n_heads, shape.v_head_dim), dtype=q_nope.dtype,
-                          device=q_nope.device)
-    _require_device(q_nope, out)
-    opt = AttnOptions(num_splits, PATHS[path])
-    need = absorb_attn_workspace_size(shape, end_pos, dt, num_splits, path)
-    if workspace is None or workspace.numel() * workspace.element_size() < need:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q_nope.device)
-    rc = lib.mla_absorb_attn(q_nope.data_ptr(), q_pe.data_ptr(), kv_cache.data_ptr(), pe_cache.data_ptr(),
-                             wkv_b.data_ptr(), end_pos, softmax_scale, out.data_ptr(), ctypes.byref(shape), dt,
-                             ctypes.byref(opt), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                             _stream_handle(q_nope.device))
-    _check(rc)
-    return out
+    return AbsorbAttnCall(q_nope, q_pe, kv_cache, pe_cache, wkv_b, end_pos, softmax_scale, out,
+                          num_splits=num_splits, path=path, workspace=workspace)()
 
 
 def expand_kv(c_kv, rms_w, wkv_b, n_heads: int, qk_nope_head_dim: int, v_head_dim: int, eps: float = 1e-6,

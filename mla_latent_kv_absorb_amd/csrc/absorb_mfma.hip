@@ -378,51 +378,65 @@ struct MergeArgs {
   int32_t splits;
 };
 
+constexpr int kMaxSplits = 4096;  // largest split count the API accepts
+
+// One workgroup per row.  The split weights exp2(m_i - M) / sum_i exp2(m_i - M) l_i are computed
+// once into LDS; then wave g sums the splits g, g+4, g+8, ... over the row's 64 16-byte chunks
+// (lane = chunk, so every split's 1 KB row is one coalesced wave load) and the four waves' sums
+// are added through LDS.
 __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
-  const int64_t gid = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  const int64_t row = gid >> 6;
-  const int ch = int(gid & 63);
-  if (row >= a.rows) return;
+  __shared__ float wts[kMaxSplits];
+  __shared__ float red[16];
+  __shared__ float part[3][64][8];
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int ch = tid & 63;
+  const int g = tid >> 6;
   const float *ml = a.part_ml + 2 * row * a.splits;
-  float M = -INFINITY;
-  for (int i = 0; i < a.splits; ++i) M = fmaxf(M, ml[2 * i]);
-  float den = 0.f;
-  for (int i = 0; i < a.splits; ++i)
-    if (ml[2 * i] != -INFINITY) den += fast_exp2(ml[2 * i] - M) * ml[2 * i + 1];
-  const float inv = 1.f / den;  // every row sees at least one position
+
+  float m = -INFINITY;
+  for (int i = tid; i < a.splits; i += 256) m = fmaxf(m, ml[2 * i]);
+  const float M = block_max(m, red);  // finite: every row sees at least one position
+  float d = 0.f;
+  for (int i = tid; i < a.splits; i += 256) {
+    const float mi = ml[2 * i];
+    const float e = (mi == -INFINITY) ? 0.f : fast_exp2(mi - M);
+    wts[i] = e;
+    d = fmaf(e, ml[2 * i + 1], d);
+  }
+  const float inv = 1.f / block_sum(d, red);  // block_sum's barriers also publish wts
+
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   const uint16_t *po = a.part_o + row * a.splits * kC + ch * 8;
-  int i = 0;
-  for (; i + 8 <= a.splits; i += 8) {
-    u32x4 v[8];
-    float w[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      v[k] = *reinterpret_cast<const u32x4 *>(po + int64_t(i + k) * kC);
-      const float mi = ml[2 * (i + k)];
-      w[k] = (mi == -INFINITY) ? 0.f : fast_exp2(mi - M) * inv;
-    }
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[2 * e] = fmaf(w[k], __uint_as_float(v[k][e] << 16), acc[2 * e]);
-        acc[2 * e + 1] = fmaf(w[k], __uint_as_float(v[k][e] & 0xffff0000u), acc[2 * e + 1]);
-      }
-  }
-  for (; i < a.splits; ++i) {
-    const u32x4 v = *reinterpret_cast<const u32x4 *>(po + int64_t(i) * kC);
-    const float mi = ml[2 * i];
-    const float w = (mi == -INFINITY) ? 0.f : fast_exp2(mi - M) * inv;
+  auto add = [&](const u32x4 &v, float w) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       acc[2 * e] = fmaf(w, __uint_as_float(v[e] << 16), acc[2 * e]);
       acc[2 * e + 1] = fmaf(w, __uint_as_float(v[e] & 0xffff0000u), acc[2 * e + 1]);
     }
+  };
+  int i = g;
+  for (; i + 12 < a.splits; i += 16) {
+    u32x4 v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = *reinterpret_cast<const u32x4 *>(po + int64_t(i + 4 * k) * kC);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) add(v[k], wts[i + 4 * k]);
   }
-  const u32x4 pk{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
-                 pack_bf16x2(acc[6], acc[7])};
-  *reinterpret_cast<u32x4 *>(a.o_lat + row * kC + ch * 8) = pk;
+  for (; i < a.splits; i += 4) add(*reinterpret_cast<const u32x4 *>(po + int64_t(i) * kC), wts[i]);
+
+  if (g) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part[g - 1][ch][e] = acc[e];
+  }
+  __syncthreads();
+  if (g == 0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = (acc[e] + part[0][ch][e] + part[1][ch][e] + part[2][ch][e]) * inv;
+    const u32x4 pk{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
+                   pack_bf16x2(acc[6], acc[7])};
+    *reinterpret_cast<u32x4 *>(a.o_lat + row * kC + ch * 8) = pk;
+  }
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -507,6 +521,10 @@ int32_t mfma_attn_splits(const AttnCall &c, int num_cus) {
 }
 
 bool mfma_attn_plan_ok(const AttnCall &c, const char **why) {
+  if (c.splits < 1 || c.splits > kMaxSplits) {
+    *why = "num_splits outside [1, 4096]";
+    return false;
+  }
   // split partials are addressed with 32-bit byte offsets
   if (c.B * c.S * c.H * int64_t(c.splits) * kC * 2 >= (int64_t(1) << 32)) {
     *why = "batch * seqlen_q * n_heads * num_splits too large for the split partials";
@@ -533,10 +551,11 @@ hipError_t mfma_absorb_attn(const AttnCall &c) {
 
   AbsorbQArgs qa{static_cast<const uint16_t *>(c.q_nope), static_cast<const uint16_t *>(c.wkv_b), q_lat, int32_t(c.H), M, 4};
   const int nrb = (M + 31) / 32;
-  timing_begin(MLA_KERNEL_ABSORB_Q, c.stream);
-  absorb_q_kernel<<<dim3(unsigned(c.H), kC / 128, unsigned((nrb + qa.row_blocks_per_wg - 1) / qa.row_blocks_per_wg)), 256,
-                    0, c.stream>>>(qa);
-  timing_end(MLA_KERNEL_ABSORB_Q, c.stream);
+  hipError_t err = launch_kernel(
+      MLA_KERNEL_ABSORB_Q, absorb_q_kernel,
+      dim3(unsigned(c.H), kC / 128, unsigned((nrb + qa.row_blocks_per_wg - 1) / qa.row_blocks_per_wg)), dim3(256), 0,
+      c.stream, qa);
+  if (err != hipSuccess) return err;
 
   AttnArgs aa{};
   aa.q_lat = q_lat;
@@ -555,25 +574,21 @@ hipError_t mfma_absorb_attn(const AttnCall &c) {
   aa.row_blocks = int32_t((c.S * c.H + kRowsWG - 1) / kRowsWG);
   aa.scale_log2 = c.scale * kLog2e;
   const int64_t nwg = c.B * int64_t(aa.splits) * aa.row_blocks;
-  timing_begin(MLA_KERNEL_ATTN, c.stream);
-  attn_kernel<<<dim3(unsigned(nwg)), 256, 0, c.stream>>>(aa);
-  timing_end(MLA_KERNEL_ATTN, c.stream);
+  err = launch_kernel(MLA_KERNEL_ATTN, attn_kernel, dim3(unsigned(nwg)), dim3(256), 0, c.stream, aa);
+  if (err != hipSuccess) return err;
 
   // split merge (skipped with one split: the attention epilogue then writes o_lat itself)
   uint16_t *o_lat = part_o;
   if (c.splits > 1) {
     o_lat = q_lat;  // q_lat is dead once the attention kernel has run
     MergeArgs ma{part_ml, part_o, o_lat, rows, c.splits};
-    timing_begin(MLA_KERNEL_MERGE, c.stream);
-    merge_kernel<<<dim3(unsigned((rows * 64 + 255) / 256)), 256, 0, c.stream>>>(ma);
-    timing_end(MLA_KERNEL_MERGE, c.stream);
+    err = launch_kernel(MLA_KERNEL_MERGE, merge_kernel, dim3(unsigned(rows)), dim3(256), 0, c.stream, ma);
+    if (err != hipSuccess) return err;
   }
   UpprojArgs ua{o_lat, static_cast<const uint16_t *>(c.wkv_b), static_cast<uint16_t *>(c.out), int32_t(c.H), M, 8};
-  timing_begin(MLA_KERNEL_UPPROJ, c.stream);
-  upproj_kernel<<<dim3(unsigned(c.H), 2, unsigned((nrb + ua.row_blocks_per_wg - 1) / ua.row_blocks_per_wg)), 128, 0,
-                  c.stream>>>(ua);
-  timing_end(MLA_KERNEL_UPPROJ, c.stream);
-  return hipGetLastError();
+  return launch_kernel(MLA_KERNEL_UPPROJ, upproj_kernel,
+                       dim3(unsigned(c.H), 2, unsigned((nrb + ua.row_blocks_per_wg - 1) / ua.row_blocks_per_wg)),
+                       dim3(128), 0, c.stream, ua);
 }
 
 }  // namespace mla

@@ -225,10 +225,8 @@ hipError_t mfma_expand_kv(const ExpandCall &c) {
   ExpandArgs a{static_cast<const uint16_t *>(c.c_kv), static_cast<const uint16_t *>(c.rms_w),
                static_cast<const uint16_t *>(c.wkv_b), static_cast<uint16_t *>(c.k_nope), static_cast<uint16_t *>(c.v),
                int32_t(c.T), int32_t(c.H), int32_t((c.T + kTT - 1) / kTT), c.eps};
-  timing_begin(MLA_KERNEL_EXPAND, c.stream);
-  expand_kernel<<<dim3(unsigned(int64_t(a.tblocks) * c.H)), 256, 0, c.stream>>>(a);
-  timing_end(MLA_KERNEL_EXPAND, c.stream);
-  return hipGetLastError();
+  return launch_kernel(MLA_KERNEL_EXPAND, expand_kernel, dim3(unsigned(int64_t(a.tblocks) * c.H)), dim3(256), 0,
+                       c.stream, a);
 }
 
 }  // namespace mla

@@ -1,6 +1,7 @@
 // Internal interface between the C-ABI layer (mla_api.cpp) and the kernel translation units.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -30,8 +31,25 @@ struct ExpandCall {
 };
 
 // ---- benchmark instrumentation (no-ops unless enabled for the kernel id) ----------------------
+// Events recorded on the stream before and after a group of launches (the plain path's kernels).
 void timing_begin(int kernel_id, hipStream_t stream);
 void timing_end(int kernel_id, hipStream_t stream);
+// Start/stop events for one launch of kernel_id (both null when its timing is off).  They are
+// handed to hipExtLaunchKernel, which stamps them with the dispatch's own start and end times.
+void timing_events(int kernel_id, hipEvent_t *start, hipEvent_t *stop);
+void timing_record(int kernel_id, hipEvent_t start, hipEvent_t stop, hipError_t launch_status);
+
+// Launch one kernel, timed per dispatch when timing is on for kernel_id; returns the launch status.
+template <typename... Params, typename... Args>
+hipError_t launch_kernel(int kernel_id, void (*kernel)(Params...), dim3 grid, dim3 block, uint32_t lds_bytes,
+                         hipStream_t stream, Args... args) {
+  hipEvent_t start = nullptr, stop = nullptr;
+  timing_events(kernel_id, &start, &stop);
+  hipExtLaunchKernelGGL(kernel, grid, block, lds_bytes, stream, start, stop, 0, args...);
+  const hipError_t e = hipGetLastError();
+  timing_record(kernel_id, start, stop, e);
+  return e;
+}
 
 // ---- plain vector-ALU path (any shape, fp32 or bf16) -------------------------------------------
 size_t plain_attn_workspace(const AttnCall &c);

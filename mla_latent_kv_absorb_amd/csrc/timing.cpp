@@ -1,4 +1,6 @@
 // Optional per-kernel HIP event timing for benchmarks (see mla_timing_enable in mla_absorb.h).
+// Single-kernel launches get events stamped by the dispatch itself (hipExtLaunchKernel); groups of
+// launches are bracketed by events recorded on the stream.
 #include <hip/hip_runtime.h>
 
 #include <vector>
@@ -74,6 +76,33 @@ void timing_end(int id, hipStream_t stream) {
     return;
   }
   t.records.push_back({id, s, e});
+}
+
+void timing_events(int id, hipEvent_t *start, hipEvent_t *stop) {
+  TimingState &t = g_timing;
+  *start = *stop = nullptr;
+  if (!(t.mask & (1u << id))) return;
+  hipEvent_t a = t.take();
+  if (!a) return;
+  hipEvent_t b = t.take();
+  if (!b) {
+    t.pool.push_back(a);
+    return;
+  }
+  *start = a;
+  *stop = b;
+}
+
+void timing_record(int id, hipEvent_t start, hipEvent_t stop, hipError_t launch_status) {
+  TimingState &t = g_timing;
+  if (!start || !stop) return;
+  if (launch_status != hipSuccess) {
+    t.failed = true;
+    t.pool.push_back(start);
+    t.pool.push_back(stop);
+    return;
+  }
+  t.records.push_back({id, start, stop});
 }
 
 }  // namespace mla
