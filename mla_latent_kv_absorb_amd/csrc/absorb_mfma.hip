@@ -4,7 +4,8 @@
 //
 // The computation is the absorb path of the page "Naive vs Absorb Attention Implementations in
 // DeepSeek-V3" (section "Absorb Path Execution"), run as up to four kernels:
-//   1. absorb_q_kernel   q_lat[row, :] = q_nope[row, :] . W_UK[h]            (query absorption)
+//   1. absorb_q_kernel   q_lat[row, :] = q_nope[row, :] . W_UK[h]            (query absorption),
+//                        stored together with q_pe in the attention kernel's operand order
 //   2. attn_kernel       per (sequence, 128-row block, position split): scores against kv_cache
 //                        (512) and pe_cache (64) as one 576-deep contraction, online softmax,
 //                        probability-weighted sum over kv_cache in latent space
@@ -52,9 +53,18 @@ __device__ __forceinline__ int pe_swz(int row) { return (row >> 1) & 7; }
 // probabilities never leave registers.
 __device__ __forceinline__ int rho(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
 
+// Absorbed query in fragment-major order, written by absorb_q_kernel and read by attn_kernel:
+// [sequence][128-row block][wave][ks = 0..35][l32][g][8 bf16].  Lane l = l32 + 32 g of wave w
+// holds row 128 rb + 32 w + l32 (rows in (s, h) order within the sequence), latent elements
+// 16 ks + 8 g .. +7 for ks < 32 and rope elements 16 (ks - 32) + 8 g .. +7 for ks >= 32.  A wave's
+// load of one ks is one contiguous 1 KB, and each row's two chunks of a ks are adjacent (32 bytes),
+// so the absorb kernel's stores complete whole 32-byte sectors.
+constexpr int kFragBytesPerWave = 36 * 1024;
+constexpr int kFragElemsPerBlock = 4 * kFragBytesPerWave / 2;
+constexpr int kQpeBytesPerWave = 4 * 1024;  // a wave's rope-query fragments, kept in LDS
+
 struct AttnArgs {
-  const uint16_t *q_lat;   // [rows, 512]
-  const uint16_t *q_pe;    // [rows, 64]
+  const uint16_t *q_frag;  // fragment-major absorbed + rope query (layout above)
   const uint16_t *kv;      // [Bmax, Tmax, 512]
   const uint16_t *pe;      // [Bmax, Tmax, 64]
   float *part_ml;          // [rows, splits, 2]   (max in log2 units, sum)
@@ -74,12 +84,14 @@ constexpr float kRescale = 8.f;
 
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 attn_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kStages * kStageBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kStages * kStageBytes + 4 * kQpeBytesPerWave];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int l32 = lane & 31, g = lane >> 5;
 
-  int bid = blockIdx.x;
+  // logical order: row block fastest, then split, then sequence; the workgroups of one sequence
+  // (which share its query rows and cache) land on one XCD
+  int bid = __builtin_amdgcn_readfirstlane(xcd_logical_id(blockIdx.x, gridDim.x));
   const int rb = __builtin_amdgcn_readfirstlane(bid % a.row_blocks);
   bid /= a.row_blocks;
   const int split = __builtin_amdgcn_readfirstlane(bid % a.splits);
@@ -102,40 +114,59 @@ attn_kernel(AttnArgs a) {
   const int wg_full = __builtin_amdgcn_readfirstlane(min(t_split_end, a.end_pos - a.S + first_row / a.H + 1));
   const int ntiles = __builtin_amdgcn_readfirstlane(wg_end > t_begin ? (wg_end - t_begin + kTile - 1) / kTile : 0);
 
-  // Absorbed query as the score B operand: lane holds q[row][16 ks + 8 g .. +7].
-  u32x4 qf[36];
-  {
-    const uint16_t *qr = a.q_lat + grow * kC + 8 * g;
-    const uint16_t *pr = a.q_pe + grow * kR + 8 * g;
-#pragma unroll
-    for (int ks = 0; ks < 32; ++ks) qf[ks] = row_ok ? *reinterpret_cast<const u32x4 *>(qr + 16 * ks) : u32x4{0, 0, 0, 0};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qf[32 + ks] = row_ok ? *reinterpret_cast<const u32x4 *>(pr + 16 * ks) : u32x4{0, 0, 0, 0};
-  }
-
   // DMA geometry.  kv: wave w moves tile rows 8w..8w+7, one 1 KB row per instruction; lane l owns
   // chunk position l and fetches source chunk swz_chunk(l, row).  pe: wave w moves rows
   // 8w..8w+7 (128 bytes each) in one instruction.  Rows past the last needed position repeat the
-  // last one (valid data, masked in the softmax).
+  // last one (valid data, masked in the softmax); wg_end >= 1, so that row always exists.
   const rsrc_t kvres = make_rsrc(a.kv + int64_t(b) * a.Tmax * kC, uint32_t(a.Tmax) * (kC * 2));
   const rsrc_t peres = make_rsrc(a.pe + int64_t(b) * a.Tmax * kR, uint32_t(a.Tmax) * (kR * 2));
-  uint32_t kv_voff[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) kv_voff[i] = uint32_t(swz_chunk(lane, 8 * (wave & 1) + i)) * 16;
   const int pe_row = wave * 8 + (lane >> 3);
   const uint32_t pe_voff = uint32_t((lane & 7) ^ pe_swz(pe_row)) * 16;
-  auto issue = [&](int j) {
+  // One of the tile's nine DMA instructions per wave: part 0..7 moves kv row 8w+part, part 8 the pe rows.
+  auto issue_part = [&](int j, int part) __attribute__((always_inline)) {
     unsigned char *st = smem + (j % kStages) * kStageBytes;
     const int t0 = t_begin + j * kTile;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int t = min(t0 + wave * 8 + i, wg_end - 1);  // wavefront-uniform
-      buf_load16_lds(kvres, st + (wave * 8 + i) * (kC * 2), kv_voff[i], uint32_t(t) * (kC * 2));
+    if (part < 8) {
+      const int t = min(t0 + wave * 8 + part, wg_end - 1);  // wavefront-uniform
+      buf_load16_lds(kvres, st + (wave * 8 + part) * (kC * 2), uint32_t(swz_chunk(lane, 8 * (wave & 1) + part)) * 16,
+                     uint32_t(t) * (kC * 2));
+    } else {
+      const int tp = min(t0 + pe_row, wg_end - 1);
+      buf_load16_lds(peres, st + kKvTileBytes + wave * 8 * (kR * 2), pe_voff + uint32_t(tp - t0) * (kR * 2),
+                     uint32_t(t0) * (kR * 2));
     }
-    const int tp = min(t0 + pe_row, wg_end - 1);
-    buf_load16_lds(peres, st + kKvTileBytes + wave * 8 * (kR * 2), pe_voff + uint32_t(tp - t0) * (kR * 2),
-                   uint32_t(t0) * (kR * 2));
   };
+  auto issue = [&](int j) __attribute__((always_inline)) {
+#pragma unroll
+    for (int part = 0; part < 9; ++part) issue_part(j, part);
+  };
+
+  // Prologue: tile 0; the absorbed query into registers and the rope query into LDS; a full wait
+  // (the query loads are the only vector loads the compiler tracks, so completing them here keeps
+  // its own vmcnt waits out of the loop body); then tile 1, always issued so that the in-loop wait
+  // counts stay exact (with a single tile it re-reads the last needed row).
+  issue(0);
+  // Absorbed query as the score B operand: lane holds q[row][16 ks + 8 g .. +7], ks < 32.
+  // absorb_q_kernel stores it fragment-major, so instruction ks of a wave reads one contiguous
+  // 1 KB; lanes past the sequence's last row read out of range and get zeros.  The rope part
+  // (ks 32..35) is copied by DMA to this wave's 4 KB of LDS in the same order.
+  u32x4 qf[32];
+  const unsigned char *qpe_lds = smem + kStages * kStageBytes + wave * kQpeBytesPerWave;
+  {
+    const rsrc_t qres = make_rsrc(a.q_frag + (int64_t(b) * a.row_blocks + rb) * kFragElemsPerBlock,
+                                  kFragElemsPerBlock * 2);
+    const uint32_t lane_slot = uint32_t(l32 * 32 + g * 16);
+    const uint32_t qoff = row_ok ? uint32_t(wave * kFragBytesPerWave) + lane_slot : 0x80000000u;
+#pragma unroll
+    for (int ks = 0; ks < 32; ++ks) qf[ks] = buf_load16(qres, qoff, ks * 1024);
+    // DMA lane l writes LDS bytes 16 l .. of the plane, so it fetches the fragment of lane slot 16 l
+    const uint32_t doff = uint32_t(wave * kFragBytesPerWave) + uint32_t(lane) * 16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      buf_load16_lds(qres, const_cast<unsigned char *>(qpe_lds) + i * 1024, doff, (32 + i) * 1024);
+  }
+  wait_vmcnt<0>();
+  issue(1);
 
   f32x16 acc[16];
 #pragma unroll
@@ -150,6 +181,7 @@ attn_kernel(AttnArgs a) {
   uint32_t pe_off[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) pe_off[i] = kKvTileBytes + uint32_t(arow) * (kR * 2) + uint32_t((2 * i + g) ^ pe_swz(arow)) * 16;
+  const uint32_t qpe_off = uint32_t(l32 * 32 + g * 16);
   // P.V A-operand (transposing) reads: source lane s16 of a 16-lane group reads row
   // 16 ks + 8 g + 4 h + s16 / 4, chunk 4 cb + 2 chalf + (s16 & 3) / 2, half (s16 & 1).
   const int s16 = lane & 15, chalf = (lane >> 4) & 1;
@@ -163,26 +195,26 @@ attn_kernel(AttnArgs a) {
       tr_off[c4][h] = uint32_t(row0) * (kC * 2) + uint32_t(swz_chunk(chunk, row0)) * 16 + (s16 & 1) * 8;
     }
 
-  for (int j = 0; j < kStages - 1 && j < ntiles; ++j) issue(j);
-
 #pragma unroll 1
   for (int j = 0; j < ntiles; ++j) {
-    // Tiles j+1 and j+2 may still be in flight; a bare s_barrier follows (a __syncthreads() fence
-    // would also wait for them).
-    const int ahead = min(ntiles - 1 - j, kStages - 2);
-    if (ahead >= 2) wait_vmcnt<2 * kLoadsPerTile>();
-    else if (ahead == 1) wait_vmcnt<kLoadsPerTile>();
+    // tile j must have landed; tile j+1 (issued one iteration ago, or in the prologue) may not
+    if (j + 1 < ntiles || j == 0) wait_vmcnt<kLoadsPerTile>();
     else wait_vmcnt<0>();
+    // after the barrier every wave is done with tile j-1, so its stage can be refilled (tile j+2
+    // goes into stage (j+2) % 4; stages of tiles j and j+1 are untouched)
     __builtin_amdgcn_s_barrier();
-    if (j + kStages - 1 < ntiles) issue(j + kStages - 1);
+    compiler_fence();
+    const bool refill = j + 2 < ntiles;  // wavefront-uniform
 
     const unsigned char *st = smem + (j % kStages) * kStageBytes;
     const int t0 = t_begin + j * kTile;
 
-    // ---- scores S^T[position][row] over the 576-wide concatenation of kv and pe
+    // ---- scores S^T[position][row] over the 576-wide concatenation of kv and pe; the nine DMA
+    // instructions of tile j+2 are spread over the MFMA groups so that a full memory queue
+    // stalls one instruction at a time
     f32x16 sacc = f32x16{};
     {
-      u32x4 fr[2][4];
+      u32x4 fr[2][4], qp[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) fr[0][i] = lds_read16(st, sc_off[i]);
 #pragma unroll
@@ -194,25 +226,29 @@ attn_kernel(AttnArgs a) {
           for (int i = 0; i < 4; ++i) fr[cur ^ 1][i] = lds_read16(st, sc_off[(k0 + i) & 7] + ((k0 + i) >> 3) * 256);
         } else if (grp + 1 == 8) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) fr[cur ^ 1][i] = lds_read16(st, pe_off[i]);
+          for (int i = 0; i < 4; ++i) {
+            fr[cur ^ 1][i] = lds_read16(st, pe_off[i]);
+            qp[i] = lds_read16(qpe_lds, qpe_off + i * 1024);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sacc = mfma32(fr[cur][i], qf[4 * grp + i], sacc);
+        for (int i = 0; i < 4; ++i) sacc = mfma32(fr[cur][i], grp < 8 ? qf[4 * grp + i] : qp[i], sacc);
+        __builtin_amdgcn_sched_barrier(0);
+        if (refill) issue_part(j + 2, grp);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
 
     // ---- online softmax (log2 domain); register r holds position 16*(r/8) + 8*g + r%8
-    const bool masked = t0 + kTile > wg_full;  // wavefront-uniform
-    float mloc = -INFINITY;
-    if (masked) {
+    if (t0 + kTile > wg_full) {  // wavefront-uniform: positions past a row's last visible one
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int t = t0 + 16 * (r >> 3) + 8 * g + (r & 7);
         if (t >= row_end) sacc[r] = -INFINITY;
       }
     }
+    float mloc = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sacc[r]);
     const float mrow = fmaxf(mloc, __shfl_xor(mloc, 32, 64)) * a.scale_log2;  // scale > 0
@@ -228,39 +264,39 @@ attn_kernel(AttnArgs a) {
         for (int r = 0; r < 16; ++r) acc[i][r] = agpr_write(agpr_read(acc[i][r]) * alpha);
     }
     const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
-    float psum = 0.f;
-    u32x4 pb[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    // probabilities of positions 0..15 (B operand of the first K half) now; those of positions
+    // 16..31 are computed while the first half's sixteen MFMAs run
+    auto probs = [&](int h) __attribute__((always_inline)) -> u32x4 {
       float p[8];
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
         p[r] = fast_exp2(fmaf(sacc[8 * h + r], a.scale_log2, -m_use));
-        psum += p[r];
+        lsum += p[r];
       }
-      pb[h] = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                    pack_bf16x2(p[6], p[7])};
-    }
-    lsum += psum;
+      return u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                   pack_bf16x2(p[6], p[7])};
+    };
+    u32x4 pb[2];
+    pb[0] = probs(0);
 
-    // ---- O^T[c][row] += KV^T[c][position] . P^T[position][row]
+    // ---- O^T[c][row] += KV^T[c][position] . P^T[position][row], first K half (positions 0..15)
+    // over all 16 column blocks, then the second half
     {
-      u32x4 fr[2][2];
+      auto trl = [&](int n, int ks) __attribute__((always_inline)) -> u32x4 {
+        return lds_read_tr_pair(st, tr_off[n & 3][0] + (n >> 2) * 256 + ks * 16384,
+                                tr_off[n & 3][1] + (n >> 2) * 256 + ks * 16384);
+      };
+      // ring of four A fragments, three MFMAs ahead
+      u32x4 fr[4];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) fr[0][ks] = lds_read_tr_pair(st, tr_off[0][0] + ks * 16384, tr_off[0][1] + ks * 16384);
+      for (int step = 0; step < 3; ++step) fr[step] = trl(step, 0);
 #pragma unroll
-      for (int cb = 0; cb < 16; ++cb) {
-        const int cur = cb & 1;
-        if (cb + 1 < 16) {
-          const int n = cb + 1;
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks)
-            fr[cur ^ 1][ks] = lds_read_tr_pair(st, tr_off[n & 3][0] + (n >> 2) * 256 + ks * 16384,
-                                               tr_off[n & 3][1] + (n >> 2) * 256 + ks * 16384);
-        }
+      for (int step = 0; step < 32; ++step) {
+        const int ks = step >> 4, cb = step & 15;
+        if (step + 3 < 32) fr[(step + 3) & 3] = trl((step + 3) & 15, (step + 3) >> 4);
         __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) acc[cb] = mfma32(fr[cur][ks], pb[ks], acc[cb]);
+        acc[cb] = mfma32(fr[step & 3], pb[ks], acc[cb]);
+        if (step == 1) pb[1] = probs(1);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -301,16 +337,26 @@ attn_kernel(AttnArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------------
-// q_lat[row, c0 + c] = sum_d q_nope[row, d] * W_UK[h][d][c0 + c] for one head h and 128 columns.
+// q_lat[row, c0 + c] = sum_d q_nope[row, d] * W_UK[h][d][c0 + c] for one head h and 128 columns,
+// written fragment-major for attn_kernel (the first column quarter also copies q_pe there).
 // W_UK is staged in LDS once ([128 d][128 c], 16-byte chunks XOR-swizzled) and read transposed,
 // because the contraction runs over d while c is the contiguous index of wkv_b.
 struct AbsorbQArgs {
   const uint16_t *q_nope;  // [rows, Dn] with rows = M * H (row = m * H + h)
+  const uint16_t *q_pe;    // [rows, 64]
   const uint16_t *wkv_b;   // [H * 256, 512]
-  uint16_t *q_lat;         // [rows, 512]
+  uint16_t *q_frag;        // fragment-major q_lat and q_pe (see kFragBytesPerWave)
   int32_t H, M;            // M = B * S query rows per head
+  int32_t S, row_blocks;   // query tokens per sequence; 128-row blocks per sequence
   int32_t row_blocks_per_wg;
 };
+
+// Byte offset of row (m, h)'s slot in the fragment buffer (add ks * 1024 + g * 16).
+__device__ __forceinline__ int64_t frag_row_offset(int m, int h, const AbsorbQArgs &a) {
+  const int b = m / a.S, lrow = (m - b * a.S) * a.H + h;
+  return ((int64_t(b) * a.row_blocks + (lrow >> 7)) * 4 + ((lrow >> 5) & 3)) * int64_t(kFragBytesPerWave) +
+         (lrow & 31) * 32;
+}
 
 // W_UK tile rows are 256 bytes (one bank period, 16 chunks).  The transposing read touches 4
 // consecutive rows x 4 chunks per 32 lanes; XOR-ing the chunk with (row & 3) << 2 puts the four
@@ -325,6 +371,8 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(AbsorbQArgs a) {
   const int h = blockIdx.x;
   const int c0 = blockIdx.y * 128;
   const int rb0 = blockIdx.z * a.row_blocks_per_wg;
+  const int nrb = (a.M + 31) / 32;
+  const int rb_end = min(nrb, rb0 + a.row_blocks_per_wg);
 
   // stage W_UK[h][0:128][c0:c0+128]: each wave instruction moves 4 rows of 256 bytes; within it the
   // lane's row is lane / 16 and its chunk position lane % 16 (source chunk swizzled by the row)
@@ -333,34 +381,61 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(AbsorbQArgs a) {
 #pragma unroll
   for (int i = 0; i < 8; ++i)
     buf_load16_lds(wres, wt + (wave * 8 + i) * 1024, w_voff, uint32_t((wave * 8 + i) * 4) * (kC * 2) + c0 * 2);
+
+  // q_nope rows of head h as the MFMA B operand (lane: row m = 32 rb + l32, elements 16 ks + 8 g ..),
+  // loaded while the W tile is in flight; rows past M read out of range and give zeros
+  const rsrc_t xres = make_rsrc(a.q_nope, uint32_t(int64_t(a.M) * a.H * kDn * 2));
+  auto load_x = [&](int rb, u32x4 (&x)[kDn / 16]) {
+    const int m = rb * 32 + l32;
+    const uint32_t off = m < a.M ? uint32_t((int64_t(m) * a.H + h) * (kDn * 2)) + 16 * g : 0x80000000u;
+#pragma unroll
+    for (int ks = 0; ks < kDn / 16; ++ks) x[ks] = buf_load16(xres, off, 32 * ks);
+  };
+  u32x4 xn[kDn / 16];
+  if (rb0 < rb_end) load_x(rb0, xn);
   wait_vmcnt<0>();
   __syncthreads();
 
   const int s16 = lane & 15, chalf = (lane >> 4) & 1;
-  const int nrb = (a.M + 31) / 32;
-  for (int rb = rb0; rb < min(nrb, rb0 + a.row_blocks_per_wg); ++rb) {
+  for (int rb = rb0; rb < rb_end; ++rb) {
     const int m = rb * 32 + l32;
     const bool ok = m < a.M;
-    const uint16_t *xr = a.q_nope + (int64_t(m) * a.H + h) * kDn + 8 * g;
+    u32x4 xc[kDn / 16];
+#pragma unroll
+    for (int ks = 0; ks < kDn / 16; ++ks) xc[ks] = xn[ks];
+    if (rb + 1 < rb_end) load_x(rb + 1, xn);  // prefetch the next row block
     f32x16 d = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < kDn / 16; ++ks) {
-      const u32x4 bf = ok ? *reinterpret_cast<const u32x4 *>(xr + 16 * ks) : u32x4{0, 0, 0, 0};
       const int row0 = 16 * ks + 8 * g + (s16 >> 2);
       const int chunk = 4 * wave + 2 * chalf + ((s16 & 3) >> 1);
       const int within = (s16 & 1) * 8;
       const uint32_t off0 = row0 * 256 + (chunk ^ w_swz(row0)) * 16 + within;
       const uint32_t off1 = (row0 + 4) * 256 + (chunk ^ w_swz(row0 + 4)) * 16 + within;
       const u32x4 af = lds_read_tr_pair(wt, off0, off1);
-      d = mfma32(af, bf, d);
+      d = mfma32(af, xc[ks], d);
     }
-    // D^T[c][m]: lane holds column m, c = 32 wave + 8 (r/4) + 4 g + r % 4
+    // D^T[c][m]: lane holds column m, c = 32 wave + 8 (r/4) + 4 g + r % 4; the four elements of
+    // register group q are half of the 16-byte chunk (c0 + 32 wave + 8 q) / 8 of the row
     if (ok) {
-      uint16_t *dst = a.q_lat + (int64_t(m) * a.H + h) * kC + c0 + 32 * wave + 4 * g;
+      unsigned char *dst = reinterpret_cast<unsigned char *>(a.q_frag) + frag_row_offset(m, h, a) + 8 * g;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
+        const int chunk = c0 / 8 + 4 * wave + q;
         const u32x2 v{pack_bf16x2(d[4 * q], d[4 * q + 1]), pack_bf16x2(d[4 * q + 2], d[4 * q + 3])};
-        *reinterpret_cast<u32x2 *>(dst + 8 * q) = v;
+        *reinterpret_cast<u32x2 *>(dst + (chunk >> 1) * 1024 + (chunk & 1) * 16) = v;
+      }
+    }
+  }
+  // the first column quarter also moves the rope query rows of its row blocks into place
+  if (blockIdx.y == 0) {
+    const int r = threadIdx.x >> 3, chunk = threadIdx.x & 7;
+    for (int rb = rb0; rb < min(nrb, rb0 + a.row_blocks_per_wg); ++rb) {
+      const int m = rb * 32 + r;
+      if (m < a.M) {
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(a.q_pe + (int64_t(m) * a.H + h) * kR + chunk * 8);
+        *reinterpret_cast<u32x4 *>(reinterpret_cast<unsigned char *>(a.q_frag) + frag_row_offset(m, h, a) +
+                                   (32 + (chunk >> 1)) * 1024 + (chunk & 1) * 16) = v;
       }
     }
   }
@@ -535,21 +610,28 @@ bool mfma_attn_plan_ok(const AttnCall &c, const char **why) {
 
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Workspace: [query fragments (later reused for the merged o_lat rows)] [split m, l] [split o].
+static size_t q_region_bytes(const AttnCall &c) {
+  const size_t row_blocks = size_t((c.S * c.H + kRowsWG - 1) / kRowsWG);
+  return align256(size_t(c.B) * row_blocks * 4 * kFragBytesPerWave);  // >= rows * 1 KB of o_lat
+}
+
 size_t mfma_attn_workspace(const AttnCall &c) {
   const size_t rows = size_t(c.B * c.S * c.H);
-  return align256(rows * kC * 2) + align256(rows * size_t(c.splits) * 2 * 4) + align256(rows * size_t(c.splits) * kC * 2);
+  return q_region_bytes(c) + align256(rows * size_t(c.splits) * 2 * 4) + align256(rows * size_t(c.splits) * kC * 2);
 }
 
 hipError_t mfma_absorb_attn(const AttnCall &c) {
   const int64_t rows = c.B * c.S * c.H;
   unsigned char *ws = static_cast<unsigned char *>(c.ws);
-  uint16_t *q_lat = reinterpret_cast<uint16_t *>(ws);
-  float *part_ml = reinterpret_cast<float *>(ws + align256(size_t(rows) * kC * 2));
-  uint16_t *part_o = reinterpret_cast<uint16_t *>(ws + align256(size_t(rows) * kC * 2) +
-                                                  align256(size_t(rows) * c.splits * 2 * 4));
+  uint16_t *q_frag = reinterpret_cast<uint16_t *>(ws);
+  float *part_ml = reinterpret_cast<float *>(ws + q_region_bytes(c));
+  uint16_t *part_o = reinterpret_cast<uint16_t *>(ws + q_region_bytes(c) + align256(size_t(rows) * c.splits * 2 * 4));
   const int32_t M = int32_t(c.B * c.S);
+  const int32_t row_blocks = int32_t((c.S * c.H + kRowsWG - 1) / kRowsWG);
 
-  AbsorbQArgs qa{static_cast<const uint16_t *>(c.q_nope), static_cast<const uint16_t *>(c.wkv_b), q_lat, int32_t(c.H), M, 4};
+  AbsorbQArgs qa{static_cast<const uint16_t *>(c.q_nope), static_cast<const uint16_t *>(c.q_pe),
+                 static_cast<const uint16_t *>(c.wkv_b), q_frag, int32_t(c.H), M, int32_t(c.S), row_blocks, 4};
   const int nrb = (M + 31) / 32;
   hipError_t err = launch_kernel(
       MLA_KERNEL_ABSORB_Q, absorb_q_kernel,
@@ -558,8 +640,7 @@ hipError_t mfma_absorb_attn(const AttnCall &c) {
   if (err != hipSuccess) return err;
 
   AttnArgs aa{};
-  aa.q_lat = q_lat;
-  aa.q_pe = static_cast<const uint16_t *>(c.q_pe);
+  aa.q_frag = q_frag;
   aa.kv = static_cast<const uint16_t *>(c.kv);
   aa.pe = static_cast<const uint16_t *>(c.pe);
   aa.part_ml = part_ml;
@@ -571,7 +652,7 @@ hipError_t mfma_absorb_attn(const AttnCall &c) {
   aa.end_pos = int32_t(c.end_pos);
   aa.splits = c.splits;
   aa.split_len = int32_t(c.split_len);
-  aa.row_blocks = int32_t((c.S * c.H + kRowsWG - 1) / kRowsWG);
+  aa.row_blocks = row_blocks;
   aa.scale_log2 = c.scale * kLog2e;
   const int64_t nwg = c.B * int64_t(aa.splits) * aa.row_blocks;
   err = launch_kernel(MLA_KERNEL_ATTN, attn_kernel, dim3(unsigned(nwg)), dim3(256), 0, c.stream, aa);
@@ -580,7 +661,7 @@ hipError_t mfma_absorb_attn(const AttnCall &c) {
   // split merge (skipped with one split: the attention epilogue then writes o_lat itself)
   uint16_t *o_lat = part_o;
   if (c.splits > 1) {
-    o_lat = q_lat;  // q_lat is dead once the attention kernel has run
+    o_lat = q_frag;  // the query fragments are dead once the attention kernel has run
     MergeArgs ma{part_ml, part_o, o_lat, rows, c.splits};
     err = launch_kernel(MLA_KERNEL_MERGE, merge_kernel, dim3(unsigned(rows)), dim3(256), 0, c.stream, ma);
     if (err != hipSuccess) return err;

@@ -69,9 +69,34 @@ __device__ __forceinline__ void buf_store8(rsrc_t r, const u32x2 &v, uint32_t vo
 }
 // 16 bytes per lane from a buffer straight into LDS: lane l's bytes land at lds_base + 16 * l
 // (lds_base is wavefront-uniform and goes through M0).
+//
+// Issued as inline asm rather than through __builtin_amdgcn_raw_ptr_buffer_load_lds: the compiler
+// treats the builtin as a pending write to all of LDS and puts s_waitcnt vmcnt(0) in front of every
+// later ds_read_b64_tr_b16, which drains every prefetched tile.  The load has no register result;
+// callers order it with explicit wait_vmcnt<N>() and barriers before reading the destination, and
+// the "memory" clobber keeps the compiler from moving LDS accesses across it.  Because the
+// compiler does not count these loads, a kernel must not leave compiler-visible vector loads
+// pending across them into code that relies on the compiler's own vmcnt waits (complete such
+// loads with wait_vmcnt<0>() first).
 __device__ __forceinline__ void buf_load16_lds(rsrc_t r, unsigned char *lds_base, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (MLA_LDS void *)(lds_base), 16, voff, soff, 0, 0);
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>((MLA_LDS void *)lds_base)));
+  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(r), "s"(soff), "{m0}"(m0) : "memory");
 }
+
+// Workgroup order for an 8-XCD part.  Workgroups are handed to the XCDs round-robin by id, so
+// ids x, x+8, x+16, ... run on XCD x and share its L2.  This maps the hardware id to a logical
+// id such that XCD x receives one contiguous range of logical ids: workgroups that are adjacent
+// in logical order (and read the same data) then share an L2.  It is a bijection on [0, n) for
+// any n; only performance depends on the dispatch order being as assumed.
+__device__ __forceinline__ int xcd_logical_id(int hw_id, int n) {
+  const int x = hw_id & 7, k = hw_id >> 3;
+  const int base = n >> 3, rem = n & 7;
+  return x * base + (x < rem ? x : rem) + k;
+}
+
+// Compiler-level memory barrier (no instruction): keeps LDS reads of a staged tile after the
+// s_barrier that publishes it.
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
 // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
 template <int N>
