@@ -146,11 +146,10 @@ int32_t mla_expand_kv(const void *c_kv, const void *rms_w, const void *wkv_b, vo
  * failed (the affected launches are then missing from the totals). */
 #define MLA_KERNEL_ABSORB_Q 0 /* query absorption through W_UK                 */
 #define MLA_KERNEL_ATTN 1     /* split-KV scores, softmax, latent sum           */
-#define MLA_KERNEL_MERGE 2    /* merge of the split partials                     */
-#define MLA_KERNEL_UPPROJ 3   /* projection out through W_UV                     */
-#define MLA_KERNEL_EXPAND 4   /* RMSNorm + projection + head-major split        */
-#define MLA_KERNEL_PLAIN 5    /* any kernel of the plain vector-ALU path        */
-#define MLA_NUM_KERNELS 6
+#define MLA_KERNEL_COMBINE 2  /* split combine + projection out through W_UV    */
+#define MLA_KERNEL_EXPAND 3   /* RMSNorm + projection + head-major split        */
+#define MLA_KERNEL_PLAIN 4    /* any kernel of the plain vector-ALU path        */
+#define MLA_NUM_KERNELS 5
 
 int32_t mla_timing_enable(uint32_t kernel_mask);
 int32_t mla_timing_collect(int32_t launches[MLA_NUM_KERNELS], double ms[MLA_NUM_KERNELS]);

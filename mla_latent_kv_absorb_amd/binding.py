@@ -32,7 +32,7 @@ PATHS = {"auto": 0, "plain": 1, "mfma": 2}
 EXPORTED = ("mla_absorb_attn", "mla_absorb_attn_workspace_size", "mla_expand_kv", "mla_strerror",
             "mla_last_error", "mla_timing_enable", "mla_timing_collect", "mla_kernel_name")
 
-NUM_KERNELS = 6  # MLA_NUM_KERNELS
+NUM_KERNELS = 5  # MLA_NUM_KERNELS
 
 
 class AttnShape(ctypes.Structure):

@@ -3,17 +3,18 @@
 // fp32 accumulation.
 //
 // The computation is the absorb path of the page "Naive vs Absorb Attention Implementations in
-// DeepSeek-V3" (section "Absorb Path Execution"), run as up to four kernels:
+// DeepSeek-V3" (section "Absorb Path Execution"), run as three kernels:
 //   1. absorb_q_kernel   q_lat[row, :] = q_nope[row, :] . W_UK[h]            (query absorption),
 //                        stored together with q_pe in the attention kernel's operand order
 //   2. attn_kernel       per (sequence, 128-row block, position split): scores against kv_cache
 //                        (512) and pe_cache (64) as one 576-deep contraction, online softmax,
 //                        probability-weighted sum over kv_cache in latent space
-//   3. merge_kernel      combine the split partials (rescaled by exp2(m_i - M)); skipped when
-//                        there is a single split
-//   4. upproj_kernel     project out through W_UV[h]
+//   3. combine_kernel    combine the split partials (rescaled by exp2(m_i - M)) and project out
+//                        through W_UV[h]
 // Rows are the B*S*H query rows in (b, s, h) order.  Every kv/pe row of a split is read from HBM
 // once per 128-row block and shared through LDS by all of the block's heads.
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 #include "mfma_common.h"
@@ -305,7 +306,7 @@ attn_kernel(AttnArgs a) {
   // ---- partial state of this split: max (log2 units), sum, unnormalised o.  o goes through LDS
   // so that every global store writes one whole 1 KB row.
   lsum += __shfl_xor(lsum, 32, 64);
-  // with a single split the result is final: normalise here and skip the merge
+  // with a single split the result is final: normalise here (the combine kernel then only projects)
   const float oscale = (a.splits == 1 && lsum > 0.f) ? 1.f / lsum : 1.f;
   wait_vmcnt<0>();
   __syncthreads();  // every wave is done with the tiles
@@ -441,132 +442,164 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(AbsorbQArgs a) {
   }
 }
 
-// ------------------------------------------------------------------------------------------------
-// Split merge: o_lat[row, :] = sum_i w_i o_i[row, :] with w_i = exp2(m_i - M) / sum_i exp2(m_i - M) l_i
-// (zero for a split that saw no position).  One thread per (row, 16-byte chunk); its split loads
-// are independent, so the whole grid keeps them in flight together.
-struct MergeArgs {
-  const float *part_ml;    // [rows, splits, 2]
-  const uint16_t *part_o;  // [rows, splits, 512]
-  uint16_t *o_lat;         // [rows, 512]
-  int64_t rows;
-  int32_t splits;
-};
-
 constexpr int kMaxSplits = 4096;  // largest split count the API accepts
 
-// One workgroup per row.  The split weights exp2(m_i - M) / sum_i exp2(m_i - M) l_i are computed
-// once into LDS; then wave g sums the splits g, g+4, g+8, ... over the row's 64 16-byte chunks
-// (lane = chunk, so every split's 1 KB row is one coalesced wave load) and the four waves' sums
-// are added through LDS.
-__global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
-  __shared__ float wts[kMaxSplits];
-  __shared__ float red[16];
-  __shared__ float part[3][64][8];
-  const int64_t row = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int ch = tid & 63;
-  const int g = tid >> 6;
-  const float *ml = a.part_ml + 2 * row * a.splits;
-
-  float m = -INFINITY;
-  for (int i = tid; i < a.splits; i += 256) m = fmaxf(m, ml[2 * i]);
-  const float M = block_max(m, red);  // finite: every row sees at least one position
-  float d = 0.f;
-  for (int i = tid; i < a.splits; i += 256) {
-    const float mi = ml[2 * i];
-    const float e = (mi == -INFINITY) ? 0.f : fast_exp2(mi - M);
-    wts[i] = e;
-    d = fmaf(e, ml[2 * i + 1], d);
-  }
-  const float inv = 1.f / block_sum(d, red);  // block_sum's barriers also publish wts
-
-  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  const uint16_t *po = a.part_o + row * a.splits * kC + ch * 8;
-  auto add = [&](const u32x4 &v, float w) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc[2 * e] = fmaf(w, __uint_as_float(v[e] << 16), acc[2 * e]);
-      acc[2 * e + 1] = fmaf(w, __uint_as_float(v[e] & 0xffff0000u), acc[2 * e + 1]);
-    }
-  };
-  int i = g;
-  for (; i + 12 < a.splits; i += 16) {
-    u32x4 v[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) v[k] = *reinterpret_cast<const u32x4 *>(po + int64_t(i + 4 * k) * kC);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) add(v[k], wts[i + 4 * k]);
-  }
-  for (; i < a.splits; i += 4) add(*reinterpret_cast<const u32x4 *>(po + int64_t(i) * kC), wts[i]);
-
-  if (g) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) part[g - 1][ch][e] = acc[e];
-  }
-  __syncthreads();
-  if (g == 0) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = (acc[e] + part[0][ch][e] + part[1][ch][e] + part[2][ch][e]) * inv;
-    const u32x4 pk{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
-                   pack_bf16x2(acc[6], acc[7])};
-    *reinterpret_cast<u32x4 *>(a.o_lat + row * kC + ch * 8) = pk;
-  }
-}
-
 // ------------------------------------------------------------------------------------------------
-// out[row, e] = sum_c o_lat[row, c] * W_UV[h][e][c] for the rows of head h.  Two waves per
-// workgroup, each owning 32 of the workgroup's 64 output columns e; the W_UV rows stay in
-// registers while the workgroup walks its 32-row blocks (o_lat rows staged in LDS).
-struct UpprojArgs {
-  const uint16_t *o_lat;   // [rows, 512], row = m * H + h
-  const uint16_t *wkv_b;
+// Split combine and projection out through W_UV in one kernel:
+//   o_lat[row, :] = sum_i exp2(m_i - M) o_i[row, :] / sum_i exp2(m_i - M) l_i
+//   out[row, e]   = sum_c o_lat[row, c] * W_UV[h][e][c]
+// A workgroup owns head h and a range of 16-row groups of m.  W_UV[h] (128 rows of 1 KB) is staged
+// in LDS by DMA once; for each group the workgroup combines the split partials of its rows into a
+// bf16 tile in LDS, then each wave computes 32 output columns e for the 16 rows with 16x16x32 MFMAs
+// (D^T[e][m] = W[e][:] . o[m][:]).  LDS rows of 1 KB are read 16 rows x one 16-byte chunk at a
+// time, so chunks are XOR-swizzled inside their 256-byte group by (row & 15).
+struct CombineArgs {
+  const float *part_ml;    // [rows, splits, 2] (max in log2 units, sum)
+  const uint16_t *part_o;  // [rows, splits, 512]
+  const uint16_t *wkv_b;   // [H * 256, 512]
   uint16_t *out;           // [rows, 128]
-  int32_t H, M, row_blocks_per_wg;
+  int32_t H, M, splits;    // rows = M * H, row = m * H + h
+  int32_t wgs_per_head, groups_per_wg;
 };
 
-__global__ void __launch_bounds__(128) upproj_kernel(UpprojArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned char ol[32 * kC * 2];  // 32 KB
+constexpr int kCombineRows = 16;
+constexpr int kCombineLoads = 16;  // partial-row loads a wave keeps in flight
+
+__device__ __forceinline__ uint32_t row_swz16(int row, int chunk) {
+  return uint32_t(row) * 1024 + uint32_t((chunk & ~15) | ((chunk & 15) ^ (row & 15))) * 16;
+}
+
+// kSingle: one split, whose partial the attention kernel already normalised; the rows are copied
+// into the tile four at a time per wave.
+template <bool kSingle>
+__global__ void __launch_bounds__(256) combine_kernel(CombineArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char wl[kDv * kC * 2];            // 128 KB
+  __shared__ __attribute__((aligned(16))) unsigned char ol[kCombineRows * kC * 2];   // 16 KB
+  __shared__ float mstat[kCombineRows][2];                                           // M, 1 / den
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int l32 = lane & 31, g = lane >> 5;
-  const int h = blockIdx.x;
-  const int e0 = blockIdx.y * 64 + 32 * wave;
-  const int rb0 = blockIdx.z * a.row_blocks_per_wg;
-  const int nrb = (a.M + 31) / 32;
+  // the workgroups of one head share W_UV[h] and sit on one XCD
+  const int lid = __builtin_amdgcn_readfirstlane(xcd_logical_id(blockIdx.x, gridDim.x));
+  const int h = lid / a.wgs_per_head;
+  const int groups = (a.M + kCombineRows - 1) / kCombineRows;
+  const int g_begin = (lid - h * a.wgs_per_head) * a.groups_per_wg;
+  const int g_end = min(groups, g_begin + a.groups_per_wg);
 
-  // W_UV[h] rows e0 + l32 as the B operand: lane holds W[e][16 ks + 8 g .. +7]
-  u32x4 wf[32];
+  // W_UV[h] -> LDS: wave w moves rows 32 w .. 32 w + 31, lane p lands at chunk position p of the
+  // row and so fetches the chunk stored there
   {
     const rsrc_t wres = make_rsrc(a.wkv_b + (int64_t(h) * (kDn + kDv) + kDn) * kC, kDv * kC * 2);
-    const uint32_t voff = uint32_t(e0 + l32) * (kC * 2) + 16 * g;
-#pragma unroll
-    for (int ks = 0; ks < 32; ++ks) wf[ks] = buf_load16(wres, voff, ks * 32);
+    for (int i = 0; i < 32; ++i) {
+      const int e = wave * 32 + i;
+      const uint32_t src_chunk = uint32_t((lane & ~15) | ((lane & 15) ^ (e & 15)));
+      buf_load16_lds(wres, wl + e * 1024, src_chunk * 16, uint32_t(e) * 1024);
+    }
   }
-  for (int rb = rb0; rb < min(nrb, rb0 + a.row_blocks_per_wg); ++rb) {
-    // stage 32 o_lat rows: wave w copies rows w, w+2, ...; lane = 16-byte chunk (swizzled by row)
-#pragma unroll 4
-    for (int r = wave; r < 32; r += 2) {
-      const int m = min(rb * 32 + r, a.M - 1);
-      const u32x4 v = *reinterpret_cast<const u32x4 *>(a.o_lat + (int64_t(m) * a.H + h) * kC + lane * 8);
-      lds_write16(ol, uint32_t(r) * (kC * 2) + uint32_t((lane & ~15) | ((lane & 15) ^ (r & 15))) * 16, v);
+
+  const int l16 = lane & 15, q = lane >> 4;
+#pragma unroll 1
+  for (int grp = g_begin; grp < g_end; ++grp) {
+    const int m0 = grp * kCombineRows;
+    const int nrows = min(kCombineRows, a.M - m0);
+    // per-row maximum and denominator: 16 lanes per row, each over splits k, k + 16, ...
+    if (!kSingle) {
+      const int r = threadIdx.x >> 4, k = threadIdx.x & 15;
+      if (r < nrows) {
+        const float *ml = a.part_ml + (int64_t(m0 + r) * a.H + h) * a.splits * 2;
+        float mx = -INFINITY;
+        for (int i = k; i < a.splits; i += 16) mx = fmaxf(mx, ml[2 * i]);
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 16));
+        float den = 0.f;
+        for (int i = k; i < a.splits; i += 16)
+          if (ml[2 * i] != -INFINITY) den += fast_exp2(ml[2 * i] - mx) * ml[2 * i + 1];
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1) den += __shfl_xor(den, o, 16);
+        if (k == 0) {
+          mstat[r][0] = mx;  // finite: every row sees at least one position
+          mstat[r][1] = 1.f / den;
+        }
+      }
     }
     __syncthreads();
-    f32x16 d = f32x16{};
+
+    if (kSingle) {
+      u32x4 v[4];
 #pragma unroll
-    for (int ks = 0; ks < 32; ++ks) {
-      const int q = 2 * ks + g;
-      const u32x4 af = lds_read16(ol, uint32_t(l32) * (kC * 2) + uint32_t((q & ~15) | ((q & 15) ^ (l32 & 15))) * 16);
-      d = mfma32(af, wf[ks], d);
-    }
-    __syncthreads();  // ol is rewritten by the next row block
-    // D[row][e]: lane holds e = e0 + l32, rows 8 (r/4) + 4 g + r % 4
+      for (int k = 0; k < 4; ++k) {
+        const int r = min(wave + 4 * k, nrows - 1);
+        v[k] = *reinterpret_cast<const u32x4 *>(a.part_o + (int64_t(m0 + r) * a.H + h) * kC + lane * 8);
+      }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int mm = rb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-      if (mm < a.M) a.out[(int64_t(mm) * a.H + h) * kDv + e0 + l32] = f32_to_bf16(d[r]);
+      for (int k = 0; k < 4; ++k)
+        if (wave + 4 * k < nrows) lds_write16(ol, row_swz16(wave + 4 * k, lane), v[k]);
     }
+    // combine: wave w takes rows w, w + 4, w + 8, w + 12; lane = 16-byte chunk of the row; up to
+    // kCombineLoads split rows in flight
+#pragma unroll 1
+    for (int r = wave; r < (kSingle ? 0 : nrows); r += 4) {
+      const int64_t row = int64_t(m0 + r) * a.H + h;
+      const float *ml = a.part_ml + row * a.splits * 2;
+      const uint16_t *po = a.part_o + row * a.splits * kC + lane * 8;
+      const float mx = mstat[r][0], inv = mstat[r][1];
+      float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      auto add = [&](const u32x4 &v, float mi) __attribute__((always_inline)) {
+        const float w = (mi == -INFINITY) ? 0.f : fast_exp2(mi - mx);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] = fmaf(w, __uint_as_float(v[e] << 16), acc[2 * e]);
+          acc[2 * e + 1] = fmaf(w, __uint_as_float(v[e] & 0xffff0000u), acc[2 * e + 1]);
+        }
+      };
+      int i = 0;
+      for (; i + kCombineLoads <= a.splits; i += kCombineLoads) {
+        u32x4 v[kCombineLoads];
+#pragma unroll
+        for (int k = 0; k < kCombineLoads; ++k) v[k] = *reinterpret_cast<const u32x4 *>(po + int64_t(i + k) * kC);
+#pragma unroll
+        for (int k = 0; k < kCombineLoads; ++k) add(v[k], ml[2 * (i + k)]);
+      }
+      for (; i + 4 <= a.splits; i += 4) {
+        u32x4 v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = *reinterpret_cast<const u32x4 *>(po + int64_t(i + k) * kC);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) add(v[k], ml[2 * (i + k)]);
+      }
+      for (; i < a.splits; ++i) add(*reinterpret_cast<const u32x4 *>(po + int64_t(i) * kC), ml[2 * i]);
+      const u32x4 pk{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
+                     pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)};
+      lds_write16(ol, row_swz16(r, lane), pk);
+    }
+    if (grp == g_begin) wait_vmcnt<0>();  // W_UV rows (LDS DMA) before the first use
+    __syncthreads();
+
+    // D^T[e][m] for e in 32 wave + 16 blk + 0..15: A = W rows (lane: row l % 16, chunk 4 ks + l / 16),
+    // B = o rows (lane: row l % 16, same chunk); tile rows past nrows hold stale data and their
+    // columns are not stored
+    f32x4 d[2] = {f32x4{}, f32x4{}};
+#pragma unroll
+    for (int ks = 0; ks < kC / 32; ++ks) {
+      const int chunk = 4 * ks + q;
+      const u32x4 bo = lds_read16(ol, row_swz16(l16, chunk));
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        const u32x4 aw = lds_read16(wl, row_swz16(32 * wave + 16 * blk + l16, chunk));
+        d[blk] = mfma16(aw, bo, d[blk]);
+      }
+    }
+    // lane holds D^T[e = 32 wave + 16 blk + 4 q + r][m = m0 + l16], r = 0..3: four consecutive e
+    if (l16 < nrows) {
+      uint16_t *dst = a.out + (int64_t(m0 + l16) * a.H + h) * kDv + 32 * wave + 4 * q;
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        const u32x2 v{pack_bf16x2(d[blk][0], d[blk][1]), pack_bf16x2(d[blk][2], d[blk][3])};
+        *reinterpret_cast<u32x2 *>(dst + 16 * blk) = v;
+      }
+    }
+    __syncthreads();  // ol and mstat are rewritten by the next group
   }
+  wait_vmcnt<0>();  // a workgroup without rows still lets its W_UV DMA land before it exits
 }
 
 }  // namespace
@@ -610,10 +643,10 @@ bool mfma_attn_plan_ok(const AttnCall &c, const char **why) {
 
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Workspace: [query fragments (later reused for the merged o_lat rows)] [split m, l] [split o].
+// Workspace: [query fragments] [split m, l] [split o].
 static size_t q_region_bytes(const AttnCall &c) {
   const size_t row_blocks = size_t((c.S * c.H + kRowsWG - 1) / kRowsWG);
-  return align256(size_t(c.B) * row_blocks * 4 * kFragBytesPerWave);  // >= rows * 1 KB of o_lat
+  return align256(size_t(c.B) * row_blocks * 4 * kFragBytesPerWave);
 }
 
 size_t mfma_attn_workspace(const AttnCall &c) {
@@ -658,18 +691,15 @@ hipError_t mfma_absorb_attn(const AttnCall &c) {
   err = launch_kernel(MLA_KERNEL_ATTN, attn_kernel, dim3(unsigned(nwg)), dim3(256), 0, c.stream, aa);
   if (err != hipSuccess) return err;
 
-  // split merge (skipped with one split: the attention epilogue then writes o_lat itself)
-  uint16_t *o_lat = part_o;
-  if (c.splits > 1) {
-    o_lat = q_frag;  // the query fragments are dead once the attention kernel has run
-    MergeArgs ma{part_ml, part_o, o_lat, rows, c.splits};
-    err = launch_kernel(MLA_KERNEL_MERGE, merge_kernel, dim3(unsigned(rows)), dim3(256), 0, c.stream, ma);
-    if (err != hipSuccess) return err;
-  }
-  UpprojArgs ua{o_lat, static_cast<const uint16_t *>(c.wkv_b), static_cast<uint16_t *>(c.out), int32_t(c.H), M, 8};
-  return launch_kernel(MLA_KERNEL_UPPROJ, upproj_kernel,
-                       dim3(unsigned(c.H), 2, unsigned((nrb + ua.row_blocks_per_wg - 1) / ua.row_blocks_per_wg)),
-                       dim3(128), 0, c.stream, ua);
+  // split combine and W_UV projection: enough workgroups per head to fill the chip, each reusing
+  // its W_UV[h] copy in LDS over up to groups_per_wg 16-row groups
+  const int groups = (M + kCombineRows - 1) / kCombineRows;
+  const int per_head = int(std::max<int64_t>(1, std::min<int64_t>(groups, (512 + c.H - 1) / c.H)));
+  CombineArgs ca{part_ml, part_o, static_cast<const uint16_t *>(c.wkv_b), static_cast<uint16_t *>(c.out),
+                 int32_t(c.H), M, c.splits, per_head, (groups + per_head - 1) / per_head};
+  const dim3 grid(unsigned(int64_t(c.H) * per_head));
+  return c.splits == 1 ? launch_kernel(MLA_KERNEL_COMBINE, combine_kernel<true>, grid, dim3(256), 0, c.stream, ca)
+                       : launch_kernel(MLA_KERNEL_COMBINE, combine_kernel<false>, grid, dim3(256), 0, c.stream, ca);
 }
 
 }  // namespace mla

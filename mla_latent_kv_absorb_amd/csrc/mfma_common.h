@@ -21,6 +21,7 @@ namespace mla {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) short s16x4;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
@@ -29,6 +30,15 @@ typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
 
 __device__ __forceinline__ f32x16 mfma32(const u32x4 &a, const u32x4 &b, const f32x16 &c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
+}
+
+// v_mfma_f32_16x16x32_bf16 computes D[16x16] += A[16x32] * B[32x16] per wavefront:
+//   A operand: lane l holds A[l % 16][8 * (l / 16) + j], j = 0..7
+//   B operand: lane l holds B[8 * (l / 16) + j][l % 16]
+//   D:         lane l, register r holds D[4 * (l / 16) + r][l % 16]
+__device__ __forceinline__ f32x4 mfma16(const u32x4 &a, const u32x4 &b, const f32x4 &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
                                                  0, 0, 0);
 }
 

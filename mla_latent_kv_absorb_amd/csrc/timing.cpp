@@ -141,8 +141,7 @@ const char *mla_kernel_name(int32_t id) {
   switch (id) {
     case MLA_KERNEL_ABSORB_Q: return "absorb_q";
     case MLA_KERNEL_ATTN: return "attn";
-    case MLA_KERNEL_MERGE: return "merge";
-    case MLA_KERNEL_UPPROJ: return "upproj";
+    case MLA_KERNEL_COMBINE: return "combine";
     case MLA_KERNEL_EXPAND: return "expand";
     case MLA_KERNEL_PLAIN: return "plain";
     default: return "";
