@@ -12,11 +12,12 @@ than the 256 MB Infinity Cache, the timed steps rotate over several complete inp
 kernel runs ahead of every timed region, so the host has queued all timed steps before the GPU
 reaches them: the figure is back-to-back GPU time, not Python launch overhead.
 
-Prints ONE JSON line.  `value` is microseconds per step (lower is better).  `roofline` reports
-the dominant kernel (the attention kernel) against HBM bandwidth: algorithmic bytes per launch
-(the kv and pe cache rows it must read plus the rope query) over its average duration, measured
-during the timed steps with HIP events that the kernel's own dispatch stamps on its stream
-(hipExtLaunchKernel start/stop events).
+Prints ONE JSON line.  `value` is microseconds per step (lower is better), from timed steps that
+carry no per-kernel events.  `roofline` reports the dominant kernel (the attention kernel) against
+HBM bandwidth: algorithmic bytes per launch (the kv and pe cache rows it must read plus the rope
+query) over its average duration, measured live by running the same timed steps again with HIP
+events that the kernel's own dispatch stamps on its stream (hipExtLaunchKernel start/stop events);
+those events add a queue barrier per timed dispatch, so that pass's step time is reported apart.
 `cpu_baseline` times the CPU oracle (NumPy, float64) on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -230,8 +231,12 @@ def main():
 
     cfg = ATTN_CONFIGS[args.workload]
     work = attn_work(cfg)
-    us, enqueue_us, kt = time_attn(cfg, args.steps, args.warmup, args.sets, torch, binding)
-    # per-kernel averages of the same workload in a separate, fully instrumented pass
+    # the step time: no per-kernel events in the timed steps (each timed dispatch adds a queue
+    # barrier of its own, several microseconds per kernel)
+    us, enqueue_us, _ = time_attn(cfg, args.steps, args.warmup, args.sets, torch, binding, timed_kernels=0)
+    # the same K steps again with the attention kernel's dispatch-stamped events: its live duration
+    us_ev, _, kt = time_attn(cfg, args.steps, args.warmup, args.sets, torch, binding, timed_kernels=0b010)
+    # per-kernel averages of the same workload in a third, fully instrumented pass
     _, _, kt_all = time_attn(cfg, 20, 3, args.sets, torch, binding, timed_kernels=0b111)
     gbs = work["bytes"] / (us * 1e-6) / 1e9
     tflops = work["flops"] / (us * 1e-6) / 1e12
@@ -270,6 +275,7 @@ def main():
         "algorithmic_bytes": work["bytes"],
         "algorithmic_flops": work["flops"],
         "host_enqueue_us_per_step": round(enqueue_us, 2),
+        "us_per_step_with_attn_events": round(us_ev, 2),
         "roofline": roofline,
         "kernels_us": {n: round(v["avg_us"], 2) for n, v in kt_all.items()},
     }
@@ -280,8 +286,9 @@ def main():
             c = ATTN_CONFIGS[name]
             w = attn_work(c)
             steps = 10 if name == "chunk_prefill" else 30
-            u, _, k = time_attn(c, steps, 3, 2 if name == "chunk_prefill" else args.sets, torch, binding,
-                                seed=c.seed, timed_kernels=0b111)
+            sets = 2 if name == "chunk_prefill" else args.sets
+            u, _, _ = time_attn(c, steps, 3, sets, torch, binding, seed=c.seed, timed_kernels=0)
+            _, _, k = time_attn(c, steps, 3, sets, torch, binding, seed=c.seed, timed_kernels=0b111)
             extras[name] = {"us_per_step": round(u, 2), "gbps": round(w["bytes"] / (u * 1e-6) / 1e9, 1),
                             "tflops": round(w["flops"] / (u * 1e-6) / 1e12, 2),
                             "kernels_us": {n: round(v["avg_us"], 2) for n, v in k.items()}}
