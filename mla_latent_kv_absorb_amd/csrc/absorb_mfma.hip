@@ -350,11 +350,16 @@ struct AbsorbQArgs {
   int32_t H, M;            // M = B * S query rows per head
   int32_t S, row_blocks;   // query tokens per sequence; 128-row blocks per sequence
   int32_t row_blocks_per_wg;
+  float inv_S;             // 1 / S
 };
 
 // Byte offset of row (m, h)'s slot in the fragment buffer (add ks * 1024 + g * 16).
 __device__ __forceinline__ int64_t frag_row_offset(int m, int h, const AbsorbQArgs &a) {
-  const int b = m / a.S, lrow = (m - b * a.S) * a.H + h;
+  // b = m / S without an integer division: m < 2^24, so the float quotient is off by at most one
+  int b = int(float(m) * a.inv_S);
+  b -= (b * a.S > m);
+  b += ((b + 1) * a.S <= m);
+  const int lrow = (m - b * a.S) * a.H + h;
   return ((int64_t(b) * a.row_blocks + (lrow >> 7)) * 4 + ((lrow >> 5) & 3)) * int64_t(kFragBytesPerWave) +
          (lrow & 31) * 32;
 }
@@ -366,6 +371,7 @@ __device__ __forceinline__ int w_swz(int row) { return (row & 3) << 2; }
 
 __global__ void __launch_bounds__(256) absorb_q_kernel(AbsorbQArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char wt[kDn * 128 * 2];  // 32 KB
+  __shared__ __attribute__((aligned(16))) unsigned char xt[2][32 * kDn * 2];  // 2 x 8 KB
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int l32 = lane & 31, g = lane >> 5;
@@ -383,17 +389,21 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(AbsorbQArgs a) {
   for (int i = 0; i < 8; ++i)
     buf_load16_lds(wres, wt + (wave * 8 + i) * 1024, w_voff, uint32_t((wave * 8 + i) * 4) * (kC * 2) + c0 * 2);
 
-  // q_nope rows of head h as the MFMA B operand (lane: row m = 32 rb + l32, elements 16 ks + 8 g ..),
-  // loaded while the W tile is in flight; rows past M read out of range and give zeros
+  // q_nope rows of head h (32 per row block, 256 bytes each) go to LDS by DMA, four rows per wave
+  // instruction: lane l moves chunk position l % 16 of row l / 16 and fetches the chunk stored
+  // there ((l % 16) ^ (row & 15)), so the B-operand reads below (16 lanes, 16 rows, one chunk) hit
+  // 16 different bank groups.  Rows past M repeat row M - 1 (their results are not stored).
   const rsrc_t xres = make_rsrc(a.q_nope, uint32_t(int64_t(a.M) * a.H * kDn * 2));
-  auto load_x = [&](int rb, u32x4 (&x)[kDn / 16]) {
-    const int m = rb * 32 + l32;
-    const uint32_t off = m < a.M ? uint32_t((int64_t(m) * a.H + h) * (kDn * 2)) + 16 * g : 0x80000000u;
+  auto issue_x = [&](int rb, int buf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int ks = 0; ks < kDn / 16; ++ks) x[ks] = buf_load16(xres, off, 32 * ks);
+    for (int i = 0; i < 2; ++i) {
+      const int r = wave * 8 + i * 4 + (lane >> 4);
+      const int m = min(rb * 32 + r, a.M - 1);
+      const uint32_t src = uint32_t((int64_t(m) * a.H + h) * (kDn * 2)) + uint32_t((lane & 15) ^ (r & 15)) * 16;
+      buf_load16_lds(xres, xt[buf] + (wave * 8 + i * 4) * 256, src, 0);
+    }
   };
-  u32x4 xn[kDn / 16];
-  if (rb0 < rb_end) load_x(rb0, xn);
+  if (rb0 < rb_end) issue_x(rb0, 0);
   wait_vmcnt<0>();
   __syncthreads();
 
@@ -401,11 +411,16 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(AbsorbQArgs a) {
   for (int rb = rb0; rb < rb_end; ++rb) {
     const int m = rb * 32 + l32;
     const bool ok = m < a.M;
+    const int buf = (rb - rb0) & 1;
+    // the other buffer was last read in the previous iteration, before its closing barrier
+    const bool prefetch = rb + 1 < rb_end;  // wavefront-uniform
+    if (prefetch) issue_x(rb + 1, buf ^ 1);
     u32x4 xc[kDn / 16];
 #pragma unroll
-    for (int ks = 0; ks < kDn / 16; ++ks) xc[ks] = xn[ks];
-    if (rb + 1 < rb_end) load_x(rb + 1, xn);  // prefetch the next row block
-    f32x16 d = f32x16{};
+    for (int ks = 0; ks < kDn / 16; ++ks)
+      xc[ks] = lds_read16(xt[buf], uint32_t(l32) * 256 + uint32_t((2 * ks + g) ^ (l32 & 15)) * 16);
+    // all eight A fragments are read before the MFMA chain so their LDS latency is paid once
+    u32x4 af[kDn / 16];
 #pragma unroll
     for (int ks = 0; ks < kDn / 16; ++ks) {
       const int row0 = 16 * ks + 8 * g + (s16 >> 2);
@@ -413,9 +428,12 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(AbsorbQArgs a) {
       const int within = (s16 & 1) * 8;
       const uint32_t off0 = row0 * 256 + (chunk ^ w_swz(row0)) * 16 + within;
       const uint32_t off1 = (row0 + 4) * 256 + (chunk ^ w_swz(row0 + 4)) * 16 + within;
-      const u32x4 af = lds_read_tr_pair(wt, off0, off1);
-      d = mfma32(af, xc[ks], d);
+      af[ks] = lds_read_tr_pair(wt, off0, off1);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 d = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < kDn / 16; ++ks) d = mfma32(af[ks], xc[ks], d);
     // D^T[c][m]: lane holds column m, c = 32 wave + 8 (r/4) + 4 g + r % 4; the four elements of
     // register group q are half of the 16-byte chunk (c0 + 32 wave + 8 q) / 8 of the row
     if (ok) {
@@ -426,6 +444,10 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(AbsorbQArgs a) {
         const u32x2 v{pack_bf16x2(d[4 * q], d[4 * q + 1]), pack_bf16x2(d[4 * q + 2], d[4 * q + 3])};
         *reinterpret_cast<u32x2 *>(dst + (chunk >> 1) * 1024 + (chunk & 1) * 16) = v;
       }
+    }
+    if (prefetch) {
+      wait_vmcnt<0>();  // the next row block's rows (and this block's stores)
+      __syncthreads();
     }
   }
   // the first column quarter also moves the rope query rows of its row blocks into place
@@ -664,7 +686,8 @@ hipError_t mfma_absorb_attn(const AttnCall &c) {
   const int32_t row_blocks = int32_t((c.S * c.H + kRowsWG - 1) / kRowsWG);
 
   AbsorbQArgs qa{static_cast<const uint16_t *>(c.q_nope), static_cast<const uint16_t *>(c.q_pe),
-                 static_cast<const uint16_t *>(c.wkv_b), q_frag, int32_t(c.H), M, int32_t(c.S), row_blocks, 4};
+                 static_cast<const uint16_t *>(c.wkv_b), q_frag, int32_t(c.H), M, int32_t(c.S), row_blocks, 4,
+                 1.f / float(c.S)};
   const int nrb = (M + 31) / 32;
   hipError_t err = launch_kernel(
       MLA_KERNEL_ABSORB_Q, absorb_q_kernel,
