@@ -126,13 +126,16 @@ def time_expand(cfg, steps, warmup, torch, binding, seed=4):
                       device="cuda") * math.sqrt(cfg.wkv_b_var)).to(torch.bfloat16)
     k = torch.empty((cfg.n_heads, cfg.n_tokens, cfg.qk_nope_head_dim), dtype=torch.bfloat16, device="cuda")
     v = torch.empty((cfg.n_heads, cfg.n_tokens, cfg.v_head_dim), dtype=torch.bfloat16, device="cuda")
+    need = binding.expand_kv_workspace_size(cfg.n_tokens, cfg.n_heads, cfg.kv_lora_rank, cfg.qk_nope_head_dim,
+                                            cfg.v_head_dim, binding.MLA_DTYPE_BF16)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
     for _ in range(warmup):
-        binding.expand_kv(x, w, wk, cfg.n_heads, cfg.qk_nope_head_dim, cfg.v_head_dim, cfg.eps, k, v)
+        binding.expand_kv(x, w, wk, cfg.n_heads, cfg.qk_nope_head_dim, cfg.v_head_dim, cfg.eps, k, v, workspace=ws)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(steps):
-        binding.expand_kv(x, w, wk, cfg.n_heads, cfg.qk_nope_head_dim, cfg.v_head_dim, cfg.eps, k, v)
+        binding.expand_kv(x, w, wk, cfg.n_heads, cfg.qk_nope_head_dim, cfg.v_head_dim, cfg.eps, k, v, workspace=ws)
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) * 1000.0 / steps

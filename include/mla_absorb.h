@@ -119,6 +119,15 @@ int32_t mla_absorb_attn(const void *q_nope, const void *q_pe, const void *kv_cac
                         size_t workspace_bytes, void *stream);
 
 /*
+ * Bytes of device workspace mla_expand_kv needs (the normalised latent n, which the matrix-core
+ * path computes once per token and every head reuses; 0 for the plain path).  Returns 0 when the
+ * arguments are invalid (the same checks as mla_expand_kv; see mla_last_error).
+ */
+size_t mla_expand_kv_workspace_size(int64_t n_tokens, int64_t n_heads, int64_t kv_lora_rank,
+                                    int64_t qk_nope_head_dim, int64_t v_head_dim, int32_t dtype,
+                                    int32_t path);
+
+/*
  * Latent KV expansion with split (kernelindex.com operation 064).
  *
  *   c_kv    [T, C]                 raw compressed latent of T tokens
@@ -127,13 +136,16 @@ int32_t mla_absorb_attn(const void *q_nope, const void *q_pe, const void *kv_cac
  *   k_nope  [H, T, Dn]             written: k_nope[h,t,:] = rows h*(Dn+Dv) .. +Dn-1 of
  *                                  wkv_b applied to n[t]
  *   v       [H, T, Dv]             written: the next Dv rows applied to n[t]
- * where n[t,:] = c_kv[t,:] / sqrt(mean_c c_kv[t,c]^2 + eps) * rms_w.  No workspace.
- * k_nope and v must not alias the inputs or each other.  Returns MLA_OK or MLA_ERR_*.
+ * where n[t,:] = c_kv[t,:] / sqrt(mean_c c_kv[t,c]^2 + eps) * rms_w.
+ * workspace: at least mla_expand_kv_workspace_size(...) bytes of device memory, 16-byte aligned
+ * (may be NULL when that size is 0); owned by the caller, not kept after the call.
+ * k_nope and v must not alias the inputs, the workspace or each other.  Returns MLA_OK or
+ * MLA_ERR_*.
  */
 int32_t mla_expand_kv(const void *c_kv, const void *rms_w, const void *wkv_b, void *k_nope,
                       void *v, int64_t n_tokens, int64_t n_heads, int64_t kv_lora_rank,
                       int64_t qk_nope_head_dim, int64_t v_head_dim, float eps, int32_t dtype,
-                      int32_t path, void *stream);
+                      int32_t path, void *workspace, size_t workspace_bytes, void *stream);
 
 /* ---- kernel timing (benchmark instrumentation) ----------------------------------------------
  * While a kernel's bit is set in the mask given to mla_timing_enable (bit k = kernel id k), every
@@ -146,10 +158,11 @@ int32_t mla_expand_kv(const void *c_kv, const void *rms_w, const void *wkv_b, vo
  * failed (the affected launches are then missing from the totals). */
 #define MLA_KERNEL_ABSORB_Q 0 /* query absorption through W_UK                 */
 #define MLA_KERNEL_ATTN 1     /* split-KV scores, softmax, latent sum           */
-#define MLA_KERNEL_COMBINE 2  /* split combine + projection out through W_UV    */
-#define MLA_KERNEL_EXPAND 3   /* RMSNorm + projection + head-major split        */
-#define MLA_KERNEL_PLAIN 4    /* any kernel of the plain vector-ALU path        */
-#define MLA_NUM_KERNELS 5
+#define MLA_KERNEL_COMBINE 2      /* split combine + projection out through W_UV */
+#define MLA_KERNEL_EXPAND_PREP 3  /* per-token weighted latent and 1/rms          */
+#define MLA_KERNEL_EXPAND 4       /* projection + head-major split               */
+#define MLA_KERNEL_PLAIN 5        /* any kernel of the plain vector-ALU path     */
+#define MLA_NUM_KERNELS 6
 
 int32_t mla_timing_enable(uint32_t kernel_mask);
 int32_t mla_timing_collect(int32_t launches[MLA_NUM_KERNELS], double ms[MLA_NUM_KERNELS]);

@@ -29,10 +29,11 @@ MLA_DTYPE_BF16 = 1
 
 PATHS = {"auto": 0, "plain": 1, "mfma": 2}
 
-EXPORTED = ("mla_absorb_attn", "mla_absorb_attn_workspace_size", "mla_expand_kv", "mla_strerror",
+EXPORTED = ("mla_absorb_attn", "mla_absorb_attn_workspace_size", "mla_expand_kv", "mla_expand_kv_workspace_size",
+            "mla_strerror",
             "mla_last_error", "mla_timing_enable", "mla_timing_collect", "mla_kernel_name")
 
-NUM_KERNELS = 5  # MLA_NUM_KERNELS
+NUM_KERNELS = 6  # MLA_NUM_KERNELS
 
 
 class AttnShape(ctypes.Structure):
@@ -68,8 +69,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_absorb_attn.restype = i32
     lib.mla_absorb_attn_workspace_size.argtypes = [ctypes.POINTER(AttnShape), i64, i32, ctypes.POINTER(AttnOptions)]
     lib.mla_absorb_attn_workspace_size.restype = sz
-    lib.mla_expand_kv.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float, i32, i32, vp]
+    lib.mla_expand_kv.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float, i32, i32, vp, sz, vp]
     lib.mla_expand_kv.restype = i32
+    lib.mla_expand_kv_workspace_size.argtypes = [i64, i64, i64, i64, i64, i32, i32]
+    lib.mla_expand_kv_workspace_size.restype = sz
     lib.mla_strerror.argtypes = [i32]
     lib.mla_strerror.restype = ctypes.c_char_p
     lib.mla_last_error.argtypes = []
@@ -208,8 +211,18 @@ def absorb_attn(q_nope, q_pe, kv_cache, pe_cache, wkv_b, end_pos: int, softmax_s
                           num_splits=num_splits, path=path, workspace=workspace)()
 
 
+def expand_kv_workspace_size(n_tokens: int, n_heads: int, kv_lora_rank: int, qk_nope_head_dim: int,
+                             v_head_dim: int, dtype: int, path: str = "auto") -> int:
+    lib = load()
+    n = lib.mla_expand_kv_workspace_size(n_tokens, n_heads, kv_lora_rank, qk_nope_head_dim, v_head_dim, dtype,
+                                         PATHS[path])
+    if n == 0 and last_error():
+        raise MLAError(MLA_ERR_SHAPE, last_error())
+    return int(n)
+
+
 def expand_kv(c_kv, rms_w, wkv_b, n_heads: int, qk_nope_head_dim: int, v_head_dim: int, eps: float = 1e-6,
-              k_nope=None, v=None, *, path: str = "auto") -> Tuple["object", "object"]:
+              k_nope=None, v=None, *, path: str = "auto", workspace=None) -> Tuple["object", "object"]:
     """Latent KV expansion with split; returns (k_nope [H, T, Dn], v [H, T, Dv])."""
     import torch
 
@@ -221,8 +234,14 @@ def expand_kv(c_kv, rms_w, wkv_b, n_heads: int, qk_nope_head_dim: int, v_head_di
     if v is None:
         v = torch.empty((n_heads, T, v_head_dim), dtype=c_kv.dtype, device=c_kv.device)
     _require_device(c_kv, k_nope, v)
+    dt = _dtype_code(c_kv)
+    need = expand_kv_workspace_size(T, n_heads, C, qk_nope_head_dim, v_head_dim, dt, path)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=c_kv.device)
+    ws_ptr = workspace.data_ptr() if need else None
+    ws_bytes = workspace.numel() * workspace.element_size() if need else 0
     rc = lib.mla_expand_kv(c_kv.data_ptr(), rms_w.data_ptr(), wkv_b.data_ptr(), k_nope.data_ptr(), v.data_ptr(),
-                           T, n_heads, C, qk_nope_head_dim, v_head_dim, eps, _dtype_code(c_kv), PATHS[path],
+                           T, n_heads, C, qk_nope_head_dim, v_head_dim, eps, dt, PATHS[path], ws_ptr, ws_bytes,
                            _stream_handle(c_kv.device))
     _check(rc)
     return k_nope, v

@@ -5,11 +5,14 @@
 //   y[t, j]   = sum_c n[t, c] * wkv_b[j, c]
 //   k_nope[h, t, :] = y[t, 256 h .. 256 h + 127],   v[h, t, :] = y[t, 256 h + 128 .. 256 h + 255]
 //
-// One workgroup produces 256 tokens x one head (all 256 output features of that head), so its
-// K_nope and V blocks are two contiguous 64 KB regions.  The per-column weight is applied while
-// staging c_kv into LDS (bf16(c_kv * w)); the per-token 1/rms factor is accumulated on the way
-// and applied in fp32 in the epilogue.  The epilogue goes through LDS so every global store is a
-// full 16-byte, fully coalesced write.
+// Two kernels:
+//   1. expand_prep_kernel  once per token: n[t, :] rounded to bf16, into the workspace; every head
+//                          reuses it.
+//   2. expand_kernel       y = n . wkv_b^T per (256 tokens, one head).  Both operands stream into LDS
+//                          by DMA through a four-stage ring of 32-column tiles; the epilogue goes
+//                          through LDS so every global store is a full 16-byte, fully coalesced
+//                          write, and each workgroup's K_nope and V blocks are two contiguous 64 KB
+//                          regions.
 #include "common.h"
 #include "launch.h"
 #include "mfma_common.h"
@@ -21,28 +24,60 @@ namespace {
 constexpr int kC = 512;
 constexpr int kDn = 128;
 constexpr int kDv = 128;
-constexpr int kTT = 256;        // tokens per workgroup
-constexpr int kKC = 64;         // contraction columns per stage
-constexpr int kStageHalf = kTT * kKC * 2;  // 32 KB: one operand tile of a stage
-constexpr int kStage = 2 * kStageHalf;     // W tile + n tile
+constexpr int kTT = 256;                   // tokens per workgroup
+constexpr int kKC = 32;                    // contraction columns per stage
+constexpr int kStages = 4;
+constexpr int kTileBytes = kTT * kKC * 2;  // 16 KB: one operand tile (256 rows x 64 bytes)
+constexpr int kStageBytes = 2 * kTileBytes;
+constexpr int kChunks = kC / kKC;          // 16
+constexpr int kDmaPerTile = kTileBytes / 1024 / 4;  // 1 KB DMA instructions per wave per tile (4)
 constexpr int kEpiPitch = 272;             // bytes per staged output row (256 + 16 pad)
 constexpr int kEpiWave = 128 * kEpiPitch;  // 34 KB per wave
-constexpr int kLds = (2 * kStage > 4 * kEpiWave) ? 2 * kStage : 4 * kEpiWave;
+constexpr int kLds = (kStages * kStageBytes > 4 * kEpiWave) ? kStages * kStageBytes : 4 * kEpiWave;
 
+__host__ __device__ __forceinline__ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// ---- 1. per-token prep --------------------------------------------------------------------------
+// One wave per token row: lane l owns columns 8 l .. 8 l + 7.  n = c_kv * rms_w / rms, rounded once.
+__global__ void __launch_bounds__(256) expand_prep_kernel(const uint16_t *__restrict__ c_kv,
+                                                          const uint16_t *__restrict__ rms_w,
+                                                          uint16_t *__restrict__ xn, int32_t T, float eps) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (t >= T) return;
+  const u32x4 xv = *reinterpret_cast<const u32x4 *>(c_kv + int64_t(t) * kC + lane * 8);
+  const u32x4 wv = *reinterpret_cast<const u32x4 *>(rms_w + lane * 8);
+  float x[8], ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[2 * e] = __uint_as_float(xv[e] << 16);
+    x[2 * e + 1] = __uint_as_float(xv[e] & 0xffff0000u);
+    ss = fmaf(x[2 * e], x[2 * e], fmaf(x[2 * e + 1], x[2 * e + 1], ss));
+  }
+  const float inv = 1.f / sqrtf(wave_sum(ss) * (1.f / kC) + eps);
+  u32x4 out;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float w0 = __uint_as_float(wv[e] << 16), w1 = __uint_as_float(wv[e] & 0xffff0000u);
+    out[e] = pack_bf16x2(x[2 * e] * inv * w0, x[2 * e + 1] * inv * w1);
+  }
+  *reinterpret_cast<u32x4 *>(xn + int64_t(t) * kC + lane * 8) = out;
+}
+
+// ---- 2. projection ------------------------------------------------------------------------------
 struct ExpandArgs {
-  const uint16_t *c_kv;   // [T, 512]
-  const uint16_t *rms_w;  // [512]
+  const uint16_t *xn;     // [T, 512] normalised latent n, bf16
   const uint16_t *wkv_b;  // [H * 256, 512]
   uint16_t *k_nope;       // [H, T, 128]
   uint16_t *v;            // [H, T, 128]
   int32_t T, H, tblocks;
-  float eps;
+  int32_t grouped;        // 1: workgroups run in blocks of 8 heads x 4 token blocks (see below)
 };
 
-// Operand tiles have 128-byte rows (8 chunks of 16 bytes): two rows per 64-bank period.  A
-// ds_read_b128 serves 16 lanes = 16 consecutive rows at once, so chunks are XOR-swizzled by
-// (row >> 1) & 7: rows of equal parity then use eight different chunk slots.
-__device__ __forceinline__ int op_swz(int row) { return (row >> 1) & 7; }
+// Operand tiles have 64-byte rows (4 chunks of 16 bytes): four rows per 64-bank period.  A
+// ds_read_b128 serves 16 lanes = 16 consecutive rows at once; XOR-ing the chunk with
+// (row >> 2) & 3 gives rows r, r+4, r+8, r+12 (which share a period slot) four different chunks.
+__device__ __forceinline__ int op_swz(int row) { return (row >> 2) & 3; }
 __device__ __forceinline__ uint32_t tile_off(int row, int chunk) {
   return uint32_t(row) * (kKC * 2) + uint32_t(chunk ^ op_swz(row)) * 16;
 }
@@ -50,76 +85,52 @@ __device__ __forceinline__ uint32_t tile_off(int row, int chunk) {
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 expand_kernel(ExpandArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kLds];
-  __shared__ float rs[kTT];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int l32 = lane & 31, g = lane >> 5;
-  const int tb = blockIdx.x % a.tblocks;
-  const int h = blockIdx.x / a.tblocks;
+  // Order: each XCD takes a contiguous range of logical ids, and (when the sizes allow) every 32
+  // consecutive ids form a block of 8 heads x 4 token blocks, so the 32 workgroups an XCD runs at
+  // once read 2 MB of wkv_b and 1 MB of n between them, all of it reused from its L2.
+  const int lid = __builtin_amdgcn_readfirstlane(xcd_logical_id(blockIdx.x, gridDim.x));
+  int h, tb;
+  if (a.grouped) {
+    const int grp = lid >> 5, in = lid & 31, tgroups = a.tblocks >> 2;
+    const int hg = grp / tgroups;
+    h = __builtin_amdgcn_readfirstlane(hg * 8 + (in >> 2));
+    tb = __builtin_amdgcn_readfirstlane((grp - hg * tgroups) * 4 + (in & 3));
+  } else {
+    h = __builtin_amdgcn_readfirstlane(lid / a.tblocks);
+    tb = __builtin_amdgcn_readfirstlane(lid - h * a.tblocks);
+  }
   const int t0 = tb * kTT;
   const int wt = wave & 1;   // token half of this wave
   const int wj = wave >> 1;  // 0: K_nope features, 1: V features
 
-  // W rows of this head; each wave instruction moves 8 rows x 128 bytes.  Within instruction i
-  // the lane's row is 8 (8 wave + i) + lane / 8 and its chunk position lane % 8, so the source
-  // chunk (lane % 8) ^ op_swz(row) depends only on the lane and the parity of i.
+  // DMA: one wave instruction moves 16 rows x 64 bytes; lane l lands at chunk position l % 4 of
+  // row l / 4 and fetches the chunk stored there.  Wave w moves rows 64 w .. 64 w + 63 of both the
+  // W tile (wkv_b rows of head h) and the token tile (n rows t0 ..; rows past T read 0).
+  const int drow = lane >> 2;
+  const uint32_t dchunk = uint32_t((lane & 3) ^ op_swz(drow)) * 16;  // op_swz(16 i + drow) == op_swz(drow)
   const rsrc_t wres = make_rsrc(a.wkv_b + int64_t(h) * (kDn + kDv) * kC, (kDn + kDv) * kC * 2);
-  uint32_t w_lane_off[2];
+  const rsrc_t xres = make_rsrc(a.xn + int64_t(t0) * kC, uint32_t(min(kTT, a.T - t0)) * (kC * 2));
+  const uint32_t d_voff = uint32_t(wave * 64 + drow) * (kC * 2) + dchunk;
+  auto issue = [&](int kc) __attribute__((always_inline)) {
+    unsigned char *st = smem + (kc % kStages) * kStageBytes;
 #pragma unroll
-  for (int par = 0; par < 2; ++par)
-    w_lane_off[par] = uint32_t(lane >> 3) * (kC * 2) + uint32_t((lane & 7) ^ op_swz(8 * par + (lane >> 3))) * 16;
-  // c_kv staging: thread owns rows srow + 32 i and chunk schunk of every stage; rows past T read 0
-  const int srow = threadIdx.x >> 3, schunk = threadIdx.x & 7;
-  const rsrc_t xres = make_rsrc(a.c_kv + int64_t(t0) * kC, uint32_t(min(kTT, a.T - t0)) * (kC * 2));
-  const rsrc_t rwres = make_rsrc(a.rms_w, kC * 2);
-  const uint32_t x_lane_off = uint32_t(srow) * (kC * 2) + schunk * 16;
-  float ss[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  u32x4 xr[8];
-
-  auto issue_w = [&](int kc, int buf) {
-    unsigned char *dst = smem + buf * kStage + wave * 8 * 1024;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      buf_load16_lds(wres, dst + i * 1024, w_lane_off[i & 1], uint32_t((wave * 8 + i) * 8 * (kC * 2) + kc * (kKC * 2)));
-  };
-  auto load_x = [&](int kc) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) xr[i] = buf_load16(xres, x_lane_off, uint32_t(i * 32 * (kC * 2) + kc * (kKC * 2)));
-  };
-  const uint32_t st_off0 = tile_off(srow, schunk);  // rows srow + 32 i share the swizzle
-  auto store_x = [&](int kc, int buf) {
-    const u32x4 wv = buf_load16(rwres, schunk * 16, kc * (kKC * 2));
-    float w[8];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      w[2 * e] = __uint_as_float(wv[e] << 16);
-      w[2 * e + 1] = __uint_as_float(wv[e] & 0xffff0000u);
-    }
-    unsigned char *dst = smem + buf * kStage + kStageHalf;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float x[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[2 * e] = __uint_as_float(xr[i][e] << 16);
-        x[2 * e + 1] = __uint_as_float(xr[i][e] & 0xffff0000u);
-      }
-      float acc = ss[i];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc = fmaf(x[e], x[e], acc);
-      ss[i] = acc;
-      const u32x4 pk{pack_bf16x2(x[0] * w[0], x[1] * w[1]), pack_bf16x2(x[2] * w[2], x[3] * w[3]),
-                     pack_bf16x2(x[4] * w[4], x[5] * w[5]), pack_bf16x2(x[6] * w[6], x[7] * w[7])};
-      lds_write16(dst, st_off0 + i * 32 * (kKC * 2), pk);
+    for (int i = 0; i < kDmaPerTile; ++i) {
+      // the row offset stays in the per-lane offset, which the buffer range check always covers
+      const uint32_t voff = d_voff + uint32_t(i * 16) * (kC * 2);
+      buf_load16_lds(wres, st + (wave * 64 + i * 16) * (kKC * 2), voff, uint32_t(kc * kKC * 2));
+      buf_load16_lds(xres, st + kTileBytes + (wave * 64 + i * 16) * (kKC * 2), voff, uint32_t(kc * kKC * 2));
     }
   };
 
   // operand reads: every operand row is 32 k + l32 (+ a multiple of 32), so it shares the swizzle of l32
-  uint32_t rd_off[4];
+  uint32_t rd_off[2];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) rd_off[ks] = tile_off(l32, 2 * ks + g);
+  for (int ks = 0; ks < 2; ++ks) rd_off[ks] = tile_off(l32, 2 * ks + g);
   const uint32_t a_base = uint32_t(wj * 128) * (kKC * 2);
-  const uint32_t b_base = kStageHalf + uint32_t(wt * 128) * (kKC * 2);
+  const uint32_t b_base = kTileBytes + uint32_t(wt * 128) * (kKC * 2);
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -127,76 +138,60 @@ expand_kernel(ExpandArgs a) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) acc[i][k] = f32x16{};
 
-  issue_w(0, 0);
-  load_x(0);
-  store_x(0, 0);
-  wait_vmcnt<0>();
-  __syncthreads();
+#pragma unroll
+  for (int kc = 0; kc < kStages - 1; ++kc) issue(kc);
 
-  constexpr int nk = kC / kKC;
+  constexpr int kDma = 2 * kDmaPerTile;  // DMA instructions per wave per chunk
 #pragma unroll 1
-  for (int kc = 0; kc < nk; ++kc) {
-    const int buf = kc & 1;
-    if (kc + 1 < nk) {
-      issue_w(kc + 1, buf ^ 1);
-      load_x(kc + 1);
-    }
-    const unsigned char *stage = smem + buf * kStage;
-    // fragments of k-step ks+1 are read while the 16 MFMAs of k-step ks run
+  for (int kc = 0; kc < kChunks; ++kc) {
+    // chunk kc must have landed (chunks kc+1, kc+2 may still be in flight); after the barrier every
+    // wave is done with chunk kc-1, whose stage takes chunk kc+3
+    const int ahead = min(kChunks - 1 - kc, kStages - 2);
+    if (ahead >= 2) wait_vmcnt<2 * kDma>();
+    else if (ahead == 1) wait_vmcnt<kDma>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+    if (kc + kStages - 1 < kChunks) issue(kc + kStages - 1);
+
+    const unsigned char *stage = smem + (kc % kStages) * kStageBytes;
+    // fragments of k-step 1 are read while the 16 MFMAs of k-step 0 run
     u32x4 af[2][4], bf[2][4];
 #pragma unroll
-    for (int jb = 0; jb < 4; ++jb) af[0][jb] = lds_read16(stage, a_base + jb * 32 * (kKC * 2) + rd_off[0]);
+    for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) bf[0][k] = lds_read16(stage, b_base + k * 32 * (kKC * 2) + rd_off[0]);
+      for (int jb = 0; jb < 4; ++jb) af[ks][jb] = lds_read16(stage, a_base + jb * 32 * (kKC * 2) + rd_off[ks]);
 #pragma unroll
-    for (int ks = 0; ks < kKC / 16; ++ks) {
-      const int cur = ks & 1;
-      if (ks + 1 < kKC / 16) {
+      for (int k = 0; k < 4; ++k) bf[ks][k] = lds_read16(stage, b_base + k * 32 * (kKC * 2) + rd_off[ks]);
+    }
 #pragma unroll
-        for (int jb = 0; jb < 4; ++jb) af[cur ^ 1][jb] = lds_read16(stage, a_base + jb * 32 * (kKC * 2) + rd_off[ks + 1]);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) bf[cur ^ 1][k] = lds_read16(stage, b_base + k * 32 * (kKC * 2) + rd_off[ks + 1]);
-      }
+    for (int ks = 0; ks < 2; ++ks) {
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int jb = 0; jb < 4; ++jb)
 #pragma unroll
-        for (int k = 0; k < 4; ++k) acc[jb][k] = mfma32(af[cur][jb], bf[cur][k], acc[jb][k]);
-      __builtin_amdgcn_sched_barrier(0);
+        for (int k = 0; k < 4; ++k) acc[jb][k] = mfma32(af[ks][jb], bf[ks][k], acc[jb][k]);
     }
-    if (kc + 1 < nk) store_x(kc + 1, buf ^ 1);
-    wait_vmcnt<0>();
-    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
   }
-
-  // 1 / rms per token: the 8 threads of a row hold disjoint column slices of its sum of squares
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    float v = ss[i];
-    v += __shfl_xor(v, 1, 64);
-    v += __shfl_xor(v, 2, 64);
-    v += __shfl_xor(v, 4, 64);
-    if (schunk == 0) rs[srow + 32 * i] = 1.f / sqrtf(v * (1.f / kC) + a.eps);
-  }
-  __syncthreads();
+  __syncthreads();  // every wave is done with the stages before the epilogue reuses them
 
   // D^T[j][t] tiles: lane holds t = 32 k + l32, j = 32 jb + 8 (r/4) + 4 g + r % 4
   unsigned char *epi = smem + wave * kEpiWave;
   const uint32_t epi_lane = uint32_t(l32) * kEpiPitch + 8 * g;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const float sc = rs[wt * 128 + 32 * k + l32];
 #pragma unroll
     for (int jb = 0; jb < 4; ++jb) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const u32x2 v{pack_bf16x2(agpr_read(acc[jb][k][4 * q]) * sc, agpr_read(acc[jb][k][4 * q + 1]) * sc),
-                      pack_bf16x2(agpr_read(acc[jb][k][4 * q + 2]) * sc, agpr_read(acc[jb][k][4 * q + 3]) * sc)};
+        const u32x2 v{pack_bf16x2(agpr_read(acc[jb][k][4 * q]), agpr_read(acc[jb][k][4 * q + 1])),
+                      pack_bf16x2(agpr_read(acc[jb][k][4 * q + 2]), agpr_read(acc[jb][k][4 * q + 3]))};
         lds_write8(epi, epi_lane + uint32_t(32 * k) * kEpiPitch + (32 * jb + 8 * q) * 2, v);
       }
     }
   }
-  __syncthreads();
+  // same wavefront wrote these rows; LDS operations of one wavefront complete in order
   const int rows_valid = max(0, min(128, a.T - (t0 + wt * 128)));
   const rsrc_t ores = make_rsrc((wj == 0 ? a.k_nope : a.v) + (int64_t(h) * a.T + t0 + wt * 128) * 128,
                                 uint32_t(rows_valid) * 256);
@@ -205,7 +200,7 @@ expand_kernel(ExpandArgs a) {
 #pragma unroll 8
   for (int it = 0; it < 32; ++it) {
     const u32x4 v = lds_read16(epi, rd_lane + it * 4 * kEpiPitch);
-    buf_store16(ores, v, st_lane, uint32_t(it * 1024));
+    buf_store16(ores, v, st_lane + uint32_t(it * 1024), 0);  // rows past T fall outside the range: dropped
   }
 }
 
@@ -217,15 +212,24 @@ bool mfma_expand_supported(const ExpandCall &c, const char **why) {
     *why = "needs kv_lora_rank 512, qk_nope_head_dim 128, v_head_dim 128";
     return false;
   }
-  if (c.T > (int64_t(1) << 30)) { *why = "too many tokens"; return false; }
+  if (c.T > (int64_t(1) << 22)) { *why = "n_tokens must be at most 4194304"; return false; }
   return true;
 }
 
+// Workspace: n [T x 512] bf16.
+size_t mfma_expand_workspace(const ExpandCall &c) { return align256(size_t(c.T) * kC * 2); }
+
 hipError_t mfma_expand_kv(const ExpandCall &c) {
-  ExpandArgs a{static_cast<const uint16_t *>(c.c_kv), static_cast<const uint16_t *>(c.rms_w),
-               static_cast<const uint16_t *>(c.wkv_b), static_cast<uint16_t *>(c.k_nope), static_cast<uint16_t *>(c.v),
-               int32_t(c.T), int32_t(c.H), int32_t((c.T + kTT - 1) / kTT), c.eps};
-  return launch_kernel(MLA_KERNEL_EXPAND, expand_kernel, dim3(unsigned(int64_t(a.tblocks) * c.H)), dim3(256), 0,
+  uint16_t *xn = static_cast<uint16_t *>(c.ws);
+  hipError_t err = launch_kernel(MLA_KERNEL_EXPAND_PREP, expand_prep_kernel, dim3(unsigned((c.T + 3) / 4)), dim3(256),
+                                 0, c.stream, static_cast<const uint16_t *>(c.c_kv),
+                                 static_cast<const uint16_t *>(c.rms_w), xn, int32_t(c.T), c.eps);
+  if (err != hipSuccess) return err;
+  const int32_t tblocks = int32_t((c.T + kTT - 1) / kTT);
+  ExpandArgs a{xn, static_cast<const uint16_t *>(c.wkv_b), static_cast<uint16_t *>(c.k_nope),
+               static_cast<uint16_t *>(c.v), int32_t(c.T), int32_t(c.H), tblocks,
+               (c.H % 8 == 0 && tblocks % 4 == 0) ? 1 : 0};
+  return launch_kernel(MLA_KERNEL_EXPAND, expand_kernel, dim3(unsigned(int64_t(tblocks) * c.H)), dim3(256), 0,
                        c.stream, a);
 }
 

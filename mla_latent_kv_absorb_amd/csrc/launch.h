@@ -27,6 +27,7 @@ struct ExpandCall {
   int32_t dtype;
   const void *c_kv, *rms_w, *wkv_b;
   void *k_nope, *v;
+  void *ws;  // workspace (layout chosen by the path's workspace function)
   hipStream_t stream;
 };
 
@@ -65,6 +66,7 @@ bool mfma_attn_plan_ok(const AttnCall &c, const char **why);  // limits that dep
 hipError_t mfma_absorb_attn(const AttnCall &c);
 
 bool mfma_expand_supported(const ExpandCall &c, const char **why);
+size_t mfma_expand_workspace(const ExpandCall &c);
 hipError_t mfma_expand_kv(const ExpandCall &c);
 
 }  // namespace mla

@@ -179,10 +179,14 @@ int32_t mla_absorb_attn(const void *q_nope, const void *q_pe, const void *kv_cac
   return MLA_OK;
 }
 
-int32_t mla_expand_kv(const void *c_kv, const void *rms_w, const void *wkv_b, void *k_nope, void *v,
-                      int64_t n_tokens, int64_t n_heads, int64_t kv_lora_rank, int64_t qk_nope_head_dim,
-                      int64_t v_head_dim, float eps, int32_t dtype, int32_t path, void *stream) {
-  clear_error();
+}  // extern "C"
+
+namespace {
+
+// Validation shared by mla_expand_kv and mla_expand_kv_workspace_size; no HIP calls.
+int32_t plan_expand(int64_t n_tokens, int64_t n_heads, int64_t kv_lora_rank, int64_t qk_nope_head_dim,
+                    int64_t v_head_dim, float eps, int32_t dtype, int32_t path, mla::ExpandCall &e,
+                    bool &use_mfma) {
   if (dtype != MLA_DTYPE_F32 && dtype != MLA_DTYPE_BF16) return fail(MLA_ERR_DTYPE, "unknown dtype %d", dtype);
   const int64_t dims[] = {n_tokens, n_heads, kv_lora_rank, qk_nope_head_dim, v_head_dim};
   const char *dnames[] = {"n_tokens", "n_heads", "kv_lora_rank", "qk_nope_head_dim", "v_head_dim"};
@@ -198,6 +202,44 @@ int32_t mla_expand_kv(const void *c_kv, const void *rms_w, const void *wkv_b, vo
   if (!(eps >= 0.f) || eps > 1e30f) return fail(MLA_ERR_SHAPE, "eps must be finite and >= 0");
   if (path != MLA_PATH_AUTO && path != MLA_PATH_PLAIN && path != MLA_PATH_MFMA)
     return fail(MLA_ERR_UNSUPPORTED, "unknown path %d", path);
+  e = mla::ExpandCall{};
+  e.T = n_tokens; e.H = n_heads; e.C = kv_lora_rank; e.Dn = qk_nope_head_dim; e.Dv = v_head_dim;
+  e.eps = eps; e.dtype = dtype;
+  use_mfma = false;
+  if (path != MLA_PATH_PLAIN) {
+    const char *why = "";
+    const bool ok = mla::mfma_expand_supported(e, &why);
+    if (path == MLA_PATH_MFMA && !ok) return fail(MLA_ERR_UNSUPPORTED, "matrix-core path: %s", why);
+    use_mfma = ok;
+  }
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mla_expand_kv_workspace_size(int64_t n_tokens, int64_t n_heads, int64_t kv_lora_rank,
+                                    int64_t qk_nope_head_dim, int64_t v_head_dim, int32_t dtype, int32_t path) {
+  clear_error();
+  mla::ExpandCall e;
+  bool use_mfma = false;
+  if (plan_expand(n_tokens, n_heads, kv_lora_rank, qk_nope_head_dim, v_head_dim, 0.f, dtype, path, e, use_mfma) !=
+      MLA_OK)
+    return 0;
+  return use_mfma ? mla::mfma_expand_workspace(e) : 0;
+}
+
+int32_t mla_expand_kv(const void *c_kv, const void *rms_w, const void *wkv_b, void *k_nope, void *v,
+                      int64_t n_tokens, int64_t n_heads, int64_t kv_lora_rank, int64_t qk_nope_head_dim,
+                      int64_t v_head_dim, float eps, int32_t dtype, int32_t path, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+  clear_error();
+  mla::ExpandCall e;
+  bool use_mfma = false;
+  const int32_t st = plan_expand(n_tokens, n_heads, kv_lora_rank, qk_nope_head_dim, v_head_dim, eps, dtype, path, e,
+                                 use_mfma);
+  if (st != MLA_OK) return st;
   const void *ptrs[] = {c_kv, rms_w, wkv_b, k_nope, v};
   const char *names[] = {"c_kv", "rms_w", "wkv_b", "k_nope", "v"};
   for (int i = 0; i < 5; ++i) {
@@ -213,17 +255,18 @@ int32_t mla_expand_kv(const void *c_kv, const void *rms_w, const void *wkv_b, vo
     for (int i = 0; i < 5; ++i)
       if (i != o && overlaps(ptrs[o], sizes[o], ptrs[i], sizes[i]))
         return fail(MLA_ERR_SHAPE, "%s overlaps %s", names[o], names[i]);
-  mla::ExpandCall e{};
-  e.T = n_tokens; e.H = n_heads; e.C = kv_lora_rank; e.Dn = qk_nope_head_dim; e.Dv = v_head_dim;
-  e.eps = eps; e.dtype = dtype; e.c_kv = c_kv; e.rms_w = rms_w; e.wkv_b = wkv_b; e.k_nope = k_nope; e.v = v;
-  e.stream = static_cast<hipStream_t>(stream);
-  bool use_mfma = false;
-  if (path != MLA_PATH_PLAIN) {
-    const char *why = "";
-    const bool ok = mla::mfma_expand_supported(e, &why);
-    if (path == MLA_PATH_MFMA && !ok) return fail(MLA_ERR_UNSUPPORTED, "matrix-core path: %s", why);
-    use_mfma = ok;
+  const size_t need = use_mfma ? mla::mfma_expand_workspace(e) : 0;
+  if (need > 0) {
+    if (!workspace) return fail(MLA_ERR_WORKSPACE, "workspace is NULL but %zu bytes are needed", need);
+    if (workspace_bytes < need)
+      return fail(MLA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+    if (misaligned(workspace)) return fail(MLA_ERR_ALIGN, "workspace is not 16-byte aligned");
+    for (int i = 0; i < 5; ++i)
+      if (overlaps(workspace, need, ptrs[i], sizes[i]))
+        return fail(MLA_ERR_WORKSPACE, "workspace overlaps %s", names[i]);
   }
+  e.c_kv = c_kv; e.rms_w = rms_w; e.wkv_b = wkv_b; e.k_nope = k_nope; e.v = v; e.ws = workspace;
+  e.stream = static_cast<hipStream_t>(stream);
   hipError_t err = use_mfma ? mla::mfma_expand_kv(e) : mla::plain_expand_kv(e);
   if (err != hipSuccess) return fail(MLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
   return MLA_OK;

@@ -142,6 +142,7 @@ const char *mla_kernel_name(int32_t id) {
     case MLA_KERNEL_ABSORB_Q: return "absorb_q";
     case MLA_KERNEL_ATTN: return "attn";
     case MLA_KERNEL_COMBINE: return "combine";
+    case MLA_KERNEL_EXPAND_PREP: return "expand_prep";
     case MLA_KERNEL_EXPAND: return "expand";
     case MLA_KERNEL_PLAIN: return "plain";
     default: return "";

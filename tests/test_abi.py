@@ -125,9 +125,14 @@ def test_attn_out_alias(lib):
     assert "overlaps" in B.last_error()
 
 
-def call_expand(lib, T=64, H=128, C=512, Dn=128, Dv=128, eps=1e-6, dtype=B.MLA_DTYPE_BF16, ptrs=None, path=0):
+def call_expand(lib, T=64, H=128, C=512, Dn=128, Dv=128, eps=1e-6, dtype=B.MLA_DTYPE_BF16, ptrs=None, path=0,
+                ws=None, ws_bytes=None):
     p = list(P[:5]) if ptrs is None else ptrs
-    return lib.mla_expand_kv(p[0], p[1], p[2], p[3], p[4], T, H, C, Dn, Dv, eps, dtype, path, None)
+    if ws is None:
+        ws = P[6]
+    if ws_bytes is None:
+        ws_bytes = 1 << 30
+    return lib.mla_expand_kv(p[0], p[1], p[2], p[3], p[4], T, H, C, Dn, Dv, eps, dtype, path, ws, ws_bytes, None)
 
 
 def test_expand_errors(lib):
@@ -147,3 +152,14 @@ def test_expand_errors(lib):
     assert call_expand(lib, ptrs=p) == B.MLA_ERR_SHAPE
     assert call_expand(lib, dtype=B.MLA_DTYPE_F32, C=64, H=4, Dn=32, Dv=32, path=B.PATHS["mfma"]) == \
         B.MLA_ERR_UNSUPPORTED
+
+
+def test_expand_workspace(lib):
+    need = lib.mla_expand_kv_workspace_size(64, 128, 512, 128, 128, B.MLA_DTYPE_BF16, B.PATHS["mfma"])
+    assert need >= 64 * 512 * 2
+    assert lib.mla_expand_kv_workspace_size(64, 128, 512, 128, 128, B.MLA_DTYPE_BF16, B.PATHS["plain"]) == 0
+    assert lib.mla_expand_kv_workspace_size(0, 128, 512, 128, 128, B.MLA_DTYPE_BF16, 0) == 0 and B.last_error()
+    assert call_expand(lib, ws=None, ws_bytes=0, path=B.PATHS["mfma"]) == B.MLA_ERR_WORKSPACE
+    assert call_expand(lib, ws_bytes=need - 1, path=B.PATHS["mfma"]) == B.MLA_ERR_WORKSPACE
+    assert call_expand(lib, ws=P[6] + 4, path=B.PATHS["mfma"]) == B.MLA_ERR_ALIGN
+    assert call_expand(lib, ws=P[0], path=B.PATHS["mfma"]) == B.MLA_ERR_WORKSPACE  # overlaps c_kv
