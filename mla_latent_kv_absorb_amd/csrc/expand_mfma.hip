@@ -8,11 +8,12 @@
 // Two kernels:
 //   1. expand_prep_kernel  once per token: n[t, :] rounded to bf16, into the workspace; every head
 //                          reuses it.
-//   2. expand_kernel       y = n . wkv_b^T per (256 tokens, one head).  Both operands stream into LDS
-//                          by DMA through a four-stage ring of 32-column tiles; the epilogue goes
-//                          through LDS so every global store is a full 16-byte, fully coalesced
-//                          write, and each workgroup's K_nope and V blocks are two contiguous 64 KB
-//                          regions.
+//   2. expand_kernel       y = n . wkv_b^T per (128 tokens, one head), two workgroups per compute
+//                          unit so one's waits and epilogue overlap the other's MFMAs.  Both
+//                          operands stream into LDS by DMA through a three-stage ring of 32-column
+//                          tiles; the epilogue goes through LDS so every global store is a full
+//                          16-byte, fully coalesced write, and each workgroup's K_nope and V blocks
+//                          are two contiguous 32 KB regions.
 #include "common.h"
 #include "launch.h"
 #include "mfma_common.h"
@@ -24,16 +25,20 @@ namespace {
 constexpr int kC = 512;
 constexpr int kDn = 128;
 constexpr int kDv = 128;
-constexpr int kTT = 256;                   // tokens per workgroup
+constexpr int kTT = 128;                   // tokens per workgroup
 constexpr int kKC = 32;                    // contraction columns per stage
-constexpr int kStages = 4;
-constexpr int kTileBytes = kTT * kKC * 2;  // 16 KB: one operand tile (256 rows x 64 bytes)
-constexpr int kStageBytes = 2 * kTileBytes;
+constexpr int kStages = 3;
+constexpr int kWTile = 256 * kKC * 2;      // 16 KB: wkv_b rows of the head (K_nope then V)
+constexpr int kNTile = kTT * kKC * 2;      // 8 KB: n rows of the token block
+constexpr int kStageBytes = kWTile + kNTile;
 constexpr int kChunks = kC / kKC;          // 16
-constexpr int kDmaPerTile = kTileBytes / 1024 / 4;  // 1 KB DMA instructions per wave per tile (4)
+constexpr int kWaves = 4;
+constexpr int kWDma = kWTile / 1024 / kWaves;  // 1 KB DMA instructions per wave per W tile (4)
+constexpr int kNDma = kNTile / 1024 / kWaves;  // per n tile (2)
 constexpr int kEpiPitch = 272;             // bytes per staged output row (256 + 16 pad)
-constexpr int kEpiWave = 128 * kEpiPitch;  // 34 KB per wave
-constexpr int kLds = (kStages * kStageBytes > 4 * kEpiWave) ? kStages * kStageBytes : 4 * kEpiWave;
+constexpr int kEpiWave = 64 * kEpiPitch;   // 17 KB per wave
+constexpr int kLds = (kStages * kStageBytes > kWaves * kEpiWave) ? kStages * kStageBytes : kWaves * kEpiWave;
+static_assert(2 * kLds <= 160 * 1024, "two workgroups share a compute unit");
 
 __host__ __device__ __forceinline__ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -82,47 +87,50 @@ __device__ __forceinline__ uint32_t tile_off(int row, int chunk) {
   return uint32_t(row) * (kKC * 2) + uint32_t(chunk ^ op_swz(row)) * 16;
 }
 
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 expand_kernel(ExpandArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kLds];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int l32 = lane & 31, g = lane >> 5;
-  // Order: each XCD takes a contiguous range of logical ids, and (when the sizes allow) every 32
-  // consecutive ids form a block of 8 heads x 4 token blocks, so the 32 workgroups an XCD runs at
-  // once read 2 MB of wkv_b and 1 MB of n between them, all of it reused from its L2.
+  // Order: each XCD takes a contiguous range of logical ids, and (when the sizes allow) every 64
+  // consecutive ids form a block of 8 heads x 8 token blocks, so the 64 workgroups an XCD runs at
+  // once (two per compute unit) read 2 MB of wkv_b and 1 MB of n between them, reused from its L2.
   const int lid = __builtin_amdgcn_readfirstlane(xcd_logical_id(blockIdx.x, gridDim.x));
   int h, tb;
   if (a.grouped) {
-    const int grp = lid >> 5, in = lid & 31, tgroups = a.tblocks >> 2;
+    const int grp = lid >> 6, in = lid & 63, tgroups = a.tblocks >> 3;
     const int hg = grp / tgroups;
-    h = __builtin_amdgcn_readfirstlane(hg * 8 + (in >> 2));
-    tb = __builtin_amdgcn_readfirstlane((grp - hg * tgroups) * 4 + (in & 3));
+    h = __builtin_amdgcn_readfirstlane(hg * 8 + (in >> 3));
+    tb = __builtin_amdgcn_readfirstlane((grp - hg * tgroups) * 8 + (in & 7));
   } else {
     h = __builtin_amdgcn_readfirstlane(lid / a.tblocks);
     tb = __builtin_amdgcn_readfirstlane(lid - h * a.tblocks);
   }
   const int t0 = tb * kTT;
-  const int wt = wave & 1;   // token half of this wave
+  const int wt = wave & 1;   // token half of this wave (64 tokens)
   const int wj = wave >> 1;  // 0: K_nope features, 1: V features
 
   // DMA: one wave instruction moves 16 rows x 64 bytes; lane l lands at chunk position l % 4 of
-  // row l / 4 and fetches the chunk stored there.  Wave w moves rows 64 w .. 64 w + 63 of both the
-  // W tile (wkv_b rows of head h) and the token tile (n rows t0 ..; rows past T read 0).
+  // row l / 4 and fetches the chunk stored there.  Wave w moves W rows 64 w .. 64 w + 63 (wkv_b
+  // rows of head h) and n rows 32 w .. 32 w + 31 (tokens t0 ..; rows past T read 0).
   const int drow = lane >> 2;
   const uint32_t dchunk = uint32_t((lane & 3) ^ op_swz(drow)) * 16;  // op_swz(16 i + drow) == op_swz(drow)
   const rsrc_t wres = make_rsrc(a.wkv_b + int64_t(h) * (kDn + kDv) * kC, (kDn + kDv) * kC * 2);
   const rsrc_t xres = make_rsrc(a.xn + int64_t(t0) * kC, uint32_t(min(kTT, a.T - t0)) * (kC * 2));
-  const uint32_t d_voff = uint32_t(wave * 64 + drow) * (kC * 2) + dchunk;
+  const uint32_t w_voff = uint32_t(wave * 64 + drow) * (kC * 2) + dchunk;
+  const uint32_t n_voff = uint32_t(wave * 32 + drow) * (kC * 2) + dchunk;
   auto issue = [&](int kc) __attribute__((always_inline)) {
     unsigned char *st = smem + (kc % kStages) * kStageBytes;
+    // row offsets stay in the per-lane offset, which the buffer range check always covers
 #pragma unroll
-    for (int i = 0; i < kDmaPerTile; ++i) {
-      // the row offset stays in the per-lane offset, which the buffer range check always covers
-      const uint32_t voff = d_voff + uint32_t(i * 16) * (kC * 2);
-      buf_load16_lds(wres, st + (wave * 64 + i * 16) * (kKC * 2), voff, uint32_t(kc * kKC * 2));
-      buf_load16_lds(xres, st + kTileBytes + (wave * 64 + i * 16) * (kKC * 2), voff, uint32_t(kc * kKC * 2));
-    }
+    for (int i = 0; i < kWDma; ++i)
+      buf_load16_lds(wres, st + (wave * 64 + i * 16) * (kKC * 2), w_voff + uint32_t(i * 16) * (kC * 2),
+                     uint32_t(kc * kKC * 2));
+#pragma unroll
+    for (int i = 0; i < kNDma; ++i)
+      buf_load16_lds(xres, st + kWTile + (wave * 32 + i * 16) * (kKC * 2), n_voff + uint32_t(i * 16) * (kC * 2),
+                     uint32_t(kc * kKC * 2));
   };
 
   // operand reads: every operand row is 32 k + l32 (+ a multiple of 32), so it shares the swizzle of l32
@@ -130,39 +138,37 @@ expand_kernel(ExpandArgs a) {
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) rd_off[ks] = tile_off(l32, 2 * ks + g);
   const uint32_t a_base = uint32_t(wj * 128) * (kKC * 2);
-  const uint32_t b_base = kTileBytes + uint32_t(wt * 128) * (kKC * 2);
+  const uint32_t b_base = kWTile + uint32_t(wt * 64) * (kKC * 2);
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int k = 0; k < 4; ++k) acc[i][k] = f32x16{};
+    for (int k = 0; k < 2; ++k) acc[i][k] = f32x16{};
 
 #pragma unroll
   for (int kc = 0; kc < kStages - 1; ++kc) issue(kc);
 
-  constexpr int kDma = 2 * kDmaPerTile;  // DMA instructions per wave per chunk
+  constexpr int kDma = kWDma + kNDma;  // DMA instructions per wave per chunk
 #pragma unroll 1
   for (int kc = 0; kc < kChunks; ++kc) {
-    // chunk kc must have landed (chunks kc+1, kc+2 may still be in flight); after the barrier every
-    // wave is done with chunk kc-1, whose stage takes chunk kc+3
-    const int ahead = min(kChunks - 1 - kc, kStages - 2);
-    if (ahead >= 2) wait_vmcnt<2 * kDma>();
-    else if (ahead == 1) wait_vmcnt<kDma>();
+    // chunk kc must have landed (chunk kc+1 may still be in flight); after the barrier every wave
+    // is done with chunk kc-1, whose stage takes chunk kc+2
+    if (kc + 1 < kChunks) wait_vmcnt<kDma>();
     else wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
     compiler_fence();
     if (kc + kStages - 1 < kChunks) issue(kc + kStages - 1);
 
     const unsigned char *stage = smem + (kc % kStages) * kStageBytes;
-    // fragments of k-step 1 are read while the 16 MFMAs of k-step 0 run
-    u32x4 af[2][4], bf[2][4];
+    // fragments of k-step 1 are read while the 8 MFMAs of k-step 0 run
+    u32x4 af[2][4], bf[2][2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
       for (int jb = 0; jb < 4; ++jb) af[ks][jb] = lds_read16(stage, a_base + jb * 32 * (kKC * 2) + rd_off[ks]);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) bf[ks][k] = lds_read16(stage, b_base + k * 32 * (kKC * 2) + rd_off[ks]);
+      for (int k = 0; k < 2; ++k) bf[ks][k] = lds_read16(stage, b_base + k * 32 * (kKC * 2) + rd_off[ks]);
     }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -170,17 +176,17 @@ expand_kernel(ExpandArgs a) {
 #pragma unroll
       for (int jb = 0; jb < 4; ++jb)
 #pragma unroll
-        for (int k = 0; k < 4; ++k) acc[jb][k] = mfma32(af[ks][jb], bf[ks][k], acc[jb][k]);
+        for (int k = 0; k < 2; ++k) acc[jb][k] = mfma32(af[ks][jb], bf[ks][k], acc[jb][k]);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
   __syncthreads();  // every wave is done with the stages before the epilogue reuses them
 
-  // D^T[j][t] tiles: lane holds t = 32 k + l32, j = 32 jb + 8 (r/4) + 4 g + r % 4
+  // D^T[j][t] tiles: lane holds t = 64 wt + 32 k + l32, j = 128 wj + 32 jb + 8 (r/4) + 4 g + r % 4
   unsigned char *epi = smem + wave * kEpiWave;
   const uint32_t epi_lane = uint32_t(l32) * kEpiPitch + 8 * g;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
+  for (int k = 0; k < 2; ++k) {
 #pragma unroll
     for (int jb = 0; jb < 4; ++jb) {
 #pragma unroll
@@ -192,13 +198,13 @@ expand_kernel(ExpandArgs a) {
     }
   }
   // same wavefront wrote these rows; LDS operations of one wavefront complete in order
-  const int rows_valid = max(0, min(128, a.T - (t0 + wt * 128)));
-  const rsrc_t ores = make_rsrc((wj == 0 ? a.k_nope : a.v) + (int64_t(h) * a.T + t0 + wt * 128) * 128,
+  const int rows_valid = max(0, min(64, a.T - (t0 + wt * 64)));
+  const rsrc_t ores = make_rsrc((wj == 0 ? a.k_nope : a.v) + (int64_t(h) * a.T + t0 + wt * 64) * 128,
                                 uint32_t(rows_valid) * 256);
   const uint32_t rd_lane = uint32_t(lane >> 4) * kEpiPitch + (lane & 15) * 16;
   const uint32_t st_lane = uint32_t(lane >> 4) * 256 + (lane & 15) * 16;
 #pragma unroll 8
-  for (int it = 0; it < 32; ++it) {
+  for (int it = 0; it < 16; ++it) {
     const u32x4 v = lds_read16(epi, rd_lane + it * 4 * kEpiPitch);
     buf_store16(ores, v, st_lane + uint32_t(it * 1024), 0);  // rows past T fall outside the range: dropped
   }
@@ -228,9 +234,9 @@ hipError_t mfma_expand_kv(const ExpandCall &c) {
   const int32_t tblocks = int32_t((c.T + kTT - 1) / kTT);
   ExpandArgs a{xn, static_cast<const uint16_t *>(c.wkv_b), static_cast<uint16_t *>(c.k_nope),
                static_cast<uint16_t *>(c.v), int32_t(c.T), int32_t(c.H), tblocks,
-               (c.H % 8 == 0 && tblocks % 4 == 0) ? 1 : 0};
-  return launch_kernel(MLA_KERNEL_EXPAND, expand_kernel, dim3(unsigned(int64_t(tblocks) * c.H)), dim3(256), 0,
-                       c.stream, a);
+               (c.H % 8 == 0 && tblocks % 8 == 0) ? 1 : 0};
+  return launch_kernel(MLA_KERNEL_EXPAND, expand_kernel, dim3(unsigned(int64_t(tblocks) * c.H)), dim3(kWaves * 64),
+                       0, c.stream, a);
 }
 
 }  // namespace mla
