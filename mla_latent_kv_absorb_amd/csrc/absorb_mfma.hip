@@ -124,17 +124,18 @@ attn_kernel(AttnArgs a) {
   const int pe_row = wave * 8 + (lane >> 3);
   const uint32_t pe_voff = uint32_t((lane & 7) ^ pe_swz(pe_row)) * 16;
   // One of the tile's nine DMA instructions per wave: part 0..7 moves kv row 8w+part, part 8 the pe rows.
+  const uint32_t smem_lds = lds_addr(smem);
   auto issue_part = [&](int j, int part) __attribute__((always_inline)) {
-    unsigned char *st = smem + (j % kStages) * kStageBytes;
+    const uint32_t st = smem_lds + uint32_t(j % kStages) * kStageBytes;
     const int t0 = t_begin + j * kTile;
     if (part < 8) {
       const int t = min(t0 + wave * 8 + part, wg_end - 1);  // wavefront-uniform
-      buf_load16_lds(kvres, st + (wave * 8 + part) * (kC * 2), uint32_t(swz_chunk(lane, 8 * (wave & 1) + part)) * 16,
-                     uint32_t(t) * (kC * 2));
+      buf_load16_lds_at(kvres, st + (wave * 8 + part) * (kC * 2),
+                        uint32_t(swz_chunk(lane, 8 * (wave & 1) + part)) * 16, uint32_t(t) * (kC * 2));
     } else {
       const int tp = min(t0 + pe_row, wg_end - 1);
-      buf_load16_lds(peres, st + kKvTileBytes + wave * 8 * (kR * 2), pe_voff + uint32_t(tp - t0) * (kR * 2),
-                     uint32_t(t0) * (kR * 2));
+      buf_load16_lds_at(peres, st + kKvTileBytes + wave * 8 * (kR * 2), pe_voff + uint32_t(tp - t0) * (kR * 2),
+                        uint32_t(t0) * (kR * 2));
     }
   };
   auto issue = [&](int j) __attribute__((always_inline)) {
@@ -213,7 +214,7 @@ attn_kernel(AttnArgs a) {
     // ---- scores S^T[position][row] over the 576-wide concatenation of kv and pe; the nine DMA
     // instructions of tile j+2 are spread over the MFMA groups so that a full memory queue
     // stalls one instruction at a time
-    f32x16 sacc = f32x16{};
+    f32x16 sacc;
     {
       u32x4 fr[2][4], qp[4];
 #pragma unroll
@@ -234,7 +235,12 @@ attn_kernel(AttnArgs a) {
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sacc = mfma32(fr[cur][i], grp < 8 ? qf[4 * grp + i] : qp[i], sacc);
+        for (int i = 0; i < 4; ++i) {
+          const u32x4 &qb = grp < 8 ? qf[4 * grp + i] : qp[i];
+          if (grp == 0 && i == 0) mfma32_v_first(sacc, fr[cur][i], qb);
+          else if (grp == 8 && i == 3) mfma32_v_last(sacc, fr[cur][i], qb);
+          else mfma32_v(sacc, fr[cur][i], qb);
+        }
         __builtin_amdgcn_sched_barrier(0);
         if (refill) issue_part(j + 2, grp);
         __builtin_amdgcn_sched_barrier(0);
@@ -252,7 +258,7 @@ attn_kernel(AttnArgs a) {
     float mloc = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sacc[r]);
-    const float mrow = fmaxf(mloc, __shfl_xor(mloc, 32, 64)) * a.scale_log2;  // scale > 0
+    const float mrow = xor32_max(mloc) * a.scale_log2;  // scale > 0
     if (m_ref == -INFINITY) {
       m_ref = mrow;  // first visible positions: nothing accumulated yet
     } else if (mrow > m_ref + kRescale) {
@@ -305,7 +311,7 @@ attn_kernel(AttnArgs a) {
 
   // ---- partial state of this split: max (log2 units), sum, unnormalised o.  o goes through LDS
   // so that every global store writes one whole 1 KB row.
-  lsum += __shfl_xor(lsum, 32, 64);
+  lsum = xor32_sum(lsum);
   // with a single split the result is final: normalise here (the combine kernel then only projects)
   const float oscale = (a.splits == 1 && lsum > 0.f) ? 1.f / lsum : 1.f;
   wait_vmcnt<0>();

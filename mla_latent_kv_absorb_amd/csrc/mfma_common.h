@@ -33,6 +33,27 @@ __device__ __forceinline__ f32x16 mfma32(const u32x4 &a, const u32x4 &b, const f
                                                  0, 0, 0);
 }
 
+// The same MFMA with its accumulator in VGPRs, for a short chain whose result the vector ALU
+// reads next (attention scores).  In a kernel that keeps other accumulators in AGPRs the compiler
+// selects the AGPR form for every MFMA, and each read of such a result then costs a
+// v_accvgpr_read; written as inline asm with "v" operands the chain stays in VGPRs.  The compiler
+// does not know these are MFMAs and inserts no wait states for them, so a chain starts with
+// mfma32_v_first (zero accumulator; two wait states ahead of it for a VALU write of the
+// destination) and ends with mfma32_v_last, whose s_nops (21 wait states) cover the longest
+// read-after-write and write-after-read distance of this 8-pass MFMA before any other instruction
+// touches the accumulator.  Between them, dependent MFMAs of the same opcode issue back to back.
+__device__ __forceinline__ void mfma32_v_first(f32x16 &acc, const u32x4 &a, const u32x4 &b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma32_v(f32x16 &acc, const u32x4 &a, const u32x4 &b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma32_v_last(f32x16 &acc, const u32x4 &a, const u32x4 &b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 4"
+               : "+v"(acc)
+               : "v"(a), "v"(b));
+}
+
 // v_mfma_f32_16x16x32_bf16 computes D[16x16] += A[16x32] * B[32x16] per wavefront:
 //   A operand: lane l holds A[l % 16][8 * (l / 16) + j], j = 0..7
 //   B operand: lane l holds B[8 * (l / 16) + j][l % 16]
@@ -92,6 +113,16 @@ __device__ __forceinline__ void buf_load16_lds(rsrc_t r, unsigned char *lds_base
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>((MLA_LDS void *)lds_base)));
   asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(r), "s"(soff), "{m0}"(m0) : "memory");
 }
+// The same with the destination given as an LDS byte address (see lds_addr), which keeps the
+// address arithmetic on the scalar unit without generic-to-LDS pointer conversions.
+__device__ __forceinline__ void buf_load16_lds_at(rsrc_t r, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr);
+  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(r), "s"(soff), "{m0}"(m0) : "memory");
+}
+// LDS byte address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return uint32_t(reinterpret_cast<uintptr_t>((const MLA_LDS void *)p));
+}
 
 // Workgroup order for an 8-XCD part.  Workgroups are handed to the XCDs round-robin by id, so
 // ids x, x+8, x+16, ... run on XCD x and share its L2.  This maps the hardware id to a logical
@@ -131,5 +162,16 @@ __device__ __forceinline__ float agpr_write(float x) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// max / sum of x over lanes l and l ^ 32 (one v_permlane32_swap: whichever way the halves are
+// exchanged, each lane ends up holding both values, so the result is the same in both halves)
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 }  // namespace mla
