@@ -125,13 +125,15 @@ attn_kernel(AttnArgs a) {
   const uint32_t pe_voff = uint32_t((lane & 7) ^ pe_swz(pe_row)) * 16;
   // One of the tile's nine DMA instructions per wave: part 0..7 moves kv row 8w+part, part 8 the pe rows.
   const uint32_t smem_lds = lds_addr(smem);
+  const uint32_t lane16 = uint32_t(lane) * 16;
   auto issue_part = [&](int j, int part) __attribute__((always_inline)) {
     const uint32_t st = smem_lds + uint32_t(j % kStages) * kStageBytes;
     const int t0 = t_begin + j * kTile;
     if (part < 8) {
       const int t = min(t0 + wave * 8 + part, wg_end - 1);  // wavefront-uniform
+      // source chunk swz_chunk(lane, row) = lane ^ kv_swz(row), kv_swz(row) wavefront-uniform
       buf_load16_lds_at(kvres, st + (wave * 8 + part) * (kC * 2),
-                        uint32_t(swz_chunk(lane, 8 * (wave & 1) + part)) * 16, uint32_t(t) * (kC * 2));
+                        lane16 ^ uint32_t(kv_swz(8 * (wave & 1) + part) * 16), uint32_t(t) * (kC * 2));
     } else {
       const int tp = min(t0 + pe_row, wg_end - 1);
       buf_load16_lds_at(peres, st + kKvTileBytes + wave * 8 * (kR * 2), pe_voff + uint32_t(tp - t0) * (kR * 2),
@@ -145,8 +147,8 @@ attn_kernel(AttnArgs a) {
 
   // Prologue: tile 0; the absorbed query into registers and the rope query into LDS; a full wait
   // (the query loads are the only vector loads the compiler tracks, so completing them here keeps
-  // its own vmcnt waits out of the loop body); then tile 1, always issued so that the in-loop wait
-  // counts stay exact (with a single tile it re-reads the last needed row).
+  // its own vmcnt waits out of the loop body); then tiles 1 and 2, always issued so that the
+  // in-loop wait counts stay exact (past the last needed position they re-read its row).
   issue(0);
   // Absorbed query as the score B operand: lane holds q[row][16 ks + 8 g .. +7], ks < 32.
   // absorb_q_kernel stores it fragment-major, so instruction ks of a wave reads one contiguous
@@ -169,144 +171,210 @@ attn_kernel(AttnArgs a) {
   }
   wait_vmcnt<0>();
   issue(1);
+  issue(2);
 
   f32x16 acc[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = f32x16{};
   float m_ref = -INFINITY, lsum = 0.f;
 
-  // score A-operand reads: tile row rho(l32), chunk 2 ks + g
+  // score A-operand reads: tile row rho(l32), chunk c = 2 i + g (i = k % 8 within a 256-byte group
+  // k / 8).  c ^ kv_swz(arow) = 2 (i ^ (kv_swz >> 1)) + (g ^ (kv_swz & 1)), so the address of i is
+  // sc_base ^ (32 i) (bits 5..7 of sc_base hold 32 (kv_swz >> 1)).  The pe rows work the same way.
   const int arow = rho(l32);
-  uint32_t sc_off[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) sc_off[i] = uint32_t(arow) * (kC * 2) + uint32_t((2 * i + g) ^ kv_swz(arow)) * 16;
-  uint32_t pe_off[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) pe_off[i] = kKvTileBytes + uint32_t(arow) * (kR * 2) + uint32_t((2 * i + g) ^ pe_swz(arow)) * 16;
+  const uint32_t sc_base = uint32_t(arow) * (kC * 2) + uint32_t(g ^ (kv_swz(arow) & 1)) * 16 + uint32_t(kv_swz(arow) >> 1) * 32;
+  const uint32_t pe_base = kKvTileBytes + uint32_t(arow) * (kR * 2) + uint32_t(g ^ (pe_swz(arow) & 1)) * 16 +
+                           uint32_t(pe_swz(arow) >> 1) * 32;
   const uint32_t qpe_off = uint32_t(l32 * 32 + g * 16);
   // P.V A-operand (transposing) reads: source lane s16 of a 16-lane group reads row
   // 16 ks + 8 g + 4 h + s16 / 4, chunk 4 cb + 2 chalf + (s16 & 3) / 2, half (s16 & 1).
   const int s16 = lane & 15, chalf = (lane >> 4) & 1;
-  uint32_t tr_off[4][2];  // [cb & 3][h]; + 16 KB for ks = 1, + 256 B per (cb >> 2)
+  // With chunk = 4 c4 + (2 chalf + (s16 & 3) / 2), chunk ^ kv_swz(row0) = 4 (c4 ^ (row0 & 3)) +
+  // ((2 chalf + (s16 & 3) / 2) ^ ((row0 >> 2) & 3)), so the address for c4 is tr_base[h] ^ (64 c4);
+  // + 256 B per (cb >> 2) and + 16 KB for ks = 1 go into the instruction offset.
+  uint32_t tr_base[2];
 #pragma unroll
-  for (int c4 = 0; c4 < 4; ++c4)
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int row0 = 8 * g + 4 * h + (s16 >> 2);
-      const int chunk = 4 * c4 + 2 * chalf + ((s16 & 3) >> 1);
-      tr_off[c4][h] = uint32_t(row0) * (kC * 2) + uint32_t(swz_chunk(chunk, row0)) * 16 + (s16 & 1) * 8;
-    }
+  for (int h = 0; h < 2; ++h) {
+    const int row0 = 8 * g + 4 * h + (s16 >> 2);
+    const int chunk = 2 * chalf + ((s16 & 3) >> 1);
+    tr_base[h] = uint32_t(row0) * (kC * 2) + uint32_t(swz_chunk(chunk, row0)) * 16 + (s16 & 1) * 8;
+  }
 
-#pragma unroll 1
-  for (int j = 0; j < ntiles; ++j) {
-    // tile j must have landed; tile j+1 (issued one iteration ago, or in the prologue) may not
-    if (j + 1 < ntiles || j == 0) wait_vmcnt<kLoadsPerTile>();
-    else wait_vmcnt<0>();
-    // after the barrier every wave is done with tile j-1, so its stage can be refilled (tile j+2
-    // goes into stage (j+2) % 4; stages of tiles j and j+1 are untouched)
-    __builtin_amdgcn_s_barrier();
-    compiler_fence();
-    const bool refill = j + 2 < ntiles;  // wavefront-uniform
-
+  // ---- scores S^T[position][row] of tile j over the 576-wide concatenation of kv and pe: 36 MFMAs
+  // (32 over kv, then 4 over pe), their kv/pe fragments read through a ring of kRing registers
+  // kRing - 1 MFMAs ahead.  After each group of four MFMAs comes one of the nine DMA instructions
+  // of tile `rtile` (when `refill`), so that a full memory queue stalls one instruction at a time.
+  constexpr int kRing = 6;
+  auto scores = [&](int j, f32x16 &sc, bool refill, int rtile) __attribute__((always_inline)) {
     const unsigned char *st = smem + (j % kStages) * kStageBytes;
-    const int t0 = t_begin + j * kTile;
-
-    // ---- scores S^T[position][row] over the 576-wide concatenation of kv and pe; the nine DMA
-    // instructions of tile j+2 are spread over the MFMA groups so that a full memory queue
-    // stalls one instruction at a time
-    f32x16 sacc;
-    {
-      u32x4 fr[2][4], qp[4];
+    auto frag = [&](int k) __attribute__((always_inline)) -> u32x4 {
+      return k < 32 ? lds_read16(st, (sc_base ^ uint32_t((k & 7) * 32)) + (k >> 3) * 256)
+                    : lds_read16(st, pe_base ^ uint32_t((k - 32) * 32));
+    };
+    u32x4 fr[kRing], qp[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) fr[0][i] = lds_read16(st, sc_off[i]);
+    for (int k = 0; k < kRing - 1; ++k) fr[k] = frag(k);
 #pragma unroll
-      for (int grp = 0; grp < 9; ++grp) {
-        const int cur = grp & 1;
-        if (grp + 1 < 8) {
-          const int k0 = 4 * (grp + 1);
+    for (int grp = 0; grp < 9; ++grp) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) fr[cur ^ 1][i] = lds_read16(st, sc_off[(k0 + i) & 7] + ((k0 + i) >> 3) * 256);
-        } else if (grp + 1 == 8) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            fr[cur ^ 1][i] = lds_read16(st, pe_off[i]);
-            qp[i] = lds_read16(qpe_lds, qpe_off + i * 1024);
-          }
-        }
+      for (int i = 0; i < 4; ++i) {
+        const int k = 4 * grp + i;
+        if (k + kRing - 1 < 36) fr[(k + kRing - 1) % kRing] = frag(k + kRing - 1);
+        if (k >= 28 && k < 32) qp[k - 28] = lds_read16(qpe_lds, qpe_off + (k - 28) * 1024);
         __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const u32x4 &qb = grp < 8 ? qf[4 * grp + i] : qp[i];
-          if (grp == 0 && i == 0) mfma32_v_first(sacc, fr[cur][i], qb);
-          else if (grp == 8 && i == 3) mfma32_v_last(sacc, fr[cur][i], qb);
-          else mfma32_v(sacc, fr[cur][i], qb);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        if (refill) issue_part(j + 2, grp);
+        const u32x4 &qb = k < 32 ? qf[k] : qp[k - 32];
+        if (k == 0) mfma32_v_first(sc, fr[k % kRing], qb);
+        else if (k == 35) mfma32_v_last(sc, fr[k % kRing], qb);
+        else mfma32_v(sc, fr[k % kRing], qb);
         __builtin_amdgcn_sched_barrier(0);
       }
+      if (refill) issue_part(rtile, grp);
+      __builtin_amdgcn_sched_barrier(0);
     }
+  };
 
-    // ---- online softmax (log2 domain); register r holds position 16*(r/8) + 8*g + r%8
+  // ---- online softmax (log2 domain) of one tile's scores; register r holds position
+  // 16*(r/8) + 8*g + r%8 of the tile
+  float mrow = 0.f;
+  auto sm_mask = [&](f32x16 &sc, int t0) __attribute__((always_inline)) {
     if (t0 + kTile > wg_full) {  // wavefront-uniform: positions past a row's last visible one
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int t = t0 + 16 * (r >> 3) + 8 * g + (r & 7);
-        if (t >= row_end) sacc[r] = -INFINITY;
+        if (t >= row_end) sc[r] = -INFINITY;
       }
     }
+  };
+  auto sm_max = [&](const f32x16 &sc) __attribute__((always_inline)) {
     float mloc = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sacc[r]);
-    const float mrow = xor32_max(mloc) * a.scale_log2;  // scale > 0
-    if (m_ref == -INFINITY) {
-      m_ref = mrow;  // first visible positions: nothing accumulated yet
-    } else if (mrow > m_ref + kRescale) {
-      const float alpha = fast_exp2(m_ref - mrow);
-      lsum *= alpha;
-      m_ref = mrow;
+    for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sc[r]);
+    mrow = xor32_max(mloc) * a.scale_log2;  // scale > 0
+  };
+  // Moving the reference max scales the running sum at once; the accumulators are scaled by
+  // apply_rescale() once the P.V product of the tiles before this one is complete (the softmax of
+  // a tile runs while that product is still accumulating).
+  // Written without branches so that it can be interleaved with the P.V MFMAs.
+  float alpha_pending = 1.f;
+  auto sm_ref = [&]() __attribute__((always_inline)) {
+    const bool first = m_ref == -INFINITY;  // first visible positions: nothing accumulated yet
+    const float m_new = (first || mrow > m_ref + kRescale) ? mrow : m_ref;
+    const float alpha = first ? 1.f : fast_exp2(m_ref - m_new);  // exactly 1 when m_new == m_ref
+    lsum *= alpha;
+    alpha_pending = alpha;
+    m_ref = m_new;
+  };
+  auto apply_rescale = [&]() __attribute__((always_inline)) {
+    if (alpha_pending != 1.f) {
 #pragma unroll
       for (int i = 0; i < 16; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][r] = agpr_write(agpr_read(acc[i][r]) * alpha);
+        for (int r = 0; r < 16; ++r) acc[i][r] = agpr_write(agpr_read(acc[i][r]) * alpha_pending);
+      alpha_pending = 1.f;
     }
+  };
+  // probabilities of positions 16 h .. 16 h + 15 (the B operand of K half h of the P.V product)
+  auto sm_probs = [&](const f32x16 &sc, int h) __attribute__((always_inline)) -> u32x4 {
     const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
-    // probabilities of positions 0..15 (B operand of the first K half) now; those of positions
-    // 16..31 are computed while the first half's sixteen MFMAs run
-    auto probs = [&](int h) __attribute__((always_inline)) -> u32x4 {
-      float p[8];
+    float p[8];
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        p[r] = fast_exp2(fmaf(sacc[8 * h + r], a.scale_log2, -m_use));
-        lsum += p[r];
-      }
-      return u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                   pack_bf16x2(p[6], p[7])};
-    };
-    u32x4 pb[2];
-    pb[0] = probs(0);
-
-    // ---- O^T[c][row] += KV^T[c][position] . P^T[position][row], first K half (positions 0..15)
-    // over all 16 column blocks, then the second half
-    {
-      auto trl = [&](int n, int ks) __attribute__((always_inline)) -> u32x4 {
-        return lds_read_tr_pair(st, tr_off[n & 3][0] + (n >> 2) * 256 + ks * 16384,
-                                tr_off[n & 3][1] + (n >> 2) * 256 + ks * 16384);
-      };
-      // ring of four A fragments, three MFMAs ahead
-      u32x4 fr[4];
-#pragma unroll
-      for (int step = 0; step < 3; ++step) fr[step] = trl(step, 0);
-#pragma unroll
-      for (int step = 0; step < 32; ++step) {
-        const int ks = step >> 4, cb = step & 15;
-        if (step + 3 < 32) fr[(step + 3) & 3] = trl((step + 3) & 15, (step + 3) >> 4);
-        __builtin_amdgcn_sched_barrier(0);
-        acc[cb] = mfma32(fr[step & 3], pb[ks], acc[cb]);
-        if (step == 1) pb[1] = probs(1);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+    for (int r = 0; r < 8; ++r) {
+      p[r] = fast_exp2(fmaf(sc[8 * h + r], a.scale_log2, -m_use));
+      lsum += p[r];
     }
+    return u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                 pack_bf16x2(p[6], p[7])};
+  };
+
+  // ---- O^T[c][row] += KV^T[c][position] . P^T[position][row] for tile j: 32 MFMAs, first K half
+  // (positions 0..15) over all 16 column blocks, then the second half.  The transposed A fragments
+  // go through a ring of four registers, three MFMAs ahead.  pv_steps runs steps [lo, hi), so that
+  // other work can be placed between ranges (the bounds are constants at every call).
+  auto trl = [&](int j, int n, int ks) __attribute__((always_inline)) -> u32x4 {
+    const unsigned char *st = smem + (j % kStages) * kStageBytes;
+    return lds_read_tr_pair(st, (tr_base[0] ^ uint32_t((n & 3) * 64)) + (n >> 2) * 256 + ks * 16384,
+                            (tr_base[1] ^ uint32_t((n & 3) * 64)) + (n >> 2) * 256 + ks * 16384);
+  };
+  u32x4 trf[4];
+  auto pv_begin = [&](int j) __attribute__((always_inline)) {
+#pragma unroll
+    for (int step = 0; step < 3; ++step) trf[step] = trl(j, step, 0);
+  };
+  auto pv_steps = [&](int j, const u32x4 (&pb)[2], int lo, int hi) __attribute__((always_inline)) {
+#pragma unroll
+    for (int step = lo; step < hi; ++step) {
+      const int ks = step >> 4, cb = step & 15;
+      if (step + 3 < 32) trf[(step + 3) & 3] = trl(j, (step + 3) & 15, (step + 3) >> 4);
+      __builtin_amdgcn_sched_barrier(0);
+      acc[cb] = mfma32(trf[step & 3], pb[ks], acc[cb]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // The same 32 steps with no fixed order, for a block that the caller interleaves with other
+  // vector work through scheduling-group barriers.
+  auto pv_all_free = [&](int j, const u32x4 (&pb)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int step = 0; step < 32; ++step) {
+      const int ks = step >> 4, cb = step & 15;
+      if (step + 3 < 32) trf[(step + 3) & 3] = trl(j, (step + 3) & 15, (step + 3) >> 4);
+      acc[cb] = mfma32(trf[step & 3], pb[ks], acc[cb]);
+    }
+  };
+
+  // Software pipeline over tiles: iteration j runs the score MFMAs of tile j + 1, then the P.V
+  // MFMAs of tile j while the vector ALU does the softmax of tile j + 1.  Tiles j and j + 1 are
+  // read in iteration j; tile j + 3 is refilled into the stage of tile j - 1, which every wave has
+  // finished after the iteration's barrier.  Tiles 0..2 are issued by the prologue in any case
+  // (rows clamped), which keeps the wait counts exact.
+  f32x16 sacc;
+  u32x4 pb[2];  // probabilities of the tile whose P.V product comes next
+  if (ntiles > 0) {
+    wait_vmcnt<2 * kLoadsPerTile>();  // tile 0 has landed; tiles 1 and 2 may be in flight
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+    scores(0, sacc, false, 0);
+    sm_mask(sacc, t_begin);
+    sm_max(sacc);
+    sm_ref();
+    pb[0] = sm_probs(sacc, 0);
+    pb[1] = sm_probs(sacc, 1);
+  }
+#pragma unroll 1
+  for (int j = 0; j + 1 < ntiles; ++j) {
+    // tile j+1 must have landed; tile j+2 (issued one iteration ago, or by the prologue) may not
+    if (j + 2 < ntiles) wait_vmcnt<kLoadsPerTile>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+    scores(j + 1, sacc, j + 3 < ntiles, j + 3);
+    const int t1 = t_begin + (j + 1) * kTile;
+    sm_mask(sacc, t1);
+    u32x4 pn[2];
+    pv_begin(j);
+    __builtin_amdgcn_sched_barrier(0);
+    // one block: the P.V MFMAs of tile j with the softmax of tile j + 1 spread between them (each
+    // MFMA followed by up to three vector instructions and two LDS reads)
+    pv_all_free(j, pb);
+    sm_max(sacc);
+    sm_ref();
+    pn[0] = sm_probs(sacc, 0);
+    pn[1] = sm_probs(sacc, 1);
+    // keeps the compiler from sinking the softmax below the block (its results are used only later)
+    asm volatile("" : "+v"(pn[0]), "+v"(pn[1]), "+v"(lsum));
+#pragma unroll
+    for (int step = 0; step < 32; ++step) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    apply_rescale();
+    pb[0] = pn[0];
+    pb[1] = pn[1];
+  }
+  if (ntiles > 0) {
+    pv_begin(ntiles - 1);
+    pv_steps(ntiles - 1, pb, 0, 32);
   }
 
   // ---- partial state of this split: max (log2 units), sum, unnormalised o.  o goes through LDS
