@@ -198,7 +198,9 @@ expand_kernel(ExpandArgs a) {
     }
   }
   // same wavefront wrote these rows; LDS operations of one wavefront complete in order
-  const int rows_valid = max(0, min(64, a.T - (t0 + wt * 64)));
+  // (re-scalarised: the store descriptor must live in scalar registers, or every store becomes a
+  // loop over lanes)
+  const int rows_valid = __builtin_amdgcn_readfirstlane(max(0, min(64, a.T - (t0 + wt * 64))));
   const rsrc_t ores = make_rsrc((wj == 0 ? a.k_nope : a.v) + (int64_t(h) * a.T + t0 + wt * 64) * 128,
                                 uint32_t(rows_valid) * 256);
   const uint32_t rd_lane = uint32_t(lane >> 4) * kEpiPitch + (lane & 15) * 16;
