@@ -449,7 +449,11 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(AbsorbQArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int l32 = lane & 31, g = lane >> 5;
-  const int h = blockIdx.x;
+  // Heads that share the fragment buffer's 128-byte lines (rows 4k .. 4k+3 of a 32-row group) run
+  // on one XCD, so their partial-line stores merge in its L2.  Workgroups reach the XCDs
+  // round-robin by linear id, whose residue mod 8 is blockIdx.x mod 8 (gridDim.x = H is a multiple
+  // of 8 here; otherwise only the merging is lost).
+  const int h = __builtin_amdgcn_readfirstlane(xcd_logical_id(blockIdx.x, gridDim.x));
   const int c0 = blockIdx.y * 128;
   const int rb0 = blockIdx.z * a.row_blocks_per_wg;
   const int nrb = (a.M + 31) / 32;
