@@ -14,6 +14,7 @@
 // Rows are the B*S*H query rows in (b, s, h) order.  Every kv/pe row of a split is read from HBM
 // once per 128-row block and shared through LDS by all of the block's heads.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "launch.h"
@@ -634,42 +635,67 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineArgs a) {
       for (int k = 0; k < 4; ++k)
         if (wave + 4 * k < nrows) lds_write16(ol, row_swz16(wave + 4 * k, lane), v[k]);
     }
-    // combine: wave w takes rows w, w + 4, w + 8, w + 12; lane = 16-byte chunk of the row; up to
-    // kCombineLoads split rows in flight
-#pragma unroll 1
-    for (int r = wave; r < (kSingle ? 0 : nrows); r += 4) {
-      const int64_t row = int64_t(m0 + r) * a.H + h;
-      const float *ml = a.part_ml + row * a.splits * 2;
-      const uint16_t *po = a.part_o + row * a.splits * kC + lane * 8;
-      const float mx = mstat[r][0], inv = mstat[r][1];
-      float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      auto add = [&](const u32x4 &v, float mi) __attribute__((always_inline)) {
-        const float w = (mi == -INFINITY) ? 0.f : fast_exp2(mi - mx);
+    // combine: wave w takes rows w, w + 4, w + 8, w + 12 (NR of them); lane = 16-byte chunk of the
+    // row.  The split rows of all NR rows are loaded kCombineLoads at a time (SB splits per row), so
+    // a whole group costs splits * NR / kCombineLoads memory round trips.
+    auto combine_rows = [&](auto nr_tag) __attribute__((always_inline)) {
+      constexpr int NR = decltype(nr_tag)::value;
+      constexpr int SB = kCombineLoads / NR;
+      const uint16_t *po[NR];
+      const float *ml[NR];
+      float mx[NR], inv[NR], acc[NR][8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc[2 * e] = fmaf(w, __uint_as_float(v[e] << 16), acc[2 * e]);
-          acc[2 * e + 1] = fmaf(w, __uint_as_float(v[e] & 0xffff0000u), acc[2 * e + 1]);
-        }
-      };
-      int i = 0;
-      for (; i + kCombineLoads <= a.splits; i += kCombineLoads) {
-        u32x4 v[kCombineLoads];
+      for (int k = 0; k < NR; ++k) {
+        const int r = min(wave + 4 * k, nrows - 1);  // rows past nrows repeat a valid one, unwritten
+        const int64_t row = int64_t(m0 + r) * a.H + h;
+        po[k] = a.part_o + row * a.splits * kC + lane * 8;
+        ml[k] = a.part_ml + row * a.splits * 2;
+        mx[k] = mstat[r][0];
+        inv[k] = mstat[r][1];
 #pragma unroll
-        for (int k = 0; k < kCombineLoads; ++k) v[k] = *reinterpret_cast<const u32x4 *>(po + int64_t(i + k) * kC);
-#pragma unroll
-        for (int k = 0; k < kCombineLoads; ++k) add(v[k], ml[2 * (i + k)]);
+        for (int e = 0; e < 8; ++e) acc[k][e] = 0.f;
       }
-      for (; i + 4 <= a.splits; i += 4) {
-        u32x4 v[4];
+      for (int i0 = 0; i0 < a.splits; i0 += SB) {
+        // splits past the last repeat it with weight 0 (no branches between the loads); the split
+        // maxima and the partial rows are all requested before any is used
+        u32x4 v[NR][SB];
+        float mi[NR][SB];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) v[k] = *reinterpret_cast<const u32x4 *>(po + int64_t(i + k) * kC);
+        for (int k = 0; k < NR; ++k)
 #pragma unroll
-        for (int k = 0; k < 4; ++k) add(v[k], ml[2 * (i + k)]);
+          for (int s = 0; s < SB; ++s) mi[k][s] = ml[k][2 * min(i0 + s, a.splits - 1)];
+#pragma unroll
+        for (int k = 0; k < NR; ++k)
+#pragma unroll
+          for (int s = 0; s < SB; ++s)
+            v[k][s] = *reinterpret_cast<const u32x4 *>(po[k] + int64_t(min(i0 + s, a.splits - 1)) * kC);
+#pragma unroll
+        for (int k = 0; k < NR; ++k)
+#pragma unroll
+          for (int s = 0; s < SB; ++s) {
+            const float w = (mi[k][s] == -INFINITY || i0 + s >= a.splits) ? 0.f : fast_exp2(mi[k][s] - mx[k]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              acc[k][2 * e] = fmaf(w, __uint_as_float(v[k][s][e] << 16), acc[k][2 * e]);
+              acc[k][2 * e + 1] = fmaf(w, __uint_as_float(v[k][s][e] & 0xffff0000u), acc[k][2 * e + 1]);
+            }
+          }
       }
-      for (; i < a.splits; ++i) add(*reinterpret_cast<const u32x4 *>(po + int64_t(i) * kC), ml[2 * i]);
-      const u32x4 pk{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
-                     pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)};
-      lds_write16(ol, row_swz16(r, lane), pk);
+#pragma unroll
+      for (int k = 0; k < NR; ++k) {
+        if (wave + 4 * k >= nrows) continue;
+        const u32x4 pk{pack_bf16x2(acc[k][0] * inv[k], acc[k][1] * inv[k]),
+                       pack_bf16x2(acc[k][2] * inv[k], acc[k][3] * inv[k]),
+                       pack_bf16x2(acc[k][4] * inv[k], acc[k][5] * inv[k]),
+                       pack_bf16x2(acc[k][6] * inv[k], acc[k][7] * inv[k])};
+        lds_write16(ol, row_swz16(wave + 4 * k, lane), pk);
+      }
+    };
+    if (!kSingle) {
+      const int nr = wave < nrows ? (nrows - wave + 3) / 4 : 0;  // wavefront-uniform
+      if (nr >= 3) combine_rows(std::integral_constant<int, 4>{});
+      else if (nr == 2) combine_rows(std::integral_constant<int, 2>{});
+      else if (nr == 1) combine_rows(std::integral_constant<int, 1>{});
     }
     if (grp == g_begin) wait_vmcnt<0>();  // W_UV rows (LDS DMA) before the first use
     __syncthreads();
