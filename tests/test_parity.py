@@ -159,6 +159,24 @@ def test_mfma_shapes(gpu_lib, kw):
     check(out, oracle_attn(cfg, x), TOL["bf16"], f"mfma {kw}")
 
 
+@pytest.mark.parametrize("kw", [
+    # 11 query rows per head: waves of the combine take 3, 3, 3 and 2 rows (a clamped repeat row),
+    # 7 splits against batches of 4; 12 heads: workgroup counts that are not multiples of 8
+    dict(batch=1, seqlen_q=11, n_heads=12, end_pos=300, splits=7),
+    # 21 rows: one full 16-row group and one of 5 (2, 1, 1, 1 rows per wave); 5 splits
+    dict(batch=3, seqlen_q=7, n_heads=20, end_pos=260, splits=5),
+    # 2 rows with 17 splits: one row per wave, two batches of 16 splits (the second mostly repeats)
+    dict(batch=2, seqlen_q=1, n_heads=40, end_pos=700, splits=17),
+])
+def test_mfma_combine_row_and_split_counts(gpu_lib, kw):
+    kw = dict(kw)
+    splits = kw.pop("splits")
+    cfg = dsv3_small(cache_batch=kw["batch"], cache_len=kw["end_pos"] + 16, **kw)
+    x = make_attn_inputs(cfg)
+    out = run_attn(gpu_lib, cfg, to_dev(x, cfg), path="mfma", splits=splits)
+    check(out, oracle_attn(cfg, x), TOL["bf16"], f"mfma {kw} splits={splits}")
+
+
 def test_mfma_repeatable_bitwise(gpu_lib):
     cfg = dsv3_small(end_pos=777, cache_len=800)
     x = make_attn_inputs(cfg)
