@@ -119,6 +119,29 @@ int32_t mla_absorb_attn(const void *q_nope, const void *q_pe, const void *kv_cac
                         size_t workspace_bytes, void *stream);
 
 /*
+ * Absorb-form MLA attention over a ragged batch: sequence b attends to its own cache positions
+ * [0, seq_lens[b]) (the page's uniform slice "[:bsz, :end_pos]" taken per sequence; its S query
+ * tokens sit at seq_lens[b] - S .. seq_lens[b] - 1, causal as in mla_absorb_attn).
+ *
+ *   seq_lens     DEVICE array of B int32 lengths (4-byte aligned), read by the kernels on the
+ *                stream; the caller guarantees S <= seq_lens[b] <= max_seq_len.  A value outside
+ *                that range is clamped into it, so no call ever reads a cache position at or past
+ *                max_seq_len (such a sequence's output is then that of the clamped length).
+ *   max_seq_len  upper bound of the lengths; 1 <= S <= max_seq_len <= Tmax.  It plays the role
+ *                of end_pos for validation, split planning and the workspace size: use
+ *                mla_absorb_attn_workspace_size(shape, max_seq_len, ...).
+ * Every other argument, the layouts and the error behaviour are those of mla_absorb_attn;
+ * out, workspace and seq_lens must not overlap.  Returns MLA_OK or a negative MLA_ERR_* status
+ * (MLA_ERR_NULL / MLA_ERR_ALIGN for seq_lens).
+ */
+int32_t mla_absorb_attn_ragged(const void *q_nope, const void *q_pe, const void *kv_cache,
+                               const void *pe_cache, const void *wkv_b, const int32_t *seq_lens,
+                               int64_t max_seq_len, float softmax_scale, void *out,
+                               const mla_attn_shape *shape, int32_t dtype,
+                               const mla_attn_options *options, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+/*
  * Bytes of device workspace mla_expand_kv needs (the normalised latent n, which the matrix-core
  * path computes once per token and every head reuses; 0 for the plain path).  Returns 0 when the
  * arguments are invalid (the same checks as mla_expand_kv; see mla_last_error).

@@ -29,7 +29,8 @@ MLA_DTYPE_BF16 = 1
 
 PATHS = {"auto": 0, "plain": 1, "mfma": 2}
 
-EXPORTED = ("mla_absorb_attn", "mla_absorb_attn_workspace_size", "mla_expand_kv", "mla_expand_kv_workspace_size",
+EXPORTED = ("mla_absorb_attn", "mla_absorb_attn_ragged", "mla_absorb_attn_workspace_size", "mla_expand_kv",
+            "mla_expand_kv_workspace_size",
             "mla_strerror",
             "mla_last_error", "mla_timing_enable", "mla_timing_collect", "mla_kernel_name")
 
@@ -67,6 +68,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_absorb_attn.argtypes = [vp, vp, vp, vp, vp, i64, ctypes.c_float, vp, ctypes.POINTER(AttnShape), i32,
                                     ctypes.POINTER(AttnOptions), vp, sz, vp]
     lib.mla_absorb_attn.restype = i32
+    lib.mla_absorb_attn_ragged.argtypes = [vp, vp, vp, vp, vp, vp, i64, ctypes.c_float, vp, ctypes.POINTER(AttnShape),
+                                           i32, ctypes.POINTER(AttnOptions), vp, sz, vp]
+    lib.mla_absorb_attn_ragged.restype = i32
     lib.mla_absorb_attn_workspace_size.argtypes = [ctypes.POINTER(AttnShape), i64, i32, ctypes.POINTER(AttnOptions)]
     lib.mla_absorb_attn_workspace_size.restype = sz
     lib.mla_expand_kv.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float, i32, i32, vp, sz, vp]
@@ -176,7 +180,9 @@ class AbsorbAttnCall:
     """
 
     def __init__(self, q_nope, q_pe, kv_cache, pe_cache, wkv_b, end_pos: int, softmax_scale: float, out=None, *,
-                 num_splits: int = 0, path: str = "auto", workspace=None):
+                 num_splits: int = 0, path: str = "auto", workspace=None, seq_lens=None):
+        """With seq_lens (an int32 tensor [B] on the same device), sequence b attends to positions
+        [0, seq_lens[b]) and end_pos is the bound of the lengths (mla_absorb_attn_ragged)."""
         import torch
 
         lib = load()
@@ -192,12 +198,20 @@ class AbsorbAttnCall:
         if workspace is None or workspace.numel() * workspace.element_size() < need:
             workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q_nope.device)
         self.out = out
-        self._keep = (q_nope, q_pe, kv_cache, pe_cache, wkv_b, out, workspace, shape, opt)
-        self._fn = lib.mla_absorb_attn
-        self._args = (q_nope.data_ptr(), q_pe.data_ptr(), kv_cache.data_ptr(), pe_cache.data_ptr(), wkv_b.data_ptr(),
-                      end_pos, softmax_scale, out.data_ptr(), ctypes.byref(shape), dt, ctypes.byref(opt),
-                      workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                      _stream_handle(q_nope.device))
+        self._keep = (q_nope, q_pe, kv_cache, pe_cache, wkv_b, out, workspace, shape, opt, seq_lens)
+        tail = (softmax_scale, out.data_ptr(), ctypes.byref(shape), dt, ctypes.byref(opt), workspace.data_ptr(),
+                workspace.numel() * workspace.element_size(), _stream_handle(q_nope.device))
+        head = (q_nope.data_ptr(), q_pe.data_ptr(), kv_cache.data_ptr(), pe_cache.data_ptr(), wkv_b.data_ptr())
+        if seq_lens is None:
+            self._fn = lib.mla_absorb_attn
+            self._args = head + (end_pos,) + tail
+        else:
+            if seq_lens.device != q_nope.device or seq_lens.dtype != torch.int32 or not seq_lens.is_contiguous():
+                raise ValueError("seq_lens must be a contiguous int32 tensor on the tensors' device")
+            if seq_lens.numel() != shape.batch:
+                raise ValueError("seq_lens must hold one length per sequence")
+            self._fn = lib.mla_absorb_attn_ragged
+            self._args = head + (seq_lens.data_ptr(), end_pos) + tail
 
     def __call__(self):
         _check(self._fn(*self._args))
@@ -205,10 +219,11 @@ class AbsorbAttnCall:
 
 
 def absorb_attn(q_nope, q_pe, kv_cache, pe_cache, wkv_b, end_pos: int, softmax_scale: float, out=None, *,
-                num_splits: int = 0, path: str = "auto", workspace=None):
-    """MLA attention in absorb form on torch GPU tensors; returns out [B, S, H, Dv]."""
+                num_splits: int = 0, path: str = "auto", workspace=None, seq_lens=None):
+    """MLA attention in absorb form on torch GPU tensors; returns out [B, S, H, Dv].  With
+    seq_lens, a ragged batch whose lengths are bounded by end_pos."""
     return AbsorbAttnCall(q_nope, q_pe, kv_cache, pe_cache, wkv_b, end_pos, softmax_scale, out,
-                          num_splits=num_splits, path=path, workspace=workspace)()
+                          num_splits=num_splits, path=path, workspace=workspace, seq_lens=seq_lens)()
 
 
 def expand_kv_workspace_size(n_tokens: int, n_heads: int, kv_lora_rank: int, qk_nope_head_dim: int,

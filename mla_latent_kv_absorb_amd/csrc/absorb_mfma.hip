@@ -74,7 +74,8 @@ struct AttnArgs {
                            // split: normalised, i.e. o_lat)
   int64_t Tmax;
   int32_t S, H, SH;        // SH = S * H rows per sequence
-  int32_t end_pos, splits, split_len, row_blocks;
+  int32_t end_pos, splits, split_len, row_blocks;  // end_pos: uniform length or the bound of seq_lens
+  const int32_t *seq_lens;  // per-sequence lengths [B] or null (every sequence has end_pos)
   float scale_log2;        // softmax_scale * log2(e)
 };
 
@@ -105,15 +106,18 @@ attn_kernel(AttnArgs a) {
   const int s = row_ok ? lrow / a.H : 0;
   const int64_t grow = int64_t(b) * a.SH + lrow;
   const int t_begin = split * a.split_len;
-  const int t_split_end = min(t_begin + a.split_len, a.end_pos);
-  const int row_end = row_ok ? min(t_split_end, a.end_pos - a.S + s + 1) : t_begin;
+  // this sequence's length: a ragged batch reads it from seq_lens, clamped to [S, end_pos] so that
+  // no access leaves the positions the caller vouched for
+  const int end_pos = a.seq_lens ? __builtin_amdgcn_readfirstlane(min(max(a.seq_lens[b], a.S), a.end_pos)) : a.end_pos;
+  const int t_split_end = min(t_begin + a.split_len, end_pos);
+  const int row_end = row_ok ? min(t_split_end, end_pos - a.S + s + 1) : t_begin;
   // Positions the workgroup needs (up to the last visible one of its last row), and the prefix
   // visible to all of its rows (tiles inside it need no mask).  Integer division runs on the
   // vector ALU, so the uniform results are re-scalarised.
   const int first_row = rb * kRowsWG;
   const int last_row = min(a.SH - 1, first_row + kRowsWG - 1);
-  const int wg_end = __builtin_amdgcn_readfirstlane(min(t_split_end, a.end_pos - a.S + last_row / a.H + 1));
-  const int wg_full = __builtin_amdgcn_readfirstlane(min(t_split_end, a.end_pos - a.S + first_row / a.H + 1));
+  const int wg_end = __builtin_amdgcn_readfirstlane(min(t_split_end, end_pos - a.S + last_row / a.H + 1));
+  const int wg_full = __builtin_amdgcn_readfirstlane(min(t_split_end, end_pos - a.S + first_row / a.H + 1));
   const int ntiles = __builtin_amdgcn_readfirstlane(wg_end > t_begin ? (wg_end - t_begin + kTile - 1) / kTile : 0);
 
   // DMA geometry.  kv: wave w moves tile rows 8w..8w+7, one 1 KB row per instruction; lane l owns
@@ -810,6 +814,7 @@ hipError_t mfma_absorb_attn(const AttnCall &c) {
   aa.H = int32_t(c.H);
   aa.SH = int32_t(c.S * c.H);
   aa.end_pos = int32_t(c.end_pos);
+  aa.seq_lens = c.seq_lens;
   aa.splits = c.splits;
   aa.split_len = int32_t(c.split_len);
   aa.row_blocks = row_blocks;

@@ -10,7 +10,8 @@ namespace mla {
 // One validated absorb-attention call.  Rows are the B*S*H query rows in (b, s, h) order.
 struct AttnCall {
   int64_t B, S, H, C, R, Dn, Dv, Bmax, Tmax;
-  int64_t end_pos;
+  int64_t end_pos;           // uniform length, or the upper bound of the per-sequence lengths
+  const int32_t *seq_lens;   // device [B] per-sequence lengths (clamped to [S, end_pos]), or null
   float scale;
   int32_t dtype;      // MLA_DTYPE_*
   int32_t splits;     // ranges the positions [0, end_pos) are cut into

@@ -134,11 +134,15 @@ size_t mla_absorb_attn_workspace_size(const mla_attn_shape *shape, int64_t end_p
   return use_mfma ? mla::mfma_attn_workspace(c) : mla::plain_attn_workspace(c);
 }
 
-int32_t mla_absorb_attn(const void *q_nope, const void *q_pe, const void *kv_cache, const void *pe_cache,
-                        const void *wkv_b, int64_t end_pos, float softmax_scale, void *out,
-                        const mla_attn_shape *shape, int32_t dtype, const mla_attn_options *options,
-                        void *workspace, size_t workspace_bytes, void *stream) {
-  clear_error();
+}  // extern "C"
+
+namespace {
+
+// The body of mla_absorb_attn and mla_absorb_attn_ragged (seq_lens null for a uniform batch).
+int32_t absorb_attn_call(const void *q_nope, const void *q_pe, const void *kv_cache, const void *pe_cache,
+                         const void *wkv_b, const int32_t *seq_lens, int64_t end_pos, float softmax_scale,
+                         void *out, const mla_attn_shape *shape, int32_t dtype, const mla_attn_options *options,
+                         void *workspace, size_t workspace_bytes, void *stream) {
   mla::AttnCall c;
   bool use_mfma = false;
   int32_t rc = plan_attn(shape, end_pos, dtype, options, c, use_mfma);
@@ -159,6 +163,8 @@ int32_t mla_absorb_attn(const void *q_nope, const void *q_pe, const void *kv_cac
   const size_t out_bytes = rows * size_t(c.Dv) * es;
   for (int i = 0; i < 5; ++i)
     if (overlaps(out, out_bytes, ptrs[i], bytes_in[i])) return fail(MLA_ERR_SHAPE, "out overlaps %s", names[i]);
+  const size_t lens_bytes = size_t(c.B) * sizeof(int32_t);
+  if (seq_lens && overlaps(out, out_bytes, seq_lens, lens_bytes)) return fail(MLA_ERR_SHAPE, "out overlaps seq_lens");
   const size_t need = use_mfma ? mla::mfma_attn_workspace(c) : mla::plain_attn_workspace(c);
   if (need > 0) {
     if (!workspace) return fail(MLA_ERR_WORKSPACE, "workspace is NULL but %zu bytes are needed", need);
@@ -169,14 +175,42 @@ int32_t mla_absorb_attn(const void *q_nope, const void *q_pe, const void *kv_cac
     for (int i = 0; i < 5; ++i)
       if (overlaps(workspace, need, ptrs[i], bytes_in[i]))
         return fail(MLA_ERR_WORKSPACE, "workspace overlaps %s", names[i]);
+    if (seq_lens && overlaps(workspace, need, seq_lens, lens_bytes))
+      return fail(MLA_ERR_WORKSPACE, "workspace overlaps seq_lens");
   }
   c.scale = softmax_scale;
   c.q_nope = q_nope; c.q_pe = q_pe; c.kv = kv_cache; c.pe = pe_cache; c.wkv_b = wkv_b;
   c.out = out; c.ws = workspace; c.stream = static_cast<hipStream_t>(stream);
+  c.seq_lens = seq_lens;
   if (use_mfma && c.splits == 0) c.splits = 1;
   hipError_t e = use_mfma ? mla::mfma_absorb_attn(c) : mla::plain_absorb_attn(c);
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t mla_absorb_attn(const void *q_nope, const void *q_pe, const void *kv_cache, const void *pe_cache,
+                        const void *wkv_b, int64_t end_pos, float softmax_scale, void *out,
+                        const mla_attn_shape *shape, int32_t dtype, const mla_attn_options *options,
+                        void *workspace, size_t workspace_bytes, void *stream) {
+  clear_error();
+  return absorb_attn_call(q_nope, q_pe, kv_cache, pe_cache, wkv_b, nullptr, end_pos, softmax_scale, out, shape,
+                          dtype, options, workspace, workspace_bytes, stream);
+}
+
+int32_t mla_absorb_attn_ragged(const void *q_nope, const void *q_pe, const void *kv_cache, const void *pe_cache,
+                               const void *wkv_b, const int32_t *seq_lens, int64_t max_seq_len,
+                               float softmax_scale, void *out, const mla_attn_shape *shape, int32_t dtype,
+                               const mla_attn_options *options, void *workspace, size_t workspace_bytes,
+                               void *stream) {
+  clear_error();
+  if (!seq_lens) return fail(MLA_ERR_NULL, "seq_lens is NULL");
+  if (reinterpret_cast<uintptr_t>(seq_lens) & 3u) return fail(MLA_ERR_ALIGN, "seq_lens is not 4-byte aligned");
+  return absorb_attn_call(q_nope, q_pe, kv_cache, pe_cache, wkv_b, seq_lens, max_seq_len, softmax_scale, out, shape,
+                          dtype, options, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -50,10 +50,17 @@ plain_attn_partial_kernel(const float *__restrict__ q_lat, const T *__restrict__
   const int tid = threadIdx.x;
   const int64_t b = row / (a.S * a.H);
   const int64_t s = (row / a.H) % a.S;
-  const int64_t last = a.end_pos - a.S + s;  // last visible position of this query
+  // this sequence's length (a ragged batch clamps seq_lens[b] to [S, end_pos])
+  int64_t end_pos = a.end_pos;
+  if (a.seq_lens) {
+    end_pos = a.seq_lens[b];
+    if (end_pos < a.S) end_pos = a.S;
+    if (end_pos > a.end_pos) end_pos = a.end_pos;
+  }
+  const int64_t last = end_pos - a.S + s;  // last visible position of this query
   const int64_t t0 = int64_t(split) * a.split_len;
   int64_t t1 = t0 + a.split_len;
-  if (t1 > a.end_pos) t1 = a.end_pos;
+  if (t1 > end_pos) t1 = end_pos;
   if (t1 > last + 1) t1 = last + 1;
 
   for (int64_t c = tid; c < a.C; c += kThreads) { sq[c] = q_lat[row * a.C + c]; so[c] = 0.f; }

@@ -17,6 +17,9 @@ Recipe
   ``N(0, v)`` means variance ``v``.
 * Attention workloads draw, in order: q_nope, q_pe, kv_cache, pe_cache, wkv_b.
 * Expansion workloads draw, in order: c_kv, rms_w, wkv_b.
+* Ragged batches take an attention workload (whose end_pos is the bound of the
+  lengths) and draw the per-sequence lengths from their own generator:
+  ``default_rng(seed).integers(lo, hi + 1, size=batch)``.
 * bf16 workloads round each fp32 draw to bfloat16 with round-to-nearest-even;
   the arrays are returned as float32 holding exactly-representable bf16 values,
   so an upcast on either side is exact.
@@ -38,6 +41,8 @@ __all__ = [
     "bf16_bits",
     "make_attn_inputs",
     "make_expand_inputs",
+    "RAGGED_CONFIGS",
+    "ragged_lengths",
 ]
 
 
@@ -137,6 +142,18 @@ EXPAND_CONFIGS: Dict[str, ExpandConfig] = {
         "dsv3_expand", "bf16", n_tokens=8192, n_heads=128, kv_lora_rank=512, qk_nope_head_dim=128,
         v_head_dim=128, eps=1e-6, wkv_b_var=1.0 / 512, rms_w_var=0.02, seed=4),
 }
+
+
+# Ragged-batch workloads: (attention workload, lowest length, highest length, seed of the lengths).
+# The decode one stands in for a serving batch whose sequences have different context lengths.
+RAGGED_CONFIGS: Dict[str, tuple] = {
+    "ragged_decode": ("dsv3_decode", 256, 4096, 5),
+}
+
+
+def ragged_lengths(batch: int, lo: int, hi: int, seed: int) -> np.ndarray:
+    """Per-sequence lengths drawn uniformly from [lo, hi] (int32)."""
+    return np.random.default_rng(seed).integers(lo, hi + 1, size=batch).astype(np.int32)
 
 
 def _draw(rng: np.random.Generator, shape, std: float, mean: float = 0.0) -> np.ndarray:

@@ -32,6 +32,9 @@ Readings adopted where the pages are silent (each is listed in the design doc):
     normalise.  The expansion normalises raw c_kv with
     x / sqrt(mean(x^2) + eps) * w, eps inside the square root.
   * The softmax scale multiplies the sum of both score terms.
+  * A ragged batch (each sequence with its own length) takes the page's slice
+    [:bsz, :end_pos] per sequence: sequence b attends to positions
+    [0, seq_lens[b]) with its queries at seq_lens[b] - S + s.
 """
 from __future__ import annotations
 
@@ -49,6 +52,7 @@ __all__ = [
     "attention_partial",
     "merge_partials",
     "absorb_attention_rows",
+    "absorb_attention_ragged",
     "rms_norm",
     "expand_kv",
 ]
@@ -239,6 +243,26 @@ def absorb_attention_rows(q_nope, q_pe, kv_cache, pe_cache, wkv_b, end_pos: int,
         o_lat = p @ kv
         res.append(w_uv[h] @ o_lat)
     return np.stack(res)
+
+
+def absorb_attention_ragged(q_nope, q_pe, kv_cache, pe_cache, wkv_b, seq_lens, softmax_scale: float,
+                            v_head_dim: int, dtype=np.float64, rows: Iterable[Tuple[int, int, int]] = None):
+    """absorb_attention for a batch whose sequences have their own lengths.
+
+    Sequence b is absorb_attention on that sequence alone with end_pos = seq_lens[b] (the
+    page's slice [:bsz, :end_pos] taken per sequence).  With `rows`, only those (b, s, h)
+    outputs are evaluated (as absorb_attention_rows) and [len(rows), Dv] is returned.
+    """
+    B = q_nope.shape[0]
+    if rows is not None:
+        res = [absorb_attention_rows(q_nope[b:b + 1], q_pe[b:b + 1], kv_cache[b:b + 1], pe_cache[b:b + 1], wkv_b,
+                                     int(seq_lens[b]), softmax_scale, v_head_dim, [(0, s, h)], dtype)[0]
+               for b, s, h in rows]
+        return np.stack(res)
+    out = [absorb_attention(q_nope[b:b + 1], q_pe[b:b + 1], kv_cache[b:b + 1], pe_cache[b:b + 1], wkv_b,
+                            int(seq_lens[b]), softmax_scale, v_head_dim, dtype)
+           for b in range(B)]
+    return np.concatenate(out, axis=0)
 
 
 def rms_norm(x, w, eps: float, dtype=np.float64):

@@ -163,3 +163,22 @@ def test_expand_workspace(lib):
     assert call_expand(lib, ws_bytes=need - 1, path=B.PATHS["mfma"]) == B.MLA_ERR_WORKSPACE
     assert call_expand(lib, ws=P[6] + 4, path=B.PATHS["mfma"]) == B.MLA_ERR_ALIGN
     assert call_expand(lib, ws=P[0], path=B.PATHS["mfma"]) == B.MLA_ERR_WORKSPACE  # overlaps c_kv
+
+
+def call_ragged(lib, s, lens, max_len=4096, ws=P[7], ws_bytes=1 << 40, out=None):
+    p = list(P[:6])
+    return lib.mla_absorb_attn_ragged(p[0], p[1], p[2], p[3], p[4], lens, max_len, 0.07, p[5] if out is None else out,
+                                      ctypes.byref(s), B.MLA_DTYPE_BF16, None, ws, ws_bytes, None)
+
+
+def test_ragged_argument_errors(lib):
+    s = shape()
+    lens = P[6]
+    assert call_ragged(lib, s, None) == B.MLA_ERR_NULL and "seq_lens" in B.last_error()
+    assert call_ragged(lib, s, lens + 2) == B.MLA_ERR_ALIGN and "seq_lens" in B.last_error()
+    # the bound plays end_pos's role in validation
+    assert call_ragged(lib, s, lens, max_len=4097) == B.MLA_ERR_RANGE
+    assert call_ragged(lib, shape(seqlen_q=8), lens, max_len=4) == B.MLA_ERR_RANGE
+    # outputs and workspace must not overlap the lengths (4-byte aligned is enough for them)
+    assert call_ragged(lib, s, lens + 4, ws=lens - 1024) == B.MLA_ERR_WORKSPACE
+    assert call_ragged(lib, s, P[5] + 64) == B.MLA_ERR_SHAPE and "seq_lens" in B.last_error()

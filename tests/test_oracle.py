@@ -258,6 +258,39 @@ def pin_expand():
     return worst
 
 
+def pin_ragged():
+    """Ragged batch: each sequence equals the naive route (a different code path) on that
+    sequence alone at its own length; cache rows past a sequence's length do not matter; equal
+    lengths give the uniform result; the row sampler agrees with the full tensor."""
+    worst = 0.0
+    for seqlen_q, lens in ((1, [1, 4, 7]), (2, [2, 5, 7])):
+        cfg = small_cfg(batch=3, cache_batch=3, seqlen_q=seqlen_q, end_pos=7, cache_len=9, seed=21 + seqlen_q)
+        x = make_attn_inputs(cfg)
+        rag = O.absorb_attention_ragged(x["q_nope"], x["q_pe"], x["kv_cache"], x["pe_cache"], x["wkv_b"], lens,
+                                        cfg.softmax_scale, cfg.v_head_dim)
+        for b, n in enumerate(lens):
+            nv = O.naive_attention(x["q_nope"][b:b + 1], x["q_pe"][b:b + 1], x["kv_cache"][b:b + 1],
+                                   x["pe_cache"][b:b + 1], x["wkv_b"], n, cfg.softmax_scale, cfg.v_head_dim)
+            worst = max(worst, rel_err(rag[b], nv[0]))
+        # garbage past each length
+        kv, pe = np.array(x["kv_cache"], np.float64), np.array(x["pe_cache"], np.float64)
+        rng = np.random.default_rng(5)
+        for b, n in enumerate(lens):
+            kv[b, n:] = rng.normal(0, 1e6, kv[b, n:].shape)
+            pe[b, n:] = rng.normal(0, 1e6, pe[b, n:].shape)
+        rag2 = O.absorb_attention_ragged(x["q_nope"], x["q_pe"], kv, pe, x["wkv_b"], lens, cfg.softmax_scale,
+                                         cfg.v_head_dim)
+        worst = max(worst, rel_err(rag2, rag))
+        rows = [(0, seqlen_q - 1, 0), (2, 0, 2), (1, seqlen_q - 1, 1)]
+        sel = O.absorb_attention_ragged(x["q_nope"], x["q_pe"], x["kv_cache"], x["pe_cache"], x["wkv_b"], lens,
+                                        cfg.softmax_scale, cfg.v_head_dim, rows=rows)
+        worst = max(worst, rel_err(sel, np.stack([rag[b, s_, h] for b, s_, h in rows])))
+        uni = O.absorb_attention_ragged(x["q_nope"], x["q_pe"], x["kv_cache"], x["pe_cache"], x["wkv_b"], [7, 7, 7],
+                                        cfg.softmax_scale, cfg.v_head_dim)
+        worst = max(worst, rel_err(uni, run("absorb", cfg, x)))
+    return worst
+
+
 PINS = {
     "naive_equals_absorb": (pin_naive_equals_absorb, 1e-12),
     "golden": (pin_golden, 1e-12),
@@ -272,6 +305,7 @@ PINS = {
     "split_merge": (pin_split_merge, 1e-12),
     "rms_norm": (pin_rms_norm, 1e-12),
     "expand": (pin_expand, 1e-12),
+    "ragged": (pin_ragged, 1e-12),
 }
 
 
@@ -369,6 +403,13 @@ def _expand_swapped(c_kv, rms_w, wkv_b, n_heads, qk_nope_head_dim, v_head_dim, e
     return y[..., v_head_dim:], y[..., :v_head_dim]
 
 
+_orig_ragged = O.absorb_attention_ragged
+
+
+def _ragged_uses_bound(q_nope, q_pe, kv_cache, pe_cache, wkv_b, seq_lens, *a, **kw):
+    return _orig_ragged(q_nope, q_pe, kv_cache, pe_cache, wkv_b, [max(seq_lens)] * len(seq_lens), *a, **kw)
+
+
 MUTATIONS = {
     "swap_uk_uv": ("split_wkv_b", _swap_split),
     "mask_off_by_one": ("allowed_positions", _off_by_one_mask),
@@ -378,6 +419,7 @@ MUTATIONS = {
     "absorb_drops_rope": ("absorb_attention", _absorb_without_rope),
     "absorb_reverses_heads": ("absorb_attention", _absorb_transposed_heads),
     "expand_split_swapped": ("expand_kv", _expand_swapped),
+    "ragged_uses_the_bound": ("absorb_attention_ragged", _ragged_uses_bound),
 }
 
 

@@ -8,8 +8,8 @@ import numpy as np
 import pytest
 import torch
 
-from mla_latent_kv_absorb_amd.workloads import (ATTN_CONFIGS, EXPAND_CONFIGS, make_attn_inputs,
-                                                 make_expand_inputs)
+from mla_latent_kv_absorb_amd.workloads import (ATTN_CONFIGS, EXPAND_CONFIGS, RAGGED_CONFIGS, make_attn_inputs,
+                                                 make_expand_inputs, ragged_lengths)
 from oracle import mla_oracle as O
 
 pytestmark = pytest.mark.gpu
@@ -222,6 +222,80 @@ def test_full_size_attention(gpu_lib, name):
     g = out.float().cpu().double().numpy()
     got = np.stack([g[b, s, h] for b, s, h in rows])
     check(got, ref, TOL["bf16"], f"{name} sampled rows")
+
+
+# --------------------------------------------------------------------------------- ragged batches
+
+def run_attn_ragged(lib, cfg, t, lens, path="auto", splits=0):
+    out = torch.full((cfg.batch, cfg.seqlen_q, cfg.n_heads, cfg.v_head_dim), float("nan"), dtype=tdtype(cfg),
+                     device="cuda")
+    seq = torch.tensor(np.asarray(lens, np.int32), device="cuda")
+    lib.absorb_attn(t["q_nope"], t["q_pe"], t["kv_cache"], t["pe_cache"], t["wkv_b"], cfg.end_pos, cfg.softmax_scale,
+                    out, num_splits=splits, path=path, seq_lens=seq)
+    torch.cuda.synchronize()
+    return out
+
+
+def poison_tails(t, lens):
+    """NaN in every cache position at or past each sequence's length: none of it may reach the output."""
+    for b, n in enumerate(lens):
+        t["kv_cache"][b, int(n):] = float("nan")
+        t["pe_cache"][b, int(n):] = float("nan")
+
+
+def oracle_ragged(cfg, x, lens, rows=None):
+    return O.absorb_attention_ragged(x["q_nope"], x["q_pe"], x["kv_cache"], x["pe_cache"], x["wkv_b"], lens,
+                                     cfg.softmax_scale, cfg.v_head_dim, rows=rows)
+
+
+@pytest.mark.parametrize("path", ["plain", "mfma"])
+@pytest.mark.parametrize("seqlen_q,lens", [(1, [1, 37, 300, 64]), (5, [5, 200, 33])])
+def test_ragged_small(gpu_lib, path, seqlen_q, lens):
+    cfg = dsv3_small(batch=len(lens), cache_batch=len(lens) + 1, seqlen_q=seqlen_q, end_pos=max(lens) + 7,
+                     cache_len=320)
+    x = make_attn_inputs(cfg)
+    t = to_dev(x, cfg)
+    poison_tails(t, lens)
+    out = run_attn_ragged(gpu_lib, cfg, t, lens, path=path)
+    check(out, oracle_ragged(cfg, x, lens), TOL["bf16"], f"ragged S={seqlen_q} lens={lens} {path}")
+
+
+@pytest.mark.parametrize("splits", [1, 3, 16])
+def test_ragged_forced_splits(gpu_lib, splits):
+    lens = [1, 700, 130, 999]
+    cfg = dsv3_small(batch=4, cache_batch=4, end_pos=1000, cache_len=1024)
+    x = make_attn_inputs(cfg)
+    t = to_dev(x, cfg)
+    poison_tails(t, lens)
+    out = run_attn_ragged(gpu_lib, cfg, t, lens, path="mfma", splits=splits)
+    check(out, oracle_ragged(cfg, x, lens), TOL["bf16"], f"ragged splits={splits}")
+
+
+def test_ragged_lengths_are_clamped(gpu_lib):
+    """Lengths outside [S, bound] behave as the nearest end of that range (and read nothing past it)."""
+    cfg = dsv3_small(batch=3, cache_batch=3, seqlen_q=2, end_pos=150, cache_len=160)
+    x = make_attn_inputs(cfg)
+    t = to_dev(x, cfg)
+    poison_tails(t, [150, 150, 150])
+    out = run_attn_ragged(gpu_lib, cfg, t, [0, 10 ** 6, -5], path="mfma")
+    check(out, oracle_ragged(cfg, x, [2, 150, 2]), TOL["bf16"], "ragged clamped lengths")
+
+
+@pytest.mark.parametrize("name", list(RAGGED_CONFIGS))
+def test_full_size_ragged(gpu_lib, name):
+    base, lo, hi, seed = RAGGED_CONFIGS[name]
+    cfg = ATTN_CONFIGS[base]
+    lens = ragged_lengths(cfg.batch, lo, hi, seed)
+    print(f"full-size {name}: B={cfg.batch} lengths {lens.min()}..{lens.max()}", flush=True)
+    x = make_attn_inputs(cfg)
+    t = to_dev(x, cfg)
+    poison_tails(t, lens)
+    out = run_attn_ragged(gpu_lib, cfg, t, lens)
+    assert torch.isfinite(out).all(), "non-finite outputs"
+    rows = sample_rows(cfg, 48, 9)
+    ref = oracle_ragged(cfg, x, lens, rows=rows)
+    g = out.float().cpu().double().numpy()
+    check(np.stack([g[b, s, h] for b, s, h in rows]), ref, TOL["bf16"], f"{name} sampled rows")
 
 
 def test_full_size_expand(gpu_lib):
