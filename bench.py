@@ -19,6 +19,8 @@ query) over its average duration, measured live by running the same timed steps 
 events that the kernel's own dispatch stamps on its stream (hipExtLaunchKernel start/stop events);
 those events add a queue barrier per timed dispatch, so that pass's step time is reported apart.
 `cpu_baseline` times the CPU oracle (NumPy, float64) on a bounded sample of the same workload.
+`extras` times the other workloads the same way: long_decode, chunk_prefill, ragged_decode (the
+decode batch with per-sequence lengths drawn uniformly from [256, 4096]) and dsv3_expand.
 """
 from __future__ import annotations
 
@@ -39,18 +41,20 @@ BF16_PEAK_TFLOPS = 2516.6
 METRIC = "MLA absorb decode µs/step, HBM GB/s & MFMA TFLOP/s as % of roofline"
 
 
-def attn_work(cfg):
-    """Algorithmic bytes and FLOPs of one absorb-attention call (caches [:B, :end_pos], wkv_b, q, out)."""
+def attn_work(cfg, lens=None):
+    """Algorithmic bytes and FLOPs of one absorb-attention call (caches [:B, :end_pos], wkv_b, q, out);
+    with lens, a ragged batch (sequence b reads positions [0, lens[b]))."""
     B, S, H = cfg.batch, cfg.seqlen_q, cfg.n_heads
     C, R, Dn, Dv, T = cfg.kv_lora_rank, cfg.qk_rope_head_dim, cfg.qk_nope_head_dim, cfg.v_head_dim, cfg.end_pos
+    lens = [T] * B if lens is None else [int(n) for n in lens]
     e = 2  # bf16
-    cache = B * T * (C + R) * e
+    cache = sum(lens) * (C + R) * e
     weights = H * (Dn + Dv) * C * e
     q = B * S * H * (Dn + R) * e
     out = B * S * H * Dv * e
-    start = T - S
-    pairs = sum(start + s + 1 for s in range(S))  # visible (query, position) pairs per (b, h)
-    flops = 2 * B * S * H * Dn * C + 2 * B * H * pairs * (C + R) + 2 * B * H * pairs * C + 2 * B * S * H * C * Dv
+    # visible (query, position) pairs per head, summed over the sequences
+    pairs = sum(n - S + s + 1 for n in lens for s in range(S))
+    flops = 2 * B * S * H * Dn * C + 2 * H * pairs * (C + R) + 2 * H * pairs * C + 2 * B * S * H * C * Dv
     return {"bytes": cache + weights + q + out, "flops": flops, "cache_bytes": cache,
             "attn_kernel_bytes": cache + B * S * H * R * e}
 
@@ -79,16 +83,18 @@ def gpu_inputs(cfg, seed, torch):
     }
 
 
-def time_attn(cfg, steps, warmup, sets, torch, binding, seed=1, timed_kernels=0b010):
-    """Returns (GPU us per step, host enqueue us per step, per-kernel timing dict)."""
+def time_attn(cfg, steps, warmup, sets, torch, binding, seed=1, timed_kernels=0b010, lens=None):
+    """Returns (GPU us per step, host enqueue us per step, per-kernel timing dict).  With lens, a
+    ragged batch (mla_absorb_attn_ragged with the lengths in device memory, bound cfg.end_pos)."""
     inputs = [gpu_inputs(cfg, seed + 1000 * i, torch) for i in range(sets)]
+    seq_lens = None if lens is None else torch.tensor([int(n) for n in lens], dtype=torch.int32, device="cuda")
     out = torch.empty((cfg.batch, cfg.seqlen_q, cfg.n_heads, cfg.v_head_dim), dtype=torch.bfloat16, device="cuda")
     shape = binding.attn_shape(inputs[0]["q_nope"], inputs[0]["q_pe"], inputs[0]["kv_cache"], inputs[0]["wkv_b"])
     need = binding.absorb_attn_workspace_size(shape, cfg.end_pos, binding.MLA_DTYPE_BF16)
     ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
 
     calls = [binding.AbsorbAttnCall(x["q_nope"], x["q_pe"], x["kv_cache"], x["pe_cache"], x["wkv_b"], cfg.end_pos,
-                                    cfg.softmax_scale, out, workspace=ws) for x in inputs]
+                                    cfg.softmax_scale, out, workspace=ws, seq_lens=seq_lens) for x in inputs]
 
     def step(i):
         calls[i % sets]()
@@ -214,7 +220,7 @@ def main():
     import torch
 
     from mla_latent_kv_absorb_amd import binding
-    from mla_latent_kv_absorb_amd.workloads import ATTN_CONFIGS, EXPAND_CONFIGS
+    from mla_latent_kv_absorb_amd.workloads import ATTN_CONFIGS, EXPAND_CONFIGS, RAGGED_CONFIGS, ragged_lengths
 
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
@@ -294,6 +300,15 @@ def main():
             _, _, k = time_attn(c, steps, 3, sets, torch, binding, seed=c.seed, timed_kernels=0b111)
             extras[name] = {"us_per_step": round(u, 2), "gbps": round(w["bytes"] / (u * 1e-6) / 1e9, 1),
                             "tflops": round(w["flops"] / (u * 1e-6) / 1e12, 2),
+                            "kernels_us": {n: round(v["avg_us"], 2) for n, v in k.items()}}
+        for name, (base, lo, hi, lseed) in RAGGED_CONFIGS.items():
+            c = ATTN_CONFIGS[base]
+            lens = ragged_lengths(c.batch, lo, hi, lseed)
+            w = attn_work(c, lens)
+            u, _, _ = time_attn(c, 30, 3, args.sets, torch, binding, seed=c.seed, timed_kernels=0, lens=lens)
+            _, _, k = time_attn(c, 30, 3, args.sets, torch, binding, seed=c.seed, timed_kernels=0b111, lens=lens)
+            extras[name] = {"us_per_step": round(u, 2), "gbps": round(w["bytes"] / (u * 1e-6) / 1e9, 1),
+                            "tflops": round(w["flops"] / (u * 1e-6) / 1e12, 2), "lengths": [lo, hi, int(sum(lens))],
                             "kernels_us": {n: round(v["avg_us"], 2) for n, v in k.items()}}
         ec = EXPAND_CONFIGS["dsv3_expand"]
         u = time_expand(ec, 20, 3, torch, binding)
