@@ -142,6 +142,31 @@ int32_t mla_absorb_attn_ragged(const void *q_nope, const void *q_pe, const void 
                                size_t workspace_bytes, void *stream);
 
 /*
+ * Cache append, the step before attending: writes the S new tokens of each sequence into the
+ * two caches mla_absorb_attn reads ("Naive vs Absorb Attention Implementations in DeepSeek-V3",
+ * section "Memory Layout and Cache Structure": kv_cache holds each position's compressed latent,
+ * pe_cache its rotary key).  The latent is stored RMS-normalised, with the norm of "Latent KV
+ * expansion with split":
+ *
+ *   c_kv_new  [B, S, C]       raw compressed latent of the new tokens
+ *   k_pe_new  [B, S, R]       their rope keys, already rotated
+ *   rms_w     [C]             RMSNorm weight
+ *   kv_cache  [Bmax, Tmax, C] row (b, p) := c_kv_new[b, s] / sqrt(mean_c c_kv_new[b, s, c]^2 + eps) * rms_w
+ *   pe_cache  [Bmax, Tmax, R] row (b, p) := k_pe_new[b, s]
+ *
+ * with p = end_pos - S + s, the positions mla_absorb_attn gives the same S query tokens; with
+ * seq_lens (DEVICE [B] int32, or NULL) p = seq_lens[b] - S + s, each length clamped to
+ * [S, end_pos] as in mla_absorb_attn_ragged.  Every other cache row is left untouched.  The shape
+ * descriptor supplies B, S, C, R, Bmax and Tmax (its other fields are not used); requires
+ * 1 <= S <= end_pos <= Tmax, B <= Bmax, 0 <= eps <= 1.  The caches must not overlap each other or
+ * any input.  Arithmetic in fp32, stores rounded to the element type.  Returns MLA_OK or a
+ * negative MLA_ERR_* status (validation before any HIP call, as everywhere).
+ */
+int32_t mla_cache_append(const void *c_kv_new, const void *k_pe_new, const void *rms_w, float eps,
+                         const int32_t *seq_lens, int64_t end_pos, void *kv_cache, void *pe_cache,
+                         const mla_attn_shape *shape, int32_t dtype, void *stream);
+
+/*
  * Bytes of device workspace mla_expand_kv needs (the normalised latent n, which the matrix-core
  * path computes once per token and every head reuses; 0 for the plain path).  Returns 0 when the
  * arguments are invalid (the same checks as mla_expand_kv; see mla_last_error).
@@ -184,7 +209,7 @@ int32_t mla_expand_kv(const void *c_kv, const void *rms_w, const void *wkv_b, vo
 #define MLA_KERNEL_COMBINE 2      /* split combine + projection out through W_UV */
 #define MLA_KERNEL_EXPAND_PREP 3  /* per-token weighted latent and 1/rms          */
 #define MLA_KERNEL_EXPAND 4       /* projection + head-major split               */
-#define MLA_KERNEL_PLAIN 5        /* any kernel of the plain vector-ALU path     */
+#define MLA_KERNEL_PLAIN 5        /* any kernel of the plain vector-ALU path, and the cache append */
 #define MLA_NUM_KERNELS 6
 
 int32_t mla_timing_enable(uint32_t kernel_mask);

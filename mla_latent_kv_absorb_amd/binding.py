@@ -29,8 +29,8 @@ MLA_DTYPE_BF16 = 1
 
 PATHS = {"auto": 0, "plain": 1, "mfma": 2}
 
-EXPORTED = ("mla_absorb_attn", "mla_absorb_attn_ragged", "mla_absorb_attn_workspace_size", "mla_expand_kv",
-            "mla_expand_kv_workspace_size",
+EXPORTED = ("mla_absorb_attn", "mla_absorb_attn_ragged", "mla_absorb_attn_workspace_size", "mla_cache_append",
+            "mla_expand_kv", "mla_expand_kv_workspace_size",
             "mla_strerror",
             "mla_last_error", "mla_timing_enable", "mla_timing_collect", "mla_kernel_name")
 
@@ -71,6 +71,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_absorb_attn_ragged.argtypes = [vp, vp, vp, vp, vp, vp, i64, ctypes.c_float, vp, ctypes.POINTER(AttnShape),
                                            i32, ctypes.POINTER(AttnOptions), vp, sz, vp]
     lib.mla_absorb_attn_ragged.restype = i32
+    lib.mla_cache_append.argtypes = [vp, vp, vp, ctypes.c_float, vp, i64, vp, vp, ctypes.POINTER(AttnShape), i32, vp]
+    lib.mla_cache_append.restype = i32
     lib.mla_absorb_attn_workspace_size.argtypes = [ctypes.POINTER(AttnShape), i64, i32, ctypes.POINTER(AttnOptions)]
     lib.mla_absorb_attn_workspace_size.restype = sz
     lib.mla_expand_kv.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float, i32, i32, vp, sz, vp]
@@ -224,6 +226,29 @@ def absorb_attn(q_nope, q_pe, kv_cache, pe_cache, wkv_b, end_pos: int, softmax_s
     seq_lens, a ragged batch whose lengths are bounded by end_pos."""
     return AbsorbAttnCall(q_nope, q_pe, kv_cache, pe_cache, wkv_b, end_pos, softmax_scale, out,
                           num_splits=num_splits, path=path, workspace=workspace, seq_lens=seq_lens)()
+
+
+def cache_append(c_kv_new, k_pe_new, rms_w, eps: float, end_pos: int, kv_cache, pe_cache, *, seq_lens=None):
+    """Write the new tokens' normalised latent and rope key into the caches in place
+    (mla_cache_append): positions end_pos - S + s, or seq_lens[b] - S + s with seq_lens."""
+    import torch
+
+    lib = load()
+    _require_device(c_kv_new, k_pe_new, rms_w, kv_cache, pe_cache)
+    B, S, C = c_kv_new.shape
+    R = k_pe_new.shape[-1]
+    Bmax, Tmax, _ = kv_cache.shape
+    if tuple(k_pe_new.shape[:2]) != (B, S) or tuple(pe_cache.shape[:2]) != (Bmax, Tmax):
+        raise ValueError("k_pe_new / pe_cache shapes disagree with c_kv_new / kv_cache")
+    shape = AttnShape(B, S, 1, C, R, 0, 0, Bmax, Tmax)
+    lens_ptr = None
+    if seq_lens is not None:
+        if seq_lens.device != c_kv_new.device or seq_lens.dtype != torch.int32 or seq_lens.numel() != B:
+            raise ValueError("seq_lens must be an int32 tensor [B] on the tensors' device")
+        lens_ptr = seq_lens.data_ptr()
+    _check(lib.mla_cache_append(c_kv_new.data_ptr(), k_pe_new.data_ptr(), rms_w.data_ptr(), eps, lens_ptr, end_pos,
+                                kv_cache.data_ptr(), pe_cache.data_ptr(), ctypes.byref(shape), _dtype_code(c_kv_new),
+                                _stream_handle(c_kv_new.device)))
 
 
 def expand_kv_workspace_size(n_tokens: int, n_heads: int, kv_lora_rank: int, qk_nope_head_dim: int,

@@ -32,6 +32,18 @@ struct ExpandCall {
   hipStream_t stream;
 };
 
+// One validated cache append (the new tokens' latent, normalised, and rope key into the caches).
+struct AppendCall {
+  int64_t B, S, C, R, Tmax;
+  int64_t end_pos;           // uniform length after the append, or the bound of seq_lens
+  const int32_t *seq_lens;   // device [B] per-sequence lengths (clamped to [S, end_pos]), or null
+  float eps;
+  int32_t dtype;
+  const void *c_kv_new, *k_pe_new, *rms_w;
+  void *kv_cache, *pe_cache;
+  hipStream_t stream;
+};
+
 // ---- benchmark instrumentation (no-ops unless enabled for the kernel id) ----------------------
 // Events recorded on the stream before and after a group of launches (the plain path's kernels).
 void timing_begin(int kernel_id, hipStream_t stream);
@@ -65,6 +77,8 @@ size_t mfma_attn_workspace(const AttnCall &c);
 int32_t mfma_attn_splits(const AttnCall &c, int num_cus);
 bool mfma_attn_plan_ok(const AttnCall &c, const char **why);  // limits that depend on the split count
 hipError_t mfma_absorb_attn(const AttnCall &c);
+
+hipError_t cache_append(const AppendCall &a);
 
 bool mfma_expand_supported(const ExpandCall &c, const char **why);
 size_t mfma_expand_workspace(const ExpandCall &c);

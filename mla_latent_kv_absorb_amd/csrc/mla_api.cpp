@@ -307,3 +307,64 @@ int32_t mla_expand_kv(const void *c_kv, const void *rms_w, const void *wkv_b, vo
 }
 
 }  // extern "C"
+
+extern "C" {
+
+int32_t mla_cache_append(const void *c_kv_new, const void *k_pe_new, const void *rms_w, float eps,
+                         const int32_t *seq_lens, int64_t end_pos, void *kv_cache, void *pe_cache,
+                         const mla_attn_shape *shape, int32_t dtype, void *stream) {
+  clear_error();
+  if (!shape) return fail(MLA_ERR_NULL, "shape is NULL");
+  if (dtype != MLA_DTYPE_F32 && dtype != MLA_DTYPE_BF16) return fail(MLA_ERR_DTYPE, "unknown dtype %d", dtype);
+  const mla_attn_shape &s = *shape;
+  const int64_t dims[] = {s.batch, s.seqlen_q, s.kv_lora_rank, s.qk_rope_head_dim, s.cache_batch, s.cache_len};
+  const char *dnames[] = {"batch", "seqlen_q", "kv_lora_rank", "qk_rope_head_dim", "cache_batch", "cache_len"};
+  for (int i = 0; i < 6; ++i)
+    if (dims[i] <= 0 || dims[i] > (int64_t(1) << 31))
+      return fail(MLA_ERR_SHAPE, "%s = %lld is out of range", dnames[i], (long long)dims[i]);
+  if (s.batch > s.cache_batch)
+    return fail(MLA_ERR_RANGE, "batch %lld exceeds cache_batch %lld", (long long)s.batch, (long long)s.cache_batch);
+  if (end_pos < 1 || end_pos > s.cache_len)
+    return fail(MLA_ERR_RANGE, "end_pos %lld outside [1, cache_len=%lld]", (long long)end_pos, (long long)s.cache_len);
+  if (s.seqlen_q > end_pos)
+    return fail(MLA_ERR_RANGE, "seqlen_q %lld exceeds end_pos %lld", (long long)s.seqlen_q, (long long)end_pos);
+  if (s.batch * s.seqlen_q > (int64_t(1) << 31) / 4)
+    return fail(MLA_ERR_SHAPE, "batch*seqlen_q = %lld is too large", (long long)(s.batch * s.seqlen_q));
+  if (!(eps >= 0.f) || eps > 1.f) return fail(MLA_ERR_SHAPE, "eps must be in [0, 1]");
+  const int64_t ealign = 16 / int64_t(elem_size(dtype));
+  if (s.kv_lora_rank % ealign || s.qk_rope_head_dim % ealign)
+    return fail(MLA_ERR_ALIGN, "kv_lora_rank and qk_rope_head_dim must be multiples of %lld elements (16-byte rows)",
+                (long long)ealign);
+  const void *ptrs[] = {c_kv_new, k_pe_new, rms_w, kv_cache, pe_cache};
+  const char *names[] = {"c_kv_new", "k_pe_new", "rms_w", "kv_cache", "pe_cache"};
+  for (int i = 0; i < 5; ++i) {
+    if (!ptrs[i]) return fail(MLA_ERR_NULL, "%s is NULL", names[i]);
+    if (misaligned(ptrs[i])) return fail(MLA_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
+  }
+  if (seq_lens && (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
+    return fail(MLA_ERR_ALIGN, "seq_lens is not 4-byte aligned");
+  const size_t es = elem_size(dtype);
+  const size_t toks = size_t(s.batch * s.seqlen_q);
+  const size_t in_bytes[] = {toks * size_t(s.kv_lora_rank) * es, toks * size_t(s.qk_rope_head_dim) * es,
+                             size_t(s.kv_lora_rank) * es};
+  const size_t kv_bytes = size_t(s.cache_batch * s.cache_len * s.kv_lora_rank) * es;
+  const size_t pe_bytes = size_t(s.cache_batch * s.cache_len * s.qk_rope_head_dim) * es;
+  if (overlaps(kv_cache, kv_bytes, pe_cache, pe_bytes)) return fail(MLA_ERR_SHAPE, "kv_cache overlaps pe_cache");
+  for (int i = 0; i < 3; ++i) {
+    if (overlaps(kv_cache, kv_bytes, ptrs[i], in_bytes[i])) return fail(MLA_ERR_SHAPE, "kv_cache overlaps %s", names[i]);
+    if (overlaps(pe_cache, pe_bytes, ptrs[i], in_bytes[i])) return fail(MLA_ERR_SHAPE, "pe_cache overlaps %s", names[i]);
+  }
+  if (seq_lens && (overlaps(kv_cache, kv_bytes, seq_lens, size_t(s.batch) * 4) ||
+                   overlaps(pe_cache, pe_bytes, seq_lens, size_t(s.batch) * 4)))
+    return fail(MLA_ERR_SHAPE, "a cache overlaps seq_lens");
+  mla::AppendCall a{};
+  a.B = s.batch; a.S = s.seqlen_q; a.C = s.kv_lora_rank; a.R = s.qk_rope_head_dim; a.Tmax = s.cache_len;
+  a.end_pos = end_pos; a.seq_lens = seq_lens; a.eps = eps; a.dtype = dtype;
+  a.c_kv_new = c_kv_new; a.k_pe_new = k_pe_new; a.rms_w = rms_w; a.kv_cache = kv_cache; a.pe_cache = pe_cache;
+  a.stream = static_cast<hipStream_t>(stream);
+  hipError_t e = mla::cache_append(a);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return MLA_OK;
+}
+
+}  // extern "C"

@@ -55,6 +55,7 @@ __all__ = [
     "absorb_attention_ragged",
     "rms_norm",
     "expand_kv",
+    "cache_append",
 ]
 
 
@@ -283,3 +284,25 @@ def expand_kv(c_kv, rms_w, wkv_b, n_heads: int, qk_nope_head_dim: int, v_head_di
     y = np.matmul(n, _as(wkv_b, dtype).T)
     y = y.reshape(T, n_heads, qk_nope_head_dim + v_head_dim).transpose(1, 0, 2)
     return np.ascontiguousarray(y[..., :qk_nope_head_dim]), np.ascontiguousarray(y[..., qk_nope_head_dim:])
+
+
+def cache_append(c_kv_new, k_pe_new, rms_w, eps: float, kv_cache, pe_cache, end_pos: int = None,
+                 seq_lens=None, dtype=np.float64):
+    """The caches after writing S new tokens per sequence ([MLA] "Memory Layout and Cache
+    Structure": kv_cache holds each position's latent, pe_cache its rotary key; the latent is
+    stored normalised, reading as for the absorb route).
+
+    c_kv_new [B,S,C] raw latent, k_pe_new [B,S,R]; token s of sequence b goes to position
+    end_pos - S + s (or seq_lens[b] - S + s): kv row := rms_norm(c_kv_new[b, s]), pe row :=
+    k_pe_new[b, s].  Returns new arrays (the inputs are not modified); other rows are copied.
+    """
+    kv, pe = _as(kv_cache, dtype).copy(), _as(pe_cache, dtype).copy()
+    B, S = c_kv_new.shape[0], c_kv_new.shape[1]
+    n = rms_norm(c_kv_new, rms_w, eps, dtype)
+    kp = _as(k_pe_new, dtype)
+    for b in range(B):
+        length = end_pos if seq_lens is None else int(seq_lens[b])
+        for s in range(S):
+            kv[b, length - S + s] = n[b, s]
+            pe[b, length - S + s] = kp[b, s]
+    return kv, pe

@@ -182,3 +182,29 @@ def test_ragged_argument_errors(lib):
     # outputs and workspace must not overlap the lengths (4-byte aligned is enough for them)
     assert call_ragged(lib, s, lens + 4, ws=lens - 1024) == B.MLA_ERR_WORKSPACE
     assert call_ragged(lib, s, P[5] + 64) == B.MLA_ERR_SHAPE and "seq_lens" in B.last_error()
+
+
+def call_append(lib, s, end_pos=4096, ptrs=None, eps=1e-6, lens=None, dtype=B.MLA_DTYPE_BF16):
+    p = list(P[:5]) if ptrs is None else ptrs
+    return lib.mla_cache_append(p[0], p[1], p[2], eps, lens, end_pos, p[3], p[4], ctypes.byref(s), dtype, None)
+
+
+def test_cache_append_argument_errors(lib):
+    s = shape()
+    assert lib.mla_cache_append(*P[:3], 1e-6, None, 4096, P[3], P[4], None, B.MLA_DTYPE_BF16, None) == B.MLA_ERR_NULL
+    assert call_append(lib, s, end_pos=4097) == B.MLA_ERR_RANGE
+    assert call_append(lib, shape(seqlen_q=9), end_pos=8) == B.MLA_ERR_RANGE
+    assert call_append(lib, shape(batch=3)) == B.MLA_ERR_RANGE
+    assert call_append(lib, s, eps=-1.0) == B.MLA_ERR_SHAPE
+    assert call_append(lib, s, dtype=5) == B.MLA_ERR_DTYPE
+    assert call_append(lib, shape(kv_lora_rank=500)) == B.MLA_ERR_ALIGN
+    for i in range(5):
+        p = list(P[:5])
+        p[i] = None
+        assert call_append(lib, s, ptrs=p) == B.MLA_ERR_NULL
+        p[i] = P[i] + 2
+        assert call_append(lib, s, ptrs=p) == B.MLA_ERR_ALIGN
+    assert call_append(lib, s, lens=P[6] + 2) == B.MLA_ERR_ALIGN
+    # the caches must not overlap each other or the new rows
+    assert call_append(lib, s, ptrs=[P[0], P[1], P[2], P[3], P[3] + 4096]) == B.MLA_ERR_SHAPE
+    assert call_append(lib, s, ptrs=[P[3] + 1024, P[1], P[2], P[3], P[4]]) == B.MLA_ERR_SHAPE

@@ -291,6 +291,47 @@ def pin_ragged():
     return worst
 
 
+def pin_append():
+    """Cache append: two appends in a row equal one append of both chunks; rows outside the new
+    positions are untouched; a written latent row r satisfies mean((r / w)^2) = m / (m + eps)
+    with m = mean(x^2) of its raw row (closed form of RMSNorm); and the expansion route
+    (expand_kv of the raw latents) gives the same keys and values as the naive route over the
+    appended cache."""
+    rng = np.random.default_rng(31)
+    B, S1, S2, C, R, T, Tmax, H, Dn, Dv, eps = 2, 2, 3, 8, 4, 9, 11, 3, 5, 6, 1e-3
+    x = rng.normal(size=(B, S1 + S2, C))
+    kp = rng.normal(size=(B, S1 + S2, R))
+    w = 1.0 + 0.1 * rng.normal(size=C)
+    kv0, pe0 = rng.normal(size=(B + 1, Tmax, C)), rng.normal(size=(B + 1, Tmax, R))
+    a1 = O.cache_append(x[:, :S1], kp[:, :S1], w, eps, kv0, pe0, end_pos=T - S2)
+    a2 = O.cache_append(x[:, S1:], kp[:, S1:], w, eps, a1[0], a1[1], end_pos=T)
+    both = O.cache_append(x, kp, w, eps, kv0, pe0, end_pos=T)
+    worst = max(rel_err(a2[0], both[0]), rel_err(a2[1], both[1]))
+    new = np.zeros((B + 1, Tmax), bool)
+    new[:B, T - S1 - S2:T] = True
+    worst = max(worst, float(np.abs(both[0][~new] - kv0[~new]).max()), float(np.abs(both[1][~new] - pe0[~new]).max()))
+    for b in range(B):
+        for s in range(S1 + S2):
+            m = np.mean(x[b, s] ** 2)
+            r = both[0][b, T - S1 - S2 + s]
+            worst = max(worst, abs(np.mean((r / w) ** 2) - m / (m + eps)))
+            worst = max(worst, rel_err(both[1][b, T - S1 - S2 + s], kp[b, s]))
+    # expansion route vs naive keys of an appended cache: every position appended from raw rows
+    wkv_b = rng.normal(size=(H * (Dn + Dv), C)) / math.sqrt(C)
+    xall = rng.normal(size=(1, T, C))
+    kv_full, _ = O.cache_append(xall, np.zeros((1, T, R)), w, eps, np.zeros((1, T, C)), np.zeros((1, T, R)), end_pos=T)
+    kn, vn = O.naive_kv(kv_full, wkv_b, 1, T, H, Dn, Dv)
+    ke, ve = O.expand_kv(xall[0], w, wkv_b, H, Dn, Dv, eps)
+    worst = max(worst, rel_err(kn[0].transpose(1, 0, 2), ke), rel_err(vn[0].transpose(1, 0, 2), ve))
+    # ragged positions: sequence b's tokens end at seq_lens[b]
+    lens = [4, 9]
+    rg = O.cache_append(x, kp, w, eps, kv0, pe0, seq_lens=lens)
+    for b, n_ in enumerate(lens):
+        one = O.cache_append(x[b:b + 1], kp[b:b + 1], w, eps, kv0[b:b + 1], pe0[b:b + 1], end_pos=n_)
+        worst = max(worst, rel_err(rg[0][b], one[0][0]), rel_err(rg[1][b], one[1][0]))
+    return worst
+
+
 PINS = {
     "naive_equals_absorb": (pin_naive_equals_absorb, 1e-12),
     "golden": (pin_golden, 1e-12),
@@ -306,6 +347,7 @@ PINS = {
     "rms_norm": (pin_rms_norm, 1e-12),
     "expand": (pin_expand, 1e-12),
     "ragged": (pin_ragged, 1e-12),
+    "append": (pin_append, 1e-12),
 }
 
 
@@ -410,6 +452,23 @@ def _ragged_uses_bound(q_nope, q_pe, kv_cache, pe_cache, wkv_b, seq_lens, *a, **
     return _orig_ragged(q_nope, q_pe, kv_cache, pe_cache, wkv_b, [max(seq_lens)] * len(seq_lens), *a, **kw)
 
 
+_orig_append = O.cache_append
+
+
+def _append_one_late(c_kv_new, k_pe_new, rms_w, eps, kv_cache, pe_cache, end_pos=None, seq_lens=None,
+                     dtype=np.float64):
+    # every token one position later than it belongs (the last one dropped)
+    S = np.asarray(c_kv_new).shape[1]
+    kv, pe = _orig_append(np.asarray(c_kv_new)[:, :S - 1], np.asarray(k_pe_new)[:, :S - 1], rms_w, eps, kv_cache,
+                          pe_cache, end_pos=end_pos, seq_lens=seq_lens, dtype=dtype) if S > 1 else (
+        _as_copy(kv_cache, dtype), _as_copy(pe_cache, dtype))
+    return kv, pe
+
+
+def _as_copy(x, dtype):
+    return np.array(x, dtype)
+
+
 MUTATIONS = {
     "swap_uk_uv": ("split_wkv_b", _swap_split),
     "mask_off_by_one": ("allowed_positions", _off_by_one_mask),
@@ -420,6 +479,7 @@ MUTATIONS = {
     "absorb_reverses_heads": ("absorb_attention", _absorb_transposed_heads),
     "expand_split_swapped": ("expand_kv", _expand_swapped),
     "ragged_uses_the_bound": ("absorb_attention_ragged", _ragged_uses_bound),
+    "append_one_position_late": ("cache_append", _append_one_late),
 }
 
 

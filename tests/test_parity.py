@@ -9,12 +9,16 @@ import pytest
 import torch
 
 from mla_latent_kv_absorb_amd.workloads import (ATTN_CONFIGS, EXPAND_CONFIGS, RAGGED_CONFIGS, make_attn_inputs,
-                                                 make_expand_inputs, ragged_lengths)
+                                                 make_expand_inputs, ragged_lengths, round_to_bf16)
 from oracle import mla_oracle as O
 
 pytestmark = pytest.mark.gpu
 
 TOL = {"f32": 1e-5, "bf16": 2e-2}
+
+
+def round_bf16(a):
+    return round_to_bf16(np.asarray(a, np.float32))
 
 
 def tdtype(cfg):
@@ -296,6 +300,57 @@ def test_full_size_ragged(gpu_lib, name):
     ref = oracle_ragged(cfg, x, lens, rows=rows)
     g = out.float().cpu().double().numpy()
     check(np.stack([g[b, s, h] for b, s, h in rows]), ref, TOL["bf16"], f"{name} sampled rows")
+
+
+# --------------------------------------------------------------------------------- cache append
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("ragged", [False, True])
+def test_cache_append(gpu_lib, dtype, ragged):
+    """Written rows match the oracle's normalised latent and rope key; every other row is unchanged."""
+    B, S, C, R, Bmax, Tmax, end_pos, eps = 3, 4, 512, 64, 4, 96, 80, 1e-6
+    rng = np.random.default_rng(41)
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    cast = (lambda a: a.astype(np.float32)) if dtype == "f32" else (lambda a: round_bf16(a))
+    x, kp = cast(rng.normal(size=(B, S, C))), cast(rng.normal(size=(B, S, R)))
+    w = cast(1.0 + 0.14 * rng.normal(size=C))
+    kv0, pe0 = cast(rng.normal(size=(Bmax, Tmax, C))), cast(rng.normal(size=(Bmax, Tmax, R)))
+    lens = [S, 37, end_pos] if ragged else None
+    dev = lambda a: torch.from_numpy(a).to("cuda").to(tdt)
+    kv, pe = dev(kv0), dev(pe0)
+    seq = torch.tensor(lens, dtype=torch.int32, device="cuda") if ragged else None
+    gpu_lib.cache_append(dev(x), dev(kp), dev(w), eps, end_pos, kv, pe, seq_lens=seq)
+    torch.cuda.synchronize()
+    kr, pr = O.cache_append(x, kp, w, eps, kv0, pe0, end_pos=end_pos, seq_lens=lens)
+    new = np.zeros((Bmax, Tmax), bool)
+    for b in range(B):
+        n = lens[b] if ragged else end_pos
+        new[b, n - S:n] = True
+    g_kv, g_pe = kv.float().cpu().numpy(), pe.float().cpu().numpy()
+    assert np.array_equal(g_kv[~new], kv0[~new]) and np.array_equal(g_pe[~new], pe0[~new]), "untouched rows changed"
+    assert np.array_equal(g_pe[new], pr[new].astype(np.float32)), "rope rows are copied exactly"
+    check(g_kv[new].astype(np.float64), kr[new], TOL[dtype], f"append {dtype} ragged={ragged} latent rows")
+
+
+def test_append_then_attend(gpu_lib):
+    """One decode step end to end: append each sequence's new token, then attend over the cache."""
+    cfg = dsv3_small(batch=3, cache_batch=3, end_pos=200, cache_len=256)
+    x = make_attn_inputs(cfg)
+    rng = np.random.default_rng(43)
+    c_new = round_bf16(rng.normal(size=(cfg.batch, 1, cfg.kv_lora_rank)))
+    kp_new = round_bf16(rng.normal(size=(cfg.batch, 1, cfg.qk_rope_head_dim)))
+    w = round_bf16(1.0 + 0.14 * rng.normal(size=cfg.kv_lora_rank))
+    t = to_dev(x, cfg)
+    dev = lambda a: torch.from_numpy(a).to("cuda").to(torch.bfloat16)
+    gpu_lib.cache_append(dev(c_new), dev(kp_new), dev(w), 1e-6, cfg.end_pos, t["kv_cache"], t["pe_cache"])
+    out = run_attn(gpu_lib, cfg, t, path="mfma")
+    kv, pe = O.cache_append(c_new, kp_new, w, 1e-6, x["kv_cache"], x["pe_cache"], end_pos=cfg.end_pos)
+    # the GPU attends to the bf16-rounded appended rows; the oracle rounds them the same way
+    kv_b = np.array(kv)
+    kv_b[:, cfg.end_pos - 1] = round_bf16(kv[:, cfg.end_pos - 1])
+    ref = O.absorb_attention(x["q_nope"], x["q_pe"], kv_b, pe, x["wkv_b"], cfg.end_pos, cfg.softmax_scale,
+                             cfg.v_head_dim)
+    check(out, ref, TOL["bf16"], "append + attend")
 
 
 def test_full_size_expand(gpu_lib):
