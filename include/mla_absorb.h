@@ -167,6 +167,30 @@ int32_t mla_cache_append(const void *c_kv_new, const void *k_pe_new, const void 
                          const mla_attn_shape *shape, int32_t dtype, void *stream);
 
 /*
+ * Attention of the naive route ("Naive vs Absorb Attention Implementations in DeepSeek-V3",
+ * section "Naive Path Execution") over keys and values that are already expanded, e.g. by
+ * mla_expand_kv of the caches' Bmax*Tmax latent rows in (b, t) order:
+ *
+ *   q_nope    [B, S, H, Dn]          query
+ *   q_pe      [B, S, H, R]           rope query (already rotated)
+ *   k_nope    [H, Bmax, Tmax, Dn]    per-head no-rope keys, head-major
+ *   v         [H, Bmax, Tmax, Dv]    per-head values, head-major
+ *   pe_cache  [Bmax, Tmax, R]        rope key per position, shared by every head
+ *   out       [B, S, H, Dv]          written: sum_t softmax_t(score) v[h, b, t] with
+ *             score = (q_nope[b,s,h] . k_nope[h,b,t] + q_pe[b,s,h] . pe_cache[b,t]) * softmax_scale
+ *
+ * Positions and the causal mask are those of mla_absorb_attn (query s at end_pos - S + s sees
+ * t <= that position).  The shape descriptor supplies B, S, H, R, Dn, Dv, Bmax and Tmax
+ * (kv_lora_rank is not used).  path: MLA_PATH_AUTO picks the matrix-core kernel for bf16 at
+ * R = 64, Dn = Dv = 128, else the plain one; MLA_PATH_MFMA refuses other shapes with
+ * MLA_ERR_UNSUPPORTED.  Needs no workspace.  out must not overlap an input.  Returns MLA_OK or a
+ * negative MLA_ERR_* status.
+ */
+int32_t mla_naive_attn(const void *q_nope, const void *q_pe, const void *k_nope, const void *v,
+                       const void *pe_cache, int64_t end_pos, float softmax_scale, void *out,
+                       const mla_attn_shape *shape, int32_t dtype, int32_t path, void *stream);
+
+/*
  * Bytes of device workspace mla_expand_kv needs (the normalised latent n, which the matrix-core
  * path computes once per token and every head reuses; 0 for the plain path).  Returns 0 when the
  * arguments are invalid (the same checks as mla_expand_kv; see mla_last_error).
@@ -210,7 +234,8 @@ int32_t mla_expand_kv(const void *c_kv, const void *rms_w, const void *wkv_b, vo
 #define MLA_KERNEL_EXPAND_PREP 3  /* per-token weighted latent and 1/rms          */
 #define MLA_KERNEL_EXPAND 4       /* projection + head-major split               */
 #define MLA_KERNEL_PLAIN 5        /* any kernel of the plain vector-ALU path, and the cache append */
-#define MLA_NUM_KERNELS 6
+#define MLA_KERNEL_NAIVE 6        /* matrix-core naive-route attention           */
+#define MLA_NUM_KERNELS 7
 
 int32_t mla_timing_enable(uint32_t kernel_mask);
 int32_t mla_timing_collect(int32_t launches[MLA_NUM_KERNELS], double ms[MLA_NUM_KERNELS]);

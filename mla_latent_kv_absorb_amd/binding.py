@@ -30,11 +30,11 @@ MLA_DTYPE_BF16 = 1
 PATHS = {"auto": 0, "plain": 1, "mfma": 2}
 
 EXPORTED = ("mla_absorb_attn", "mla_absorb_attn_ragged", "mla_absorb_attn_workspace_size", "mla_cache_append",
-            "mla_expand_kv", "mla_expand_kv_workspace_size",
+            "mla_expand_kv", "mla_expand_kv_workspace_size", "mla_naive_attn",
             "mla_strerror",
             "mla_last_error", "mla_timing_enable", "mla_timing_collect", "mla_kernel_name")
 
-NUM_KERNELS = 6  # MLA_NUM_KERNELS
+NUM_KERNELS = 7  # MLA_NUM_KERNELS
 
 
 class AttnShape(ctypes.Structure):
@@ -73,6 +73,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_absorb_attn_ragged.restype = i32
     lib.mla_cache_append.argtypes = [vp, vp, vp, ctypes.c_float, vp, i64, vp, vp, ctypes.POINTER(AttnShape), i32, vp]
     lib.mla_cache_append.restype = i32
+    lib.mla_naive_attn.argtypes = [vp, vp, vp, vp, vp, i64, ctypes.c_float, vp, ctypes.POINTER(AttnShape), i32, i32, vp]
+    lib.mla_naive_attn.restype = i32
     lib.mla_absorb_attn_workspace_size.argtypes = [ctypes.POINTER(AttnShape), i64, i32, ctypes.POINTER(AttnOptions)]
     lib.mla_absorb_attn_workspace_size.restype = sz
     lib.mla_expand_kv.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float, i32, i32, vp, sz, vp]
@@ -249,6 +251,31 @@ def cache_append(c_kv_new, k_pe_new, rms_w, eps: float, end_pos: int, kv_cache, 
     _check(lib.mla_cache_append(c_kv_new.data_ptr(), k_pe_new.data_ptr(), rms_w.data_ptr(), eps, lens_ptr, end_pos,
                                 kv_cache.data_ptr(), pe_cache.data_ptr(), ctypes.byref(shape), _dtype_code(c_kv_new),
                                 _stream_handle(c_kv_new.device)))
+
+
+def naive_attn(q_nope, q_pe, k_nope, v, pe_cache, end_pos: int, softmax_scale: float, out=None, *,
+               path: str = "auto"):
+    """Naive-route attention over expanded keys and values (mla_naive_attn): k_nope [H, Bmax,
+    Tmax, Dn] and v [H, Bmax, Tmax, Dv] head-major, pe_cache [Bmax, Tmax, R]; returns out
+    [B, S, H, Dv]."""
+    import torch
+
+    lib = load()
+    _require_device(q_nope, q_pe, k_nope, v, pe_cache)
+    B, S, H, Dn = q_nope.shape
+    R = q_pe.shape[-1]
+    Hk, Bmax, Tmax, Dk = k_nope.shape
+    Dv = v.shape[-1]
+    if Hk != H or Dk != Dn or tuple(v.shape[:3]) != (H, Bmax, Tmax) or tuple(pe_cache.shape) != (Bmax, Tmax, R):
+        raise ValueError("k_nope / v / pe_cache shapes disagree with the query")
+    if out is None:
+        out = torch.empty((B, S, H, Dv), dtype=q_nope.dtype, device=q_nope.device)
+    _require_device(q_nope, out)
+    shape = AttnShape(B, S, H, 0, R, Dn, Dv, Bmax, Tmax)
+    _check(lib.mla_naive_attn(q_nope.data_ptr(), q_pe.data_ptr(), k_nope.data_ptr(), v.data_ptr(), pe_cache.data_ptr(),
+                              end_pos, softmax_scale, out.data_ptr(), ctypes.byref(shape), _dtype_code(q_nope),
+                              PATHS[path], _stream_handle(q_nope.device)))
+    return out
 
 
 def expand_kv_workspace_size(n_tokens: int, n_heads: int, kv_lora_rank: int, qk_nope_head_dim: int,

@@ -20,7 +20,8 @@ LIB_NAME = "libmla_absorb.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 BUILD_DIR = os.path.join(HERE, "_build")
 
-SOURCES = ["mla_api.cpp", "timing.cpp", "plain_kernels.hip", "absorb_mfma.hip", "expand_mfma.hip", "cache_append.hip"]
+SOURCES = ["mla_api.cpp", "timing.cpp", "plain_kernels.hip", "absorb_mfma.hip", "expand_mfma.hip", "cache_append.hip",
+           "naive_mfma.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -32,6 +32,16 @@ struct ExpandCall {
   hipStream_t stream;
 };
 
+// One validated naive-route attention call over expanded keys and values.
+struct NaiveCall {
+  int64_t B, S, H, R, Dn, Dv, Bmax, Tmax, end_pos;
+  float scale;
+  int32_t dtype;
+  const void *q_nope, *q_pe, *k_nope, *v, *pe;  // k_nope / v: [H, Bmax, Tmax, Dn / Dv]
+  void *out;
+  hipStream_t stream;
+};
+
 // One validated cache append (the new tokens' latent, normalised, and rope key into the caches).
 struct AppendCall {
   int64_t B, S, C, R, Tmax;
@@ -79,6 +89,10 @@ bool mfma_attn_plan_ok(const AttnCall &c, const char **why);  // limits that dep
 hipError_t mfma_absorb_attn(const AttnCall &c);
 
 hipError_t cache_append(const AppendCall &a);
+
+hipError_t plain_naive_attn(const NaiveCall &c);
+bool mfma_naive_supported(const NaiveCall &c, const char **why);
+hipError_t mfma_naive_attn(const NaiveCall &c);
 
 bool mfma_expand_supported(const ExpandCall &c, const char **why);
 size_t mfma_expand_workspace(const ExpandCall &c);

@@ -368,3 +368,68 @@ int32_t mla_cache_append(const void *c_kv_new, const void *k_pe_new, const void 
 }
 
 }  // extern "C"
+
+extern "C" {
+
+int32_t mla_naive_attn(const void *q_nope, const void *q_pe, const void *k_nope, const void *v, const void *pe_cache,
+                       int64_t end_pos, float softmax_scale, void *out, const mla_attn_shape *shape, int32_t dtype,
+                       int32_t path, void *stream) {
+  clear_error();
+  if (!shape) return fail(MLA_ERR_NULL, "shape is NULL");
+  if (dtype != MLA_DTYPE_F32 && dtype != MLA_DTYPE_BF16) return fail(MLA_ERR_DTYPE, "unknown dtype %d", dtype);
+  const mla_attn_shape &s = *shape;
+  const int64_t dims[] = {s.batch, s.seqlen_q, s.n_heads, s.qk_rope_head_dim, s.qk_nope_head_dim,
+                          s.v_head_dim, s.cache_batch, s.cache_len};
+  const char *dnames[] = {"batch", "seqlen_q", "n_heads", "qk_rope_head_dim", "qk_nope_head_dim",
+                          "v_head_dim", "cache_batch", "cache_len"};
+  for (int i = 0; i < 8; ++i)
+    if (dims[i] <= 0 || dims[i] > (int64_t(1) << 31))
+      return fail(MLA_ERR_SHAPE, "%s = %lld is out of range", dnames[i], (long long)dims[i]);
+  if (s.batch > s.cache_batch)
+    return fail(MLA_ERR_RANGE, "batch %lld exceeds cache_batch %lld", (long long)s.batch, (long long)s.cache_batch);
+  if (end_pos < 1 || end_pos > s.cache_len)
+    return fail(MLA_ERR_RANGE, "end_pos %lld outside [1, cache_len=%lld]", (long long)end_pos, (long long)s.cache_len);
+  if (s.seqlen_q > end_pos)
+    return fail(MLA_ERR_RANGE, "seqlen_q %lld exceeds end_pos %lld", (long long)s.seqlen_q, (long long)end_pos);
+  const int64_t rows = s.batch * s.seqlen_q * s.n_heads;
+  if (rows > (int64_t(1) << 31) / 4) return fail(MLA_ERR_SHAPE, "batch*seqlen_q*n_heads = %lld is too large", (long long)rows);
+  const int64_t ealign = 16 / int64_t(elem_size(dtype));
+  if (s.qk_rope_head_dim % ealign || s.qk_nope_head_dim % ealign || s.v_head_dim % ealign)
+    return fail(MLA_ERR_ALIGN, "qk_rope_head_dim, qk_nope_head_dim and v_head_dim must be multiples of %lld elements",
+                (long long)ealign);
+  if (!(softmax_scale == softmax_scale) || softmax_scale <= 0.f || softmax_scale > 1e30f)
+    return fail(MLA_ERR_SHAPE, "softmax_scale must be a positive finite number");
+  if (path != MLA_PATH_AUTO && path != MLA_PATH_PLAIN && path != MLA_PATH_MFMA)
+    return fail(MLA_ERR_UNSUPPORTED, "unknown path %d", path);
+  const void *ptrs[] = {q_nope, q_pe, k_nope, v, pe_cache, out};
+  const char *names[] = {"q_nope", "q_pe", "k_nope", "v", "pe_cache", "out"};
+  for (int i = 0; i < 6; ++i) {
+    if (!ptrs[i]) return fail(MLA_ERR_NULL, "%s is NULL", names[i]);
+    if (misaligned(ptrs[i])) return fail(MLA_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
+  }
+  const size_t es = elem_size(dtype);
+  const size_t kv_rows = size_t(s.n_heads * s.cache_batch * s.cache_len);
+  const size_t bytes_in[] = {size_t(rows * s.qk_nope_head_dim) * es, size_t(rows * s.qk_rope_head_dim) * es,
+                             kv_rows * size_t(s.qk_nope_head_dim) * es, kv_rows * size_t(s.v_head_dim) * es,
+                             size_t(s.cache_batch * s.cache_len * s.qk_rope_head_dim) * es};
+  const size_t out_bytes = size_t(rows * s.v_head_dim) * es;
+  for (int i = 0; i < 5; ++i)
+    if (overlaps(out, out_bytes, ptrs[i], bytes_in[i])) return fail(MLA_ERR_SHAPE, "out overlaps %s", names[i]);
+  mla::NaiveCall c{};
+  c.B = s.batch; c.S = s.seqlen_q; c.H = s.n_heads; c.R = s.qk_rope_head_dim; c.Dn = s.qk_nope_head_dim;
+  c.Dv = s.v_head_dim; c.Bmax = s.cache_batch; c.Tmax = s.cache_len; c.end_pos = end_pos;
+  c.scale = softmax_scale; c.dtype = dtype;
+  c.q_nope = q_nope; c.q_pe = q_pe; c.k_nope = k_nope; c.v = v; c.pe = pe_cache; c.out = out;
+  c.stream = static_cast<hipStream_t>(stream);
+  bool use_mfma = false;
+  if (path != MLA_PATH_PLAIN) {
+    const char *why = "";
+    use_mfma = mla::mfma_naive_supported(c, &why);
+    if (path == MLA_PATH_MFMA && !use_mfma) return fail(MLA_ERR_UNSUPPORTED, "matrix-core path: %s", why);
+  }
+  hipError_t e = use_mfma ? mla::mfma_naive_attn(c) : mla::plain_naive_attn(c);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return MLA_OK;
+}
+
+}  // extern "C"

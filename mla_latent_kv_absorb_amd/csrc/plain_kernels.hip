@@ -193,6 +193,64 @@ hipError_t run_expand(const ExpandCall &e) {
   return hipGetLastError();
 }
 
+// Naive-route attention over expanded keys and values, one block per query row (b, s, h):
+// score over the visible positions in chunks of kThreads (online softmax), then the value sum.
+template <typename T>
+__global__ void __launch_bounds__(kThreads)
+plain_naive_attn_kernel(const T *__restrict__ q_nope, const T *__restrict__ q_pe, const T *__restrict__ k_nope,
+                        const T *__restrict__ v, const T *__restrict__ pe, T *__restrict__ out, NaiveCall a) {
+  extern __shared__ float sm[];
+  float *sq = sm;              // Dn + R   query
+  float *so = sq + a.Dn + a.R; // Dv       running weighted sum
+  float *sp = so + a.Dv;       // kThreads probabilities of the current chunk
+  float *red = sp + kThreads;  // 16
+  const int64_t row = blockIdx.x;  // (b, s, h)
+  const int tid = threadIdx.x;
+  const int64_t b = row / (a.S * a.H), s = (row / a.H) % a.S, h = row % a.H;
+  const int64_t t1 = a.end_pos - a.S + s + 1;  // visible positions [0, t1)
+  for (int64_t d = tid; d < a.Dn; d += kThreads) sq[d] = Elem<T>::load(q_nope, row * a.Dn + d);
+  for (int64_t r = tid; r < a.R; r += kThreads) sq[a.Dn + r] = Elem<T>::load(q_pe, row * a.R + r);
+  for (int64_t c = tid; c < a.Dv; c += kThreads) so[c] = 0.f;
+  __syncthreads();
+  const T *kb = k_nope + (h * a.Bmax + b) * a.Tmax * a.Dn;
+  const T *vb = v + (h * a.Bmax + b) * a.Tmax * a.Dv;
+  const T *pb = pe + b * a.Tmax * a.R;
+  float m = -INFINITY, l = 0.f;
+  for (int64_t tc = 0; tc < t1; tc += kThreads) {
+    const int n = int((t1 - tc) < kThreads ? (t1 - tc) : kThreads);
+    float sc = -INFINITY;
+    if (tid < n) {
+      const int64_t t = tc + tid;
+      float acc = 0.f;
+      for (int64_t d = 0; d < a.Dn; ++d) acc = fmaf(sq[d], Elem<T>::load(kb, t * a.Dn + d), acc);
+      for (int64_t r = 0; r < a.R; ++r) acc = fmaf(sq[a.Dn + r], Elem<T>::load(pb, t * a.R + r), acc);
+      sc = acc * a.scale;
+    }
+    const float m_new = fmaxf(m, block_max(sc, red));
+    const float p = (tid < n) ? expf(sc - m_new) : 0.f;
+    sp[tid] = p;
+    const float alpha = (m == -INFINITY) ? 0.f : expf(m - m_new);
+    l = l * alpha + block_sum(p, red);  // block_sum synchronises, so sp is visible below
+    for (int64_t c = tid; c < a.Dv; c += kThreads) {
+      float acc = so[c] * alpha;
+      for (int j = 0; j < n; ++j) acc = fmaf(sp[j], Elem<T>::load(vb, (tc + j) * a.Dv + c), acc);
+      so[c] = acc;
+    }
+    m = m_new;
+    __syncthreads();
+  }
+  for (int64_t c = tid; c < a.Dv; c += kThreads) Elem<T>::store(out, row * a.Dv + c, so[c] / l);
+}
+
+template <typename T>
+hipError_t run_naive(const NaiveCall &c) {
+  const size_t lds = sizeof(float) * size_t(c.Dn + c.R + c.Dv + kThreads + 16);
+  return launch_kernel(MLA_KERNEL_PLAIN, plain_naive_attn_kernel<T>, dim3(unsigned(c.B * c.S * c.H)),
+                       dim3(kThreads), uint32_t(lds), c.stream, static_cast<const T *>(c.q_nope),
+                       static_cast<const T *>(c.q_pe), static_cast<const T *>(c.k_nope), static_cast<const T *>(c.v),
+                       static_cast<const T *>(c.pe), static_cast<T *>(c.out), c);
+}
+
 }  // namespace
 
 int32_t plain_attn_splits(const AttnCall &c) {
@@ -216,6 +274,10 @@ hipError_t plain_absorb_attn(const AttnCall &c) {
 
 hipError_t plain_expand_kv(const ExpandCall &e) {
   return e.dtype == MLA_DTYPE_F32 ? run_expand<float>(e) : run_expand<uint16_t>(e);
+}
+
+hipError_t plain_naive_attn(const NaiveCall &c) {
+  return c.dtype == MLA_DTYPE_F32 ? run_naive<float>(c) : run_naive<uint16_t>(c);
 }
 
 }  // namespace mla

@@ -145,6 +145,7 @@ const char *mla_kernel_name(int32_t id) {
     case MLA_KERNEL_EXPAND_PREP: return "expand_prep";
     case MLA_KERNEL_EXPAND: return "expand";
     case MLA_KERNEL_PLAIN: return "plain";
+    case MLA_KERNEL_NAIVE: return "naive";
     default: return "";
   }
 }

@@ -49,6 +49,7 @@ __all__ = [
     "absorb_attention",
     "naive_kv",
     "naive_attention",
+    "attention_over_kv",
     "attention_partial",
     "merge_partials",
     "absorb_attention_rows",
@@ -175,6 +176,31 @@ def naive_attention(q_nope, q_pe, kv_cache, pe_cache, wkv_b, end_pos: int, softm
     out = np.matmul(p.transpose(0, 2, 1, 3), v.transpose(0, 2, 1, 3)).transpose(0, 2, 1, 3)
     if return_intermediates:
         return out, {"k": k, "v": v, "scores": scores, "p": p}
+    return out
+
+
+def attention_over_kv(q_nope, q_pe, k_nope, v, pe_cache, end_pos: int, softmax_scale: float,
+                      dtype=np.float64):
+    """The attention half of the naive route ([MLA] "Naive Path Execution") on keys and values
+    that are already expanded: k_nope [H, Bmax, Tmax, Dn] and v [H, Bmax, Tmax, Dv] head-major
+    (the layout the expansion of [EXP] writes for the caches' Bmax*Tmax rows in (b, t) order).
+
+    Key of head h at position t: concat(k_nope[h, b, t], pe_cache[b, t]) (the rope key shared by
+    every head); query: concat(q_nope[b, s, h], q_pe[b, s, h]).  Masking and softmax as in
+    absorb_attention.  Returns out [B, S, H, Dv].
+    """
+    q = np.concatenate([_as(q_nope, dtype), _as(q_pe, dtype)], axis=-1)  # [B,S,H,Dn+R]
+    B, S, H, _ = q.shape
+    allowed = allowed_positions(S, end_pos)
+    Dv = v.shape[-1]
+    out = np.zeros((B, S, H, Dv), dtype)
+    for b in range(B):
+        pe = _as(pe_cache[b, :end_pos], dtype)  # [T, R]
+        for h in range(H):
+            k = np.concatenate([_as(k_nope[h, b, :end_pos], dtype), pe], axis=-1)  # [T, Dn+R]
+            scores = np.matmul(q[b, :, h], k.T) * softmax_scale  # [S, T]
+            p = masked_softmax(scores, allowed)
+            out[b, :, h] = np.matmul(p, _as(v[h, b, :end_pos], dtype))
     return out
 
 

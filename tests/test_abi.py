@@ -208,3 +208,37 @@ def test_cache_append_argument_errors(lib):
     # the caches must not overlap each other or the new rows
     assert call_append(lib, s, ptrs=[P[0], P[1], P[2], P[3], P[3] + 4096]) == B.MLA_ERR_SHAPE
     assert call_append(lib, s, ptrs=[P[3] + 1024, P[1], P[2], P[3], P[4]]) == B.MLA_ERR_SHAPE
+
+
+def call_naive(lib, s, end_pos=4096, ptrs=None, scale=0.07, dtype=B.MLA_DTYPE_BF16, path=B.PATHS["auto"]):
+    p = list(P[:6]) if ptrs is None else ptrs
+    return lib.mla_naive_attn(p[0], p[1], p[2], p[3], p[4], end_pos, scale, p[5], ctypes.byref(s), dtype, path, None)
+
+
+def test_naive_attn_argument_errors(lib):
+    s = shape()
+    assert lib.mla_naive_attn(*P[:5], 4096, 0.07, P[5], None, B.MLA_DTYPE_BF16, 0, None) == B.MLA_ERR_NULL
+    assert call_naive(lib, s, end_pos=4097) == B.MLA_ERR_RANGE
+    assert call_naive(lib, s, end_pos=0) == B.MLA_ERR_RANGE
+    assert call_naive(lib, shape(seqlen_q=9), end_pos=8) == B.MLA_ERR_RANGE
+    assert call_naive(lib, shape(batch=3)) == B.MLA_ERR_RANGE
+    assert call_naive(lib, shape(n_heads=0)) == B.MLA_ERR_SHAPE
+    assert call_naive(lib, s, scale=0.0) == B.MLA_ERR_SHAPE
+    assert call_naive(lib, s, scale=float("nan")) == B.MLA_ERR_SHAPE
+    assert call_naive(lib, s, dtype=5) == B.MLA_ERR_DTYPE
+    assert call_naive(lib, s, path=7) == B.MLA_ERR_UNSUPPORTED
+    assert call_naive(lib, shape(v_head_dim=100)) == B.MLA_ERR_ALIGN
+    # the matrix-core kernel is for the bf16 DeepSeek-V3 head shape only
+    assert call_naive(lib, s, dtype=B.MLA_DTYPE_F32, path=B.PATHS["mfma"]) == B.MLA_ERR_UNSUPPORTED
+    assert call_naive(lib, shape(qk_nope_head_dim=64), path=B.PATHS["mfma"]) == B.MLA_ERR_UNSUPPORTED
+    assert call_naive(lib, shape(qk_rope_head_dim=128), path=B.PATHS["mfma"]) == B.MLA_ERR_UNSUPPORTED
+    for i in range(6):
+        p = list(P[:6])
+        p[i] = None
+        assert call_naive(lib, s, ptrs=p) == B.MLA_ERR_NULL
+        p[i] = P[i] + 2
+        assert call_naive(lib, s, ptrs=p) == B.MLA_ERR_ALIGN
+    for i in range(5):  # out overlapping any input
+        p = list(P[:6])
+        p[5] = P[i] + 4096
+        assert call_naive(lib, s, ptrs=p) == B.MLA_ERR_SHAPE

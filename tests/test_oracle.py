@@ -332,6 +332,22 @@ def pin_append():
     return worst
 
 
+def pin_attention_over_kv():
+    """The attention half of the naive route on head-major expanded keys equals the whole naive
+    route (which expands inside), decode and causal chunk; and equals the absorb route."""
+    worst = 0.0
+    for cfg in (small_cfg(seed=51), small_cfg(seqlen_q=3, end_pos=7, seed=52)):
+        x = make_attn_inputs(cfg)
+        H, Dn, Dv = cfg.n_heads, cfg.qk_nope_head_dim, cfg.v_head_dim
+        Bmax, Tmax = cfg.cache_batch, cfg.cache_len
+        # expand every cache row, then lay the result out head-major [H, Bmax, Tmax, D]
+        kn, vn = O.naive_kv(x["kv_cache"], x["wkv_b"], Bmax, Tmax, H, Dn, Dv)
+        k_hm, v_hm = kn.transpose(2, 0, 1, 3), vn.transpose(2, 0, 1, 3)
+        got = O.attention_over_kv(x["q_nope"], x["q_pe"], k_hm, v_hm, x["pe_cache"], cfg.end_pos, cfg.softmax_scale)
+        worst = max(worst, rel_err(got, run("naive", cfg, x)), rel_err(got, run("absorb", cfg, x)))
+    return worst
+
+
 PINS = {
     "naive_equals_absorb": (pin_naive_equals_absorb, 1e-12),
     "golden": (pin_golden, 1e-12),
@@ -348,6 +364,7 @@ PINS = {
     "expand": (pin_expand, 1e-12),
     "ragged": (pin_ragged, 1e-12),
     "append": (pin_append, 1e-12),
+    "attention_over_kv": (pin_attention_over_kv, 1e-12),
 }
 
 

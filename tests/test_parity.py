@@ -353,6 +353,92 @@ def test_append_then_attend(gpu_lib):
     check(out, ref, TOL["bf16"], "append + attend")
 
 
+# --------------------------------------------------------------------------------- naive route
+
+def head_major_kv(x, cfg):
+    """The oracle's naive keys and values of every cache row, head-major [H, Bmax, Tmax, D], bf16-rounded."""
+    kn, vn = O.naive_kv(x["kv_cache"], x["wkv_b"], cfg.cache_batch, cfg.cache_len, cfg.n_heads,
+                        cfg.qk_nope_head_dim, cfg.v_head_dim)
+    return round_bf16(kn.transpose(2, 0, 1, 3)), round_bf16(vn.transpose(2, 0, 1, 3))
+
+
+def run_naive(lib, cfg, t, k, v, path="auto"):
+    out = torch.full((cfg.batch, cfg.seqlen_q, cfg.n_heads, cfg.v_head_dim), float("nan"), dtype=torch.bfloat16,
+                     device="cuda")
+    lib.naive_attn(t["q_nope"], t["q_pe"], k, v, t["pe_cache"], cfg.end_pos, cfg.softmax_scale, out, path=path)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("path", ["plain", "mfma"])
+@pytest.mark.parametrize("kw", [
+    dict(seqlen_q=1, end_pos=300),    # decode
+    dict(seqlen_q=5, end_pos=200),    # causal chunk
+    dict(seqlen_q=130, end_pos=170),  # two query blocks, the second of 2 rows
+    dict(seqlen_q=64, end_pos=64),    # chunk covering the whole prefix
+])
+def test_naive_attn(gpu_lib, path, kw):
+    cfg = dsv3_small(batch=2, cache_batch=3, cache_len=320, n_heads=16, **kw)
+    x = make_attn_inputs(cfg)
+    kh, vh = head_major_kv(x, cfg)
+    t = to_dev(x, cfg)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to("cuda").to(torch.bfloat16)
+    out = run_naive(gpu_lib, cfg, t, dev(kh), dev(vh), path=path)
+    ref = O.attention_over_kv(x["q_nope"], x["q_pe"], kh, vh, x["pe_cache"], cfg.end_pos, cfg.softmax_scale)
+    check(out, ref, TOL["bf16"], f"naive attention {kw} {path}")
+
+
+def test_naive_route_matches_absorb_on_gpu(gpu_lib):
+    """The pages' FAQ invariant with both routes on the GPU: raw latents appended (normalised) into
+    the cache feed the absorb route; the same latents expanded feed the naive route."""
+    cfg = dsv3_small(batch=2, cache_batch=2, seqlen_q=3, end_pos=250, cache_len=256, n_heads=32)
+    x = make_attn_inputs(cfg)
+    rng = np.random.default_rng(61)
+    raw = round_bf16(rng.normal(size=(cfg.cache_batch, cfg.cache_len, cfg.kv_lora_rank)))
+    w = round_bf16(1.0 + 0.14 * rng.normal(size=cfg.kv_lora_rank))
+    t = to_dev(x, cfg)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to("cuda").to(torch.bfloat16)
+    # absorb route: every position appended from the raw latent (positions 0..Tmax-1)
+    gpu_lib.cache_append(dev(raw), dev(np.zeros((cfg.cache_batch, cfg.cache_len, cfg.qk_rope_head_dim))), dev(w),
+                         1e-6, cfg.cache_len, t["kv_cache"], torch.empty_like(t["pe_cache"]))
+    a = run_attn(gpu_lib, cfg, t, path="mfma")
+    # naive route: the expansion of the same raw latents, head-major [H, Bmax*Tmax, D]
+    k, v = gpu_lib.expand_kv(dev(raw.reshape(-1, cfg.kv_lora_rank)), dev(w), t["wkv_b"], cfg.n_heads,
+                             cfg.qk_nope_head_dim, cfg.v_head_dim, 1e-6)
+    n = run_naive(gpu_lib, cfg, t, k.view(cfg.n_heads, cfg.cache_batch, cfg.cache_len, -1),
+                  v.view(cfg.n_heads, cfg.cache_batch, cfg.cache_len, -1), path="mfma")
+    ref = O.naive_attention(x["q_nope"], x["q_pe"], O.rms_norm(raw, w, 1e-6), x["pe_cache"], x["wkv_b"], cfg.end_pos,
+                            cfg.softmax_scale, cfg.v_head_dim)
+    check(a, ref, TOL["bf16"], "absorb route (GPU) vs oracle")
+    check(n, ref, TOL["bf16"], "naive route (GPU) vs oracle")
+    check(n, a.float().cpu().double().numpy(), TOL["bf16"], "naive route vs absorb route, both on the GPU")
+
+
+def test_full_size_naive_vs_absorb_prefill(gpu_lib):
+    """chunk_prefill through both routes on the GPU (expansion of the 2 x 4096 cached latents, then
+    naive attention), compared with each other everywhere and with the oracle on sampled rows."""
+    cfg = ATTN_CONFIGS["chunk_prefill"]
+    print(f"full-size naive vs absorb: B={cfg.batch} S={cfg.seqlen_q} T={cfg.end_pos}", flush=True)
+    x = make_attn_inputs(cfg)
+    # cache rows of unit RMS (what the append step stores for unit weight), so that expanding the
+    # cache with weight 1 reproduces the rows up to rounding and both routes see the same latents
+    x["kv_cache"] = round_bf16(O.rms_norm(x["kv_cache"], np.ones(cfg.kv_lora_rank), 0.0))
+    t = to_dev(x, cfg)
+    a = run_attn(gpu_lib, cfg, t)
+    k, v = gpu_lib.expand_kv(t["kv_cache"].reshape(-1, cfg.kv_lora_rank),
+                             torch.ones(cfg.kv_lora_rank, dtype=torch.bfloat16, device="cuda"), t["wkv_b"],
+                             cfg.n_heads, cfg.qk_nope_head_dim, cfg.v_head_dim, 0.0)
+    n = run_naive(gpu_lib, cfg, t, k.view(cfg.n_heads, cfg.cache_batch, cfg.cache_len, -1),
+                  v.view(cfg.n_heads, cfg.cache_batch, cfg.cache_len, -1))
+    assert torch.isfinite(n).all()
+    check(n, a.float().cpu().double().numpy(), TOL["bf16"], "chunk_prefill naive route vs absorb route")
+    rows = sample_rows(cfg, 32, 11)
+    ref = O.absorb_attention_rows(x["q_nope"], x["q_pe"], x["kv_cache"], x["pe_cache"], x["wkv_b"], cfg.end_pos,
+                                  cfg.softmax_scale, cfg.v_head_dim, rows)
+    g = n.float().cpu().double().numpy()
+    check(np.stack([g[b, s, h] for b, s, h in rows]), ref, TOL["bf16"], "chunk_prefill naive route sampled rows")
+
+
 def test_full_size_expand(gpu_lib):
     cfg = EXPAND_CONFIGS["dsv3_expand"]
     x = make_expand_inputs(cfg)
