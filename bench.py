@@ -20,7 +20,10 @@ events that the kernel's own dispatch stamps on its stream (hipExtLaunchKernel s
 those events add a queue barrier per timed dispatch, so that pass's step time is reported apart.
 `cpu_baseline` times the CPU oracle (NumPy, float64) on a bounded sample of the same workload.
 `extras` times the other workloads the same way: long_decode, chunk_prefill, ragged_decode (the
-decode batch with per-sequence lengths drawn uniformly from [256, 4096]) and dsv3_expand.
+decode batch with per-sequence lengths drawn uniformly from [256, 4096]), paged_decode (the decode
+batch with its caches in pools of 64-position pages in random order), chunk_prefill_naive (the
+same chunk through the naive route: expansion of the 2 x 4096 cached latents, then attention over
+the expanded keys and values) and dsv3_expand.
 """
 from __future__ import annotations
 
@@ -83,18 +86,39 @@ def gpu_inputs(cfg, seed, torch):
     }
 
 
-def time_attn(cfg, steps, warmup, sets, torch, binding, seed=1, timed_kernels=0b010, lens=None):
+def to_paged(x, cfg, page_size, seed, torch):
+    """Move one input set's caches into page pools in a random page order; returns the table."""
+    B, T = cfg.cache_batch, cfg.cache_len
+    npp = T // page_size
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    table = torch.randperm(B * npp, generator=g).to(torch.int32).view(B, npp).contiguous().to("cuda")
+    for key in ("kv_cache", "pe_cache"):
+        pool = torch.empty((B * npp, page_size, x[key].shape[-1]), dtype=x[key].dtype, device="cuda")
+        pool[table.long()] = x[key].view(B, npp, page_size, -1)
+        x[key] = pool
+    return table
+
+
+def time_attn(cfg, steps, warmup, sets, torch, binding, seed=1, timed_kernels=0b010, lens=None, page_size=0):
     """Returns (GPU us per step, host enqueue us per step, per-kernel timing dict).  With lens, a
-    ragged batch (mla_absorb_attn_ragged with the lengths in device memory, bound cfg.end_pos)."""
+    ragged batch (mla_absorb_attn_ragged with the lengths in device memory, bound cfg.end_pos);
+    with page_size, the caches live in page pools in random page order (mla_absorb_attn_paged)."""
     inputs = [gpu_inputs(cfg, seed + 1000 * i, torch) for i in range(sets)]
     seq_lens = None if lens is None else torch.tensor([int(n) for n in lens], dtype=torch.int32, device="cuda")
     out = torch.empty((cfg.batch, cfg.seqlen_q, cfg.n_heads, cfg.v_head_dim), dtype=torch.bfloat16, device="cuda")
     shape = binding.attn_shape(inputs[0]["q_nope"], inputs[0]["q_pe"], inputs[0]["kv_cache"], inputs[0]["wkv_b"])
-    need = binding.absorb_attn_workspace_size(shape, cfg.end_pos, binding.MLA_DTYPE_BF16)
+    if page_size:
+        paged = binding.PagedCache(page_size, cfg.cache_batch * cfg.cache_len // page_size,
+                                   cfg.cache_len // page_size)
+        need = binding.absorb_attn_paged_workspace_size(shape, cfg.end_pos, paged, binding.MLA_DTYPE_BF16)
+    else:
+        need = binding.absorb_attn_workspace_size(shape, cfg.end_pos, binding.MLA_DTYPE_BF16)
     ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
-
+    tables = [to_paged(x, cfg, page_size, seed + i, torch) if page_size else None for i, x in enumerate(inputs)]
     calls = [binding.AbsorbAttnCall(x["q_nope"], x["q_pe"], x["kv_cache"], x["pe_cache"], x["wkv_b"], cfg.end_pos,
-                                    cfg.softmax_scale, out, workspace=ws, seq_lens=seq_lens) for x in inputs]
+                                    cfg.softmax_scale, out, workspace=ws, seq_lens=seq_lens, block_table=tb)
+             for x, tb in zip(inputs, tables)]
 
     def step(i):
         calls[i % sets]()
@@ -118,7 +142,7 @@ def time_attn(cfg, steps, warmup, sets, torch, binding, seed=1, timed_kernels=0b
     torch.cuda.synchronize()
     kt = binding.timing_collect()
     binding.timing_enable(0)
-    del inputs, calls
+    del inputs, calls, tables
     torch.cuda.empty_cache()
     return e0.elapsed_time(e1) * 1000.0 / steps, enqueue, kt
 
@@ -145,6 +169,63 @@ def time_expand(cfg, steps, warmup, torch, binding, seed=4):
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) * 1000.0 / steps
+
+
+def naive_work(cfg):
+    """Algorithmic bytes and FLOPs of the naive route's attention over expanded keys and values:
+    k_nope, v and pe rows of the visible positions, q and out; scores over Dn + R, sum over Dv."""
+    B, S, H = cfg.batch, cfg.seqlen_q, cfg.n_heads
+    R, Dn, Dv, T = cfg.qk_rope_head_dim, cfg.qk_nope_head_dim, cfg.v_head_dim, cfg.end_pos
+    e = 2
+    pairs = B * sum(T - S + s + 1 for s in range(S))
+    return {"bytes": (B * T * H * (Dn + Dv) + B * T * R + B * S * H * (Dn + R + Dv)) * e,
+            "flops": 2 * H * pairs * (Dn + R + Dv)}
+
+
+def time_naive_route(cfg, steps, warmup, torch, binding, seed=3):
+    """The naive route over a chunk: expansion of every cached latent row (RMSNorm, wkv_b, split
+    into head-major k_nope / v), then attention over the expanded rows.  Returns (us per step,
+    per-kernel timing dict)."""
+    x = gpu_inputs(cfg, seed, torch)
+    H, C, Dn, Dv = cfg.n_heads, cfg.kv_lora_rank, cfg.qk_nope_head_dim, cfg.v_head_dim
+    rows = cfg.cache_batch * cfg.cache_len
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed + 7)
+    w = (1.0 + 0.14 * torch.randn((C,), generator=g, device="cuda")).to(torch.bfloat16)
+    k = torch.empty((H, rows, Dn), dtype=torch.bfloat16, device="cuda")
+    v = torch.empty((H, rows, Dv), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((cfg.batch, cfg.seqlen_q, H, Dv), dtype=torch.bfloat16, device="cuda")
+    need = binding.expand_kv_workspace_size(rows, H, C, Dn, Dv, binding.MLA_DTYPE_BF16)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+    lat = x["kv_cache"].view(rows, C)
+    k4, v4 = k.view(H, cfg.cache_batch, cfg.cache_len, Dn), v.view(H, cfg.cache_batch, cfg.cache_len, Dv)
+
+    def step():
+        binding.expand_kv(lat, w, x["wkv_b"], H, Dn, Dv, 1e-6, k, v, workspace=ws)
+        binding.naive_attn(x["q_nope"], x["q_pe"], k4, v4, x["pe_cache"], cfg.end_pos, cfg.softmax_scale, out)
+
+    def timed(mask):
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        binding.timing_enable(mask)
+        binding.timing_collect()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(SPIN_CYCLES)
+        e0.record()
+        for _ in range(steps):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        kt = binding.timing_collect()
+        binding.timing_enable(0)
+        return e0.elapsed_time(e1) * 1000.0 / steps, kt
+
+    us, _ = timed(0)
+    _, kt = timed((1 << 3) | (1 << 4) | (1 << 6))
+    del x, k, v, out, ws
+    torch.cuda.empty_cache()
+    return us, kt
 
 
 def cpu_baseline(cfg, budget_s=12.0):
@@ -310,6 +391,21 @@ def main():
             extras[name] = {"us_per_step": round(u, 2), "gbps": round(w["bytes"] / (u * 1e-6) / 1e9, 1),
                             "tflops": round(w["flops"] / (u * 1e-6) / 1e12, 2), "lengths": [lo, hi, int(sum(lens))],
                             "kernels_us": {n: round(v["avg_us"], 2) for n, v in k.items()}}
+        c = ATTN_CONFIGS["dsv3_decode"]
+        w = attn_work(c)
+        u, _, _ = time_attn(c, 30, 3, args.sets, torch, binding, seed=c.seed, timed_kernels=0, page_size=64)
+        _, _, k = time_attn(c, 30, 3, args.sets, torch, binding, seed=c.seed, timed_kernels=0b111, page_size=64)
+        extras["paged_decode"] = {"us_per_step": round(u, 2), "gbps": round(w["bytes"] / (u * 1e-6) / 1e9, 1),
+                                  "page_size": 64, "kernels_us": {n: round(v["avg_us"], 2) for n, v in k.items()}}
+        c = ATTN_CONFIGS["chunk_prefill"]
+        u, k = time_naive_route(c, 10, 3, torch, binding, seed=c.seed)
+        w = naive_work(c)
+        a_us = k["naive"]["avg_us"]
+        extras["chunk_prefill_naive"] = {
+            "us_per_step": round(u, 2), "kernels_us": {n: round(v["avg_us"], 2) for n, v in k.items()},
+            "naive_attn_tflops": round(w["flops"] / (a_us * 1e-6) / 1e12, 1),
+            "naive_attn_mfma_frac": round(w["flops"] / (a_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "naive_attn_gbps": round(w["bytes"] / (a_us * 1e-6) / 1e9, 1)}
         ec = EXPAND_CONFIGS["dsv3_expand"]
         u = time_expand(ec, 20, 3, torch, binding)
         w = expand_work(ec)

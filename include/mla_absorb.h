@@ -142,6 +142,59 @@ int32_t mla_absorb_attn_ragged(const void *q_nope, const void *q_pe, const void 
                                size_t workspace_bytes, void *stream);
 
 /*
+ * Paged caches.  The DeepSeek Sparse Attention explainer (sider.ai, sections on efficient batching
+ * and memory, and on runtime complexity) notes that serving runtimes keep the KV cache in pages
+ * (paged attention) under continuous batching.  Here the two caches of "Memory Layout and Cache
+ * Structure" are pools of fixed-size pages:
+ *
+ *   kv_pages     [num_pages, page_size, C]   compressed latent (normalised, as kv_cache)
+ *   pe_pages     [num_pages, page_size, R]   rope key (as pe_cache)
+ *   block_table  DEVICE int32 [B, max_pages_per_seq]: position t of sequence b lives in page
+ *                block_table[b, t / page_size], row t % page_size
+ *
+ * The attention is that of mla_absorb_attn_ragged over the cache each sequence's pages spell out.
+ */
+typedef struct mla_paged_cache {
+  int64_t page_size;          /* positions per page, >= 1; the matrix-core kernels need a power
+                                 of two >= 32 (other sizes run on the plain kernels) */
+  int64_t num_pages;          /* pages in kv_pages and in pe_pages, >= 1 */
+  int64_t max_pages_per_seq;  /* row length of block_table, >= 1 */
+} mla_paged_cache;
+
+/*
+ * Bytes of device workspace mla_absorb_attn_paged needs for these arguments (0 if none, and 0
+ * with mla_last_error set when they are invalid).  The split plan of a paged call may differ from
+ * that of a contiguous one (the matrix-core kernels start every split on a 32-position boundary
+ * and bound the pages one workgroup reads), so the size has its own query.
+ */
+size_t mla_absorb_attn_paged_workspace_size(const mla_attn_shape *shape, int64_t max_seq_len,
+                                            const mla_paged_cache *paged, int32_t dtype,
+                                            const mla_attn_options *options);
+
+/*
+ * Absorb-form MLA attention over paged caches (layout above).  Sequence b attends to its
+ * positions [0, len_b) with len_b = seq_lens[b] (DEVICE int32 [B], 4-byte aligned) or, when
+ * seq_lens is NULL, len_b = max_seq_len for every sequence; queries and the causal mask as in
+ * mla_absorb_attn_ragged, lengths clamped to [S, max_seq_len] likewise.
+ *
+ *   block_table  DEVICE int32 [B, max_pages_per_seq], 4-byte aligned.  Entries of pages a
+ *                sequence reads must be valid page ids; an id outside [0, num_pages) is clamped
+ *                into it, so no call reads outside the pools.
+ *   max_seq_len  1 <= S <= max_seq_len <= max_pages_per_seq * page_size.
+ *   shape        B, S, H, C, R, Dn, Dv as for mla_absorb_attn; cache_batch and cache_len are
+ *                not used.
+ *   workspace    at least mla_absorb_attn_paged_workspace_size(...) bytes.
+ * Pointers, ownership, options and errors as in mla_absorb_attn; out, the workspace, seq_lens
+ * and block_table must not overlap.  Returns MLA_OK or a negative MLA_ERR_* status.
+ */
+int32_t mla_absorb_attn_paged(const void *q_nope, const void *q_pe, const void *kv_pages,
+                              const void *pe_pages, const void *wkv_b, const int32_t *block_table,
+                              const int32_t *seq_lens, int64_t max_seq_len, float softmax_scale,
+                              void *out, const mla_attn_shape *shape, const mla_paged_cache *paged,
+                              int32_t dtype, const mla_attn_options *options, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
+/*
  * Cache append, the step before attending: writes the S new tokens of each sequence into the
  * two caches mla_absorb_attn reads ("Naive vs Absorb Attention Implementations in DeepSeek-V3",
  * section "Memory Layout and Cache Structure": kv_cache holds each position's compressed latent,

@@ -29,7 +29,8 @@ MLA_DTYPE_BF16 = 1
 
 PATHS = {"auto": 0, "plain": 1, "mfma": 2}
 
-EXPORTED = ("mla_absorb_attn", "mla_absorb_attn_ragged", "mla_absorb_attn_workspace_size", "mla_cache_append",
+EXPORTED = ("mla_absorb_attn", "mla_absorb_attn_ragged", "mla_absorb_attn_paged", "mla_absorb_attn_workspace_size",
+            "mla_absorb_attn_paged_workspace_size", "mla_cache_append",
             "mla_expand_kv", "mla_expand_kv_workspace_size", "mla_naive_attn",
             "mla_strerror",
             "mla_last_error", "mla_timing_enable", "mla_timing_collect", "mla_kernel_name")
@@ -41,6 +42,10 @@ class AttnShape(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in (
         "batch", "seqlen_q", "n_heads", "kv_lora_rank", "qk_rope_head_dim", "qk_nope_head_dim",
         "v_head_dim", "cache_batch", "cache_len")]
+
+
+class PagedCache(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("page_size", "num_pages", "max_pages_per_seq")]
 
 
 class AttnOptions(ctypes.Structure):
@@ -71,6 +76,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_absorb_attn_ragged.argtypes = [vp, vp, vp, vp, vp, vp, i64, ctypes.c_float, vp, ctypes.POINTER(AttnShape),
                                            i32, ctypes.POINTER(AttnOptions), vp, sz, vp]
     lib.mla_absorb_attn_ragged.restype = i32
+    lib.mla_absorb_attn_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, ctypes.c_float, vp,
+                                          ctypes.POINTER(AttnShape), ctypes.POINTER(PagedCache), i32,
+                                          ctypes.POINTER(AttnOptions), vp, sz, vp]
+    lib.mla_absorb_attn_paged.restype = i32
+    lib.mla_absorb_attn_paged_workspace_size.argtypes = [ctypes.POINTER(AttnShape), i64, ctypes.POINTER(PagedCache),
+                                                         i32, ctypes.POINTER(AttnOptions)]
+    lib.mla_absorb_attn_paged_workspace_size.restype = sz
     lib.mla_cache_append.argtypes = [vp, vp, vp, ctypes.c_float, vp, i64, vp, vp, ctypes.POINTER(AttnShape), i32, vp]
     lib.mla_cache_append.restype = i32
     lib.mla_naive_attn.argtypes = [vp, vp, vp, vp, vp, i64, ctypes.c_float, vp, ctypes.POINTER(AttnShape), i32, i32, vp]
@@ -174,6 +186,17 @@ def absorb_attn_workspace_size(shape: AttnShape, end_pos: int, dtype: int, num_s
     return int(n)
 
 
+def absorb_attn_paged_workspace_size(shape: AttnShape, max_seq_len: int, paged: PagedCache, dtype: int,
+                                     num_splits: int = 0, path: str = "auto") -> int:
+    lib = load()
+    opt = AttnOptions(num_splits, PATHS[path])
+    n = lib.mla_absorb_attn_paged_workspace_size(ctypes.byref(shape), max_seq_len, ctypes.byref(paged), dtype,
+                                                 ctypes.byref(opt))
+    if n == 0 and last_error():
+        raise MLAError(MLA_ERR_SHAPE, last_error())
+    return int(n)
+
+
 class AbsorbAttnCall:
     """One absorb-attention call with its arguments marshalled once.
 
@@ -184,38 +207,61 @@ class AbsorbAttnCall:
     """
 
     def __init__(self, q_nope, q_pe, kv_cache, pe_cache, wkv_b, end_pos: int, softmax_scale: float, out=None, *,
-                 num_splits: int = 0, path: str = "auto", workspace=None, seq_lens=None):
+                 num_splits: int = 0, path: str = "auto", workspace=None, seq_lens=None, block_table=None):
         """With seq_lens (an int32 tensor [B] on the same device), sequence b attends to positions
-        [0, seq_lens[b]) and end_pos is the bound of the lengths (mla_absorb_attn_ragged)."""
+        [0, seq_lens[b]) and end_pos is the bound of the lengths (mla_absorb_attn_ragged).  With
+        block_table (int32 [B, max_pages_per_seq]), kv_cache and pe_cache are page pools
+        [num_pages, page_size, C / R] (mla_absorb_attn_paged; seq_lens optional)."""
         import torch
 
         lib = load()
         _require_device(q_nope, q_pe, kv_cache, pe_cache, wkv_b)
         shape = attn_shape(q_nope, q_pe, kv_cache, wkv_b)
         dt = _dtype_code(q_nope)
+        for name, t in (("seq_lens", seq_lens), ("block_table", block_table)):
+            if t is not None and (t.device != q_nope.device or t.dtype != torch.int32 or not t.is_contiguous()):
+                raise ValueError(f"{name} must be a contiguous int32 tensor on the tensors' device")
+        if seq_lens is not None and seq_lens.numel() != shape.batch:
+            raise ValueError("seq_lens must hold one length per sequence")
+        paged = None
+        if block_table is not None:
+            if block_table.dim() != 2 or block_table.shape[0] != shape.batch:
+                raise ValueError("block_table must be [batch, max_pages_per_seq]")
+            num_pages, page_size = kv_cache.shape[0], kv_cache.shape[1]
+            if tuple(pe_cache.shape[:2]) != (num_pages, page_size):
+                raise ValueError("kv and pe page pools disagree")
+            paged = PagedCache(page_size, num_pages, block_table.shape[1])
+            shape.cache_batch, shape.cache_len = shape.batch, block_table.shape[1] * page_size
         if out is None:
             out = torch.empty((shape.batch, shape.seqlen_q, shape.n_heads, shape.v_head_dim), dtype=q_nope.dtype,
                               device=q_nope.device)
         _require_device(q_nope, out)
         opt = AttnOptions(num_splits, PATHS[path])
-        need = absorb_attn_workspace_size(shape, end_pos, dt, num_splits, path)
+        if paged is None:
+            need = absorb_attn_workspace_size(shape, end_pos, dt, num_splits, path)
+        else:
+            need = absorb_attn_paged_workspace_size(shape, end_pos, paged, dt, num_splits, path)
         if workspace is None or workspace.numel() * workspace.element_size() < need:
             workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q_nope.device)
         self.out = out
-        self._keep = (q_nope, q_pe, kv_cache, pe_cache, wkv_b, out, workspace, shape, opt, seq_lens)
+        self._keep = (q_nope, q_pe, kv_cache, pe_cache, wkv_b, out, workspace, shape, opt, seq_lens, block_table,
+                      paged)
         tail = (softmax_scale, out.data_ptr(), ctypes.byref(shape), dt, ctypes.byref(opt), workspace.data_ptr(),
                 workspace.numel() * workspace.element_size(), _stream_handle(q_nope.device))
         head = (q_nope.data_ptr(), q_pe.data_ptr(), kv_cache.data_ptr(), pe_cache.data_ptr(), wkv_b.data_ptr())
-        if seq_lens is None:
+        lens_ptr = None if seq_lens is None else seq_lens.data_ptr()
+        if paged is not None:
+            self._fn = lib.mla_absorb_attn_paged
+            self._args = head + (block_table.data_ptr(), lens_ptr, end_pos, softmax_scale, out.data_ptr(),
+                                 ctypes.byref(shape), ctypes.byref(paged), dt, ctypes.byref(opt),
+                                 workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                 _stream_handle(q_nope.device))
+        elif seq_lens is None:
             self._fn = lib.mla_absorb_attn
             self._args = head + (end_pos,) + tail
         else:
-            if seq_lens.device != q_nope.device or seq_lens.dtype != torch.int32 or not seq_lens.is_contiguous():
-                raise ValueError("seq_lens must be a contiguous int32 tensor on the tensors' device")
-            if seq_lens.numel() != shape.batch:
-                raise ValueError("seq_lens must hold one length per sequence")
             self._fn = lib.mla_absorb_attn_ragged
-            self._args = head + (seq_lens.data_ptr(), end_pos) + tail
+            self._args = head + (lens_ptr, end_pos) + tail
 
     def __call__(self):
         _check(self._fn(*self._args))
@@ -223,11 +269,13 @@ class AbsorbAttnCall:
 
 
 def absorb_attn(q_nope, q_pe, kv_cache, pe_cache, wkv_b, end_pos: int, softmax_scale: float, out=None, *,
-                num_splits: int = 0, path: str = "auto", workspace=None, seq_lens=None):
+                num_splits: int = 0, path: str = "auto", workspace=None, seq_lens=None, block_table=None):
     """MLA attention in absorb form on torch GPU tensors; returns out [B, S, H, Dv].  With
-    seq_lens, a ragged batch whose lengths are bounded by end_pos."""
+    seq_lens, a ragged batch whose lengths are bounded by end_pos; with block_table, paged caches
+    (kv_cache / pe_cache are the page pools)."""
     return AbsorbAttnCall(q_nope, q_pe, kv_cache, pe_cache, wkv_b, end_pos, softmax_scale, out,
-                          num_splits=num_splits, path=path, workspace=workspace, seq_lens=seq_lens)()
+                          num_splits=num_splits, path=path, workspace=workspace, seq_lens=seq_lens,
+                          block_table=block_table)()
 
 
 def cache_append(c_kv_new, k_pe_new, rms_w, eps: float, end_pos: int, kv_cache, pe_cache, *, seq_lens=None):

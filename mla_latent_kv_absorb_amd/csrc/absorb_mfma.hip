@@ -77,7 +77,14 @@ struct AttnArgs {
   int32_t end_pos, splits, split_len, row_blocks;  // end_pos: uniform length or the bound of seq_lens
   const int32_t *seq_lens;  // per-sequence lengths [B] or null (every sequence has end_pos)
   float scale_log2;        // softmax_scale * log2(e)
+  // paged caches: kv / pe are pools of 2^log2_page positions per page, block_table [B, max_pages]
+  const int32_t *block_table;
+  int32_t log2_page, max_pages, num_pages;
 };
+
+// A paged workgroup keeps the page ids of its positions in kPageRegs registers (one per lane and
+// register), so a split may touch at most 64 kPageRegs pages.
+constexpr int kPageRegs = 4;
 
 // Softmax rows keep a reference maximum m_ref and only move it (rescaling the running sum and the
 // 512 accumulators) when a tile's maximum exceeds it by more than kRescale (log2 units), so
@@ -85,6 +92,7 @@ struct AttnArgs {
 // share the same reference.
 constexpr float kRescale = 8.f;
 
+template <bool kPaged>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 attn_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kStages * kStageBytes + 4 * kQpeBytesPerWave];
@@ -124,30 +132,76 @@ attn_kernel(AttnArgs a) {
   // chunk position l and fetches source chunk swz_chunk(l, row).  pe: wave w moves rows
   // 8w..8w+7 (128 bytes each) in one instruction.  Rows past the last needed position repeat the
   // last one (valid data, masked in the softmax); wg_end >= 1, so that row always exists.
-  const rsrc_t kvres = make_rsrc(a.kv + int64_t(b) * a.Tmax * kC, uint32_t(a.Tmax) * (kC * 2));
-  const rsrc_t peres = make_rsrc(a.pe + int64_t(b) * a.Tmax * kR, uint32_t(a.Tmax) * (kR * 2));
+  //
+  // Paged caches: splits start on 32-position boundaries and pages hold a power of two >= 32
+  // positions, so each tile lies in one page, whose base goes into the tile's buffer descriptors
+  // (64-bit, any pool size); the rows' offsets within the page stay 32-bit.  The page ids of the
+  // split's positions sit in registers (slot 64 k + lane of register k is page index
+  // t_begin / page_size + slot), read per tile with v_readlane; tile 0's id comes from a scalar
+  // load so that its DMA need not wait for them.  Rows are clamped into [t0, t0 + 31] as well,
+  // which keeps every offset inside the page even for a workgroup with no tile to compute.
+  const rsrc_t kvres = make_rsrc(a.kv + (kPaged ? 0 : int64_t(b) * a.Tmax * kC), kPaged ? 0u : uint32_t(a.Tmax) * (kC * 2));
+  const rsrc_t peres = make_rsrc(a.pe + (kPaged ? 0 : int64_t(b) * a.Tmax * kR), kPaged ? 0u : uint32_t(a.Tmax) * (kR * 2));
+  const int pg_first = t_begin >> a.log2_page;
+  int ptab[kPageRegs];
+  int page0 = 0;
+  if constexpr (kPaged) {
+    const int32_t *bt = a.block_table + int64_t(b) * a.max_pages;
+    page0 = __builtin_amdgcn_readfirstlane(min(max(bt[min(pg_first, a.max_pages - 1)], 0), a.num_pages - 1));
+    const rsrc_t btres = make_rsrc(bt, uint32_t(a.max_pages) * 4u);
+#pragma unroll
+    for (int k = 0; k < kPageRegs; ++k)  // indices past the table row read 0
+      ptab[k] = min(max(buf_load_i32(btres, uint32_t(pg_first + 64 * k + lane) * 4u, 0), 0), a.num_pages - 1);
+  }
+  auto tile_page = [&](int j, int t0) __attribute__((always_inline)) -> int {
+    if (j == 0) return page0;
+    const int slot = (t0 >> a.log2_page) - pg_first;  // < 64 kPageRegs by the split plan
+    const int ln = slot & 63, k = slot >> 6;
+    int p = __builtin_amdgcn_readlane(ptab[0], ln);
+#pragma unroll
+    for (int r = 1; r < kPageRegs; ++r) p = k == r ? __builtin_amdgcn_readlane(ptab[r], ln) : p;
+    return p;
+  };
   const int pe_row = wave * 8 + (lane >> 3);
   const uint32_t pe_voff = uint32_t((lane & 7) ^ pe_swz(pe_row)) * 16;
   // One of the tile's nine DMA instructions per wave: part 0..7 moves kv row 8w+part, part 8 the pe rows.
   const uint32_t smem_lds = lds_addr(smem);
   const uint32_t lane16 = uint32_t(lane) * 16;
-  auto issue_part = [&](int j, int part) __attribute__((always_inline)) {
+  // Where tile j's rows come from: buffer descriptors, the position at their offset 0, and the
+  // last row to read (rows past it repeat it).
+  struct TileSrc {
+    rsrc_t kv, pe;
+    int tb, tlast;
+  };
+  auto tile_src = [&](int j) __attribute__((always_inline)) -> TileSrc {
+    if constexpr (kPaged) {
+      const int t0 = t_begin + j * kTile;
+      const int64_t page = tile_page(j, t0);
+      return TileSrc{make_rsrc(a.kv + (page << (a.log2_page + 9)), uint32_t(kC * 2) << a.log2_page),
+                     make_rsrc(a.pe + (page << (a.log2_page + 6)), uint32_t(kR * 2) << a.log2_page),
+                     t0 & ~((1 << a.log2_page) - 1), max(wg_end - 1, t0)};
+    } else {
+      return TileSrc{kvres, peres, 0, wg_end - 1};
+    }
+  };
+  auto issue_part = [&](int j, int part, const TileSrc &src) __attribute__((always_inline)) {
     const uint32_t st = smem_lds + uint32_t(j % kStages) * kStageBytes;
     const int t0 = t_begin + j * kTile;
     if (part < 8) {
-      const int t = min(t0 + wave * 8 + part, wg_end - 1);  // wavefront-uniform
+      const int t = min(t0 + wave * 8 + part, src.tlast);  // wavefront-uniform
       // source chunk swz_chunk(lane, row) = lane ^ kv_swz(row), kv_swz(row) wavefront-uniform
-      buf_load16_lds_at(kvres, st + (wave * 8 + part) * (kC * 2),
-                        lane16 ^ uint32_t(kv_swz(8 * (wave & 1) + part) * 16), uint32_t(t) * (kC * 2));
+      buf_load16_lds_at(src.kv, st + (wave * 8 + part) * (kC * 2),
+                        lane16 ^ uint32_t(kv_swz(8 * (wave & 1) + part) * 16), uint32_t(t - src.tb) * (kC * 2));
     } else {
-      const int tp = min(t0 + pe_row, wg_end - 1);
-      buf_load16_lds_at(peres, st + kKvTileBytes + wave * 8 * (kR * 2), pe_voff + uint32_t(tp - t0) * (kR * 2),
-                        uint32_t(t0) * (kR * 2));
+      const int tp = min(t0 + pe_row, src.tlast);
+      buf_load16_lds_at(src.pe, st + kKvTileBytes + wave * 8 * (kR * 2), pe_voff + uint32_t(tp - t0) * (kR * 2),
+                        uint32_t(t0 - src.tb) * (kR * 2));
     }
   };
   auto issue = [&](int j) __attribute__((always_inline)) {
+    const TileSrc src = tile_src(j);
 #pragma unroll
-    for (int part = 0; part < 9; ++part) issue_part(j, part);
+    for (int part = 0; part < 9; ++part) issue_part(j, part, src);
   };
 
   // Prologue: tile 0; the absorbed query into registers and the rope query into LDS; a full wait
@@ -210,7 +264,7 @@ attn_kernel(AttnArgs a) {
   // kRing - 1 MFMAs ahead.  After each group of four MFMAs comes one of the nine DMA instructions
   // of tile `rtile` (when `refill`), so that a full memory queue stalls one instruction at a time.
   constexpr int kRing = 6;
-  auto scores = [&](int j, f32x16 &sc, bool refill, int rtile) __attribute__((always_inline)) {
+  auto scores = [&](int j, f32x16 &sc, bool refill, int rtile, const TileSrc &rsrc) __attribute__((always_inline)) {
     const unsigned char *st = smem + (j % kStages) * kStageBytes;
     auto frag = [&](int k) __attribute__((always_inline)) -> u32x4 {
       return k < 32 ? lds_read16(st, (sc_base ^ uint32_t((k & 7) * 32)) + (k >> 3) * 256)
@@ -233,7 +287,7 @@ attn_kernel(AttnArgs a) {
         else mfma32_v(sc, fr[k % kRing], qb);
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (refill) issue_part(rtile, grp);
+      if (refill) issue_part(rtile, grp, rsrc);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -337,7 +391,7 @@ attn_kernel(AttnArgs a) {
     wait_vmcnt<2 * kLoadsPerTile>();  // tile 0 has landed; tiles 1 and 2 may be in flight
     __builtin_amdgcn_s_barrier();
     compiler_fence();
-    scores(0, sacc, false, 0);
+    scores(0, sacc, false, 0, tile_src(0));
     sm_mask(sacc, t_begin);
     sm_max(sacc);
     sm_ref();
@@ -351,7 +405,7 @@ attn_kernel(AttnArgs a) {
     else wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
     compiler_fence();
-    scores(j + 1, sacc, j + 3 < ntiles, j + 3);
+    scores(j + 1, sacc, j + 3 < ntiles, j + 3, tile_src(j + 3));
     const int t1 = t_begin + (j + 1) * kTile;
     sm_mask(sacc, t1);
     u32x4 pn[2];
@@ -740,8 +794,20 @@ bool mfma_attn_supported(const AttnCall &c, const char **why) {
     *why = "needs kv_lora_rank 512, qk_rope_head_dim 64, qk_nope_head_dim 128, v_head_dim 128";
     return false;
   }
-  // per-sequence buffer ranges are byte counts below 2^32
-  if (c.Tmax >= (int64_t(1) << 22)) { *why = "cache_len must be below 4194304"; return false; }
+  if (c.page_size > 0) {
+    // a tile must lie in one page; page ranges are 32-bit byte counts
+    if (c.page_size < kTile || (c.page_size & (c.page_size - 1)) || c.page_size > 65536) {
+      *why = "needs a page_size that is a power of two in [32, 65536]";
+      return false;
+    }
+    if (c.max_pages >= (int64_t(1) << 28)) {  // the table row's byte range is 32-bit
+      *why = "max_pages_per_seq must be below 2^28";
+      return false;
+    }
+  } else if (c.Tmax >= (int64_t(1) << 22)) {  // per-sequence buffer ranges are byte counts below 2^32
+    *why = "cache_len must be below 4194304";
+    return false;
+  }
   if (c.B * c.S * c.H * int64_t(kC) * 2 >= (int64_t(1) << 32)) { *why = "too many query rows"; return false; }
   return true;
 }
@@ -754,13 +820,23 @@ int32_t mfma_attn_splits(const AttnCall &c, int num_cus) {
   const int64_t max_by_len = (c.end_pos + 127) / 128;
   if (splits > max_by_len) splits = max_by_len;
   if (splits < 1) splits = 1;
+  if (c.page_size > 0) {  // a split may span at most 64 kPageRegs pages
+    const int64_t cap = mfma_paged_max_split_len(c);
+    splits = std::max<int64_t>(splits, (c.end_pos + cap - 1) / cap);
+  }
   if (splits > 4096) splits = 4096;
   return int32_t(splits);
 }
 
+int64_t mfma_paged_max_split_len(const AttnCall &c) { return (64 * kPageRegs - 1) * c.page_size; }
+
 bool mfma_attn_plan_ok(const AttnCall &c, const char **why) {
   if (c.splits < 1 || c.splits > kMaxSplits) {
     *why = "num_splits outside [1, 4096]";
+    return false;
+  }
+  if (c.page_size > 0 && (c.split_len % kTile || c.split_len > mfma_paged_max_split_len(c))) {
+    *why = "paged splits must be multiples of 32 positions spanning at most 255 pages";
     return false;
   }
   // split partials are addressed with 32-bit byte offsets
@@ -820,7 +896,16 @@ hipError_t mfma_absorb_attn(const AttnCall &c) {
   aa.row_blocks = row_blocks;
   aa.scale_log2 = c.scale * kLog2e;
   const int64_t nwg = c.B * int64_t(aa.splits) * aa.row_blocks;
-  err = launch_kernel(MLA_KERNEL_ATTN, attn_kernel, dim3(unsigned(nwg)), dim3(256), 0, c.stream, aa);
+  if (c.page_size > 0) {
+    aa.block_table = c.block_table;
+    aa.log2_page = 0;
+    while ((int64_t(1) << aa.log2_page) < c.page_size) ++aa.log2_page;
+    aa.max_pages = int32_t(c.max_pages);
+    aa.num_pages = int32_t(c.num_pages);
+    err = launch_kernel(MLA_KERNEL_ATTN, attn_kernel<true>, dim3(unsigned(nwg)), dim3(256), 0, c.stream, aa);
+  } else {
+    err = launch_kernel(MLA_KERNEL_ATTN, attn_kernel<false>, dim3(unsigned(nwg)), dim3(256), 0, c.stream, aa);
+  }
   if (err != hipSuccess) return err;
 
   // split combine and W_UV projection: enough workgroups per head to fill the chip, each reusing

@@ -12,6 +12,11 @@ struct AttnCall {
   int64_t B, S, H, C, R, Dn, Dv, Bmax, Tmax;
   int64_t end_pos;           // uniform length, or the upper bound of the per-sequence lengths
   const int32_t *seq_lens;   // device [B] per-sequence lengths (clamped to [S, end_pos]), or null
+  // paged caches (page_size > 0): kv / pe are pools [num_pages, page_size, C / R] and position t
+  // of sequence b is row t % page_size of page block_table[b * max_pages + t / page_size]
+  // (clamped into [0, num_pages)); with page_size 0 the caches are [Bmax, Tmax, C / R]
+  const int32_t *block_table;
+  int64_t page_size, num_pages, max_pages;
   float scale;
   int32_t dtype;      // MLA_DTYPE_*
   int32_t splits;     // ranges the positions [0, end_pos) are cut into
@@ -86,6 +91,7 @@ bool mfma_attn_supported(const AttnCall &c, const char **why);
 size_t mfma_attn_workspace(const AttnCall &c);
 int32_t mfma_attn_splits(const AttnCall &c, int num_cus);
 bool mfma_attn_plan_ok(const AttnCall &c, const char **why);  // limits that depend on the split count
+int64_t mfma_paged_max_split_len(const AttnCall &c);           // longest split of a paged call
 hipError_t mfma_absorb_attn(const AttnCall &c);
 
 hipError_t cache_append(const AppendCall &a);

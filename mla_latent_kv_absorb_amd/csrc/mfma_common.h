@@ -92,6 +92,9 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
 __device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
 }
+__device__ __forceinline__ int buf_load_i32(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return int(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
 __device__ __forceinline__ void buf_store16(rsrc_t r, const u32x4 &v, uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, soff, 0);
 }

@@ -2,6 +2,7 @@
 // Every check runs before the first HIP call, so a rejected call enqueues nothing.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -35,11 +36,28 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
 // Shape, dtype and option checks shared by the size query and the call.  Fills `c` (without
 // pointers) and picks the kernel path.  Makes no HIP call: the plan depends only on the
 // arguments, so the size query and the call always agree.
-int32_t plan_attn(const mla_attn_shape *shape, int64_t end_pos, int32_t dtype,
+// With `paged` the caches are page pools: the shape's cache fields are replaced by the batch and
+// the per-sequence capacity max_pages_per_seq * page_size.
+int32_t plan_attn(const mla_attn_shape *shape, int64_t end_pos, const mla_paged_cache *paged, int32_t dtype,
                   const mla_attn_options *options, mla::AttnCall &c, bool &use_mfma) {
   if (!shape) return fail(MLA_ERR_NULL, "shape is NULL");
   if (dtype != MLA_DTYPE_F32 && dtype != MLA_DTYPE_BF16) return fail(MLA_ERR_DTYPE, "unknown dtype %d", dtype);
-  const mla_attn_shape &s = *shape;
+  mla_attn_shape s = *shape;
+  if (paged) {
+    const mla_paged_cache &pg = *paged;
+    if (pg.page_size < 1 || pg.page_size > (int64_t(1) << 20))
+      return fail(MLA_ERR_SHAPE, "page_size = %lld outside [1, 1048576]", (long long)pg.page_size);
+    if (pg.num_pages < 1 || pg.num_pages > (int64_t(1) << 31) - 1)
+      return fail(MLA_ERR_SHAPE, "num_pages = %lld outside [1, 2^31 - 1]", (long long)pg.num_pages);
+    if (pg.max_pages_per_seq < 1 || pg.max_pages_per_seq > (int64_t(1) << 31) - 1)
+      return fail(MLA_ERR_SHAPE, "max_pages_per_seq = %lld outside [1, 2^31 - 1]", (long long)pg.max_pages_per_seq);
+    if (s.batch > 0 && s.batch * pg.max_pages_per_seq > (int64_t(1) << 31) - 1)
+      return fail(MLA_ERR_SHAPE, "batch * max_pages_per_seq is too large");
+    if (pg.num_pages * pg.page_size > (int64_t(1) << 40))
+      return fail(MLA_ERR_SHAPE, "num_pages * page_size is too large");
+    s.cache_batch = s.batch;
+    s.cache_len = std::min<int64_t>(pg.max_pages_per_seq * pg.page_size, int64_t(1) << 31);
+  }
   const int64_t dims[] = {s.batch, s.seqlen_q, s.n_heads, s.kv_lora_rank, s.qk_rope_head_dim,
                           s.qk_nope_head_dim, s.v_head_dim, s.cache_batch, s.cache_len};
   const char *names[] = {"batch", "seqlen_q", "n_heads", "kv_lora_rank", "qk_rope_head_dim",
@@ -74,6 +92,9 @@ int32_t plan_attn(const mla_attn_shape *shape, int64_t end_pos, int32_t dtype,
   c.B = s.batch; c.S = s.seqlen_q; c.H = s.n_heads; c.C = s.kv_lora_rank; c.R = s.qk_rope_head_dim;
   c.Dn = s.qk_nope_head_dim; c.Dv = s.v_head_dim; c.Bmax = s.cache_batch; c.Tmax = s.cache_len;
   c.end_pos = end_pos; c.dtype = dtype;
+  if (paged) {
+    c.page_size = paged->page_size; c.num_pages = paged->num_pages; c.max_pages = paged->max_pages_per_seq;
+  }
 
   use_mfma = false;
   if (opt.path != MLA_PATH_PLAIN) {
@@ -89,6 +110,7 @@ int32_t plan_attn(const mla_attn_shape *shape, int64_t end_pos, int32_t dtype,
   }
   if (c.splits > end_pos) c.splits = int32_t(end_pos);
   c.split_len = (end_pos + c.splits - 1) / c.splits;
+  if (use_mfma && c.page_size > 0) c.split_len = (c.split_len + 31) / 32 * 32;  // tiles within pages
   if (use_mfma) {
     const char *why = "";
     if (!mla::mfma_attn_plan_ok(c, &why)) {
@@ -130,7 +152,18 @@ size_t mla_absorb_attn_workspace_size(const mla_attn_shape *shape, int64_t end_p
   clear_error();
   mla::AttnCall c;
   bool use_mfma = false;
-  if (plan_attn(shape, end_pos, dtype, options, c, use_mfma) != MLA_OK) return 0;
+  if (plan_attn(shape, end_pos, nullptr, dtype, options, c, use_mfma) != MLA_OK) return 0;
+  return use_mfma ? mla::mfma_attn_workspace(c) : mla::plain_attn_workspace(c);
+}
+
+size_t mla_absorb_attn_paged_workspace_size(const mla_attn_shape *shape, int64_t max_seq_len,
+                                            const mla_paged_cache *paged, int32_t dtype,
+                                            const mla_attn_options *options) {
+  clear_error();
+  if (!paged) { fail(MLA_ERR_NULL, "paged is NULL"); return 0; }
+  mla::AttnCall c;
+  bool use_mfma = false;
+  if (plan_attn(shape, max_seq_len, paged, dtype, options, c, use_mfma) != MLA_OK) return 0;
   return use_mfma ? mla::mfma_attn_workspace(c) : mla::plain_attn_workspace(c);
 }
 
@@ -138,14 +171,16 @@ size_t mla_absorb_attn_workspace_size(const mla_attn_shape *shape, int64_t end_p
 
 namespace {
 
-// The body of mla_absorb_attn and mla_absorb_attn_ragged (seq_lens null for a uniform batch).
+// The body of mla_absorb_attn, mla_absorb_attn_ragged and mla_absorb_attn_paged (seq_lens null
+// for a uniform batch; paged and block_table null for contiguous caches).
 int32_t absorb_attn_call(const void *q_nope, const void *q_pe, const void *kv_cache, const void *pe_cache,
-                         const void *wkv_b, const int32_t *seq_lens, int64_t end_pos, float softmax_scale,
-                         void *out, const mla_attn_shape *shape, int32_t dtype, const mla_attn_options *options,
+                         const void *wkv_b, const int32_t *seq_lens, const int32_t *block_table,
+                         const mla_paged_cache *paged, int64_t end_pos, float softmax_scale, void *out,
+                         const mla_attn_shape *shape, int32_t dtype, const mla_attn_options *options,
                          void *workspace, size_t workspace_bytes, void *stream) {
   mla::AttnCall c;
   bool use_mfma = false;
-  int32_t rc = plan_attn(shape, end_pos, dtype, options, c, use_mfma);
+  int32_t rc = plan_attn(shape, end_pos, paged, dtype, options, c, use_mfma);
   if (rc != MLA_OK) return rc;
   const void *ptrs[] = {q_nope, q_pe, kv_cache, pe_cache, wkv_b, out};
   const char *names[] = {"q_nope", "q_pe", "kv_cache", "pe_cache", "wkv_b", "out"};
@@ -157,14 +192,18 @@ int32_t absorb_attn_call(const void *q_nope, const void *q_pe, const void *kv_ca
     return fail(MLA_ERR_SHAPE, "softmax_scale must be a positive finite number");
   const size_t es = elem_size(dtype);
   const size_t rows = size_t(c.B * c.S * c.H);
+  const size_t cache_rows = paged ? size_t(c.num_pages * c.page_size) : size_t(c.Bmax * c.Tmax);
   const size_t bytes_in[] = {rows * size_t(c.Dn) * es, rows * size_t(c.R) * es,
-                             size_t(c.Bmax * c.Tmax * c.C) * es, size_t(c.Bmax * c.Tmax * c.R) * es,
+                             cache_rows * size_t(c.C) * es, cache_rows * size_t(c.R) * es,
                              size_t(c.H * (c.Dn + c.Dv) * c.C) * es};
   const size_t out_bytes = rows * size_t(c.Dv) * es;
   for (int i = 0; i < 5; ++i)
     if (overlaps(out, out_bytes, ptrs[i], bytes_in[i])) return fail(MLA_ERR_SHAPE, "out overlaps %s", names[i]);
   const size_t lens_bytes = size_t(c.B) * sizeof(int32_t);
   if (seq_lens && overlaps(out, out_bytes, seq_lens, lens_bytes)) return fail(MLA_ERR_SHAPE, "out overlaps seq_lens");
+  const size_t table_bytes = size_t(c.B * c.max_pages) * sizeof(int32_t);
+  if (block_table && overlaps(out, out_bytes, block_table, table_bytes))
+    return fail(MLA_ERR_SHAPE, "out overlaps block_table");
   const size_t need = use_mfma ? mla::mfma_attn_workspace(c) : mla::plain_attn_workspace(c);
   if (need > 0) {
     if (!workspace) return fail(MLA_ERR_WORKSPACE, "workspace is NULL but %zu bytes are needed", need);
@@ -177,11 +216,14 @@ int32_t absorb_attn_call(const void *q_nope, const void *q_pe, const void *kv_ca
         return fail(MLA_ERR_WORKSPACE, "workspace overlaps %s", names[i]);
     if (seq_lens && overlaps(workspace, need, seq_lens, lens_bytes))
       return fail(MLA_ERR_WORKSPACE, "workspace overlaps seq_lens");
+    if (block_table && overlaps(workspace, need, block_table, table_bytes))
+      return fail(MLA_ERR_WORKSPACE, "workspace overlaps block_table");
   }
   c.scale = softmax_scale;
   c.q_nope = q_nope; c.q_pe = q_pe; c.kv = kv_cache; c.pe = pe_cache; c.wkv_b = wkv_b;
   c.out = out; c.ws = workspace; c.stream = static_cast<hipStream_t>(stream);
   c.seq_lens = seq_lens;
+  c.block_table = block_table;
   if (use_mfma && c.splits == 0) c.splits = 1;
   hipError_t e = use_mfma ? mla::mfma_absorb_attn(c) : mla::plain_absorb_attn(c);
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
@@ -197,8 +239,8 @@ int32_t mla_absorb_attn(const void *q_nope, const void *q_pe, const void *kv_cac
                         const mla_attn_shape *shape, int32_t dtype, const mla_attn_options *options,
                         void *workspace, size_t workspace_bytes, void *stream) {
   clear_error();
-  return absorb_attn_call(q_nope, q_pe, kv_cache, pe_cache, wkv_b, nullptr, end_pos, softmax_scale, out, shape,
-                          dtype, options, workspace, workspace_bytes, stream);
+  return absorb_attn_call(q_nope, q_pe, kv_cache, pe_cache, wkv_b, nullptr, nullptr, nullptr, end_pos, softmax_scale,
+                          out, shape, dtype, options, workspace, workspace_bytes, stream);
 }
 
 int32_t mla_absorb_attn_ragged(const void *q_nope, const void *q_pe, const void *kv_cache, const void *pe_cache,
@@ -209,8 +251,22 @@ int32_t mla_absorb_attn_ragged(const void *q_nope, const void *q_pe, const void 
   clear_error();
   if (!seq_lens) return fail(MLA_ERR_NULL, "seq_lens is NULL");
   if (reinterpret_cast<uintptr_t>(seq_lens) & 3u) return fail(MLA_ERR_ALIGN, "seq_lens is not 4-byte aligned");
-  return absorb_attn_call(q_nope, q_pe, kv_cache, pe_cache, wkv_b, seq_lens, max_seq_len, softmax_scale, out, shape,
-                          dtype, options, workspace, workspace_bytes, stream);
+  return absorb_attn_call(q_nope, q_pe, kv_cache, pe_cache, wkv_b, seq_lens, nullptr, nullptr, max_seq_len,
+                          softmax_scale, out, shape, dtype, options, workspace, workspace_bytes, stream);
+}
+
+int32_t mla_absorb_attn_paged(const void *q_nope, const void *q_pe, const void *kv_pages, const void *pe_pages,
+                              const void *wkv_b, const int32_t *block_table, const int32_t *seq_lens,
+                              int64_t max_seq_len, float softmax_scale, void *out, const mla_attn_shape *shape,
+                              const mla_paged_cache *paged, int32_t dtype, const mla_attn_options *options,
+                              void *workspace, size_t workspace_bytes, void *stream) {
+  clear_error();
+  if (!paged) return fail(MLA_ERR_NULL, "paged is NULL");
+  if (!block_table) return fail(MLA_ERR_NULL, "block_table is NULL");
+  if (reinterpret_cast<uintptr_t>(block_table) & 3u) return fail(MLA_ERR_ALIGN, "block_table is not 4-byte aligned");
+  if (reinterpret_cast<uintptr_t>(seq_lens) & 3u) return fail(MLA_ERR_ALIGN, "seq_lens is not 4-byte aligned");
+  return absorb_attn_call(q_nope, q_pe, kv_pages, pe_pages, wkv_b, seq_lens, block_table, paged, max_seq_len,
+                          softmax_scale, out, shape, dtype, options, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

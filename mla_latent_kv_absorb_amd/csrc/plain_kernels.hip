@@ -30,6 +30,15 @@ plain_absorb_q_kernel(const T *__restrict__ q_nope, const T *__restrict__ wkv_b,
   q_lat[row * C + c] = acc;
 }
 
+// Row of position t of sequence b in the kv / pe arrays: b * Tmax + t for contiguous caches; for
+// paged ones row t % page_size of the sequence's page for t, its id clamped into [0, num_pages).
+__device__ __forceinline__ int64_t cache_row(const AttnCall &a, int64_t b, int64_t t) {
+  if (a.page_size == 0) return b * a.Tmax + t;
+  int64_t pg = a.block_table[b * a.max_pages + t / a.page_size];
+  pg = pg < 0 ? 0 : (pg >= a.num_pages ? a.num_pages - 1 : pg);
+  return pg * a.page_size + t % a.page_size;
+}
+
 // One block per (row, split): online softmax over the split's visible positions.
 // Writes m (largest scaled score, -inf if none visible), l (sum of exp(score - m)) and
 // o[c] = sum exp(score - m) * kv[t, c].
@@ -44,6 +53,7 @@ plain_attn_partial_kernel(const float *__restrict__ q_lat, const T *__restrict__
   float *so = sqp + a.R;      // C   running weighted sum
   float *sp = so + a.C;       // kThreads probabilities of the current chunk
   float *red = sp + kThreads; // 16
+  int64_t *srow = reinterpret_cast<int64_t *>(red + 16);  // kThreads cache rows of the current chunk
 
   const int64_t row = blockIdx.x;
   const int split = blockIdx.y;
@@ -67,17 +77,17 @@ plain_attn_partial_kernel(const float *__restrict__ q_lat, const T *__restrict__
   for (int64_t r = tid; r < a.R; r += kThreads) sqp[r] = Elem<T>::load(q_pe, row * a.R + r);
   __syncthreads();
 
-  const T *kvb = kv + b * a.Tmax * a.C;
-  const T *peb = pe + b * a.Tmax * a.R;
   float m = -INFINITY, l = 0.f;
   for (int64_t tc = t0; tc < t1; tc += kThreads) {
     const int n = int((t1 - tc) < kThreads ? (t1 - tc) : kThreads);
+    if (tid < n) srow[tid] = cache_row(a, b, tc + tid);
+    __syncthreads();
     float sc = -INFINITY;
     if (tid < n) {
-      const int64_t t = tc + tid;
+      const int64_t r0 = srow[tid];
       float acc = 0.f;
-      for (int64_t c = 0; c < a.C; ++c) acc = fmaf(sq[c], Elem<T>::load(kvb, t * a.C + c), acc);
-      for (int64_t r = 0; r < a.R; ++r) acc = fmaf(sqp[r], Elem<T>::load(peb, t * a.R + r), acc);
+      for (int64_t c = 0; c < a.C; ++c) acc = fmaf(sq[c], Elem<T>::load(kv, r0 * a.C + c), acc);
+      for (int64_t r = 0; r < a.R; ++r) acc = fmaf(sqp[r], Elem<T>::load(pe, r0 * a.R + r), acc);
       sc = acc * a.scale;
     }
     const float m_new = fmaxf(m, block_max(sc, red));
@@ -87,7 +97,7 @@ plain_attn_partial_kernel(const float *__restrict__ q_lat, const T *__restrict__
     l = l * alpha + block_sum(p, red);  // block_sum synchronises, so sp is visible below
     for (int64_t c = tid; c < a.C; c += kThreads) {
       float acc = so[c] * alpha;
-      for (int j = 0; j < n; ++j) acc = fmaf(sp[j], Elem<T>::load(kvb, (tc + j) * a.C + c), acc);
+      for (int j = 0; j < n; ++j) acc = fmaf(sp[j], Elem<T>::load(kv, srow[j] * a.C + c), acc);
       so[c] = acc;
     }
     m = m_new;
@@ -171,7 +181,7 @@ hipError_t run_attn(const AttnCall &a) {
   timing_begin(MLA_KERNEL_PLAIN, a.stream);
   plain_absorb_q_kernel<T><<<dim3(unsigned(rows), unsigned((a.C + kThreads - 1) / kThreads)), kThreads, 0,
                              a.stream>>>(q_nope, static_cast<const T *>(a.wkv_b), q_lat, a.H, a.C, a.Dn, a.Dv);
-  const size_t sm_attn = sizeof(float) * size_t(2 * a.C + a.R + kThreads + 16);
+  const size_t sm_attn = sizeof(float) * size_t(2 * a.C + a.R + kThreads + 16) + sizeof(int64_t) * kThreads;
   plain_attn_partial_kernel<T><<<dim3(unsigned(rows), unsigned(a.splits)), kThreads, sm_attn, a.stream>>>(
       q_lat, static_cast<const T *>(a.q_pe), static_cast<const T *>(a.kv), static_cast<const T *>(a.pe),
       part_ml, part_o, a);

@@ -35,6 +35,10 @@ Readings adopted where the pages are silent (each is listed in the design doc):
   * A ragged batch (each sequence with its own length) takes the page's slice
     [:bsz, :end_pos] per sequence: sequence b attends to positions
     [0, seq_lens[b]) with its queries at seq_lens[b] - S + s.
+  * A paged cache (the DeepSeek Sparse Attention explainer's paged attention /
+    KV-cache pages) is storage only: position t of sequence b is row
+    t % page_size of page block_table[b, t // page_size]; the attention is that
+    of the ragged batch over the rows the pages spell out.
 """
 from __future__ import annotations
 
@@ -54,6 +58,8 @@ __all__ = [
     "merge_partials",
     "absorb_attention_rows",
     "absorb_attention_ragged",
+    "paged_gather",
+    "absorb_attention_paged",
     "rms_norm",
     "expand_kv",
     "cache_append",
@@ -290,6 +296,29 @@ def absorb_attention_ragged(q_nope, q_pe, kv_cache, pe_cache, wkv_b, seq_lens, s
                             int(seq_lens[b]), softmax_scale, v_head_dim, dtype)
            for b in range(B)]
     return np.concatenate(out, axis=0)
+
+
+def paged_gather(pages, block_table, length: int, b: int, page_size: int):
+    """The cache rows [0, length) of sequence b spelled out by its pages: row t is
+    pages[block_table[b, t // page_size], t % page_size]."""
+    t = np.arange(length)
+    return pages[np.asarray(block_table)[b, t // page_size], t % page_size]
+
+
+def absorb_attention_paged(q_nope, q_pe, kv_pages, pe_pages, wkv_b, block_table, seq_lens, page_size: int,
+                           softmax_scale: float, v_head_dim: int, dtype=np.float64,
+                           rows: Iterable[Tuple[int, int, int]] = None):
+    """absorb_attention_ragged over paged caches: kv_pages [P, page_size, C], pe_pages
+    [P, page_size, R], block_table [B, max_pages]; sequence b's cache is its gathered rows."""
+    B = q_nope.shape[0]
+    lens = [int(n) for n in seq_lens]
+    T = max(lens)
+    kv = np.zeros((B, T, kv_pages.shape[-1]), dtype)
+    pe = np.zeros((B, T, pe_pages.shape[-1]), dtype)
+    for b in range(B):
+        kv[b, :lens[b]] = paged_gather(_as(kv_pages, dtype), block_table, lens[b], b, page_size)
+        pe[b, :lens[b]] = paged_gather(_as(pe_pages, dtype), block_table, lens[b], b, page_size)
+    return absorb_attention_ragged(q_nope, q_pe, kv, pe, wkv_b, lens, softmax_scale, v_head_dim, dtype, rows)
 
 
 def rms_norm(x, w, eps: float, dtype=np.float64):

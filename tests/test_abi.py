@@ -242,3 +242,55 @@ def test_naive_attn_argument_errors(lib):
         p = list(P[:6])
         p[5] = P[i] + 4096
         assert call_naive(lib, s, ptrs=p) == B.MLA_ERR_SHAPE
+
+
+def call_paged(lib, s, max_len=4096, ptrs=None, bt=P[6], lens=None, pg=None, path=B.PATHS["auto"], splits=0,
+               ws=P[7], ws_bytes=1 << 40):
+    p = list(P[:6]) if ptrs is None else ptrs
+    pg = B.PagedCache(64, 256, 64) if pg is None else pg
+    opt = B.AttnOptions(splits, path)
+    return lib.mla_absorb_attn_paged(p[0], p[1], p[2], p[3], p[4], bt, lens, max_len, 0.07, p[5], ctypes.byref(s),
+                                     ctypes.byref(pg), B.MLA_DTYPE_BF16, ctypes.byref(opt), ws, ws_bytes, None)
+
+
+def test_paged_argument_errors(lib):
+    s = shape()
+    opt = B.AttnOptions(0, 0)
+    assert lib.mla_absorb_attn_paged(*P[:5], P[6], None, 4096, 0.07, P[5], ctypes.byref(s), None, B.MLA_DTYPE_BF16,
+                                     ctypes.byref(opt), P[7], 1 << 40, None) == B.MLA_ERR_NULL
+    assert call_paged(lib, s, bt=None) == B.MLA_ERR_NULL
+    assert call_paged(lib, s, bt=P[6] + 2) == B.MLA_ERR_ALIGN
+    assert call_paged(lib, s, lens=P[6] + 4096 + 2) == B.MLA_ERR_ALIGN
+    assert call_paged(lib, s, pg=B.PagedCache(0, 256, 64)) == B.MLA_ERR_SHAPE
+    assert call_paged(lib, s, pg=B.PagedCache(64, 0, 64)) == B.MLA_ERR_SHAPE
+    assert call_paged(lib, s, pg=B.PagedCache(64, 256, 0)) == B.MLA_ERR_SHAPE
+    # capacity max_pages_per_seq * page_size bounds max_seq_len; shape's cache fields are not used
+    assert call_paged(lib, s, max_len=4097) == B.MLA_ERR_RANGE
+    assert call_paged(lib, shape(cache_batch=1, cache_len=1), max_len=4097) == B.MLA_ERR_RANGE
+    assert call_paged(lib, s, max_len=0) == B.MLA_ERR_RANGE
+    # the matrix-core kernels need a power-of-two page of at least 32 positions
+    for bad in (16, 48, 100):
+        pg = B.PagedCache(bad, 4096, 4096 // bad + 1)
+        assert call_paged(lib, s, pg=pg, path=B.PATHS["mfma"]) == B.MLA_ERR_UNSUPPORTED
+    # out, workspace, block_table and seq_lens must not overlap
+    assert call_paged(lib, s, bt=P[5] + 64) == B.MLA_ERR_SHAPE
+    assert call_paged(lib, s, bt=P[7] + 64) == B.MLA_ERR_WORKSPACE
+    assert call_paged(lib, s, lens=P[5] + 64) == B.MLA_ERR_SHAPE
+    assert call_paged(lib, s, ws_bytes=16) == B.MLA_ERR_WORKSPACE
+
+
+def test_paged_workspace_and_split_plan(lib):
+    s = shape(batch=32)
+    pg = B.PagedCache(64, 32 * 64, 64)
+    # at the decode shape the paged plan is the contiguous one
+    assert B.absorb_attn_paged_workspace_size(s, 4096, pg, B.MLA_DTYPE_BF16) == \
+        B.absorb_attn_workspace_size(shape(batch=32, cache_batch=32), 4096, B.MLA_DTYPE_BF16)
+    # one split over 16384 positions spans more pages of 32 than a workgroup keeps: refused on the
+    # matrix-core path, planned with more splits by default
+    one = shape(batch=1, seqlen_q=512, n_heads=128, cache_batch=1, cache_len=16384)
+    pg32 = B.PagedCache(32, 512, 512)
+    with pytest.raises(B.MLAError):
+        B.absorb_attn_paged_workspace_size(one, 16384, pg32, B.MLA_DTYPE_BF16, num_splits=1, path="mfma")
+    ws = {p: B.absorb_attn_paged_workspace_size(one, 16384, B.PagedCache(p, 16384 // p, 16384 // p),
+                                                B.MLA_DTYPE_BF16, path="mfma") for p in (32, 64, 128)}
+    assert ws[32] > ws[64] > ws[128] == B.absorb_attn_workspace_size(one, 16384, B.MLA_DTYPE_BF16, path="mfma")

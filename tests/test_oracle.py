@@ -348,6 +348,58 @@ def pin_attention_over_kv():
     return worst
 
 
+def scatter_to_pages(cache, lens, page_size, num_pages, rng, table=None):
+    """Write each sequence's rows [0, len) into randomly chosen distinct pages of a pool filled
+    with garbage (or into the pages `table` names); returns (pool, block_table).  Page k of
+    sequence b holds its positions k*page_size .. k*page_size + page_size - 1."""
+    B = cache.shape[0]
+    need = [-(-n // page_size) for n in lens]
+    if table is None:
+        ids = rng.permutation(num_pages)
+        table = rng.integers(0, num_pages, (B, max(need) + 1)).astype(np.int32)  # unused entries: any id
+        used = 0
+        for b in range(B):
+            for k in range(need[b]):
+                table[b, k] = ids[used]
+                used += 1
+    pool = rng.normal(0, 1e6, (num_pages, page_size) + cache.shape[2:])
+    for b in range(B):
+        for k in range(need[b]):
+            for slot in range(page_size):
+                t = k * page_size + slot
+                if t < lens[b]:
+                    pool[table[b, k], slot] = cache[b, t]
+    return pool, table
+
+
+def pin_paged():
+    """Paged caches: rows scattered into random pages of a garbage-filled pool (unused table
+    entries pointing anywhere) give the naive route on the contiguous cache, sequence by
+    sequence at its own length (a different code path), for page sizes that do and do not
+    divide the lengths; and gathering the scattered rows returns them unchanged."""
+    worst = 0.0
+    rng = np.random.default_rng(71)
+    for seqlen_q, lens, page_size in ((1, [5, 9, 12], 4), (2, [3, 12, 7], 3), (1, [12, 1, 8], 1)):
+        cfg = small_cfg(batch=3, cache_batch=3, seqlen_q=seqlen_q, end_pos=12, cache_len=12, seed=72 + page_size)
+        x = make_attn_inputs(cfg)
+        num_pages = sum(-(-n // page_size) for n in lens) + 5
+        kvp, table = scatter_to_pages(np.asarray(x["kv_cache"], np.float64), lens, page_size, num_pages, rng)
+        pep, _ = scatter_to_pages(np.asarray(x["pe_cache"], np.float64), lens, page_size, num_pages, rng, table)
+        got = O.absorb_attention_paged(x["q_nope"], x["q_pe"], kvp, pep, x["wkv_b"], table, lens, page_size,
+                                       cfg.softmax_scale, cfg.v_head_dim)
+        for b, n in enumerate(lens):
+            nv = O.naive_attention(x["q_nope"][b:b + 1], x["q_pe"][b:b + 1], x["kv_cache"][b:b + 1],
+                                   x["pe_cache"][b:b + 1], x["wkv_b"], n, cfg.softmax_scale, cfg.v_head_dim)
+            worst = max(worst, rel_err(got[b], nv[0]))
+            g = O.paged_gather(kvp, table, n, b, page_size)
+            worst = max(worst, float(np.abs(g - x["kv_cache"][b, :n]).max()))
+        rows = [(0, seqlen_q - 1, 0), (2, 0, 2)]
+        sel = O.absorb_attention_paged(x["q_nope"], x["q_pe"], kvp, pep, x["wkv_b"], table, lens, page_size,
+                                       cfg.softmax_scale, cfg.v_head_dim, rows=rows)
+        worst = max(worst, rel_err(sel, np.stack([got[b, s_, h] for b, s_, h in rows])))
+    return worst
+
+
 PINS = {
     "naive_equals_absorb": (pin_naive_equals_absorb, 1e-12),
     "golden": (pin_golden, 1e-12),
@@ -365,6 +417,7 @@ PINS = {
     "ragged": (pin_ragged, 1e-12),
     "append": (pin_append, 1e-12),
     "attention_over_kv": (pin_attention_over_kv, 1e-12),
+    "paged": (pin_paged, 1e-12),
 }
 
 
@@ -482,6 +535,17 @@ def _append_one_late(c_kv_new, k_pe_new, rms_w, eps, kv_cache, pe_cache, end_pos
     return kv, pe
 
 
+def _gather_ignores_table(pages, block_table, length, b, page_size):
+    # pages taken in pool order (sequence b's k-th page = page b * max_pages + k)
+    t = np.arange(length)
+    return pages[(b * np.asarray(block_table).shape[1] + t // page_size) % pages.shape[0], t % page_size]
+
+
+def _gather_slot_from_page_end(pages, block_table, length, b, page_size):
+    t = np.arange(length)
+    return pages[np.asarray(block_table)[b, t // page_size], page_size - 1 - t % page_size]
+
+
 def _as_copy(x, dtype):
     return np.array(x, dtype)
 
@@ -497,6 +561,8 @@ MUTATIONS = {
     "expand_split_swapped": ("expand_kv", _expand_swapped),
     "ragged_uses_the_bound": ("absorb_attention_ragged", _ragged_uses_bound),
     "append_one_position_late": ("cache_append", _append_one_late),
+    "paged_ignores_the_table": ("paged_gather", _gather_ignores_table),
+    "paged_slot_reversed": ("paged_gather", _gather_slot_from_page_end),
 }
 
 

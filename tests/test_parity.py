@@ -302,6 +302,137 @@ def test_full_size_ragged(gpu_lib, name):
     check(np.stack([g[b, s, h] for b, s, h in rows]), ref, TOL["bf16"], f"{name} sampled rows")
 
 
+# --------------------------------------------------------------------------------- paged caches
+
+def to_pages(cache, lens, page_size, extra_pages, seed, table=None):
+    """Scatter each sequence's rows [0, len) into distinct random pages of a NaN-filled pool (rows
+    no sequence owns stay NaN, so any read of them would show in the output), or into the pages
+    a given table names.  Returns the pool [num_pages, page_size, D] and block_table
+    [B, max_pages] (random entries past a sequence's pages)."""
+    rng = np.random.default_rng(seed)
+    B, _, D = cache.shape
+    need = [-(-int(n) // page_size) for n in lens]
+    num_pages = sum(need) + extra_pages
+    if table is None:
+        ids = rng.permutation(num_pages)
+        table = rng.integers(0, num_pages, (B, max(need) + 2)).astype(np.int32)
+        used = 0
+        for b in range(B):
+            for k in range(need[b]):
+                table[b, k] = ids[used]
+                used += 1
+    pool = np.full((num_pages, page_size, D), np.nan, np.float32)
+    for b in range(B):
+        for k in range(need[b]):
+            n = min(page_size, int(lens[b]) - k * page_size)
+            pool[table[b, k], :n] = cache[b, k * page_size:k * page_size + n]
+    return pool, table
+
+
+def run_attn_paged(lib, cfg, t, kvp, pep, table, bound, lens=None, path="auto", splits=0):
+    out = torch.full((cfg.batch, cfg.seqlen_q, cfg.n_heads, cfg.v_head_dim), float("nan"), dtype=tdtype(cfg),
+                     device="cuda")
+    seq = None if lens is None else torch.tensor([int(n) for n in lens], dtype=torch.int32, device="cuda")
+    lib.absorb_attn(t["q_nope"], t["q_pe"], kvp, pep, t["wkv_b"], bound, cfg.softmax_scale, out, num_splits=splits,
+                    path=path, seq_lens=seq, block_table=table)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("path,page_size", [("mfma", 32), ("mfma", 64), ("mfma", 256), ("plain", 16),
+                                            ("plain", 48), ("auto", 64)])
+@pytest.mark.parametrize("seqlen_q", [1, 3])
+def test_paged_small(gpu_lib, path, page_size, seqlen_q):
+    cfg = dsv3_small(batch=3, cache_batch=3, seqlen_q=seqlen_q, end_pos=300, cache_len=320)
+    if path == "plain":
+        cfg = cfg.replace(n_heads=16)
+    x = make_attn_inputs(cfg)
+    lens = [300, 37, 161]
+    kvp, table = to_pages(x["kv_cache"], lens, page_size, 3, 81 + page_size)
+    pep, _ = to_pages(x["pe_cache"], lens, page_size, 3, 81 + page_size)  # same seed: same table
+    t = to_dev(x, cfg)
+    dev = lambda a: torch.from_numpy(a).to("cuda").to(torch.bfloat16)
+    out = run_attn_paged(gpu_lib, cfg, t, dev(kvp), dev(pep), torch.from_numpy(table).to("cuda"), cfg.end_pos,
+                         lens=lens, path=path)
+    ref = O.absorb_attention_paged(x["q_nope"], x["q_pe"], kvp, pep, x["wkv_b"], table, lens, page_size,
+                                   cfg.softmax_scale, cfg.v_head_dim)
+    check(out, ref, TOL["bf16"], f"paged {path} page_size={page_size} S={seqlen_q}")
+
+
+@pytest.mark.parametrize("splits", [1, 3, 7, 40])
+def test_paged_forced_splits(gpu_lib, splits):
+    """Split starts rounded to 32 positions; splits that end up empty; a page of 32 per tile."""
+    cfg = dsv3_small(batch=2, cache_batch=2, seqlen_q=2, end_pos=290, cache_len=320)
+    x = make_attn_inputs(cfg)
+    lens = [290, 75]
+    kvp, table = to_pages(x["kv_cache"], lens, 32, 2, 91)
+    pep, _ = to_pages(x["pe_cache"], lens, 32, 2, 91)
+    t = to_dev(x, cfg)
+    dev = lambda a: torch.from_numpy(a).to("cuda").to(torch.bfloat16)
+    out = run_attn_paged(gpu_lib, cfg, t, dev(kvp), dev(pep), torch.from_numpy(table).to("cuda"), cfg.end_pos,
+                         lens=lens, path="mfma", splits=splits)
+    ref = O.absorb_attention_paged(x["q_nope"], x["q_pe"], kvp, pep, x["wkv_b"], table, lens, 32,
+                                   cfg.softmax_scale, cfg.v_head_dim)
+    check(out, ref, TOL["bf16"], f"paged forced splits={splits}")
+
+
+def test_paged_uniform_and_clamped_ids(gpu_lib):
+    """No seq_lens: every sequence has max_seq_len positions.  Page ids outside the pool are
+    clamped into it (here -5 -> 0 and num_pages + 3 -> num_pages - 1), on both kernel paths."""
+    cfg = dsv3_small(batch=2, cache_batch=2, end_pos=256, cache_len=256)
+    x = make_attn_inputs(cfg)
+    table = np.array([[0, 5, 2, 7], [3, 6, 1, 4]], np.int32)  # 8 pages of 64, ids 0 and 7 in use
+    kvp, _ = to_pages(x["kv_cache"], [256, 256], 64, 0, 0, table)
+    pep, _ = to_pages(x["pe_cache"], [256, 256], 64, 0, 0, table)
+    bad = table.copy()
+    bad[table == 0] = -5
+    bad[table == 7] = 11
+    t = to_dev(x, cfg)
+    dev = lambda a: torch.from_numpy(a).to("cuda").to(torch.bfloat16)
+    ref = O.absorb_attention(x["q_nope"], x["q_pe"], x["kv_cache"], x["pe_cache"], x["wkv_b"], cfg.end_pos,
+                             cfg.softmax_scale, cfg.v_head_dim)
+    for path in ("mfma", "plain"):
+        out = run_attn_paged(gpu_lib, cfg, t, dev(kvp), dev(pep), torch.from_numpy(bad).to("cuda"), cfg.end_pos,
+                             path=path)
+        check(out, ref, TOL["bf16"], f"paged uniform, clamped ids, {path}")
+
+
+@pytest.mark.parametrize("name,page_size", [("dsv3_decode", 64), ("chunk_prefill", 64), ("long_decode", 256),
+                                            ("ragged_decode", 64)])
+def test_full_size_paged_matches_contiguous(gpu_lib, name, page_size):
+    """The paged kernels read the same rows in the same order as the contiguous ones: outputs are
+    bitwise equal at full size (pages in random order in a NaN-filled pool)."""
+    lens = None
+    if name in RAGGED_CONFIGS:
+        base, lo, hi, lseed = RAGGED_CONFIGS[name]
+        cfg = ATTN_CONFIGS[base]
+        lens = ragged_lengths(cfg.batch, lo, hi, lseed)
+    else:
+        cfg = ATTN_CONFIGS[name]
+    print(f"full-size paged {name}: B={cfg.batch} S={cfg.seqlen_q} T={cfg.end_pos} page={page_size}", flush=True)
+    x = make_attn_inputs(cfg)
+    t = to_dev(x, cfg)
+    B, T = cfg.batch, cfg.end_pos
+    npp = T // page_size
+    g = torch.Generator(device="cpu")
+    g.manual_seed(97)
+    num_pages = B * npp + 16
+    perm = torch.randperm(num_pages, generator=g)[:B * npp].to(torch.int32)
+    table = perm.view(B, npp).contiguous().to("cuda")
+    kvp = torch.full((num_pages, page_size, cfg.kv_lora_rank), float("nan"), dtype=torch.bfloat16, device="cuda")
+    pep = torch.full((num_pages, page_size, cfg.qk_rope_head_dim), float("nan"), dtype=torch.bfloat16, device="cuda")
+    kvp[table.long()] = t["kv_cache"][:B].reshape(B, npp, page_size, -1)
+    pep[table.long()] = t["pe_cache"][:B].reshape(B, npp, page_size, -1)
+    seq = None if lens is None else torch.tensor(lens, dtype=torch.int32, device="cuda")
+    if lens is None:
+        ref = run_attn(gpu_lib, cfg, t)
+    else:
+        ref = run_attn_ragged(gpu_lib, cfg, t, lens)
+    out = run_attn_paged(gpu_lib, cfg, t, kvp, pep, table, cfg.end_pos, lens=lens)
+    assert torch.isfinite(out).all(), "non-finite outputs"
+    assert torch.equal(out, ref), f"paged differs from contiguous: max {float((out.float() - ref.float()).abs().max())}"
+
+
 # --------------------------------------------------------------------------------- cache append
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
