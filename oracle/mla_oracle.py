@@ -39,6 +39,12 @@ Readings adopted where the pages are silent (each is listed in the design doc):
     KV-cache pages) is storage only: position t of sequence b is row
     t % page_size of page block_table[b, t // page_size]; the attention is that
     of the ragged batch over the rows the pages spell out.
+  * Sparse attention over a selected set of positions (the same explainer's
+    fine-grained sparse attention over the spans a pre-selector keeps): query
+    token (b, s) attends to the cache positions its index list names, shared by
+    all heads; an entry counts only if 0 <= idx <= the token's own position, each
+    counting entry is one term of the softmax (a repeated entry counts twice), and
+    a token with no counting entry gets output 0.
 """
 from __future__ import annotations
 
@@ -60,6 +66,7 @@ __all__ = [
     "absorb_attention_ragged",
     "paged_gather",
     "absorb_attention_paged",
+    "absorb_attention_sparse",
     "rms_norm",
     "expand_kv",
     "cache_append",
@@ -319,6 +326,43 @@ def absorb_attention_paged(q_nope, q_pe, kv_pages, pe_pages, wkv_b, block_table,
         kv[b, :lens[b]] = paged_gather(_as(kv_pages, dtype), block_table, lens[b], b, page_size)
         pe[b, :lens[b]] = paged_gather(_as(pe_pages, dtype), block_table, lens[b], b, page_size)
     return absorb_attention_ragged(q_nope, q_pe, kv, pe, wkv_b, lens, softmax_scale, v_head_dim, dtype, rows)
+
+
+def absorb_attention_sparse(q_nope, q_pe, kv_cache, pe_cache, wkv_b, indices, seq_lens, softmax_scale: float,
+                            v_head_dim: int, dtype=np.float64, rows: Iterable[Tuple[int, int, int]] = None):
+    """Absorb-route attention over selected positions: indices [B, S, K] (int), seq_lens [B].
+
+    Token s of sequence b sits at position seq_lens[b] - S + s; its entries idx with
+    0 <= idx <= that position are the positions it attends to (in list order, repeats kept).
+    Per head: q_lat = q_nope . W_UK[h]; scores over the entries (q_lat . kv[b, idx] +
+    q_pe . pe[b, idx]) * scale; softmax; o_lat = sum p kv[b, idx]; out = W_UV[h] . o_lat.
+    With no counting entry the output is 0.  With `rows`, [len(rows), Dv] for those (b, s, h).
+    """
+    q_nope, q_pe = _as(q_nope, dtype), _as(q_pe, dtype)
+    B, S, H, Dn = q_nope.shape
+    w_uk, w_uv = split_wkv_b(_as(wkv_b, dtype), H, Dn, v_head_dim)
+    idx_all = np.asarray(indices)
+    want = sorted({(b, s) for b, s, _ in rows}) if rows is not None else [(b, s) for b in range(B) for s in range(S)]
+    res = {}
+    for b, s in want:
+        last = int(seq_lens[b]) - S + s
+        idx = idx_all[b, s]
+        sel = idx[(idx >= 0) & (idx <= last)]
+        if sel.size == 0:
+            res[(b, s)] = np.zeros((H, v_head_dim), dtype)
+            continue
+        kv = _as(kv_cache, dtype)[b, sel]  # [K', C]
+        pe = _as(pe_cache, dtype)[b, sel]  # [K', R]
+        q_lat = np.einsum("hd,hdc->hc", q_nope[b, s], w_uk)
+        scores = (q_lat @ kv.T + q_pe[b, s] @ pe.T) * softmax_scale  # [H, K']
+        p = masked_softmax(scores, np.ones(scores.shape, bool))
+        res[(b, s)] = np.einsum("hc,hdc->hd", p @ kv, w_uv)
+    if rows is not None:
+        return np.stack([res[(b, s)][h] for b, s, h in rows])
+    out = np.zeros((B, S, H, v_head_dim), dtype)
+    for (b, s), v in res.items():
+        out[b, s] = v
+    return out
 
 
 def rms_norm(x, w, eps: float, dtype=np.float64):

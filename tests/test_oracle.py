@@ -400,6 +400,54 @@ def pin_paged():
     return worst
 
 
+def pin_sparse():
+    """Sparse attention over index lists: (1) a list naming every cache position, in random order
+    and with positions past the token's own mixed in, equals dense causal absorb attention; (2) a
+    subset with repeats equals the naive route over a cache holding exactly the listed rows (a
+    different code path); (3) entries that name no visible position (-1, the token's position + 1,
+    the sequence length, beyond the cache) change nothing; (4) a list with no visible entry gives
+    output 0."""
+    worst = 0.0
+    rng = np.random.default_rng(81)
+    for seqlen_q in (1, 3):
+        cfg = small_cfg(batch=2, cache_batch=2, seqlen_q=seqlen_q, end_pos=9, cache_len=11, seed=82 + seqlen_q)
+        x = make_attn_inputs(cfg)
+        B, S, T = cfg.batch, seqlen_q, cfg.end_pos
+        lens = [T] * B
+        args = (x["q_nope"], x["q_pe"], x["kv_cache"], x["pe_cache"], x["wkv_b"])
+        full = np.stack([np.stack([rng.permutation(cfg.cache_len) for _ in range(S)]) for _ in range(B)])
+        got = O.absorb_attention_sparse(*args, full, lens, cfg.softmax_scale, cfg.v_head_dim)
+        worst = max(worst, rel_err(got, run("absorb", cfg, x)))
+        # subset with repeats vs naive route over the listed rows
+        K = 6
+        sub = rng.integers(0, T - S + 1, (B, S, K))
+        sub[:, :, 1] = sub[:, :, 0]  # a repeated entry
+        got = O.absorb_attention_sparse(*args, sub, lens, cfg.softmax_scale, cfg.v_head_dim)
+        for b in range(B):
+            for s_ in range(S):
+                kv = np.asarray(x["kv_cache"])[b, sub[b, s_]][None]
+                pe = np.asarray(x["pe_cache"])[b, sub[b, s_]][None]
+                nv = O.naive_attention(x["q_nope"][b:b + 1, s_:s_ + 1], x["q_pe"][b:b + 1, s_:s_ + 1], kv, pe,
+                                       x["wkv_b"], K, cfg.softmax_scale, cfg.v_head_dim)
+                worst = max(worst, rel_err(got[b, s_], nv[0, 0]))
+        # entries that name no visible position
+        extra = np.zeros((B, S, 4), np.int64)
+        for s_ in range(S):
+            extra[:, s_] = [-1, T - S + s_ + 1, T, cfg.cache_len + 7]
+        padded = np.concatenate([extra[:, :, :2], sub, extra[:, :, 2:]], axis=2)
+        if S == 1:
+            padded[:, :, 1] = -3  # for a decode token the next position is the length itself
+        got2 = O.absorb_attention_sparse(*args, padded, lens, cfg.softmax_scale, cfg.v_head_dim)
+        worst = max(worst, rel_err(got2, got))
+        # nothing visible
+        none = O.absorb_attention_sparse(*args, extra, lens, cfg.softmax_scale, cfg.v_head_dim)
+        worst = max(worst, float(np.abs(none).max()))
+        rows = [(0, S - 1, 0), (1, 0, 2)]
+        sel = O.absorb_attention_sparse(*args, sub, lens, cfg.softmax_scale, cfg.v_head_dim, rows=rows)
+        worst = max(worst, rel_err(sel, np.stack([got[b, s_, h] for b, s_, h in rows])))
+    return worst
+
+
 PINS = {
     "naive_equals_absorb": (pin_naive_equals_absorb, 1e-12),
     "golden": (pin_golden, 1e-12),
@@ -418,6 +466,7 @@ PINS = {
     "append": (pin_append, 1e-12),
     "attention_over_kv": (pin_attention_over_kv, 1e-12),
     "paged": (pin_paged, 1e-12),
+    "sparse": (pin_sparse, 1e-12),
 }
 
 
@@ -546,6 +595,29 @@ def _gather_slot_from_page_end(pages, block_table, length, b, page_size):
     return pages[np.asarray(block_table)[b, t // page_size], page_size - 1 - t % page_size]
 
 
+_orig_sparse = O.absorb_attention_sparse
+
+
+def _sparse_ignores_causal_bound(q_nope, q_pe, kv_cache, pe_cache, wkv_b, indices, seq_lens, *a, **kw):
+    # every token sees up to the chunk's last position (lengths moved up by S - 1)
+    S = np.asarray(q_nope).shape[1]
+    return _orig_sparse(q_nope, q_pe, kv_cache, pe_cache, wkv_b, indices, [int(n) + S - 1 for n in seq_lens],
+                        *a, **kw)
+
+
+def _sparse_drops_repeats(q_nope, q_pe, kv_cache, pe_cache, wkv_b, indices, seq_lens, *a, **kw):
+    idx = np.array(indices)
+    for b in range(idx.shape[0]):
+        for s_ in range(idx.shape[1]):
+            row = idx[b, s_]
+            seen = set()
+            for k in range(row.shape[0]):
+                if int(row[k]) in seen:
+                    row[k] = -1
+                seen.add(int(row[k]))
+    return _orig_sparse(q_nope, q_pe, kv_cache, pe_cache, wkv_b, idx, seq_lens, *a, **kw)
+
+
 def _as_copy(x, dtype):
     return np.array(x, dtype)
 
@@ -563,6 +635,8 @@ MUTATIONS = {
     "append_one_position_late": ("cache_append", _append_one_late),
     "paged_ignores_the_table": ("paged_gather", _gather_ignores_table),
     "paged_slot_reversed": ("paged_gather", _gather_slot_from_page_end),
+    "sparse_ignores_causal_bound": ("absorb_attention_sparse", _sparse_ignores_causal_bound),
+    "sparse_drops_repeats": ("absorb_attention_sparse", _sparse_drops_repeats),
 }
 
 
