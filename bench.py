@@ -21,7 +21,9 @@ those events add a queue barrier per timed dispatch, so that pass's step time is
 `cpu_baseline` times the CPU oracle (NumPy, float64) on a bounded sample of the same workload.
 `extras` times the other workloads the same way: long_decode, chunk_prefill, ragged_decode (the
 decode batch with per-sequence lengths drawn uniformly from [256, 4096]), paged_decode (the decode
-batch with its caches in pools of 64-position pages in random order), chunk_prefill_naive (the
+batch with its caches in pools of 64-position pages in random order), sparse_decode and
+sparse_long_decode (the decode and long-context batches with each token attending to 2048 random
+positions of its cache through an index list), chunk_prefill_naive (the
 same chunk through the naive route: expansion of the 2 x 4096 cached latents, then attention over
 the expanded keys and values) and dsv3_expand.
 """
@@ -42,6 +44,18 @@ HBM_PEAK_GBS = 8000.0
 SPIN_CYCLES = 20_000_000  # GPU clock cycles of spin ahead of a timed region (about 10 ms)
 BF16_PEAK_TFLOPS = 2516.6
 METRIC = "MLA absorb decode µs/step, HBM GB/s & MFMA TFLOP/s as % of roofline"
+
+
+def sparse_work(cfg, topk):
+    """Algorithmic bytes and FLOPs of attention over index lists of topk distinct visible positions
+    per query token: the listed cache rows, the lists, wkv_b, q and out."""
+    B, S, H = cfg.batch, cfg.seqlen_q, cfg.n_heads
+    C, R, Dn, Dv = cfg.kv_lora_rank, cfg.qk_rope_head_dim, cfg.qk_nope_head_dim, cfg.v_head_dim
+    e = 2
+    rows = B * S * topk
+    flops = 2 * B * S * H * Dn * C + 2 * H * rows * (C + R) + 2 * H * rows * C + 2 * B * S * H * C * Dv
+    return {"bytes": rows * (C + R) * e + rows * 4 + H * (Dn + Dv) * C * e + B * S * H * (Dn + R + Dv) * e,
+            "flops": flops, "attn_kernel_bytes": rows * (C + R) * e + rows * 4 + B * S * H * R * e}
 
 
 def attn_work(cfg, lens=None):
@@ -100,25 +114,39 @@ def to_paged(x, cfg, page_size, seed, torch):
     return table
 
 
-def time_attn(cfg, steps, warmup, sets, torch, binding, seed=1, timed_kernels=0b010, lens=None, page_size=0):
+def random_lists(cfg, topk, seed, torch):
+    """topk distinct positions per query token, drawn uniformly from the visible ones (decode)."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    rows = [torch.randperm(cfg.end_pos, generator=g)[:topk] for _ in range(cfg.batch * cfg.seqlen_q)]
+    return torch.stack(rows).to(torch.int32).view(cfg.batch, cfg.seqlen_q, topk).contiguous().to("cuda")
+
+
+def time_attn(cfg, steps, warmup, sets, torch, binding, seed=1, timed_kernels=0b010, lens=None, page_size=0,
+              topk=0):
     """Returns (GPU us per step, host enqueue us per step, per-kernel timing dict).  With lens, a
     ragged batch (mla_absorb_attn_ragged with the lengths in device memory, bound cfg.end_pos);
-    with page_size, the caches live in page pools in random page order (mla_absorb_attn_paged)."""
+    with page_size, the caches live in page pools in random page order (mla_absorb_attn_paged);
+    with topk, each token attends to topk random positions (mla_absorb_attn_sparse)."""
     inputs = [gpu_inputs(cfg, seed + 1000 * i, torch) for i in range(sets)]
     seq_lens = None if lens is None else torch.tensor([int(n) for n in lens], dtype=torch.int32, device="cuda")
     out = torch.empty((cfg.batch, cfg.seqlen_q, cfg.n_heads, cfg.v_head_dim), dtype=torch.bfloat16, device="cuda")
     shape = binding.attn_shape(inputs[0]["q_nope"], inputs[0]["q_pe"], inputs[0]["kv_cache"], inputs[0]["wkv_b"])
+    lists = [random_lists(cfg, topk, seed + i, torch) if topk else None for i in range(sets)]
     if page_size:
         paged = binding.PagedCache(page_size, cfg.cache_batch * cfg.cache_len // page_size,
                                    cfg.cache_len // page_size)
         need = binding.absorb_attn_paged_workspace_size(shape, cfg.end_pos, paged, binding.MLA_DTYPE_BF16)
+    elif topk:
+        need = binding.absorb_attn_sparse_workspace_size(shape, cfg.end_pos, topk, binding.MLA_DTYPE_BF16)
     else:
         need = binding.absorb_attn_workspace_size(shape, cfg.end_pos, binding.MLA_DTYPE_BF16)
     ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
     tables = [to_paged(x, cfg, page_size, seed + i, torch) if page_size else None for i, x in enumerate(inputs)]
     calls = [binding.AbsorbAttnCall(x["q_nope"], x["q_pe"], x["kv_cache"], x["pe_cache"], x["wkv_b"], cfg.end_pos,
-                                    cfg.softmax_scale, out, workspace=ws, seq_lens=seq_lens, block_table=tb)
-             for x, tb in zip(inputs, tables)]
+                                    cfg.softmax_scale, out, workspace=ws, seq_lens=seq_lens, block_table=tb,
+                                    indices=il)
+             for x, tb, il in zip(inputs, tables, lists)]
 
     def step(i):
         calls[i % sets]()
@@ -142,7 +170,7 @@ def time_attn(cfg, steps, warmup, sets, torch, binding, seed=1, timed_kernels=0b
     torch.cuda.synchronize()
     kt = binding.timing_collect()
     binding.timing_enable(0)
-    del inputs, calls, tables
+    del inputs, calls, tables, lists
     torch.cuda.empty_cache()
     return e0.elapsed_time(e1) * 1000.0 / steps, enqueue, kt
 
@@ -397,6 +425,14 @@ def main():
         _, _, k = time_attn(c, 30, 3, args.sets, torch, binding, seed=c.seed, timed_kernels=0b111, page_size=64)
         extras["paged_decode"] = {"us_per_step": round(u, 2), "gbps": round(w["bytes"] / (u * 1e-6) / 1e9, 1),
                                   "page_size": 64, "kernels_us": {n: round(v["avg_us"], 2) for n, v in k.items()}}
+        for name, base in (("sparse_decode", "dsv3_decode"), ("sparse_long_decode", "long_decode")):
+            c = ATTN_CONFIGS[base]
+            w = sparse_work(c, 2048)
+            u, _, _ = time_attn(c, 30, 3, args.sets, torch, binding, seed=c.seed, timed_kernels=0, topk=2048)
+            _, _, k = time_attn(c, 30, 3, args.sets, torch, binding, seed=c.seed, timed_kernels=0b111, topk=2048)
+            extras[name] = {"us_per_step": round(u, 2), "gbps": round(w["bytes"] / (u * 1e-6) / 1e9, 1),
+                            "topk": 2048, "kernels_us": {n: round(v["avg_us"], 2) for n, v in k.items()},
+                            "attn_gbps": round(w["attn_kernel_bytes"] / (k["attn"]["avg_us"] * 1e-6) / 1e9, 1)}
         c = ATTN_CONFIGS["chunk_prefill"]
         u, k = time_naive_route(c, 10, 3, torch, binding, seed=c.seed)
         w = naive_work(c)

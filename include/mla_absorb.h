@@ -195,6 +195,41 @@ int32_t mla_absorb_attn_paged(const void *q_nope, const void *q_pe, const void *
                               size_t workspace_bytes, void *stream);
 
 /*
+ * Absorb-form MLA attention over selected positions.  The DeepSeek Sparse Attention explainer
+ * (sider.ai, sections on how DSA differs from dense attention and on fine-grained sparse
+ * attention) describes a cheap pre-selector (the "lightning indexer") that keeps a short list of
+ * positions per query token, after which exact attention runs over that list only.  The
+ * selection itself needs trained weights and is the caller's; this call is the attention over it:
+ *
+ *   indices  DEVICE int32 [B, S, topk], 4-byte aligned: the positions query token (b, s) attends
+ *            to, shared by all of its heads.  An entry counts if 0 <= idx <= p with p =
+ *            len_b - S + s the token's own position (so a list naming every position gives
+ *            mla_absorb_attn's causal result); any other value (e.g. -1 as padding) is ignored and
+ *            never read.  Each counting entry is one term of the softmax (a repeated position
+ *            counts twice).  A token with no counting entry gets out = 0.
+ *   topk     entries per list, 1 <= topk <= 2^24.
+ *   seq_lens DEVICE int32 [B] or NULL: len_b as in mla_absorb_attn_ragged (clamped to
+ *            [S, end_pos]); NULL gives every sequence the length end_pos.
+ *   end_pos  uniform length, or the bound of seq_lens; 1 <= S <= end_pos <= Tmax.
+ *
+ * Caches, weights, shapes, options and errors as in mla_absorb_attn (contiguous caches); the
+ * matrix-core kernels need each 128-row block of query rows to be the heads of one token
+ * (n_heads a multiple of 128, or seqlen_q 1 with n_heads <= 128), other shapes run on the plain
+ * kernels.  workspace: mla_absorb_attn_sparse_workspace_size(...) bytes (splits cut the list
+ * entries).  out, the workspace, indices and seq_lens must not overlap.
+ */
+size_t mla_absorb_attn_sparse_workspace_size(const mla_attn_shape *shape, int64_t end_pos,
+                                             int64_t topk, int32_t dtype,
+                                             const mla_attn_options *options);
+
+int32_t mla_absorb_attn_sparse(const void *q_nope, const void *q_pe, const void *kv_cache,
+                               const void *pe_cache, const void *wkv_b, const int32_t *indices,
+                               int64_t topk, const int32_t *seq_lens, int64_t end_pos,
+                               float softmax_scale, void *out, const mla_attn_shape *shape,
+                               int32_t dtype, const mla_attn_options *options, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+/*
  * Cache append, the step before attending: writes the S new tokens of each sequence into the
  * two caches mla_absorb_attn reads ("Naive vs Absorb Attention Implementations in DeepSeek-V3",
  * section "Memory Layout and Cache Structure": kv_cache holds each position's compressed latent,

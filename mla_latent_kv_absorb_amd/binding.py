@@ -29,8 +29,9 @@ MLA_DTYPE_BF16 = 1
 
 PATHS = {"auto": 0, "plain": 1, "mfma": 2}
 
-EXPORTED = ("mla_absorb_attn", "mla_absorb_attn_ragged", "mla_absorb_attn_paged", "mla_absorb_attn_workspace_size",
-            "mla_absorb_attn_paged_workspace_size", "mla_cache_append",
+EXPORTED = ("mla_absorb_attn", "mla_absorb_attn_ragged", "mla_absorb_attn_paged", "mla_absorb_attn_sparse",
+            "mla_absorb_attn_workspace_size", "mla_absorb_attn_paged_workspace_size",
+            "mla_absorb_attn_sparse_workspace_size", "mla_cache_append",
             "mla_expand_kv", "mla_expand_kv_workspace_size", "mla_naive_attn",
             "mla_strerror",
             "mla_last_error", "mla_timing_enable", "mla_timing_collect", "mla_kernel_name")
@@ -83,6 +84,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_absorb_attn_paged_workspace_size.argtypes = [ctypes.POINTER(AttnShape), i64, ctypes.POINTER(PagedCache),
                                                          i32, ctypes.POINTER(AttnOptions)]
     lib.mla_absorb_attn_paged_workspace_size.restype = sz
+    lib.mla_absorb_attn_sparse.argtypes = [vp, vp, vp, vp, vp, vp, i64, vp, i64, ctypes.c_float, vp,
+                                           ctypes.POINTER(AttnShape), i32, ctypes.POINTER(AttnOptions), vp, sz, vp]
+    lib.mla_absorb_attn_sparse.restype = i32
+    lib.mla_absorb_attn_sparse_workspace_size.argtypes = [ctypes.POINTER(AttnShape), i64, i64, i32,
+                                                          ctypes.POINTER(AttnOptions)]
+    lib.mla_absorb_attn_sparse_workspace_size.restype = sz
     lib.mla_cache_append.argtypes = [vp, vp, vp, ctypes.c_float, vp, i64, vp, vp, ctypes.POINTER(AttnShape), i32, vp]
     lib.mla_cache_append.restype = i32
     lib.mla_naive_attn.argtypes = [vp, vp, vp, vp, vp, i64, ctypes.c_float, vp, ctypes.POINTER(AttnShape), i32, i32, vp]
@@ -197,6 +204,16 @@ def absorb_attn_paged_workspace_size(shape: AttnShape, max_seq_len: int, paged: 
     return int(n)
 
 
+def absorb_attn_sparse_workspace_size(shape: AttnShape, end_pos: int, topk: int, dtype: int, num_splits: int = 0,
+                                      path: str = "auto") -> int:
+    lib = load()
+    opt = AttnOptions(num_splits, PATHS[path])
+    n = lib.mla_absorb_attn_sparse_workspace_size(ctypes.byref(shape), end_pos, topk, dtype, ctypes.byref(opt))
+    if n == 0 and last_error():
+        raise MLAError(MLA_ERR_SHAPE, last_error())
+    return int(n)
+
+
 class AbsorbAttnCall:
     """One absorb-attention call with its arguments marshalled once.
 
@@ -207,18 +224,21 @@ class AbsorbAttnCall:
     """
 
     def __init__(self, q_nope, q_pe, kv_cache, pe_cache, wkv_b, end_pos: int, softmax_scale: float, out=None, *,
-                 num_splits: int = 0, path: str = "auto", workspace=None, seq_lens=None, block_table=None):
+                 num_splits: int = 0, path: str = "auto", workspace=None, seq_lens=None, block_table=None,
+                 indices=None):
         """With seq_lens (an int32 tensor [B] on the same device), sequence b attends to positions
         [0, seq_lens[b]) and end_pos is the bound of the lengths (mla_absorb_attn_ragged).  With
         block_table (int32 [B, max_pages_per_seq]), kv_cache and pe_cache are page pools
-        [num_pages, page_size, C / R] (mla_absorb_attn_paged; seq_lens optional)."""
+        [num_pages, page_size, C / R] (mla_absorb_attn_paged; seq_lens optional).  With indices
+        (int32 [B, S, topk]), each query token attends to the positions its list names
+        (mla_absorb_attn_sparse; seq_lens optional)."""
         import torch
 
         lib = load()
         _require_device(q_nope, q_pe, kv_cache, pe_cache, wkv_b)
         shape = attn_shape(q_nope, q_pe, kv_cache, wkv_b)
         dt = _dtype_code(q_nope)
-        for name, t in (("seq_lens", seq_lens), ("block_table", block_table)):
+        for name, t in (("seq_lens", seq_lens), ("block_table", block_table), ("indices", indices)):
             if t is not None and (t.device != q_nope.device or t.dtype != torch.int32 or not t.is_contiguous()):
                 raise ValueError(f"{name} must be a contiguous int32 tensor on the tensors' device")
         if seq_lens is not None and seq_lens.numel() != shape.batch:
@@ -237,7 +257,13 @@ class AbsorbAttnCall:
                               device=q_nope.device)
         _require_device(q_nope, out)
         opt = AttnOptions(num_splits, PATHS[path])
-        if paged is None:
+        if indices is not None:
+            if block_table is not None:
+                raise ValueError("index lists over paged caches are not supported")
+            if indices.dim() != 3 or tuple(indices.shape[:2]) != (shape.batch, shape.seqlen_q):
+                raise ValueError("indices must be [batch, seqlen_q, topk]")
+            need = absorb_attn_sparse_workspace_size(shape, end_pos, indices.shape[2], dt, num_splits, path)
+        elif paged is None:
             need = absorb_attn_workspace_size(shape, end_pos, dt, num_splits, path)
         else:
             need = absorb_attn_paged_workspace_size(shape, end_pos, paged, dt, num_splits, path)
@@ -245,12 +271,15 @@ class AbsorbAttnCall:
             workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q_nope.device)
         self.out = out
         self._keep = (q_nope, q_pe, kv_cache, pe_cache, wkv_b, out, workspace, shape, opt, seq_lens, block_table,
-                      paged)
+                      paged, indices)
         tail = (softmax_scale, out.data_ptr(), ctypes.byref(shape), dt, ctypes.byref(opt), workspace.data_ptr(),
                 workspace.numel() * workspace.element_size(), _stream_handle(q_nope.device))
         head = (q_nope.data_ptr(), q_pe.data_ptr(), kv_cache.data_ptr(), pe_cache.data_ptr(), wkv_b.data_ptr())
         lens_ptr = None if seq_lens is None else seq_lens.data_ptr()
-        if paged is not None:
+        if indices is not None:
+            self._fn = lib.mla_absorb_attn_sparse
+            self._args = head + (indices.data_ptr(), indices.shape[2], lens_ptr, end_pos) + tail
+        elif paged is not None:
             self._fn = lib.mla_absorb_attn_paged
             self._args = head + (block_table.data_ptr(), lens_ptr, end_pos, softmax_scale, out.data_ptr(),
                                  ctypes.byref(shape), ctypes.byref(paged), dt, ctypes.byref(opt),
@@ -269,13 +298,15 @@ class AbsorbAttnCall:
 
 
 def absorb_attn(q_nope, q_pe, kv_cache, pe_cache, wkv_b, end_pos: int, softmax_scale: float, out=None, *,
-                num_splits: int = 0, path: str = "auto", workspace=None, seq_lens=None, block_table=None):
+                num_splits: int = 0, path: str = "auto", workspace=None, seq_lens=None, block_table=None,
+                indices=None):
     """MLA attention in absorb form on torch GPU tensors; returns out [B, S, H, Dv].  With
     seq_lens, a ragged batch whose lengths are bounded by end_pos; with block_table, paged caches
-    (kv_cache / pe_cache are the page pools)."""
+    (kv_cache / pe_cache are the page pools); with indices [B, S, topk], attention over the
+    positions each token's list names."""
     return AbsorbAttnCall(q_nope, q_pe, kv_cache, pe_cache, wkv_b, end_pos, softmax_scale, out,
                           num_splits=num_splits, path=path, workspace=workspace, seq_lens=seq_lens,
-                          block_table=block_table)()
+                          block_table=block_table, indices=indices)()
 
 
 def cache_append(c_kv_new, k_pe_new, rms_w, eps: float, end_pos: int, kv_cache, pe_cache, *, seq_lens=None):

@@ -80,10 +80,18 @@ struct AttnArgs {
   // paged caches: kv / pe are pools of 2^log2_page positions per page, block_table [B, max_pages]
   const int32_t *block_table;
   int32_t log2_page, max_pages, num_pages;
+  // index lists [B, S, topk]: token (b, s) attends to the positions its list names
+  const int32_t *indices;
+  int32_t topk;
 };
 
-// A paged workgroup keeps the page ids of its positions in kPageRegs registers (one per lane and
-// register), so a split may touch at most 64 kPageRegs pages.
+// Where tile rows come from: contiguous caches [Bmax, Tmax, .]; page pools; or the rows an index
+// list names (the tiles then run over list entries instead of positions).
+enum : int { kModeContig = 0, kModePaged = 1, kModeSparse = 2 };
+
+// A paged workgroup keeps the page ids of its positions, a sparse one the entries of its index
+// list, in kPageRegs registers (one per lane and register): a split may touch at most 64 kPageRegs
+// pages or list entries.
 constexpr int kPageRegs = 4;
 
 // Softmax rows keep a reference maximum m_ref and only move it (rescaling the running sum and the
@@ -92,9 +100,10 @@ constexpr int kPageRegs = 4;
 // share the same reference.
 constexpr float kRescale = 8.f;
 
-template <bool kPaged>
+template <int kMode>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 attn_kernel(AttnArgs a) {
+  constexpr bool kPaged = kMode == kModePaged, kSparse = kMode == kModeSparse;
   __shared__ __attribute__((aligned(16))) unsigned char smem[kStages * kStageBytes + 4 * kQpeBytesPerWave];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -117,15 +126,18 @@ attn_kernel(AttnArgs a) {
   // this sequence's length: a ragged batch reads it from seq_lens, clamped to [S, end_pos] so that
   // no access leaves the positions the caller vouched for
   const int end_pos = a.seq_lens ? __builtin_amdgcn_readfirstlane(min(max(a.seq_lens[b], a.S), a.end_pos)) : a.end_pos;
-  const int t_split_end = min(t_begin + a.split_len, end_pos);
+  // sparse: the split covers list entries [t_begin, t_split_end) of one query token
+  const int t_split_end = min(t_begin + a.split_len, kSparse ? a.topk : end_pos);
   const int row_end = row_ok ? min(t_split_end, end_pos - a.S + s + 1) : t_begin;
   // Positions the workgroup needs (up to the last visible one of its last row), and the prefix
   // visible to all of its rows (tiles inside it need no mask).  Integer division runs on the
   // vector ALU, so the uniform results are re-scalarised.
   const int first_row = rb * kRowsWG;
   const int last_row = min(a.SH - 1, first_row + kRowsWG - 1);
-  const int wg_end = __builtin_amdgcn_readfirstlane(min(t_split_end, end_pos - a.S + last_row / a.H + 1));
-  const int wg_full = __builtin_amdgcn_readfirstlane(min(t_split_end, end_pos - a.S + first_row / a.H + 1));
+  const int wg_end = __builtin_amdgcn_readfirstlane(kSparse ? t_split_end
+                                                            : min(t_split_end, end_pos - a.S + last_row / a.H + 1));
+  const int wg_full = __builtin_amdgcn_readfirstlane(kSparse ? t_split_end
+                                                             : min(t_split_end, end_pos - a.S + first_row / a.H + 1));
   const int ntiles = __builtin_amdgcn_readfirstlane(wg_end > t_begin ? (wg_end - t_begin + kTile - 1) / kTile : 0);
 
   // DMA geometry.  kv: wave w moves tile rows 8w..8w+7, one 1 KB row per instruction; lane l owns
@@ -162,6 +174,30 @@ attn_kernel(AttnArgs a) {
     for (int r = 1; r < kPageRegs; ++r) p = k == r ? __builtin_amdgcn_readlane(ptab[r], ln) : p;
     return p;
   };
+  // Sparse: the workgroup's rows are the heads of one query token, at position `bound`; list entry
+  // t_begin + 64 k + lane sits in lane `lane` of ivreg[k].  Tile j's 32 entries are lanes
+  // 32 (j & 1) .. + 31 of ivreg[j >> 1].  Rows are read at the entry's position clamped into the
+  // sequence; entries naming no visible position are masked in the softmax.
+  // (four named registers rather than an array: a select among array elements by a run-time
+  // index would be lowered to an indexed scratch access)
+  static_assert(kPageRegs == 4, "sparse_reg selects among four registers");
+  int iv0 = 0, iv1 = 0, iv2 = 0, iv3 = 0;
+  int bound = 0;
+  if constexpr (kSparse) {
+    const int s_tok = __builtin_amdgcn_readfirstlane(first_row / a.H);
+    bound = end_pos - a.S + s_tok;
+    const rsrc_t ires = make_rsrc(a.indices + (int64_t(b) * a.S + s_tok) * a.topk, uint32_t(a.topk) * 4u);
+    const uint32_t off = uint32_t(t_begin + lane) * 4u;
+    iv0 = buf_load_i32(ires, off, 0);
+    iv1 = buf_load_i32(ires, off + 256u, 0);
+    iv2 = buf_load_i32(ires, off + 512u, 0);
+    iv3 = buf_load_i32(ires, off + 768u, 0);
+  }
+  auto sparse_reg = [&](int j) __attribute__((always_inline)) -> int {
+    const int k = j >> 1;
+    const int lo = (k & 1) ? iv1 : iv0, hi = (k & 1) ? iv3 : iv2;
+    return (k & 2) ? hi : lo;
+  };
   const int pe_row = wave * 8 + (lane >> 3);
   const uint32_t pe_voff = uint32_t((lane & 7) ^ pe_swz(pe_row)) * 16;
   // One of the tile's nine DMA instructions per wave: part 0..7 moves kv row 8w+part, part 8 the pe rows.
@@ -172,6 +208,7 @@ attn_kernel(AttnArgs a) {
   struct TileSrc {
     rsrc_t kv, pe;
     int tb, tlast;
+    int cur, pidx, lo;  // sparse: the entries' register, this lane's pe row, the tile's first lane
   };
   auto tile_src = [&](int j) __attribute__((always_inline)) -> TileSrc {
     if constexpr (kPaged) {
@@ -179,15 +216,25 @@ attn_kernel(AttnArgs a) {
       const int64_t page = tile_page(j, t0);
       return TileSrc{make_rsrc(a.kv + (page << (a.log2_page + 9)), uint32_t(kC * 2) << a.log2_page),
                      make_rsrc(a.pe + (page << (a.log2_page + 6)), uint32_t(kR * 2) << a.log2_page),
-                     t0 & ~((1 << a.log2_page) - 1), max(wg_end - 1, t0)};
+                     t0 & ~((1 << a.log2_page) - 1), max(wg_end - 1, t0), 0, 0, 0};
+    } else if constexpr (kSparse) {
+      const int cur = sparse_reg(j), lo = (j & 1) * 32;
+      const int pidx = __builtin_amdgcn_ds_bpermute((lo + pe_row) * 4, cur);
+      return TileSrc{kvres, peres, 0, 0, cur, min(max(pidx, 0), end_pos - 1), lo};
     } else {
-      return TileSrc{kvres, peres, 0, wg_end - 1};
+      return TileSrc{kvres, peres, 0, wg_end - 1, 0, 0, 0};
     }
   };
   auto issue_part = [&](int j, int part, const TileSrc &src) __attribute__((always_inline)) {
     const uint32_t st = smem_lds + uint32_t(j % kStages) * kStageBytes;
     const int t0 = t_begin + j * kTile;
-    if (part < 8) {
+    if (kSparse && part < 8) {
+      const int t = min(max(__builtin_amdgcn_readlane(src.cur, src.lo + wave * 8 + part), 0), end_pos - 1);
+      buf_load16_lds_at(src.kv, st + (wave * 8 + part) * (kC * 2),
+                        lane16 ^ uint32_t(kv_swz(8 * (wave & 1) + part) * 16), uint32_t(t) * (kC * 2));
+    } else if (kSparse) {
+      buf_load16_lds_at(src.pe, st + kKvTileBytes + wave * 8 * (kR * 2), pe_voff + uint32_t(src.pidx) * (kR * 2), 0);
+    } else if (part < 8) {
       const int t = min(t0 + wave * 8 + part, src.tlast);  // wavefront-uniform
       // source chunk swz_chunk(lane, row) = lane ^ kv_swz(row), kv_swz(row) wavefront-uniform
       buf_load16_lds_at(src.kv, st + (wave * 8 + part) * (kC * 2),
@@ -208,7 +255,7 @@ attn_kernel(AttnArgs a) {
   // (the query loads are the only vector loads the compiler tracks, so completing them here keeps
   // its own vmcnt waits out of the loop body); then tiles 1 and 2, always issued so that the
   // in-loop wait counts stay exact (past the last needed position they re-read its row).
-  issue(0);
+  if constexpr (!kSparse) issue(0);  // (sparse: after the query loads, behind its index loads)
   // Absorbed query as the score B operand: lane holds q[row][16 ks + 8 g .. +7], ks < 32.
   // absorb_q_kernel stores it fragment-major, so instruction ks of a wave reads one contiguous
   // 1 KB; lanes past the sequence's last row read out of range and get zeros.  The rope part
@@ -228,6 +275,7 @@ attn_kernel(AttnArgs a) {
     for (int i = 0; i < 4; ++i)
       buf_load16_lds(qres, const_cast<unsigned char *>(qpe_lds) + i * 1024, doff, (32 + i) * 1024);
   }
+  if constexpr (kSparse) issue(0);
   wait_vmcnt<0>();
   issue(1);
   issue(2);
@@ -296,6 +344,20 @@ attn_kernel(AttnArgs a) {
   // 16*(r/8) + 8*g + r%8 of the tile
   float mrow = 0.f;
   auto sm_mask = [&](f32x16 &sc, int t0) __attribute__((always_inline)) {
+    if constexpr (kSparse) {  // entries of the split naming a position in [0, bound]
+      const int j = (t0 - t_begin) >> 5;
+      const int cur = sparse_reg(j);
+      const int e = t_begin + ((j >> 1) << 6) + lane;
+      const bool ok = e < wg_end && cur >= 0 && cur <= bound;
+      const uint32_t valid = uint32_t(__builtin_amdgcn_ballot_w64(ok) >> ((j & 1) * 32));
+      if (valid != 0xffffffffu) {  // wavefront-uniform
+        const uint32_t vg = valid >> (8 * g);
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (!((vg >> (16 * (r >> 3) + (r & 7))) & 1u)) sc[r] = -INFINITY;
+      }
+      return;
+    }
     if (t0 + kTile > wg_full) {  // wavefront-uniform: positions past a row's last visible one
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -405,7 +467,9 @@ attn_kernel(AttnArgs a) {
     else wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
     compiler_fence();
-    scores(j + 1, sacc, j + 3 < ntiles, j + 3, tile_src(j + 3));
+    const TileSrc rs = tile_src(j + 3);
+    if constexpr (kSparse) asm volatile("" ::"v"(rs.pidx));  // wait for the permute here, not among the score reads
+    scores(j + 1, sacc, j + 3 < ntiles, j + 3, rs);
     const int t1 = t_begin + (j + 1) * kTile;
     sm_mask(sacc, t1);
     u32x4 pn[2];
@@ -675,8 +739,8 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineArgs a) {
 #pragma unroll
         for (int o = 8; o > 0; o >>= 1) den += __shfl_xor(den, o, 16);
         if (k == 0) {
-          mstat[r][0] = mx;  // finite: every row sees at least one position
-          mstat[r][1] = 1.f / den;
+          mstat[r][0] = mx;  // -inf only for a sparse row whose list names no visible position
+          mstat[r][1] = den > 0.f ? 1.f / den : 0.f;  // such a row's output is 0
         }
       }
     }
@@ -794,6 +858,14 @@ bool mfma_attn_supported(const AttnCall &c, const char **why) {
     *why = "needs kv_lora_rank 512, qk_rope_head_dim 64, qk_nope_head_dim 128, v_head_dim 128";
     return false;
   }
+  if (c.topk > 0) {
+    if (c.page_size > 0) { *why = "index lists over paged caches are not supported"; return false; }
+    // one index list per workgroup: its 128 rows must be heads of one query token
+    if (!((c.S == 1 && c.H <= kRowsWG) || c.H % kRowsWG == 0)) {
+      *why = "needs n_heads a multiple of 128, or seqlen_q 1 and n_heads <= 128";
+      return false;
+    }
+  }
   if (c.page_size > 0) {
     // a tile must lie in one page; page ranges are 32-bit byte counts
     if (c.page_size < kTile || (c.page_size & (c.page_size - 1)) || c.page_size > 65536) {
@@ -817,13 +889,15 @@ int32_t mfma_attn_splits(const AttnCall &c, int num_cus) {
   const int64_t row_blocks = (c.S * c.H + kRowsWG - 1) / kRowsWG;
   const int64_t units = c.B * row_blocks;
   int64_t splits = (num_cus + units / 2) / units;
-  const int64_t max_by_len = (c.end_pos + 127) / 128;
+  const int64_t items = c.topk > 0 ? c.topk : c.end_pos;  // positions, or list entries
+  const int64_t max_by_len = (items + 127) / 128;
   if (splits > max_by_len) splits = max_by_len;
   if (splits < 1) splits = 1;
   if (c.page_size > 0) {  // a split may span at most 64 kPageRegs pages
     const int64_t cap = mfma_paged_max_split_len(c);
     splits = std::max<int64_t>(splits, (c.end_pos + cap - 1) / cap);
   }
+  if (c.topk > 0) splits = std::max<int64_t>(splits, (c.topk + 64 * kPageRegs - 1) / (64 * kPageRegs));
   if (splits > 4096) splits = 4096;
   return int32_t(splits);
 }
@@ -837,6 +911,10 @@ bool mfma_attn_plan_ok(const AttnCall &c, const char **why) {
   }
   if (c.page_size > 0 && (c.split_len % kTile || c.split_len > mfma_paged_max_split_len(c))) {
     *why = "paged splits must be multiples of 32 positions spanning at most 255 pages";
+    return false;
+  }
+  if (c.topk > 0 && c.split_len > 64 * kPageRegs) {
+    *why = "a split of an index list may hold at most 256 entries";
     return false;
   }
   // split partials are addressed with 32-bit byte offsets
@@ -896,15 +974,19 @@ hipError_t mfma_absorb_attn(const AttnCall &c) {
   aa.row_blocks = row_blocks;
   aa.scale_log2 = c.scale * kLog2e;
   const int64_t nwg = c.B * int64_t(aa.splits) * aa.row_blocks;
-  if (c.page_size > 0) {
+  if (c.topk > 0) {
+    aa.indices = c.indices;
+    aa.topk = int32_t(c.topk);
+    err = launch_kernel(MLA_KERNEL_ATTN, attn_kernel<kModeSparse>, dim3(unsigned(nwg)), dim3(256), 0, c.stream, aa);
+  } else if (c.page_size > 0) {
     aa.block_table = c.block_table;
     aa.log2_page = 0;
     while ((int64_t(1) << aa.log2_page) < c.page_size) ++aa.log2_page;
     aa.max_pages = int32_t(c.max_pages);
     aa.num_pages = int32_t(c.num_pages);
-    err = launch_kernel(MLA_KERNEL_ATTN, attn_kernel<true>, dim3(unsigned(nwg)), dim3(256), 0, c.stream, aa);
+    err = launch_kernel(MLA_KERNEL_ATTN, attn_kernel<kModePaged>, dim3(unsigned(nwg)), dim3(256), 0, c.stream, aa);
   } else {
-    err = launch_kernel(MLA_KERNEL_ATTN, attn_kernel<false>, dim3(unsigned(nwg)), dim3(256), 0, c.stream, aa);
+    err = launch_kernel(MLA_KERNEL_ATTN, attn_kernel<kModeContig>, dim3(unsigned(nwg)), dim3(256), 0, c.stream, aa);
   }
   if (err != hipSuccess) return err;
 

@@ -17,6 +17,11 @@ struct AttnCall {
   // (clamped into [0, num_pages)); with page_size 0 the caches are [Bmax, Tmax, C / R]
   const int32_t *block_table;
   int64_t page_size, num_pages, max_pages;
+  // index lists (topk > 0): device [B, S, topk]; token (b, s) attends to the positions its list
+  // names that lie in [0, end_pos - S + s] (end_pos per sequence as above); splits then cut the
+  // list entries instead of the positions
+  const int32_t *indices;
+  int64_t topk;
   float scale;
   int32_t dtype;      // MLA_DTYPE_*
   int32_t splits;     // ranges the positions [0, end_pos) are cut into

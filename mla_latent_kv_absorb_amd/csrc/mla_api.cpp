@@ -38,8 +38,10 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
 // arguments, so the size query and the call always agree.
 // With `paged` the caches are page pools: the shape's cache fields are replaced by the batch and
 // the per-sequence capacity max_pages_per_seq * page_size.
-int32_t plan_attn(const mla_attn_shape *shape, int64_t end_pos, const mla_paged_cache *paged, int32_t dtype,
-                  const mla_attn_options *options, mla::AttnCall &c, bool &use_mfma) {
+// With topk > 0 each query token attends to an index list of topk entries, and the splits cut
+// the entries.
+int32_t plan_attn(const mla_attn_shape *shape, int64_t end_pos, const mla_paged_cache *paged, int64_t topk,
+                  int32_t dtype, const mla_attn_options *options, mla::AttnCall &c, bool &use_mfma) {
   if (!shape) return fail(MLA_ERR_NULL, "shape is NULL");
   if (dtype != MLA_DTYPE_F32 && dtype != MLA_DTYPE_BF16) return fail(MLA_ERR_DTYPE, "unknown dtype %d", dtype);
   mla_attn_shape s = *shape;
@@ -92,6 +94,10 @@ int32_t plan_attn(const mla_attn_shape *shape, int64_t end_pos, const mla_paged_
   c.B = s.batch; c.S = s.seqlen_q; c.H = s.n_heads; c.C = s.kv_lora_rank; c.R = s.qk_rope_head_dim;
   c.Dn = s.qk_nope_head_dim; c.Dv = s.v_head_dim; c.Bmax = s.cache_batch; c.Tmax = s.cache_len;
   c.end_pos = end_pos; c.dtype = dtype;
+  if (topk < 0 || topk > (int64_t(1) << 24)) return fail(MLA_ERR_SHAPE, "topk = %lld outside [1, 2^24]", (long long)topk);
+  c.topk = topk;
+  if (topk > 0 && s.batch * s.seqlen_q * topk > (int64_t(1) << 31) - 1)
+    return fail(MLA_ERR_SHAPE, "batch * seqlen_q * topk is too large");
   if (paged) {
     c.page_size = paged->page_size; c.num_pages = paged->num_pages; c.max_pages = paged->max_pages_per_seq;
   }
@@ -108,8 +114,9 @@ int32_t plan_attn(const mla_attn_shape *shape, int64_t end_pos, const mla_paged_
   } else {
     c.splits = use_mfma ? mla::mfma_attn_splits(c, 256) : mla::plain_attn_splits(c);
   }
-  if (c.splits > end_pos) c.splits = int32_t(end_pos);
-  c.split_len = (end_pos + c.splits - 1) / c.splits;
+  const int64_t items = topk > 0 ? topk : end_pos;  // positions, or list entries
+  if (c.splits > items) c.splits = int32_t(items);
+  c.split_len = (items + c.splits - 1) / c.splits;
   if (use_mfma && c.page_size > 0) c.split_len = (c.split_len + 31) / 32 * 32;  // tiles within pages
   if (use_mfma) {
     const char *why = "";
@@ -118,8 +125,8 @@ int32_t plan_attn(const mla_attn_shape *shape, int64_t end_pos, const mla_paged_
       use_mfma = false;
       if (opt.num_splits == 0) {
         c.splits = mla::plain_attn_splits(c);
-        if (c.splits > end_pos) c.splits = int32_t(end_pos);
-        c.split_len = (end_pos + c.splits - 1) / c.splits;
+        if (c.splits > items) c.splits = int32_t(items);
+        c.split_len = (items + c.splits - 1) / c.splits;
       }
     }
   }
@@ -152,7 +159,7 @@ size_t mla_absorb_attn_workspace_size(const mla_attn_shape *shape, int64_t end_p
   clear_error();
   mla::AttnCall c;
   bool use_mfma = false;
-  if (plan_attn(shape, end_pos, nullptr, dtype, options, c, use_mfma) != MLA_OK) return 0;
+  if (plan_attn(shape, end_pos, nullptr, 0, dtype, options, c, use_mfma) != MLA_OK) return 0;
   return use_mfma ? mla::mfma_attn_workspace(c) : mla::plain_attn_workspace(c);
 }
 
@@ -163,7 +170,17 @@ size_t mla_absorb_attn_paged_workspace_size(const mla_attn_shape *shape, int64_t
   if (!paged) { fail(MLA_ERR_NULL, "paged is NULL"); return 0; }
   mla::AttnCall c;
   bool use_mfma = false;
-  if (plan_attn(shape, max_seq_len, paged, dtype, options, c, use_mfma) != MLA_OK) return 0;
+  if (plan_attn(shape, max_seq_len, paged, 0, dtype, options, c, use_mfma) != MLA_OK) return 0;
+  return use_mfma ? mla::mfma_attn_workspace(c) : mla::plain_attn_workspace(c);
+}
+
+size_t mla_absorb_attn_sparse_workspace_size(const mla_attn_shape *shape, int64_t end_pos, int64_t topk,
+                                             int32_t dtype, const mla_attn_options *options) {
+  clear_error();
+  if (topk < 1) { fail(MLA_ERR_SHAPE, "topk = %lld must be >= 1", (long long)topk); return 0; }
+  mla::AttnCall c;
+  bool use_mfma = false;
+  if (plan_attn(shape, end_pos, nullptr, topk, dtype, options, c, use_mfma) != MLA_OK) return 0;
   return use_mfma ? mla::mfma_attn_workspace(c) : mla::plain_attn_workspace(c);
 }
 
@@ -175,12 +192,12 @@ namespace {
 // for a uniform batch; paged and block_table null for contiguous caches).
 int32_t absorb_attn_call(const void *q_nope, const void *q_pe, const void *kv_cache, const void *pe_cache,
                          const void *wkv_b, const int32_t *seq_lens, const int32_t *block_table,
-                         const mla_paged_cache *paged, int64_t end_pos, float softmax_scale, void *out,
-                         const mla_attn_shape *shape, int32_t dtype, const mla_attn_options *options,
-                         void *workspace, size_t workspace_bytes, void *stream) {
+                         const mla_paged_cache *paged, const int32_t *indices, int64_t topk, int64_t end_pos,
+                         float softmax_scale, void *out, const mla_attn_shape *shape, int32_t dtype,
+                         const mla_attn_options *options, void *workspace, size_t workspace_bytes, void *stream) {
   mla::AttnCall c;
   bool use_mfma = false;
-  int32_t rc = plan_attn(shape, end_pos, paged, dtype, options, c, use_mfma);
+  int32_t rc = plan_attn(shape, end_pos, paged, indices ? topk : 0, dtype, options, c, use_mfma);
   if (rc != MLA_OK) return rc;
   const void *ptrs[] = {q_nope, q_pe, kv_cache, pe_cache, wkv_b, out};
   const char *names[] = {"q_nope", "q_pe", "kv_cache", "pe_cache", "wkv_b", "out"};
@@ -204,6 +221,8 @@ int32_t absorb_attn_call(const void *q_nope, const void *q_pe, const void *kv_ca
   const size_t table_bytes = size_t(c.B * c.max_pages) * sizeof(int32_t);
   if (block_table && overlaps(out, out_bytes, block_table, table_bytes))
     return fail(MLA_ERR_SHAPE, "out overlaps block_table");
+  const size_t index_bytes = size_t(c.B * c.S * c.topk) * sizeof(int32_t);
+  if (indices && overlaps(out, out_bytes, indices, index_bytes)) return fail(MLA_ERR_SHAPE, "out overlaps indices");
   const size_t need = use_mfma ? mla::mfma_attn_workspace(c) : mla::plain_attn_workspace(c);
   if (need > 0) {
     if (!workspace) return fail(MLA_ERR_WORKSPACE, "workspace is NULL but %zu bytes are needed", need);
@@ -218,12 +237,15 @@ int32_t absorb_attn_call(const void *q_nope, const void *q_pe, const void *kv_ca
       return fail(MLA_ERR_WORKSPACE, "workspace overlaps seq_lens");
     if (block_table && overlaps(workspace, need, block_table, table_bytes))
       return fail(MLA_ERR_WORKSPACE, "workspace overlaps block_table");
+    if (indices && overlaps(workspace, need, indices, index_bytes))
+      return fail(MLA_ERR_WORKSPACE, "workspace overlaps indices");
   }
   c.scale = softmax_scale;
   c.q_nope = q_nope; c.q_pe = q_pe; c.kv = kv_cache; c.pe = pe_cache; c.wkv_b = wkv_b;
   c.out = out; c.ws = workspace; c.stream = static_cast<hipStream_t>(stream);
   c.seq_lens = seq_lens;
   c.block_table = block_table;
+  c.indices = indices;
   if (use_mfma && c.splits == 0) c.splits = 1;
   hipError_t e = use_mfma ? mla::mfma_absorb_attn(c) : mla::plain_absorb_attn(c);
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
@@ -239,8 +261,8 @@ int32_t mla_absorb_attn(const void *q_nope, const void *q_pe, const void *kv_cac
                         const mla_attn_shape *shape, int32_t dtype, const mla_attn_options *options,
                         void *workspace, size_t workspace_bytes, void *stream) {
   clear_error();
-  return absorb_attn_call(q_nope, q_pe, kv_cache, pe_cache, wkv_b, nullptr, nullptr, nullptr, end_pos, softmax_scale,
-                          out, shape, dtype, options, workspace, workspace_bytes, stream);
+  return absorb_attn_call(q_nope, q_pe, kv_cache, pe_cache, wkv_b, nullptr, nullptr, nullptr, nullptr, 0, end_pos,
+                          softmax_scale, out, shape, dtype, options, workspace, workspace_bytes, stream);
 }
 
 int32_t mla_absorb_attn_ragged(const void *q_nope, const void *q_pe, const void *kv_cache, const void *pe_cache,
@@ -251,8 +273,8 @@ int32_t mla_absorb_attn_ragged(const void *q_nope, const void *q_pe, const void 
   clear_error();
   if (!seq_lens) return fail(MLA_ERR_NULL, "seq_lens is NULL");
   if (reinterpret_cast<uintptr_t>(seq_lens) & 3u) return fail(MLA_ERR_ALIGN, "seq_lens is not 4-byte aligned");
-  return absorb_attn_call(q_nope, q_pe, kv_cache, pe_cache, wkv_b, seq_lens, nullptr, nullptr, max_seq_len,
-                          softmax_scale, out, shape, dtype, options, workspace, workspace_bytes, stream);
+  return absorb_attn_call(q_nope, q_pe, kv_cache, pe_cache, wkv_b, seq_lens, nullptr, nullptr, nullptr, 0,
+                          max_seq_len, softmax_scale, out, shape, dtype, options, workspace, workspace_bytes, stream);
 }
 
 int32_t mla_absorb_attn_paged(const void *q_nope, const void *q_pe, const void *kv_pages, const void *pe_pages,
@@ -265,8 +287,22 @@ int32_t mla_absorb_attn_paged(const void *q_nope, const void *q_pe, const void *
   if (!block_table) return fail(MLA_ERR_NULL, "block_table is NULL");
   if (reinterpret_cast<uintptr_t>(block_table) & 3u) return fail(MLA_ERR_ALIGN, "block_table is not 4-byte aligned");
   if (reinterpret_cast<uintptr_t>(seq_lens) & 3u) return fail(MLA_ERR_ALIGN, "seq_lens is not 4-byte aligned");
-  return absorb_attn_call(q_nope, q_pe, kv_pages, pe_pages, wkv_b, seq_lens, block_table, paged, max_seq_len,
-                          softmax_scale, out, shape, dtype, options, workspace, workspace_bytes, stream);
+  return absorb_attn_call(q_nope, q_pe, kv_pages, pe_pages, wkv_b, seq_lens, block_table, paged, nullptr, 0,
+                          max_seq_len, softmax_scale, out, shape, dtype, options, workspace, workspace_bytes, stream);
+}
+
+int32_t mla_absorb_attn_sparse(const void *q_nope, const void *q_pe, const void *kv_cache, const void *pe_cache,
+                               const void *wkv_b, const int32_t *indices, int64_t topk, const int32_t *seq_lens,
+                               int64_t end_pos, float softmax_scale, void *out, const mla_attn_shape *shape,
+                               int32_t dtype, const mla_attn_options *options, void *workspace,
+                               size_t workspace_bytes, void *stream) {
+  clear_error();
+  if (!indices) return fail(MLA_ERR_NULL, "indices is NULL");
+  if (reinterpret_cast<uintptr_t>(indices) & 3u) return fail(MLA_ERR_ALIGN, "indices is not 4-byte aligned");
+  if (reinterpret_cast<uintptr_t>(seq_lens) & 3u) return fail(MLA_ERR_ALIGN, "seq_lens is not 4-byte aligned");
+  if (topk < 1) return fail(MLA_ERR_SHAPE, "topk = %lld must be >= 1", (long long)topk);
+  return absorb_attn_call(q_nope, q_pe, kv_cache, pe_cache, wkv_b, seq_lens, nullptr, nullptr, indices, topk,
+                          end_pos, softmax_scale, out, shape, dtype, options, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -68,10 +68,16 @@ plain_attn_partial_kernel(const float *__restrict__ q_lat, const T *__restrict__
     if (end_pos > a.end_pos) end_pos = a.end_pos;
   }
   const int64_t last = end_pos - a.S + s;  // last visible position of this query
+  // the split's positions [t0, t1), or with an index list its entries [t0, t1)
   const int64_t t0 = int64_t(split) * a.split_len;
   int64_t t1 = t0 + a.split_len;
-  if (t1 > end_pos) t1 = end_pos;
-  if (t1 > last + 1) t1 = last + 1;
+  if (a.topk > 0) {
+    if (t1 > a.topk) t1 = a.topk;
+  } else {
+    if (t1 > end_pos) t1 = end_pos;
+    if (t1 > last + 1) t1 = last + 1;
+  }
+  const int32_t *list = a.topk > 0 ? a.indices + (b * a.S + s) * a.topk : nullptr;
 
   for (int64_t c = tid; c < a.C; c += kThreads) { sq[c] = q_lat[row * a.C + c]; so[c] = 0.f; }
   for (int64_t r = tid; r < a.R; r += kThreads) sqp[r] = Elem<T>::load(q_pe, row * a.R + r);
@@ -80,10 +86,19 @@ plain_attn_partial_kernel(const float *__restrict__ q_lat, const T *__restrict__
   float m = -INFINITY, l = 0.f;
   for (int64_t tc = t0; tc < t1; tc += kThreads) {
     const int n = int((t1 - tc) < kThreads ? (t1 - tc) : kThreads);
-    if (tid < n) srow[tid] = cache_row(a, b, tc + tid);
+    bool ok = tid < n;
+    if (ok) {
+      int64_t t = tc + tid;
+      if (list) {  // an entry counts if it names a visible position; others read row 0, weight 0
+        t = list[tc + tid];
+        ok = t >= 0 && t <= last;
+        if (!ok) t = 0;
+      }
+      srow[tid] = cache_row(a, b, t);
+    }
     __syncthreads();
     float sc = -INFINITY;
-    if (tid < n) {
+    if (ok) {
       const int64_t r0 = srow[tid];
       float acc = 0.f;
       for (int64_t c = 0; c < a.C; ++c) acc = fmaf(sq[c], Elem<T>::load(kv, r0 * a.C + c), acc);
@@ -91,7 +106,7 @@ plain_attn_partial_kernel(const float *__restrict__ q_lat, const T *__restrict__
       sc = acc * a.scale;
     }
     const float m_new = fmaxf(m, block_max(sc, red));
-    const float p = (tid < n) ? expf(sc - m_new) : 0.f;
+    const float p = ok ? expf(sc - m_new) : 0.f;
     sp[tid] = p;
     const float alpha = (m == -INFINITY) ? 0.f : expf(m - m_new);
     l = l * alpha + block_sum(p, red);  // block_sum synchronises, so sp is visible below
@@ -124,7 +139,7 @@ plain_merge_upproj_kernel(const float *__restrict__ part_ml, const float *__rest
   float den = 0.f;
   for (int i = 0; i < a.splits; ++i)
     if (ml[2 * i] != -INFINITY) den += expf(ml[2 * i] - M) * ml[2 * i + 1];
-  const float inv = 1.f / den;
+  const float inv = den > 0.f ? 1.f / den : 0.f;  // 0: a sparse row whose list names no visible position
   for (int64_t c = tid; c < a.C; c += kThreads) {
     float acc = 0.f;
     for (int i = 0; i < a.splits; ++i)
@@ -264,10 +279,11 @@ hipError_t run_naive(const NaiveCall &c) {
 }  // namespace
 
 int32_t plain_attn_splits(const AttnCall &c) {
-  // Enough blocks to spread over the chip, but never fewer than 256 positions per split.
+  // Enough blocks to spread over the chip, but never fewer than 256 positions (or list entries)
+  // per split.
   const int64_t rows = c.B * c.S * c.H;
   int64_t splits = (2048 + rows - 1) / rows;
-  const int64_t max_by_len = (c.end_pos + 255) / 256;
+  const int64_t max_by_len = ((c.topk > 0 ? c.topk : c.end_pos) + 255) / 256;
   if (splits > max_by_len) splits = max_by_len;
   if (splits < 1) splits = 1;
   return int32_t(splits);

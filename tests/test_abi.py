@@ -294,3 +294,47 @@ def test_paged_workspace_and_split_plan(lib):
     ws = {p: B.absorb_attn_paged_workspace_size(one, 16384, B.PagedCache(p, 16384 // p, 16384 // p),
                                                 B.MLA_DTYPE_BF16, path="mfma") for p in (32, 64, 128)}
     assert ws[32] > ws[64] > ws[128] == B.absorb_attn_workspace_size(one, 16384, B.MLA_DTYPE_BF16, path="mfma")
+
+
+def call_sparse(lib, s, end_pos=4096, ptrs=None, idx=P[6], topk=2048, lens=None, path=B.PATHS["auto"], splits=0,
+                ws=P[7], ws_bytes=1 << 40):
+    p = list(P[:6]) if ptrs is None else ptrs
+    opt = B.AttnOptions(splits, path)
+    return lib.mla_absorb_attn_sparse(p[0], p[1], p[2], p[3], p[4], idx, topk, lens, end_pos, 0.07, p[5],
+                                      ctypes.byref(s), B.MLA_DTYPE_BF16, ctypes.byref(opt), ws, ws_bytes, None)
+
+
+def test_sparse_argument_errors(lib):
+    s = shape()
+    assert call_sparse(lib, s, idx=None) == B.MLA_ERR_NULL
+    assert call_sparse(lib, s, idx=P[6] + 2) == B.MLA_ERR_ALIGN
+    assert call_sparse(lib, s, lens=P[6] + (1 << 20) + 2) == B.MLA_ERR_ALIGN
+    assert call_sparse(lib, s, topk=0) == B.MLA_ERR_SHAPE
+    assert call_sparse(lib, s, topk=(1 << 24) + 1) == B.MLA_ERR_SHAPE
+    assert call_sparse(lib, s, end_pos=4097) == B.MLA_ERR_RANGE
+    assert call_sparse(lib, shape(seqlen_q=9), end_pos=8) == B.MLA_ERR_RANGE
+    # a matrix-core workgroup's 128 rows must be the heads of one token
+    assert call_sparse(lib, shape(seqlen_q=2, n_heads=64), path=B.PATHS["mfma"]) == B.MLA_ERR_UNSUPPORTED
+    assert call_sparse(lib, shape(seqlen_q=1, n_heads=192), path=B.PATHS["mfma"]) == B.MLA_ERR_UNSUPPORTED
+    # a forced split may hold at most 256 list entries on the matrix-core path
+    assert call_sparse(lib, s, splits=1, topk=257, path=B.PATHS["mfma"]) == B.MLA_ERR_UNSUPPORTED
+    # out, workspace, indices and seq_lens must not overlap
+    assert call_sparse(lib, s, idx=P[5] + 64) == B.MLA_ERR_SHAPE
+    assert call_sparse(lib, s, idx=P[7] + 64) == B.MLA_ERR_WORKSPACE
+    assert call_sparse(lib, s, ws_bytes=16) == B.MLA_ERR_WORKSPACE
+    for i in range(6):
+        p = list(P[:6])
+        p[i] = None
+        assert call_sparse(lib, s, ptrs=p) == B.MLA_ERR_NULL
+
+
+def test_sparse_workspace_plan(lib):
+    # splits cut the list entries: 2048 entries of 32 decode tokens plan like 2048 positions
+    s = shape(batch=32, cache_batch=32)
+    assert B.absorb_attn_sparse_workspace_size(s, 4096, 2048, B.MLA_DTYPE_BF16) == \
+        B.absorb_attn_workspace_size(s, 2048, B.MLA_DTYPE_BF16)
+    # one token with a long list: at least topk / 256 splits on the matrix-core path
+    one = shape(batch=1, seqlen_q=1, cache_batch=1, cache_len=65536)
+    few = B.absorb_attn_sparse_workspace_size(one, 65536, 256, B.MLA_DTYPE_BF16, path="mfma")
+    many = B.absorb_attn_sparse_workspace_size(one, 65536, 65536, B.MLA_DTYPE_BF16, path="mfma")
+    assert many > few

@@ -433,6 +433,108 @@ def test_full_size_paged_matches_contiguous(gpu_lib, name, page_size):
     assert torch.equal(out, ref), f"paged differs from contiguous: max {float((out.float() - ref.float()).abs().max())}"
 
 
+# --------------------------------------------------------------------------------- index lists
+
+def make_lists(cfg, lens, topk, seed, empty=None):
+    """Per-token lists: mostly positions the token sees, some repeats, and entries that name no
+    visible position (-1, the next position, past the length, past the cache); token `empty`
+    (b, s) gets only such entries."""
+    rng = np.random.default_rng(seed)
+    B, S = cfg.batch, cfg.seqlen_q
+    idx = np.zeros((B, S, topk), np.int32)
+    for b in range(B):
+        for s_ in range(S):
+            pos = int(lens[b]) - S + s_
+            row = rng.integers(0, pos + 1, topk)
+            row[rng.random(topk) < 0.05] = -1
+            row[rng.random(topk) < 0.03] = pos + 1
+            row[rng.random(topk) < 0.02] = cfg.cache_len + 100
+            if topk > 4:
+                row[3] = row[2]
+            idx[b, s_] = row
+    if empty is not None:
+        idx[empty] = -1
+        idx[empty][::2] = int(lens[empty[0]]) - S + empty[1] + 1
+    return idx
+
+
+def run_attn_sparse(lib, cfg, t, idx, lens=None, path="auto", splits=0):
+    out = torch.full((cfg.batch, cfg.seqlen_q, cfg.n_heads, cfg.v_head_dim), float("nan"), dtype=tdtype(cfg),
+                     device="cuda")
+    seq = None if lens is None else torch.tensor([int(n) for n in lens], dtype=torch.int32, device="cuda")
+    lib.absorb_attn(t["q_nope"], t["q_pe"], t["kv_cache"], t["pe_cache"], t["wkv_b"], cfg.end_pos,
+                    cfg.softmax_scale, out, num_splits=splits, path=path, seq_lens=seq,
+                    indices=torch.from_numpy(np.ascontiguousarray(idx, np.int32)).to("cuda"))
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("path", ["mfma", "plain", "auto"])
+@pytest.mark.parametrize("seqlen_q,topk", [(1, 37), (1, 300), (3, 64), (1, 1)])
+def test_sparse_small(gpu_lib, path, seqlen_q, topk):
+    cfg = dsv3_small(batch=3, cache_batch=3, seqlen_q=seqlen_q, end_pos=300, cache_len=320)
+    if path == "plain":
+        cfg = cfg.replace(n_heads=16)
+    x = make_attn_inputs(cfg)
+    lens = [300, 41, 170]
+    idx = make_lists(cfg, lens, topk, 101 + topk, empty=(1, seqlen_q - 1))
+    t = to_dev(x, cfg)
+    poison_tails(t, lens)
+    out = run_attn_sparse(gpu_lib, cfg, t, idx, lens, path=path)
+    ref = O.absorb_attention_sparse(x["q_nope"], x["q_pe"], x["kv_cache"], x["pe_cache"], x["wkv_b"], idx, lens,
+                                    cfg.softmax_scale, cfg.v_head_dim)
+    check(out, ref, TOL["bf16"], f"sparse {path} S={seqlen_q} topk={topk}")
+    assert torch.all(out[1, seqlen_q - 1] == 0), "a token with no visible entry must give 0"
+
+
+@pytest.mark.parametrize("path,splits", [("mfma", 1), ("mfma", 2), ("mfma", 5), ("mfma", 9), ("plain", 4)])
+def test_sparse_forced_splits(gpu_lib, path, splits):
+    """Splits over list entries (one not a multiple of 32, empty ones), with a token whose list
+    names nothing visible in any split."""
+    cfg = dsv3_small(batch=2, cache_batch=2, seqlen_q=1, end_pos=280, cache_len=300)
+    x = make_attn_inputs(cfg)
+    lens = [280, 90]
+    idx = make_lists(cfg, lens, 250, 111 + splits, empty=(0, 0))
+    t = to_dev(x, cfg)
+    out = run_attn_sparse(gpu_lib, cfg, t, idx, lens, path=path, splits=splits)
+    ref = O.absorb_attention_sparse(x["q_nope"], x["q_pe"], x["kv_cache"], x["pe_cache"], x["wkv_b"], idx, lens,
+                                    cfg.softmax_scale, cfg.v_head_dim)
+    check(out, ref, TOL["bf16"], f"sparse {path} splits={splits}")
+    assert torch.all(out[0, 0] == 0)
+
+
+@pytest.mark.parametrize("seqlen_q", [1, 4])
+def test_sparse_full_list_equals_dense(gpu_lib, seqlen_q):
+    """A list naming every cache position (random order; later positions masked per token) gives
+    the dense causal result of mla_absorb_attn, both on the GPU."""
+    cfg = dsv3_small(batch=2, cache_batch=2, seqlen_q=seqlen_q, end_pos=256, cache_len=256)
+    x = make_attn_inputs(cfg)
+    rng = np.random.default_rng(121)
+    idx = np.stack([np.stack([rng.permutation(cfg.cache_len) for _ in range(seqlen_q)]) for _ in range(cfg.batch)])
+    t = to_dev(x, cfg)
+    sp = run_attn_sparse(gpu_lib, cfg, t, idx)
+    dense = run_attn(gpu_lib, cfg, t)
+    check(sp, dense.float().cpu().double().numpy(), TOL["bf16"], f"full list vs dense S={seqlen_q}")
+
+
+@pytest.mark.parametrize("name,topk", [("dsv3_decode", 2048), ("long_decode", 2048), ("dsv3_decode", 100)])
+def test_full_size_sparse(gpu_lib, name, topk):
+    cfg = ATTN_CONFIGS[name]
+    print(f"full-size sparse {name}: B={cfg.batch} T={cfg.end_pos} topk={topk}", flush=True)
+    x = make_attn_inputs(cfg)
+    rng = np.random.default_rng(131)
+    idx = np.stack([np.stack([rng.choice(cfg.end_pos, topk, replace=False) for _ in range(cfg.seqlen_q)])
+                    for _ in range(cfg.batch)]).astype(np.int32)
+    t = to_dev(x, cfg)
+    out = run_attn_sparse(gpu_lib, cfg, t, idx)
+    assert torch.isfinite(out).all(), "non-finite outputs"
+    rows = sample_rows(cfg, 48, 13)
+    ref = O.absorb_attention_sparse(x["q_nope"], x["q_pe"], x["kv_cache"], x["pe_cache"], x["wkv_b"], idx,
+                                    [cfg.end_pos] * cfg.batch, cfg.softmax_scale, cfg.v_head_dim, rows=rows)
+    g = out.float().cpu().double().numpy()
+    check(np.stack([g[b, s_, h] for b, s_, h in rows]), ref, TOL["bf16"], f"{name} topk={topk} sampled rows")
+
+
 # --------------------------------------------------------------------------------- cache append
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
