@@ -8,9 +8,11 @@ over kv_cache + pe_cache, merge and W_UV projection) over one batch: 32 sequence
 positions x 128 heads, bf16.  Inputs are seeded synthetic tensors drawn on the GPU with the
 workload's shapes and distributions (q, caches ~N(0,1); wkv_b ~N(0,1/512)).  To measure HBM rather
 than the 256 MB Infinity Cache, the timed steps rotate over several complete input sets (about
-750 MB in all), so each step's operands were last touched three steps earlier.  A GPU spin
-kernel runs ahead of every timed region, so the host has queued all timed steps before the GPU
-reaches them: the figure is back-to-back GPU time, not Python launch overhead.
+750 MB in all), so each step's operands were last touched three steps earlier.  The timed region
+starts on an idle, synchronised GPU; the host enqueues a step in about 9 us against about 65 us
+of GPU work, so after the first launch the queue stays ahead of the GPU and the figure is
+back-to-back GPU time (the first launch's latency is included).  No spin kernel runs ahead: a
+sleeping spin let the clocks fall and cost about 4 us per step.
 
 Prints ONE JSON line.  `value` is microseconds per step (lower is better), from timed steps that
 carry no per-kernel events.  `roofline` reports the dominant kernel (the attention kernel) against
@@ -41,9 +43,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-SPIN_CYCLES = 20_000_000  # GPU clock cycles of spin ahead of a timed region (about 10 ms)
 BF16_PEAK_TFLOPS = 2516.6
 METRIC = "MLA absorb decode µs/step, HBM GB/s & MFMA TFLOP/s as % of roofline"
+
+
+def progress(msg):
+    """One line per finished pass on stderr (stdout carries only the result line)."""
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
 
 
 def sparse_work(cfg, topk):
@@ -158,9 +164,6 @@ def time_attn(cfg, steps, warmup, sets, torch, binding, seed=1, timed_kernels=0b
     binding.timing_collect()  # drop anything recorded before the timed region
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    # A spin kernel ahead of the timed region keeps the GPU busy while the host enqueues every
-    # timed step, so the events measure back-to-back GPU work, not host launch overhead.
-    torch.cuda._sleep(SPIN_CYCLES)
     t0 = time.perf_counter()
     e0.record()
     for i in range(steps):
@@ -172,7 +175,9 @@ def time_attn(cfg, steps, warmup, sets, torch, binding, seed=1, timed_kernels=0b
     binding.timing_enable(0)
     del inputs, calls, tables, lists
     torch.cuda.empty_cache()
-    return e0.elapsed_time(e1) * 1000.0 / steps, enqueue, kt
+    us = e0.elapsed_time(e1) * 1000.0 / steps
+    progress(f"{cfg.name} lens={lens is not None} page={page_size} topk={topk} kernels={timed_kernels:#x}: {us:.2f} us/step")
+    return us, enqueue, kt
 
 
 def time_expand(cfg, steps, warmup, torch, binding, seed=4):
@@ -239,7 +244,6 @@ def time_naive_route(cfg, steps, warmup, torch, binding, seed=3):
         binding.timing_enable(mask)
         binding.timing_collect()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda._sleep(SPIN_CYCLES)
         e0.record()
         for _ in range(steps):
             step()
@@ -251,6 +255,7 @@ def time_naive_route(cfg, steps, warmup, torch, binding, seed=3):
 
     us, _ = timed(0)
     _, kt = timed((1 << 3) | (1 << 4) | (1 << 6))
+    progress(f"{cfg.name} naive route: {us:.2f} us/step")
     del x, k, v, out, ws
     torch.cuda.empty_cache()
     return us, kt
@@ -285,6 +290,7 @@ def cpu_baseline(cfg, budget_s=12.0):
             break
     per_call = elapsed / reps
     us_per_step = per_call * 1e6 * cfg.batch / n_seq
+    progress(f"cpu baseline: {reps} oracle calls in {elapsed:.1f} s")
     return {"value": round(us_per_step, 1), "unit": "us/step", "cores": int(threads), "kind": "oracle",
             "sample": f"absorb route, float64, {n_seq} of {cfg.batch} sequences (same shapes otherwise), "
                       f"{reps} calls in {elapsed:.1f} s, scaled by {cfg.batch}/{n_seq}",
