@@ -240,9 +240,12 @@ attn_kernel(AttnArgs a) {
       buf_load16_lds_at(src.kv, st + (wave * 8 + part) * (kC * 2),
                         lane16 ^ uint32_t(kv_swz(8 * (wave & 1) + part) * 16), uint32_t(t - src.tb) * (kC * 2));
     } else {
+      // rows from the tile's first one, or (a tile past the end) from the last needed one, so
+      // that every offset is that of a row the workgroup may read
+      const int tq = min(t0, src.tlast);
       const int tp = min(t0 + pe_row, src.tlast);
-      buf_load16_lds_at(src.pe, st + kKvTileBytes + wave * 8 * (kR * 2), pe_voff + uint32_t(tp - t0) * (kR * 2),
-                        uint32_t(t0 - src.tb) * (kR * 2));
+      buf_load16_lds_at(src.pe, st + kKvTileBytes + wave * 8 * (kR * 2), pe_voff + uint32_t(tp - tq) * (kR * 2),
+                        uint32_t(tq - src.tb) * (kR * 2));
     }
   };
   auto issue = [&](int j) __attribute__((always_inline)) {
@@ -311,12 +314,24 @@ attn_kernel(AttnArgs a) {
   // (32 over kv, then 4 over pe), their kv/pe fragments read through a ring of kRing registers
   // kRing - 1 MFMAs ahead.  After each group of four MFMAs comes one of the nine DMA instructions
   // of tile `rtile` (when `refill`), so that a full memory queue stalls one instruction at a time.
+  // (In the loop the refill is unconditional: a tile past the workgroup's last one re-reads its
+  // last needed row into the stage of a finished tile, which is cheaper than a branch per part.)
+  // the swizzled per-lane read addresses, XOR-ed once here instead of once per tile
+  uint32_t scx[8], pex[4], trx[2][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) scx[i] = sc_base ^ uint32_t(32 * i);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    pex[i] = pe_base ^ uint32_t(32 * i);
+    trx[0][i] = tr_base[0] ^ uint32_t(64 * i);
+    trx[1][i] = tr_base[1] ^ uint32_t(64 * i);
+  }
   constexpr int kRing = 6;
   auto scores = [&](int j, f32x16 &sc, bool refill, int rtile, const TileSrc &rsrc) __attribute__((always_inline)) {
     const unsigned char *st = smem + (j % kStages) * kStageBytes;
     auto frag = [&](int k) __attribute__((always_inline)) -> u32x4 {
-      return k < 32 ? lds_read16(st, (sc_base ^ uint32_t((k & 7) * 32)) + (k >> 3) * 256)
-                    : lds_read16(st, pe_base ^ uint32_t((k - 32) * 32));
+      return k < 32 ? lds_read16(st, scx[k & 7] + (k >> 3) * 256)
+                    : lds_read16(st, pex[k - 32]);
     };
     u32x4 fr[kRing], qp[4];
 #pragma unroll
@@ -413,8 +428,8 @@ attn_kernel(AttnArgs a) {
   // other work can be placed between ranges (the bounds are constants at every call).
   auto trl = [&](int j, int n, int ks) __attribute__((always_inline)) -> u32x4 {
     const unsigned char *st = smem + (j % kStages) * kStageBytes;
-    return lds_read_tr_pair(st, (tr_base[0] ^ uint32_t((n & 3) * 64)) + (n >> 2) * 256 + ks * 16384,
-                            (tr_base[1] ^ uint32_t((n & 3) * 64)) + (n >> 2) * 256 + ks * 16384);
+    return lds_read_tr_pair(st, trx[0][n & 3] + (n >> 2) * 256 + ks * 16384,
+                            trx[1][n & 3] + (n >> 2) * 256 + ks * 16384);
   };
   u32x4 trf[4];
   auto pv_begin = [&](int j) __attribute__((always_inline)) {
@@ -445,8 +460,8 @@ attn_kernel(AttnArgs a) {
   // Software pipeline over tiles: iteration j runs the score MFMAs of tile j + 1, then the P.V
   // MFMAs of tile j while the vector ALU does the softmax of tile j + 1.  Tiles j and j + 1 are
   // read in iteration j; tile j + 3 is refilled into the stage of tile j - 1, which every wave has
-  // finished after the iteration's barrier.  Tiles 0..2 are issued by the prologue in any case
-  // (rows clamped), which keeps the wait counts exact.
+  // finished after the iteration's barrier.  Tiles 0..2 are issued by the prologue and one tile
+  // per iteration by the loop in any case (rows clamped), which keeps the wait counts exact.
   f32x16 sacc;
   u32x4 pb[2];  // probabilities of the tile whose P.V product comes next
   if (ntiles > 0) {
@@ -462,14 +477,14 @@ attn_kernel(AttnArgs a) {
   }
 #pragma unroll 1
   for (int j = 0; j + 1 < ntiles; ++j) {
-    // tile j+1 must have landed; tile j+2 (issued one iteration ago, or by the prologue) may not
-    if (j + 2 < ntiles) wait_vmcnt<kLoadsPerTile>();
-    else wait_vmcnt<0>();
+    // tile j+1 must have landed; tile j+2 (issued one iteration ago, or by the prologue, real or
+    // past the end) may not
+    wait_vmcnt<kLoadsPerTile>();
     __builtin_amdgcn_s_barrier();
     compiler_fence();
     const TileSrc rs = tile_src(j + 3);
     if constexpr (kSparse) asm volatile("" ::"v"(rs.pidx));  // wait for the permute here, not among the score reads
-    scores(j + 1, sacc, j + 3 < ntiles, j + 3, rs);
+    scores(j + 1, sacc, true, j + 3, rs);
     const int t1 = t_begin + (j + 1) * kTile;
     sm_mask(sacc, t1);
     u32x4 pn[2];
