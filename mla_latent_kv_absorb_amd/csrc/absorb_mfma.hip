@@ -554,6 +554,8 @@ attn_kernel(AttnArgs a) {
 // written fragment-major for attn_kernel (the first column quarter also copies q_pe there).
 // W_UK is staged in LDS once ([128 d][128 c], 16-byte chunks XOR-swizzled) and read transposed,
 // because the contraction runs over d while c is the contiguous index of wkv_b.
+constexpr int kQBlocksPerWG = 4;  // 32-row blocks of query rows per absorb_q workgroup
+
 struct AbsorbQArgs {
   const uint16_t *q_nope;  // [rows, Dn] with rows = M * H (row = m * H + h)
   const uint16_t *q_pe;    // [rows, 64]
@@ -620,6 +622,18 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(AbsorbQArgs a) {
     }
   };
   if (rb0 < rb_end) issue_x(rb0, 0);
+  // the first column quarter also moves the rope query rows of its row blocks into place: loaded
+  // here, with the rest of the first round trip, and stored at the end
+  const int pe_r = threadIdx.x >> 3, pe_chunk = threadIdx.x & 7;
+  u32x4 pe_v[kQBlocksPerWG];
+  const bool pe_copy = blockIdx.y == 0;
+  if (pe_copy) {
+#pragma unroll
+    for (int k = 0; k < kQBlocksPerWG; ++k) {
+      const int m = min((rb0 + k) * 32 + pe_r, a.M - 1);
+      pe_v[k] = *reinterpret_cast<const u32x4 *>(a.q_pe + (int64_t(m) * a.H + h) * kR + pe_chunk * 8);
+    }
+  }
   wait_vmcnt<0>();
   __syncthreads();
 
@@ -666,16 +680,13 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(AbsorbQArgs a) {
       __syncthreads();
     }
   }
-  // the first column quarter also moves the rope query rows of its row blocks into place
-  if (blockIdx.y == 0) {
-    const int r = threadIdx.x >> 3, chunk = threadIdx.x & 7;
-    for (int rb = rb0; rb < min(nrb, rb0 + a.row_blocks_per_wg); ++rb) {
-      const int m = rb * 32 + r;
-      if (m < a.M) {
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(a.q_pe + (int64_t(m) * a.H + h) * kR + chunk * 8);
+  if (pe_copy) {
+#pragma unroll
+    for (int k = 0; k < kQBlocksPerWG; ++k) {
+      const int m = (rb0 + k) * 32 + pe_r;
+      if (rb0 + k < rb_end && m < a.M)
         *reinterpret_cast<u32x4 *>(reinterpret_cast<unsigned char *>(a.q_frag) + frag_row_offset(m, h, a) +
-                                   (32 + (chunk >> 1)) * 1024 + (chunk & 1) * 16) = v;
-      }
+                                   (32 + (pe_chunk >> 1)) * 1024 + (pe_chunk & 1) * 16) = pe_v[k];
     }
   }
 }
@@ -963,7 +974,7 @@ hipError_t mfma_absorb_attn(const AttnCall &c) {
   const int32_t row_blocks = int32_t((c.S * c.H + kRowsWG - 1) / kRowsWG);
 
   AbsorbQArgs qa{static_cast<const uint16_t *>(c.q_nope), static_cast<const uint16_t *>(c.q_pe),
-                 static_cast<const uint16_t *>(c.wkv_b), q_frag, int32_t(c.H), M, int32_t(c.S), row_blocks, 4,
+                 static_cast<const uint16_t *>(c.wkv_b), q_frag, int32_t(c.H), M, int32_t(c.S), row_blocks, kQBlocksPerWG,
                  1.f / float(c.S)};
   const int nrb = (M + 31) / 32;
   hipError_t err = launch_kernel(
