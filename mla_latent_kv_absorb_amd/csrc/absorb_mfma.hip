@@ -724,7 +724,6 @@ template <bool kSingle>
 __global__ void __launch_bounds__(256) combine_kernel(CombineArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char wl[kDv * kC * 2];            // 128 KB
   __shared__ __attribute__((aligned(16))) unsigned char ol[kCombineRows * kC * 2];   // 16 KB
-  __shared__ float mstat[kCombineRows][2];                                           // M, 1 / den
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   // the workgroups of one head share W_UV[h] and sit on one XCD
@@ -750,28 +749,7 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineArgs a) {
   for (int grp = g_begin; grp < g_end; ++grp) {
     const int m0 = grp * kCombineRows;
     const int nrows = min(kCombineRows, a.M - m0);
-    // per-row maximum and denominator: 16 lanes per row, each over splits k, k + 16, ...
-    if (!kSingle) {
-      const int r = threadIdx.x >> 4, k = threadIdx.x & 15;
-      if (r < nrows) {
-        const float *ml = a.part_ml + (int64_t(m0 + r) * a.H + h) * a.splits * 2;
-        float mx = -INFINITY;
-        for (int i = k; i < a.splits; i += 16) mx = fmaxf(mx, ml[2 * i]);
-#pragma unroll
-        for (int o = 8; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 16));
-        float den = 0.f;
-        for (int i = k; i < a.splits; i += 16)
-          if (ml[2 * i] != -INFINITY) den += fast_exp2(ml[2 * i] - mx) * ml[2 * i + 1];
-#pragma unroll
-        for (int o = 8; o > 0; o >>= 1) den += __shfl_xor(den, o, 16);
-        if (k == 0) {
-          mstat[r][0] = mx;  // -inf only for a sparse row whose list names no visible position
-          mstat[r][1] = den > 0.f ? 1.f / den : 0.f;  // such a row's output is 0
-        }
-      }
-    }
-    __syncthreads();
-
+    // (with several splits each wave merges its own rows below, with running maxima)
     if (kSingle) {
       u32x4 v[4];
 #pragma unroll
@@ -784,58 +762,72 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineArgs a) {
         if (wave + 4 * k < nrows) lds_write16(ol, row_swz16(wave + 4 * k, lane), v[k]);
     }
     // combine: wave w takes rows w, w + 4, w + 8, w + 12 (NR of them); lane = 16-byte chunk of the
-    // row.  The split rows of all NR rows are loaded kCombineLoads at a time (SB splits per row), so
-    // a whole group costs splits * NR / kCombineLoads memory round trips.
+    // row.  The split statistics and partial rows of all NR rows are loaded kCombineLoads at a
+    // time (SB splits per row), and merged with a running maximum per row: a batch whose maximum
+    // exceeds it rescales the row's sum and denominator first.  So a group costs
+    // splits * NR / kCombineLoads memory round trips, with no pass over the statistics before.
     auto combine_rows = [&](auto nr_tag) __attribute__((always_inline)) {
       constexpr int NR = decltype(nr_tag)::value;
       constexpr int SB = kCombineLoads / NR;
       const uint16_t *po[NR];
       const float *ml[NR];
-      float mx[NR], inv[NR], acc[NR][8];
+      float mx[NR], den[NR], acc[NR][8];
 #pragma unroll
       for (int k = 0; k < NR; ++k) {
         const int r = min(wave + 4 * k, nrows - 1);  // rows past nrows repeat a valid one, unwritten
         const int64_t row = int64_t(m0 + r) * a.H + h;
         po[k] = a.part_o + row * a.splits * kC + lane * 8;
         ml[k] = a.part_ml + row * a.splits * 2;
-        mx[k] = mstat[r][0];
-        inv[k] = mstat[r][1];
+        mx[k] = -INFINITY;
+        den[k] = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[k][e] = 0.f;
       }
       for (int i0 = 0; i0 < a.splits; i0 += SB) {
         // splits past the last repeat it with weight 0 (no branches between the loads); the split
-        // maxima and the partial rows are all requested before any is used
+        // statistics and the partial rows are all requested before any is used
         u32x4 v[NR][SB];
-        float mi[NR][SB];
+        f32x2 st[NR][SB];
 #pragma unroll
         for (int k = 0; k < NR; ++k)
 #pragma unroll
-          for (int s = 0; s < SB; ++s) mi[k][s] = ml[k][2 * min(i0 + s, a.splits - 1)];
+          for (int s = 0; s < SB; ++s)
+            st[k][s] = *reinterpret_cast<const f32x2 *>(ml[k] + 2 * min(i0 + s, a.splits - 1));
 #pragma unroll
         for (int k = 0; k < NR; ++k)
 #pragma unroll
           for (int s = 0; s < SB; ++s)
             v[k][s] = *reinterpret_cast<const u32x4 *>(po[k] + int64_t(min(i0 + s, a.splits - 1)) * kC);
 #pragma unroll
-        for (int k = 0; k < NR; ++k)
+        for (int k = 0; k < NR; ++k) {
+          float bm = mx[k];
+#pragma unroll
+          for (int s = 0; s < SB; ++s) bm = fmaxf(bm, i0 + s < a.splits ? st[k][s][0] : -INFINITY);
+          // -inf only while no split of the row has seen a position (a sparse row may never)
+          const float alpha = (mx[k] == -INFINITY) ? 0.f : fast_exp2(mx[k] - bm);
+          mx[k] = bm;
+          den[k] *= alpha;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[k][e] *= alpha;
 #pragma unroll
           for (int s = 0; s < SB; ++s) {
-            const float w = (mi[k][s] == -INFINITY || i0 + s >= a.splits) ? 0.f : fast_exp2(mi[k][s] - mx[k]);
+            const float mi = st[k][s][0];
+            const float w = (mi == -INFINITY || i0 + s >= a.splits) ? 0.f : fast_exp2(mi - bm);
+            den[k] = fmaf(w, st[k][s][1], den[k]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               acc[k][2 * e] = fmaf(w, __uint_as_float(v[k][s][e] << 16), acc[k][2 * e]);
               acc[k][2 * e + 1] = fmaf(w, __uint_as_float(v[k][s][e] & 0xffff0000u), acc[k][2 * e + 1]);
             }
           }
+        }
       }
 #pragma unroll
       for (int k = 0; k < NR; ++k) {
         if (wave + 4 * k >= nrows) continue;
-        const u32x4 pk{pack_bf16x2(acc[k][0] * inv[k], acc[k][1] * inv[k]),
-                       pack_bf16x2(acc[k][2] * inv[k], acc[k][3] * inv[k]),
-                       pack_bf16x2(acc[k][4] * inv[k], acc[k][5] * inv[k]),
-                       pack_bf16x2(acc[k][6] * inv[k], acc[k][7] * inv[k])};
+        const float inv = den[k] > 0.f ? 1.f / den[k] : 0.f;  // 0: a row no split saw (sparse)
+        const u32x4 pk{pack_bf16x2(acc[k][0] * inv, acc[k][1] * inv), pack_bf16x2(acc[k][2] * inv, acc[k][3] * inv),
+                       pack_bf16x2(acc[k][4] * inv, acc[k][5] * inv), pack_bf16x2(acc[k][6] * inv, acc[k][7] * inv)};
         lds_write16(ol, row_swz16(wave + 4 * k, lane), pk);
       }
     };
@@ -871,7 +863,7 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineArgs a) {
         *reinterpret_cast<u32x2 *>(dst + 16 * blk) = v;
       }
     }
-    __syncthreads();  // ol and mstat are rewritten by the next group
+    __syncthreads();  // ol is rewritten by the next group
   }
   wait_vmcnt<0>();  // a workgroup without rows still lets its W_UV DMA land before it exits
 }
