@@ -535,6 +535,44 @@ def test_full_size_sparse(gpu_lib, name, topk):
     check(np.stack([g[b, s_, h] for b, s_, h in rows]), ref, TOL["bf16"], f"{name} topk={topk} sampled rows")
 
 
+# --------------------------------------------------------------------------------- fp32 extensions
+
+@pytest.mark.parametrize("seqlen_q", [1, 2])
+def test_tiny_f32_extensions(gpu_lib, seqlen_q):
+    """The fp32 tiny shape (plain kernels) through every extension entry point, at the fp32
+    tolerance: ragged lengths, paged caches with page sizes 8 and 5, index lists, and naive
+    attention over expanded keys and values."""
+    cfg = ATTN_CONFIGS["tiny_f32"].replace(batch=3, cache_batch=3, seqlen_q=seqlen_q, seed=17)
+    x = make_attn_inputs(cfg)
+    lens = [seqlen_q, 57, cfg.cache_len]
+    t = to_dev(x, cfg)
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to("cuda")
+    out = run_attn_ragged(gpu_lib, cfg, t, lens, path="plain")
+    check(out, oracle_ragged(cfg, x, lens), TOL["f32"], f"f32 ragged S={seqlen_q}")
+    for page_size in (8, 5):
+        kvp, table = to_pages(x["kv_cache"], lens, page_size, 2, 151 + page_size)
+        pep, _ = to_pages(x["pe_cache"], lens, page_size, 2, 151 + page_size)
+        out = run_attn_paged(gpu_lib, cfg, t, f32(kvp), f32(pep), torch.from_numpy(table).to("cuda"), cfg.end_pos,
+                             lens=lens, path="plain")
+        ref = O.absorb_attention_paged(x["q_nope"], x["q_pe"], kvp, pep, x["wkv_b"], table, lens, page_size,
+                                       cfg.softmax_scale, cfg.v_head_dim)
+        check(out, ref, TOL["f32"], f"f32 paged page_size={page_size} S={seqlen_q}")
+    idx = make_lists(cfg, lens, 40, 161, empty=(0, 0))
+    out = run_attn_sparse(gpu_lib, cfg, t, idx, lens, path="plain")
+    ref = O.absorb_attention_sparse(x["q_nope"], x["q_pe"], x["kv_cache"], x["pe_cache"], x["wkv_b"], idx, lens,
+                                    cfg.softmax_scale, cfg.v_head_dim)
+    check(out, ref, TOL["f32"], f"f32 index lists S={seqlen_q}")
+    kn, vn = O.naive_kv(x["kv_cache"], x["wkv_b"], cfg.cache_batch, cfg.cache_len, cfg.n_heads,
+                        cfg.qk_nope_head_dim, cfg.v_head_dim)
+    kh, vh = kn.transpose(2, 0, 1, 3), vn.transpose(2, 0, 1, 3)
+    out = torch.full((cfg.batch, seqlen_q, cfg.n_heads, cfg.v_head_dim), float("nan"), device="cuda")
+    gpu_lib.naive_attn(t["q_nope"], t["q_pe"], f32(kh), f32(vh), t["pe_cache"], cfg.end_pos, cfg.softmax_scale, out,
+                       path="plain")
+    torch.cuda.synchronize()
+    ref = O.attention_over_kv(x["q_nope"], x["q_pe"], kh, vh, x["pe_cache"], cfg.end_pos, cfg.softmax_scale)
+    check(out, ref, TOL["f32"], f"f32 naive attention S={seqlen_q}")
+
+
 # --------------------------------------------------------------------------------- cache append
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
