@@ -255,6 +255,23 @@ int32_t mla_cache_append(const void *c_kv_new, const void *k_pe_new, const void 
                          const mla_attn_shape *shape, int32_t dtype, void *stream);
 
 /*
+ * Cache append into paged caches (the page pools of mla_absorb_attn_paged): the rows of
+ * mla_cache_append, written at row p % page_size of page block_table[b, p / page_size] for each
+ * new token's position p (end_pos - S + s, or seq_lens[b] - S + s clamped to [S, max_seq_len]).
+ * Page ids outside [0, num_pages) are clamped into it, as in mla_absorb_attn_paged.
+ *   block_table  DEVICE int32 [B, max_pages_per_seq], 4-byte aligned
+ *   max_seq_len  1 <= S <= max_seq_len <= max_pages_per_seq * page_size
+ *   shape        B, S, C, R; cache_batch and cache_len are not used
+ * The pools must not overlap each other, the new rows, seq_lens or the table.  Returns MLA_OK or
+ * a negative MLA_ERR_* status.
+ */
+int32_t mla_cache_append_paged(const void *c_kv_new, const void *k_pe_new, const void *rms_w,
+                               float eps, const int32_t *seq_lens, int64_t max_seq_len,
+                               const int32_t *block_table, void *kv_pages, void *pe_pages,
+                               const mla_attn_shape *shape, const mla_paged_cache *paged,
+                               int32_t dtype, void *stream);
+
+/*
  * Attention of the naive route ("Naive vs Absorb Attention Implementations in DeepSeek-V3",
  * section "Naive Path Execution") over keys and values that are already expanded, e.g. by
  * mla_expand_kv of the caches' Bmax*Tmax latent rows in (b, t) order:

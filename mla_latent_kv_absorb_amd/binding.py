@@ -31,7 +31,7 @@ PATHS = {"auto": 0, "plain": 1, "mfma": 2}
 
 EXPORTED = ("mla_absorb_attn", "mla_absorb_attn_ragged", "mla_absorb_attn_paged", "mla_absorb_attn_sparse",
             "mla_absorb_attn_workspace_size", "mla_absorb_attn_paged_workspace_size",
-            "mla_absorb_attn_sparse_workspace_size", "mla_cache_append",
+            "mla_absorb_attn_sparse_workspace_size", "mla_cache_append", "mla_cache_append_paged",
             "mla_expand_kv", "mla_expand_kv_workspace_size", "mla_naive_attn",
             "mla_strerror",
             "mla_last_error", "mla_timing_enable", "mla_timing_collect", "mla_kernel_name")
@@ -92,6 +92,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_absorb_attn_sparse_workspace_size.restype = sz
     lib.mla_cache_append.argtypes = [vp, vp, vp, ctypes.c_float, vp, i64, vp, vp, ctypes.POINTER(AttnShape), i32, vp]
     lib.mla_cache_append.restype = i32
+    lib.mla_cache_append_paged.argtypes = [vp, vp, vp, ctypes.c_float, vp, i64, vp, vp, vp, ctypes.POINTER(AttnShape),
+                                           ctypes.POINTER(PagedCache), i32, vp]
+    lib.mla_cache_append_paged.restype = i32
     lib.mla_naive_attn.argtypes = [vp, vp, vp, vp, vp, i64, ctypes.c_float, vp, ctypes.POINTER(AttnShape), i32, i32, vp]
     lib.mla_naive_attn.restype = i32
     lib.mla_absorb_attn_workspace_size.argtypes = [ctypes.POINTER(AttnShape), i64, i32, ctypes.POINTER(AttnOptions)]
@@ -309,9 +312,12 @@ def absorb_attn(q_nope, q_pe, kv_cache, pe_cache, wkv_b, end_pos: int, softmax_s
                           block_table=block_table, indices=indices)()
 
 
-def cache_append(c_kv_new, k_pe_new, rms_w, eps: float, end_pos: int, kv_cache, pe_cache, *, seq_lens=None):
+def cache_append(c_kv_new, k_pe_new, rms_w, eps: float, end_pos: int, kv_cache, pe_cache, *, seq_lens=None,
+                 block_table=None):
     """Write the new tokens' normalised latent and rope key into the caches in place
-    (mla_cache_append): positions end_pos - S + s, or seq_lens[b] - S + s with seq_lens."""
+    (mla_cache_append): positions end_pos - S + s, or seq_lens[b] - S + s with seq_lens.  With
+    block_table (int32 [B, max_pages_per_seq]), kv_cache and pe_cache are page pools
+    [num_pages, page_size, C / R] and end_pos is the bound of the lengths (mla_cache_append_paged)."""
     import torch
 
     lib = load()
@@ -327,9 +333,19 @@ def cache_append(c_kv_new, k_pe_new, rms_w, eps: float, end_pos: int, kv_cache, 
         if seq_lens.device != c_kv_new.device or seq_lens.dtype != torch.int32 or seq_lens.numel() != B:
             raise ValueError("seq_lens must be an int32 tensor [B] on the tensors' device")
         lens_ptr = seq_lens.data_ptr()
-    _check(lib.mla_cache_append(c_kv_new.data_ptr(), k_pe_new.data_ptr(), rms_w.data_ptr(), eps, lens_ptr, end_pos,
-                                kv_cache.data_ptr(), pe_cache.data_ptr(), ctypes.byref(shape), _dtype_code(c_kv_new),
-                                _stream_handle(c_kv_new.device)))
+    if block_table is None:
+        _check(lib.mla_cache_append(c_kv_new.data_ptr(), k_pe_new.data_ptr(), rms_w.data_ptr(), eps, lens_ptr,
+                                    end_pos, kv_cache.data_ptr(), pe_cache.data_ptr(), ctypes.byref(shape),
+                                    _dtype_code(c_kv_new), _stream_handle(c_kv_new.device)))
+        return
+    if (block_table.device != c_kv_new.device or block_table.dtype != torch.int32 or block_table.dim() != 2
+            or block_table.shape[0] != B or not block_table.is_contiguous()):
+        raise ValueError("block_table must be a contiguous int32 tensor [B, max_pages_per_seq] on the tensors' device")
+    paged = PagedCache(Tmax, Bmax, block_table.shape[1])  # pools: [num_pages, page_size, .]
+    _check(lib.mla_cache_append_paged(c_kv_new.data_ptr(), k_pe_new.data_ptr(), rms_w.data_ptr(), eps, lens_ptr,
+                                      end_pos, block_table.data_ptr(), kv_cache.data_ptr(), pe_cache.data_ptr(),
+                                      ctypes.byref(shape), ctypes.byref(paged), _dtype_code(c_kv_new),
+                                      _stream_handle(c_kv_new.device)))
 
 
 def naive_attn(q_nope, q_pe, k_nope, v, pe_cache, end_pos: int, softmax_scale: float, out=None, *,

@@ -8,9 +8,12 @@
 //                        stored together with q_pe in the attention kernel's operand order
 //   2. attn_kernel       per (sequence, 128-row block, position split): scores against kv_cache
 //                        (512) and pe_cache (64) as one 576-deep contraction, online softmax,
-//                        probability-weighted sum over kv_cache in latent space
-//   3. combine_kernel    combine the split partials (rescaled by exp2(m_i - M)) and project out
-//                        through W_UV[h]
+//                        probability-weighted sum over kv_cache in latent space.  The cache rows
+//                        come from contiguous caches, from page pools through a block table, or
+//                        from the positions a per-token index list names (three instances of one
+//                        template; only the row addressing and the mask differ)
+//   3. combine_kernel    merge the split partials (running maximum, weights exp2(m_i - M)) and
+//                        project out through W_UV[h]
 // Rows are the B*S*H query rows in (b, s, h) order.  Every kv/pe row of a split is read from HBM
 // once per 128-row block and shared through LDS by all of the block's heads.
 #include <algorithm>
@@ -540,13 +543,11 @@ attn_kernel(AttnArgs a) {
   }
   // same wavefront wrote these rows; LDS operations of one wavefront complete in order
   const int rows_here = min(32, a.SH - (first_row + wave * 32));
-  const uint32_t rd_lane = uint32_t((lane & ~15) | ((lane & 15))) * 16;
   for (int r = 0; r < rows_here; ++r) {
     const u32x4 v = lds_read16(stage, uint32_t(r) * (kC * 2) + uint32_t((lane & ~15) | ((lane & 15) ^ (r & 15))) * 16);
     const int64_t idx = (int64_t(b) * a.SH + first_row + wave * 32 + r) * a.splits + split;
     *reinterpret_cast<u32x4 *>(a.part_o + idx * kC + lane * 8) = v;
   }
-  (void)rd_lane;
 }
 
 // ------------------------------------------------------------------------------------------------

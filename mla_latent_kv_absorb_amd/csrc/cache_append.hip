@@ -7,8 +7,10 @@
 //   kv_cache[b, p, :] = c_kv_new[b, s, :] / sqrt(mean(c_kv_new[b, s, :]^2) + eps) * rms_w
 //   pe_cache[b, p, :] = k_pe_new[b, s, :]
 //
-// with p = end_pos - S + s, or seq_lens[b] - S + s for a ragged batch.  One wavefront per token;
-// fp32 arithmetic, stores rounded to the cache's element type.
+// with p = end_pos - S + s, or seq_lens[b] - S + s for a ragged batch.  With paged caches the row
+// of position p is row p % page_size of the sequence's page for p (the block table's id, clamped
+// into the pool).  One wavefront per token; fp32 arithmetic, stores rounded to the cache's
+// element type.
 #include "common.h"
 #include "launch.h"
 #include "../../include/mla_absorb.h"
@@ -31,6 +33,12 @@ cache_append_kernel(const T *__restrict__ c_kv_new, const T *__restrict__ k_pe_n
     if (end_pos > a.end_pos) end_pos = a.end_pos;
   }
   const int64_t p = end_pos - a.S + s;
+  int64_t row = b * a.Tmax + p;  // destination row of kv_cache / pe_cache
+  if (a.page_size > 0) {
+    int64_t pg = a.block_table[b * a.max_pages + p / a.page_size];
+    pg = pg < 0 ? 0 : (pg >= a.num_pages ? a.num_pages - 1 : pg);
+    row = pg * a.page_size + p % a.page_size;
+  }
   const T *x = c_kv_new + tok * a.C;
   float ss = 0.f;
   for (int64_t c = lane; c < a.C; c += 64) {
@@ -38,10 +46,10 @@ cache_append_kernel(const T *__restrict__ c_kv_new, const T *__restrict__ k_pe_n
     ss = fmaf(v, v, ss);
   }
   const float inv = 1.f / sqrtf(wave_sum(ss) / float(a.C) + a.eps);
-  T *kv = kv_cache + (b * a.Tmax + p) * a.C;
+  T *kv = kv_cache + row * a.C;
   for (int64_t c = lane; c < a.C; c += 64) Elem<T>::store(kv, c, Elem<T>::load(x, c) * inv * Elem<T>::load(rms_w, c));
   const T *kp = k_pe_new + tok * a.R;
-  T *pe = pe_cache + (b * a.Tmax + p) * a.R;
+  T *pe = pe_cache + row * a.R;
   for (int64_t r = lane; r < a.R; r += 64) pe[r] = kp[r];
 }
 

@@ -60,7 +60,11 @@ struct AppendCall {
   float eps;
   int32_t dtype;
   const void *c_kv_new, *k_pe_new, *rms_w;
-  void *kv_cache, *pe_cache;
+  void *kv_cache, *pe_cache;  // [Bmax, Tmax, C / R], or page pools [num_pages, page_size, C / R]
+  // paged caches (page_size > 0): position p of sequence b is row p % page_size of page
+  // block_table[b * max_pages + p / page_size] (clamped into [0, num_pages))
+  const int32_t *block_table;
+  int64_t page_size, num_pages, max_pages;
   hipStream_t stream;
 };
 

@@ -400,15 +400,31 @@ int32_t mla_expand_kv(const void *c_kv, const void *rms_w, const void *wkv_b, vo
 
 }  // extern "C"
 
-extern "C" {
+namespace {
 
-int32_t mla_cache_append(const void *c_kv_new, const void *k_pe_new, const void *rms_w, float eps,
-                         const int32_t *seq_lens, int64_t end_pos, void *kv_cache, void *pe_cache,
-                         const mla_attn_shape *shape, int32_t dtype, void *stream) {
-  clear_error();
+// The body of mla_cache_append and mla_cache_append_paged (block_table and paged null for
+// contiguous caches).
+int32_t cache_append_call(const void *c_kv_new, const void *k_pe_new, const void *rms_w, float eps,
+                          const int32_t *seq_lens, int64_t end_pos, const int32_t *block_table,
+                          const mla_paged_cache *paged, void *kv_cache, void *pe_cache,
+                          const mla_attn_shape *shape, int32_t dtype, void *stream) {
   if (!shape) return fail(MLA_ERR_NULL, "shape is NULL");
   if (dtype != MLA_DTYPE_F32 && dtype != MLA_DTYPE_BF16) return fail(MLA_ERR_DTYPE, "unknown dtype %d", dtype);
-  const mla_attn_shape &s = *shape;
+  mla_attn_shape s = *shape;
+  if (paged) {
+    const mla_paged_cache &pg = *paged;
+    if (pg.page_size < 1 || pg.page_size > (int64_t(1) << 20))
+      return fail(MLA_ERR_SHAPE, "page_size = %lld outside [1, 1048576]", (long long)pg.page_size);
+    if (pg.num_pages < 1 || pg.num_pages > (int64_t(1) << 31) - 1)
+      return fail(MLA_ERR_SHAPE, "num_pages = %lld outside [1, 2^31 - 1]", (long long)pg.num_pages);
+    if (pg.max_pages_per_seq < 1 || pg.max_pages_per_seq > (int64_t(1) << 31) - 1)
+      return fail(MLA_ERR_SHAPE, "max_pages_per_seq = %lld outside [1, 2^31 - 1]", (long long)pg.max_pages_per_seq);
+    if (s.batch > 0 && s.batch * pg.max_pages_per_seq > (int64_t(1) << 31) - 1)
+      return fail(MLA_ERR_SHAPE, "batch * max_pages_per_seq is too large");
+    if (pg.num_pages * pg.page_size > (int64_t(1) << 40)) return fail(MLA_ERR_SHAPE, "num_pages * page_size is too large");
+    s.cache_batch = s.batch;
+    s.cache_len = std::min<int64_t>(pg.max_pages_per_seq * pg.page_size, int64_t(1) << 31);
+  }
   const int64_t dims[] = {s.batch, s.seqlen_q, s.kv_lora_rank, s.qk_rope_head_dim, s.cache_batch, s.cache_len};
   const char *dnames[] = {"batch", "seqlen_q", "kv_lora_rank", "qk_rope_head_dim", "cache_batch", "cache_len"};
   for (int i = 0; i < 6; ++i)
@@ -439,8 +455,9 @@ int32_t mla_cache_append(const void *c_kv_new, const void *k_pe_new, const void 
   const size_t toks = size_t(s.batch * s.seqlen_q);
   const size_t in_bytes[] = {toks * size_t(s.kv_lora_rank) * es, toks * size_t(s.qk_rope_head_dim) * es,
                              size_t(s.kv_lora_rank) * es};
-  const size_t kv_bytes = size_t(s.cache_batch * s.cache_len * s.kv_lora_rank) * es;
-  const size_t pe_bytes = size_t(s.cache_batch * s.cache_len * s.qk_rope_head_dim) * es;
+  const size_t cache_rows = paged ? size_t(paged->num_pages * paged->page_size) : size_t(s.cache_batch * s.cache_len);
+  const size_t kv_bytes = cache_rows * size_t(s.kv_lora_rank) * es;
+  const size_t pe_bytes = cache_rows * size_t(s.qk_rope_head_dim) * es;
   if (overlaps(kv_cache, kv_bytes, pe_cache, pe_bytes)) return fail(MLA_ERR_SHAPE, "kv_cache overlaps pe_cache");
   for (int i = 0; i < 3; ++i) {
     if (overlaps(kv_cache, kv_bytes, ptrs[i], in_bytes[i])) return fail(MLA_ERR_SHAPE, "kv_cache overlaps %s", names[i]);
@@ -449,14 +466,47 @@ int32_t mla_cache_append(const void *c_kv_new, const void *k_pe_new, const void 
   if (seq_lens && (overlaps(kv_cache, kv_bytes, seq_lens, size_t(s.batch) * 4) ||
                    overlaps(pe_cache, pe_bytes, seq_lens, size_t(s.batch) * 4)))
     return fail(MLA_ERR_SHAPE, "a cache overlaps seq_lens");
+  if (block_table) {
+    const size_t tb = size_t(s.batch * paged->max_pages_per_seq) * 4;
+    if (overlaps(kv_cache, kv_bytes, block_table, tb) || overlaps(pe_cache, pe_bytes, block_table, tb))
+      return fail(MLA_ERR_SHAPE, "a cache overlaps block_table");
+  }
   mla::AppendCall a{};
   a.B = s.batch; a.S = s.seqlen_q; a.C = s.kv_lora_rank; a.R = s.qk_rope_head_dim; a.Tmax = s.cache_len;
   a.end_pos = end_pos; a.seq_lens = seq_lens; a.eps = eps; a.dtype = dtype;
   a.c_kv_new = c_kv_new; a.k_pe_new = k_pe_new; a.rms_w = rms_w; a.kv_cache = kv_cache; a.pe_cache = pe_cache;
   a.stream = static_cast<hipStream_t>(stream);
+  if (paged) {
+    a.block_table = block_table;
+    a.page_size = paged->page_size; a.num_pages = paged->num_pages; a.max_pages = paged->max_pages_per_seq;
+  }
   hipError_t e = mla::cache_append(a);
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t mla_cache_append(const void *c_kv_new, const void *k_pe_new, const void *rms_w, float eps,
+                         const int32_t *seq_lens, int64_t end_pos, void *kv_cache, void *pe_cache,
+                         const mla_attn_shape *shape, int32_t dtype, void *stream) {
+  clear_error();
+  return cache_append_call(c_kv_new, k_pe_new, rms_w, eps, seq_lens, end_pos, nullptr, nullptr, kv_cache, pe_cache,
+                           shape, dtype, stream);
+}
+
+int32_t mla_cache_append_paged(const void *c_kv_new, const void *k_pe_new, const void *rms_w, float eps,
+                               const int32_t *seq_lens, int64_t max_seq_len, const int32_t *block_table,
+                               void *kv_pages, void *pe_pages, const mla_attn_shape *shape,
+                               const mla_paged_cache *paged, int32_t dtype, void *stream) {
+  clear_error();
+  if (!paged) return fail(MLA_ERR_NULL, "paged is NULL");
+  if (!block_table) return fail(MLA_ERR_NULL, "block_table is NULL");
+  if (reinterpret_cast<uintptr_t>(block_table) & 3u) return fail(MLA_ERR_ALIGN, "block_table is not 4-byte aligned");
+  return cache_append_call(c_kv_new, k_pe_new, rms_w, eps, seq_lens, max_seq_len, block_table, paged, kv_pages,
+                           pe_pages, shape, dtype, stream);
 }
 
 }  // extern "C"

@@ -70,6 +70,7 @@ __all__ = [
     "rms_norm",
     "expand_kv",
     "cache_append",
+    "cache_append_paged",
 ]
 
 
@@ -404,4 +405,24 @@ def cache_append(c_kv_new, k_pe_new, rms_w, eps: float, kv_cache, pe_cache, end_
         for s in range(S):
             kv[b, length - S + s] = n[b, s]
             pe[b, length - S + s] = kp[b, s]
+    return kv, pe
+
+
+def cache_append_paged(c_kv_new, k_pe_new, rms_w, eps: float, kv_pages, pe_pages, block_table, page_size: int,
+                       end_pos: int = None, seq_lens=None, dtype=np.float64):
+    """cache_append into page pools (the paged layout of absorb_attention_paged): token s of
+    sequence b goes to position p = end_pos - S + s (or seq_lens[b] - S + s), i.e. row
+    p % page_size of page block_table[b, p // page_size].  Returns new pools."""
+    kv, pe = _as(kv_pages, dtype).copy(), _as(pe_pages, dtype).copy()
+    B, S = c_kv_new.shape[0], c_kv_new.shape[1]
+    n = rms_norm(c_kv_new, rms_w, eps, dtype)
+    kp = _as(k_pe_new, dtype)
+    table = np.asarray(block_table)
+    for b in range(B):
+        length = end_pos if seq_lens is None else int(seq_lens[b])
+        for s in range(S):
+            p = length - S + s
+            page, slot = table[b, p // page_size], p % page_size
+            kv[page, slot] = n[b, s]
+            pe[page, slot] = kp[b, s]
     return kv, pe

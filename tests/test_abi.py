@@ -338,3 +338,30 @@ def test_sparse_workspace_plan(lib):
     few = B.absorb_attn_sparse_workspace_size(one, 65536, 256, B.MLA_DTYPE_BF16, path="mfma")
     many = B.absorb_attn_sparse_workspace_size(one, 65536, 65536, B.MLA_DTYPE_BF16, path="mfma")
     assert many > few
+
+
+def call_append_paged(lib, s, max_len=4096, ptrs=None, bt=P[6], lens=None, pg=None, eps=1e-6):
+    p = list(P[:5]) if ptrs is None else ptrs
+    pg = B.PagedCache(64, 256, 64) if pg is None else pg
+    return lib.mla_cache_append_paged(p[0], p[1], p[2], eps, lens, max_len, bt, p[3], p[4], ctypes.byref(s),
+                                      ctypes.byref(pg), B.MLA_DTYPE_BF16, None)
+
+
+def test_cache_append_paged_argument_errors(lib):
+    s = shape()
+    assert lib.mla_cache_append_paged(*P[:3], 1e-6, None, 4096, P[6], P[3], P[4], ctypes.byref(s), None,
+                                      B.MLA_DTYPE_BF16, None) == B.MLA_ERR_NULL
+    assert call_append_paged(lib, s, bt=None) == B.MLA_ERR_NULL
+    assert call_append_paged(lib, s, bt=P[6] + 2) == B.MLA_ERR_ALIGN
+    assert call_append_paged(lib, s, pg=B.PagedCache(0, 256, 64)) == B.MLA_ERR_SHAPE
+    assert call_append_paged(lib, s, pg=B.PagedCache(64, 0, 64)) == B.MLA_ERR_SHAPE
+    assert call_append_paged(lib, s, max_len=4097) == B.MLA_ERR_RANGE
+    assert call_append_paged(lib, shape(seqlen_q=9), max_len=8) == B.MLA_ERR_RANGE
+    assert call_append_paged(lib, s, eps=-1.0) == B.MLA_ERR_SHAPE
+    # the pools must not overlap the table or each other
+    assert call_append_paged(lib, s, bt=P[3] + 64) == B.MLA_ERR_SHAPE
+    assert call_append_paged(lib, s, ptrs=[P[0], P[1], P[2], P[3], P[3] + 4096]) == B.MLA_ERR_SHAPE
+    for i in range(5):
+        p = list(P[:5])
+        p[i] = None
+        assert call_append_paged(lib, s, ptrs=p) == B.MLA_ERR_NULL

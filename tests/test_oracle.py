@@ -448,6 +448,33 @@ def pin_sparse():
     return worst
 
 
+def pin_append_paged():
+    """Appending into page pools equals appending into the contiguous cache the pages spell out
+    (a different code path): gathering each sequence's rows after the paged append gives the
+    contiguous append's rows; rows of pages no sequence owns are untouched."""
+    rng = np.random.default_rng(91)
+    worst = 0.0
+    for page_size, ragged in ((4, False), (3, True)):
+        B, S, C, R, T, eps = 3, 3, 8, 4, 14, 1e-3
+        lens = [T, 5, 9] if ragged else None
+        x, kp = rng.normal(size=(B, S, C)), rng.normal(size=(B, S, R))
+        w = 1.0 + 0.1 * rng.normal(size=C)
+        kv0, pe0 = rng.normal(size=(B, T, C)), rng.normal(size=(B, T, R))
+        full = [T] * B
+        num_pages = B * -(-T // page_size) + 3
+        kvp, table = scatter_to_pages(kv0, full, page_size, num_pages, rng)
+        pep, _ = scatter_to_pages(pe0, full, page_size, num_pages, rng, table)
+        kva, pea = O.cache_append_paged(x, kp, w, eps, kvp, pep, table, page_size, end_pos=T, seq_lens=lens)
+        kvc, pec = O.cache_append(x, kp, w, eps, kv0, pe0, end_pos=T, seq_lens=lens)
+        for b in range(B):
+            worst = max(worst, float(np.abs(O.paged_gather(kva, table, T, b, page_size) - kvc[b]).max()),
+                        float(np.abs(O.paged_gather(pea, table, T, b, page_size) - pec[b]).max()))
+        owned = np.zeros(num_pages, bool)
+        owned[np.asarray(table)[:, :-(-T // page_size)].ravel()] = True
+        worst = max(worst, float(np.abs(kva[~owned] - kvp[~owned]).max()), float(np.abs(pea[~owned] - pep[~owned]).max()))
+    return worst
+
+
 PINS = {
     "naive_equals_absorb": (pin_naive_equals_absorb, 1e-12),
     "golden": (pin_golden, 1e-12),
@@ -467,6 +494,7 @@ PINS = {
     "attention_over_kv": (pin_attention_over_kv, 1e-12),
     "paged": (pin_paged, 1e-12),
     "sparse": (pin_sparse, 1e-12),
+    "append_paged": (pin_append_paged, 1e-12),
 }
 
 
@@ -618,6 +646,15 @@ def _sparse_drops_repeats(q_nope, q_pe, kv_cache, pe_cache, wkv_b, indices, seq_
     return _orig_sparse(q_nope, q_pe, kv_cache, pe_cache, wkv_b, idx, seq_lens, *a, **kw)
 
 
+_orig_append_paged = O.cache_append_paged
+
+
+def _append_paged_next_page(c_kv_new, k_pe_new, rms_w, eps, kv_pages, pe_pages, block_table, page_size, **kw):
+    # page index read one table entry too far
+    shifted = np.roll(np.asarray(block_table), -1, axis=1)
+    return _orig_append_paged(c_kv_new, k_pe_new, rms_w, eps, kv_pages, pe_pages, shifted, page_size, **kw)
+
+
 def _as_copy(x, dtype):
     return np.array(x, dtype)
 
@@ -637,6 +674,7 @@ MUTATIONS = {
     "paged_slot_reversed": ("paged_gather", _gather_slot_from_page_end),
     "sparse_ignores_causal_bound": ("absorb_attention_sparse", _sparse_ignores_causal_bound),
     "sparse_drops_repeats": ("absorb_attention_sparse", _sparse_drops_repeats),
+    "append_paged_next_page": ("cache_append_paged", _append_paged_next_page),
 }
 
 

@@ -624,6 +624,65 @@ def test_append_then_attend(gpu_lib):
     check(out, ref, TOL["bf16"], "append + attend")
 
 
+@pytest.mark.parametrize("dtype,page_size,ragged", [("f32", 16, False), ("bf16", 64, True), ("bf16", 5, True)])
+def test_cache_append_paged(gpu_lib, dtype, page_size, ragged):
+    """Rows appended into page pools match the oracle's; every other pool row is unchanged."""
+    B, S, C, R, T, eps = 3, 4, 512, 64, 192, 1e-6
+    rng = np.random.default_rng(45)
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    cast = (lambda a: a.astype(np.float32)) if dtype == "f32" else (lambda a: round_bf16(a))
+    x, kp = cast(rng.normal(size=(B, S, C))), cast(rng.normal(size=(B, S, R)))
+    w = cast(1.0 + 0.14 * rng.normal(size=C))
+    npp = -(-T // page_size)
+    num_pages = B * npp + 4
+    table = rng.permutation(num_pages)[:B * npp].reshape(B, npp).astype(np.int32)
+    kv0, pe0 = cast(rng.normal(size=(num_pages, page_size, C))), cast(rng.normal(size=(num_pages, page_size, R)))
+    lens = [S, 101, T] if ragged else None
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(tdt)
+    kv, pe = dev(kv0), dev(pe0)
+    seq = torch.tensor(lens, dtype=torch.int32, device="cuda") if ragged else None
+    gpu_lib.cache_append(dev(x), dev(kp), dev(w), eps, T, kv, pe, seq_lens=seq,
+                         block_table=torch.from_numpy(table).to("cuda"))
+    torch.cuda.synchronize()
+    kr, pr = O.cache_append_paged(x, kp, w, eps, kv0, pe0, table, page_size, end_pos=T, seq_lens=lens)
+    new = np.zeros((num_pages, page_size), bool)
+    for b in range(B):
+        n = lens[b] if ragged else T
+        for p_ in range(n - S, n):
+            new[table[b, p_ // page_size], p_ % page_size] = True
+    g_kv, g_pe = kv.float().cpu().numpy(), pe.float().cpu().numpy()
+    assert np.array_equal(g_kv[~new], kv0[~new]) and np.array_equal(g_pe[~new], pe0[~new]), "untouched rows changed"
+    assert np.array_equal(g_pe[new], pr[new].astype(np.float32)), "rope rows are copied exactly"
+    check(g_kv[new].astype(np.float64), kr[new], TOL[dtype], f"paged append {dtype} page={page_size} latent rows")
+
+
+def test_append_then_attend_paged(gpu_lib):
+    """One decode step over paged caches: append each sequence's new token, then paged attention."""
+    cfg = dsv3_small(batch=3, cache_batch=3, end_pos=200, cache_len=256)
+    x = make_attn_inputs(cfg)
+    lens = [200, 77, 130]
+    kvp, table = to_pages(x["kv_cache"], lens, 64, 2, 47)
+    pep, _ = to_pages(x["pe_cache"], lens, 64, 2, 47)
+    rng = np.random.default_rng(49)
+    c_new = round_bf16(rng.normal(size=(cfg.batch, 1, cfg.kv_lora_rank)))
+    kp_new = round_bf16(rng.normal(size=(cfg.batch, 1, cfg.qk_rope_head_dim)))
+    w = round_bf16(1.0 + 0.14 * rng.normal(size=cfg.kv_lora_rank))
+    t = to_dev(x, cfg)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to("cuda").to(torch.bfloat16)
+    kv_d, pe_d, tb = dev(kvp), dev(pep), torch.from_numpy(table).to("cuda")
+    seq = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    gpu_lib.cache_append(dev(c_new), dev(kp_new), dev(w), 1e-6, cfg.end_pos, kv_d, pe_d, seq_lens=seq, block_table=tb)
+    out = run_attn_paged(gpu_lib, cfg, t, kv_d, pe_d, tb, cfg.end_pos, lens=lens, path="mfma")
+    kva, pea = O.cache_append_paged(c_new, kp_new, w, 1e-6, kvp, pep, table, 64, end_pos=cfg.end_pos, seq_lens=lens)
+    # the GPU attends to the bf16-rounded appended rows; the oracle rounds them the same way
+    for b, n in enumerate(lens):
+        page, slot = table[b, (n - 1) // 64], (n - 1) % 64
+        kva[page, slot] = round_bf16(kva[page, slot])
+    ref = O.absorb_attention_paged(x["q_nope"], x["q_pe"], kva, pea, x["wkv_b"], table, lens, 64, cfg.softmax_scale,
+                                   cfg.v_head_dim)
+    check(out, ref, TOL["bf16"], "paged append + attend")
+
+
 # --------------------------------------------------------------------------------- naive route
 
 def head_major_kv(x, cfg):
