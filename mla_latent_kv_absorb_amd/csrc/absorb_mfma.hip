@@ -142,6 +142,17 @@ attn_kernel(AttnArgs a) {
   const int wg_full = __builtin_amdgcn_readfirstlane(kSparse ? t_split_end
                                                              : min(t_split_end, end_pos - a.S + first_row / a.H + 1));
   const int ntiles = __builtin_amdgcn_readfirstlane(wg_end > t_begin ? (wg_end - t_begin + kTile - 1) / kTile : 0);
+  if (ntiles == 0) {
+    // nothing of this split is visible to the workgroup's rows (a short sequence of a ragged
+    // batch): only the statistics of an empty partial; the combine never reads its o rows.  (With
+    // a single split every workgroup has a tile, so this needs the multi-split combine.)
+    if (row_ok && g == 0) {
+      const int64_t idx = grow * a.splits + split;
+      a.part_ml[2 * idx] = -INFINITY;
+      a.part_ml[2 * idx + 1] = 0.f;
+    }
+    return;
+  }
 
   // DMA geometry.  kv: wave w moves tile rows 8w..8w+7, one 1 KB row per instruction; lane l owns
   // chunk position l and fetches source chunk swz_chunk(l, row).  pe: wave w moves rows
@@ -813,12 +824,17 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineArgs a) {
 #pragma unroll
           for (int s = 0; s < SB; ++s) {
             const float mi = st[k][s][0];
-            const float w = (mi == -INFINITY || i0 + s >= a.splits) ? 0.f : fast_exp2(mi - bm);
+            const bool used = mi != -INFINITY && i0 + s < a.splits;
+            const float w = used ? fast_exp2(mi - bm) : 0.f;
+            // an empty split's o row was never written: zero its bits rather than multiply
+            // whatever the memory holds (possibly NaN) by 0
+            const uint32_t keep = used ? 0xffffffffu : 0u;
             den[k] = fmaf(w, st[k][s][1], den[k]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              acc[k][2 * e] = fmaf(w, __uint_as_float(v[k][s][e] << 16), acc[k][2 * e]);
-              acc[k][2 * e + 1] = fmaf(w, __uint_as_float(v[k][s][e] & 0xffff0000u), acc[k][2 * e + 1]);
+              const uint32_t x = v[k][s][e] & keep;
+              acc[k][2 * e] = fmaf(w, __uint_as_float(x << 16), acc[k][2 * e]);
+              acc[k][2 * e + 1] = fmaf(w, __uint_as_float(x & 0xffff0000u), acc[k][2 * e + 1]);
             }
           }
         }

@@ -264,6 +264,26 @@ def test_ragged_small(gpu_lib, path, seqlen_q, lens):
     check(out, oracle_ragged(cfg, x, lens), TOL["bf16"], f"ragged S={seqlen_q} lens={lens} {path}")
 
 
+@pytest.mark.parametrize("splits", [0, 8, 24])
+def test_ragged_empty_splits_nan_workspace(gpu_lib, splits):
+    """Splits past a short sequence's end write only their statistics; the combine must not read
+    their partial rows.  The workspace starts as all-ones bytes (NaN in bf16 and fp32)."""
+    lens = [1, 40, 700, 999, 2]
+    cfg = dsv3_small(batch=len(lens), cache_batch=len(lens), end_pos=999, cache_len=1024)
+    x = make_attn_inputs(cfg)
+    t = to_dev(x, cfg)
+    shape = gpu_lib.attn_shape(t["q_nope"], t["q_pe"], t["kv_cache"], t["wkv_b"])
+    need = gpu_lib.absorb_attn_workspace_size(shape, cfg.end_pos, gpu_lib.MLA_DTYPE_BF16, splits, "mfma")
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    out = torch.full((cfg.batch, cfg.seqlen_q, cfg.n_heads, cfg.v_head_dim), float("nan"), dtype=torch.bfloat16,
+                     device="cuda")
+    seq = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    gpu_lib.absorb_attn(t["q_nope"], t["q_pe"], t["kv_cache"], t["pe_cache"], t["wkv_b"], cfg.end_pos,
+                        cfg.softmax_scale, out, num_splits=splits, path="mfma", workspace=ws, seq_lens=seq)
+    torch.cuda.synchronize()
+    check(out, oracle_ragged(cfg, x, lens), TOL["bf16"], f"ragged, NaN-filled workspace, splits={splits}")
+
+
 @pytest.mark.parametrize("splits", [1, 3, 16])
 def test_ragged_forced_splits(gpu_lib, splits):
     lens = [1, 700, 130, 999]
