@@ -145,6 +145,8 @@ def time_attn(cfg, steps, warmup, sets, torch, binding, seed=1, timed_kernels=0b
         need = binding.absorb_attn_paged_workspace_size(shape, cfg.end_pos, paged, binding.MLA_DTYPE_BF16)
     elif topk:
         need = binding.absorb_attn_sparse_workspace_size(shape, cfg.end_pos, topk, binding.MLA_DTYPE_BF16)
+    elif lens is not None:
+        need = binding.absorb_attn_ragged_workspace_size(shape, cfg.end_pos, binding.MLA_DTYPE_BF16)
     else:
         need = binding.absorb_attn_workspace_size(shape, cfg.end_pos, binding.MLA_DTYPE_BF16)
     ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")

@@ -128,12 +128,19 @@ int32_t mla_absorb_attn(const void *q_nope, const void *q_pe, const void *kv_cac
  *                that range is clamped into it, so no call ever reads a cache position at or past
  *                max_seq_len (such a sequence's output is then that of the clamped length).
  *   max_seq_len  upper bound of the lengths; 1 <= S <= max_seq_len <= Tmax.  It plays the role
- *                of end_pos for validation, split planning and the workspace size: use
- *                mla_absorb_attn_workspace_size(shape, max_seq_len, ...).
+ *                of end_pos for validation and split planning.
+ * workspace: mla_absorb_attn_ragged_workspace_size(shape, max_seq_len, ...) bytes.  With an
+ * automatic split count the matrix-core kernels balance the batch on the device: every sequence
+ * is cut into chunks of about one common length (a multiple of 32) chosen from the lengths, and
+ * each workgroup takes one chunk, so long sequences take more workgroups than short ones (up to
+ * four times the splits of a uniform batch) and the workgroups about equal work.
  * Every other argument, the layouts and the error behaviour are those of mla_absorb_attn;
  * out, workspace and seq_lens must not overlap.  Returns MLA_OK or a negative MLA_ERR_* status
  * (MLA_ERR_NULL / MLA_ERR_ALIGN for seq_lens).
  */
+size_t mla_absorb_attn_ragged_workspace_size(const mla_attn_shape *shape, int64_t max_seq_len,
+                                             int32_t dtype, const mla_attn_options *options);
+
 int32_t mla_absorb_attn_ragged(const void *q_nope, const void *q_pe, const void *kv_cache,
                                const void *pe_cache, const void *wkv_b, const int32_t *seq_lens,
                                int64_t max_seq_len, float softmax_scale, void *out,
@@ -165,7 +172,8 @@ typedef struct mla_paged_cache {
  * Bytes of device workspace mla_absorb_attn_paged needs for these arguments (0 if none, and 0
  * with mla_last_error set when they are invalid).  The split plan of a paged call may differ from
  * that of a contiguous one (the matrix-core kernels start every split on a 32-position boundary
- * and bound the pages one workgroup reads), so the size has its own query.
+ * and bound the pages one workgroup reads), so the size has its own query; it covers the balanced
+ * plan of a call with seq_lens (see mla_absorb_attn_ragged), which a call without needs less of.
  */
 size_t mla_absorb_attn_paged_workspace_size(const mla_attn_shape *shape, int64_t max_seq_len,
                                             const mla_paged_cache *paged, int32_t dtype,

@@ -30,7 +30,8 @@ MLA_DTYPE_BF16 = 1
 PATHS = {"auto": 0, "plain": 1, "mfma": 2}
 
 EXPORTED = ("mla_absorb_attn", "mla_absorb_attn_ragged", "mla_absorb_attn_paged", "mla_absorb_attn_sparse",
-            "mla_absorb_attn_workspace_size", "mla_absorb_attn_paged_workspace_size",
+            "mla_absorb_attn_workspace_size", "mla_absorb_attn_ragged_workspace_size",
+            "mla_absorb_attn_paged_workspace_size",
             "mla_absorb_attn_sparse_workspace_size", "mla_cache_append", "mla_cache_append_paged",
             "mla_expand_kv", "mla_expand_kv_workspace_size", "mla_naive_attn",
             "mla_strerror",
@@ -99,6 +100,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_naive_attn.restype = i32
     lib.mla_absorb_attn_workspace_size.argtypes = [ctypes.POINTER(AttnShape), i64, i32, ctypes.POINTER(AttnOptions)]
     lib.mla_absorb_attn_workspace_size.restype = sz
+    lib.mla_absorb_attn_ragged_workspace_size.argtypes = [ctypes.POINTER(AttnShape), i64, i32,
+                                                          ctypes.POINTER(AttnOptions)]
+    lib.mla_absorb_attn_ragged_workspace_size.restype = sz
     lib.mla_expand_kv.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float, i32, i32, vp, sz, vp]
     lib.mla_expand_kv.restype = i32
     lib.mla_expand_kv_workspace_size.argtypes = [i64, i64, i64, i64, i64, i32, i32]
@@ -196,6 +200,16 @@ def absorb_attn_workspace_size(shape: AttnShape, end_pos: int, dtype: int, num_s
     return int(n)
 
 
+def absorb_attn_ragged_workspace_size(shape: AttnShape, max_seq_len: int, dtype: int, num_splits: int = 0,
+                                      path: str = "auto") -> int:
+    lib = load()
+    opt = AttnOptions(num_splits, PATHS[path])
+    n = lib.mla_absorb_attn_ragged_workspace_size(ctypes.byref(shape), max_seq_len, dtype, ctypes.byref(opt))
+    if n == 0 and last_error():
+        raise MLAError(MLA_ERR_SHAPE, last_error())
+    return int(n)
+
+
 def absorb_attn_paged_workspace_size(shape: AttnShape, max_seq_len: int, paged: PagedCache, dtype: int,
                                      num_splits: int = 0, path: str = "auto") -> int:
     lib = load()
@@ -266,6 +280,8 @@ class AbsorbAttnCall:
             if indices.dim() != 3 or tuple(indices.shape[:2]) != (shape.batch, shape.seqlen_q):
                 raise ValueError("indices must be [batch, seqlen_q, topk]")
             need = absorb_attn_sparse_workspace_size(shape, end_pos, indices.shape[2], dt, num_splits, path)
+        elif paged is None and seq_lens is not None:
+            need = absorb_attn_ragged_workspace_size(shape, end_pos, dt, num_splits, path)
         elif paged is None:
             need = absorb_attn_workspace_size(shape, end_pos, dt, num_splits, path)
         else:

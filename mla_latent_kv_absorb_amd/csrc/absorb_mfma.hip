@@ -86,7 +86,80 @@ struct AttnArgs {
   // index lists [B, S, topk]: token (b, s) attends to the positions its list names
   const int32_t *indices;
   int32_t topk;
+  // balanced ragged plan (bal_target > 0): sequence b's positions are cut into n_b chunks of one
+  // common length (see balanced_chunk), long sequences into more of them; splits is the most
+  // chunks a sequence may take, bal_target the number of workgroups per row block (one per chunk,
+  // chunks packed in sequence order), and bal_nb [B * S] receives n_b for each query row of
+  // sequence b (b * S + s), for the combine
+  int32_t B, bal_target, bal_cap;  // bal_cap: longest chunk the row source allows (paged caches)
+  int32_t *bal_nb;
 };
+
+// Chunk length of a sequence of len positions in a balanced plan whose common chunk length is L:
+// len / n rounded up to 32 positions, for n = ceil(len / L) chunks, or more where the row source
+// caps a chunk at cap positions, at most smax.
+__device__ __forceinline__ int bal_len(int len, int L, int smax, int cap) {
+  const int n = min(smax, max((len + L - 1) / L, len <= cap ? 1 : (len - 1) / cap + 1));
+  return ((len + n - 1) / n + 31) & ~31;
+}
+// Chunks of that sequence: every one starts before len (rounding can leave fewer than n).
+__device__ __forceinline__ int bal_chunks(int len, int L, int smax, int cap) {
+  const int sl = bal_len(len, L, smax, cap);
+  return (len + sl - 1) / sl;
+}
+
+// Chunk length of a balanced ragged plan: the smallest multiple L of 32, at least 256 (or the
+// bound), with sum_b bal_chunks(len_b, L) <= target (len_b the clamped lengths), found by a binary
+// search in which every step is one wave-wide count.  Every wave of every workgroup computes it
+// from the same inputs and gets the same L.  L = bound always qualifies: it gives each sequence
+// one chunk, or ceil(len / cap) where the row source caps a chunk, and the plan's target covers
+// B of the latter.
+__device__ int balanced_chunk(const int32_t *lens, int len0, int B, int S, int bound, int smax, int cap, int target,
+                              int lane) {
+  auto count = [&](int L) {
+    int c = lane < B ? bal_chunks(len0, L, smax, cap) : 0;
+    for (int i = lane + 64; i < B; i += 64) c += bal_chunks(min(max(lens[i], S), bound), L, smax, cap);
+    for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
+    return __builtin_amdgcn_readfirstlane(c);
+  };
+  // in units of 32 positions; chunks of at least 256 positions where sequences allow: below that
+  // a workgroup's fixed start and end (query and first tiles in, partial rows out) outweigh its
+  // share of the positions, and every extra chunk adds a partial row to the combine
+  int hi = (bound + 31) / 32, lo = min(8, hi);
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (count(32 * mid) <= target) hi = mid;
+    else lo = mid + 1;
+  }
+  return 32 * lo;
+}
+
+// Sequence and chunk of chunk rank r (chunks counted in sequence order), via a wave-wide prefix sum
+// of the sequences' chunk counts, 64 sequences at a time.  False if r is past the last chunk.
+__device__ bool balanced_find(const int32_t *lens, int len0, int B, int S, int bound, int smax, int cap, int L,
+                              int r, int lane, int &b_out, int &c_out) {
+  int base = 0;
+  for (int j0 = 0; j0 < B; j0 += 64) {
+    const int i = j0 + lane;
+    const int n = j0 == 0 ? len0 : (i < B ? min(max(lens[i], S), bound) : 0);
+    const int nb = i < B ? bal_chunks(n, L, smax, cap) : 0;
+    int incl = nb;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(incl, o);
+      if (lane >= o) incl += t;
+    }
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(base + incl > r);
+    if (hit) {
+      const int l = __builtin_ctzll(hit);
+      b_out = __builtin_amdgcn_readfirstlane(j0 + l);
+      c_out = __builtin_amdgcn_readfirstlane(r - base - __shfl(incl - nb, l));
+      return true;
+    }
+    base += __shfl(incl, 63);
+  }
+  return false;
+}
 
 // Where tile rows come from: contiguous caches [Bmax, Tmax, .]; page pools; or the rows an index
 // list names (the tiles then run over list entries instead of positions).
@@ -117,20 +190,39 @@ attn_kernel(AttnArgs a) {
   int bid = __builtin_amdgcn_readfirstlane(xcd_logical_id(blockIdx.x, gridDim.x));
   const int rb = __builtin_amdgcn_readfirstlane(bid % a.row_blocks);
   bid /= a.row_blocks;
-  const int split = __builtin_amdgcn_readfirstlane(bid % a.splits);
-  const int b = __builtin_amdgcn_readfirstlane(bid / a.splits);
+  // balanced ragged plan: bid is a chunk rank; the chunk length comes from all lengths
+  const bool balanced = !kSparse && a.bal_target > 0;
+  int split = __builtin_amdgcn_readfirstlane(bid % a.splits);
+  int b = __builtin_amdgcn_readfirstlane(bid / a.splits);
+  int bal_L = 0;
+  if (balanced) {
+    // lane l holds sequence l's clamped length (the first 64; more are re-read as needed)
+    const int len0 = lane < a.B ? min(max(a.seq_lens[lane], a.S), a.end_pos) : 0;
+    bal_L = __builtin_amdgcn_readfirstlane(
+        balanced_chunk(a.seq_lens, len0, a.B, a.S, a.end_pos, a.splits, a.bal_cap, a.bal_target, lane));
+    if (!balanced_find(a.seq_lens, len0, a.B, a.S, a.end_pos, a.splits, a.bal_cap, bal_L, bid, lane, b, split))
+      return;  // fewer chunks than workgroups: nothing to do
+  }
 
   // this lane's query row (its column of the score tile)
   const int lrow = rb * kRowsWG + wave * 32 + l32;
   const bool row_ok = lrow < a.SH;
   const int s = row_ok ? lrow / a.H : 0;
   const int64_t grow = int64_t(b) * a.SH + lrow;
-  const int t_begin = split * a.split_len;
   // this sequence's length: a ragged batch reads it from seq_lens, clamped to [S, end_pos] so that
   // no access leaves the positions the caller vouched for
   const int end_pos = a.seq_lens ? __builtin_amdgcn_readfirstlane(min(max(a.seq_lens[b], a.S), a.end_pos)) : a.end_pos;
-  // sparse: the split covers list entries [t_begin, t_split_end) of one query token
-  const int t_split_end = min(t_begin + a.split_len, kSparse ? a.topk : end_pos);
+  // The split's positions [t_begin, t_split_end): a fixed split length, or (balanced ragged plan)
+  // this sequence's share of its n_b chunks of about equal length, a multiple of 32.  Sparse: the
+  // split covers list entries [t_begin, t_split_end) of one query token.
+  int split_len = a.split_len, t_begin = split * a.split_len;
+  if (balanced) {  // chunk `split` of the sequence's chunks (split < their count by construction)
+    split_len = __builtin_amdgcn_readfirstlane(bal_len(end_pos, bal_L, a.splits, a.bal_cap));
+    t_begin = split * split_len;
+    if (split == 0 && rb == 0)  // the chunk count, for the combine: one entry per query row
+      for (int i = threadIdx.x; i < a.S; i += 256) a.bal_nb[b * a.S + i] = (end_pos + split_len - 1) / split_len;
+  }
+  const int t_split_end = min(t_begin + split_len, kSparse ? a.topk : end_pos);
   const int row_end = row_ok ? min(t_split_end, end_pos - a.S + s + 1) : t_begin;
   // Positions the workgroup needs (up to the last visible one of its last row), and the prefix
   // visible to all of its rows (tiles inside it need no mask).  Integer division runs on the
@@ -721,6 +813,7 @@ struct CombineArgs {
   uint16_t *out;           // [rows, 128]
   int32_t H, M, splits;    // rows = M * H, row = m * H + h
   int32_t wgs_per_head, groups_per_wg;
+  const int32_t *bal_nb;   // balanced ragged plan: [M] splits used by row m's sequence, else null
 };
 
 constexpr int kCombineRows = 16;
@@ -778,43 +871,56 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineArgs a) {
     // time (SB splits per row), and merged with a running maximum per row: a batch whose maximum
     // exceeds it rescales the row's sum and denominator first.  So a group costs
     // splits * NR / kCombineLoads memory round trips, with no pass over the statistics before.
+    // A balanced ragged batch gives each row the split count its sequence used (bal_nb): the
+    // first round does not wait for the counts (it reads slots of the row's own range, stale ones
+    // masked), and the later rounds are bounded by them.
     auto combine_rows = [&](auto nr_tag) __attribute__((always_inline)) {
       constexpr int NR = decltype(nr_tag)::value;
       constexpr int SB = kCombineLoads / NR;
       const uint16_t *po[NR];
       const float *ml[NR];
       float mx[NR], den[NR], acc[NR][8];
+      // splits of row k as read (uniform in value, kept in vector registers: a zero the compiler
+      // cannot see through keeps the count loads per lane, and nothing uses them before the first
+      // round's partial rows are requested), and clamped to [1, splits] for the later rounds
+      int ns[NR], lim[NR];
+      int zero;
+      asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
 #pragma unroll
       for (int k = 0; k < NR; ++k) {
         const int r = min(wave + 4 * k, nrows - 1);  // rows past nrows repeat a valid one, unwritten
         const int64_t row = int64_t(m0 + r) * a.H + h;
         po[k] = a.part_o + row * a.splits * kC + lane * 8;
         ml[k] = a.part_ml + row * a.splits * 2;
+        ns[k] = a.splits;
+        if (a.bal_nb) ns[k] = a.bal_nb[m0 + r + zero];
         mx[k] = -INFINITY;
         den[k] = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[k][e] = 0.f;
       }
-      for (int i0 = 0; i0 < a.splits; i0 += SB) {
-        // splits past the last repeat it with weight 0 (no branches between the loads); the split
-        // statistics and the partial rows are all requested before any is used
+      // one round: splits i0 .. i0 + SB - 1 of every row.  The first reads slots of the row's own
+      // range without the counts; splits past a row's last repeat it with weight 0 (no branches
+      // between the loads); the statistics and partial rows are all requested before any is used
+      auto round = [&](int i0, auto first_tag) __attribute__((always_inline)) {
+        constexpr bool kFirst = decltype(first_tag)::value;
         u32x4 v[NR][SB];
         f32x2 st[NR][SB];
 #pragma unroll
         for (int k = 0; k < NR; ++k)
 #pragma unroll
           for (int s = 0; s < SB; ++s)
-            st[k][s] = *reinterpret_cast<const f32x2 *>(ml[k] + 2 * min(i0 + s, a.splits - 1));
+            st[k][s] = *reinterpret_cast<const f32x2 *>(ml[k] + 2 * min(i0 + s, (kFirst ? a.splits : lim[k]) - 1));
 #pragma unroll
         for (int k = 0; k < NR; ++k)
 #pragma unroll
           for (int s = 0; s < SB; ++s)
-            v[k][s] = *reinterpret_cast<const u32x4 *>(po[k] + int64_t(min(i0 + s, a.splits - 1)) * kC);
+            v[k][s] = *reinterpret_cast<const u32x4 *>(po[k] + int64_t(min(i0 + s, (kFirst ? a.splits : lim[k]) - 1)) * kC);
 #pragma unroll
         for (int k = 0; k < NR; ++k) {
           float bm = mx[k];
 #pragma unroll
-          for (int s = 0; s < SB; ++s) bm = fmaxf(bm, i0 + s < a.splits ? st[k][s][0] : -INFINITY);
+          for (int s = 0; s < SB; ++s) bm = fmaxf(bm, i0 + s < (kFirst ? ns[k] : lim[k]) ? st[k][s][0] : -INFINITY);
           // -inf only while no split of the row has seen a position (a sparse row may never)
           const float alpha = (mx[k] == -INFINITY) ? 0.f : fast_exp2(mx[k] - bm);
           mx[k] = bm;
@@ -824,12 +930,12 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineArgs a) {
 #pragma unroll
           for (int s = 0; s < SB; ++s) {
             const float mi = st[k][s][0];
-            const bool used = mi != -INFINITY && i0 + s < a.splits;
+            const bool used = i0 + s < (kFirst ? ns[k] : lim[k]) && mi != -INFINITY;
             const float w = used ? fast_exp2(mi - bm) : 0.f;
             // an empty split's o row was never written: zero its bits rather than multiply
             // whatever the memory holds (possibly NaN) by 0
             const uint32_t keep = used ? 0xffffffffu : 0u;
-            den[k] = fmaf(w, st[k][s][1], den[k]);
+            den[k] = fmaf(w, used ? st[k][s][1] : 0.f, den[k]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const uint32_t x = v[k][s][e] & keep;
@@ -838,7 +944,16 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineArgs a) {
             }
           }
         }
+      };
+      round(0, std::true_type{});
+      int nmax = 1;
+#pragma unroll
+      for (int k = 0; k < NR; ++k) {
+        lim[k] = min(max(ns[k], 1), a.splits);
+        nmax = max(nmax, lim[k]);
       }
+      nmax = __builtin_amdgcn_readfirstlane(nmax);
+      for (int i0 = SB; i0 < nmax; i0 += SB) round(i0, std::false_type{});
 #pragma unroll
       for (int k = 0; k < NR; ++k) {
         if (wave + 4 * k >= nrows) continue;
@@ -962,7 +1077,7 @@ bool mfma_attn_plan_ok(const AttnCall &c, const char **why) {
 
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Workspace: [query fragments] [split m, l] [split o].
+// Workspace: [query fragments] [split m, l] [split o] [split counts of the balanced plan].
 static size_t q_region_bytes(const AttnCall &c) {
   const size_t row_blocks = size_t((c.S * c.H + kRowsWG - 1) / kRowsWG);
   return align256(size_t(c.B) * row_blocks * 4 * kFragBytesPerWave);
@@ -970,7 +1085,8 @@ static size_t q_region_bytes(const AttnCall &c) {
 
 size_t mfma_attn_workspace(const AttnCall &c) {
   const size_t rows = size_t(c.B * c.S * c.H);
-  return q_region_bytes(c) + align256(rows * size_t(c.splits) * 2 * 4) + align256(rows * size_t(c.splits) * kC * 2);
+  return q_region_bytes(c) + align256(rows * size_t(c.splits) * 2 * 4) + align256(rows * size_t(c.splits) * kC * 2) +
+         (c.bal_target > 0 ? align256(size_t(c.B * c.S) * 4) : 0);
 }
 
 hipError_t mfma_absorb_attn(const AttnCall &c) {
@@ -979,6 +1095,10 @@ hipError_t mfma_absorb_attn(const AttnCall &c) {
   uint16_t *q_frag = reinterpret_cast<uint16_t *>(ws);
   float *part_ml = reinterpret_cast<float *>(ws + q_region_bytes(c));
   uint16_t *part_o = reinterpret_cast<uint16_t *>(ws + q_region_bytes(c) + align256(size_t(rows) * c.splits * 2 * 4));
+  int32_t *bal_nb = c.bal_target > 0 ? reinterpret_cast<int32_t *>(ws + q_region_bytes(c) +
+                                                                  align256(size_t(rows) * c.splits * 2 * 4) +
+                                                                  align256(size_t(rows) * c.splits * kC * 2))
+                                     : nullptr;
   const int32_t M = int32_t(c.B * c.S);
   const int32_t row_blocks = int32_t((c.S * c.H + kRowsWG - 1) / kRowsWG);
 
@@ -1006,9 +1126,15 @@ hipError_t mfma_absorb_attn(const AttnCall &c) {
   aa.seq_lens = c.seq_lens;
   aa.splits = c.splits;
   aa.split_len = int32_t(c.split_len);
+  aa.B = int32_t(c.B);
+  aa.bal_target = c.bal_target;
+  aa.bal_cap = c.page_size > 0 ? int32_t(mfma_paged_max_split_len(c)) : (1 << 30);
+  aa.bal_nb = bal_nb;
   aa.row_blocks = row_blocks;
   aa.scale_log2 = c.scale * kLog2e;
-  const int64_t nwg = c.B * int64_t(aa.splits) * aa.row_blocks;
+  // balanced plan: bal_target chunk workgroups per row block (the plan keeps it >= every chunk
+  // count the lengths can produce), else one per (sequence, split)
+  const int64_t nwg = (c.bal_target > 0 ? int64_t(c.bal_target) : c.B * int64_t(aa.splits)) * aa.row_blocks;
   if (c.topk > 0) {
     aa.indices = c.indices;
     aa.topk = int32_t(c.topk);
@@ -1030,7 +1156,7 @@ hipError_t mfma_absorb_attn(const AttnCall &c) {
   const int groups = (M + kCombineRows - 1) / kCombineRows;
   const int per_head = int(std::max<int64_t>(1, std::min<int64_t>(groups, (512 + c.H - 1) / c.H)));
   CombineArgs ca{part_ml, part_o, static_cast<const uint16_t *>(c.wkv_b), static_cast<uint16_t *>(c.out),
-                 int32_t(c.H), M, c.splits, per_head, (groups + per_head - 1) / per_head};
+                 int32_t(c.H), M, c.splits, per_head, (groups + per_head - 1) / per_head, bal_nb};
   const dim3 grid(unsigned(int64_t(c.H) * per_head));
   return c.splits == 1 ? launch_kernel(MLA_KERNEL_COMBINE, combine_kernel<true>, grid, dim3(256), 0, c.stream, ca)
                        : launch_kernel(MLA_KERNEL_COMBINE, combine_kernel<false>, grid, dim3(256), 0, c.stream, ca);

@@ -22,6 +22,9 @@ struct AttnCall {
   // list entries instead of the positions
   const int32_t *indices;
   int64_t topk;
+  // balanced ragged plan (matrix-core path, bal_target > 0): splits is the most chunks one
+  // sequence may take, bal_target the workgroups per row block, one chunk each (see attn_kernel)
+  int32_t bal_target;
   float scale;
   int32_t dtype;      // MLA_DTYPE_*
   int32_t splits;     // ranges the positions [0, end_pos) are cut into

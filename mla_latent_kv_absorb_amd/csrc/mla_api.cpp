@@ -40,8 +40,12 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
 // the per-sequence capacity max_pages_per_seq * page_size.
 // With topk > 0 each query token attends to an index list of topk entries, and the splits cut
 // the entries.
+// With ragged (per-sequence lengths in device memory) and an automatic split count, the matrix-core
+// plan is the balanced one: as many workgroups as the uniform plan, each taking one chunk of one
+// sequence, the kernel picking one chunk length from all lengths so that long sequences take more
+// chunks (up to four times the uniform split count) and every workgroup about equal work.
 int32_t plan_attn(const mla_attn_shape *shape, int64_t end_pos, const mla_paged_cache *paged, int64_t topk,
-                  int32_t dtype, const mla_attn_options *options, mla::AttnCall &c, bool &use_mfma) {
+                  bool ragged, int32_t dtype, const mla_attn_options *options, mla::AttnCall &c, bool &use_mfma) {
   if (!shape) return fail(MLA_ERR_NULL, "shape is NULL");
   if (dtype != MLA_DTYPE_F32 && dtype != MLA_DTYPE_BF16) return fail(MLA_ERR_DTYPE, "unknown dtype %d", dtype);
   mla_attn_shape s = *shape;
@@ -118,6 +122,22 @@ int32_t plan_attn(const mla_attn_shape *shape, int64_t end_pos, const mla_paged_
   if (c.splits > items) c.splits = int32_t(items);
   c.split_len = (items + c.splits - 1) / c.splits;
   if (use_mfma && c.page_size > 0) c.split_len = (c.split_len + 31) / 32 * 32;  // tiles within pages
+  if (use_mfma && ragged && topk == 0 && opt.num_splits == 0 && c.splits > 0) {
+    const int64_t s0 = c.splits;
+    const int64_t smax =
+        c.B > 1 ? std::min<int64_t>(std::min<int64_t>(4 * s0, std::max<int64_t>(s0, (end_pos + 31) / 32)), 4096) : s0;
+    // chunks a sequence needs at the longest chunk length: one, or more where pages cap a chunk;
+    // the grid must hold B of them so that the kernel's search for a chunk length always ends
+    const int64_t need = c.page_size > 0 ? (end_pos + mla::mfma_paged_max_split_len(c) - 1) / mla::mfma_paged_max_split_len(c) : 1;
+    {
+      mla::AttnCall cb = c;
+      cb.splits = int32_t(smax);
+      cb.split_len = ((end_pos + smax - 1) / smax + 31) / 32 * 32;
+      cb.bal_target = int32_t(c.B * std::max(s0, std::min(smax, need)));
+      const char *why = "";
+      if (mla::mfma_attn_plan_ok(cb, &why)) c = cb;  // else keep the uniform plan
+    }
+  }
   if (use_mfma) {
     const char *why = "";
     if (!mla::mfma_attn_plan_ok(c, &why)) {
@@ -159,7 +179,16 @@ size_t mla_absorb_attn_workspace_size(const mla_attn_shape *shape, int64_t end_p
   clear_error();
   mla::AttnCall c;
   bool use_mfma = false;
-  if (plan_attn(shape, end_pos, nullptr, 0, dtype, options, c, use_mfma) != MLA_OK) return 0;
+  if (plan_attn(shape, end_pos, nullptr, 0, false, dtype, options, c, use_mfma) != MLA_OK) return 0;
+  return use_mfma ? mla::mfma_attn_workspace(c) : mla::plain_attn_workspace(c);
+}
+
+size_t mla_absorb_attn_ragged_workspace_size(const mla_attn_shape *shape, int64_t max_seq_len, int32_t dtype,
+                                             const mla_attn_options *options) {
+  clear_error();
+  mla::AttnCall c;
+  bool use_mfma = false;
+  if (plan_attn(shape, max_seq_len, nullptr, 0, true, dtype, options, c, use_mfma) != MLA_OK) return 0;
   return use_mfma ? mla::mfma_attn_workspace(c) : mla::plain_attn_workspace(c);
 }
 
@@ -170,7 +199,7 @@ size_t mla_absorb_attn_paged_workspace_size(const mla_attn_shape *shape, int64_t
   if (!paged) { fail(MLA_ERR_NULL, "paged is NULL"); return 0; }
   mla::AttnCall c;
   bool use_mfma = false;
-  if (plan_attn(shape, max_seq_len, paged, 0, dtype, options, c, use_mfma) != MLA_OK) return 0;
+  if (plan_attn(shape, max_seq_len, paged, 0, true, dtype, options, c, use_mfma) != MLA_OK) return 0;
   return use_mfma ? mla::mfma_attn_workspace(c) : mla::plain_attn_workspace(c);
 }
 
@@ -180,7 +209,7 @@ size_t mla_absorb_attn_sparse_workspace_size(const mla_attn_shape *shape, int64_
   if (topk < 1) { fail(MLA_ERR_SHAPE, "topk = %lld must be >= 1", (long long)topk); return 0; }
   mla::AttnCall c;
   bool use_mfma = false;
-  if (plan_attn(shape, end_pos, nullptr, topk, dtype, options, c, use_mfma) != MLA_OK) return 0;
+  if (plan_attn(shape, end_pos, nullptr, topk, false, dtype, options, c, use_mfma) != MLA_OK) return 0;
   return use_mfma ? mla::mfma_attn_workspace(c) : mla::plain_attn_workspace(c);
 }
 
@@ -197,7 +226,7 @@ int32_t absorb_attn_call(const void *q_nope, const void *q_pe, const void *kv_ca
                          const mla_attn_options *options, void *workspace, size_t workspace_bytes, void *stream) {
   mla::AttnCall c;
   bool use_mfma = false;
-  int32_t rc = plan_attn(shape, end_pos, paged, indices ? topk : 0, dtype, options, c, use_mfma);
+  int32_t rc = plan_attn(shape, end_pos, paged, indices ? topk : 0, seq_lens != nullptr, dtype, options, c, use_mfma);
   if (rc != MLA_OK) return rc;
   const void *ptrs[] = {q_nope, q_pe, kv_cache, pe_cache, wkv_b, out};
   const char *names[] = {"q_nope", "q_pe", "kv_cache", "pe_cache", "wkv_b", "out"};

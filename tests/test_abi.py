@@ -282,9 +282,17 @@ def test_paged_argument_errors(lib):
 def test_paged_workspace_and_split_plan(lib):
     s = shape(batch=32)
     pg = B.PagedCache(64, 32 * 64, 64)
-    # at the decode shape the paged plan is the contiguous one
-    assert B.absorb_attn_paged_workspace_size(s, 4096, pg, B.MLA_DTYPE_BF16) == \
-        B.absorb_attn_workspace_size(shape(batch=32, cache_batch=32), 4096, B.MLA_DTYPE_BF16)
+    # at the decode shape the paged size is that of the ragged (balanced) contiguous plan, which
+    # provides more split slots than the uniform plan; a forced split count is not balanced
+    dense = B.absorb_attn_workspace_size(shape(batch=32, cache_batch=32), 4096, B.MLA_DTYPE_BF16)
+    ragged = B.absorb_attn_ragged_workspace_size(shape(batch=32, cache_batch=32), 4096, B.MLA_DTYPE_BF16)
+    assert B.absorb_attn_paged_workspace_size(s, 4096, pg, B.MLA_DTYPE_BF16) == ragged > dense
+    assert B.absorb_attn_ragged_workspace_size(shape(batch=32, cache_batch=32), 4096, B.MLA_DTYPE_BF16, num_splits=8) \
+        == B.absorb_attn_workspace_size(shape(batch=32, cache_batch=32), 4096, B.MLA_DTYPE_BF16, num_splits=8)
+    # the plain path plans the same with or without lengths
+    assert B.absorb_attn_ragged_workspace_size(shape(batch=32, cache_batch=32), 4096, B.MLA_DTYPE_BF16,
+                                               path="plain") == \
+        B.absorb_attn_workspace_size(shape(batch=32, cache_batch=32), 4096, B.MLA_DTYPE_BF16, path="plain")
     # one split over 16384 positions spans more pages of 32 than a workgroup keeps: refused on the
     # matrix-core path, planned with more splits by default
     one = shape(batch=1, seqlen_q=512, n_heads=128, cache_batch=1, cache_len=16384)
@@ -293,7 +301,7 @@ def test_paged_workspace_and_split_plan(lib):
         B.absorb_attn_paged_workspace_size(one, 16384, pg32, B.MLA_DTYPE_BF16, num_splits=1, path="mfma")
     ws = {p: B.absorb_attn_paged_workspace_size(one, 16384, B.PagedCache(p, 16384 // p, 16384 // p),
                                                 B.MLA_DTYPE_BF16, path="mfma") for p in (32, 64, 128)}
-    assert ws[32] > ws[64] > ws[128] == B.absorb_attn_workspace_size(one, 16384, B.MLA_DTYPE_BF16, path="mfma")
+    assert ws[32] > ws[64] > ws[128] == B.absorb_attn_ragged_workspace_size(one, 16384, B.MLA_DTYPE_BF16, path="mfma")
 
 
 def call_sparse(lib, s, end_pos=4096, ptrs=None, idx=P[6], topk=2048, lens=None, path=B.PATHS["auto"], splits=0,

@@ -264,6 +264,23 @@ def test_ragged_small(gpu_lib, path, seqlen_q, lens):
     check(out, oracle_ragged(cfg, x, lens), TOL["bf16"], f"ragged S={seqlen_q} lens={lens} {path}")
 
 
+@pytest.mark.parametrize("lens", [[4096] + [1] * 31, [1] * 31 + [4096], [64 * (i + 1) for i in range(32)]])
+def test_ragged_balanced_full_heads(gpu_lib, lens):
+    """The balanced plan at the decode head shape: one long sequence among very short ones (it
+    takes up to four times the uniform plan's chunks), at either end of the chunk order, and a
+    linear spread of lengths; sampled rows."""
+    cfg = ATTN_CONFIGS["dsv3_decode"]
+    x = make_attn_inputs(cfg)
+    t = to_dev(x, cfg)
+    poison_tails(t, lens)
+    out = run_attn_ragged(gpu_lib, cfg, t, lens)
+    assert torch.isfinite(out).all(), "non-finite outputs"
+    rows = sample_rows(cfg, 40, 17) + [(b, 0, 5) for b in range(0, 32, 3)]
+    ref = oracle_ragged(cfg, x, lens, rows=rows)
+    g = out.float().cpu().double().numpy()
+    check(np.stack([g[b, s_, h] for b, s_, h in rows]), ref, TOL["bf16"], f"balanced ragged lens[0]={lens[0]}")
+
+
 @pytest.mark.parametrize("splits", [0, 8, 24])
 def test_ragged_empty_splits_nan_workspace(gpu_lib, splits):
     """Splits past a short sequence's end write only their statistics; the combine must not read
@@ -273,7 +290,7 @@ def test_ragged_empty_splits_nan_workspace(gpu_lib, splits):
     x = make_attn_inputs(cfg)
     t = to_dev(x, cfg)
     shape = gpu_lib.attn_shape(t["q_nope"], t["q_pe"], t["kv_cache"], t["wkv_b"])
-    need = gpu_lib.absorb_attn_workspace_size(shape, cfg.end_pos, gpu_lib.MLA_DTYPE_BF16, splits, "mfma")
+    need = gpu_lib.absorb_attn_ragged_workspace_size(shape, cfg.end_pos, gpu_lib.MLA_DTYPE_BF16, splits, "mfma")
     ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
     out = torch.full((cfg.batch, cfg.seqlen_q, cfg.n_heads, cfg.v_head_dim), float("nan"), dtype=torch.bfloat16,
                      device="cuda")
