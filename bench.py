@@ -22,7 +22,9 @@ events that the kernel's own dispatch stamps on its stream (hipExtLaunchKernel s
 those events add a queue barrier per timed dispatch, so that pass's step time is reported apart.
 `cpu_baseline` times the CPU oracle (NumPy, float64) on a bounded sample of the same workload.
 `extras` times the other workloads the same way: long_decode, chunk_prefill, ragged_decode (the
-decode batch with per-sequence lengths drawn uniformly from [256, 4096]), paged_decode (the decode
+decode batch with per-sequence lengths drawn uniformly from [256, 4096]) and skewed_decode (4 of
+its sequences at 4096 positions, 28 at 64), each also under the uniform split plan for
+comparison with the balanced one the library picks, paged_decode (the decode
 batch with its caches in pools of 64-position pages in random order), sparse_decode and
 sparse_long_decode (the decode and long-context batches with each token attending to 2048 random
 positions of its cache through an index list), chunk_prefill_naive (the
@@ -129,11 +131,12 @@ def random_lists(cfg, topk, seed, torch):
 
 
 def time_attn(cfg, steps, warmup, sets, torch, binding, seed=1, timed_kernels=0b010, lens=None, page_size=0,
-              topk=0):
+              topk=0, num_splits=0):
     """Returns (GPU us per step, host enqueue us per step, per-kernel timing dict).  With lens, a
     ragged batch (mla_absorb_attn_ragged with the lengths in device memory, bound cfg.end_pos);
     with page_size, the caches live in page pools in random page order (mla_absorb_attn_paged);
-    with topk, each token attends to topk random positions (mla_absorb_attn_sparse)."""
+    with topk, each token attends to topk random positions (mla_absorb_attn_sparse).  num_splits > 0
+    forces the split count (0: the library's plan)."""
     inputs = [gpu_inputs(cfg, seed + 1000 * i, torch) for i in range(sets)]
     seq_lens = None if lens is None else torch.tensor([int(n) for n in lens], dtype=torch.int32, device="cuda")
     out = torch.empty((cfg.batch, cfg.seqlen_q, cfg.n_heads, cfg.v_head_dim), dtype=torch.bfloat16, device="cuda")
@@ -146,14 +149,14 @@ def time_attn(cfg, steps, warmup, sets, torch, binding, seed=1, timed_kernels=0b
     elif topk:
         need = binding.absorb_attn_sparse_workspace_size(shape, cfg.end_pos, topk, binding.MLA_DTYPE_BF16)
     elif lens is not None:
-        need = binding.absorb_attn_ragged_workspace_size(shape, cfg.end_pos, binding.MLA_DTYPE_BF16)
+        need = binding.absorb_attn_ragged_workspace_size(shape, cfg.end_pos, binding.MLA_DTYPE_BF16, num_splits)
     else:
         need = binding.absorb_attn_workspace_size(shape, cfg.end_pos, binding.MLA_DTYPE_BF16)
     ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
     tables = [to_paged(x, cfg, page_size, seed + i, torch) if page_size else None for i, x in enumerate(inputs)]
     calls = [binding.AbsorbAttnCall(x["q_nope"], x["q_pe"], x["kv_cache"], x["pe_cache"], x["wkv_b"], cfg.end_pos,
                                     cfg.softmax_scale, out, workspace=ws, seq_lens=seq_lens, block_table=tb,
-                                    indices=il)
+                                    indices=il, num_splits=num_splits)
              for x, tb, il in zip(inputs, tables, lists)]
 
     def step(i):
@@ -337,7 +340,7 @@ def main():
     import torch
 
     from mla_latent_kv_absorb_amd import binding
-    from mla_latent_kv_absorb_amd.workloads import ATTN_CONFIGS, EXPAND_CONFIGS, RAGGED_CONFIGS, ragged_lengths
+    from mla_latent_kv_absorb_amd.workloads import ATTN_CONFIGS, EXPAND_CONFIGS, RAGGED_WORKLOADS, ragged_workload
 
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
@@ -418,15 +421,23 @@ def main():
             extras[name] = {"us_per_step": round(u, 2), "gbps": round(w["bytes"] / (u * 1e-6) / 1e9, 1),
                             "tflops": round(w["flops"] / (u * 1e-6) / 1e12, 2),
                             "kernels_us": {n: round(v["avg_us"], 2) for n, v in k.items()}}
-        for name, (base, lo, hi, lseed) in RAGGED_CONFIGS.items():
+        for name in RAGGED_WORKLOADS:
+            base, lens = ragged_workload(name)
             c = ATTN_CONFIGS[base]
-            lens = ragged_lengths(c.batch, lo, hi, lseed)
             w = attn_work(c, lens)
             u, _, _ = time_attn(c, 30, 3, args.sets, torch, binding, seed=c.seed, timed_kernels=0, lens=lens)
             _, _, k = time_attn(c, 30, 3, args.sets, torch, binding, seed=c.seed, timed_kernels=0b111, lens=lens)
+            # the same batch under the uniform plan: every sequence cut into the split count a batch
+            # of equal lengths gets (one workgroup per compute unit, at least 128 positions a split)
+            units = c.batch * -(-c.seqlen_q * c.n_heads // 128)
+            uniform = max(1, min((256 + units // 2) // units, -(-c.end_pos // 128)))
+            uu, _, _ = time_attn(c, 30, 3, args.sets, torch, binding, seed=c.seed, timed_kernels=0, lens=lens,
+                                 num_splits=uniform)
             extras[name] = {"us_per_step": round(u, 2), "gbps": round(w["bytes"] / (u * 1e-6) / 1e9, 1),
-                            "tflops": round(w["flops"] / (u * 1e-6) / 1e12, 2), "lengths": [lo, hi, int(sum(lens))],
-                            "kernels_us": {n: round(v["avg_us"], 2) for n, v in k.items()}}
+                            "tflops": round(w["flops"] / (u * 1e-6) / 1e12, 2),
+                            "lengths": [int(lens.min()), int(lens.max()), int(sum(lens))],
+                            "kernels_us": {n: round(v["avg_us"], 2) for n, v in k.items()},
+                            "uniform_plan": {"num_splits": uniform, "us_per_step": round(uu, 2)}}
         c = ATTN_CONFIGS["dsv3_decode"]
         w = attn_work(c)
         u, _, _ = time_attn(c, 30, 3, args.sets, torch, binding, seed=c.seed, timed_kernels=0, page_size=64)

@@ -874,8 +874,9 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineArgs a) {
     // A balanced ragged batch gives each row the split count its sequence used (bal_nb): the
     // first round does not wait for the counts (it reads slots of the row's own range, stale ones
     // masked), and the later rounds are bounded by them.
-    auto combine_rows = [&](auto nr_tag) __attribute__((always_inline)) {
+    auto combine_rows = [&](auto nr_tag, auto bal_tag) __attribute__((always_inline)) {
       constexpr int NR = decltype(nr_tag)::value;
+      constexpr bool kBal = decltype(bal_tag)::value;  // counts per row (balanced ragged plan)
       constexpr int SB = kCombineLoads / NR;
       const uint16_t *po[NR];
       const float *ml[NR];
@@ -884,16 +885,15 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineArgs a) {
       // cannot see through keeps the count loads per lane, and nothing uses them before the first
       // round's partial rows are requested), and clamped to [1, splits] for the later rounds
       int ns[NR], lim[NR];
-      int zero;
-      asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
+      int zero = 0;
+      if constexpr (kBal) asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
 #pragma unroll
       for (int k = 0; k < NR; ++k) {
         const int r = min(wave + 4 * k, nrows - 1);  // rows past nrows repeat a valid one, unwritten
         const int64_t row = int64_t(m0 + r) * a.H + h;
         po[k] = a.part_o + row * a.splits * kC + lane * 8;
         ml[k] = a.part_ml + row * a.splits * 2;
-        ns[k] = a.splits;
-        if (a.bal_nb) ns[k] = a.bal_nb[m0 + r + zero];
+        ns[k] = kBal ? a.bal_nb[m0 + r + zero] : a.splits;
         mx[k] = -INFINITY;
         den[k] = 0.f;
 #pragma unroll
@@ -916,6 +916,8 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineArgs a) {
 #pragma unroll
           for (int s = 0; s < SB; ++s)
             v[k][s] = *reinterpret_cast<const u32x4 *>(po[k] + int64_t(min(i0 + s, (kFirst ? a.splits : lim[k]) - 1)) * kC);
+        // balanced plan: nothing of the merge (which reads the counts) moves above the loads
+        if constexpr (kBal) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int k = 0; k < NR; ++k) {
           float bm = mx[k];
@@ -935,7 +937,8 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineArgs a) {
             // an empty split's o row was never written: zero its bits rather than multiply
             // whatever the memory holds (possibly NaN) by 0
             const uint32_t keep = used ? 0xffffffffu : 0u;
-            den[k] = fmaf(w, used ? st[k][s][1] : 0.f, den[k]);
+            // (balanced plan: a first-round slot past the row's count may hold a stale sum)
+            den[k] = fmaf(w, !kBal || used ? st[k][s][1] : 0.f, den[k]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const uint32_t x = v[k][s][e] & keep;
@@ -945,15 +948,20 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineArgs a) {
           }
         }
       };
-      round(0, std::true_type{});
-      int nmax = 1;
+      if constexpr (kBal) {
+        round(0, std::true_type{});
+        int nmax = 1;
 #pragma unroll
-      for (int k = 0; k < NR; ++k) {
-        lim[k] = min(max(ns[k], 1), a.splits);
-        nmax = max(nmax, lim[k]);
+        for (int k = 0; k < NR; ++k) {  // scalars now: the counts arrived with the first round
+          lim[k] = __builtin_amdgcn_readfirstlane(min(max(ns[k], 1), a.splits));
+          nmax = max(nmax, lim[k]);
+        }
+        for (int i0 = SB; i0 < nmax; i0 += SB) round(i0, std::false_type{});
+      } else {  // every row has all the splits: scalar bounds
+#pragma unroll
+        for (int k = 0; k < NR; ++k) lim[k] = a.splits;
+        for (int i0 = 0; i0 < a.splits; i0 += SB) round(i0, std::false_type{});
       }
-      nmax = __builtin_amdgcn_readfirstlane(nmax);
-      for (int i0 = SB; i0 < nmax; i0 += SB) round(i0, std::false_type{});
 #pragma unroll
       for (int k = 0; k < NR; ++k) {
         if (wave + 4 * k >= nrows) continue;
@@ -965,9 +973,16 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineArgs a) {
     };
     if (!kSingle) {
       const int nr = wave < nrows ? (nrows - wave + 3) / 4 : 0;  // wavefront-uniform
-      if (nr >= 3) combine_rows(std::integral_constant<int, 4>{});
-      else if (nr == 2) combine_rows(std::integral_constant<int, 2>{});
-      else if (nr == 1) combine_rows(std::integral_constant<int, 1>{});
+      using I4 = std::integral_constant<int, 4>;
+      using I2 = std::integral_constant<int, 2>;
+      using I1 = std::integral_constant<int, 1>;
+      if (a.bal_nb) {  // one instantiation (fewer registers held across the kernel's paths)
+        if (nr > 0) combine_rows(I4{}, std::true_type{});
+      } else {
+        if (nr >= 3) combine_rows(I4{}, std::false_type{});
+        else if (nr == 2) combine_rows(I2{}, std::false_type{});
+        else if (nr == 1) combine_rows(I1{}, std::false_type{});
+      }
     }
     if (grp == g_begin) wait_vmcnt<0>();  // W_UV rows (LDS DMA) before the first use
     __syncthreads();

@@ -42,7 +42,10 @@ __all__ = [
     "make_attn_inputs",
     "make_expand_inputs",
     "RAGGED_CONFIGS",
+    "SKEWED_CONFIGS",
+    "RAGGED_WORKLOADS",
     "ragged_lengths",
+    "ragged_workload",
 ]
 
 
@@ -151,9 +154,29 @@ RAGGED_CONFIGS: Dict[str, tuple] = {
 }
 
 
+# Skewed ragged workloads: (attention workload, sequences at the long length, long length, short
+# length).  A few long contexts among many short ones: the batch in which one split count for
+# every sequence leaves most workgroups idle.
+SKEWED_CONFIGS: Dict[str, tuple] = {
+    "skewed_decode": ("dsv3_decode", 4, 4096, 64),
+}
+
+RAGGED_WORKLOADS = list(RAGGED_CONFIGS) + list(SKEWED_CONFIGS)
+
+
 def ragged_lengths(batch: int, lo: int, hi: int, seed: int) -> np.ndarray:
     """Per-sequence lengths drawn uniformly from [lo, hi] (int32)."""
     return np.random.default_rng(seed).integers(lo, hi + 1, size=batch).astype(np.int32)
+
+
+def ragged_workload(name: str):
+    """(attention workload name, int32 lengths [batch]) of a ragged or skewed workload."""
+    if name in RAGGED_CONFIGS:
+        base, lo, hi, seed = RAGGED_CONFIGS[name]
+        return base, ragged_lengths(ATTN_CONFIGS[base].batch, lo, hi, seed)
+    base, n_long, long_len, short_len = SKEWED_CONFIGS[name]
+    batch = ATTN_CONFIGS[base].batch
+    return base, np.array([long_len] * n_long + [short_len] * (batch - n_long), dtype=np.int32)
 
 
 def _draw(rng: np.random.Generator, shape, std: float, mean: float = 0.0) -> np.ndarray:

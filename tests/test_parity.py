@@ -8,8 +8,8 @@ import numpy as np
 import pytest
 import torch
 
-from mla_latent_kv_absorb_amd.workloads import (ATTN_CONFIGS, EXPAND_CONFIGS, RAGGED_CONFIGS, make_attn_inputs,
-                                                 make_expand_inputs, ragged_lengths, round_to_bf16)
+from mla_latent_kv_absorb_amd.workloads import (ATTN_CONFIGS, EXPAND_CONFIGS, RAGGED_WORKLOADS, make_attn_inputs,
+                                                 make_expand_inputs, ragged_workload, round_to_bf16)
 from oracle import mla_oracle as O
 
 pytestmark = pytest.mark.gpu
@@ -322,11 +322,10 @@ def test_ragged_lengths_are_clamped(gpu_lib):
     check(out, oracle_ragged(cfg, x, [2, 150, 2]), TOL["bf16"], "ragged clamped lengths")
 
 
-@pytest.mark.parametrize("name", list(RAGGED_CONFIGS))
+@pytest.mark.parametrize("name", RAGGED_WORKLOADS)
 def test_full_size_ragged(gpu_lib, name):
-    base, lo, hi, seed = RAGGED_CONFIGS[name]
+    base, lens = ragged_workload(name)
     cfg = ATTN_CONFIGS[base]
-    lens = ragged_lengths(cfg.batch, lo, hi, seed)
     print(f"full-size {name}: B={cfg.batch} lengths {lens.min()}..{lens.max()}", flush=True)
     x = make_attn_inputs(cfg)
     t = to_dev(x, cfg)
@@ -435,15 +434,14 @@ def test_paged_uniform_and_clamped_ids(gpu_lib):
 
 
 @pytest.mark.parametrize("name,page_size", [("dsv3_decode", 64), ("chunk_prefill", 64), ("long_decode", 256),
-                                            ("ragged_decode", 64)])
+                                            ("ragged_decode", 64), ("skewed_decode", 64)])
 def test_full_size_paged_matches_contiguous(gpu_lib, name, page_size):
     """The paged kernels read the same rows in the same order as the contiguous ones: outputs are
     bitwise equal at full size (pages in random order in a NaN-filled pool)."""
     lens = None
-    if name in RAGGED_CONFIGS:
-        base, lo, hi, lseed = RAGGED_CONFIGS[name]
+    if name in RAGGED_WORKLOADS:
+        base, lens = ragged_workload(name)
         cfg = ATTN_CONFIGS[base]
-        lens = ragged_lengths(cfg.batch, lo, hi, lseed)
     else:
         cfg = ATTN_CONFIGS[name]
     print(f"full-size paged {name}: B={cfg.batch} S={cfg.seqlen_q} T={cfg.end_pos} page={page_size}", flush=True)
