@@ -126,17 +126,17 @@ int32_t plan_attn(const mla_attn_shape *shape, int64_t end_pos, const mla_paged_
     const int64_t s0 = c.splits;
     const int64_t smax =
         c.B > 1 ? std::min<int64_t>(std::min<int64_t>(4 * s0, std::max<int64_t>(s0, (end_pos + 31) / 32)), 4096) : s0;
-    // chunks a sequence needs at the longest chunk length: one, or more where pages cap a chunk;
-    // the grid must hold B of them so that the kernel's search for a chunk length always ends
-    const int64_t need = c.page_size > 0 ? (end_pos + mla::mfma_paged_max_split_len(c) - 1) / mla::mfma_paged_max_split_len(c) : 1;
-    {
-      mla::AttnCall cb = c;
-      cb.splits = int32_t(smax);
-      cb.split_len = ((end_pos + smax - 1) / smax + 31) / 32 * 32;
-      cb.bal_target = int32_t(c.B * std::max(s0, std::min(smax, need)));
-      const char *why = "";
-      if (mla::mfma_attn_plan_ok(cb, &why)) c = cb;  // else keep the uniform plan
-    }
+    // chunks a sequence needs at the longest chunk length: one, or more where pages cap a chunk
+    // (s0 already covers that); the grid must hold B of them so that the kernel's search for a
+    // chunk length always ends
+    const int64_t cap = c.page_size > 0 ? mla::mfma_paged_max_split_len(c) : end_pos;
+    const int64_t need = (end_pos + cap - 1) / cap;
+    mla::AttnCall cb = c;
+    cb.splits = int32_t(smax);
+    cb.split_len = ((end_pos + smax - 1) / smax + 31) / 32 * 32;
+    cb.bal_target = int32_t(c.B * std::max(s0, std::min(smax, need)));
+    const char *why = "";
+    if (mla::mfma_attn_plan_ok(cb, &why)) c = cb;  // else keep the uniform plan
   }
   if (use_mfma) {
     const char *why = "";
