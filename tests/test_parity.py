@@ -281,6 +281,22 @@ def test_ragged_balanced_full_heads(gpu_lib, lens):
     check(np.stack([g[b, s_, h] for b, s_, h in rows]), ref, TOL["bf16"], f"balanced ragged lens[0]={lens[0]}")
 
 
+@pytest.mark.parametrize("seqlen_q", [1, 3])
+def test_ragged_balanced_many_sequences(gpu_lib, seqlen_q):
+    """More than 64 sequences: the balanced plan's chunk-length search and chunk lookup walk the
+    lengths 64 at a time (130 sequences, lengths up to 600, some cut into several chunks)."""
+    rng = np.random.default_rng(11)
+    B = 130
+    lens = [int(v) for v in rng.integers(seqlen_q, 601, size=B)]
+    lens[7], lens[64], lens[100], lens[129] = 600, seqlen_q, 600, 257
+    cfg = dsv3_small(batch=B, cache_batch=B, n_heads=16, seqlen_q=seqlen_q, end_pos=600, cache_len=640)
+    x = make_attn_inputs(cfg)
+    t = to_dev(x, cfg)
+    poison_tails(t, lens)
+    out = run_attn_ragged(gpu_lib, cfg, t, lens, path="mfma")
+    check(out, oracle_ragged(cfg, x, lens), TOL["bf16"], f"balanced ragged, {B} sequences, S={seqlen_q}")
+
+
 @pytest.mark.parametrize("splits", [0, 8, 24])
 def test_ragged_empty_splits_nan_workspace(gpu_lib, splits):
     """Splits past a short sequence's end write only their statistics; the combine must not read
