@@ -11,9 +11,9 @@
 // v_head_dim 128; bf16 storage, fp32 accumulation.
 //
 // One workgroup per (sequence, head, 128 query tokens): four waves of 32 query rows.  Tiles of 32
-// positions (8 KB of k_nope, 4 KB of pe, 8 KB of v) stream into LDS by DMA, four stages deep; per
-// tile a wave runs 12 score MFMAs (a 192-deep contraction), an online softmax in the log2
-// domain, and 8 MFMAs of the value sum.
+// positions (8 KB of k_nope, 4 KB of pe, 8 KB of v) stream into LDS by DMA, four stages, taken in
+// pairs: per pair one barrier, and per tile a wave runs 12 score MFMAs (a 192-deep contraction)
+// and 8 MFMAs of the value sum, with one online-softmax update (log2 domain) per pair.
 #include "common.h"
 #include "launch.h"
 #include "mfma_common.h"
@@ -32,7 +32,6 @@ constexpr int kVBytes = kTile * kDv * 2;   // 8 KB
 constexpr int kPeOff = kKBytes;
 constexpr int kVOff = kKBytes + kPeBytes;
 constexpr int kStageBytes = kKBytes + kPeBytes + kVBytes;  // 20 KB
-constexpr int kDmaPerTile = 5;  // 1 KB DMA instructions per wave per tile: 2 k_nope, 1 pe, 2 v
 constexpr float kRescale = 8.f;  // lazy rescale threshold (log2 units), as in the absorb kernel
 
 // LDS swizzles (16-byte chunks XOR-ed by a function of the row):
@@ -80,6 +79,9 @@ naive_attn_kernel(NaiveArgs a) {
   const int wg_end = __builtin_amdgcn_readfirstlane(a.end_pos - a.S + last_s + 1);  // >= 1
   const int wg_full = __builtin_amdgcn_readfirstlane(a.end_pos - a.S + first_s + 1);
   const int ntiles = __builtin_amdgcn_readfirstlane((wg_end + kTile - 1) / kTile);
+  // tiles go in pairs (one barrier per 64 positions); an odd count ends with a tile past the
+  // visible positions, which reads clamped rows and is masked whole
+  const int npairs = (ntiles + 1) / 2;
 
   // ---- DMA: one instruction moves 1 KB; rows past the last needed position repeat it
   const int64_t kv_row0 = (int64_t(h) * a.Bmax + b) * a.Tmax;
@@ -105,8 +107,8 @@ naive_attn_kernel(NaiveArgs a) {
     buf_load16_lds_at(peres, st + kPeOff + wave * 1024, uint32_t(tp) * (kR * 2) + uint32_t((lane & 7) ^ pe_swz(prow)) * 16, 0);
   };
 
-  // ---- prologue: tile 0, the query as score operand (row s: 16 bytes at 16 ks + 8 g), a full
-  // wait (the query loads are the only compiler-tracked vector loads), then tiles 1 and 2
+  // ---- prologue: tiles 0 and 1, the query as score operand (row s: 16 bytes at 16 ks + 8 g), a
+  // full wait (the query loads are the only compiler-tracked vector loads), then tiles 2 and 3
   issue(0);
   u32x4 qf[12];
   {
@@ -121,9 +123,12 @@ naive_attn_kernel(NaiveArgs a) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) qf[8 + ks] = buf_load16(qp, srow * (kR * 2) + uint32_t(16 * ks + 8 * g) * 2, 0);
   }
-  wait_vmcnt<0>();
   issue(1);
-  issue(2);
+  wait_vmcnt<0>();
+  if (npairs > 1) {
+    issue(2);
+    issue(3);
+  }
 
   // score operand reads: tile row rho(l32), chunk 2 ks + g (k_nope) / 2 (ks - 8) + g (pe)
   const int arow = rho(l32);
@@ -151,39 +156,45 @@ naive_attn_kernel(NaiveArgs a) {
   float m_ref = -INFINITY, lsum = 0.f;
 
 #pragma unroll 1
-  for (int j = 0; j < ntiles; ++j) {
-    // tile j must have landed; tiles j+1, j+2 (if issued) may still be in flight
-    const int after = (j + 1 <= 2 || j + 1 < ntiles) + (j + 2 <= 2 || j + 2 < ntiles);
-    if (after == 2) wait_vmcnt<2 * kDmaPerTile>();
-    else if (after == 1) wait_vmcnt<kDmaPerTile>();
-    else wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();  // every wave's part of tile j is in; every wave is done with tile j-1
+  for (int p = 0; p < npairs; ++p) {
+    // pair p must have landed: pair 0 with the query, pair p > 0 as the latest issued
+    if (p > 0) wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();  // every wave's part of pair p is in; every wave is done with pair p - 1
     compiler_fence();
-    if (j + 3 < ntiles) issue(j + 3);  // into the stage of tile j-1
-    const unsigned char *st = smem + (j % kStages) * kStageBytes;
-    const int t0 = j * kTile;
+    if (p > 0 && p + 1 < npairs) {  // pair p + 1 into pair p - 1's stages (pair 1: issued ahead of the loop)
+      issue(2 * p + 2);
+      issue(2 * p + 3);
+    }
 
-    // scores S^T[position][row] (register r: position 16 (r / 8) + 8 g + r % 8)
-    f32x16 sacc = f32x16{};
-    {
+    // scores S^T[position][row] of the pair's two tiles
+    f32x16 sacc[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const unsigned char *st = smem + ((2 * p + u) % kStages) * kStageBytes;
       u32x4 fr[12];
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) fr[ks] = lds_read16(st, k_off[ks]);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) fr[8 + ks] = lds_read16(st, p_off[ks]);
+      sacc[u] = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < 12; ++ks) sacc = mfma32(fr[ks], qf[ks], sacc);
+      for (int ks = 0; ks < 12; ++ks) sacc[u] = mfma32(fr[ks], qf[ks], sacc[u]);
     }
-    if (t0 + kTile > wg_full) {  // wavefront-uniform: positions past some row's last visible one
+    const int t0 = 2 * p * kTile;
+    if (t0 + 2 * kTile > wg_full) {  // wavefront-uniform: positions past some row's last visible one
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int t = t0 + 16 * (r >> 3) + 8 * g + (r & 7);
-        if (t >= row_end) sacc[r] = -INFINITY;
-      }
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int t = t0 + kTile * u + 16 * (r >> 3) + 8 * g + (r & 7);
+          if (t >= row_end) sacc[u][r] = -INFINITY;
+        }
     }
     float mloc = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sacc[r]);
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sacc[u][r]);
     const float mrow = xor32_max(mloc) * a.scale_log2;
     if (m_ref == -INFINITY) {
       m_ref = mrow;
@@ -195,26 +206,30 @@ naive_attn_kernel(NaiveArgs a) {
       for (int i = 0; i < 4; ++i) acc[i] *= alpha;
     }
     const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
-    u32x4 pb[2];
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      float p[8];
+    for (int u = 0; u < 2; ++u) {
+      const unsigned char *st = smem + ((2 * p + u) % kStages) * kStageBytes;
+      u32x4 pb[2];
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        p[r] = fast_exp2(fmaf(sacc[8 * hh + r], a.scale_log2, -m_use));
-        lsum += p[r];
+      for (int hh = 0; hh < 2; ++hh) {
+        float pr[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          pr[r] = fast_exp2(fmaf(sacc[u][8 * hh + r], a.scale_log2, -m_use));
+          lsum += pr[r];
+        }
+        pb[hh] = u32x4{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]), pack_bf16x2(pr[4], pr[5]),
+                       pack_bf16x2(pr[6], pr[7])};
       }
-      pb[hh] = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+      // O^T[c][row] += V^T[c][position] . P^T[position][row]
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+          const u32x4 vf = lds_read_tr_pair(st, tr_off[cb][0] + ks * 16 * (kDv * 2), tr_off[cb][1] + ks * 16 * (kDv * 2));
+          acc[cb] = mfma32(vf, pb[ks], acc[cb]);
+        }
     }
-
-    // O^T[c][row] += V^T[c][position] . P^T[position][row]
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        const u32x4 vf = lds_read_tr_pair(st, tr_off[cb][0] + ks * 16 * (kDv * 2), tr_off[cb][1] + ks * 16 * (kDv * 2));
-        acc[cb] = mfma32(vf, pb[ks], acc[cb]);
-      }
   }
   wait_vmcnt<0>();  // tiles issued past the last needed one land before the workgroup ends
 
