@@ -130,10 +130,11 @@ int32_t mla_absorb_attn(const void *q_nope, const void *q_pe, const void *kv_cac
  *   max_seq_len  upper bound of the lengths; 1 <= S <= max_seq_len <= Tmax.  It plays the role
  *                of end_pos for validation and split planning.
  * workspace: mla_absorb_attn_ragged_workspace_size(shape, max_seq_len, ...) bytes.  With an
- * automatic split count the matrix-core kernels balance the batch on the device: every sequence
- * is cut into chunks of about one common length (a multiple of 32) chosen from the lengths, and
- * each workgroup takes one chunk, so long sequences take more workgroups than short ones (up to
- * four times the splits of a uniform batch) and the workgroups about equal work.
+ * automatic split count the matrix-core kernels plan the batch on the device from the lengths:
+ * a skewed batch (positions filling at most about a third of batch x the longest length) is cut
+ * into chunks of about one common length (a multiple of 32), one per workgroup, so long
+ * sequences take more workgroups than short ones (up to four times the splits of a uniform
+ * batch); any other batch keeps the uniform split count.
  * Every other argument, the layouts and the error behaviour are those of mla_absorb_attn;
  * out, workspace and seq_lens must not overlap.  Returns MLA_OK or a negative MLA_ERR_* status
  * (MLA_ERR_NULL / MLA_ERR_ALIGN for seq_lens).

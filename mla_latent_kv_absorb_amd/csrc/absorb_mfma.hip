@@ -134,6 +134,26 @@ __device__ int balanced_chunk(const int32_t *lens, int len0, int B, int S, int b
   return 32 * lo;
 }
 
+// Whether a ragged batch runs the uniform plan inside the balanced launch: when its positions
+// fill more than kUniformFill of B x the longest length.  Equal-length chunks pay off where a
+// few long sequences would leave most of the uniform plan's workgroups idle; on a near-uniform
+// spread the long sequences' extra chunks cost the combine more than they save.
+constexpr float kUniformFill = 0.35f;
+__device__ bool uniform_fits(const int32_t *lens, int len0, int B, int S, int bound, int lane) {
+  float tot = lane < B ? float(len0) : 0.f;
+  int mx = lane < B ? len0 : 0;
+  for (int i = lane + 64; i < B; i += 64) {
+    const int n = min(max(lens[i], S), bound);
+    tot += float(n);
+    mx = max(mx, n);
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    tot += __shfl_xor(tot, o);
+    mx = max(mx, __shfl_xor(mx, o));
+  }
+  return __builtin_amdgcn_readfirstlane(int(tot > kUniformFill * float(B) * float(mx)));
+}
+
 // Sequence and chunk of chunk rank r (chunks counted in sequence order), via a wave-wide prefix sum
 // of the sequences' chunk counts, 64 sequences at a time.  False if r is past the last chunk.
 __device__ bool balanced_find(const int32_t *lens, int len0, int B, int S, int bound, int smax, int cap, int L,
@@ -190,18 +210,28 @@ attn_kernel(AttnArgs a) {
   int bid = __builtin_amdgcn_readfirstlane(xcd_logical_id(blockIdx.x, gridDim.x));
   const int rb = __builtin_amdgcn_readfirstlane(bid % a.row_blocks);
   bid /= a.row_blocks;
-  // balanced ragged plan: bid is a chunk rank; the chunk length comes from all lengths
+  // balanced ragged plan: bid is a chunk rank, and the plan comes from all lengths
   const bool balanced = !kSparse && a.bal_target > 0;
   int split = __builtin_amdgcn_readfirstlane(bid % a.splits);
   int b = __builtin_amdgcn_readfirstlane(bid / a.splits);
-  int bal_L = 0;
+  int bal_L = 0;     // chunk length of the equal-chunk plan
+  int uni_len = 0;   // > 0: the batch runs the uniform plan with splits of this length
   if (balanced) {
     // lane l holds sequence l's clamped length (the first 64; more are re-read as needed)
     const int len0 = lane < a.B ? min(max(a.seq_lens[lane], a.S), a.end_pos) : 0;
-    bal_L = __builtin_amdgcn_readfirstlane(
-        balanced_chunk(a.seq_lens, len0, a.B, a.S, a.end_pos, a.splits, a.bal_cap, a.bal_target, lane));
-    if (!balanced_find(a.seq_lens, len0, a.B, a.S, a.end_pos, a.splits, a.bal_cap, bal_L, bid, lane, b, split))
-      return;  // fewer chunks than workgroups: nothing to do
+    if (uniform_fits(a.seq_lens, len0, a.B, a.S, a.end_pos, lane)) {
+      // every sequence s0 splits of the bound's length (the grid holds B s0 workgroups); the
+      // combine still reads only each sequence's non-empty ones
+      const int s0 = a.bal_target / a.B;
+      uni_len = __builtin_amdgcn_readfirstlane(((a.end_pos + s0 - 1) / s0 + 31) & ~31);
+      b = __builtin_amdgcn_readfirstlane(bid / s0);
+      split = __builtin_amdgcn_readfirstlane(bid - b * s0);
+    } else {
+      bal_L = __builtin_amdgcn_readfirstlane(
+          balanced_chunk(a.seq_lens, len0, a.B, a.S, a.end_pos, a.splits, a.bal_cap, a.bal_target, lane));
+      if (!balanced_find(a.seq_lens, len0, a.B, a.S, a.end_pos, a.splits, a.bal_cap, bal_L, bid, lane, b, split))
+        return;  // fewer chunks than workgroups: nothing to do
+    }
   }
 
   // this lane's query row (its column of the score tile)
@@ -216,8 +246,9 @@ attn_kernel(AttnArgs a) {
   // this sequence's share of its n_b chunks of about equal length, a multiple of 32.  Sparse: the
   // split covers list entries [t_begin, t_split_end) of one query token.
   int split_len = a.split_len, t_begin = split * a.split_len;
-  if (balanced) {  // chunk `split` of the sequence's chunks (split < their count by construction)
-    split_len = __builtin_amdgcn_readfirstlane(bal_len(end_pos, bal_L, a.splits, a.bal_cap));
+  if (balanced) {  // chunk `split` of the sequence's chunks (split < their count by construction,
+                   // except in the uniform plan, whose splits past the sequence are empty)
+    split_len = uni_len > 0 ? uni_len : __builtin_amdgcn_readfirstlane(bal_len(end_pos, bal_L, a.splits, a.bal_cap));
     t_begin = split * split_len;
     if (split == 0 && rb == 0)  // the chunk count, for the combine: one entry per query row
       for (int i = threadIdx.x; i < a.S; i += 256) a.bal_nb[b * a.S + i] = (end_pos + split_len - 1) / split_len;

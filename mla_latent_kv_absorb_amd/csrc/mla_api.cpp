@@ -42,8 +42,9 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
 // the entries.
 // With ragged (per-sequence lengths in device memory) and an automatic split count, the matrix-core
 // plan is the balanced one: as many workgroups as the uniform plan, each taking one chunk of one
-// sequence, the kernel picking one chunk length from all lengths so that long sequences take more
-// chunks (up to four times the uniform split count) and every workgroup about equal work.
+// sequence.  The kernel plans from all lengths: a skewed batch gets one chunk length so that long
+// sequences take more chunks (up to four times the uniform split count) and every workgroup
+// about equal work; any other batch keeps the uniform splits.
 int32_t plan_attn(const mla_attn_shape *shape, int64_t end_pos, const mla_paged_cache *paged, int64_t topk,
                   bool ragged, int32_t dtype, const mla_attn_options *options, mla::AttnCall &c, bool &use_mfma) {
   if (!shape) return fail(MLA_ERR_NULL, "shape is NULL");

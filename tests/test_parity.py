@@ -266,9 +266,9 @@ def test_ragged_small(gpu_lib, path, seqlen_q, lens):
 
 @pytest.mark.parametrize("lens", [[4096] + [1] * 31, [1] * 31 + [4096], [64 * (i + 1) for i in range(32)]])
 def test_ragged_balanced_full_heads(gpu_lib, lens):
-    """The balanced plan at the decode head shape: one long sequence among very short ones (it
-    takes up to four times the uniform plan's chunks), at either end of the chunk order, and a
-    linear spread of lengths; sampled rows."""
+    """The device plan at the decode head shape: one long sequence among very short ones (the
+    equal-chunk plan; it takes up to four times the uniform plan's chunks), at either end of the
+    chunk order, and a linear spread of lengths (the uniform splits); sampled rows."""
     cfg = ATTN_CONFIGS["dsv3_decode"]
     x = make_attn_inputs(cfg)
     t = to_dev(x, cfg)
@@ -281,20 +281,27 @@ def test_ragged_balanced_full_heads(gpu_lib, lens):
     check(np.stack([g[b, s_, h] for b, s_, h in rows]), ref, TOL["bf16"], f"balanced ragged lens[0]={lens[0]}")
 
 
+@pytest.mark.parametrize("mix", ["spread", "skewed"])
 @pytest.mark.parametrize("seqlen_q", [1, 3])
-def test_ragged_balanced_many_sequences(gpu_lib, seqlen_q):
-    """More than 64 sequences: the balanced plan's chunk-length search and chunk lookup walk the
-    lengths 64 at a time (130 sequences, lengths up to 600, some cut into several chunks)."""
+def test_ragged_balanced_many_sequences(gpu_lib, seqlen_q, mix):
+    """More than 64 sequences: the device plan walks the lengths 64 at a time.  A spread of
+    lengths up to 600 keeps the uniform splits; a skewed mix (a few at 600 among short ones)
+    takes the equal-chunk plan, with the long sequences cut into several chunks."""
     rng = np.random.default_rng(11)
     B = 130
-    lens = [int(v) for v in rng.integers(seqlen_q, 601, size=B)]
+    if mix == "spread":
+        lens = [int(v) for v in rng.integers(seqlen_q, 601, size=B)]
+    else:
+        lens = [int(v) for v in rng.integers(seqlen_q, 41, size=B)]
+        for i in (3, 50, 77, 90, 120):
+            lens[i] = int(rng.integers(300, 601))
     lens[7], lens[64], lens[100], lens[129] = 600, seqlen_q, 600, 257
     cfg = dsv3_small(batch=B, cache_batch=B, n_heads=16, seqlen_q=seqlen_q, end_pos=600, cache_len=640)
     x = make_attn_inputs(cfg)
     t = to_dev(x, cfg)
     poison_tails(t, lens)
     out = run_attn_ragged(gpu_lib, cfg, t, lens, path="mfma")
-    check(out, oracle_ragged(cfg, x, lens), TOL["bf16"], f"balanced ragged, {B} sequences, S={seqlen_q}")
+    check(out, oracle_ragged(cfg, x, lens), TOL["bf16"], f"ragged, {B} sequences ({mix}), S={seqlen_q}")
 
 
 @pytest.mark.parametrize("splits", [0, 8, 24])
