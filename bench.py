@@ -1,7 +1,7 @@
 """Benchmark: MLA absorb decode on one MI355X, DeepSeek-V3 decode shape.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dsv3_decode]
-                    [--no-extras] [--no-cpu-baseline]
+                    [--no-extras] [--no-cpu-baseline] [--no-peaks] [--sustained-ms MS]
 
 A step is one absorb-attention decode call (query absorption through W_UK, split-KV attention
 over kv_cache + pe_cache, merge and W_UV projection) over one batch: 32 sequences x 4096 cached
@@ -20,7 +20,11 @@ HBM bandwidth: algorithmic bytes per launch (the kv and pe cache rows it must re
 query) over its average duration, measured live by running the same timed steps again with HIP
 events that the kernel's own dispatch stamps on its stream (hipExtLaunchKernel start/stop events);
 those events add a queue barrier per timed dispatch, so that pass's step time is reported apart.
-`cpu_baseline` times the CPU oracle (NumPy, float64) on a bounded sample of the same workload.
+`cpu_baseline` times the CPU oracle (float32 NumPy, all host cores, and one core) on a bounded
+sample of the same workload.  `peaks_measured` holds what simple probe kernels reach on this machine
+(streaming read and copy, dense bf16 MFMA with its clock, LDS reads), and the fractions against
+them stand beside the fractions against the published peaks.  `sustained` is the decode step over
+a longer back-to-back run, after the chip's power management has settled its clocks.
 `extras` times the other workloads the same way: long_decode, chunk_prefill, ragged_decode (the
 decode batch with per-sequence lengths drawn uniformly from [256, 4096]) and skewed_decode (4 of
 its sequences at 4096 positions, 28 at 64), each also under the uniform split plan for
@@ -29,7 +33,8 @@ batch with its caches in pools of 64-position pages in random order), sparse_dec
 sparse_long_decode (the decode and long-context batches with each token attending to 2048 random
 positions of its cache through an index list), chunk_prefill_naive (the
 same chunk through the naive route: expansion of the 2 x 4096 cached latents, then attention over
-the expanded keys and values) and dsv3_expand.
+the expanded keys and values), dsv3_expand (four rotated input sets) and tiny_f32 (the fp32
+decode of one sequence, 4 heads, 128 positions).
 """
 from __future__ import annotations
 
@@ -185,28 +190,72 @@ def time_attn(cfg, steps, warmup, sets, torch, binding, seed=1, timed_kernels=0b
     return us, enqueue, kt
 
 
-def time_expand(cfg, steps, warmup, torch, binding, seed=4):
+def time_expand(cfg, steps, warmup, torch, binding, seed=4, sets=4, timed_kernels=0):
+    """GPU us per expansion over `sets` rotated input sets (c_kv, rms_w, wkv_b) and output pairs,
+    so that no call finds its operands in the Infinity Cache; with timed_kernels, also the
+    per-kernel timing dict."""
     g = torch.Generator(device="cuda")
     g.manual_seed(seed)
-    x = torch.randn((cfg.n_tokens, cfg.kv_lora_rank), generator=g, device="cuda").to(torch.bfloat16)
-    w = (1.0 + math.sqrt(cfg.rms_w_var) * torch.randn((cfg.kv_lora_rank,), generator=g, device="cuda")).to(torch.bfloat16)
-    wk = (torch.randn((cfg.n_heads * (cfg.qk_nope_head_dim + cfg.v_head_dim), cfg.kv_lora_rank), generator=g,
-                      device="cuda") * math.sqrt(cfg.wkv_b_var)).to(torch.bfloat16)
-    k = torch.empty((cfg.n_heads, cfg.n_tokens, cfg.qk_nope_head_dim), dtype=torch.bfloat16, device="cuda")
-    v = torch.empty((cfg.n_heads, cfg.n_tokens, cfg.v_head_dim), dtype=torch.bfloat16, device="cuda")
+    ins, outs = [], []
+    for _ in range(sets):
+        x = torch.randn((cfg.n_tokens, cfg.kv_lora_rank), generator=g, device="cuda").to(torch.bfloat16)
+        w = (1.0 + math.sqrt(cfg.rms_w_var) * torch.randn((cfg.kv_lora_rank,), generator=g, device="cuda")).to(
+            torch.bfloat16)
+        wk = (torch.randn((cfg.n_heads * (cfg.qk_nope_head_dim + cfg.v_head_dim), cfg.kv_lora_rank), generator=g,
+                          device="cuda") * math.sqrt(cfg.wkv_b_var)).to(torch.bfloat16)
+        ins.append((x, w, wk))
+    for _ in range(2):  # two output pairs (537 MB each) alternate
+        outs.append((torch.empty((cfg.n_heads, cfg.n_tokens, cfg.qk_nope_head_dim), dtype=torch.bfloat16, device="cuda"),
+                     torch.empty((cfg.n_heads, cfg.n_tokens, cfg.v_head_dim), dtype=torch.bfloat16, device="cuda")))
     need = binding.expand_kv_workspace_size(cfg.n_tokens, cfg.n_heads, cfg.kv_lora_rank, cfg.qk_nope_head_dim,
                                             cfg.v_head_dim, binding.MLA_DTYPE_BF16)
     ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
-    for _ in range(warmup):
+
+    def step(i):
+        x, w, wk = ins[i % sets]
+        k, v = outs[i % 2]
         binding.expand_kv(x, w, wk, cfg.n_heads, cfg.qk_nope_head_dim, cfg.v_head_dim, cfg.eps, k, v, workspace=ws)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    binding.timing_enable(timed_kernels)
+    binding.timing_collect()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        step(warmup + i)
+    e1.record()
+    torch.cuda.synchronize()
+    kt = binding.timing_collect()
+    binding.timing_enable(0)
+    del ins, outs, ws
+    torch.cuda.empty_cache()
+    us = e0.elapsed_time(e1) * 1000.0 / steps
+    progress(f"{cfg.name}: {us:.2f} us/step")
+    return (us, kt) if timed_kernels else us
+
+
+def time_tiny_f32(cfg, steps, warmup, torch, binding):
+    """The tiny fp32 decode (one sequence, 4 heads, 128 positions) on the plain kernels: launch
+    latency, not bandwidth, sets its time.  Inputs are the oracle tests' seeded ones."""
+    from mla_latent_kv_absorb_amd.workloads import make_attn_inputs
+
+    x = {k: torch.from_numpy(v).to("cuda") for k, v in make_attn_inputs(cfg).items()}
+    call = binding.AbsorbAttnCall(x["q_nope"], x["q_pe"], x["kv_cache"], x["pe_cache"], x["wkv_b"], cfg.end_pos,
+                                  cfg.softmax_scale)
+    for _ in range(warmup):
+        call()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(steps):
-        binding.expand_kv(x, w, wk, cfg.n_heads, cfg.qk_nope_head_dim, cfg.v_head_dim, cfg.eps, k, v, workspace=ws)
+        call()
     e1.record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) * 1000.0 / steps
+    us = e0.elapsed_time(e1) * 1000.0 / steps
+    progress(f"{cfg.name}: {us:.2f} us/step")
+    return us
 
 
 def naive_work(cfg):
@@ -266,40 +315,114 @@ def time_naive_route(cfg, steps, warmup, torch, binding, seed=3):
     return us, kt
 
 
-def cpu_baseline(cfg, budget_s=12.0):
-    """The CPU oracle (absorb route, float64 NumPy) on the first sequences of the workload.
-
-    Scaled to microseconds per full step; `cores` is the thread count the BLAS library used."""
+def cpu_baseline(cfg, n_seq=4):
+    """The CPU oracle's absorb route in float32 NumPy (BLAS-backed matmuls) on the first n_seq
+    sequences of the workload, all host cores and then one core: one warm-up call, then the
+    median of three timed calls, scaled to microseconds per full step (batch / n_seq)."""
     import numpy as np
 
     from mla_latent_kv_absorb_amd.workloads import make_attn_inputs
     from oracle import mla_oracle as O
 
     try:
-        from threadpoolctl import threadpool_info
-
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
-    n_seq = 4
+        from threadpoolctl import threadpool_info, threadpool_limits
+    except Exception:  # pragma: no cover - threadpoolctl ships with the image
+        threadpool_info = threadpool_limits = None
     sub = cfg.replace(batch=n_seq, cache_batch=n_seq)
     x = make_attn_inputs(sub, seed=cfg.seed)
-    reps, elapsed = 0, 0.0
-    t0 = time.perf_counter()
-    while elapsed < budget_s or reps < 2:
+
+    def run():
         O.absorb_attention(x["q_nope"], x["q_pe"], x["kv_cache"], x["pe_cache"], x["wkv_b"], cfg.end_pos,
-                           cfg.softmax_scale, cfg.v_head_dim)
-        reps += 1
-        elapsed = time.perf_counter() - t0
-        if reps >= 500:
-            break
-    per_call = elapsed / reps
-    us_per_step = per_call * 1e6 * cfg.batch / n_seq
-    progress(f"cpu baseline: {reps} oracle calls in {elapsed:.1f} s")
-    return {"value": round(us_per_step, 1), "unit": "us/step", "cores": int(threads), "kind": "oracle",
-            "sample": f"absorb route, float64, {n_seq} of {cfg.batch} sequences (same shapes otherwise), "
-                      f"{reps} calls in {elapsed:.1f} s, scaled by {cfg.batch}/{n_seq}",
-            "host_cpus": os.cpu_count()}
+                           cfg.softmax_scale, cfg.v_head_dim, dtype=np.float32)
+
+    def median_of_three():
+        run()
+        times = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            run()
+            times.append(time.perf_counter() - t0)
+        return sorted(times)[1]
+
+    threads = os.cpu_count() or 1
+    if threadpool_info is not None:
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    t_all = median_of_three()
+    t_one = None
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1, user_api="blas"):
+            t_one = median_of_three()
+    scale = cfg.batch / n_seq
+    progress(f"cpu baseline: {t_all * 1e3:.1f} ms on {threads} threads, "
+             f"{(t_one or 0) * 1e3:.1f} ms on 1, per {n_seq}-sequence call")
+    res = {"value": round(t_all * 1e6 * scale, 1), "unit": "us/step", "cores": int(threads), "kind": "oracle",
+           "sample": f"absorb route, float32 NumPy, {n_seq} of {cfg.batch} sequences (same shapes otherwise), "
+                     f"median of 3 calls after 1 warm-up, scaled by {cfg.batch}/{n_seq}",
+           "host_cpus": os.cpu_count()}
+    if t_one is not None:
+        res["single_core"] = {"value": round(t_one * 1e6 * scale, 1), "unit": "us/step", "cores": 1}
+    return res
+
+
+def measure_peaks(torch):
+    """What this machine's HBM, matrix cores and LDS deliver to simple kernels (the probes in
+    libmla_peaks.so): streaming read and copy bandwidth, dense bf16 MFMA rate with the engine clock
+    it ran at, and LDS read bytes per clock per compute unit."""
+    import ctypes
+
+    from mla_latent_kv_absorb_amd import build as B
+
+    lib = ctypes.CDLL(B.PEAKS_LIB_PATH)
+    vp, i32, u64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64
+    lib.mla_peak_read.argtypes = [vp, u64, vp, i32, vp]
+    lib.mla_peak_copy.argtypes = [vp, vp, u64, i32, vp]
+    lib.mla_peak_mfma.argtypes = [i32, i32, vp, vp, vp]
+    lib.mla_peak_lds.argtypes = [i32, i32, vp, vp, vp]
+    for f in (lib.mla_peak_read, lib.mla_peak_copy, lib.mla_peak_mfma, lib.mla_peak_lds):
+        f.restype = i32
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def timed(launch, reps):
+        for _ in range(2):
+            assert launch() == 0
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            assert launch() == 0
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    n = 2 << 30  # 2 GiB: far past the 256 MB Infinity Cache
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    sink = torch.zeros(1 << 20, dtype=torch.int32, device="cuda")
+    blocks = 256 * 8
+    t_read = timed(lambda: lib.mla_peak_read(a.data_ptr(), n, sink.data_ptr(), blocks, stream), 10)
+    half = n // 2
+    t_copy = timed(lambda: lib.mla_peak_copy(a.data_ptr(), a.data_ptr() + half, half, blocks, stream), 10)
+    del a
+    iters, mblocks = 4096, 256 * 4
+    clocks = torch.zeros(2 * mblocks, dtype=torch.int64, device="cuda")
+    fsink = torch.zeros(mblocks * 256, dtype=torch.float32, device="cuda")
+    t_mfma = timed(lambda: lib.mla_peak_mfma(iters, mblocks, fsink.data_ptr(), clocks.data_ptr(), stream), 5)
+    c = clocks.view(mblocks, 2).double()
+    mhz = float((c[:, 0] / c[:, 1]).median()) * 100.0  # shader clocks per 100 MHz real-time tick
+    flops = mblocks * 4 * iters * 8 * 32768
+    lclocks = torch.zeros(512, dtype=torch.int64, device="cuda")
+    liters = 2048
+    t_lds = timed(lambda: lib.mla_peak_lds(liters, 512, sink.data_ptr(), lclocks.data_ptr(), stream), 5)
+    lds_cyc = float(lclocks.double().median())
+    # two workgroups per compute unit (64 KB of LDS each), each moving 4 waves x 8 x 1 KB per iteration
+    lds_bpc = 2 * 4 * 8 * 1024 * liters / lds_cyc
+    del clocks, fsink, lclocks, sink
+    torch.cuda.empty_cache()
+    res = {"read_gbs": round(n / t_read / 1e9, 1), "copy_gbs": round(2 * half / t_copy / 1e9, 1),
+           "mfma_bf16_tflops": round(flops / t_mfma / 1e12, 1), "mfma_clock_mhz": round(mhz, 0),
+           "lds_read_bytes_per_clk_per_cu": round(lds_bpc, 1), "lds_wall_gbs": round(512 * 4 * 8 * 1024 * liters / t_lds / 1e9, 1)}
+    progress(f"peaks: {res}")
+    return res
 
 
 def traffic_for(kernel_src, name):
@@ -326,6 +449,9 @@ def main():
     ap.add_argument("--sets", type=int, default=4, help="input sets rotated over (cold Infinity Cache)")
     ap.add_argument("--no-extras", action="store_true", help="skip timing the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the streaming / matrix-core / LDS peak probes")
+    ap.add_argument("--sustained-ms", type=float, default=40.0,
+                    help="length of the labelled sustained-load decode run (0 to skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB, --steps times (reference "
                          "kernel of known size for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -358,6 +484,7 @@ def main():
         print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "dispatches": args.steps}))
         return
 
+    peaks = None if args.no_peaks else measure_peaks(torch)
     cfg = ATTN_CONFIGS[args.workload]
     work = attn_work(cfg)
     # the step time: no per-kernel events in the timed steps (each timed dispatch adds a queue
@@ -379,6 +506,9 @@ def main():
         roofline = {"kernel": "attn_kernel", "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic_for(src, "attn_kernel"),
                     "algorithmic_bytes": kb, "avg_us": round(attn["avg_us"], 2), "launches": attn["launches"]}
+        if peaks:
+            roofline["measured_peak"] = peaks["read_gbs"]
+            roofline["frac_measured_peak"] = round(ach / peaks["read_gbs"], 4)
 
     line = {
         "metric": METRIC,
@@ -408,6 +538,16 @@ def main():
         "roofline": roofline,
         "kernels_us": {n: round(v["avg_us"], 2) for n, v in kt_all.items()},
     }
+    if peaks:
+        line["peaks_measured"] = peaks
+        line["hbm_frac_measured_peak"] = round(gbs / peaks["read_gbs"], 4)
+        line["mfma_frac_measured_peak"] = round(tflops / peaks["mfma_bf16_tflops"], 4)
+    if args.sustained_ms > 0:
+        # a labelled extra: back-to-back steps for sustained_ms of GPU time (the chip's power
+        # management lowers its clocks after a few milliseconds of load)
+        n = max(args.steps, int(args.sustained_ms * 1000.0 / us))
+        su, _, _ = time_attn(cfg, n, args.warmup, args.sets, torch, binding, timed_kernels=0)
+        line["sustained"] = {"us_per_step": round(su, 2), "steps": n, "gpu_ms": round(su * n / 1000.0, 1)}
 
     if not args.no_extras:
         extras = {}
@@ -463,10 +603,19 @@ def main():
             "naive_attn_gbps": round(w["bytes"] / (a_us * 1e-6) / 1e9, 1)}
         ec = EXPAND_CONFIGS["dsv3_expand"]
         u = time_expand(ec, 20, 3, torch, binding)
+        _, k = time_expand(ec, 20, 3, torch, binding, timed_kernels=(1 << 3) | (1 << 4))
         w = expand_work(ec)
+        tf = w["flops"] / (u * 1e-6) / 1e12
         extras["dsv3_expand"] = {"us_per_step": round(u, 2), "gbps": round(w["bytes"] / (u * 1e-6) / 1e9, 1),
-                                 "tflops": round(w["flops"] / (u * 1e-6) / 1e12, 2),
-                                 "mfma_frac": round(w["flops"] / (u * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+                                 "tflops": round(tf, 2), "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                                 "kernels_us": {n: round(v["avg_us"], 2) for n, v in k.items()}}
+        if peaks:
+            extras["dsv3_expand"]["mfma_frac_measured_peak"] = round(tf / peaks["mfma_bf16_tflops"], 4)
+        tc = ATTN_CONFIGS["tiny_f32"]
+        tw = attn_work(tc)
+        u = time_tiny_f32(tc, 200, 20, torch, binding)
+        extras["tiny_f32"] = {"us_per_step": round(u, 2), "note": "fp32, plain kernels; launch latency bound",
+                              "gbps": round(tw["bytes"] * 2 / (u * 1e-6) / 1e9, 3)}
         line["extras"] = extras
 
     if not args.no_cpu_baseline:

@@ -21,9 +21,10 @@
  *   - Data pointers are DEVICE pointers (hipMalloc'd or torch CUDA tensors) on the current HIP
  *     device; the caller owns every buffer, including the workspace.  The library keeps no
  *     pointer after a call returns and never modifies inputs.
- *   - All tensors are dense, row-major (innermost index contiguous) and of one element type:
- *     MLA_DTYPE_F32 (float) or MLA_DTYPE_BF16 (bfloat16 stored as uint16).  Every pointer must
- *     be 16-byte aligned.
+ *   - All tensors are row-major (innermost index contiguous) and of one element type:
+ *     MLA_DTYPE_F32 (float) or MLA_DTYPE_BF16 (bfloat16 stored as uint16).  They are dense
+ *     unless mla_attn_options.strides says otherwise (the absorb-attention entry points only).
+ *     Every pointer must be 16-byte aligned.
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL means the default stream); results
  *     are valid once the stream has synchronised.  Calls on one stream are ordered; concurrent
  *     calls on different streams must not share a workspace.
@@ -76,10 +77,37 @@ typedef struct mla_attn_shape {
   int64_t cache_len;        /* Tmax positions allocated per cache row (>= end_pos)              */
 } mla_attn_shape;
 
+/*
+ * Element strides of the tensors of an absorb-attention call, for tensors that are views of larger
+ * ones.  The page's absorb path splits each head's query into its no-rope part q_nope and its
+ * rotary part q_pe ("Naive vs Absorb Attention Implementations in DeepSeek-V3", section "Absorb
+ * Path Execution"), so the two usually arrive as the two halves of one [B, S, H, Dn + R] tensor:
+ * then q_nope_row = q_pe_row = Dn + R and q_pe points Dn elements past q_nope.  Likewise kv_cache
+ * and pe_cache may be the two parts of one [Bmax, Tmax, C + R] cache (kv_pos = pe_pos = C + R).
+ *
+ * The innermost index is always contiguous.  A field of 0 means the dense value given in its
+ * comment.  A query row is one (b, s, h); rows are evenly spaced: row (b, s, h) of q_nope starts
+ * at ((b * S + s) * H + h) * q_nope_row.  Every stride must be at least the row width it steps
+ * over and keep every row 16-byte aligned (a multiple of 16 bytes); the extents they imply are
+ * what the overlap checks and the kernels' bounds use.
+ */
+typedef struct mla_attn_strides {
+  int64_t q_nope_row; /* between consecutive query rows of q_nope; dense: Dn                    */
+  int64_t q_pe_row;   /* between consecutive query rows of q_pe; dense: R                       */
+  int64_t out_row;    /* between consecutive rows of out; dense: Dv                             */
+  int64_t kv_batch;   /* between cache rows b and b + 1 of kv_cache; dense: Tmax * kv_pos       */
+  int64_t kv_pos;     /* between positions t and t + 1 of kv_cache (and of a kv page); dense: C */
+  int64_t pe_batch;   /* between cache rows b and b + 1 of pe_cache; dense: Tmax * pe_pos       */
+  int64_t pe_pos;     /* between positions t and t + 1 of pe_cache (and of a pe page); dense: R */
+} mla_attn_strides;
+
 /* Optional knobs of mla_absorb_attn; pass NULL for the defaults (all zero). */
 typedef struct mla_attn_options {
   int32_t num_splits; /* 0: the planner chooses; n > 0: split [0, end_pos) into n ranges        */
   int32_t path;       /* MLA_PATH_*                                                             */
+  const mla_attn_strides *strides; /* NULL: every tensor dense (row-major, no gaps).  Page pools
+                                      take kv_pos / pe_pos (rows within and across pages; a
+                                      page is page_size such rows) and ignore the batch strides */
 } mla_attn_options;
 
 /*

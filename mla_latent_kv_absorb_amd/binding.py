@@ -50,8 +50,14 @@ class PagedCache(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in ("page_size", "num_pages", "max_pages_per_seq")]
 
 
+class AttnStrides(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in (
+        "q_nope_row", "q_pe_row", "out_row", "kv_batch", "kv_pos", "pe_batch", "pe_pos")]
+
+
 class AttnOptions(ctypes.Structure):
-    _fields_ = [("num_splits", ctypes.c_int32), ("path", ctypes.c_int32)]
+    _fields_ = [("num_splits", ctypes.c_int32), ("path", ctypes.c_int32),
+                ("strides", ctypes.POINTER(AttnStrides))]
 
 
 class MLAError(RuntimeError):
@@ -167,33 +173,76 @@ def _stream_handle(device) -> Optional[int]:
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def _require_device(*ts) -> None:
+def _require_device(*ts, contiguous: bool = True) -> None:
     dev = ts[0].device
     for t in ts:
         if not t.is_cuda:
             raise ValueError("tensors must live on a GPU device")
         if t.device != dev:
             raise ValueError("all tensors must be on the same device")
-        if not t.is_contiguous():
+        if contiguous and not t.is_contiguous():
             raise ValueError("tensors must be contiguous")
         if t.dtype != ts[0].dtype:
             raise ValueError("all tensors must share one dtype")
 
 
-def attn_shape(q_nope, q_pe, kv_cache, wkv_b) -> AttnShape:
+def _shape(t, want, name: str) -> None:
+    if tuple(t.shape) != tuple(want):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(want)}")
+
+
+def _row_stride(t, name: str) -> int:
+    """Element stride between the evenly spaced rows of a tensor whose leading dimensions all
+    step by whole rows (e.g. q[..., :Dn] of a contiguous q); 0 when the rows are dense."""
+    if t.stride(-1) != 1 and t.shape[-1] > 1:
+        raise ValueError(f"{name}: the innermost dimension must be contiguous")
+    rs = None
+    step = None
+    for d in range(t.dim() - 2, -1, -1):  # innermost leading dimension first
+        if t.shape[d] == 1:
+            continue
+        if rs is None:
+            rs, step = t.stride(d), t.stride(d) * t.shape[d]
+        elif t.stride(d) != step:
+            raise ValueError(f"{name}: rows of the leading dimensions are not evenly spaced")
+        else:
+            step *= t.shape[d]
+    return 0 if rs is None or rs == t.shape[-1] else int(rs)
+
+
+def _cache_strides(t, name: str):
+    """(batch, position) element strides of a [Bmax, Tmax, D] cache view; 0 where dense."""
+    if t.stride(2) != 1 and t.shape[2] > 1:
+        raise ValueError(f"{name}: the innermost dimension must be contiguous")
+    pos = t.stride(1) if t.shape[1] > 1 else t.shape[2]
+    bat = t.stride(0) if t.shape[0] > 1 else t.shape[1] * pos
+    return (0 if bat == t.shape[1] * pos and pos == t.shape[2] else int(bat), 0 if pos == t.shape[2] else int(pos))
+
+
+def attn_shape(q_nope, q_pe, kv_cache, wkv_b, pe_cache=None) -> AttnShape:
+    """The shape descriptor of an absorb-attention call, with every tensor's shape checked against
+    it (the library only sees pointers, so a mismatch must be caught here)."""
+    if q_nope.dim() != 4 or q_pe.dim() != 4 or kv_cache.dim() != 3 or wkv_b.dim() != 2:
+        raise ValueError("expected q_nope [B,S,H,Dn], q_pe [B,S,H,R], kv_cache [Bmax,Tmax,C], wkv_b [H*(Dn+Dv),C]")
     B, S, H, Dn = q_nope.shape
     R = q_pe.shape[-1]
     Bmax, Tmax, C = kv_cache.shape
-    if wkv_b.shape[0] % H:
-        raise ValueError("wkv_b rows must be a multiple of n_heads")
+    _shape(q_pe, (B, S, H, R), "q_pe")
+    if wkv_b.shape[1] != C:
+        raise ValueError(f"wkv_b has {wkv_b.shape[1]} columns, kv_cache rows have {C}")
+    if wkv_b.shape[0] % H or wkv_b.shape[0] // H <= Dn:
+        raise ValueError("wkv_b rows must be n_heads * (qk_nope_head_dim + v_head_dim) with v_head_dim >= 1")
     Dv = wkv_b.shape[0] // H - Dn
+    if pe_cache is not None:
+        _shape(pe_cache, (Bmax, Tmax, R), "pe_cache")
     return AttnShape(B, S, H, C, R, Dn, Dv, Bmax, Tmax)
 
 
 def absorb_attn_workspace_size(shape: AttnShape, end_pos: int, dtype: int, num_splits: int = 0,
-                               path: str = "auto") -> int:
+                               path: str = "auto",
+        strides: Optional[AttnStrides] = None) -> int:
     lib = load()
-    opt = AttnOptions(num_splits, PATHS[path])
+    opt = AttnOptions(num_splits, PATHS[path], None if strides is None else ctypes.pointer(strides))
     n = lib.mla_absorb_attn_workspace_size(ctypes.byref(shape), end_pos, dtype, ctypes.byref(opt))
     if n == 0 and last_error():
         raise MLAError(MLA_ERR_SHAPE, last_error())
@@ -201,9 +250,10 @@ def absorb_attn_workspace_size(shape: AttnShape, end_pos: int, dtype: int, num_s
 
 
 def absorb_attn_ragged_workspace_size(shape: AttnShape, max_seq_len: int, dtype: int, num_splits: int = 0,
-                                      path: str = "auto") -> int:
+                                      path: str = "auto",
+        strides: Optional[AttnStrides] = None) -> int:
     lib = load()
-    opt = AttnOptions(num_splits, PATHS[path])
+    opt = AttnOptions(num_splits, PATHS[path], None if strides is None else ctypes.pointer(strides))
     n = lib.mla_absorb_attn_ragged_workspace_size(ctypes.byref(shape), max_seq_len, dtype, ctypes.byref(opt))
     if n == 0 and last_error():
         raise MLAError(MLA_ERR_SHAPE, last_error())
@@ -211,9 +261,10 @@ def absorb_attn_ragged_workspace_size(shape: AttnShape, max_seq_len: int, dtype:
 
 
 def absorb_attn_paged_workspace_size(shape: AttnShape, max_seq_len: int, paged: PagedCache, dtype: int,
-                                     num_splits: int = 0, path: str = "auto") -> int:
+                                     num_splits: int = 0, path: str = "auto",
+        strides: Optional[AttnStrides] = None) -> int:
     lib = load()
-    opt = AttnOptions(num_splits, PATHS[path])
+    opt = AttnOptions(num_splits, PATHS[path], None if strides is None else ctypes.pointer(strides))
     n = lib.mla_absorb_attn_paged_workspace_size(ctypes.byref(shape), max_seq_len, ctypes.byref(paged), dtype,
                                                  ctypes.byref(opt))
     if n == 0 and last_error():
@@ -222,9 +273,10 @@ def absorb_attn_paged_workspace_size(shape: AttnShape, max_seq_len: int, paged: 
 
 
 def absorb_attn_sparse_workspace_size(shape: AttnShape, end_pos: int, topk: int, dtype: int, num_splits: int = 0,
-                                      path: str = "auto") -> int:
+                                      path: str = "auto",
+        strides: Optional[AttnStrides] = None) -> int:
     lib = load()
-    opt = AttnOptions(num_splits, PATHS[path])
+    opt = AttnOptions(num_splits, PATHS[path], None if strides is None else ctypes.pointer(strides))
     n = lib.mla_absorb_attn_sparse_workspace_size(ctypes.byref(shape), end_pos, topk, dtype, ctypes.byref(opt))
     if n == 0 and last_error():
         raise MLAError(MLA_ERR_SHAPE, last_error())
@@ -252,12 +304,12 @@ class AbsorbAttnCall:
         import torch
 
         lib = load()
-        _require_device(q_nope, q_pe, kv_cache, pe_cache, wkv_b)
         shape = attn_shape(q_nope, q_pe, kv_cache, wkv_b)
-        dt = _dtype_code(q_nope)
         for name, t in (("seq_lens", seq_lens), ("block_table", block_table), ("indices", indices)):
             if t is not None and (t.device != q_nope.device or t.dtype != torch.int32 or not t.is_contiguous()):
                 raise ValueError(f"{name} must be a contiguous int32 tensor on the tensors' device")
+        if indices is not None and (indices.dim() != 3 or tuple(indices.shape[:2]) != (shape.batch, shape.seqlen_q)):
+            raise ValueError("indices must be [batch, seqlen_q, topk]")
         if seq_lens is not None and seq_lens.numel() != shape.batch:
             raise ValueError("seq_lens must hold one length per sequence")
         paged = None
@@ -265,32 +317,48 @@ class AbsorbAttnCall:
             if block_table.dim() != 2 or block_table.shape[0] != shape.batch:
                 raise ValueError("block_table must be [batch, max_pages_per_seq]")
             num_pages, page_size = kv_cache.shape[0], kv_cache.shape[1]
-            if tuple(pe_cache.shape[:2]) != (num_pages, page_size):
-                raise ValueError("kv and pe page pools disagree")
+            _shape(pe_cache, (num_pages, page_size, shape.qk_rope_head_dim), "pe_cache (page pool)")
+            for name, t in (("kv_cache", kv_cache), ("pe_cache", pe_cache)):
+                if num_pages > 1 and t.stride(0) != page_size * t.stride(1):
+                    raise ValueError(f"{name}: pages of a pool must follow each other at page_size rows")
             paged = PagedCache(page_size, num_pages, block_table.shape[1])
             shape.cache_batch, shape.cache_len = shape.batch, block_table.shape[1] * page_size
+        else:
+            _shape(pe_cache, (shape.cache_batch, shape.cache_len, shape.qk_rope_head_dim), "pe_cache")
+        if out is not None:
+            _shape(out, (shape.batch, shape.seqlen_q, shape.n_heads, shape.v_head_dim), "out")
+        # q_nope, q_pe, the caches and out may be strided views (evenly spaced rows, contiguous
+        # innermost dimension); the weight is dense
+        _require_device(q_nope, q_pe, kv_cache, pe_cache, wkv_b, contiguous=False)
+        _require_device(wkv_b)
+        dt = _dtype_code(q_nope)
         if out is None:
             out = torch.empty((shape.batch, shape.seqlen_q, shape.n_heads, shape.v_head_dim), dtype=q_nope.dtype,
                               device=q_nope.device)
-        _require_device(q_nope, out)
-        opt = AttnOptions(num_splits, PATHS[path])
+        _require_device(q_nope, out, contiguous=False)
+        kv_b, kv_p = _cache_strides(kv_cache, "kv_cache")
+        pe_b, pe_p = _cache_strides(pe_cache, "pe_cache")
+        strides = AttnStrides(_row_stride(q_nope, "q_nope"), _row_stride(q_pe, "q_pe"), _row_stride(out, "out"),
+                              kv_b, kv_p, pe_b, pe_p)
+        sp = None if all(getattr(strides, f) == 0 for f, _ in AttnStrides._fields_) else strides
+        opt = AttnOptions(num_splits, PATHS[path], None if sp is None else ctypes.pointer(strides))
         if indices is not None:
             if block_table is not None:
                 raise ValueError("index lists over paged caches are not supported")
             if indices.dim() != 3 or tuple(indices.shape[:2]) != (shape.batch, shape.seqlen_q):
                 raise ValueError("indices must be [batch, seqlen_q, topk]")
-            need = absorb_attn_sparse_workspace_size(shape, end_pos, indices.shape[2], dt, num_splits, path)
+            need = absorb_attn_sparse_workspace_size(shape, end_pos, indices.shape[2], dt, num_splits, path, sp)
         elif paged is None and seq_lens is not None:
-            need = absorb_attn_ragged_workspace_size(shape, end_pos, dt, num_splits, path)
+            need = absorb_attn_ragged_workspace_size(shape, end_pos, dt, num_splits, path, sp)
         elif paged is None:
-            need = absorb_attn_workspace_size(shape, end_pos, dt, num_splits, path)
+            need = absorb_attn_workspace_size(shape, end_pos, dt, num_splits, path, sp)
         else:
-            need = absorb_attn_paged_workspace_size(shape, end_pos, paged, dt, num_splits, path)
+            need = absorb_attn_paged_workspace_size(shape, end_pos, paged, dt, num_splits, path, sp)
         if workspace is None or workspace.numel() * workspace.element_size() < need:
             workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q_nope.device)
         self.out = out
-        self._keep = (q_nope, q_pe, kv_cache, pe_cache, wkv_b, out, workspace, shape, opt, seq_lens, block_table,
-                      paged, indices)
+        self._keep = (q_nope, q_pe, kv_cache, pe_cache, wkv_b, out, workspace, shape, opt, strides, seq_lens,
+                      block_table, paged, indices)
         tail = (softmax_scale, out.data_ptr(), ctypes.byref(shape), dt, ctypes.byref(opt), workspace.data_ptr(),
                 workspace.numel() * workspace.element_size(), _stream_handle(q_nope.device))
         head = (q_nope.data_ptr(), q_pe.data_ptr(), kv_cache.data_ptr(), pe_cache.data_ptr(), wkv_b.data_ptr())
@@ -337,12 +405,16 @@ def cache_append(c_kv_new, k_pe_new, rms_w, eps: float, end_pos: int, kv_cache, 
     import torch
 
     lib = load()
-    _require_device(c_kv_new, k_pe_new, rms_w, kv_cache, pe_cache)
+    if c_kv_new.dim() != 3 or k_pe_new.dim() != 3 or kv_cache.dim() != 3:
+        raise ValueError("expected c_kv_new [B,S,C], k_pe_new [B,S,R], kv_cache [Bmax,Tmax,C] (or pools)")
     B, S, C = c_kv_new.shape
     R = k_pe_new.shape[-1]
     Bmax, Tmax, _ = kv_cache.shape
-    if tuple(k_pe_new.shape[:2]) != (B, S) or tuple(pe_cache.shape[:2]) != (Bmax, Tmax):
-        raise ValueError("k_pe_new / pe_cache shapes disagree with c_kv_new / kv_cache")
+    _shape(k_pe_new, (B, S, R), "k_pe_new")
+    _shape(rms_w, (C,), "rms_w")
+    _shape(kv_cache, (Bmax, Tmax, C), "kv_cache")
+    _shape(pe_cache, (Bmax, Tmax, R), "pe_cache")
+    _require_device(c_kv_new, k_pe_new, rms_w, kv_cache, pe_cache)
     shape = AttnShape(B, S, 1, C, R, 0, 0, Bmax, Tmax)
     lens_ptr = None
     if seq_lens is not None:
@@ -372,13 +444,18 @@ def naive_attn(q_nope, q_pe, k_nope, v, pe_cache, end_pos: int, softmax_scale: f
     import torch
 
     lib = load()
-    _require_device(q_nope, q_pe, k_nope, v, pe_cache)
+    if q_nope.dim() != 4 or q_pe.dim() != 4 or k_nope.dim() != 4 or v.dim() != 4 or pe_cache.dim() != 3:
+        raise ValueError("expected q_nope/q_pe [B,S,H,.], k_nope/v [H,Bmax,Tmax,.], pe_cache [Bmax,Tmax,R]")
     B, S, H, Dn = q_nope.shape
     R = q_pe.shape[-1]
     Hk, Bmax, Tmax, Dk = k_nope.shape
     Dv = v.shape[-1]
+    _shape(q_pe, (B, S, H, R), "q_pe")
     if Hk != H or Dk != Dn or tuple(v.shape[:3]) != (H, Bmax, Tmax) or tuple(pe_cache.shape) != (Bmax, Tmax, R):
         raise ValueError("k_nope / v / pe_cache shapes disagree with the query")
+    if out is not None:
+        _shape(out, (B, S, H, Dv), "out")
+    _require_device(q_nope, q_pe, k_nope, v, pe_cache)
     if out is None:
         out = torch.empty((B, S, H, Dv), dtype=q_nope.dtype, device=q_nope.device)
     _require_device(q_nope, out)
@@ -405,8 +482,16 @@ def expand_kv(c_kv, rms_w, wkv_b, n_heads: int, qk_nope_head_dim: int, v_head_di
     import torch
 
     lib = load()
-    _require_device(c_kv, rms_w, wkv_b)
+    if c_kv.dim() != 2:
+        raise ValueError("c_kv must be [n_tokens, kv_lora_rank]")
     T, C = c_kv.shape
+    _shape(rms_w, (C,), "rms_w")
+    _shape(wkv_b, (n_heads * (qk_nope_head_dim + v_head_dim), C), "wkv_b")
+    if k_nope is not None:
+        _shape(k_nope, (n_heads, T, qk_nope_head_dim), "k_nope")
+    if v is not None:
+        _shape(v, (n_heads, T, v_head_dim), "v")
+    _require_device(c_kv, rms_w, wkv_b)
     if k_nope is None:
         k_nope = torch.empty((n_heads, T, qk_nope_head_dim), dtype=c_kv.dtype, device=c_kv.device)
     if v is None:

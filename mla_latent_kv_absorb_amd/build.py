@@ -22,6 +22,10 @@ BUILD_DIR = os.path.join(HERE, "_build")
 
 SOURCES = ["mla_api.cpp", "timing.cpp", "plain_kernels.hip", "absorb_mfma.hip", "expand_mfma.hip", "cache_append.hip",
            "naive_mfma.hip"]
+# peak probes for the benchmark (streaming read and copy, matrix-core and LDS rates): a library of
+# their own, never linked into the attention library
+PEAKS_SOURCES = ["peaks.hip"]
+PEAKS_LIB_PATH = os.path.join(HERE, "libmla_peaks.so")
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -56,20 +60,26 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    """Compile every source and link the shared library; returns its path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    srcs = [s for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB_PATH + ".tmp"
+def _link(objs, path: str) -> None:
+    tmp = path + ".tmp"
     cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, path)
+
+
+def build(verbose: bool = True) -> str:
+    """Compile every source and link the attention library and the probe library; returns the
+    attention library's path."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = [s for s in SOURCES + PEAKS_SOURCES if os.path.exists(os.path.join(CSRC, s))]
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES if s in objs], LIB_PATH)
+    _link([objs[s] for s in PEAKS_SOURCES if s in objs], PEAKS_LIB_PATH)
     if verbose:
-        print(f"built {LIB_PATH}")
+        print(f"built {LIB_PATH} and {PEAKS_LIB_PATH}")
     return LIB_PATH
 
 

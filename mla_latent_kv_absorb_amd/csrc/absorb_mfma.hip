@@ -76,6 +76,8 @@ struct AttnArgs {
   uint16_t *part_o;        // [rows, splits, 512] (unnormalised, relative to the max; with one
                            // split: normalised, i.e. o_lat)
   int64_t Tmax;
+  int64_t kv_bs, pe_bs;    // element strides between cache rows b and b + 1 (contiguous caches)
+  int32_t kv_rb, pe_rb;    // bytes between positions t and t + 1 (and between rows of a page)
   int32_t S, H, SH;        // SH = S * H rows per sequence
   int32_t end_pos, splits, split_len, row_blocks;  // end_pos: uniform length or the bound of seq_lens
   const int32_t *seq_lens;  // per-sequence lengths [B] or null (every sequence has end_pos)
@@ -289,8 +291,10 @@ attn_kernel(AttnArgs a) {
   // t_begin / page_size + slot), read per tile with v_readlane; tile 0's id comes from a scalar
   // load so that its DMA need not wait for them.  Rows are clamped into [t0, t0 + 31] as well,
   // which keeps every offset inside the page even for a workgroup with no tile to compute.
-  const rsrc_t kvres = make_rsrc(a.kv + (kPaged ? 0 : int64_t(b) * a.Tmax * kC), kPaged ? 0u : uint32_t(a.Tmax) * (kC * 2));
-  const rsrc_t peres = make_rsrc(a.pe + (kPaged ? 0 : int64_t(b) * a.Tmax * kR), kPaged ? 0u : uint32_t(a.Tmax) * (kR * 2));
+  const rsrc_t kvres = make_rsrc(a.kv + (kPaged ? 0 : int64_t(b) * a.kv_bs),
+                                 kPaged ? 0u : uint32_t(a.Tmax - 1) * uint32_t(a.kv_rb) + kC * 2);
+  const rsrc_t peres = make_rsrc(a.pe + (kPaged ? 0 : int64_t(b) * a.pe_bs),
+                                 kPaged ? 0u : uint32_t(a.Tmax - 1) * uint32_t(a.pe_rb) + kR * 2);
   const int pg_first = t_begin >> a.log2_page;
   int ptab[kPageRegs];
   int page0 = 0;
@@ -351,8 +355,8 @@ attn_kernel(AttnArgs a) {
     if constexpr (kPaged) {
       const int t0 = t_begin + j * kTile;
       const int64_t page = tile_page(j, t0);
-      return TileSrc{make_rsrc(a.kv + (page << (a.log2_page + 9)), uint32_t(kC * 2) << a.log2_page),
-                     make_rsrc(a.pe + (page << (a.log2_page + 6)), uint32_t(kR * 2) << a.log2_page),
+      return TileSrc{make_rsrc(a.kv + (page << a.log2_page) * (a.kv_rb >> 1), uint32_t(a.kv_rb) << a.log2_page),
+                     make_rsrc(a.pe + (page << a.log2_page) * (a.pe_rb >> 1), uint32_t(a.pe_rb) << a.log2_page),
                      t0 & ~((1 << a.log2_page) - 1), max(wg_end - 1, t0), 0, 0, 0};
     } else if constexpr (kSparse) {
       const int cur = sparse_reg(j), lo = (j & 1) * 32;
@@ -368,21 +372,22 @@ attn_kernel(AttnArgs a) {
     if (kSparse && part < 8) {
       const int t = min(max(__builtin_amdgcn_readlane(src.cur, src.lo + wave * 8 + part), 0), end_pos - 1);
       buf_load16_lds_at(src.kv, st + (wave * 8 + part) * (kC * 2),
-                        lane16 ^ uint32_t(kv_swz(8 * (wave & 1) + part) * 16), uint32_t(t) * (kC * 2));
+                        lane16 ^ uint32_t(kv_swz(8 * (wave & 1) + part) * 16), uint32_t(t) * uint32_t(a.kv_rb));
     } else if (kSparse) {
-      buf_load16_lds_at(src.pe, st + kKvTileBytes + wave * 8 * (kR * 2), pe_voff + uint32_t(src.pidx) * (kR * 2), 0);
+      buf_load16_lds_at(src.pe, st + kKvTileBytes + wave * 8 * (kR * 2),
+                        pe_voff + uint32_t(src.pidx) * uint32_t(a.pe_rb), 0);
     } else if (part < 8) {
       const int t = min(t0 + wave * 8 + part, src.tlast);  // wavefront-uniform
       // source chunk swz_chunk(lane, row) = lane ^ kv_swz(row), kv_swz(row) wavefront-uniform
       buf_load16_lds_at(src.kv, st + (wave * 8 + part) * (kC * 2),
-                        lane16 ^ uint32_t(kv_swz(8 * (wave & 1) + part) * 16), uint32_t(t - src.tb) * (kC * 2));
+                        lane16 ^ uint32_t(kv_swz(8 * (wave & 1) + part) * 16), uint32_t(t - src.tb) * uint32_t(a.kv_rb));
     } else {
       // rows from the tile's first one, or (a tile past the end) from the last needed one, so
       // that every offset is that of a row the workgroup may read
       const int tq = min(t0, src.tlast);
       const int tp = min(t0 + pe_row, src.tlast);
-      buf_load16_lds_at(src.pe, st + kKvTileBytes + wave * 8 * (kR * 2), pe_voff + uint32_t(tp - tq) * (kR * 2),
-                        uint32_t(tq - src.tb) * (kR * 2));
+      buf_load16_lds_at(src.pe, st + kKvTileBytes + wave * 8 * (kR * 2), pe_voff + uint32_t(tp - tq) * uint32_t(a.pe_rb),
+                        uint32_t(tq - src.tb) * uint32_t(a.pe_rb));
     }
   };
   auto issue = [&](int j) __attribute__((always_inline)) {
@@ -700,6 +705,7 @@ struct AbsorbQArgs {
   int32_t S, row_blocks;   // query tokens per sequence; 128-row blocks per sequence
   int32_t row_blocks_per_wg;
   float inv_S;             // 1 / S
+  int32_t qn_rs, qp_rs;    // elements between consecutive query rows of q_nope and of q_pe
 };
 
 // Byte offset of row (m, h)'s slot in the fragment buffer (add ks * 1024 + g * 16).
@@ -746,13 +752,13 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(AbsorbQArgs a) {
   // instruction: lane l moves chunk position l % 16 of row l / 16 and fetches the chunk stored
   // there ((l % 16) ^ (row & 15)), so the B-operand reads below (16 lanes, 16 rows, one chunk) hit
   // 16 different bank groups.  Rows past M repeat row M - 1 (their results are not stored).
-  const rsrc_t xres = make_rsrc(a.q_nope, uint32_t(int64_t(a.M) * a.H * kDn * 2));
+  const rsrc_t xres = make_rsrc(a.q_nope, uint32_t((int64_t(a.M) * a.H - 1) * a.qn_rs * 2 + kDn * 2));
   auto issue_x = [&](int rb, int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int r = wave * 8 + i * 4 + (lane >> 4);
       const int m = min(rb * 32 + r, a.M - 1);
-      const uint32_t src = uint32_t((int64_t(m) * a.H + h) * (kDn * 2)) + uint32_t((lane & 15) ^ (r & 15)) * 16;
+      const uint32_t src = uint32_t((int64_t(m) * a.H + h) * a.qn_rs * 2) + uint32_t((lane & 15) ^ (r & 15)) * 16;
       buf_load16_lds(xres, xt[buf] + (wave * 8 + i * 4) * 256, src, 0);
     }
   };
@@ -766,7 +772,7 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(AbsorbQArgs a) {
 #pragma unroll
     for (int k = 0; k < kQBlocksPerWG; ++k) {
       const int m = min((rb0 + k) * 32 + pe_r, a.M - 1);
-      pe_v[k] = *reinterpret_cast<const u32x4 *>(a.q_pe + (int64_t(m) * a.H + h) * kR + pe_chunk * 8);
+      pe_v[k] = *reinterpret_cast<const u32x4 *>(a.q_pe + (int64_t(m) * a.H + h) * a.qp_rs + pe_chunk * 8);
     }
   }
   wait_vmcnt<0>();
@@ -841,7 +847,8 @@ struct CombineArgs {
   const float *part_ml;    // [rows, splits, 2] (max in log2 units, sum)
   const uint16_t *part_o;  // [rows, splits, 512]
   const uint16_t *wkv_b;   // [H * 256, 512]
-  uint16_t *out;           // [rows, 128]
+  uint16_t *out;           // [rows, 128], rows out_rs elements apart
+  int64_t out_rs;
   int32_t H, M, splits;    // rows = M * H, row = m * H + h
   int32_t wgs_per_head, groups_per_wg;
   const int32_t *bal_nb;   // balanced ragged plan: [M] splits used by row m's sequence, else null
@@ -1034,7 +1041,7 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineArgs a) {
     }
     // lane holds D^T[e = 32 wave + 16 blk + 4 q + r][m = m0 + l16], r = 0..3: four consecutive e
     if (l16 < nrows) {
-      uint16_t *dst = a.out + (int64_t(m0 + l16) * a.H + h) * kDv + 32 * wave + 4 * q;
+      uint16_t *dst = a.out + (int64_t(m0 + l16) * a.H + h) * a.out_rs + 32 * wave + 4 * q;
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
         const u32x2 v{pack_bf16x2(d[blk][0], d[blk][1]), pack_bf16x2(d[blk][2], d[blk][3])};
@@ -1072,11 +1079,21 @@ bool mfma_attn_supported(const AttnCall &c, const char **why) {
       *why = "max_pages_per_seq must be below 2^28";
       return false;
     }
-  } else if (c.Tmax >= (int64_t(1) << 22)) {  // per-sequence buffer ranges are byte counts below 2^32
-    *why = "cache_len must be below 4194304";
+    if ((c.kv_ps << 1) * c.page_size >= (int64_t(1) << 32) || (c.pe_ps << 1) * c.page_size >= (int64_t(1) << 32)) {
+      *why = "page_size * position stride must be below 2^31 elements";  // page ranges are byte counts
+      return false;
+    }
+  } else if (c.Tmax * c.kv_ps * 2 >= (int64_t(1) << 32) || c.Tmax * c.pe_ps * 2 >= (int64_t(1) << 32)) {
+    // per-sequence buffer ranges are byte counts below 2^32
+    *why = "cache_len * position stride must be below 2^31 elements";
     return false;
   }
   if (c.B * c.S * c.H * int64_t(kC) * 2 >= (int64_t(1) << 32)) { *why = "too many query rows"; return false; }
+  // strided query rows: byte offsets of the query buffers are 32-bit
+  if (c.B * c.S * c.H * std::max(c.q_nope_rs, c.q_pe_rs) * 2 >= (int64_t(1) << 32)) {
+    *why = "batch * seqlen_q * n_heads * query row stride too large";
+    return false;
+  }
   return true;
 }
 
@@ -1150,7 +1167,7 @@ hipError_t mfma_absorb_attn(const AttnCall &c) {
 
   AbsorbQArgs qa{static_cast<const uint16_t *>(c.q_nope), static_cast<const uint16_t *>(c.q_pe),
                  static_cast<const uint16_t *>(c.wkv_b), q_frag, int32_t(c.H), M, int32_t(c.S), row_blocks, kQBlocksPerWG,
-                 1.f / float(c.S)};
+                 1.f / float(c.S), int32_t(c.q_nope_rs), int32_t(c.q_pe_rs)};
   const int nrb = (M + 31) / 32;
   hipError_t err = launch_kernel(
       MLA_KERNEL_ABSORB_Q, absorb_q_kernel,
@@ -1165,6 +1182,10 @@ hipError_t mfma_absorb_attn(const AttnCall &c) {
   aa.part_ml = part_ml;
   aa.part_o = part_o;
   aa.Tmax = c.Tmax;
+  aa.kv_bs = c.kv_bs;
+  aa.pe_bs = c.pe_bs;
+  aa.kv_rb = int32_t(c.kv_ps * 2);
+  aa.pe_rb = int32_t(c.pe_ps * 2);
   aa.S = int32_t(c.S);
   aa.H = int32_t(c.H);
   aa.SH = int32_t(c.S * c.H);
@@ -1201,7 +1222,7 @@ hipError_t mfma_absorb_attn(const AttnCall &c) {
   // its W_UV[h] copy in LDS over up to groups_per_wg 16-row groups
   const int groups = (M + kCombineRows - 1) / kCombineRows;
   const int per_head = int(std::max<int64_t>(1, std::min<int64_t>(groups, (512 + c.H - 1) / c.H)));
-  CombineArgs ca{part_ml, part_o, static_cast<const uint16_t *>(c.wkv_b), static_cast<uint16_t *>(c.out),
+  CombineArgs ca{part_ml, part_o, static_cast<const uint16_t *>(c.wkv_b), static_cast<uint16_t *>(c.out), c.out_rs,
                  int32_t(c.H), M, c.splits, per_head, (groups + per_head - 1) / per_head, bal_nb};
   const dim3 grid(unsigned(int64_t(c.H) * per_head));
   return c.splits == 1 ? launch_kernel(MLA_KERNEL_COMBINE, combine_kernel<true>, grid, dim3(256), 0, c.stream, ca)

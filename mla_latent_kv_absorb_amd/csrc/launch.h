@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/mla_absorb.h"
+
 namespace mla {
 
 // One validated absorb-attention call.  Rows are the B*S*H query rows in (b, s, h) order.
@@ -27,6 +29,10 @@ struct AttnCall {
   int32_t bal_target;
   float scale;
   int32_t dtype;      // MLA_DTYPE_*
+  // element strides (dense values filled in when the caller gives none): query rows of q_nope and
+  // q_pe, rows of out, cache rows (b) and positions (t) of kv and pe; page pools use the position
+  // strides for rows within and across pages
+  int64_t q_nope_rs, q_pe_rs, out_rs, kv_bs, kv_ps, pe_bs, pe_ps;
   int32_t splits;     // ranges the positions [0, end_pos) are cut into
   int64_t split_len;  // positions per range (the last may be shorter or empty)
   const void *q_nope, *q_pe, *kv, *pe, *wkv_b;

@@ -88,7 +88,7 @@ int32_t plan_attn(const mla_attn_shape *shape, int64_t end_pos, const mla_paged_
     return fail(MLA_ERR_ALIGN, "kv_lora_rank, qk_rope_head_dim, qk_nope_head_dim and v_head_dim must be "
                                "multiples of %lld elements (16-byte rows)", (long long)ealign);
 
-  mla_attn_options opt = {0, MLA_PATH_AUTO};
+  mla_attn_options opt = {0, MLA_PATH_AUTO, nullptr};
   if (options) opt = *options;
   if (opt.num_splits < 0 || opt.num_splits > 4096)
     return fail(MLA_ERR_SHAPE, "num_splits %d outside [0, 4096]", opt.num_splits);
@@ -99,6 +99,29 @@ int32_t plan_attn(const mla_attn_shape *shape, int64_t end_pos, const mla_paged_
   c.B = s.batch; c.S = s.seqlen_q; c.H = s.n_heads; c.C = s.kv_lora_rank; c.R = s.qk_rope_head_dim;
   c.Dn = s.qk_nope_head_dim; c.Dv = s.v_head_dim; c.Bmax = s.cache_batch; c.Tmax = s.cache_len;
   c.end_pos = end_pos; c.dtype = dtype;
+  // element strides: the caller's, a 0 field (or no struct) meaning the dense value
+  const mla_attn_strides st = opt.strides ? *opt.strides : mla_attn_strides{0, 0, 0, 0, 0, 0, 0};
+  c.q_nope_rs = st.q_nope_row ? st.q_nope_row : c.Dn;
+  c.q_pe_rs = st.q_pe_row ? st.q_pe_row : c.R;
+  c.out_rs = st.out_row ? st.out_row : c.Dv;
+  c.kv_ps = st.kv_pos ? st.kv_pos : c.C;
+  c.pe_ps = st.pe_pos ? st.pe_pos : c.R;
+  // (page pools ignore the batch strides: a page is page_size rows at the position stride)
+  c.kv_bs = paged ? 0 : (st.kv_batch ? st.kv_batch : c.Tmax * c.kv_ps);
+  c.pe_bs = paged ? 0 : (st.pe_batch ? st.pe_batch : c.Tmax * c.pe_ps);
+  {
+    const int64_t vals[] = {c.q_nope_rs, c.q_pe_rs, c.out_rs, c.kv_ps, c.pe_ps, c.kv_bs, c.pe_bs};
+    const int64_t mins[] = {c.Dn, c.R, c.Dv, c.C, c.R, 1, 1};
+    const char *snames[] = {"q_nope_row", "q_pe_row", "out_row", "kv_pos", "pe_pos", "kv_batch", "pe_batch"};
+    for (int i = 0; i < (paged ? 5 : 7); ++i) {
+      if (vals[i] < mins[i] || vals[i] > (int64_t(1) << 40))
+        return fail(MLA_ERR_SHAPE, "stride %s = %lld outside [%lld, 2^40]", snames[i], (long long)vals[i],
+                    (long long)mins[i]);
+      if (vals[i] % ealign)
+        return fail(MLA_ERR_ALIGN, "stride %s = %lld is not a multiple of %lld elements (16 bytes)", snames[i],
+                    (long long)vals[i], (long long)ealign);
+    }
+  }
   if (topk < 0 || topk > (int64_t(1) << 24)) return fail(MLA_ERR_SHAPE, "topk = %lld outside [1, 2^24]", (long long)topk);
   c.topk = topk;
   if (topk > 0 && s.batch * s.seqlen_q * topk > (int64_t(1) << 31) - 1)
@@ -239,11 +262,15 @@ int32_t absorb_attn_call(const void *q_nope, const void *q_pe, const void *kv_ca
     return fail(MLA_ERR_SHAPE, "softmax_scale must be a positive finite number");
   const size_t es = elem_size(dtype);
   const size_t rows = size_t(c.B * c.S * c.H);
-  const size_t cache_rows = paged ? size_t(c.num_pages * c.page_size) : size_t(c.Bmax * c.Tmax);
-  const size_t bytes_in[] = {rows * size_t(c.Dn) * es, rows * size_t(c.R) * es,
-                             cache_rows * size_t(c.C) * es, cache_rows * size_t(c.R) * es,
-                             size_t(c.H * (c.Dn + c.Dv) * c.C) * es};
-  const size_t out_bytes = rows * size_t(c.Dv) * es;
+  // byte extents of the (possibly strided) tensors: from the first element to past the last
+  const int64_t cache_kv = paged ? (c.num_pages * c.page_size - 1) * c.kv_ps + c.C
+                                 : (c.Bmax - 1) * c.kv_bs + (c.Tmax - 1) * c.kv_ps + c.C;
+  const int64_t cache_pe = paged ? (c.num_pages * c.page_size - 1) * c.pe_ps + c.R
+                                 : (c.Bmax - 1) * c.pe_bs + (c.Tmax - 1) * c.pe_ps + c.R;
+  const size_t bytes_in[] = {size_t((int64_t(rows) - 1) * c.q_nope_rs + c.Dn) * es,
+                             size_t((int64_t(rows) - 1) * c.q_pe_rs + c.R) * es, size_t(cache_kv) * es,
+                             size_t(cache_pe) * es, size_t(c.H * (c.Dn + c.Dv) * c.C) * es};
+  const size_t out_bytes = size_t((int64_t(rows) - 1) * c.out_rs + c.Dv) * es;
   for (int i = 0; i < 5; ++i)
     if (overlaps(out, out_bytes, ptrs[i], bytes_in[i])) return fail(MLA_ERR_SHAPE, "out overlaps %s", names[i]);
   const size_t lens_bytes = size_t(c.B) * sizeof(int32_t);

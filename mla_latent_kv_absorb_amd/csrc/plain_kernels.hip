@@ -18,25 +18,33 @@ constexpr int kThreads = 256;
 template <typename T>
 __global__ void __launch_bounds__(kThreads)
 plain_absorb_q_kernel(const T *__restrict__ q_nope, const T *__restrict__ wkv_b,
-                      float *__restrict__ q_lat, int64_t H, int64_t C, int64_t Dn, int64_t Dv) {
+                      float *__restrict__ q_lat, int64_t H, int64_t C, int64_t Dn, int64_t Dv, int64_t q_rs) {
   const int64_t row = blockIdx.x;
   const int64_t c = int64_t(blockIdx.y) * kThreads + threadIdx.x;
   if (c >= C) return;
   const int64_t h = row % H;
-  const T *q = q_nope + row * Dn;
+  const T *q = q_nope + row * q_rs;
   const T *w = wkv_b + h * (Dn + Dv) * C + c;
   float acc = 0.f;
   for (int64_t d = 0; d < Dn; ++d) acc = fmaf(Elem<T>::load(q, d), Elem<T>::load(w, d * C), acc);
   q_lat[row * C + c] = acc;
 }
 
-// Row of position t of sequence b in the kv / pe arrays: b * Tmax + t for contiguous caches; for
-// paged ones row t % page_size of the sequence's page for t, its id clamped into [0, num_pages).
-__device__ __forceinline__ int64_t cache_row(const AttnCall &a, int64_t b, int64_t t) {
-  if (a.page_size == 0) return b * a.Tmax + t;
+// Element offsets of position t of sequence b in the kv and pe arrays: b * batch stride + t *
+// position stride for contiguous caches; for paged ones row t % page_size of the sequence's page
+// for t (its id clamped into [0, num_pages)), rows counted across pages at the position stride.
+__device__ __forceinline__ void cache_offsets(const AttnCall &a, int64_t b, int64_t t, int64_t &kv_off,
+                                              int64_t &pe_off) {
+  if (a.page_size == 0) {
+    kv_off = b * a.kv_bs + t * a.kv_ps;
+    pe_off = b * a.pe_bs + t * a.pe_ps;
+    return;
+  }
   int64_t pg = a.block_table[b * a.max_pages + t / a.page_size];
   pg = pg < 0 ? 0 : (pg >= a.num_pages ? a.num_pages - 1 : pg);
-  return pg * a.page_size + t % a.page_size;
+  const int64_t r = pg * a.page_size + t % a.page_size;
+  kv_off = r * a.kv_ps;
+  pe_off = r * a.pe_ps;
 }
 
 // One block per (row, split): online softmax over the split's visible positions.
@@ -53,7 +61,8 @@ plain_attn_partial_kernel(const float *__restrict__ q_lat, const T *__restrict__
   float *so = sqp + a.R;      // C   running weighted sum
   float *sp = so + a.C;       // kThreads probabilities of the current chunk
   float *red = sp + kThreads; // 16
-  int64_t *srow = reinterpret_cast<int64_t *>(red + 16);  // kThreads cache rows of the current chunk
+  int64_t *skv = reinterpret_cast<int64_t *>(red + 16);  // kThreads kv offsets of the current chunk
+  int64_t *spe = skv + kThreads;                          // kThreads pe offsets
 
   const int64_t row = blockIdx.x;
   const int split = blockIdx.y;
@@ -80,7 +89,7 @@ plain_attn_partial_kernel(const float *__restrict__ q_lat, const T *__restrict__
   const int32_t *list = a.topk > 0 ? a.indices + (b * a.S + s) * a.topk : nullptr;
 
   for (int64_t c = tid; c < a.C; c += kThreads) { sq[c] = q_lat[row * a.C + c]; so[c] = 0.f; }
-  for (int64_t r = tid; r < a.R; r += kThreads) sqp[r] = Elem<T>::load(q_pe, row * a.R + r);
+  for (int64_t r = tid; r < a.R; r += kThreads) sqp[r] = Elem<T>::load(q_pe, row * a.q_pe_rs + r);
   __syncthreads();
 
   float m = -INFINITY, l = 0.f;
@@ -94,15 +103,15 @@ plain_attn_partial_kernel(const float *__restrict__ q_lat, const T *__restrict__
         ok = t >= 0 && t <= last;
         if (!ok) t = 0;
       }
-      srow[tid] = cache_row(a, b, t);
+      cache_offsets(a, b, t, skv[tid], spe[tid]);
     }
     __syncthreads();
     float sc = -INFINITY;
     if (ok) {
-      const int64_t r0 = srow[tid];
+      const int64_t k0 = skv[tid], p0 = spe[tid];
       float acc = 0.f;
-      for (int64_t c = 0; c < a.C; ++c) acc = fmaf(sq[c], Elem<T>::load(kv, r0 * a.C + c), acc);
-      for (int64_t r = 0; r < a.R; ++r) acc = fmaf(sqp[r], Elem<T>::load(pe, r0 * a.R + r), acc);
+      for (int64_t c = 0; c < a.C; ++c) acc = fmaf(sq[c], Elem<T>::load(kv, k0 + c), acc);
+      for (int64_t r = 0; r < a.R; ++r) acc = fmaf(sqp[r], Elem<T>::load(pe, p0 + r), acc);
       sc = acc * a.scale;
     }
     const float m_new = fmaxf(m, block_max(sc, red));
@@ -112,7 +121,7 @@ plain_attn_partial_kernel(const float *__restrict__ q_lat, const T *__restrict__
     l = l * alpha + block_sum(p, red);  // block_sum synchronises, so sp is visible below
     for (int64_t c = tid; c < a.C; c += kThreads) {
       float acc = so[c] * alpha;
-      for (int j = 0; j < n; ++j) acc = fmaf(sp[j], Elem<T>::load(kv, srow[j] * a.C + c), acc);
+      for (int j = 0; j < n; ++j) acc = fmaf(sp[j], Elem<T>::load(kv, skv[j] + c), acc);
       so[c] = acc;
     }
     m = m_new;
@@ -151,7 +160,7 @@ plain_merge_upproj_kernel(const float *__restrict__ part_ml, const float *__rest
   for (int64_t e = tid; e < a.Dv; e += kThreads) {
     float acc = 0.f;
     for (int64_t c = 0; c < a.C; ++c) acc = fmaf(so[c], Elem<T>::load(wuv, e * a.C + c), acc);
-    Elem<T>::store(static_cast<T *>(a.out), row * a.Dv + e, acc);
+    Elem<T>::store(static_cast<T *>(a.out), row * a.out_rs + e, acc);
   }
 }
 
@@ -195,8 +204,9 @@ hipError_t run_attn(const AttnCall &a) {
   const T *q_nope = static_cast<const T *>(a.q_nope);
   timing_begin(MLA_KERNEL_PLAIN, a.stream);
   plain_absorb_q_kernel<T><<<dim3(unsigned(rows), unsigned((a.C + kThreads - 1) / kThreads)), kThreads, 0,
-                             a.stream>>>(q_nope, static_cast<const T *>(a.wkv_b), q_lat, a.H, a.C, a.Dn, a.Dv);
-  const size_t sm_attn = sizeof(float) * size_t(2 * a.C + a.R + kThreads + 16) + sizeof(int64_t) * kThreads;
+                             a.stream>>>(q_nope, static_cast<const T *>(a.wkv_b), q_lat, a.H, a.C, a.Dn, a.Dv,
+                                         a.q_nope_rs);
+  const size_t sm_attn = sizeof(float) * size_t(2 * a.C + a.R + kThreads + 16) + 2 * sizeof(int64_t) * kThreads;
   plain_attn_partial_kernel<T><<<dim3(unsigned(rows), unsigned(a.splits)), kThreads, sm_attn, a.stream>>>(
       q_lat, static_cast<const T *>(a.q_pe), static_cast<const T *>(a.kv), static_cast<const T *>(a.pe),
       part_ml, part_o, a);

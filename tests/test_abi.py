@@ -373,3 +373,122 @@ def test_cache_append_paged_argument_errors(lib):
         p = list(P[:5])
         p[i] = None
         assert call_append_paged(lib, s, ptrs=p) == B.MLA_ERR_NULL
+
+
+# ------------------------------------------------------------------------------- strides
+
+def strides(**kw):
+    d = {f: 0 for f, _ in B.AttnStrides._fields_}
+    d.update(kw)
+    return B.AttnStrides(*[d[f] for f, _ in B.AttnStrides._fields_])
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(q_nope_row=100), B.MLA_ERR_SHAPE, "q_nope_row"),   # narrower than a row
+    (dict(q_pe_row=60), B.MLA_ERR_SHAPE, "q_pe_row"),
+    (dict(out_row=-128), B.MLA_ERR_SHAPE, "out_row"),
+    (dict(kv_pos=511), B.MLA_ERR_SHAPE, "kv_pos"),
+    (dict(pe_pos=63), B.MLA_ERR_SHAPE, "pe_pos"),
+    (dict(kv_batch=-1), B.MLA_ERR_SHAPE, "kv_batch"),
+    (dict(q_nope_row=196), B.MLA_ERR_ALIGN, "q_nope_row"),  # 392 bytes: rows off 16-byte boundaries
+    (dict(kv_pos=516), B.MLA_ERR_ALIGN, "kv_pos"),
+    (dict(pe_batch=4 * 64 + 4), B.MLA_ERR_ALIGN, "pe_batch"),
+    (dict(q_pe_row=1 << 41), B.MLA_ERR_SHAPE, "q_pe_row"),
+])
+def test_attn_stride_errors(lib, kw, code, needle):
+    st = strides(**kw)
+    opt = B.AttnOptions(0, 0, ctypes.pointer(st))
+    assert call_attn(lib, shape(), opt=opt) == code
+    assert needle in B.last_error()
+    # the size query validates the same way
+    assert lib.mla_absorb_attn_workspace_size(ctypes.byref(shape()), 4096, B.MLA_DTYPE_BF16, ctypes.byref(opt)) == 0
+
+
+def test_attn_strided_extents_in_overlap_checks(lib):
+    """Overlap checks use the extents the strides imply: a row stride that spreads out's 256 rows
+    over 2^33 elements reaches into the next tensor (the fake pointers are 4 GiB apart)."""
+    p = list(P[:6])
+    p[5] = P[0] - (1 << 20)  # out just below q_nope: dense it ends 64 KiB later, well before q_nope
+    # (ws=None: the call still fails validation, at the workspace, after the overlap checks, so
+    # nothing is ever launched on these fake pointers)
+    assert call_attn(lib, shape(), ptrs=p, ws=None) == B.MLA_ERR_WORKSPACE
+    st = strides(out_row=1 << 25)
+    opt = B.AttnOptions(0, 0, ctypes.pointer(st))
+    assert call_attn(lib, shape(), ptrs=p, opt=opt) == B.MLA_ERR_SHAPE
+    assert "out overlaps q_nope" in B.last_error()
+    # a combined [Bmax, Tmax, 576] cache (kv and pe interleaved): inputs may overlap each other
+    st = strides(kv_pos=576, pe_pos=576, q_nope_row=192, q_pe_row=192)
+    opt = B.AttnOptions(0, 0, ctypes.pointer(st))
+    q = list(P[:6])
+    q[1], q[3] = q[0] + 256, q[2] + 1024
+    rc = call_attn(lib, shape(), ptrs=q, opt=opt, ws=None)
+    assert rc == B.MLA_ERR_WORKSPACE  # validation got past shapes, strides and overlaps
+
+
+def test_binding_rejects_mismatched_shapes():
+    """The binding checks every tensor's shape against the call's sizes before it touches a device
+    (the library sees only pointers); CPU tensors suffice, since the shape checks come first."""
+    import torch
+
+    bf = torch.bfloat16
+    q_nope = torch.zeros(2, 1, 4, 128, dtype=bf)
+    q_pe = torch.zeros(2, 1, 4, 64, dtype=bf)
+    kv = torch.zeros(2, 64, 512, dtype=bf)
+    pe = torch.zeros(2, 64, 64, dtype=bf)
+    w = torch.zeros(4 * 256, 512, dtype=bf)
+    cases = [
+        (dict(q_pe=torch.zeros(2, 1, 3, 64, dtype=bf)), "q_pe"),
+        (dict(pe_cache=torch.zeros(2, 64, 32, dtype=bf)), "pe_cache"),
+        (dict(pe_cache=torch.zeros(2, 60, 64, dtype=bf)), "pe_cache"),
+        (dict(wkv_b=torch.zeros(4 * 256, 256, dtype=bf)), "wkv_b"),
+        (dict(wkv_b=torch.zeros(4 * 128, 512, dtype=bf)), "wkv_b"),
+        (dict(out=torch.zeros(2, 1, 4, 64, dtype=bf)), "out"),
+        (dict(indices=torch.zeros(2, 2, 8, dtype=torch.int32)), "indices"),
+    ]
+    for kw, needle in cases:
+        args = dict(q_nope=q_nope, q_pe=q_pe, kv_cache=kv, pe_cache=pe, wkv_b=w)
+        extra = {k: kw.pop(k) for k in ("out", "indices") if k in kw}
+        args.update(kw)
+        with pytest.raises(ValueError, match=needle):
+            B.absorb_attn(args["q_nope"], args["q_pe"], args["kv_cache"], args["pe_cache"], args["wkv_b"], 64, 0.07,
+                          **extra)
+    with pytest.raises(ValueError, match="rms_w"):
+        B.expand_kv(torch.zeros(16, 512, dtype=bf), torch.zeros(256, dtype=bf), w, 4, 128, 128)
+    with pytest.raises(ValueError, match="wkv_b"):
+        B.expand_kv(torch.zeros(16, 512, dtype=bf), torch.zeros(512, dtype=bf), w, 8, 128, 128)
+    with pytest.raises(ValueError, match="k_nope"):
+        B.expand_kv(torch.zeros(16, 512, dtype=bf), torch.zeros(512, dtype=bf), w, 4, 128, 128,
+                    k_nope=torch.zeros(4, 15, 128, dtype=bf))
+    with pytest.raises(ValueError, match="v"):
+        B.expand_kv(torch.zeros(16, 512, dtype=bf), torch.zeros(512, dtype=bf), w, 4, 128, 128,
+                    v=torch.zeros(4, 16, 64, dtype=bf))
+    with pytest.raises(ValueError, match="rms_w"):
+        B.cache_append(torch.zeros(2, 1, 512, dtype=bf), torch.zeros(2, 1, 64, dtype=bf), torch.zeros(64, dtype=bf),
+                       1e-6, 8, kv, pe)
+    with pytest.raises(ValueError, match="pe_cache"):
+        B.cache_append(torch.zeros(2, 1, 512, dtype=bf), torch.zeros(2, 1, 64, dtype=bf),
+                       torch.zeros(512, dtype=bf), 1e-6, 8, kv, torch.zeros(2, 64, 32, dtype=bf))
+    with pytest.raises(ValueError, match="out"):
+        B.naive_attn(q_nope, q_pe, torch.zeros(4, 2, 64, 128, dtype=bf), torch.zeros(4, 2, 64, 128, dtype=bf), pe, 64,
+                     0.07, out=torch.zeros(2, 1, 4, 100, dtype=bf))
+
+
+def test_binding_row_strides():
+    """Views whose rows are evenly spaced give their row stride; dense tensors give 0."""
+    import torch
+
+    q = torch.zeros(2, 3, 4, 192)
+    assert B._row_stride(q[..., :128], "q_nope") == 192
+    assert B._row_stride(q[..., 128:], "q_pe") == 192
+    assert B._row_stride(q, "q") == 0
+    assert B._row_stride(q[:1, :1, :1, :128], "one row") == 0
+    with pytest.raises(ValueError, match="evenly spaced"):
+        B._row_stride(q[:, :2], "q")
+    with pytest.raises(ValueError, match="evenly spaced"):
+        B._row_stride(torch.zeros(2, 4, 3, 64).transpose(1, 2), "q")
+    cache = torch.zeros(3, 10, 576)
+    assert B._cache_strides(cache[..., :512], "kv") == (5760, 576)
+    assert B._cache_strides(cache[..., 512:], "pe") == (5760, 576)
+    assert B._cache_strides(torch.zeros(3, 10, 512), "kv") == (0, 0)
+    assert B._cache_strides(torch.zeros(4, 10, 512)[:3], "kv") == (0, 0)
+    assert B._cache_strides(torch.zeros(3, 12, 512)[:, :10], "kv") == (6144, 0)

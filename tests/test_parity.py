@@ -204,28 +204,31 @@ def test_mfma_larger_than_tile_max_shift(gpu_lib):
     check(out, oracle_attn(cfg, x), TOL["bf16"], "mfma growing scores")
 
 
-def sample_rows(cfg, n, seed):
-    rng = np.random.default_rng(seed)
-    rows = {(0, 0, 0), (cfg.batch - 1, cfg.seqlen_q - 1, cfg.n_heads - 1), (0, cfg.seqlen_q - 1, 0),
-            (cfg.batch - 1, 0, cfg.n_heads // 2)}
-    while len(rows) < n:
-        rows.add((int(rng.integers(cfg.batch)), int(rng.integers(cfg.seqlen_q)), int(rng.integers(cfg.n_heads))))
-    return sorted(rows)
+def oracle_attn_full(cfg, x, lens=None, q_block=64):
+    """The oracle's absorb route for every output element, one sequence (and for S > 1 one block of
+    query tokens) at a time, so that host memory stays small.  Query tokens [s0, s1) of a sequence of
+    length n sit at positions n - S + s0 .. n - S + s1 - 1, so they are the absorb route of those
+    tokens alone with end_pos = n - S + s1: the mask definition the chunk-rows-are-decodes pin fixes."""
+    B, S = cfg.batch, cfg.seqlen_q
+    out = np.empty((B, S, cfg.n_heads, cfg.v_head_dim))
+    for b in range(B):
+        n = cfg.end_pos if lens is None else int(lens[b])
+        for s0 in range(0, S, q_block):
+            s1 = min(S, s0 + q_block)
+            out[b:b + 1, s0:s1] = O.absorb_attention(x["q_nope"][b:b + 1, s0:s1], x["q_pe"][b:b + 1, s0:s1],
+                                                     x["kv_cache"][b:b + 1], x["pe_cache"][b:b + 1], x["wkv_b"],
+                                                     n - S + s1, cfg.softmax_scale, cfg.v_head_dim)
+    return out
 
 
 @pytest.mark.parametrize("name", ["dsv3_decode", "long_decode", "chunk_prefill"])
 def test_full_size_attention(gpu_lib, name):
+    """Every output element of the full-size workload against the oracle."""
     cfg = ATTN_CONFIGS[name]
     print(f"full-size {name}: B={cfg.batch} S={cfg.seqlen_q} T={cfg.end_pos}", flush=True)
     x = make_attn_inputs(cfg)
     out = run_attn(gpu_lib, cfg, to_dev(x, cfg))
-    assert torch.isfinite(out).all(), "non-finite outputs"
-    rows = sample_rows(cfg, 48, 7)
-    ref = O.absorb_attention_rows(x["q_nope"], x["q_pe"], x["kv_cache"], x["pe_cache"], x["wkv_b"], cfg.end_pos,
-                                  cfg.softmax_scale, cfg.v_head_dim, rows)
-    g = out.float().cpu().double().numpy()
-    got = np.stack([g[b, s, h] for b, s, h in rows])
-    check(got, ref, TOL["bf16"], f"{name} sampled rows")
+    check(out, oracle_attn_full(cfg, x), TOL["bf16"], f"{name} all outputs")
 
 
 # --------------------------------------------------------------------------------- ragged batches
@@ -268,17 +271,13 @@ def test_ragged_small(gpu_lib, path, seqlen_q, lens):
 def test_ragged_balanced_full_heads(gpu_lib, lens):
     """The device plan at the decode head shape: one long sequence among very short ones (the
     equal-chunk plan; it takes up to four times the uniform plan's chunks), at either end of the
-    chunk order, and a linear spread of lengths (the uniform splits); sampled rows."""
+    chunk order, and a linear spread of lengths (the uniform splits); every output element."""
     cfg = ATTN_CONFIGS["dsv3_decode"]
     x = make_attn_inputs(cfg)
     t = to_dev(x, cfg)
     poison_tails(t, lens)
     out = run_attn_ragged(gpu_lib, cfg, t, lens)
-    assert torch.isfinite(out).all(), "non-finite outputs"
-    rows = sample_rows(cfg, 40, 17) + [(b, 0, 5) for b in range(0, 32, 3)]
-    ref = oracle_ragged(cfg, x, lens, rows=rows)
-    g = out.float().cpu().double().numpy()
-    check(np.stack([g[b, s_, h] for b, s_, h in rows]), ref, TOL["bf16"], f"balanced ragged lens[0]={lens[0]}")
+    check(out, oracle_attn_full(cfg, x, lens=lens), TOL["bf16"], f"balanced ragged lens[0]={lens[0]}, all outputs")
 
 
 @pytest.mark.parametrize("mix", ["spread", "skewed"])
@@ -354,11 +353,7 @@ def test_full_size_ragged(gpu_lib, name):
     t = to_dev(x, cfg)
     poison_tails(t, lens)
     out = run_attn_ragged(gpu_lib, cfg, t, lens)
-    assert torch.isfinite(out).all(), "non-finite outputs"
-    rows = sample_rows(cfg, 48, 9)
-    ref = oracle_ragged(cfg, x, lens, rows=rows)
-    g = out.float().cpu().double().numpy()
-    check(np.stack([g[b, s, h] for b, s, h in rows]), ref, TOL["bf16"], f"{name} sampled rows")
+    check(out, oracle_attn_full(cfg, x, lens=lens), TOL["bf16"], f"{name} all outputs")
 
 
 # --------------------------------------------------------------------------------- paged caches
@@ -454,6 +449,27 @@ def test_paged_uniform_and_clamped_ids(gpu_lib):
         out = run_attn_paged(gpu_lib, cfg, t, dev(kvp), dev(pep), torch.from_numpy(bad).to("cuda"), cfg.end_pos,
                              path=path)
         check(out, ref, TOL["bf16"], f"paged uniform, clamped ids, {path}")
+
+
+def test_paged_balanced_long_sequences(gpu_lib):
+    """Pages of 32 (a split may span at most 255 of them, 8160 positions), automatic splits and a
+    skewed ragged batch whose two long sequences exceed that span: the device plan takes equal
+    chunks, with the paged chunk bound evaluated for sequences longer than it, and each chunk
+    walks up to 255 page ids held in registers."""
+    lens = [12000, 50, 70, 33, 9000, 64, 1, 100]
+    cfg = ATTN_CONFIGS["dsv3_decode"].replace(batch=len(lens), cache_batch=len(lens), end_pos=12000,
+                                              cache_len=12032)
+    print(f"paged balanced: lens {lens} page 32", flush=True)
+    x = make_attn_inputs(cfg)
+    kvp, table = to_pages(x["kv_cache"], lens, 32, 5, 141)
+    pep, _ = to_pages(x["pe_cache"], lens, 32, 5, 141)
+    t = to_dev(x, cfg)
+    dev = lambda a: torch.from_numpy(a).to("cuda").to(torch.bfloat16)
+    out = run_attn_paged(gpu_lib, cfg, t, dev(kvp), dev(pep), torch.from_numpy(table).to("cuda"), cfg.end_pos,
+                         lens=lens, path="mfma")
+    ref = O.absorb_attention_paged(x["q_nope"], x["q_pe"], kvp, pep, x["wkv_b"], table, lens, 32, cfg.softmax_scale,
+                                   cfg.v_head_dim)
+    check(out, ref, TOL["bf16"], "paged balanced, sequences longer than one split's page span")
 
 
 @pytest.mark.parametrize("name,page_size", [("dsv3_decode", 64), ("chunk_prefill", 64), ("long_decode", 256),
@@ -585,12 +601,121 @@ def test_full_size_sparse(gpu_lib, name, topk):
                     for _ in range(cfg.batch)]).astype(np.int32)
     t = to_dev(x, cfg)
     out = run_attn_sparse(gpu_lib, cfg, t, idx)
-    assert torch.isfinite(out).all(), "non-finite outputs"
-    rows = sample_rows(cfg, 48, 13)
     ref = O.absorb_attention_sparse(x["q_nope"], x["q_pe"], x["kv_cache"], x["pe_cache"], x["wkv_b"], idx,
-                                    [cfg.end_pos] * cfg.batch, cfg.softmax_scale, cfg.v_head_dim, rows=rows)
-    g = out.float().cpu().double().numpy()
-    check(np.stack([g[b, s_, h] for b, s_, h in rows]), ref, TOL["bf16"], f"{name} topk={topk} sampled rows")
+                                    [cfg.end_pos] * cfg.batch, cfg.softmax_scale, cfg.v_head_dim)
+    check(out, ref, TOL["bf16"], f"{name} topk={topk} all outputs")
+
+
+# --------------------------------------------------------------------------------- strided views
+
+def strided_views(t, cfg, pad_out=64):
+    """The same inputs as views of combined tensors, the way a model holds them: q_nope and q_pe
+    the two parts of one [B, S, H, Dn + R] query, kv_cache and pe_cache the two parts of one
+    [Bmax, Tmax, C + R] cache (with a spare position row per sequence, so the batch stride is not
+    Tmax rows), and out the first Dv columns of a wider NaN-filled buffer.  Returns (views, out
+    buffer); the views hold bitwise the values of t."""
+    dt = t["q_nope"].dtype
+    Dn, R, C = cfg.qk_nope_head_dim, cfg.qk_rope_head_dim, cfg.kv_lora_rank
+    q = torch.cat([t["q_nope"], t["q_pe"]], dim=-1).contiguous()
+    Bm, Tm = t["kv_cache"].shape[:2]
+    cache = torch.full((Bm, Tm + 1, C + R), float("nan"), dtype=dt, device="cuda")
+    cache[:, :Tm, :C] = t["kv_cache"]
+    cache[:, :Tm, C:] = t["pe_cache"]
+    obuf = torch.full((cfg.batch, cfg.seqlen_q, cfg.n_heads, cfg.v_head_dim + pad_out), float("nan"), dtype=dt,
+                      device="cuda")
+    v = dict(t, q_nope=q[..., :Dn], q_pe=q[..., Dn:], kv_cache=cache[:, :Tm, :C], pe_cache=cache[:, :Tm, C:])
+    return v, obuf
+
+
+@pytest.mark.parametrize("path", ["mfma", "plain"])
+@pytest.mark.parametrize("seqlen_q", [1, 3])
+def test_strided_views(gpu_lib, path, seqlen_q):
+    """Query halves of one tensor, caches interleaved in one 576-wide cache and out as a view: the
+    same result as dense tensors (bitwise), the oracle's at the bf16 bar, and out's padding
+    untouched."""
+    cfg = dsv3_small(seqlen_q=seqlen_q)
+    if path == "plain":
+        cfg = cfg.replace(n_heads=16)
+    x = make_attn_inputs(cfg)
+    t = to_dev(x, cfg)
+    dense = run_attn(gpu_lib, cfg, t, path=path)
+    v, obuf = strided_views(t, cfg)
+    out = obuf[..., :cfg.v_head_dim]
+    assert not out.is_contiguous() and not v["q_nope"].is_contiguous() and not v["kv_cache"].is_contiguous()
+    gpu_lib.absorb_attn(v["q_nope"], v["q_pe"], v["kv_cache"], v["pe_cache"], v["wkv_b"], cfg.end_pos,
+                        cfg.softmax_scale, out, path=path)
+    torch.cuda.synchronize()
+    assert torch.isnan(obuf[..., cfg.v_head_dim:]).all(), "a store landed in out's padding"
+    assert torch.equal(out, dense), "strided views differ from dense tensors"
+    check(out, oracle_attn(cfg, x), TOL["bf16"], f"strided views {path} S={seqlen_q}")
+
+
+def test_strided_views_f32(gpu_lib):
+    cfg = ATTN_CONFIGS["tiny_f32"]
+    x = make_attn_inputs(cfg)
+    t = to_dev(x, cfg)
+    v, obuf = strided_views(t, cfg, pad_out=4)
+    out = obuf[..., :cfg.v_head_dim]
+    gpu_lib.absorb_attn(v["q_nope"], v["q_pe"], v["kv_cache"], v["pe_cache"], v["wkv_b"], cfg.end_pos,
+                        cfg.softmax_scale, out)
+    torch.cuda.synchronize()
+    assert torch.isnan(obuf[..., cfg.v_head_dim:]).all()
+    check(out, oracle_attn(cfg, x), TOL["f32"], "tiny_f32 strided views")
+
+
+def test_strided_views_ragged_sparse_paged(gpu_lib):
+    """Strides through the ragged, index-list and paged entry points (pools of 576-wide rows)."""
+    lens = [300, 37, 161]
+    cfg = dsv3_small(batch=3, cache_batch=3, seqlen_q=2, end_pos=300, cache_len=320)
+    x = make_attn_inputs(cfg)
+    t = to_dev(x, cfg)
+    v, obuf = strided_views(t, cfg)
+    out = obuf[..., :cfg.v_head_dim]
+    seq = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    gpu_lib.absorb_attn(v["q_nope"], v["q_pe"], v["kv_cache"], v["pe_cache"], v["wkv_b"], cfg.end_pos,
+                        cfg.softmax_scale, out, seq_lens=seq)
+    torch.cuda.synchronize()
+    assert torch.equal(out, run_attn_ragged(gpu_lib, cfg, t, lens)), "ragged: strided differs from dense"
+    check(out, oracle_ragged(cfg, x, lens), TOL["bf16"], "ragged strided views")
+
+    idx = make_lists(cfg, lens, 64, 5)
+    obuf.fill_(float("nan"))
+    gpu_lib.absorb_attn(v["q_nope"], v["q_pe"], v["kv_cache"], v["pe_cache"], v["wkv_b"], cfg.end_pos,
+                        cfg.softmax_scale, out, seq_lens=seq, indices=torch.from_numpy(idx).to("cuda"))
+    torch.cuda.synchronize()
+    ref = O.absorb_attention_sparse(x["q_nope"], x["q_pe"], x["kv_cache"], x["pe_cache"], x["wkv_b"], idx, lens,
+                                    cfg.softmax_scale, cfg.v_head_dim)
+    check(out, ref, TOL["bf16"], "index lists, strided views")
+
+    kvp, table = to_pages(x["kv_cache"], lens, 32, 3, 71)
+    pep, _ = to_pages(x["pe_cache"], lens, 32, 3, 71)
+    pool = torch.cat([torch.from_numpy(kvp), torch.from_numpy(pep)], dim=-1).to("cuda").to(torch.bfloat16)
+    obuf.fill_(float("nan"))
+    gpu_lib.absorb_attn(v["q_nope"], v["q_pe"], pool[..., :cfg.kv_lora_rank], pool[..., cfg.kv_lora_rank:],
+                        v["wkv_b"], cfg.end_pos, cfg.softmax_scale, out, seq_lens=seq,
+                        block_table=torch.from_numpy(table).to("cuda"))
+    torch.cuda.synchronize()
+    ref = O.absorb_attention_paged(x["q_nope"], x["q_pe"], kvp, pep, x["wkv_b"], table, lens, 32, cfg.softmax_scale,
+                                   cfg.v_head_dim)
+    check(out, ref, TOL["bf16"], "paged 576-wide pools, strided views")
+    assert torch.isnan(obuf[..., cfg.v_head_dim:]).all()
+
+
+def test_full_size_strided_views(gpu_lib):
+    """dsv3_decode with q and the caches as views of combined tensors: every output element
+    against the oracle."""
+    cfg = ATTN_CONFIGS["dsv3_decode"]
+    print(f"full-size strided views: B={cfg.batch} T={cfg.end_pos}", flush=True)
+    x = make_attn_inputs(cfg)
+    t = to_dev(x, cfg)
+    v, obuf = strided_views(t, cfg)
+    del t
+    out = obuf[..., :cfg.v_head_dim]
+    gpu_lib.absorb_attn(v["q_nope"], v["q_pe"], v["kv_cache"], v["pe_cache"], v["wkv_b"], cfg.end_pos,
+                        cfg.softmax_scale, out)
+    torch.cuda.synchronize()
+    assert torch.isnan(obuf[..., cfg.v_head_dim:]).all()
+    check(out, oracle_attn_full(cfg, x), TOL["bf16"], "dsv3_decode strided views, all outputs")
 
 
 # --------------------------------------------------------------------------------- fp32 extensions
@@ -804,7 +929,7 @@ def test_naive_route_matches_absorb_on_gpu(gpu_lib):
 
 def test_full_size_naive_vs_absorb_prefill(gpu_lib):
     """chunk_prefill through both routes on the GPU (expansion of the 2 x 4096 cached latents, then
-    naive attention), compared with each other everywhere and with the oracle on sampled rows."""
+    naive attention), compared with each other and with the oracle on every output element."""
     cfg = ATTN_CONFIGS["chunk_prefill"]
     print(f"full-size naive vs absorb: B={cfg.batch} S={cfg.seqlen_q} T={cfg.end_pos}", flush=True)
     x = make_attn_inputs(cfg)
@@ -820,11 +945,7 @@ def test_full_size_naive_vs_absorb_prefill(gpu_lib):
                   v.view(cfg.n_heads, cfg.cache_batch, cfg.cache_len, -1))
     assert torch.isfinite(n).all()
     check(n, a.float().cpu().double().numpy(), TOL["bf16"], "chunk_prefill naive route vs absorb route")
-    rows = sample_rows(cfg, 32, 11)
-    ref = O.absorb_attention_rows(x["q_nope"], x["q_pe"], x["kv_cache"], x["pe_cache"], x["wkv_b"], cfg.end_pos,
-                                  cfg.softmax_scale, cfg.v_head_dim, rows)
-    g = n.float().cpu().double().numpy()
-    check(np.stack([g[b, s, h] for b, s, h in rows]), ref, TOL["bf16"], "chunk_prefill naive route sampled rows")
+    check(n, oracle_attn_full(cfg, x), TOL["bf16"], "chunk_prefill naive route, all outputs")
 
 
 def test_full_size_expand(gpu_lib):
@@ -837,14 +958,12 @@ def test_full_size_expand(gpu_lib):
     gpu_lib.expand_kv(t["c_kv"], t["rms_w"], t["wkv_b"], cfg.n_heads, cfg.qk_nope_head_dim, cfg.v_head_dim, cfg.eps,
                       k, v)
     torch.cuda.synchronize()
-    assert torch.isfinite(k).all() and torch.isfinite(v).all()
-    rng = np.random.default_rng(11)
-    toks = np.unique(np.concatenate([[0, 255, 256, cfg.n_tokens - 1], rng.integers(0, cfg.n_tokens, 60)]))
-    kr, vr = O.expand_kv(x["c_kv"][toks], x["rms_w"], x["wkv_b"], cfg.n_heads, cfg.qk_nope_head_dim,
-                         cfg.v_head_dim, cfg.eps)
-    idx = torch.from_numpy(toks).cuda()
-    check(k[:, idx], kr, TOL["bf16"], "dsv3_expand K_nope sampled tokens")
-    check(v[:, idx], vr, TOL["bf16"], "dsv3_expand V sampled tokens")
+    # every token against the oracle, 1024 tokens at a time (each token's rows depend on it alone)
+    for t0 in range(0, cfg.n_tokens, 1024):
+        kr, vr = O.expand_kv(x["c_kv"][t0:t0 + 1024], x["rms_w"], x["wkv_b"], cfg.n_heads, cfg.qk_nope_head_dim,
+                             cfg.v_head_dim, cfg.eps)
+        check(k[:, t0:t0 + 1024], kr, TOL["bf16"], f"dsv3_expand K_nope tokens {t0}..")
+        check(v[:, t0:t0 + 1024], vr, TOL["bf16"], f"dsv3_expand V tokens {t0}..")
 
 
 @pytest.mark.parametrize("T", [1, 100, 257, 1000])
