@@ -147,6 +147,28 @@ int32_t mla_absorb_attn(const void *q_nope, const void *q_pe, const void *kv_cac
                         size_t workspace_bytes, void *stream);
 
 /*
+ * mla_absorb_attn without a workspace argument, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * workspace lives in a file-scope device array of MLA_NOALLOC_SCRATCH_BYTES in the library (one
+ * copy per GPU, held until the process ends; its device address is looked up once per device, on
+ * the first call with that device current).  The call allocates nothing: no hipMalloc, no hipFree.
+ *
+ * Arguments, layouts, results and errors are those of mla_absorb_attn.  A call whose workspace
+ * (mla_absorb_attn_workspace_size) exceeds MLA_NOALLOC_SCRATCH_BYTES fails with
+ * MLA_ERR_WORKSPACE before any HIP call (64 MiB covers, for example, the DeepSeek-V3 decode step
+ * of 32 sequences x 128 heads at any cache length, which takes 38.5 MB).  Every call on a GPU uses
+ * that GPU's one array and leaves its contents behind; nothing in it has to start at zero (each
+ * call writes every slot it reads).  Calls whose executions overlap on one GPU -- on different
+ * streams, or from different threads -- race on the array and must be serialised by the caller.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+int32_t mla_absorb_attn_noalloc(const void *q_nope, const void *q_pe, const void *kv_cache,
+                                const void *pe_cache, const void *wkv_b, int64_t end_pos,
+                                float softmax_scale, void *out, const mla_attn_shape *shape,
+                                int32_t dtype, const mla_attn_options *options, void *stream);
+
+/*
  * Absorb-form MLA attention over a ragged batch: sequence b attends to its own cache positions
  * [0, seq_lens[b]) (the page's uniform slice "[:bsz, :end_pos]" taken per sequence; its S query
  * tokens sit at seq_lens[b] - S .. seq_lens[b] - 1, causal as in mla_absorb_attn).

@@ -29,7 +29,7 @@ MLA_DTYPE_BF16 = 1
 
 PATHS = {"auto": 0, "plain": 1, "mfma": 2}
 
-EXPORTED = ("mla_absorb_attn", "mla_absorb_attn_ragged", "mla_absorb_attn_paged", "mla_absorb_attn_sparse",
+EXPORTED = ("mla_absorb_attn", "mla_absorb_attn_noalloc", "mla_absorb_attn_ragged", "mla_absorb_attn_paged", "mla_absorb_attn_sparse",
             "mla_absorb_attn_workspace_size", "mla_absorb_attn_ragged_workspace_size",
             "mla_absorb_attn_paged_workspace_size",
             "mla_absorb_attn_sparse_workspace_size", "mla_cache_append", "mla_cache_append_paged",
@@ -76,11 +76,22 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         return _lib
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is not built; run `python -m mla_latent_kv_absorb_amd.build`")
+    # torch ships its own copy of the HIP runtime under the same soname.  Loading torch first makes
+    # the library bind to that copy, so that the library and torch share one runtime (streams,
+    # current device, loaded code objects); loading the library first would put two runtimes in the
+    # process, and the library's would not see torch's device selection.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
     lib.mla_absorb_attn.argtypes = [vp, vp, vp, vp, vp, i64, ctypes.c_float, vp, ctypes.POINTER(AttnShape), i32,
                                     ctypes.POINTER(AttnOptions), vp, sz, vp]
     lib.mla_absorb_attn.restype = i32
+    lib.mla_absorb_attn_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, ctypes.c_float, vp, ctypes.POINTER(AttnShape),
+                                            i32, ctypes.POINTER(AttnOptions), vp]
+    lib.mla_absorb_attn_noalloc.restype = i32
     lib.mla_absorb_attn_ragged.argtypes = [vp, vp, vp, vp, vp, vp, i64, ctypes.c_float, vp, ctypes.POINTER(AttnShape),
                                            i32, ctypes.POINTER(AttnOptions), vp, sz, vp]
     lib.mla_absorb_attn_ragged.restype = i32
@@ -394,6 +405,30 @@ def absorb_attn(q_nope, q_pe, kv_cache, pe_cache, wkv_b, end_pos: int, softmax_s
     return AbsorbAttnCall(q_nope, q_pe, kv_cache, pe_cache, wkv_b, end_pos, softmax_scale, out,
                           num_splits=num_splits, path=path, workspace=workspace, seq_lens=seq_lens,
                           block_table=block_table, indices=indices)()
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MLA_NOALLOC_SCRATCH_BYTES
+
+
+def absorb_attn_noalloc(q_nope, q_pe, kv_cache, pe_cache, wkv_b, end_pos: int, softmax_scale: float, out, *,
+                        num_splits: int = 0, path: str = "auto"):
+    """mla_absorb_attn_noalloc: the absorb attention of absorb_attn with the library's own scratch
+    array as workspace.  `out` is the caller's (nothing is allocated here or in the library)."""
+    shape = attn_shape(q_nope, q_pe, kv_cache, wkv_b, pe_cache)
+    _shape(out, (shape.batch, shape.seqlen_q, shape.n_heads, shape.v_head_dim), "out")
+    _require_device(q_nope, q_pe, kv_cache, pe_cache, wkv_b, out, contiguous=False)
+    _require_device(wkv_b)
+    kv_b, kv_p = _cache_strides(kv_cache, "kv_cache")
+    pe_b, pe_p = _cache_strides(pe_cache, "pe_cache")
+    strides = AttnStrides(_row_stride(q_nope, "q_nope"), _row_stride(q_pe, "q_pe"), _row_stride(out, "out"),
+                          kv_b, kv_p, pe_b, pe_p)
+    dense = all(getattr(strides, f) == 0 for f, _ in AttnStrides._fields_)
+    opt = AttnOptions(num_splits, PATHS[path], None if dense else ctypes.pointer(strides))
+    _check(load().mla_absorb_attn_noalloc(q_nope.data_ptr(), q_pe.data_ptr(), kv_cache.data_ptr(), pe_cache.data_ptr(),
+                                          wkv_b.data_ptr(), end_pos, softmax_scale, out.data_ptr(),
+                                          ctypes.byref(shape), _dtype_code(q_nope), ctypes.byref(opt),
+                                          _stream_handle(q_nope.device)))
+    return out
 
 
 def cache_append(c_kv_new, k_pe_new, rms_w, eps: float, end_pos: int, kv_cache, pe_cache, *, seq_lens=None,

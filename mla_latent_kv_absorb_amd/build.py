@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(HERE, LIB_NAME)
 BUILD_DIR = os.path.join(HERE, "_build")
 
 SOURCES = ["mla_api.cpp", "timing.cpp", "plain_kernels.hip", "absorb_mfma.hip", "expand_mfma.hip", "cache_append.hip",
-           "naive_mfma.hip"]
+           "naive_mfma.hip", "noalloc.hip"]
 # peak probes for the benchmark (streaming read and copy, matrix-core and LDS rates): a library of
 # their own, never linked into the attention library
 PEAKS_SOURCES = ["peaks.hip"]

@@ -77,6 +77,16 @@ struct AppendCall {
   hipStream_t stream;
 };
 
+// ---- shared with the allocation-free entry point ------------------------------------------------
+// Every check of mla_absorb_attn except the workspace's, with no HIP call and nothing launched;
+// *need receives the workspace size the call would take.
+int32_t absorb_attn_dry_run(const void *q_nope, const void *q_pe, const void *kv_cache, const void *pe_cache,
+                            const void *wkv_b, int64_t end_pos, float softmax_scale, void *out,
+                            const mla_attn_shape *shape, int32_t dtype, const mla_attn_options *options,
+                            size_t *need);
+// Records msg as this thread's last error and returns status.
+int32_t set_error(int32_t status, const char *msg);
+
 // ---- benchmark instrumentation (no-ops unless enabled for the kernel id) ----------------------
 // Events recorded on the stream before and after a group of launches (the plain path's kernels).
 void timing_begin(int kernel_id, hipStream_t stream);

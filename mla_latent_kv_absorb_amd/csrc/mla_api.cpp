@@ -247,7 +247,8 @@ int32_t absorb_attn_call(const void *q_nope, const void *q_pe, const void *kv_ca
                          const void *wkv_b, const int32_t *seq_lens, const int32_t *block_table,
                          const mla_paged_cache *paged, const int32_t *indices, int64_t topk, int64_t end_pos,
                          float softmax_scale, void *out, const mla_attn_shape *shape, int32_t dtype,
-                         const mla_attn_options *options, void *workspace, size_t workspace_bytes, void *stream) {
+                         const mla_attn_options *options, void *workspace, size_t workspace_bytes, void *stream,
+                         size_t *dry_need = nullptr) {
   mla::AttnCall c;
   bool use_mfma = false;
   int32_t rc = plan_attn(shape, end_pos, paged, indices ? topk : 0, seq_lens != nullptr, dtype, options, c, use_mfma);
@@ -281,6 +282,10 @@ int32_t absorb_attn_call(const void *q_nope, const void *q_pe, const void *kv_ca
   const size_t index_bytes = size_t(c.B * c.S * c.topk) * sizeof(int32_t);
   if (indices && overlaps(out, out_bytes, indices, index_bytes)) return fail(MLA_ERR_SHAPE, "out overlaps indices");
   const size_t need = use_mfma ? mla::mfma_attn_workspace(c) : mla::plain_attn_workspace(c);
+  if (dry_need) {  // every check but the workspace's; nothing is launched
+    *dry_need = need;
+    return MLA_OK;
+  }
   if (need > 0) {
     if (!workspace) return fail(MLA_ERR_WORKSPACE, "workspace is NULL but %zu bytes are needed", need);
     if (workspace_bytes < need)
@@ -310,6 +315,21 @@ int32_t absorb_attn_call(const void *q_nope, const void *q_pe, const void *kv_ca
 }
 
 }  // namespace
+
+namespace mla {
+
+int32_t set_error(int32_t status, const char *msg) { return fail(status, "%s", msg); }
+
+int32_t absorb_attn_dry_run(const void *q_nope, const void *q_pe, const void *kv_cache, const void *pe_cache,
+                            const void *wkv_b, int64_t end_pos, float softmax_scale, void *out,
+                            const mla_attn_shape *shape, int32_t dtype, const mla_attn_options *options,
+                            size_t *need) {
+  clear_error();
+  return absorb_attn_call(q_nope, q_pe, kv_cache, pe_cache, wkv_b, nullptr, nullptr, nullptr, nullptr, 0, end_pos,
+                          softmax_scale, out, shape, dtype, options, nullptr, 0, nullptr, need);
+}
+
+}  // namespace mla
 
 extern "C" {
 
