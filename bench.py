@@ -450,6 +450,10 @@ def main():
     ap.add_argument("--no-extras", action="store_true", help="skip timing the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true", help="skip the streaming / matrix-core / LDS peak probes")
+    ap.add_argument("--profile", action="store_true",
+                    help="only run --warmup + --steps steps of --workload (an attention workload, "
+                         "chunk_prefill_naive or dsv3_expand) with no timing passes, extras, probes or CPU "
+                         "baseline: the command rocprofv3 profiles")
     ap.add_argument("--sustained-ms", type=float, default=40.0,
                     help="length of the labelled sustained-load decode run (0 to skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -482,6 +486,19 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "dispatches": args.steps}))
+        return
+
+    if args.profile:
+        if args.workload == "dsv3_expand":
+            us = time_expand(EXPAND_CONFIGS["dsv3_expand"], args.steps, args.warmup, torch, binding)
+        elif args.workload == "chunk_prefill_naive":
+            us, _ = time_naive_route(ATTN_CONFIGS["chunk_prefill"], args.steps, args.warmup, torch, binding,
+                                     seed=ATTN_CONFIGS["chunk_prefill"].seed)
+        else:
+            c = ATTN_CONFIGS[args.workload]
+            us, _, _ = time_attn(c, args.steps, args.warmup, min(args.sets, 2 if c.seqlen_q > 1 else args.sets),
+                                 torch, binding, seed=c.seed, timed_kernels=0)
+        print(json.dumps({"profile_run": args.workload, "steps": args.steps, "us_per_step": round(us, 2)}))
         return
 
     peaks = None if args.no_peaks else measure_peaks(torch)
