@@ -17,6 +17,7 @@
 // Rows are the B*S*H query rows in (b, s, h) order.  Every kv/pe row of a split is read from HBM
 // once per 128-row block and shared through LDS by all of the block's heads.
 #include <algorithm>
+#include <numeric>
 #include <type_traits>
 
 #include "common.h"
@@ -94,6 +95,7 @@ struct AttnArgs {
   // chunks packed in sequence order), and bal_nb [B * S] receives n_b for each query row of
   // sequence b (b * S + s), for the combine
   int32_t B, bal_target, bal_cap;  // bal_cap: longest chunk the row source allows (paged caches)
+  int32_t rb_stride;  // row block of logical index r within a sequence: r * rb_stride mod row_blocks
   int32_t *bal_nb;
 };
 
@@ -210,7 +212,12 @@ attn_kernel(AttnArgs a) {
   // logical order: row block fastest, then split, then sequence; the workgroups of one sequence
   // (which share its query rows and cache) land on one XCD
   int bid = __builtin_amdgcn_readfirstlane(xcd_logical_id(blockIdx.x, gridDim.x));
-  const int rb = __builtin_amdgcn_readfirstlane(bid % a.row_blocks);
+  // Row blocks go to the workgroups of a sequence in a strided order (a permutation: rb_stride is
+  // coprime with row_blocks), so that each XCD's contiguous share mixes early and late query
+  // tokens of a causal chunk, whose lengths differ, instead of taking all the short or all the
+  // long ones.
+  const int rb = __builtin_amdgcn_readfirstlane(
+      int(uint64_t(bid % a.row_blocks) * uint32_t(a.rb_stride) % uint32_t(a.row_blocks)));
   bid /= a.row_blocks;
   // balanced ragged plan: bid is a chunk rank, and the plan comes from all lengths
   const bool balanced = !kSparse && a.bal_target > 0;
@@ -888,21 +895,29 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineArgs a) {
   }
 
   const int l16 = lane & 15, q = lane >> 4;
+  // one split: the group's rows are copied to the o tile; the next group's rows are requested
+  // before this group's projection, so their latency hides behind it
+  u32x4 vrow[4];
+  auto load_rows = [&](int grp, u32x4 (&v)[4]) __attribute__((always_inline)) {
+    const int m0 = grp * kCombineRows;
+    const int nrows = min(kCombineRows, a.M - m0);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int r = min(wave + 4 * k, nrows - 1);
+      v[k] = *reinterpret_cast<const u32x4 *>(a.part_o + (int64_t(m0 + r) * a.H + h) * kC + lane * 8);
+    }
+  };
+  if (kSingle && g_begin < g_end) load_rows(g_begin, vrow);
 #pragma unroll 1
   for (int grp = g_begin; grp < g_end; ++grp) {
     const int m0 = grp * kCombineRows;
     const int nrows = min(kCombineRows, a.M - m0);
     // (with several splits each wave merges its own rows below, with running maxima)
     if (kSingle) {
-      u32x4 v[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int r = min(wave + 4 * k, nrows - 1);
-        v[k] = *reinterpret_cast<const u32x4 *>(a.part_o + (int64_t(m0 + r) * a.H + h) * kC + lane * 8);
-      }
 #pragma unroll
       for (int k = 0; k < 4; ++k)
-        if (wave + 4 * k < nrows) lds_write16(ol, row_swz16(wave + 4 * k, lane), v[k]);
+        if (wave + 4 * k < nrows) lds_write16(ol, row_swz16(wave + 4 * k, lane), vrow[k]);
+      if (grp + 1 < g_end) load_rows(grp + 1, vrow);
     }
     // combine: wave w takes rows w, w + 4, w + 8, w + 12 (NR of them); lane = 16-byte chunk of the
     // row.  The split statistics and partial rows of all NR rows are loaded kCombineLoads at a
@@ -1022,7 +1037,12 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineArgs a) {
         else if (nr == 1) combine_rows(I1{}, std::false_type{});
       }
     }
-    if (grp == g_begin) wait_vmcnt<0>();  // W_UV rows (LDS DMA) before the first use
+    // W_UV rows (LDS DMA) before the first use; with one split the next group's four row loads
+    // (issued last) may stay in flight
+    if (grp == g_begin) {
+      if (kSingle && grp + 1 < g_end) wait_vmcnt<4>();
+      else wait_vmcnt<0>();
+    }
     __syncthreads();
 
     // D^T[e][m] for e in 32 wave + 16 blk + 0..15: A = W rows (lane: row l % 16, chunk 4 ks + l / 16),
@@ -1140,6 +1160,15 @@ bool mfma_attn_plan_ok(const AttnCall &c, const char **why) {
 
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// An odd stride near 0.618 n that is coprime with n: multiples of it modulo n spread any run of
+// consecutive indices evenly over [0, n).
+static int32_t row_block_stride(int32_t n) {
+  if (n <= 2) return 1;
+  int32_t s = int32_t(double(n) * 0.6180339887498949) | 1;
+  while (std::gcd(s, n) != 1) s += 2;
+  return s % n;
+}
+
 // Workspace: [query fragments] [split m, l] [split o] [split counts of the balanced plan].
 static size_t q_region_bytes(const AttnCall &c) {
   const size_t row_blocks = size_t((c.S * c.H + kRowsWG - 1) / kRowsWG);
@@ -1198,6 +1227,7 @@ hipError_t mfma_absorb_attn(const AttnCall &c) {
   aa.bal_cap = c.page_size > 0 ? int32_t(mfma_paged_max_split_len(c)) : (1 << 30);
   aa.bal_nb = bal_nb;
   aa.row_blocks = row_blocks;
+  aa.rb_stride = row_block_stride(row_blocks);
   aa.scale_log2 = c.scale * kLog2e;
   // balanced plan: bal_target chunk workgroups per row block (the plan keeps it >= every chunk
   // count the lengths can produce), else one per (sequence, split)
