@@ -31,10 +31,12 @@ its sequences at 4096 positions, 28 at 64), each also under the uniform split pl
 comparison with the balanced one the library picks, paged_decode (the decode
 batch with its caches in pools of 64-position pages in random order), sparse_decode and
 sparse_long_decode (the decode and long-context batches with each token attending to 2048 random
-positions of its cache through an index list), chunk_prefill_naive (the
-same chunk through the naive route: expansion of the 2 x 4096 cached latents, then attention over
-the expanded keys and values), dsv3_expand (four rotated input sets) and tiny_f32 (the fp32
-decode of one sequence, 4 heads, 128 positions).
+positions of its cache through an index list), chunk_prefill_naive (the same chunk through the
+naive path as the pages lay it out: full-width key and value caches, into which a step expands the
+2 x 512 new tokens, then attention over the caches), chunk_prefill_naive_from_latent (the naive
+attention fed from the latent cache: a step expands all 2 x 4096 cached latents first),
+dsv3_expand (four rotated input sets) and tiny_f32 (the fp32 decode of one sequence, 4 heads,
+128 positions).
 """
 from __future__ import annotations
 
@@ -269,12 +271,16 @@ def naive_work(cfg):
             "flops": 2 * H * pairs * (Dn + R + Dv)}
 
 
-def time_naive_route(cfg, steps, warmup, torch, binding, seed=3):
-    """The naive route over a chunk: expansion of every cached latent row (RMSNorm, wkv_b, split
-    into head-major k_nope / v), then attention over the expanded rows.  Returns (us per step,
-    per-kernel timing dict)."""
+def time_naive_route(cfg, steps, warmup, torch, binding, seed=3, from_latent=False):
+    """A chunk step of the naive route.  By default the naive path as the pages lay it out: the
+    caches hold full-width head-major keys and values (filled once, before timing, with the
+    expansion of the cached latents), and a step expands the chunk's B x S new tokens into them
+    with their rope keys (mla_expand_kv_append), then attends over the caches.  With from_latent,
+    a step instead expands every cached latent row (what the naive attention needs when only the
+    latent cache is kept), then attends.  Returns (us per step, per-kernel timing dict)."""
     x = gpu_inputs(cfg, seed, torch)
     H, C, Dn, Dv = cfg.n_heads, cfg.kv_lora_rank, cfg.qk_nope_head_dim, cfg.v_head_dim
+    B, S, R = cfg.batch, cfg.seqlen_q, cfg.qk_rope_head_dim
     rows = cfg.cache_batch * cfg.cache_len
     g = torch.Generator(device="cuda")
     g.manual_seed(seed + 7)
@@ -286,10 +292,20 @@ def time_naive_route(cfg, steps, warmup, torch, binding, seed=3):
     ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
     lat = x["kv_cache"].view(rows, C)
     k4, v4 = k.view(H, cfg.cache_batch, cfg.cache_len, Dn), v.view(H, cfg.cache_batch, cfg.cache_len, Dv)
+    if from_latent:
+        def step():
+            binding.expand_kv(lat, w, x["wkv_b"], H, Dn, Dv, 1e-6, k, v, workspace=ws)
+            binding.naive_attn(x["q_nope"], x["q_pe"], k4, v4, x["pe_cache"], cfg.end_pos, cfg.softmax_scale, out)
+    else:
+        binding.expand_kv(lat, w, x["wkv_b"], H, Dn, Dv, 1e-6, k, v, workspace=ws)  # the earlier positions
+        c_new = torch.randn((B, S, C), generator=g, device="cuda").to(torch.bfloat16)
+        kp_new = torch.randn((B, S, R), generator=g, device="cuda").to(torch.bfloat16)
+        append = binding.ExpandAppendCall(c_new, kp_new, w, x["wkv_b"], 1e-6, cfg.end_pos, k4, v4, x["pe_cache"],
+                                          workspace=ws)
 
-    def step():
-        binding.expand_kv(lat, w, x["wkv_b"], H, Dn, Dv, 1e-6, k, v, workspace=ws)
-        binding.naive_attn(x["q_nope"], x["q_pe"], k4, v4, x["pe_cache"], cfg.end_pos, cfg.softmax_scale, out)
+        def step():
+            append()
+            binding.naive_attn(x["q_nope"], x["q_pe"], k4, v4, x["pe_cache"], cfg.end_pos, cfg.softmax_scale, out)
 
     def timed(mask):
         for _ in range(warmup):
@@ -309,7 +325,7 @@ def time_naive_route(cfg, steps, warmup, torch, binding, seed=3):
 
     us, _ = timed(0)
     _, kt = timed((1 << 3) | (1 << 4) | (1 << 6))
-    progress(f"{cfg.name} naive route: {us:.2f} us/step")
+    progress(f"{cfg.name} naive route{' from the latent cache' if from_latent else ''}: {us:.2f} us/step")
     del x, k, v, out, ws
     torch.cuda.empty_cache()
     return us, kt
@@ -452,8 +468,8 @@ def main():
     ap.add_argument("--no-peaks", action="store_true", help="skip the streaming / matrix-core / LDS peak probes")
     ap.add_argument("--profile", action="store_true",
                     help="only run --warmup + --steps steps of --workload (an attention workload, "
-                         "chunk_prefill_naive or dsv3_expand) with no timing passes, extras, probes or CPU "
-                         "baseline: the command rocprofv3 profiles")
+                         "chunk_prefill_naive, chunk_prefill_naive_from_latent or dsv3_expand) with no timing "
+                         "passes, extras, probes or CPU baseline: the command rocprofv3 profiles")
     ap.add_argument("--sustained-ms", type=float, default=40.0,
                     help="length of the labelled sustained-load decode run (0 to skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -491,9 +507,10 @@ def main():
     if args.profile:
         if args.workload == "dsv3_expand":
             us = time_expand(EXPAND_CONFIGS["dsv3_expand"], args.steps, args.warmup, torch, binding)
-        elif args.workload == "chunk_prefill_naive":
+        elif args.workload in ("chunk_prefill_naive", "chunk_prefill_naive_from_latent"):
             us, _ = time_naive_route(ATTN_CONFIGS["chunk_prefill"], args.steps, args.warmup, torch, binding,
-                                     seed=ATTN_CONFIGS["chunk_prefill"].seed)
+                                     seed=ATTN_CONFIGS["chunk_prefill"].seed,
+                                     from_latent=args.workload.endswith("from_latent"))
         else:
             c = ATTN_CONFIGS[args.workload]
             us, _, _ = time_attn(c, args.steps, args.warmup, min(args.sets, 2 if c.seqlen_q > 1 else args.sets),
@@ -610,14 +627,16 @@ def main():
                             "topk": 2048, "kernels_us": {n: round(v["avg_us"], 2) for n, v in k.items()},
                             "attn_gbps": round(w["attn_kernel_bytes"] / (k["attn"]["avg_us"] * 1e-6) / 1e9, 1)}
         c = ATTN_CONFIGS["chunk_prefill"]
-        u, k = time_naive_route(c, 10, 3, torch, binding, seed=c.seed)
         w = naive_work(c)
-        a_us = k["naive"]["avg_us"]
-        extras["chunk_prefill_naive"] = {
-            "us_per_step": round(u, 2), "kernels_us": {n: round(v["avg_us"], 2) for n, v in k.items()},
-            "naive_attn_tflops": round(w["flops"] / (a_us * 1e-6) / 1e12, 1),
-            "naive_attn_mfma_frac": round(w["flops"] / (a_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
-            "naive_attn_gbps": round(w["bytes"] / (a_us * 1e-6) / 1e9, 1)}
+        for name, from_latent in (("chunk_prefill_naive", False), ("chunk_prefill_naive_from_latent", True)):
+            u, k = time_naive_route(c, 10, 3, torch, binding, seed=c.seed, from_latent=from_latent)
+            a_us = k["naive"]["avg_us"]
+            extras[name] = {
+                "us_per_step": round(u, 2), "kernels_us": {n: round(v["avg_us"], 2) for n, v in k.items()},
+                "expanded_tokens": (c.cache_batch * c.cache_len) if from_latent else c.batch * c.seqlen_q,
+                "naive_attn_tflops": round(w["flops"] / (a_us * 1e-6) / 1e12, 1),
+                "naive_attn_mfma_frac": round(w["flops"] / (a_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                "naive_attn_gbps": round(w["bytes"] / (a_us * 1e-6) / 1e9, 1)}
         ec = EXPAND_CONFIGS["dsv3_expand"]
         u = time_expand(ec, 20, 3, torch, binding)
         _, k = time_expand(ec, 20, 3, torch, binding, timed_kernels=(1 << 3) | (1 << 4))

@@ -383,6 +383,35 @@ int32_t mla_expand_kv(const void *c_kv, const void *rms_w, const void *wkv_b, vo
                       int64_t qk_nope_head_dim, int64_t v_head_dim, float eps, int32_t dtype,
                       int32_t path, void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Cache append of the naive route: the page "Naive vs Absorb Attention Implementations in
+ * DeepSeek-V3" (sections "Memory Layout and Cache Structure" and "Naive Path Execution") has the
+ * naive path produce keys and values through wkv_b and cache them at full width.  This writes the
+ * S new tokens of each sequence into such caches, in the head-major layout mla_naive_attn reads:
+ *
+ *   c_kv_new  [B, S, C]              raw compressed latent of the new tokens
+ *   k_pe_new  [B, S, R]              their rope keys, already rotated (or NULL)
+ *   rms_w     [C], wkv_b [H * (Dn + Dv), C]   as in mla_expand_kv
+ *   k_cache   [H, Bmax, Tmax, Dn]    row (h, b, p) := the K_nope row mla_expand_kv computes for
+ *                                    token (b, s)
+ *   v_cache   [H, Bmax, Tmax, Dv]    row (h, b, p) := its V row
+ *   pe_cache  [Bmax, Tmax, R]        row (b, p) := k_pe_new[b, s] (or NULL, with k_pe_new NULL)
+ *
+ * with p = end_pos - S + s, the positions mla_naive_attn gives the same S query tokens.  Every
+ * other cache row is left untouched.  The shape descriptor supplies B, S, H, C, R, Dn, Dv, Bmax
+ * and Tmax; requires 1 <= S <= end_pos <= Tmax and B <= Bmax.  The rows written are bit-identical
+ * to mla_expand_kv's rows for the same tokens, dtype and kernel path; MLA_PATH_AUTO takes the
+ * matrix-core kernels where mla_expand_kv would, unless Bmax * Tmax exceeds 2^23 or R is not a
+ * multiple of 8 (then the plain ones).  workspace: at least
+ * mla_expand_kv_workspace_size(B * S, H, C, Dn, Dv, dtype, path) bytes.  The caches must not
+ * overlap each other, an input or the workspace.  Returns MLA_OK or a negative MLA_ERR_* status.
+ */
+int32_t mla_expand_kv_append(const void *c_kv_new, const void *k_pe_new, const void *rms_w,
+                             const void *wkv_b, float eps, int64_t end_pos, void *k_cache,
+                             void *v_cache, void *pe_cache, const mla_attn_shape *shape,
+                             int32_t dtype, int32_t path, void *workspace, size_t workspace_bytes,
+                             void *stream);
+
 /* ---- kernel timing (benchmark instrumentation) ----------------------------------------------
  * While a kernel's bit is set in the mask given to mla_timing_enable (bit k = kernel id k), every
  * launch of it from this thread carries a pair of HIP events on the launch stream.  A single

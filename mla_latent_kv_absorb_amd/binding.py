@@ -33,7 +33,7 @@ EXPORTED = ("mla_absorb_attn", "mla_absorb_attn_noalloc", "mla_absorb_attn_ragge
             "mla_absorb_attn_workspace_size", "mla_absorb_attn_ragged_workspace_size",
             "mla_absorb_attn_paged_workspace_size",
             "mla_absorb_attn_sparse_workspace_size", "mla_cache_append", "mla_cache_append_paged",
-            "mla_expand_kv", "mla_expand_kv_workspace_size", "mla_naive_attn",
+            "mla_expand_kv", "mla_expand_kv_workspace_size", "mla_expand_kv_append", "mla_naive_attn",
             "mla_strerror",
             "mla_last_error", "mla_timing_enable", "mla_timing_collect", "mla_kernel_name")
 
@@ -124,6 +124,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_expand_kv.restype = i32
     lib.mla_expand_kv_workspace_size.argtypes = [i64, i64, i64, i64, i64, i32, i32]
     lib.mla_expand_kv_workspace_size.restype = sz
+    lib.mla_expand_kv_append.argtypes = [vp, vp, vp, vp, ctypes.c_float, i64, vp, vp, vp, ctypes.POINTER(AttnShape),
+                                         i32, i32, vp, sz, vp]
+    lib.mla_expand_kv_append.restype = i32
     lib.mla_strerror.argtypes = [i32]
     lib.mla_strerror.restype = ctypes.c_char_p
     lib.mla_last_error.argtypes = []
@@ -543,3 +546,56 @@ def expand_kv(c_kv, rms_w, wkv_b, n_heads: int, qk_nope_head_dim: int, v_head_di
                            _stream_handle(c_kv.device))
     _check(rc)
     return k_nope, v
+
+
+class ExpandAppendCall:
+    """One naive-route cache append (mla_expand_kv_append) with its arguments marshalled once: the
+    new tokens' keys and values, expanded through wkv_b, into the full-width head-major caches
+    k_cache [H, Bmax, Tmax, Dn] / v_cache [H, Bmax, Tmax, Dv] at positions end_pos - S + s, and
+    their rope keys into pe_cache [Bmax, Tmax, R] (k_pe_new and pe_cache: both or neither).  Every
+    call of the object re-issues the append on the stream current at construction."""
+
+    def __init__(self, c_kv_new, k_pe_new, rms_w, wkv_b, eps: float, end_pos: int, k_cache, v_cache, pe_cache, *,
+                 path: str = "auto", workspace=None):
+        import torch
+
+        lib = load()
+        if c_kv_new.dim() != 3 or k_cache.dim() != 4 or v_cache.dim() != 4:
+            raise ValueError("expected c_kv_new [B,S,C], k_cache [H,Bmax,Tmax,Dn], v_cache [H,Bmax,Tmax,Dv]")
+        if (k_pe_new is None) != (pe_cache is None):
+            raise ValueError("k_pe_new and pe_cache go together")
+        B, S, C = c_kv_new.shape
+        H, Bmax, Tmax, Dn = k_cache.shape
+        Dv = v_cache.shape[3]
+        R = k_pe_new.shape[-1] if k_pe_new is not None else (pe_cache.shape[-1] if pe_cache is not None else 64)
+        _shape(rms_w, (C,), "rms_w")
+        _shape(wkv_b, (H * (Dn + Dv), C), "wkv_b")
+        _shape(v_cache, (H, Bmax, Tmax, Dv), "v_cache")
+        tensors = [c_kv_new, rms_w, wkv_b, k_cache, v_cache]
+        if k_pe_new is not None:
+            _shape(k_pe_new, (B, S, R), "k_pe_new")
+            _shape(pe_cache, (Bmax, Tmax, R), "pe_cache")
+            tensors += [k_pe_new, pe_cache]
+        _require_device(*tensors)
+        dt = _dtype_code(c_kv_new)
+        shape = AttnShape(B, S, H, C, R, Dn, Dv, Bmax, Tmax)
+        need = expand_kv_workspace_size(B * S, H, C, Dn, Dv, dt, path)
+        if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+            workspace = torch.empty(need, dtype=torch.uint8, device=c_kv_new.device)
+        self._keep = (c_kv_new, k_pe_new, rms_w, wkv_b, k_cache, v_cache, pe_cache, workspace, shape)
+        self._fn = lib.mla_expand_kv_append
+        self._args = (c_kv_new.data_ptr(), None if k_pe_new is None else k_pe_new.data_ptr(), rms_w.data_ptr(),
+                      wkv_b.data_ptr(), eps, end_pos, k_cache.data_ptr(), v_cache.data_ptr(),
+                      None if pe_cache is None else pe_cache.data_ptr(), ctypes.byref(shape), dt, PATHS[path],
+                      workspace.data_ptr() if need else None,
+                      workspace.numel() * workspace.element_size() if need else 0, _stream_handle(c_kv_new.device))
+
+    def __call__(self):
+        _check(self._fn(*self._args))
+
+
+def expand_kv_append(c_kv_new, k_pe_new, rms_w, wkv_b, eps: float, end_pos: int, k_cache, v_cache, pe_cache, *,
+                     path: str = "auto", workspace=None):
+    """The naive path's cache append (mla_expand_kv_append), in place; see ExpandAppendCall."""
+    ExpandAppendCall(c_kv_new, k_pe_new, rms_w, wkv_b, eps, end_pos, k_cache, v_cache, pe_cache, path=path,
+                     workspace=workspace)()

@@ -11,9 +11,14 @@
 //   2. expand_kernel       y = n . wkv_b^T per (128 tokens, one head), two workgroups per compute
 //                          unit so one's waits and epilogue overlap the other's MFMAs.  Both
 //                          operands stream into LDS by DMA through a three-stage ring of 32-column
-//                          tiles; the epilogue goes through LDS so every global store is a full
-//                          16-byte, fully coalesced write, and each workgroup's K_nope and V blocks
-//                          are two contiguous 32 KB regions.
+//                          tiles; the epilogue goes through LDS so every global store writes whole
+//                          256-byte K / V rows with streaming (non-temporal) stores.
+//
+// Output rows: input token t = b * S_in + s lands in row b * out_seq_stride + out_row0 + s of each
+// head's block.  The plain expansion writes row t; the naive path's cache append ("Naive vs Absorb
+// Attention Implementations in DeepSeek-V3", section "Memory Layout and Cache Structure": keys and
+// values are cached at full width) writes the new tokens' rows of the head-major caches
+// [H, Bmax, Tmax, 128], and the prep kernel copies their rope keys into the rope cache alongside.
 #include "common.h"
 #include "launch.h"
 #include "mfma_common.h"
@@ -42,14 +47,38 @@ static_assert(2 * kLds <= 160 * 1024, "two workgroups share a compute unit");
 
 __host__ __device__ __forceinline__ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Row of an output block that input token t goes to (see the header).
+__device__ __forceinline__ uint32_t out_row(uint32_t t, uint32_t S_in, uint32_t seq_stride, uint32_t row0) {
+  const uint32_t b = t / S_in;
+  return b * seq_stride + row0 + (t - b * S_in);
+}
+
 // ---- 1. per-token prep --------------------------------------------------------------------------
+struct PrepArgs {
+  const uint16_t *c_kv;   // [T, 512]
+  const uint16_t *rms_w;  // [512]
+  uint16_t *xn;           // [T, 512] workspace
+  const uint16_t *k_pe;   // [T, R] or null
+  uint16_t *pe_out;       // [out_rows, R] or null
+  int32_t T, R, S_in, seq_stride, row0;
+  float eps;
+};
+
 // One wave per token row: lane l owns columns 8 l .. 8 l + 7.  n = c_kv * rms_w / rms, rounded once.
-__global__ void __launch_bounds__(256) expand_prep_kernel(const uint16_t *__restrict__ c_kv,
-                                                          const uint16_t *__restrict__ rms_w,
-                                                          uint16_t *__restrict__ xn, int32_t T, float eps) {
+// With a rope cache, lanes 0 .. R / 8 - 1 also copy the token's rope key row to its cache row.
+__global__ void __launch_bounds__(256) expand_prep_kernel(PrepArgs a) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (t >= T) return;
+  if (t >= a.T) return;
+  const uint16_t *__restrict__ c_kv = a.c_kv;
+  const uint16_t *__restrict__ rms_w = a.rms_w;
+  uint16_t *__restrict__ xn = a.xn;
+  const float eps = a.eps;
+  if (a.pe_out && lane < a.R / 8) {
+    const u32x4 pv = *reinterpret_cast<const u32x4 *>(a.k_pe + int64_t(t) * a.R + lane * 8);
+    const uint32_t r = out_row(uint32_t(t), uint32_t(a.S_in), uint32_t(a.seq_stride), uint32_t(a.row0));
+    *reinterpret_cast<u32x4 *>(a.pe_out + int64_t(r) * a.R + lane * 8) = pv;
+  }
   const u32x4 xv = *reinterpret_cast<const u32x4 *>(c_kv + int64_t(t) * kC + lane * 8);
   const u32x4 wv = *reinterpret_cast<const u32x4 *>(rms_w + lane * 8);
   float x[8], ss = 0.f;
@@ -73,9 +102,10 @@ __global__ void __launch_bounds__(256) expand_prep_kernel(const uint16_t *__rest
 struct ExpandArgs {
   const uint16_t *xn;     // [T, 512] normalised latent n, bf16
   const uint16_t *wkv_b;  // [H * 256, 512]
-  uint16_t *k_nope;       // [H, T, 128]
-  uint16_t *v;            // [H, T, 128]
+  uint16_t *k_nope;       // [H, out_rows, 128]
+  uint16_t *v;            // [H, out_rows, 128]
   int32_t T, H, tblocks;
+  int32_t S_in, seq_stride, row0, out_rows;  // output placement (see the header)
   int32_t grouped;        // 1: workgroups run in blocks of 8 heads x 4 token blocks (see below)
 };
 
@@ -197,18 +227,30 @@ expand_kernel(ExpandArgs a) {
       }
     }
   }
-  // same wavefront wrote these rows; LDS operations of one wavefront complete in order
-  // (re-scalarised: the store descriptor must live in scalar registers, or every store becomes a
+  // same wavefront wrote these rows; LDS operations of one wavefront complete in order.  Each store
+  // writes 4 token rows (16 lanes x 16 bytes each) to their output rows; rows past T get an offset
+  // outside the head's block, and the store drops them.
+  // (the descriptor is re-scalarised: it must live in scalar registers, or every store becomes a
   // loop over lanes)
-  const int rows_valid = __builtin_amdgcn_readfirstlane(max(0, min(64, a.T - (t0 + wt * 64))));
-  const rsrc_t ores = make_rsrc((wj == 0 ? a.k_nope : a.v) + (int64_t(h) * a.T + t0 + wt * 64) * 128,
-                                uint32_t(rows_valid) * 256);
+  const rsrc_t ores = make_rsrc((wj == 0 ? a.k_nope : a.v) + int64_t(h) * a.out_rows * 128,
+                                uint32_t(a.out_rows) * 256);
   const uint32_t rd_lane = uint32_t(lane >> 4) * kEpiPitch + (lane & 15) * 16;
-  const uint32_t st_lane = uint32_t(lane >> 4) * 256 + (lane & 15) * 16;
+  // this lane's token at store 0, its sequence and its index in the sequence
+  uint32_t tok = uint32_t(t0 + wt * 64 + (lane >> 4));
+  uint32_t sb = tok / uint32_t(a.S_in);
+  uint32_t ss = tok - sb * uint32_t(a.S_in);
 #pragma unroll 8
   for (int it = 0; it < 16; ++it) {
     const u32x4 v = lds_read16(epi, rd_lane + it * 4 * kEpiPitch);
-    buf_store16(ores, v, st_lane + uint32_t(it * 1024), 0);  // rows past T fall outside the range: dropped
+    const uint32_t row = sb * uint32_t(a.seq_stride) + uint32_t(a.row0) + ss;
+    const uint32_t voff = tok < uint32_t(a.T) ? row * 256u + (lane & 15) * 16 : 0x80000000u;
+    buf_store16_nt(ores, v, voff, 0);
+    tok += 4;
+    ss += 4;
+    while (ss >= uint32_t(a.S_in)) {  // at most once unless a sequence holds fewer than 4 tokens
+      ss -= uint32_t(a.S_in);
+      ++sb;
+    }
   }
 }
 
@@ -221,6 +263,9 @@ bool mfma_expand_supported(const ExpandCall &c, const char **why) {
     return false;
   }
   if (c.T > (int64_t(1) << 22)) { *why = "n_tokens must be at most 4194304"; return false; }
+  // output offsets within one head's block are 32-bit byte counts below 2^31
+  if (c.out_rows > (int64_t(1) << 23)) { *why = "output rows per head must be at most 8388608"; return false; }
+  if (c.k_pe && (c.R % 8 != 0 || c.R > 512)) { *why = "rope width must be a multiple of 8 up to 512"; return false; }
   return true;
 }
 
@@ -229,13 +274,16 @@ size_t mfma_expand_workspace(const ExpandCall &c) { return align256(size_t(c.T) 
 
 hipError_t mfma_expand_kv(const ExpandCall &c) {
   uint16_t *xn = static_cast<uint16_t *>(c.ws);
+  PrepArgs p{static_cast<const uint16_t *>(c.c_kv), static_cast<const uint16_t *>(c.rms_w), xn,
+             static_cast<const uint16_t *>(c.k_pe), static_cast<uint16_t *>(c.pe_out), int32_t(c.T),
+             int32_t(c.R), int32_t(c.S_in), int32_t(c.out_seq_stride), int32_t(c.out_row0), c.eps};
   hipError_t err = launch_kernel(MLA_KERNEL_EXPAND_PREP, expand_prep_kernel, dim3(unsigned((c.T + 3) / 4)), dim3(256),
-                                 0, c.stream, static_cast<const uint16_t *>(c.c_kv),
-                                 static_cast<const uint16_t *>(c.rms_w), xn, int32_t(c.T), c.eps);
+                                 0, c.stream, p);
   if (err != hipSuccess) return err;
   const int32_t tblocks = int32_t((c.T + kTT - 1) / kTT);
   ExpandArgs a{xn, static_cast<const uint16_t *>(c.wkv_b), static_cast<uint16_t *>(c.k_nope),
                static_cast<uint16_t *>(c.v), int32_t(c.T), int32_t(c.H), tblocks,
+               int32_t(c.S_in), int32_t(c.out_seq_stride), int32_t(c.out_row0), int32_t(c.out_rows),
                (c.H % 8 == 0 && tblocks % 8 == 0) ? 1 : 0};
   return launch_kernel(MLA_KERNEL_EXPAND, expand_kernel, dim3(unsigned(int64_t(tblocks) * c.H)), dim3(kWaves * 64),
                        0, c.stream, a);

@@ -47,6 +47,17 @@ struct ExpandCall {
   int32_t dtype;
   const void *c_kv, *rms_w, *wkv_b;
   void *k_nope, *v;
+  // Output placement: input token t = b * S_in + s (s < S_in) goes to row
+  // b * out_seq_stride + out_row0 + s of each head's [out_rows, Dn] / [out_rows, Dv] block.  A
+  // plain expansion has S_in = out_seq_stride = out_rows = T and out_row0 = 0 (row t); the naive
+  // path's cache append has S_in = new tokens per sequence, out_seq_stride = Tmax, out_row0 =
+  // start_pos and out_rows = Bmax * Tmax.
+  int64_t S_in, out_seq_stride, out_row0, out_rows;
+  // Optional rope keys copied along (both null or both set): k_pe [T, R] row t to row
+  // (placement as above) of pe_out [out_rows, R].
+  const void *k_pe;
+  void *pe_out;
+  int64_t R;
   void *ws;  // workspace (layout chosen by the path's workspace function)
   hipStream_t stream;
 };

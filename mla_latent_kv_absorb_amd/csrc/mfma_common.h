@@ -102,6 +102,10 @@ __device__ __forceinline__ void buf_store16(rsrc_t r, const u32x4 &v, uint32_t v
 __device__ __forceinline__ void buf_store8(rsrc_t r, const u32x2 &v, uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_buffer_store_b64(v, r, voff, soff, 0);
 }
+// A streaming store (non-temporal hint): for outputs that no later step of the same call reads.
+__device__ __forceinline__ void buf_store16_nt(rsrc_t r, const u32x4 &v, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, soff, 2);
+}
 // 16 bytes per lane from a buffer straight into LDS: lane l's bytes land at lds_base + 16 * l
 // (lds_base is wavefront-uniform and goes through M0).
 //

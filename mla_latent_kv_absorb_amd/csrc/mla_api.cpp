@@ -386,6 +386,20 @@ int32_t mla_absorb_attn_sparse(const void *q_nope, const void *q_pe, const void 
 
 namespace {
 
+// The kernel path of a planned expansion (placement and rope copy already set in e).
+int32_t choose_expand_path(const mla::ExpandCall &e, int32_t path, bool &use_mfma) {
+  use_mfma = false;
+  if (path != MLA_PATH_AUTO && path != MLA_PATH_PLAIN && path != MLA_PATH_MFMA)
+    return fail(MLA_ERR_UNSUPPORTED, "unknown path %d", path);
+  if (path != MLA_PATH_PLAIN) {
+    const char *why = "";
+    const bool ok = mla::mfma_expand_supported(e, &why);
+    if (path == MLA_PATH_MFMA && !ok) return fail(MLA_ERR_UNSUPPORTED, "matrix-core path: %s", why);
+    use_mfma = ok;
+  }
+  return MLA_OK;
+}
+
 // Validation shared by mla_expand_kv and mla_expand_kv_workspace_size; no HIP calls.
 int32_t plan_expand(int64_t n_tokens, int64_t n_heads, int64_t kv_lora_rank, int64_t qk_nope_head_dim,
                     int64_t v_head_dim, float eps, int32_t dtype, int32_t path, mla::ExpandCall &e,
@@ -408,13 +422,45 @@ int32_t plan_expand(int64_t n_tokens, int64_t n_heads, int64_t kv_lora_rank, int
   e = mla::ExpandCall{};
   e.T = n_tokens; e.H = n_heads; e.C = kv_lora_rank; e.Dn = qk_nope_head_dim; e.Dv = v_head_dim;
   e.eps = eps; e.dtype = dtype;
+  // plain placement (row t of each head's block); the cache append overrides it before the path
+  // check, which depends on it
+  e.S_in = n_tokens; e.out_seq_stride = n_tokens; e.out_row0 = 0; e.out_rows = n_tokens;
   use_mfma = false;
-  if (path != MLA_PATH_PLAIN) {
-    const char *why = "";
-    const bool ok = mla::mfma_expand_supported(e, &why);
-    if (path == MLA_PATH_MFMA && !ok) return fail(MLA_ERR_UNSUPPORTED, "matrix-core path: %s", why);
-    use_mfma = ok;
+  return choose_expand_path(e, path, use_mfma);
+}
+
+// Enqueues a planned expansion (e without pointers) after the pointer, overlap and workspace
+// checks.  ins: c_kv, rms_w, wkv_b[, k_pe]; outs: k_nope, v[, pe_out], with their byte sizes.
+int32_t run_expand_call(mla::ExpandCall &e, bool use_mfma, const void *const *ptrs, const size_t *sizes,
+                        const char *const *names, int n_in, int n_out, void *workspace, size_t workspace_bytes,
+                        void *stream) {
+  const int n = n_in + n_out;
+  for (int i = 0; i < n; ++i) {
+    if (!ptrs[i]) return fail(MLA_ERR_NULL, "%s is NULL", names[i]);
+    if (misaligned(ptrs[i])) return fail(MLA_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
   }
+  for (int o = n_in; o < n; ++o)
+    for (int i = 0; i < n; ++i)
+      if (i != o && overlaps(ptrs[o], sizes[o], ptrs[i], sizes[i]))
+        return fail(MLA_ERR_SHAPE, "%s overlaps %s", names[o], names[i]);
+  const size_t need = use_mfma ? mla::mfma_expand_workspace(e) : 0;
+  if (need > 0) {
+    if (!workspace) return fail(MLA_ERR_WORKSPACE, "workspace is NULL but %zu bytes are needed", need);
+    if (workspace_bytes < need)
+      return fail(MLA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+    if (misaligned(workspace)) return fail(MLA_ERR_ALIGN, "workspace is not 16-byte aligned");
+    for (int i = 0; i < n; ++i)
+      if (overlaps(workspace, need, ptrs[i], sizes[i]))
+        return fail(MLA_ERR_WORKSPACE, "workspace overlaps %s", names[i]);
+  }
+  e.c_kv = ptrs[0]; e.rms_w = ptrs[1]; e.wkv_b = ptrs[2];
+  e.k_pe = n_in > 3 ? ptrs[3] : nullptr;
+  e.k_nope = const_cast<void *>(ptrs[n_in]); e.v = const_cast<void *>(ptrs[n_in + 1]);
+  e.pe_out = n_out > 2 ? const_cast<void *>(ptrs[n_in + 2]) : nullptr;
+  e.ws = workspace;
+  e.stream = static_cast<hipStream_t>(stream);
+  hipError_t err = use_mfma ? mla::mfma_expand_kv(e) : mla::plain_expand_kv(e);
+  if (err != hipSuccess) return fail(MLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
   return MLA_OK;
 }
 
@@ -445,34 +491,70 @@ int32_t mla_expand_kv(const void *c_kv, const void *rms_w, const void *wkv_b, vo
   if (st != MLA_OK) return st;
   const void *ptrs[] = {c_kv, rms_w, wkv_b, k_nope, v};
   const char *names[] = {"c_kv", "rms_w", "wkv_b", "k_nope", "v"};
-  for (int i = 0; i < 5; ++i) {
-    if (!ptrs[i]) return fail(MLA_ERR_NULL, "%s is NULL", names[i]);
-    if (misaligned(ptrs[i])) return fail(MLA_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
-  }
   const size_t es = elem_size(dtype);
   const size_t sizes[] = {size_t(n_tokens * kv_lora_rank) * es, size_t(kv_lora_rank) * es,
                           size_t(n_heads * (qk_nope_head_dim + v_head_dim) * kv_lora_rank) * es,
                           size_t(n_heads * n_tokens * qk_nope_head_dim) * es,
                           size_t(n_heads * n_tokens * v_head_dim) * es};
-  for (int o = 3; o < 5; ++o)
-    for (int i = 0; i < 5; ++i)
-      if (i != o && overlaps(ptrs[o], sizes[o], ptrs[i], sizes[i]))
-        return fail(MLA_ERR_SHAPE, "%s overlaps %s", names[o], names[i]);
-  const size_t need = use_mfma ? mla::mfma_expand_workspace(e) : 0;
-  if (need > 0) {
-    if (!workspace) return fail(MLA_ERR_WORKSPACE, "workspace is NULL but %zu bytes are needed", need);
-    if (workspace_bytes < need)
-      return fail(MLA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
-    if (misaligned(workspace)) return fail(MLA_ERR_ALIGN, "workspace is not 16-byte aligned");
-    for (int i = 0; i < 5; ++i)
-      if (overlaps(workspace, need, ptrs[i], sizes[i]))
-        return fail(MLA_ERR_WORKSPACE, "workspace overlaps %s", names[i]);
-  }
-  e.c_kv = c_kv; e.rms_w = rms_w; e.wkv_b = wkv_b; e.k_nope = k_nope; e.v = v; e.ws = workspace;
-  e.stream = static_cast<hipStream_t>(stream);
-  hipError_t err = use_mfma ? mla::mfma_expand_kv(e) : mla::plain_expand_kv(e);
-  if (err != hipSuccess) return fail(MLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
-  return MLA_OK;
+  return run_expand_call(e, use_mfma, ptrs, sizes, names, 3, 2, workspace, workspace_bytes, stream);
+}
+
+int32_t mla_expand_kv_append(const void *c_kv_new, const void *k_pe_new, const void *rms_w, const void *wkv_b,
+                             float eps, int64_t end_pos, void *k_cache, void *v_cache, void *pe_cache,
+                             const mla_attn_shape *shape, int32_t dtype, int32_t path, void *workspace,
+                             size_t workspace_bytes, void *stream) {
+  clear_error();
+  if (!shape) return fail(MLA_ERR_NULL, "shape is NULL");
+  const mla_attn_shape s = *shape;
+  const int64_t dims[] = {s.batch, s.seqlen_q, s.n_heads, s.kv_lora_rank, s.qk_rope_head_dim,
+                          s.qk_nope_head_dim, s.v_head_dim, s.cache_batch, s.cache_len};
+  const char *dnames[] = {"batch", "seqlen_q", "n_heads", "kv_lora_rank", "qk_rope_head_dim",
+                          "qk_nope_head_dim", "v_head_dim", "cache_batch", "cache_len"};
+  for (int i = 0; i < 9; ++i)
+    if (dims[i] <= 0 || dims[i] > (int64_t(1) << 31))
+      return fail(MLA_ERR_SHAPE, "%s = %lld is out of range", dnames[i], (long long)dims[i]);
+  if (s.batch > s.cache_batch)
+    return fail(MLA_ERR_RANGE, "batch %lld exceeds cache_batch %lld", (long long)s.batch, (long long)s.cache_batch);
+  if (end_pos < 1 || end_pos > s.cache_len)
+    return fail(MLA_ERR_RANGE, "end_pos %lld outside [1, cache_len=%lld]", (long long)end_pos, (long long)s.cache_len);
+  if (s.seqlen_q > end_pos)
+    return fail(MLA_ERR_RANGE, "seqlen_q %lld exceeds end_pos %lld", (long long)s.seqlen_q, (long long)end_pos);
+  if ((k_pe_new == nullptr) != (pe_cache == nullptr))
+    return fail(MLA_ERR_NULL, "k_pe_new and pe_cache must both be given or both be NULL");
+  const int64_t T = s.batch * s.seqlen_q, rows = s.cache_batch * s.cache_len;
+  if (T > (int64_t(1) << 31) || rows > (int64_t(1) << 40))
+    return fail(MLA_ERR_SHAPE, "batch * seqlen_q or cache_batch * cache_len is too large");
+  mla::ExpandCall e;
+  bool use_mfma = false;
+  // the checks of mla_expand_kv for the B * S new tokens (path chosen below, after placement)
+  int32_t st = plan_expand(T, s.n_heads, s.kv_lora_rank, s.qk_nope_head_dim, s.v_head_dim, eps, dtype,
+                           MLA_PATH_PLAIN, e, use_mfma);
+  if (st != MLA_OK) return st;
+  const bool with_pe = pe_cache != nullptr;
+  if (with_pe && s.qk_rope_head_dim % int64_t(16 / elem_size(dtype)))
+    return fail(MLA_ERR_ALIGN, "qk_rope_head_dim must be a multiple of %lld elements (16-byte rows)",
+                (long long)(16 / elem_size(dtype)));
+  e.S_in = s.seqlen_q;
+  e.out_seq_stride = s.cache_len;
+  e.out_row0 = end_pos - s.seqlen_q;
+  e.out_rows = rows;
+  e.R = s.qk_rope_head_dim;
+  e.k_pe = with_pe ? k_pe_new : nullptr;  // placeholders: the path check looks at the rope copy
+  e.pe_out = with_pe ? pe_cache : nullptr;
+  st = choose_expand_path(e, path, use_mfma);
+  if (st != MLA_OK) return st;
+  const size_t es = elem_size(dtype);
+  const void *ptrs[] = {c_kv_new, rms_w, wkv_b, k_pe_new, k_cache, v_cache, pe_cache};
+  const char *names[] = {"c_kv_new", "rms_w", "wkv_b", "k_pe_new", "k_cache", "v_cache", "pe_cache"};
+  const size_t sizes[] = {size_t(T * s.kv_lora_rank) * es, size_t(s.kv_lora_rank) * es,
+                          size_t(s.n_heads * (s.qk_nope_head_dim + s.v_head_dim) * s.kv_lora_rank) * es,
+                          size_t(T * s.qk_rope_head_dim) * es, size_t(s.n_heads * rows * s.qk_nope_head_dim) * es,
+                          size_t(s.n_heads * rows * s.v_head_dim) * es, size_t(rows * s.qk_rope_head_dim) * es};
+  if (with_pe) return run_expand_call(e, use_mfma, ptrs, sizes, names, 4, 3, workspace, workspace_bytes, stream);
+  const void *p2[] = {c_kv_new, rms_w, wkv_b, k_cache, v_cache};
+  const char *n2[] = {"c_kv_new", "rms_w", "wkv_b", "k_cache", "v_cache"};
+  const size_t s2[] = {sizes[0], sizes[1], sizes[2], sizes[4], sizes[5]};
+  return run_expand_call(e, use_mfma, p2, s2, n2, 3, 2, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

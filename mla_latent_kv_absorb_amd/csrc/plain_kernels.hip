@@ -165,7 +165,9 @@ plain_merge_upproj_kernel(const float *__restrict__ part_ml, const float *__rest
 }
 
 // One block per (token, 256 output features): RMSNorm of the token's latent, then the
-// projection; feature j of head h = j / (Dn+Dv) goes to k_nope or v by its offset in the head.
+// projection; feature j of head h = j / (Dn+Dv) goes to k_nope or v by its offset in the head, in
+// the token's output row (b * out_seq_stride + out_row0 + s for token t = b * S_in + s).  With a
+// rope cache, the blocks of the first feature range also copy the token's rope key row.
 template <typename T>
 __global__ void __launch_bounds__(kThreads)
 plain_expand_kernel(const T *__restrict__ c_kv, const T *__restrict__ rms_w, const T *__restrict__ wkv_b,
@@ -175,6 +177,10 @@ plain_expand_kernel(const T *__restrict__ c_kv, const T *__restrict__ rms_w, con
   float *red = sn + e.C;    // 16
   const int64_t t = blockIdx.x;
   const int tid = threadIdx.x;
+  const int64_t orow = (t / e.S_in) * e.out_seq_stride + e.out_row0 + t % e.S_in;
+  if (e.pe_out && blockIdx.y == 0)
+    for (int64_t r = tid; r < e.R; r += kThreads)
+      static_cast<T *>(e.pe_out)[orow * e.R + r] = static_cast<const T *>(e.k_pe)[t * e.R + r];
   float ss = 0.f;
   for (int64_t c = tid; c < e.C; c += kThreads) {
     const float x = Elem<T>::load(c_kv, t * e.C + c);
@@ -191,8 +197,8 @@ plain_expand_kernel(const T *__restrict__ c_kv, const T *__restrict__ rms_w, con
   float acc = 0.f;
   for (int64_t c = 0; c < e.C; ++c) acc = fmaf(sn[c], Elem<T>::load(wkv_b, j * e.C + c), acc);
   const int64_t h = j / per_head, jj = j % per_head;
-  if (jj < e.Dn) Elem<T>::store(k_nope, (h * e.T + t) * e.Dn + jj, acc);
-  else Elem<T>::store(v, (h * e.T + t) * e.Dv + (jj - e.Dn), acc);
+  if (jj < e.Dn) Elem<T>::store(k_nope, (h * e.out_rows + orow) * e.Dn + jj, acc);
+  else Elem<T>::store(v, (h * e.out_rows + orow) * e.Dv + (jj - e.Dn), acc);
 }
 
 template <typename T>

@@ -165,6 +165,58 @@ def test_expand_workspace(lib):
     assert call_expand(lib, ws=P[0], path=B.PATHS["mfma"]) == B.MLA_ERR_WORKSPACE  # overlaps c_kv
 
 
+def call_expand_append(lib, s, end_pos=4096, eps=1e-6, dtype=B.MLA_DTYPE_BF16, ptrs=None, path=0, ws=P[7],
+                       ws_bytes=1 << 40):
+    p = list(P[:7]) if ptrs is None else ptrs
+    return lib.mla_expand_kv_append(p[0], p[1], p[2], p[3], eps, end_pos, p[4], p[5], p[6], ctypes.byref(s), dtype,
+                                    path, ws, ws_bytes, None)
+
+
+def test_expand_append_argument_errors(lib):
+    s = shape(seqlen_q=512)
+    assert lib.mla_expand_kv_append(*P[:4], 1e-6, 4096, *P[4:7], None, B.MLA_DTYPE_BF16, 0, P[7], 1 << 40,
+                                    None) == B.MLA_ERR_NULL
+    assert call_expand_append(lib, s, end_pos=4097) == B.MLA_ERR_RANGE
+    assert call_expand_append(lib, s, end_pos=511) == B.MLA_ERR_RANGE  # S > end_pos
+    assert call_expand_append(lib, shape(batch=3)) == B.MLA_ERR_RANGE
+    assert call_expand_append(lib, shape(n_heads=0)) == B.MLA_ERR_SHAPE
+    assert call_expand_append(lib, s, eps=-1.0) == B.MLA_ERR_SHAPE
+    assert call_expand_append(lib, s, dtype=4) == B.MLA_ERR_DTYPE
+    assert call_expand_append(lib, s, path=9) == B.MLA_ERR_UNSUPPORTED
+    assert call_expand_append(lib, shape(kv_lora_rank=500)) == B.MLA_ERR_ALIGN
+    assert call_expand_append(lib, shape(qk_rope_head_dim=4)) == B.MLA_ERR_ALIGN
+    # the rope rows go together: a rope source without a rope cache (and the reverse) is refused
+    for i in (1, 6):
+        p = list(P[:7])
+        p[i] = None
+        assert call_expand_append(lib, s, ptrs=p) == B.MLA_ERR_NULL and "k_pe_new" in B.last_error()
+    for i in (0, 2, 3, 4, 5):
+        p = list(P[:7])
+        p[i] = None
+        assert call_expand_append(lib, s, ptrs=p) == B.MLA_ERR_NULL
+    for i in range(7):
+        p = list(P[:7])
+        p[i] = P[i] + 2
+        assert call_expand_append(lib, s, ptrs=p) == B.MLA_ERR_ALIGN
+    # the caches must not overlap each other, the new rows or the workspace
+    p = list(P[:7])
+    p[5] = P[4] + 4096  # v_cache inside k_cache
+    assert call_expand_append(lib, s, ptrs=p) == B.MLA_ERR_SHAPE
+    p = list(P[:7])
+    p[6] = P[0] + 1024  # pe_cache inside c_kv_new
+    assert call_expand_append(lib, s, ptrs=p) == B.MLA_ERR_SHAPE
+    need = lib.mla_expand_kv_workspace_size(2 * 512, 128, 512, 128, 128, B.MLA_DTYPE_BF16, B.PATHS["mfma"])
+    assert need >= 2 * 512 * 512 * 2
+    mfma = B.PATHS["mfma"]
+    assert call_expand_append(lib, s, path=mfma, ws=None, ws_bytes=0) == B.MLA_ERR_WORKSPACE
+    assert call_expand_append(lib, s, path=mfma, ws_bytes=need - 1) == B.MLA_ERR_WORKSPACE
+    assert call_expand_append(lib, s, path=mfma, ws=P[4] + 256) == B.MLA_ERR_WORKSPACE  # inside k_cache
+    # the matrix-core kernels take bf16 and at most 2^23 cache rows per head
+    assert call_expand_append(lib, s, path=mfma, dtype=B.MLA_DTYPE_F32) == B.MLA_ERR_UNSUPPORTED
+    big = shape(seqlen_q=512, cache_batch=2049, cache_len=4096)
+    assert call_expand_append(lib, big, path=mfma) == B.MLA_ERR_UNSUPPORTED and "rows" in B.last_error()
+
+
 def call_ragged(lib, s, lens, max_len=4096, ws=P[7], ws_bytes=1 << 40, out=None):
     p = list(P[:6])
     return lib.mla_absorb_attn_ragged(p[0], p[1], p[2], p[3], p[4], lens, max_len, 0.07, p[5] if out is None else out,

@@ -948,6 +948,109 @@ def test_full_size_naive_vs_absorb_prefill(gpu_lib):
     check(n, oracle_attn_full(cfg, x), TOL["bf16"], "chunk_prefill naive route, all outputs")
 
 
+# ------------------------------------------------------------------ naive-route cache append
+
+@pytest.mark.parametrize("path,dtype,S", [("mfma", "bf16", 37), ("mfma", "bf16", 3), ("mfma", "bf16", 1),
+                                          ("mfma", "bf16", 200), ("plain", "bf16", 37), ("plain", "f32", 5)])
+def test_expand_kv_append(gpu_lib, path, dtype, S):
+    """Cache rows (h, b, end_pos - S + s) get the oracle's expansion of new token (b, s), bit for bit
+    what mla_expand_kv writes for the same tokens; the rope rows are copied; every other row of the
+    three caches keeps its bits.  S = 37 and 200 put sequence boundaries inside token blocks, S = 3
+    and 1 several inside one 4-row store."""
+    if dtype == "f32":
+        H, C, R, Dn, Dv = 4, 64, 16, 32, 32
+    else:
+        H, C, R, Dn, Dv = 8, 512, 64, 128, 128
+    B, Bmax, Tmax, end_pos, eps = 2, 3, 300, 251, 1e-6
+    print(f"expand append {path} {dtype} B={B} S={S} H={H} end_pos={end_pos}", flush=True)
+    rng = np.random.default_rng(71 + S)
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    cast = (lambda a: np.asarray(a, np.float32)) if dtype == "f32" else round_bf16
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to("cuda").to(tdt)
+    c_new, kp_new = cast(rng.normal(size=(B, S, C))), cast(rng.normal(size=(B, S, R)))
+    w = cast(1.0 + 0.14 * rng.normal(size=C))
+    wkv = cast(rng.normal(size=(H * (Dn + Dv), C)) / np.sqrt(C))
+    k0, v0 = cast(rng.normal(size=(H, Bmax, Tmax, Dn))), cast(rng.normal(size=(H, Bmax, Tmax, Dv)))
+    pe0 = cast(rng.normal(size=(Bmax, Tmax, R)))
+    kc, vc, pc = dev(k0), dev(v0), dev(pe0)
+    gpu_lib.expand_kv_append(dev(c_new), dev(kp_new), dev(w), dev(wkv), eps, end_pos, kc, vc, pc, path=path)
+    ke, ve = gpu_lib.expand_kv(dev(c_new.reshape(-1, C)), dev(w), dev(wkv), H, Dn, Dv, eps, path=path)
+    torch.cuda.synchronize()
+    new = np.zeros((Bmax, Tmax), bool)
+    new[:B, end_pos - S:end_pos] = True
+    gk, gv, gp = (t.float().cpu().numpy() for t in (kc, vc, pc))
+    assert np.array_equal(gk[:, ~new], k0[:, ~new]) and np.array_equal(gv[:, ~new], v0[:, ~new]), "untouched rows"
+    assert np.array_equal(gp[~new], pe0[~new]), "untouched rope rows"
+    assert np.array_equal(gp[new], kp_new.reshape(-1, R)), "rope rows are copied exactly"
+    k_new, v_new = gk[:, new], gv[:, new]  # [H, B*S, D] in (b, s) order
+    assert np.array_equal(k_new, ke.float().cpu().numpy()) and np.array_equal(v_new, ve.float().cpu().numpy()), \
+        "appended rows differ from mla_expand_kv on the same tokens"
+    kr, vr = O.expand_kv(c_new.reshape(-1, C), w, wkv, H, Dn, Dv, eps)
+    check(k_new.astype(np.float64), kr, TOL[dtype], f"append {path} {dtype} S={S} K rows")
+    check(v_new.astype(np.float64), vr, TOL[dtype], f"append {path} {dtype} S={S} V rows")
+
+
+def test_naive_route_append_then_attend(gpu_lib):
+    """One chunk step of the naive path as the pages lay it out: the caches hold full-width keys and
+    values of the earlier positions; the chunk's new tokens are expanded into them, with their rope
+    keys, and the naive attention reads the result.  Against the oracle's expansion and attention."""
+    cfg = dsv3_small(batch=2, cache_batch=2, seqlen_q=40, end_pos=230, cache_len=256, n_heads=16)
+    print(f"naive route append+attend S={cfg.seqlen_q} end_pos={cfg.end_pos}", flush=True)
+    x = make_attn_inputs(cfg)
+    kh, vh = head_major_kv(x, cfg)  # earlier positions' full-width rows (the new rows get overwritten)
+    rng = np.random.default_rng(73)
+    c_new = round_bf16(rng.normal(size=(cfg.batch, cfg.seqlen_q, cfg.kv_lora_rank)))
+    kp_new = round_bf16(rng.normal(size=(cfg.batch, cfg.seqlen_q, cfg.qk_rope_head_dim)))
+    w = round_bf16(1.0 + 0.14 * rng.normal(size=cfg.kv_lora_rank))
+    t = to_dev(x, cfg)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to("cuda").to(torch.bfloat16)
+    kc, vc = dev(kh), dev(vh)
+    gpu_lib.expand_kv_append(dev(c_new), dev(kp_new), dev(w), t["wkv_b"], 1e-6, cfg.end_pos, kc, vc, t["pe_cache"])
+    out = run_naive(gpu_lib, cfg, t, kc, vc, path="mfma")
+    # the oracle's caches after the same append, rounded to bf16 as stored
+    kr, vr = O.expand_kv(c_new.reshape(-1, cfg.kv_lora_rank), w, x["wkv_b"], cfg.n_heads, cfg.qk_nope_head_dim,
+                         cfg.v_head_dim, 1e-6)
+    k_ref, v_ref, pe_ref = np.array(kh), np.array(vh), np.array(x["pe_cache"])
+    p0 = cfg.end_pos - cfg.seqlen_q
+    k_ref[:, :cfg.batch, p0:cfg.end_pos] = round_bf16(kr).reshape(cfg.n_heads, cfg.batch, cfg.seqlen_q, -1)
+    v_ref[:, :cfg.batch, p0:cfg.end_pos] = round_bf16(vr).reshape(cfg.n_heads, cfg.batch, cfg.seqlen_q, -1)
+    pe_ref[:cfg.batch, p0:cfg.end_pos] = kp_new
+    ref = O.attention_over_kv(x["q_nope"], x["q_pe"], k_ref, v_ref, pe_ref, cfg.end_pos, cfg.softmax_scale)
+    check(out, ref, TOL["bf16"], "naive route: append the chunk, then attend")
+
+
+def test_full_size_expand_append(gpu_lib):
+    """chunk_prefill's naive-route append: 2 x 512 new tokens into [128, 2, 4096, 128] caches at
+    positions 3584..4095; every appended element against the oracle and bit for bit against
+    mla_expand_kv, and the earlier positions untouched."""
+    cfg = ATTN_CONFIGS["chunk_prefill"]
+    B, S, H, C, R = cfg.batch, cfg.seqlen_q, cfg.n_heads, cfg.kv_lora_rank, cfg.qk_rope_head_dim
+    print(f"full-size expand append: B={B} S={S} H={H} end_pos={cfg.end_pos}", flush=True)
+    rng = np.random.default_rng(79)
+    c_new = round_bf16(rng.normal(size=(B, S, C)))
+    kp_new = round_bf16(rng.normal(size=(B, S, R)))
+    w = round_bf16(1.0 + 0.14 * rng.normal(size=C))
+    wkv = round_bf16(rng.normal(size=(H * 256, C)) / np.sqrt(C))
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to("cuda").to(torch.bfloat16)
+    shape_kv = (H, cfg.cache_batch, cfg.cache_len, 128)
+    kc = torch.full(shape_kv, 3.0, dtype=torch.bfloat16, device="cuda")
+    vc = torch.full(shape_kv, -3.0, dtype=torch.bfloat16, device="cuda")
+    pc = torch.full((cfg.cache_batch, cfg.cache_len, R), 5.0, dtype=torch.bfloat16, device="cuda")
+    gpu_lib.expand_kv_append(dev(c_new), dev(kp_new), dev(w), dev(wkv), 1e-6, cfg.end_pos, kc, vc, pc)
+    ke, ve = gpu_lib.expand_kv(dev(c_new.reshape(-1, C)), dev(w), dev(wkv), H, 128, 128, 1e-6)
+    torch.cuda.synchronize()
+    p0 = cfg.end_pos - S
+    assert bool((kc[:, :, :p0] == 3.0).all()) and bool((vc[:, :, :p0] == -3.0).all()) and \
+        bool((pc[:, :p0] == 5.0).all()), "earlier positions changed"
+    k_new = kc[:, :, p0:].reshape(H, B * S, 128)
+    v_new = vc[:, :, p0:].reshape(H, B * S, 128)
+    assert torch.equal(k_new, ke) and torch.equal(v_new, ve), "appended rows differ from mla_expand_kv"
+    assert torch.equal(pc[:, p0:].reshape(B * S, R), dev(kp_new.reshape(-1, R))), "rope rows"
+    kr, vr = O.expand_kv(c_new.reshape(-1, C), w, wkv, H, 128, 128, 1e-6)
+    check(k_new, kr, TOL["bf16"], "chunk_prefill append K rows")
+    check(v_new, vr, TOL["bf16"], "chunk_prefill append V rows")
+
+
 def test_full_size_expand(gpu_lib):
     cfg = EXPAND_CONFIGS["dsv3_expand"]
     x = make_expand_inputs(cfg)
