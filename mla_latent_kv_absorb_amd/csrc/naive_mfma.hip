@@ -155,8 +155,9 @@ naive_attn_kernel(NaiveArgs a) {
   for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
   float m_ref = -INFINITY, lsum = 0.f;
 
-#pragma unroll 1
-  for (int p = 0; p < npairs; ++p) {
+  // one pair of tiles; sp is the stage of its first tile (0 or 2, a constant in each inlined copy,
+  // so that every LDS address is a loop-invariant register plus an immediate offset)
+  auto pair = [&](int p, const int sp) __attribute__((always_inline)) {
     // pair p must have landed: pair 0 with the query, pair p > 0 as the latest issued
     if (p > 0) wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();  // every wave's part of pair p is in; every wave is done with pair p - 1
@@ -170,7 +171,7 @@ naive_attn_kernel(NaiveArgs a) {
     f32x16 sacc[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const unsigned char *st = smem + ((2 * p + u) % kStages) * kStageBytes;
+      const unsigned char *st = smem + (sp + u) * kStageBytes;
       u32x4 fr[12];
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) fr[ks] = lds_read16(st, k_off[ks]);
@@ -208,7 +209,7 @@ naive_attn_kernel(NaiveArgs a) {
     const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const unsigned char *st = smem + ((2 * p + u) % kStages) * kStageBytes;
+      const unsigned char *st = smem + (sp + u) * kStageBytes;
       u32x4 pb[2];
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
@@ -230,6 +231,11 @@ naive_attn_kernel(NaiveArgs a) {
           acc[cb] = mfma32(vf, pb[ks], acc[cb]);
         }
     }
+  };
+#pragma unroll 1
+  for (int p = 0; p < npairs; p += 2) {  // pair p in stages 0 and 1, pair p + 1 in stages 2 and 3
+    pair(p, 0);
+    if (p + 1 < npairs) pair(p + 1, 2);
   }
   wait_vmcnt<0>();  // tiles issued past the last needed one land before the workgroup ends
 
