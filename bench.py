@@ -292,10 +292,11 @@ def time_naive_route(cfg, steps, warmup, torch, binding, seed=3, from_latent=Fal
     ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
     lat = x["kv_cache"].view(rows, C)
     k4, v4 = k.view(H, cfg.cache_batch, cfg.cache_len, Dn), v.view(H, cfg.cache_batch, cfg.cache_len, Dv)
+    attend = binding.NaiveAttnCall(x["q_nope"], x["q_pe"], k4, v4, x["pe_cache"], cfg.end_pos, cfg.softmax_scale, out)
     if from_latent:
         def step():
             binding.expand_kv(lat, w, x["wkv_b"], H, Dn, Dv, 1e-6, k, v, workspace=ws)
-            binding.naive_attn(x["q_nope"], x["q_pe"], k4, v4, x["pe_cache"], cfg.end_pos, cfg.softmax_scale, out)
+            attend()
     else:
         binding.expand_kv(lat, w, x["wkv_b"], H, Dn, Dv, 1e-6, k, v, workspace=ws)  # the earlier positions
         c_new = torch.randn((B, S, C), generator=g, device="cuda").to(torch.bfloat16)
@@ -305,7 +306,7 @@ def time_naive_route(cfg, steps, warmup, torch, binding, seed=3, from_latent=Fal
 
         def step():
             append()
-            binding.naive_attn(x["q_nope"], x["q_pe"], k4, v4, x["pe_cache"], cfg.end_pos, cfg.softmax_scale, out)
+            attend()
 
     def timed(mask):
         for _ in range(warmup):

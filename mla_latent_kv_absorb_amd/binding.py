@@ -474,34 +474,50 @@ def cache_append(c_kv_new, k_pe_new, rms_w, eps: float, end_pos: int, kv_cache, 
                                       _stream_handle(c_kv_new.device)))
 
 
+class NaiveAttnCall:
+    """One naive-route attention call (mla_naive_attn) with its arguments marshalled once, over
+    expanded keys and values: k_nope [H, Bmax, Tmax, Dn] and v [H, Bmax, Tmax, Dv] head-major,
+    pe_cache [Bmax, Tmax, R].  Every call of the object re-issues it on the stream current at
+    construction; the object keeps the tensors alive."""
+
+    def __init__(self, q_nope, q_pe, k_nope, v, pe_cache, end_pos: int, softmax_scale: float, out=None, *,
+                 path: str = "auto"):
+        import torch
+
+        lib = load()
+        if q_nope.dim() != 4 or q_pe.dim() != 4 or k_nope.dim() != 4 or v.dim() != 4 or pe_cache.dim() != 3:
+            raise ValueError("expected q_nope/q_pe [B,S,H,.], k_nope/v [H,Bmax,Tmax,.], pe_cache [Bmax,Tmax,R]")
+        B, S, H, Dn = q_nope.shape
+        R = q_pe.shape[-1]
+        Hk, Bmax, Tmax, Dk = k_nope.shape
+        Dv = v.shape[-1]
+        _shape(q_pe, (B, S, H, R), "q_pe")
+        if Hk != H or Dk != Dn or tuple(v.shape[:3]) != (H, Bmax, Tmax) or tuple(pe_cache.shape) != (Bmax, Tmax, R):
+            raise ValueError("k_nope / v / pe_cache shapes disagree with the query")
+        if out is not None:
+            _shape(out, (B, S, H, Dv), "out")
+        _require_device(q_nope, q_pe, k_nope, v, pe_cache)
+        if out is None:
+            out = torch.empty((B, S, H, Dv), dtype=q_nope.dtype, device=q_nope.device)
+        _require_device(q_nope, out)
+        shape = AttnShape(B, S, H, 0, R, Dn, Dv, Bmax, Tmax)
+        self.out = out
+        self._keep = (q_nope, q_pe, k_nope, v, pe_cache, out, shape)
+        self._fn = lib.mla_naive_attn
+        self._args = (q_nope.data_ptr(), q_pe.data_ptr(), k_nope.data_ptr(), v.data_ptr(), pe_cache.data_ptr(),
+                      end_pos, softmax_scale, out.data_ptr(), ctypes.byref(shape), _dtype_code(q_nope), PATHS[path],
+                      _stream_handle(q_nope.device))
+
+    def __call__(self):
+        _check(self._fn(*self._args))
+        return self.out
+
+
 def naive_attn(q_nope, q_pe, k_nope, v, pe_cache, end_pos: int, softmax_scale: float, out=None, *,
                path: str = "auto"):
-    """Naive-route attention over expanded keys and values (mla_naive_attn): k_nope [H, Bmax,
-    Tmax, Dn] and v [H, Bmax, Tmax, Dv] head-major, pe_cache [Bmax, Tmax, R]; returns out
-    [B, S, H, Dv]."""
-    import torch
-
-    lib = load()
-    if q_nope.dim() != 4 or q_pe.dim() != 4 or k_nope.dim() != 4 or v.dim() != 4 or pe_cache.dim() != 3:
-        raise ValueError("expected q_nope/q_pe [B,S,H,.], k_nope/v [H,Bmax,Tmax,.], pe_cache [Bmax,Tmax,R]")
-    B, S, H, Dn = q_nope.shape
-    R = q_pe.shape[-1]
-    Hk, Bmax, Tmax, Dk = k_nope.shape
-    Dv = v.shape[-1]
-    _shape(q_pe, (B, S, H, R), "q_pe")
-    if Hk != H or Dk != Dn or tuple(v.shape[:3]) != (H, Bmax, Tmax) or tuple(pe_cache.shape) != (Bmax, Tmax, R):
-        raise ValueError("k_nope / v / pe_cache shapes disagree with the query")
-    if out is not None:
-        _shape(out, (B, S, H, Dv), "out")
-    _require_device(q_nope, q_pe, k_nope, v, pe_cache)
-    if out is None:
-        out = torch.empty((B, S, H, Dv), dtype=q_nope.dtype, device=q_nope.device)
-    _require_device(q_nope, out)
-    shape = AttnShape(B, S, H, 0, R, Dn, Dv, Bmax, Tmax)
-    _check(lib.mla_naive_attn(q_nope.data_ptr(), q_pe.data_ptr(), k_nope.data_ptr(), v.data_ptr(), pe_cache.data_ptr(),
-                              end_pos, softmax_scale, out.data_ptr(), ctypes.byref(shape), _dtype_code(q_nope),
-                              PATHS[path], _stream_handle(q_nope.device)))
-    return out
+    """Naive-route attention over expanded keys and values (mla_naive_attn); see NaiveAttnCall.
+    Returns out [B, S, H, Dv]."""
+    return NaiveAttnCall(q_nope, q_pe, k_nope, v, pe_cache, end_pos, softmax_scale, out, path=path)()
 
 
 def expand_kv_workspace_size(n_tokens: int, n_heads: int, kv_lora_rank: int, qk_nope_head_dim: int,
