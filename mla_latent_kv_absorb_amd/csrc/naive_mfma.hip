@@ -89,22 +89,31 @@ naive_attn_kernel(NaiveArgs a) {
   const rsrc_t vres = make_rsrc(a.v + kv_row0 * kDv, uint32_t(a.Tmax) * (kDv * 2));
   const rsrc_t peres = make_rsrc(a.pe + int64_t(b) * a.Tmax * kR, uint32_t(a.Tmax) * (kR * 2));
   const uint32_t smem_lds = lds_addr(smem);
-  auto issue = [&](int j) __attribute__((always_inline)) {
+  // one of the five DMA instructions of tile j of this wave: parts 0 and 1 are k_nope rows
+  // 4 (2 wave + part) .. +3, parts 2 and 3 the same v rows, part 4 the pe rows 8 wave .. +7
+  auto issue_part = [&](int j, const int part) __attribute__((always_inline)) {
     const uint32_t st = smem_lds + uint32_t(j % kStages) * kStageBytes;
     const int t0 = j * kTile;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      // k_nope / v instruction 2 wave + i: tile rows 4 (2 wave + i) .. +3, lane -> row + l / 16, slot l % 16
+    if (part < 4) {
+      const int i = part & 1;
       const int row = 4 * (2 * wave + i) + (lane >> 4);
       const int t = min(t0 + row, wg_end - 1);
-      const uint32_t kchunk = uint32_t((lane & 15) ^ k_swz(row)), vchunk = uint32_t((lane & 15) ^ v_swz(row));
-      buf_load16_lds_at(kres, st + (2 * wave + i) * 1024, uint32_t(t) * (kDn * 2) + kchunk * 16, 0);
-      buf_load16_lds_at(vres, st + kVOff + (2 * wave + i) * 1024, uint32_t(t) * (kDv * 2) + vchunk * 16, 0);
+      if (part < 2) {
+        const uint32_t kchunk = uint32_t((lane & 15) ^ k_swz(row));
+        buf_load16_lds_at(kres, st + (2 * wave + i) * 1024, uint32_t(t) * (kDn * 2) + kchunk * 16, 0);
+      } else {
+        const uint32_t vchunk = uint32_t((lane & 15) ^ v_swz(row));
+        buf_load16_lds_at(vres, st + kVOff + (2 * wave + i) * 1024, uint32_t(t) * (kDv * 2) + vchunk * 16, 0);
+      }
+    } else {
+      const int prow = 8 * wave + (lane >> 3);
+      const int tp = min(t0 + prow, wg_end - 1);
+      buf_load16_lds_at(peres, st + kPeOff + wave * 1024, uint32_t(tp) * (kR * 2) + uint32_t((lane & 7) ^ pe_swz(prow)) * 16, 0);
     }
-    // pe instruction wave: rows 8 wave .. +7, lane -> row + l / 8, slot l % 8
-    const int prow = 8 * wave + (lane >> 3);
-    const int tp = min(t0 + prow, wg_end - 1);
-    buf_load16_lds_at(peres, st + kPeOff + wave * 1024, uint32_t(tp) * (kR * 2) + uint32_t((lane & 7) ^ pe_swz(prow)) * 16, 0);
+  };
+  auto issue = [&](int j) __attribute__((always_inline)) {
+#pragma unroll
+    for (int part = 0; part < 5; ++part) issue_part(j, part);
   };
 
   // ---- prologue: tiles 0 and 1, the query as score operand (row s: 16 bytes at 16 ks + 8 g), a
@@ -125,10 +134,6 @@ naive_attn_kernel(NaiveArgs a) {
   }
   issue(1);
   wait_vmcnt<0>();
-  if (npairs > 1) {
-    issue(2);
-    issue(3);
-  }
 
   // score operand reads: tile row rho(l32), chunk 2 ks + g (k_nope) / 2 (ks - 8) + g (pe)
   const int arow = rho(l32);
@@ -162,10 +167,6 @@ naive_attn_kernel(NaiveArgs a) {
     if (p > 0) wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();  // every wave's part of pair p is in; every wave is done with pair p - 1
     compiler_fence();
-    if (p > 0 && p + 1 < npairs) {  // pair p + 1 into pair p - 1's stages (pair 1: issued ahead of the loop)
-      issue(2 * p + 2);
-      issue(2 * p + 3);
-    }
 
     // scores S^T[position][row] of the pair's two tiles
     f32x16 sacc[2];
@@ -178,8 +179,13 @@ naive_attn_kernel(NaiveArgs a) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) fr[8 + ks] = lds_read16(st, p_off[ks]);
       sacc[u] = f32x16{};
+      // pair p + 1 goes into pair p - 1's stages, one DMA instruction after every second score
+      // MFMA (unconditionally: past the last pair it re-reads clamped rows into finished stages)
 #pragma unroll
-      for (int ks = 0; ks < 12; ++ks) sacc[u] = mfma32(fr[ks], qf[ks], sacc[u]);
+      for (int ks = 0; ks < 12; ++ks) {
+        sacc[u] = mfma32(fr[ks], qf[ks], sacc[u]);
+        if ((ks & 1) && ks < 10) issue_part(2 * p + 2 + u, ks >> 1);
+      }
     }
     const int t0 = 2 * p * kTile;
     if (t0 + 2 * kTile > wg_full) {  // wavefront-uniform: positions past some row's last visible one
