@@ -522,8 +522,9 @@ int32_t mla_expand_kv_append(const void *c_kv_new, const void *k_pe_new, const v
   if ((k_pe_new == nullptr) != (pe_cache == nullptr))
     return fail(MLA_ERR_NULL, "k_pe_new and pe_cache must both be given or both be NULL");
   const int64_t T = s.batch * s.seqlen_q, rows = s.cache_batch * s.cache_len;
-  if (T > (int64_t(1) << 31) || rows > (int64_t(1) << 40))
-    return fail(MLA_ERR_SHAPE, "batch * seqlen_q or cache_batch * cache_len is too large");
+  if (T > (int64_t(1) << 31) || rows > (int64_t(1) << 40) ||
+      double(s.n_heads) * double(rows) * double(std::max(s.qk_nope_head_dim, s.v_head_dim)) > 0x1p56)
+    return fail(MLA_ERR_SHAPE, "batch * seqlen_q or the caches' element count is too large");
   mla::ExpandCall e;
   bool use_mfma = false;
   // the checks of mla_expand_kv for the B * S new tokens (path chosen below, after placement)

@@ -215,6 +215,9 @@ def test_expand_append_argument_errors(lib):
     assert call_expand_append(lib, s, path=mfma, dtype=B.MLA_DTYPE_F32) == B.MLA_ERR_UNSUPPORTED
     big = shape(seqlen_q=512, cache_batch=2049, cache_len=4096)
     assert call_expand_append(lib, big, path=mfma) == B.MLA_ERR_UNSUPPORTED and "rows" in B.last_error()
+    # caches whose element count would overflow the size arithmetic are refused outright
+    huge = shape(seqlen_q=512, n_heads=1 << 20, cache_batch=1 << 20, cache_len=1 << 20)
+    assert call_expand_append(lib, huge) == B.MLA_ERR_SHAPE
 
 
 def call_ragged(lib, s, lens, max_len=4096, ws=P[7], ws_bytes=1 << 40, out=None):
