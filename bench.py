@@ -1,6 +1,6 @@
 """Benchmark: MLA absorb decode on one MI355X, DeepSeek-V3 decode shape.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dsv3_decode]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dsv3_decode] [--peaks]
                     [--no-extras] [--no-cpu-baseline] [--no-peaks] [--sustained-ms MS]
 
 A step is one absorb-attention decode call (query absorption through W_UK, split-KV attention
@@ -473,6 +473,8 @@ def main():
                          "passes, extras, probes or CPU baseline: the command rocprofv3 profiles")
     ap.add_argument("--sustained-ms", type=float, default=40.0,
                     help="length of the labelled sustained-load decode run (0 to skip)")
+    ap.add_argument("--peaks", action="store_true",
+                    help="only run the streaming-read, copy, matrix-core and LDS probes and print what they reach")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB, --steps times (reference "
                          "kernel of known size for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -494,6 +496,10 @@ def main():
         sys.exit(1)
     binding.load()  # fails loudly if the HIP library is not built
     torch.cuda.set_device(0)
+
+    if args.peaks:
+        print(json.dumps({"peaks_measured": measure_peaks(torch)}))
+        return
 
     if args.copy_calibration:
         n = args.copy_calibration * (1 << 20)
