@@ -1,0 +1,92 @@
+"""GPU parity over a seeded sweep of shapes: batch, query length, head count, cache length and
+capacity, split count and per-sequence lengths drawn at random (fixed seeds), each case through
+the matrix-core kernels and compared with the CPU oracle on every output element.
+
+The fixed-shape tests pin the workloads and the edge cases one by one; this sweep covers the
+combinations between them (row blocks that straddle sequences, odd causal chunks, split counts
+that do not divide the length, capacities larger than the lengths)."""
+import numpy as np
+import pytest
+import torch
+
+from mla_latent_kv_absorb_amd.workloads import ATTN_CONFIGS, EXPAND_CONFIGS, make_attn_inputs, make_expand_inputs, \
+    round_to_bf16
+from oracle import mla_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2  # bf16 storage, fp32 accumulation: max|gpu - ref| <= TOL * max|ref|
+
+
+def check(gpu, ref, what):
+    g = gpu.float().cpu().double().numpy()
+    assert np.isfinite(g).all(), f"{what}: non-finite outputs"
+    worst = float(np.abs(g - ref).max() / np.abs(ref).max())
+    print(f"{what}: max rel err {worst:.3e}", flush=True)
+    assert worst <= TOL, f"{what}: {worst:.3e} > {TOL}"
+
+
+def draw_attn_case(seed):
+    rng = np.random.default_rng(1000 + seed)
+    B = int(rng.integers(1, 6))
+    S = int(rng.choice([1, 1, 2, 3, 5, 9, 17]))
+    H = int(rng.choice([16, 32, 128]))
+    end_pos = int(rng.integers(S, 700))
+    cfg = ATTN_CONFIGS["dsv3_decode"].replace(batch=B, seqlen_q=S, n_heads=H, end_pos=end_pos,
+                                              cache_len=end_pos + int(rng.integers(0, 65)),
+                                              cache_batch=B + int(rng.integers(0, 3)))
+    splits = int(rng.choice([0, 0, 1, 2, 3, 5, 7, 12]))
+    lens = [int(n) for n in rng.integers(S, end_pos + 1, size=B)] if rng.random() < 0.3 else None
+    return cfg, splits, lens
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_attention_sweep(gpu_lib, seed):
+    cfg, splits, lens = draw_attn_case(seed)
+    print(f"sweep {seed}: B={cfg.batch} S={cfg.seqlen_q} H={cfg.n_heads} end_pos={cfg.end_pos} "
+          f"Tmax={cfg.cache_len} Bmax={cfg.cache_batch} splits={splits} lens={lens}", flush=True)
+    x = make_attn_inputs(cfg, seed=2000 + seed)
+    t = {k: torch.from_numpy(v).to("cuda").to(torch.bfloat16) for k, v in x.items()}
+    out = torch.full((cfg.batch, cfg.seqlen_q, cfg.n_heads, cfg.v_head_dim), float("nan"), dtype=torch.bfloat16,
+                     device="cuda")
+    seq_lens = None if lens is None else torch.tensor(lens, dtype=torch.int32, device="cuda")
+    gpu_lib.absorb_attn(t["q_nope"], t["q_pe"], t["kv_cache"], t["pe_cache"], t["wkv_b"], cfg.end_pos,
+                        cfg.softmax_scale, out, num_splits=splits, path="mfma", seq_lens=seq_lens)
+    torch.cuda.synchronize()
+    if lens is None:
+        ref = O.absorb_attention(x["q_nope"], x["q_pe"], x["kv_cache"], x["pe_cache"], x["wkv_b"], cfg.end_pos,
+                                 cfg.softmax_scale, cfg.v_head_dim)
+    else:
+        ref = O.absorb_attention_ragged(x["q_nope"], x["q_pe"], x["kv_cache"], x["pe_cache"], x["wkv_b"], lens,
+                                        cfg.softmax_scale, cfg.v_head_dim)
+    check(out, ref, f"sweep {seed}")
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_expansion_append_sweep(gpu_lib, seed):
+    """The naive path's append at random batch, chunk length, position and capacity: the rows
+    match the oracle's expansion of the same tokens, and every other cache row keeps its bits."""
+    rng = np.random.default_rng(3000 + seed)
+    B, S = int(rng.integers(1, 5)), int(rng.choice([1, 2, 3, 7, 31, 33, 100, 257]))
+    H = int(rng.choice([4, 8, 16]))
+    end_pos = S + int(rng.integers(0, 200))
+    Bmax, Tmax = B + int(rng.integers(0, 3)), end_pos + int(rng.integers(0, 40))
+    print(f"append sweep {seed}: B={B} S={S} H={H} end_pos={end_pos} Bmax={Bmax} Tmax={Tmax}", flush=True)
+    cfg = EXPAND_CONFIGS["dsv3_expand"].replace(n_tokens=B * S, n_heads=H)
+    x = make_expand_inputs(cfg, seed=4000 + seed)
+    kp = round_to_bf16(rng.normal(size=(B, S, 64)).astype(np.float32))
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to("cuda").to(torch.bfloat16)
+    k0 = dev(rng.normal(size=(H, Bmax, Tmax, 128)))
+    v0 = dev(rng.normal(size=(H, Bmax, Tmax, 128)))
+    p0 = dev(rng.normal(size=(Bmax, Tmax, 64)))
+    kc, vc, pc = k0.clone(), v0.clone(), p0.clone()
+    gpu_lib.expand_kv_append(dev(x["c_kv"].reshape(B, S, -1)), dev(kp), dev(x["rms_w"]), dev(x["wkv_b"]), cfg.eps,
+                             end_pos, kc, vc, pc, path="mfma")
+    torch.cuda.synchronize()
+    new = torch.zeros((Bmax, Tmax), dtype=torch.bool, device="cuda")
+    new[:B, end_pos - S:end_pos] = True
+    assert torch.equal(kc[:, ~new], k0[:, ~new]) and torch.equal(vc[:, ~new], v0[:, ~new]), "untouched rows"
+    assert torch.equal(pc[~new], p0[~new]) and torch.equal(pc[new], dev(kp.reshape(-1, 64))), "rope rows"
+    kr, vr = O.expand_kv(x["c_kv"], x["rms_w"], x["wkv_b"], H, 128, 128, cfg.eps)
+    check(kc[:, new], kr, f"append sweep {seed} K rows")
+    check(vc[:, new], vr, f"append sweep {seed} V rows")
