@@ -1,6 +1,7 @@
 """GPU parity over a seeded sweep of shapes: batch, query length, head count, cache length and
-capacity, split count and per-sequence lengths drawn at random (fixed seeds), each case through
-the matrix-core kernels and compared with the CPU oracle on every output element.
+capacity, split count and per-sequence lengths drawn at random (fixed seeds), for contiguous
+caches, page pools, index lists and the naive path's append, each case through the matrix-core
+kernels and compared with the CPU oracle on every output element.
 
 The fixed-shape tests pin the workloads and the edge cases one by one; this sweep covers the
 combinations between them (row blocks that straddle sequences, odd causal chunks, split counts
@@ -90,3 +91,59 @@ def test_expansion_append_sweep(gpu_lib, seed):
     kr, vr = O.expand_kv(x["c_kv"], x["rms_w"], x["wkv_b"], H, 128, 128, cfg.eps)
     check(kc[:, new], kr, f"append sweep {seed} K rows")
     check(vc[:, new], vr, f"append sweep {seed} V rows")
+
+
+def dev_inputs(x):
+    return {k: torch.from_numpy(v).to("cuda").to(torch.bfloat16) for k, v in x.items()}
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_paged_sweep(gpu_lib, seed):
+    """Page pools in random order at random page sizes, lengths and split counts."""
+    from test_parity import run_attn_paged, to_pages
+
+    rng = np.random.default_rng(5000 + seed)
+    B = int(rng.integers(1, 5))
+    S = int(rng.choice([1, 1, 2, 4]))
+    H = int(rng.choice([16, 128]))
+    page_size = int(rng.choice([32, 64, 128, 256]))
+    lens = [int(n) for n in rng.integers(S, int(rng.integers(S, 600)) + 1, size=B)]
+    bound = max(lens)  # the lengths' bound; the pools hold up to (pages per row) x page_size positions
+    splits = int(rng.choice([0, 0, 1, 3, 6]))
+    cfg = ATTN_CONFIGS["dsv3_decode"].replace(batch=B, seqlen_q=S, n_heads=H, end_pos=bound, cache_len=bound,
+                                              cache_batch=B)
+    print(f"paged sweep {seed}: B={B} S={S} H={H} page={page_size} lens={lens} splits={splits}", flush=True)
+    x = make_attn_inputs(cfg, seed=6000 + seed)
+    kvp, table = to_pages(x["kv_cache"], lens, page_size, 2, 7000 + seed)
+    pep, _ = to_pages(x["pe_cache"], lens, page_size, 2, 7000 + seed)
+    dev = lambda a: torch.from_numpy(a).to("cuda").to(torch.bfloat16)
+    out = run_attn_paged(gpu_lib, cfg, dev_inputs(x), dev(kvp), dev(pep), torch.from_numpy(table).to("cuda"), bound,
+                         lens=lens, path="mfma", splits=splits)
+    ref = O.absorb_attention_paged(x["q_nope"], x["q_pe"], kvp, pep, x["wkv_b"], table, lens, page_size,
+                                   cfg.softmax_scale, cfg.v_head_dim)
+    check(out, ref, f"paged sweep {seed}")
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_sparse_sweep(gpu_lib, seed):
+    """Index lists (with padding, repeats and entries past the visible positions) at random list
+    lengths, batch sizes and split counts."""
+    from test_parity import make_lists, run_attn_sparse
+
+    rng = np.random.default_rng(8000 + seed)
+    B = int(rng.integers(1, 5))
+    S = int(rng.choice([1, 1, 2, 3]))
+    H = 128 if S > 1 else int(rng.choice([16, 128]))
+    end_pos = int(rng.integers(S + 1, 600))
+    lens = [int(n) for n in rng.integers(S, end_pos + 1, size=B)]
+    topk = int(rng.choice([1, 17, 64, 200, 513]))
+    splits = int(rng.choice([0, 0, 1, 2, 5]))
+    cfg = ATTN_CONFIGS["dsv3_decode"].replace(batch=B, seqlen_q=S, n_heads=H, end_pos=end_pos, cache_len=end_pos + 8,
+                                              cache_batch=B)
+    print(f"sparse sweep {seed}: B={B} S={S} H={H} topk={topk} lens={lens} splits={splits}", flush=True)
+    x = make_attn_inputs(cfg, seed=9000 + seed)
+    idx = make_lists(cfg, lens, topk, 9500 + seed)
+    out = run_attn_sparse(gpu_lib, cfg, dev_inputs(x), idx, lens, path="mfma", splits=splits)
+    ref = O.absorb_attention_sparse(x["q_nope"], x["q_pe"], x["kv_cache"], x["pe_cache"], x["wkv_b"], idx, lens,
+                                    cfg.softmax_scale, cfg.v_head_dim)
+    check(out, ref, f"sparse sweep {seed}")
