@@ -147,3 +147,34 @@ def test_sparse_sweep(gpu_lib, seed):
     ref = O.absorb_attention_sparse(x["q_nope"], x["q_pe"], x["kv_cache"], x["pe_cache"], x["wkv_b"], idx, lens,
                                     cfg.softmax_scale, cfg.v_head_dim)
     check(out, ref, f"sparse sweep {seed}")
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_plain_fp32_sweep(gpu_lib, seed):
+    """The plain kernels (fp32, any head shape) at random widths, batch, query length, cache
+    length and split count, against the oracle at the fp32 tolerance."""
+    rng = np.random.default_rng(10000 + seed)
+    B, S = int(rng.integers(1, 4)), int(rng.choice([1, 1, 2, 5]))
+    H = int(rng.integers(1, 9))
+    C, R = int(rng.choice([16, 32, 64, 96])), int(rng.choice([4, 8, 16]))
+    Dn, Dv = int(rng.choice([8, 16, 32])), int(rng.choice([8, 16, 32]))
+    end_pos = int(rng.integers(S, 300))
+    splits = int(rng.choice([0, 1, 3, 8]))
+    cfg = ATTN_CONFIGS["tiny_f32"].replace(batch=B, seqlen_q=S, n_heads=H, kv_lora_rank=C, qk_rope_head_dim=R,
+                                           qk_nope_head_dim=Dn, v_head_dim=Dv, end_pos=end_pos,
+                                           cache_len=end_pos + int(rng.integers(0, 20)), cache_batch=B + 1,
+                                           wkv_b_var=1.0 / C)
+    print(f"plain sweep {seed}: B={B} S={S} H={H} C={C} R={R} Dn={Dn} Dv={Dv} end_pos={end_pos} splits={splits}",
+          flush=True)
+    x = make_attn_inputs(cfg, seed=11000 + seed)
+    t = {k: torch.from_numpy(v).to("cuda") for k, v in x.items()}
+    out = torch.full((B, S, H, Dv), float("nan"), dtype=torch.float32, device="cuda")
+    gpu_lib.absorb_attn(t["q_nope"], t["q_pe"], t["kv_cache"], t["pe_cache"], t["wkv_b"], end_pos, cfg.softmax_scale,
+                        out, num_splits=splits, path="plain")
+    torch.cuda.synchronize()
+    ref = O.absorb_attention(x["q_nope"], x["q_pe"], x["kv_cache"], x["pe_cache"], x["wkv_b"], end_pos,
+                             cfg.softmax_scale, Dv)
+    g = out.cpu().double().numpy()
+    worst = float(np.abs(g - ref).max() / np.abs(ref).max())
+    print(f"plain sweep {seed}: max rel err {worst:.3e}", flush=True)
+    assert np.isfinite(g).all() and worst <= 1e-5, f"plain sweep {seed}: {worst:.3e}"
