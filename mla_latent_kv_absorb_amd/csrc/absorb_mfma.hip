@@ -692,7 +692,8 @@ attn_kernel(AttnArgs a) {
   for (int r = 0; r < rows_here; ++r) {
     const u32x4 v = lds_read16(stage, uint32_t(r) * (kC * 2) + uint32_t((lane & ~15) | ((lane & 15) ^ (r & 15))) * 16);
     const int64_t idx = (int64_t(b) * a.SH + first_row + wave * 32 + r) * a.splits + split;
-    *reinterpret_cast<u32x4 *>(a.part_o + idx * kC + lane * 8) = v;
+    // written through: the combine reads the rows from the XCD of their head, not this one
+    buf_store16_sys(make_rsrc(a.part_o + idx * kC, kC * 2), v, uint32_t(lane) * 16, 0);
   }
 }
 

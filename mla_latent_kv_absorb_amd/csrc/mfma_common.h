@@ -106,6 +106,12 @@ __device__ __forceinline__ void buf_store8(rsrc_t r, const u32x2 &v, uint32_t vo
 __device__ __forceinline__ void buf_store16_nt(rsrc_t r, const u32x4 &v, uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, soff, 2);
 }
+// A store with the system-scope cache policy (sc0 and sc1 set): the line is written through to
+// memory rather than left dirty in this XCD's L2.  For rows that a later kernel reads from
+// other XCDs, which cannot see this L2 anyway.
+__device__ __forceinline__ void buf_store16_sys(rsrc_t r, const u32x4 &v, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, soff, 17);
+}
 // 16 bytes per lane from a buffer straight into LDS: lane l's bytes land at lds_base + 16 * l
 // (lds_base is wavefront-uniform and goes through M0).
 //
