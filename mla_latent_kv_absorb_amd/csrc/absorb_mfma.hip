@@ -200,7 +200,9 @@ constexpr int kPageRegs = 4;
 // share the same reference.
 constexpr float kRescale = 8.f;
 
-template <int kMode>
+// kStream: one row block covers every query row of a sequence (decode), so each cache row is read
+// by one workgroup only and its DMA carries the non-temporal hint
+template <int kMode, bool kStream>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 attn_kernel(AttnArgs a) {
   constexpr bool kPaged = kMode == kModePaged, kSparse = kMode == kModeSparse;
@@ -373,27 +375,31 @@ attn_kernel(AttnArgs a) {
       return TileSrc{kvres, peres, 0, wg_end - 1, 0, 0, 0};
     }
   };
+  auto dma = [&](rsrc_t r, uint32_t lds, uint32_t voff, uint32_t soff) __attribute__((always_inline)) {
+    if constexpr (kStream) buf_load16_lds_at_nt(r, lds, voff, soff);
+    else buf_load16_lds_at(r, lds, voff, soff);
+  };
   auto issue_part = [&](int j, int part, const TileSrc &src) __attribute__((always_inline)) {
     const uint32_t st = smem_lds + uint32_t(j % kStages) * kStageBytes;
     const int t0 = t_begin + j * kTile;
     if (kSparse && part < 8) {
       const int t = min(max(__builtin_amdgcn_readlane(src.cur, src.lo + wave * 8 + part), 0), end_pos - 1);
-      buf_load16_lds_at(src.kv, st + (wave * 8 + part) * (kC * 2),
+      dma(src.kv, st + (wave * 8 + part) * (kC * 2),
                         lane16 ^ uint32_t(kv_swz(8 * (wave & 1) + part) * 16), uint32_t(t) * uint32_t(a.kv_rb));
     } else if (kSparse) {
-      buf_load16_lds_at(src.pe, st + kKvTileBytes + wave * 8 * (kR * 2),
+      dma(src.pe, st + kKvTileBytes + wave * 8 * (kR * 2),
                         pe_voff + uint32_t(src.pidx) * uint32_t(a.pe_rb), 0);
     } else if (part < 8) {
       const int t = min(t0 + wave * 8 + part, src.tlast);  // wavefront-uniform
       // source chunk swz_chunk(lane, row) = lane ^ kv_swz(row), kv_swz(row) wavefront-uniform
-      buf_load16_lds_at(src.kv, st + (wave * 8 + part) * (kC * 2),
+      dma(src.kv, st + (wave * 8 + part) * (kC * 2),
                         lane16 ^ uint32_t(kv_swz(8 * (wave & 1) + part) * 16), uint32_t(t - src.tb) * uint32_t(a.kv_rb));
     } else {
       // rows from the tile's first one, or (a tile past the end) from the last needed one, so
       // that every offset is that of a row the workgroup may read
       const int tq = min(t0, src.tlast);
       const int tp = min(t0 + pe_row, src.tlast);
-      buf_load16_lds_at(src.pe, st + kKvTileBytes + wave * 8 * (kR * 2), pe_voff + uint32_t(tp - tq) * uint32_t(a.pe_rb),
+      dma(src.pe, st + kKvTileBytes + wave * 8 * (kR * 2), pe_voff + uint32_t(tp - tq) * uint32_t(a.pe_rb),
                         uint32_t(tq - src.tb) * uint32_t(a.pe_rb));
     }
   };
@@ -1236,16 +1242,23 @@ hipError_t mfma_absorb_attn(const AttnCall &c) {
   if (c.topk > 0) {
     aa.indices = c.indices;
     aa.topk = int32_t(c.topk);
-    err = launch_kernel(MLA_KERNEL_ATTN, attn_kernel<kModeSparse>, dim3(unsigned(nwg)), dim3(256), 0, c.stream, aa);
+    err = row_blocks == 1
+              ? launch_kernel(MLA_KERNEL_ATTN, attn_kernel<kModeSparse, true>, dim3(unsigned(nwg)), dim3(256), 0, c.stream, aa)
+              : launch_kernel(MLA_KERNEL_ATTN, attn_kernel<kModeSparse, false>, dim3(unsigned(nwg)), dim3(256), 0, c.stream, aa);
   } else if (c.page_size > 0) {
     aa.block_table = c.block_table;
     aa.log2_page = 0;
     while ((int64_t(1) << aa.log2_page) < c.page_size) ++aa.log2_page;
     aa.max_pages = int32_t(c.max_pages);
     aa.num_pages = int32_t(c.num_pages);
-    err = launch_kernel(MLA_KERNEL_ATTN, attn_kernel<kModePaged>, dim3(unsigned(nwg)), dim3(256), 0, c.stream, aa);
+    err = row_blocks == 1
+              ? launch_kernel(MLA_KERNEL_ATTN, attn_kernel<kModePaged, true>, dim3(unsigned(nwg)), dim3(256), 0, c.stream, aa)
+              : launch_kernel(MLA_KERNEL_ATTN, attn_kernel<kModePaged, false>, dim3(unsigned(nwg)), dim3(256), 0, c.stream, aa);
   } else {
-    err = launch_kernel(MLA_KERNEL_ATTN, attn_kernel<kModeContig>, dim3(unsigned(nwg)), dim3(256), 0, c.stream, aa);
+    // one row block: every cache row has a single reader
+    err = row_blocks == 1
+              ? launch_kernel(MLA_KERNEL_ATTN, attn_kernel<kModeContig, true>, dim3(unsigned(nwg)), dim3(256), 0, c.stream, aa)
+              : launch_kernel(MLA_KERNEL_ATTN, attn_kernel<kModeContig, false>, dim3(unsigned(nwg)), dim3(256), 0, c.stream, aa);
   }
   if (err != hipSuccess) return err;
 

@@ -133,6 +133,12 @@ __device__ __forceinline__ void buf_load16_lds_at(rsrc_t r, uint32_t lds_addr, u
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr);
   asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(r), "s"(soff), "{m0}"(m0) : "memory");
 }
+// The same with the non-temporal hint, for rows that no other workgroup reads: they stream
+// through instead of displacing what other workgroups and later kernels reuse from L2 and MALL.
+__device__ __forceinline__ void buf_load16_lds_at_nt(rsrc_t r, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr);
+  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen nt lds" ::"v"(voff), "s"(r), "s"(soff), "{m0}"(m0) : "memory");
+}
 // LDS byte address of a __shared__ object.
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return uint32_t(reinterpret_cast<uintptr_t>((const MLA_LDS void *)p));
