@@ -10,8 +10,10 @@
 //                        (512) and pe_cache (64) as one 576-deep contraction, online softmax,
 //                        probability-weighted sum over kv_cache in latent space.  The cache rows
 //                        come from contiguous caches, from page pools through a block table, or
-//                        from the positions a per-token index list names (three instances of one
-//                        template; only the row addressing and the mask differ)
+//                        from the positions a per-token index list names (one template; only the
+//                        row addressing and the mask differ).  Each source has a second instance
+//                        whose cache DMA carries the non-temporal hint, for launches with one row
+//                        block, where every cache row has a single reader
 //   3. combine_kernel    merge the split partials (running maximum, weights exp2(m_i - M)) and
 //                        project out through W_UV[h]
 // Rows are the B*S*H query rows in (b, s, h) order.  Every kv/pe row of a split is read from HBM
