@@ -659,6 +659,48 @@ def _as_copy(x, dtype):
     return np.array(x, dtype)
 
 
+_orig_naive = O.naive_attention
+_orig_naive_kv = O.naive_kv
+_orig_over_kv = O.attention_over_kv
+_orig_partial = O.attention_partial
+_orig_rows = O.absorb_attention_rows
+_orig_rms = O.rms_norm
+
+
+def _naive_forgets_scale(q_nope, q_pe, kv_cache, pe_cache, wkv_b, end_pos, softmax_scale, *a, **kw):
+    return _orig_naive(q_nope, q_pe, kv_cache, pe_cache, wkv_b, end_pos, 1.0, *a, **kw)
+
+
+def _absorb_scale_squared(q_nope, q_pe, kv_cache, pe_cache, wkv_b, end_pos, softmax_scale, *a, **kw):
+    return _orig_absorb(q_nope, q_pe, kv_cache, pe_cache, wkv_b, end_pos, softmax_scale * softmax_scale, *a, **kw)
+
+
+def _naive_kv_heads_reversed(*a, **kw):
+    k, v = _orig_naive_kv(*a, **kw)  # [B, T, H, D]
+    return k[:, :, ::-1], v[:, :, ::-1]
+
+
+def _over_kv_rope_of_next_sequence(q_nope, q_pe, k_nope, v, pe_cache, *a, **kw):
+    return _orig_over_kv(q_nope, q_pe, k_nope, v, np.roll(np.asarray(pe_cache), 1, axis=0), *a, **kw)
+
+
+def _over_kv_values_of_next_head(q_nope, q_pe, k_nope, v, *a, **kw):
+    return _orig_over_kv(q_nope, q_pe, k_nope, np.roll(np.asarray(v), 1, axis=0), *a, **kw)
+
+
+def _partial_forgets_rope(q_lat, q_pe, *a, **kw):
+    return _orig_partial(q_lat, np.zeros(np.shape(q_pe)), *a, **kw)
+
+
+def _rows_see_one_fewer(q_nope, q_pe, kv_cache, pe_cache, wkv_b, end_pos, *a, **kw):
+    # every sampled row evaluated one position short (its last visible position dropped)
+    return _orig_rows(q_nope, q_pe, kv_cache, pe_cache, wkv_b, end_pos - 1, *a, **kw)
+
+
+def _rms_forgets_weight(x, w, eps, dtype=np.float64):
+    return _orig_rms(x, np.ones(np.shape(w)), eps, dtype)
+
+
 MUTATIONS = {
     "swap_uk_uv": ("split_wkv_b", _swap_split),
     "mask_off_by_one": ("allowed_positions", _off_by_one_mask),
@@ -675,6 +717,14 @@ MUTATIONS = {
     "sparse_ignores_causal_bound": ("absorb_attention_sparse", _sparse_ignores_causal_bound),
     "sparse_drops_repeats": ("absorb_attention_sparse", _sparse_drops_repeats),
     "append_paged_next_page": ("cache_append_paged", _append_paged_next_page),
+    "naive_forgets_scale": ("naive_attention", _naive_forgets_scale),
+    "absorb_scale_squared": ("absorb_attention", _absorb_scale_squared),
+    "naive_kv_heads_reversed": ("naive_kv", _naive_kv_heads_reversed),
+    "over_kv_rope_of_next_sequence": ("attention_over_kv", _over_kv_rope_of_next_sequence),
+    "over_kv_values_of_next_head": ("attention_over_kv", _over_kv_values_of_next_head),
+    "partial_forgets_rope": ("attention_partial", _partial_forgets_rope),
+    "rows_see_one_fewer": ("absorb_attention_rows", _rows_see_one_fewer),
+    "rms_norm_forgets_weight": ("rms_norm", _rms_forgets_weight),
 }
 
 
