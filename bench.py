@@ -29,7 +29,9 @@ a longer back-to-back run, after the chip's power management has settled its clo
 decode batch with per-sequence lengths drawn uniformly from [256, 4096]) and skewed_decode (4 of
 its sequences at 4096 positions, 28 at 64), each also under the uniform split plan for
 comparison with the balanced one the library picks, paged_decode (the decode
-batch with its caches in pools of 64-position pages in random order), sparse_decode and
+batch with its caches in pools of 64-position pages in random order), decode_append (a serving
+decode step that first writes each sequence's new token into the caches: one fused
+mla_absorb_attn_append call against mla_cache_append followed by mla_absorb_attn), sparse_decode and
 sparse_long_decode (the decode and long-context batches with each token attending to 2048 random
 positions of its cache through an index list), chunk_prefill_naive (the same chunk through the
 naive path as the pages lay it out: full-width key and value caches, into which a step expands the
@@ -190,6 +192,63 @@ def time_attn(cfg, steps, warmup, sets, torch, binding, seed=1, timed_kernels=0b
     us = e0.elapsed_time(e1) * 1000.0 / steps
     progress(f"{cfg.name} lens={lens is not None} page={page_size} topk={topk} kernels={timed_kernels:#x}: {us:.2f} us/step")
     return us, enqueue, kt
+
+
+def time_append_attn(cfg, steps, warmup, sets, torch, binding, fused, seed=1):
+    """GPU us per serving decode step: each sequence's new token appended into the caches (its
+    RMS-normalised latent and its rope key at position end_pos - 1), then absorb attention over
+    [0, end_pos).  fused: one mla_absorb_attn_append call; else mla_cache_append followed by
+    mla_absorb_attn."""
+    import ctypes
+
+    inputs = [gpu_inputs(cfg, seed + 1000 * i, torch) for i in range(sets)]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed + 7)
+    news = [(torch.randn((cfg.batch, cfg.seqlen_q, cfg.kv_lora_rank), generator=g, device="cuda").to(torch.bfloat16),
+             torch.randn((cfg.batch, cfg.seqlen_q, cfg.qk_rope_head_dim), generator=g, device="cuda").to(torch.bfloat16))
+            for _ in range(sets)]
+    rms_w = (1.0 + 0.14 * torch.randn((cfg.kv_lora_rank,), generator=g, device="cuda")).to(torch.bfloat16)
+    out = torch.empty((cfg.batch, cfg.seqlen_q, cfg.n_heads, cfg.v_head_dim), dtype=torch.bfloat16, device="cuda")
+    shape = binding.attn_shape(inputs[0]["q_nope"], inputs[0]["q_pe"], inputs[0]["kv_cache"], inputs[0]["wkv_b"])
+    ws = torch.empty(binding.absorb_attn_workspace_size(shape, cfg.end_pos, binding.MLA_DTYPE_BF16), dtype=torch.uint8,
+                     device="cuda")
+    lib = binding.load()
+    steps_fn = []
+    for x, (c_new, kp_new) in zip(inputs, news):
+        if fused:
+            steps_fn.append(binding.AbsorbAttnCall(x["q_nope"], x["q_pe"], x["kv_cache"], x["pe_cache"], x["wkv_b"],
+                                                   cfg.end_pos, cfg.softmax_scale, out, workspace=ws,
+                                                   append=(c_new, kp_new, rms_w, 1e-6)))
+            continue
+        attn = binding.AbsorbAttnCall(x["q_nope"], x["q_pe"], x["kv_cache"], x["pe_cache"], x["wkv_b"], cfg.end_pos,
+                                      cfg.softmax_scale, out, workspace=ws)
+        ashape = binding.AttnShape(cfg.batch, cfg.seqlen_q, 1, cfg.kv_lora_rank, cfg.qk_rope_head_dim, 0, 0,
+                                   cfg.cache_batch, cfg.cache_len)
+        args = (c_new.data_ptr(), kp_new.data_ptr(), rms_w.data_ptr(), 1e-6, None, cfg.end_pos,
+                x["kv_cache"].data_ptr(), x["pe_cache"].data_ptr(), ctypes.byref(ashape), binding.MLA_DTYPE_BF16,
+                torch.cuda.current_stream().cuda_stream)
+
+        def two_calls(args=args, attn=attn, keep=ashape):
+            rc = lib.mla_cache_append(*args)
+            if rc != 0:
+                raise RuntimeError(binding.last_error())
+            attn()
+
+        steps_fn.append(two_calls)
+    for i in range(warmup):
+        steps_fn[i % sets]()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        steps_fn[(warmup + i) % sets]()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1000.0 / steps
+    del inputs, news, steps_fn
+    torch.cuda.empty_cache()
+    progress(f"{cfg.name} append+attend fused={fused}: {us:.2f} us/step")
+    return us
 
 
 def time_expand(cfg, steps, warmup, torch, binding, seed=4, sets=4, timed_kernels=0):
@@ -625,6 +684,11 @@ def main():
         _, _, k = time_attn(c, 30, 3, args.sets, torch, binding, seed=c.seed, timed_kernels=0b111, page_size=64)
         extras["paged_decode"] = {"us_per_step": round(u, 2), "gbps": round(w["bytes"] / (u * 1e-6) / 1e9, 1),
                                   "page_size": 64, "kernels_us": {n: round(v["avg_us"], 2) for n, v in k.items()}}
+        # a serving decode step: the new token's cache rows, then attention; fused into one call
+        # (the rows written by the query-absorption kernel) against the two calls
+        uf = time_append_attn(c, 30, 3, args.sets, torch, binding, fused=True)
+        us2 = time_append_attn(c, 30, 3, args.sets, torch, binding, fused=False)
+        extras["decode_append"] = {"fused_us_per_step": round(uf, 2), "two_calls_us_per_step": round(us2, 2)}
         for name, base in (("sparse_decode", "dsv3_decode"), ("sparse_long_decode", "long_decode")):
             c = ATTN_CONFIGS[base]
             w = sparse_work(c, 2048)

@@ -331,6 +331,48 @@ int32_t mla_cache_append_paged(const void *c_kv_new, const void *k_pe_new, const
                                int32_t dtype, void *stream);
 
 /*
+ * Cache append fused into absorb attention: one call writes the new tokens' cache rows and then
+ * attends over the caches with those rows in place (page "Naive vs Absorb Attention
+ * Implementations in DeepSeek-V3", sections "Memory Layout and Cache Structure" and "Absorb Path
+ * Execution": the step writes the current tokens' latent and rope key into the caches at
+ * [start_pos, end_pos), then attends over [0, end_pos)).  The result, and every cache byte, is that
+ * of mla_cache_append followed by mla_absorb_attn (seq_lens NULL) or mla_absorb_attn_ragged
+ * (seq_lens given) on the same stream, bit for bit.  On the matrix-core path the rows are written
+ * by the query-absorption kernel, so the call launches one kernel fewer; the plain path makes the
+ * two calls.
+ *   c_kv_new, k_pe_new, rms_w, eps   as mla_cache_append (dense [B, S, C], [B, S, R], [C])
+ *   kv_cache, pe_cache               written, then read: the caches of mla_absorb_attn, with the
+ *                                    strides of options (the rows go where the attention reads)
+ *   seq_lens, end_pos                as mla_absorb_attn_ragged (seq_lens NULL: uniform end_pos)
+ *   everything else                  as mla_absorb_attn
+ * The workspace is that of mla_absorb_attn_workspace_size (seq_lens NULL) or
+ * mla_absorb_attn_ragged_workspace_size.  The caches must not overlap each other, the queries,
+ * wkv_b, out, the new rows, seq_lens or the workspace.  Returns MLA_OK or a negative MLA_ERR_*
+ * status (validation before any HIP call).
+ */
+int32_t mla_absorb_attn_append(const void *q_nope, const void *q_pe, const void *c_kv_new,
+                               const void *k_pe_new, const void *rms_w, float eps, void *kv_cache,
+                               void *pe_cache, const void *wkv_b, const int32_t *seq_lens,
+                               int64_t end_pos, float softmax_scale, void *out,
+                               const mla_attn_shape *shape, int32_t dtype,
+                               const mla_attn_options *options, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+/*
+ * The same over page pools: mla_cache_append_paged followed by mla_absorb_attn_paged, bit for
+ * bit, in one call (arguments as those two; workspace from
+ * mla_absorb_attn_paged_workspace_size).
+ */
+int32_t mla_absorb_attn_paged_append(const void *q_nope, const void *q_pe, const void *c_kv_new,
+                                     const void *k_pe_new, const void *rms_w, float eps,
+                                     void *kv_pages, void *pe_pages, const void *wkv_b,
+                                     const int32_t *block_table, const int32_t *seq_lens,
+                                     int64_t max_seq_len, float softmax_scale, void *out,
+                                     const mla_attn_shape *shape, const mla_paged_cache *paged,
+                                     int32_t dtype, const mla_attn_options *options,
+                                     void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Attention of the naive route ("Naive vs Absorb Attention Implementations in DeepSeek-V3",
  * section "Naive Path Execution") over keys and values that are already expanded, e.g. by
  * mla_expand_kv of the caches' Bmax*Tmax latent rows in (b, t) order:

@@ -30,6 +30,7 @@ MLA_DTYPE_BF16 = 1
 PATHS = {"auto": 0, "plain": 1, "mfma": 2}
 
 EXPORTED = ("mla_absorb_attn", "mla_absorb_attn_noalloc", "mla_absorb_attn_ragged", "mla_absorb_attn_paged", "mla_absorb_attn_sparse",
+            "mla_absorb_attn_append", "mla_absorb_attn_paged_append",
             "mla_absorb_attn_workspace_size", "mla_absorb_attn_ragged_workspace_size",
             "mla_absorb_attn_paged_workspace_size",
             "mla_absorb_attn_sparse_workspace_size", "mla_cache_append", "mla_cache_append_paged",
@@ -127,6 +128,14 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_expand_kv_append.argtypes = [vp, vp, vp, vp, ctypes.c_float, i64, vp, vp, vp, ctypes.POINTER(AttnShape),
                                          i32, i32, vp, sz, vp]
     lib.mla_expand_kv_append.restype = i32
+    lib.mla_absorb_attn_append.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, i64, ctypes.c_float,
+                                           vp, ctypes.POINTER(AttnShape), i32, ctypes.POINTER(AttnOptions), vp, sz, vp]
+    lib.mla_absorb_attn_append.restype = i32
+    lib.mla_absorb_attn_paged_append.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, vp, i64,
+                                                 ctypes.c_float, vp, ctypes.POINTER(AttnShape),
+                                                 ctypes.POINTER(PagedCache), i32, ctypes.POINTER(AttnOptions), vp, sz,
+                                                 vp]
+    lib.mla_absorb_attn_paged_append.restype = i32
     lib.mla_strerror.argtypes = [i32]
     lib.mla_strerror.restype = ctypes.c_char_p
     lib.mla_last_error.argtypes = []
@@ -308,13 +317,15 @@ class AbsorbAttnCall:
 
     def __init__(self, q_nope, q_pe, kv_cache, pe_cache, wkv_b, end_pos: int, softmax_scale: float, out=None, *,
                  num_splits: int = 0, path: str = "auto", workspace=None, seq_lens=None, block_table=None,
-                 indices=None):
+                 indices=None, append=None):
         """With seq_lens (an int32 tensor [B] on the same device), sequence b attends to positions
         [0, seq_lens[b]) and end_pos is the bound of the lengths (mla_absorb_attn_ragged).  With
         block_table (int32 [B, max_pages_per_seq]), kv_cache and pe_cache are page pools
         [num_pages, page_size, C / R] (mla_absorb_attn_paged; seq_lens optional).  With indices
         (int32 [B, S, topk]), each query token attends to the positions its list names
-        (mla_absorb_attn_sparse; seq_lens optional)."""
+        (mla_absorb_attn_sparse; seq_lens optional).  With append = (c_kv_new [B, S, C],
+        k_pe_new [B, S, R], rms_w [C], eps), every call first writes the new tokens' cache rows
+        and then attends (mla_absorb_attn_append / mla_absorb_attn_paged_append)."""
         import torch
 
         lib = load()
@@ -368,16 +379,37 @@ class AbsorbAttnCall:
             need = absorb_attn_workspace_size(shape, end_pos, dt, num_splits, path, sp)
         else:
             need = absorb_attn_paged_workspace_size(shape, end_pos, paged, dt, num_splits, path, sp)
+        if append is not None:
+            if indices is not None:
+                raise ValueError("a fused cache append with index lists is not supported")
+            c_kv_new, k_pe_new, rms_w, eps = append
+            _shape(c_kv_new, (shape.batch, shape.seqlen_q, shape.kv_lora_rank), "c_kv_new")
+            _shape(k_pe_new, (shape.batch, shape.seqlen_q, shape.qk_rope_head_dim), "k_pe_new")
+            _shape(rms_w, (shape.kv_lora_rank,), "rms_w")
+            _require_device(q_nope, c_kv_new, k_pe_new, rms_w, contiguous=False)
+            _require_device(c_kv_new, k_pe_new, rms_w)
         if workspace is None or workspace.numel() * workspace.element_size() < need:
             workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q_nope.device)
         self.out = out
         self._keep = (q_nope, q_pe, kv_cache, pe_cache, wkv_b, out, workspace, shape, opt, strides, seq_lens,
-                      block_table, paged, indices)
+                      block_table, paged, indices, append)
         tail = (softmax_scale, out.data_ptr(), ctypes.byref(shape), dt, ctypes.byref(opt), workspace.data_ptr(),
                 workspace.numel() * workspace.element_size(), _stream_handle(q_nope.device))
         head = (q_nope.data_ptr(), q_pe.data_ptr(), kv_cache.data_ptr(), pe_cache.data_ptr(), wkv_b.data_ptr())
         lens_ptr = None if seq_lens is None else seq_lens.data_ptr()
-        if indices is not None:
+        if append is not None:
+            new = (q_nope.data_ptr(), q_pe.data_ptr(), c_kv_new.data_ptr(), k_pe_new.data_ptr(), rms_w.data_ptr(),
+                   float(eps), kv_cache.data_ptr(), pe_cache.data_ptr(), wkv_b.data_ptr())
+            if paged is not None:
+                self._fn = lib.mla_absorb_attn_paged_append
+                self._args = new + (block_table.data_ptr(), lens_ptr, end_pos, softmax_scale, out.data_ptr(),
+                                    ctypes.byref(shape), ctypes.byref(paged), dt, ctypes.byref(opt),
+                                    workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                    _stream_handle(q_nope.device))
+            else:
+                self._fn = lib.mla_absorb_attn_append
+                self._args = new + (lens_ptr, end_pos) + tail
+        elif indices is not None:
             self._fn = lib.mla_absorb_attn_sparse
             self._args = head + (indices.data_ptr(), indices.shape[2], lens_ptr, end_pos) + tail
         elif paged is not None:
@@ -400,14 +432,15 @@ class AbsorbAttnCall:
 
 def absorb_attn(q_nope, q_pe, kv_cache, pe_cache, wkv_b, end_pos: int, softmax_scale: float, out=None, *,
                 num_splits: int = 0, path: str = "auto", workspace=None, seq_lens=None, block_table=None,
-                indices=None):
+                indices=None, append=None):
     """MLA attention in absorb form on torch GPU tensors; returns out [B, S, H, Dv].  With
     seq_lens, a ragged batch whose lengths are bounded by end_pos; with block_table, paged caches
     (kv_cache / pe_cache are the page pools); with indices [B, S, topk], attention over the
-    positions each token's list names."""
+    positions each token's list names; with append = (c_kv_new, k_pe_new, rms_w, eps), the new
+    tokens' cache rows are written first, in the same call."""
     return AbsorbAttnCall(q_nope, q_pe, kv_cache, pe_cache, wkv_b, end_pos, softmax_scale, out,
                           num_splits=num_splits, path=path, workspace=workspace, seq_lens=seq_lens,
-                          block_table=block_table, indices=indices)()
+                          block_table=block_table, indices=indices, append=append)()
 
 
 NOALLOC_SCRATCH_BYTES = 64 << 20  # MLA_NOALLOC_SCRATCH_BYTES

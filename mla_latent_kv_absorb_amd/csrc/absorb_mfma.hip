@@ -22,6 +22,7 @@
 #include <numeric>
 #include <type_traits>
 
+#include "append_row.h"
 #include "common.h"
 #include "launch.h"
 #include "mfma_common.h"
@@ -722,6 +723,7 @@ struct AbsorbQArgs {
   int32_t row_blocks_per_wg;
   float inv_S;             // 1 / S
   int32_t qn_rs, qp_rs;    // elements between consecutive query rows of q_nope and of q_pe
+  AppendCall app;          // fused cache append (kApp): its rows are written by this launch
 };
 
 // Byte offset of row (m, h)'s slot in the fragment buffer (add ks * 1024 + g * 16).
@@ -740,11 +742,22 @@ __device__ __forceinline__ int64_t frag_row_offset(int m, int h, const AbsorbQAr
 // rows in different 64-byte quarters.
 __device__ __forceinline__ int w_swz(int row) { return (row & 3) << 2; }
 
+// kApp: the launch also writes the rows of a fused cache append (a.app): an extra column of
+// workgroups (blockIdx.y == kC / 128) does only that, one wavefront per token, beside the
+// absorption; the attention kernel, launched after this one, reads the rows
+template <bool kApp>
 __global__ void __launch_bounds__(256) absorb_q_kernel(AbsorbQArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char wt[kDn * 128 * 2];  // 32 KB
   __shared__ __attribute__((aligned(16))) unsigned char xt[2][32 * kDn * 2];  // 2 x 8 KB
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
+  if (kApp && blockIdx.y == kC / 128) {
+    const int64_t ntok = a.app.B * a.app.S;
+    const int64_t stride = int64_t(gridDim.x) * gridDim.z * 4;
+    for (int64_t tok = (int64_t(blockIdx.z) * gridDim.x + blockIdx.x) * 4 + wave; tok < ntok; tok += stride)
+      append_token<uint16_t>(a.app, tok, lane);
+    return;
+  }
   const int l32 = lane & 31, g = lane >> 5;
   // Heads that share the fragment buffer's 128-byte lines (rows 4k .. 4k+3 of a 32-row group) run
   // on one XCD, so their partial-line stores merge in its L2.  Workgroups reach the XCDs
@@ -1205,12 +1218,14 @@ hipError_t mfma_absorb_attn(const AttnCall &c) {
 
   AbsorbQArgs qa{static_cast<const uint16_t *>(c.q_nope), static_cast<const uint16_t *>(c.q_pe),
                  static_cast<const uint16_t *>(c.wkv_b), q_frag, int32_t(c.H), M, int32_t(c.S), row_blocks, kQBlocksPerWG,
-                 1.f / float(c.S), int32_t(c.q_nope_rs), int32_t(c.q_pe_rs)};
+                 1.f / float(c.S), int32_t(c.q_nope_rs), int32_t(c.q_pe_rs), AppendCall{}};
+  if (c.append) qa.app = *c.append;
   const int nrb = (M + 31) / 32;
-  hipError_t err = launch_kernel(
-      MLA_KERNEL_ABSORB_Q, absorb_q_kernel,
-      dim3(unsigned(c.H), kC / 128, unsigned((nrb + qa.row_blocks_per_wg - 1) / qa.row_blocks_per_wg)), dim3(256), 0,
-      c.stream, qa);
+  const unsigned qz = unsigned((nrb + qa.row_blocks_per_wg - 1) / qa.row_blocks_per_wg);
+  hipError_t err = c.append ? launch_kernel(MLA_KERNEL_ABSORB_Q, absorb_q_kernel<true>, dim3(unsigned(c.H), kC / 128 + 1, qz),
+                                            dim3(256), 0, c.stream, qa)
+                            : launch_kernel(MLA_KERNEL_ABSORB_Q, absorb_q_kernel<false>, dim3(unsigned(c.H), kC / 128, qz),
+                                            dim3(256), 0, c.stream, qa);
   if (err != hipSuccess) return err;
 
   AttnArgs aa{};

@@ -39,6 +39,9 @@ struct AttnCall {
   void *out;
   void *ws;           // workspace (layout chosen by the path's workspace function)
   hipStream_t stream;
+  // cache append fused into the call (mla_absorb_attn_append), or null: its rows are written
+  // before the attention reads the caches
+  const struct AppendCall *append;
 };
 
 struct ExpandCall {
@@ -81,6 +84,9 @@ struct AppendCall {
   int32_t dtype;
   const void *c_kv_new, *k_pe_new, *rms_w;
   void *kv_cache, *pe_cache;  // [Bmax, Tmax, C / R], or page pools [num_pages, page_size, C / R]
+  // element strides of the caches: sequence (b) and position (t) of kv and pe; page pools use the
+  // position strides for rows within and across pages (dense: Tmax * C, C, Tmax * R, R)
+  int64_t kv_bs, kv_ps, pe_bs, pe_ps;
   // paged caches (page_size > 0): position p of sequence b is row p % page_size of page
   // block_table[b * max_pages + p / page_size] (clamped into [0, num_pages))
   const int32_t *block_table;

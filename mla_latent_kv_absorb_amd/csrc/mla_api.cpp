@@ -241,14 +241,21 @@ size_t mla_absorb_attn_sparse_workspace_size(const mla_attn_shape *shape, int64_
 
 namespace {
 
+// The new tokens of a fused cache append (mla_absorb_attn_append and its paged form).
+struct AppendIn {
+  const void *c_kv_new, *k_pe_new, *rms_w;
+  float eps;
+};
+
 // The body of mla_absorb_attn, mla_absorb_attn_ragged and mla_absorb_attn_paged (seq_lens null
-// for a uniform batch; paged and block_table null for contiguous caches).
+// for a uniform batch; paged and block_table null for contiguous caches), and with `app` of the
+// fused append entry points, whose rows are written into the caches before the attention reads them.
 int32_t absorb_attn_call(const void *q_nope, const void *q_pe, const void *kv_cache, const void *pe_cache,
                          const void *wkv_b, const int32_t *seq_lens, const int32_t *block_table,
                          const mla_paged_cache *paged, const int32_t *indices, int64_t topk, int64_t end_pos,
                          float softmax_scale, void *out, const mla_attn_shape *shape, int32_t dtype,
                          const mla_attn_options *options, void *workspace, size_t workspace_bytes, void *stream,
-                         size_t *dry_need = nullptr) {
+                         size_t *dry_need = nullptr, const AppendIn *app = nullptr) {
   mla::AttnCall c;
   bool use_mfma = false;
   int32_t rc = plan_attn(shape, end_pos, paged, indices ? topk : 0, seq_lens != nullptr, dtype, options, c, use_mfma);
@@ -281,6 +288,45 @@ int32_t absorb_attn_call(const void *q_nope, const void *q_pe, const void *kv_ca
     return fail(MLA_ERR_SHAPE, "out overlaps block_table");
   const size_t index_bytes = size_t(c.B * c.S * c.topk) * sizeof(int32_t);
   if (indices && overlaps(out, out_bytes, indices, index_bytes)) return fail(MLA_ERR_SHAPE, "out overlaps indices");
+  // fused append: the caches are written, so nothing else the call touches may overlap them
+  mla::AppendCall ac{};
+  const size_t toks = size_t(c.B * c.S);
+  const void *aptrs[] = {app ? app->c_kv_new : nullptr, app ? app->k_pe_new : nullptr, app ? app->rms_w : nullptr};
+  const char *anames[] = {"c_kv_new", "k_pe_new", "rms_w"};
+  const size_t abytes[] = {toks * size_t(c.C) * es, toks * size_t(c.R) * es, size_t(c.C) * es};
+  if (app) {
+    for (int i = 0; i < 3; ++i) {
+      if (!aptrs[i]) return fail(MLA_ERR_NULL, "%s is NULL", anames[i]);
+      if (misaligned(aptrs[i])) return fail(MLA_ERR_ALIGN, "%s is not 16-byte aligned", anames[i]);
+    }
+    if (!(app->eps >= 0.f) || app->eps > 1.f) return fail(MLA_ERR_SHAPE, "eps must be in [0, 1]");
+    if (overlaps(kv_cache, bytes_in[2], pe_cache, bytes_in[3])) return fail(MLA_ERR_SHAPE, "kv_cache overlaps pe_cache");
+    const void *wr[] = {kv_cache, pe_cache};
+    const size_t wr_bytes[] = {bytes_in[2], bytes_in[3]};
+    for (int k = 0; k < 2; ++k) {
+      for (int i : {0, 1, 4})
+        if (overlaps(wr[k], wr_bytes[k], ptrs[i], bytes_in[i]))
+          return fail(MLA_ERR_SHAPE, "%s overlaps %s", names[2 + k], names[i]);
+      for (int i = 0; i < 3; ++i)
+        if (overlaps(wr[k], wr_bytes[k], aptrs[i], abytes[i]))
+          return fail(MLA_ERR_SHAPE, "%s overlaps %s", names[2 + k], anames[i]);
+      if (seq_lens && overlaps(wr[k], wr_bytes[k], seq_lens, lens_bytes))
+        return fail(MLA_ERR_SHAPE, "%s overlaps seq_lens", names[2 + k]);
+      if (block_table && overlaps(wr[k], wr_bytes[k], block_table, table_bytes))
+        return fail(MLA_ERR_SHAPE, "%s overlaps block_table", names[2 + k]);
+    }
+    for (int i = 0; i < 3; ++i)
+      if (overlaps(out, out_bytes, aptrs[i], abytes[i])) return fail(MLA_ERR_SHAPE, "out overlaps %s", anames[i]);
+    ac.B = c.B; ac.S = c.S; ac.C = c.C; ac.R = c.R; ac.Tmax = c.Tmax;
+    ac.end_pos = end_pos; ac.seq_lens = seq_lens; ac.eps = app->eps; ac.dtype = dtype;
+    ac.c_kv_new = app->c_kv_new; ac.k_pe_new = app->k_pe_new; ac.rms_w = app->rms_w;
+    ac.kv_cache = const_cast<void *>(kv_cache); ac.pe_cache = const_cast<void *>(pe_cache);
+    ac.kv_bs = c.kv_bs; ac.kv_ps = c.kv_ps; ac.pe_bs = c.pe_bs; ac.pe_ps = c.pe_ps;
+    if (paged) {
+      ac.block_table = block_table;
+      ac.page_size = c.page_size; ac.num_pages = c.num_pages; ac.max_pages = c.max_pages;
+    }
+  }
   const size_t need = use_mfma ? mla::mfma_attn_workspace(c) : mla::plain_attn_workspace(c);
   if (dry_need) {  // every check but the workspace's; nothing is launched
     *dry_need = need;
@@ -301,6 +347,10 @@ int32_t absorb_attn_call(const void *q_nope, const void *q_pe, const void *kv_ca
       return fail(MLA_ERR_WORKSPACE, "workspace overlaps block_table");
     if (indices && overlaps(workspace, need, indices, index_bytes))
       return fail(MLA_ERR_WORKSPACE, "workspace overlaps indices");
+    if (app)
+      for (int i = 0; i < 3; ++i)
+        if (overlaps(workspace, need, aptrs[i], abytes[i]))
+          return fail(MLA_ERR_WORKSPACE, "workspace overlaps %s", anames[i]);
   }
   c.scale = softmax_scale;
   c.q_nope = q_nope; c.q_pe = q_pe; c.kv = kv_cache; c.pe = pe_cache; c.wkv_b = wkv_b;
@@ -309,7 +359,17 @@ int32_t absorb_attn_call(const void *q_nope, const void *q_pe, const void *kv_ca
   c.block_table = block_table;
   c.indices = indices;
   if (use_mfma && c.splits == 0) c.splits = 1;
-  hipError_t e = use_mfma ? mla::mfma_absorb_attn(c) : mla::plain_absorb_attn(c);
+  hipError_t e = hipSuccess;
+  if (app) {
+    ac.stream = c.stream;
+    if (use_mfma) {
+      c.append = &ac;  // written by the query-absorption kernel
+    } else {
+      e = mla::cache_append(ac);
+      if (e != hipSuccess) return fail(MLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    }
+  }
+  e = use_mfma ? mla::mfma_absorb_attn(c) : mla::plain_absorb_attn(c);
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return MLA_OK;
 }
@@ -366,6 +426,36 @@ int32_t mla_absorb_attn_paged(const void *q_nope, const void *q_pe, const void *
   if (reinterpret_cast<uintptr_t>(seq_lens) & 3u) return fail(MLA_ERR_ALIGN, "seq_lens is not 4-byte aligned");
   return absorb_attn_call(q_nope, q_pe, kv_pages, pe_pages, wkv_b, seq_lens, block_table, paged, nullptr, 0,
                           max_seq_len, softmax_scale, out, shape, dtype, options, workspace, workspace_bytes, stream);
+}
+
+int32_t mla_absorb_attn_append(const void *q_nope, const void *q_pe, const void *c_kv_new, const void *k_pe_new,
+                               const void *rms_w, float eps, void *kv_cache, void *pe_cache, const void *wkv_b,
+                               const int32_t *seq_lens, int64_t end_pos, float softmax_scale, void *out,
+                               const mla_attn_shape *shape, int32_t dtype, const mla_attn_options *options,
+                               void *workspace, size_t workspace_bytes, void *stream) {
+  clear_error();
+  if (reinterpret_cast<uintptr_t>(seq_lens) & 3u) return fail(MLA_ERR_ALIGN, "seq_lens is not 4-byte aligned");
+  const AppendIn app{c_kv_new, k_pe_new, rms_w, eps};
+  return absorb_attn_call(q_nope, q_pe, kv_cache, pe_cache, wkv_b, seq_lens, nullptr, nullptr, nullptr, 0, end_pos,
+                          softmax_scale, out, shape, dtype, options, workspace, workspace_bytes, stream, nullptr, &app);
+}
+
+int32_t mla_absorb_attn_paged_append(const void *q_nope, const void *q_pe, const void *c_kv_new,
+                                     const void *k_pe_new, const void *rms_w, float eps, void *kv_pages,
+                                     void *pe_pages, const void *wkv_b, const int32_t *block_table,
+                                     const int32_t *seq_lens, int64_t max_seq_len, float softmax_scale, void *out,
+                                     const mla_attn_shape *shape, const mla_paged_cache *paged, int32_t dtype,
+                                     const mla_attn_options *options, void *workspace, size_t workspace_bytes,
+                                     void *stream) {
+  clear_error();
+  if (!paged) return fail(MLA_ERR_NULL, "paged is NULL");
+  if (!block_table) return fail(MLA_ERR_NULL, "block_table is NULL");
+  if (reinterpret_cast<uintptr_t>(block_table) & 3u) return fail(MLA_ERR_ALIGN, "block_table is not 4-byte aligned");
+  if (reinterpret_cast<uintptr_t>(seq_lens) & 3u) return fail(MLA_ERR_ALIGN, "seq_lens is not 4-byte aligned");
+  const AppendIn app{c_kv_new, k_pe_new, rms_w, eps};
+  return absorb_attn_call(q_nope, q_pe, kv_pages, pe_pages, wkv_b, seq_lens, block_table, paged, nullptr, 0,
+                          max_seq_len, softmax_scale, out, shape, dtype, options, workspace, workspace_bytes, stream,
+                          nullptr, &app);
 }
 
 int32_t mla_absorb_attn_sparse(const void *q_nope, const void *q_pe, const void *kv_cache, const void *pe_cache,
@@ -635,6 +725,9 @@ int32_t cache_append_call(const void *c_kv_new, const void *k_pe_new, const void
   a.B = s.batch; a.S = s.seqlen_q; a.C = s.kv_lora_rank; a.R = s.qk_rope_head_dim; a.Tmax = s.cache_len;
   a.end_pos = end_pos; a.seq_lens = seq_lens; a.eps = eps; a.dtype = dtype;
   a.c_kv_new = c_kv_new; a.k_pe_new = k_pe_new; a.rms_w = rms_w; a.kv_cache = kv_cache; a.pe_cache = pe_cache;
+  a.kv_ps = s.kv_lora_rank; a.pe_ps = s.qk_rope_head_dim;
+  a.kv_bs = paged ? 0 : s.cache_len * a.kv_ps;
+  a.pe_bs = paged ? 0 : s.cache_len * a.pe_ps;
   a.stream = static_cast<hipStream_t>(stream);
   if (paged) {
     a.block_table = block_table;

@@ -265,6 +265,65 @@ def test_cache_append_argument_errors(lib):
     assert call_append(lib, s, ptrs=[P[3] + 1024, P[1], P[2], P[3], P[4]]) == B.MLA_ERR_SHAPE
 
 
+# new-token rows of the fused append (fake, aligned, apart from P)
+A = [0x7e0000000000 + i * 0x100000000 for i in range(3)]
+
+
+def call_attn_append(lib, s, end_pos=4096, ptrs=None, aptrs=None, eps=1e-6, lens=None, dtype=B.MLA_DTYPE_BF16,
+                     ws=P[7], ws_bytes=1 << 40):
+    p = list(P[:6]) if ptrs is None else ptrs
+    a = list(A) if aptrs is None else aptrs
+    return lib.mla_absorb_attn_append(p[0], p[1], a[0], a[1], a[2], eps, p[2], p[3], p[4], lens, end_pos, 0.07, p[5],
+                                      ctypes.byref(s), dtype, None, ws, ws_bytes, None)
+
+
+def test_attn_append_argument_errors(lib):
+    s = shape()
+    # the attention's own checks
+    assert call_attn_append(lib, s, end_pos=4097) == B.MLA_ERR_RANGE
+    assert call_attn_append(lib, shape(seqlen_q=9), end_pos=8) == B.MLA_ERR_RANGE
+    assert call_attn_append(lib, s, dtype=5) == B.MLA_ERR_DTYPE
+    assert call_attn_append(lib, s, ws=None) == B.MLA_ERR_WORKSPACE
+    # the append's
+    assert call_attn_append(lib, s, eps=-1.0) == B.MLA_ERR_SHAPE
+    assert call_attn_append(lib, s, eps=float("nan")) == B.MLA_ERR_SHAPE
+    for i in range(3):
+        a = list(A)
+        a[i] = None
+        assert call_attn_append(lib, s, aptrs=a) == B.MLA_ERR_NULL
+        a[i] = A[i] + 2
+        assert call_attn_append(lib, s, aptrs=a) == B.MLA_ERR_ALIGN
+    assert call_attn_append(lib, s, lens=P[6] + 2) == B.MLA_ERR_ALIGN
+    # the caches are written: nothing else the call reads may overlap them
+    assert call_attn_append(lib, s, ptrs=[P[2] + 4096, P[1], P[2], P[3], P[4], P[5]]) == B.MLA_ERR_SHAPE  # q_nope
+    assert call_attn_append(lib, s, ptrs=[P[0], P[1], P[2], P[3], P[3] + 1024, P[5]]) == B.MLA_ERR_SHAPE  # wkv_b
+    assert call_attn_append(lib, s, ptrs=[P[0], P[1], P[2], P[2] + 4096, P[4], P[5]]) == B.MLA_ERR_SHAPE  # pe in kv
+    assert call_attn_append(lib, s, aptrs=[P[2] + 1024, A[1], A[2]]) == B.MLA_ERR_SHAPE  # new rows in kv
+    assert call_attn_append(lib, s, aptrs=[A[0], A[1], P[3] + 1024]) == B.MLA_ERR_SHAPE  # rms_w in pe
+    assert call_attn_append(lib, s, lens=P[2] + 1024) == B.MLA_ERR_SHAPE  # seq_lens in kv
+    assert call_attn_append(lib, s, ptrs=[P[0], P[1], P[2], P[3], P[4], A[1]]) == B.MLA_ERR_SHAPE  # out on k_pe_new
+    assert call_attn_append(lib, s, ws=A[0]) == B.MLA_ERR_WORKSPACE  # workspace on c_kv_new
+
+
+def test_attn_paged_append_argument_errors(lib):
+    s = shape()
+    pg = B.PagedCache(64, 256, 64)
+
+    def call(p=None, a=None, bt=P[6], paged=pg, lens=None, eps=1e-6):
+        p = list(P[:6]) if p is None else p
+        a = list(A) if a is None else a
+        return lib.mla_absorb_attn_paged_append(p[0], p[1], a[0], a[1], a[2], eps, p[2], p[3], p[4], bt, lens, 4096,
+                                                0.07, p[5], ctypes.byref(s), None if paged is None else ctypes.byref(paged),
+                                                B.MLA_DTYPE_BF16, None, P[7], 1 << 40, None)
+
+    assert call(paged=None) == B.MLA_ERR_NULL
+    assert call(bt=None) == B.MLA_ERR_NULL
+    assert call(bt=P[6] + 2) == B.MLA_ERR_ALIGN
+    assert call(eps=2.0) == B.MLA_ERR_SHAPE
+    assert call(bt=P[2] + 4096) == B.MLA_ERR_SHAPE  # the table inside the kv pool, which is written
+    assert call(a=[A[0], P[3] + 64, A[2]]) == B.MLA_ERR_SHAPE  # new rope rows inside the pe pool
+
+
 def call_naive(lib, s, end_pos=4096, ptrs=None, scale=0.07, dtype=B.MLA_DTYPE_BF16, path=B.PATHS["auto"]):
     p = list(P[:6]) if ptrs is None else ptrs
     return lib.mla_naive_attn(p[0], p[1], p[2], p[3], p[4], end_pos, scale, p[5], ctypes.byref(s), dtype, path, None)

@@ -866,6 +866,122 @@ def test_append_then_attend_paged(gpu_lib):
     check(out, ref, TOL["bf16"], "paged append + attend")
 
 
+def _append_inputs(cfg, S, seed):
+    rng = np.random.default_rng(seed)
+    cast = (lambda a: a.astype(np.float32)) if cfg.dtype == "f32" else round_bf16
+    c_new = cast(rng.normal(size=(cfg.batch, S, cfg.kv_lora_rank)))
+    kp_new = cast(rng.normal(size=(cfg.batch, S, cfg.qk_rope_head_dim)))
+    w = cast(1.0 + 0.14 * rng.normal(size=cfg.kv_lora_rank))
+    return c_new, kp_new, w
+
+
+@pytest.mark.parametrize("dtype,S,ragged,strided,path", [
+    ("bf16", 1, False, False, "mfma"), ("bf16", 5, True, False, "mfma"), ("bf16", 1, True, True, "mfma"),
+    ("bf16", 130, False, False, "mfma"), ("bf16", 3, True, False, "plain"), ("f32", 3, False, False, "auto"),
+    ("f32", 2, True, True, "auto")])
+def test_fused_append_attend(gpu_lib, dtype, S, ragged, strided, path):
+    """mla_absorb_attn_append: the caches and the output equal, bit for bit, those of the cache
+    append followed by the attention call on copies of the same buffers, and the output matches the
+    oracle's append followed by absorb attention."""
+    if dtype == "bf16":
+        cfg = dsv3_small(batch=3, cache_batch=4, seqlen_q=S, end_pos=260, cache_len=300)
+    else:
+        cfg = ATTN_CONFIGS["tiny_f32"].replace(batch=3, cache_batch=4, seqlen_q=S, end_pos=100, cache_len=120)
+    x = make_attn_inputs(cfg)
+    c_new, kp_new, w = _append_inputs(cfg, S, 61 + S)
+    eps = 1e-6
+    lens = [cfg.end_pos, S + 20, 150 if dtype == "bf16" else 60] if ragged else None
+    t = to_dev(x, cfg)
+    tdt = tdtype(cfg)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(tdt)
+    seq = None if lens is None else torch.tensor(lens, dtype=torch.int32, device="cuda")
+
+    def caches():
+        if not strided:
+            return t["kv_cache"].clone(), t["pe_cache"].clone()
+        # rows padded to a wider stride: the appended rows must land where the attention reads
+        kvw = torch.full((cfg.cache_batch, cfg.cache_len, cfg.kv_lora_rank + 64), float("nan"), dtype=tdt, device="cuda")
+        pew = torch.full((cfg.cache_batch, cfg.cache_len, cfg.qk_rope_head_dim + 32), float("nan"), dtype=tdt,
+                         device="cuda")
+        kvw[..., :cfg.kv_lora_rank] = t["kv_cache"]
+        pew[..., :cfg.qk_rope_head_dim] = t["pe_cache"]
+        return kvw[..., :cfg.kv_lora_rank], pew[..., :cfg.qk_rope_head_dim]
+
+    out_f = torch.full((cfg.batch, S, cfg.n_heads, cfg.v_head_dim), float("nan"), dtype=tdt, device="cuda")
+    kv_f, pe_f = caches()
+    gpu_lib.absorb_attn(t["q_nope"], t["q_pe"], kv_f, pe_f, t["wkv_b"], cfg.end_pos, cfg.softmax_scale, out_f,
+                        path=path, seq_lens=seq, append=(dev(c_new), dev(kp_new), dev(w), eps))
+    out_2 = torch.full_like(out_f, float("nan"))
+    kv_2, pe_2 = caches()
+    if strided:  # the stand-alone append takes dense caches: append into dense copies, then copy in
+        kd, pd = kv_2.contiguous(), pe_2.contiguous()
+        gpu_lib.cache_append(dev(c_new), dev(kp_new), dev(w), eps, cfg.end_pos, kd, pd, seq_lens=seq)
+        kv_2.copy_(kd)
+        pe_2.copy_(pd)
+    else:
+        gpu_lib.cache_append(dev(c_new), dev(kp_new), dev(w), eps, cfg.end_pos, kv_2, pe_2, seq_lens=seq)
+    gpu_lib.absorb_attn(t["q_nope"], t["q_pe"], kv_2, pe_2, t["wkv_b"], cfg.end_pos, cfg.softmax_scale, out_2,
+                        path=path, seq_lens=seq)
+    torch.cuda.synchronize()
+    what = f"fused append {dtype} S={S} ragged={ragged} strided={strided} {path}"
+    assert torch.equal(kv_f.view(torch.int16 if dtype == "bf16" else torch.int32),
+                       kv_2.view(torch.int16 if dtype == "bf16" else torch.int32)), f"{what}: kv_cache differs"
+    assert torch.equal(pe_f.view(torch.int16 if dtype == "bf16" else torch.int32),
+                       pe_2.view(torch.int16 if dtype == "bf16" else torch.int32)), f"{what}: pe_cache differs"
+    assert torch.equal(out_f.view(torch.int16 if dtype == "bf16" else torch.int32),
+                       out_2.view(torch.int16 if dtype == "bf16" else torch.int32)), f"{what}: out differs"
+    # the oracle: append, the GPU's rounding of the written rows, then absorb attention
+    kv_o, pe_o = O.cache_append(c_new, kp_new, w, eps, x["kv_cache"], x["pe_cache"], end_pos=cfg.end_pos,
+                                seq_lens=lens)
+    kv_o = np.array(kv_o)
+    g_kv = kv_f.float().cpu().numpy()
+    for b in range(cfg.batch):
+        n = lens[b] if ragged else cfg.end_pos
+        check(g_kv[b, n - S:n].astype(np.float64), kv_o[b, n - S:n], TOL[dtype], f"{what}: latent rows of {b}")
+        kv_o[b, n - S:n] = g_kv[b, n - S:n]
+    if lens is None:
+        ref = O.absorb_attention(x["q_nope"], x["q_pe"], kv_o, pe_o, x["wkv_b"], cfg.end_pos, cfg.softmax_scale,
+                                 cfg.v_head_dim)
+    else:
+        ref = O.absorb_attention_ragged(x["q_nope"], x["q_pe"], kv_o, pe_o, x["wkv_b"], lens, cfg.softmax_scale,
+                                        cfg.v_head_dim)
+    check(out_f, ref, TOL[dtype], what)
+
+
+@pytest.mark.parametrize("S", [1, 4])
+def test_fused_append_attend_paged(gpu_lib, S):
+    """mla_absorb_attn_paged_append equals the paged append followed by paged attention, bit for bit."""
+    cfg = dsv3_small(batch=3, cache_batch=3, seqlen_q=S, end_pos=200, cache_len=256)
+    x = make_attn_inputs(cfg)
+    lens = [200, 77, 130]
+    kvp, table = to_pages(x["kv_cache"], lens, 64, 2, 53)
+    pep, _ = to_pages(x["pe_cache"], lens, 64, 2, 53)
+    c_new, kp_new, w = _append_inputs(cfg, S, 67 + S)
+    t = to_dev(x, cfg)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to("cuda").to(torch.bfloat16)
+    tb = torch.from_numpy(table).to("cuda")
+    seq = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    outs, pools = [], []
+    for fused in (True, False):
+        kv_d, pe_d = dev(kvp), dev(pep)
+        out = torch.full((cfg.batch, S, cfg.n_heads, cfg.v_head_dim), float("nan"), dtype=torch.bfloat16, device="cuda")
+        if fused:
+            gpu_lib.absorb_attn(t["q_nope"], t["q_pe"], kv_d, pe_d, t["wkv_b"], cfg.end_pos, cfg.softmax_scale, out,
+                                path="mfma", seq_lens=seq, block_table=tb, append=(dev(c_new), dev(kp_new), dev(w), 1e-6))
+        else:
+            gpu_lib.cache_append(dev(c_new), dev(kp_new), dev(w), 1e-6, cfg.end_pos, kv_d, pe_d, seq_lens=seq,
+                                 block_table=tb)
+            gpu_lib.absorb_attn(t["q_nope"], t["q_pe"], kv_d, pe_d, t["wkv_b"], cfg.end_pos, cfg.softmax_scale, out,
+                                path="mfma", seq_lens=seq, block_table=tb)
+        torch.cuda.synchronize()
+        outs.append(out)
+        pools.append((kv_d, pe_d))
+    for a, b in zip((outs[0],) + pools[0], (outs[1],) + pools[1]):
+        # NaN rows of the pools (pages no sequence owns) compare equal bit for bit
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), "fused paged append differs from the two calls"
+    assert torch.isfinite(outs[0]).all()
+
+
 # --------------------------------------------------------------------------------- naive route
 
 def head_major_kv(x, cfg):
