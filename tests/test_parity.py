@@ -948,38 +948,55 @@ def test_fused_append_attend(gpu_lib, dtype, S, ragged, strided, path):
     check(out_f, ref, TOL[dtype], what)
 
 
-@pytest.mark.parametrize("S", [1, 4])
-def test_fused_append_attend_paged(gpu_lib, S):
+@pytest.mark.parametrize("dtype,page_size,S,path", [("bf16", 64, 1, "mfma"), ("bf16", 64, 4, "mfma"),
+                                                    ("bf16", 32, 3, "plain"), ("f32", 16, 2, "auto")])
+def test_fused_append_attend_paged(gpu_lib, dtype, page_size, S, path):
     """mla_absorb_attn_paged_append equals the paged append followed by paged attention, bit for bit."""
-    cfg = dsv3_small(batch=3, cache_batch=3, seqlen_q=S, end_pos=200, cache_len=256)
+    if dtype == "bf16":
+        cfg = dsv3_small(batch=3, cache_batch=3, seqlen_q=S, end_pos=200, cache_len=256)
+        lens = [200, 77, 130]
+    else:
+        cfg = ATTN_CONFIGS["tiny_f32"].replace(batch=3, cache_batch=3, seqlen_q=S, end_pos=100, cache_len=112)
+        lens = [100, 37, 64]
     x = make_attn_inputs(cfg)
-    lens = [200, 77, 130]
-    kvp, table = to_pages(x["kv_cache"], lens, 64, 2, 53)
-    pep, _ = to_pages(x["pe_cache"], lens, 64, 2, 53)
+    kvp, table = to_pages(x["kv_cache"], lens, page_size, 2, 53)
+    pep, _ = to_pages(x["pe_cache"], lens, page_size, 2, 53)
     c_new, kp_new, w = _append_inputs(cfg, S, 67 + S)
     t = to_dev(x, cfg)
-    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to("cuda").to(torch.bfloat16)
+    tdt = tdtype(cfg)
+    bits = torch.int16 if dtype == "bf16" else torch.int32
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to("cuda").to(tdt)
     tb = torch.from_numpy(table).to("cuda")
     seq = torch.tensor(lens, dtype=torch.int32, device="cuda")
     outs, pools = [], []
     for fused in (True, False):
         kv_d, pe_d = dev(kvp), dev(pep)
-        out = torch.full((cfg.batch, S, cfg.n_heads, cfg.v_head_dim), float("nan"), dtype=torch.bfloat16, device="cuda")
+        out = torch.full((cfg.batch, S, cfg.n_heads, cfg.v_head_dim), float("nan"), dtype=tdt, device="cuda")
         if fused:
             gpu_lib.absorb_attn(t["q_nope"], t["q_pe"], kv_d, pe_d, t["wkv_b"], cfg.end_pos, cfg.softmax_scale, out,
-                                path="mfma", seq_lens=seq, block_table=tb, append=(dev(c_new), dev(kp_new), dev(w), 1e-6))
+                                path=path, seq_lens=seq, block_table=tb, append=(dev(c_new), dev(kp_new), dev(w), 1e-6))
         else:
             gpu_lib.cache_append(dev(c_new), dev(kp_new), dev(w), 1e-6, cfg.end_pos, kv_d, pe_d, seq_lens=seq,
                                  block_table=tb)
             gpu_lib.absorb_attn(t["q_nope"], t["q_pe"], kv_d, pe_d, t["wkv_b"], cfg.end_pos, cfg.softmax_scale, out,
-                                path="mfma", seq_lens=seq, block_table=tb)
+                                path=path, seq_lens=seq, block_table=tb)
         torch.cuda.synchronize()
         outs.append(out)
         pools.append((kv_d, pe_d))
     for a, b in zip((outs[0],) + pools[0], (outs[1],) + pools[1]):
         # NaN rows of the pools (pages no sequence owns) compare equal bit for bit
-        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), "fused paged append differs from the two calls"
-    assert torch.isfinite(outs[0]).all()
+        assert torch.equal(a.view(bits), b.view(bits)), f"fused paged append ({dtype}, {path}) differs from the two calls"
+    # and the oracle: paged append, the GPU's rounding of the written rows, paged attention
+    kva, pea = O.cache_append_paged(c_new, kp_new, w, 1e-6, kvp, pep, table, page_size, end_pos=cfg.end_pos,
+                                    seq_lens=lens)
+    g_kv = pools[0][0].float().cpu().numpy()
+    for b, n in enumerate(lens):
+        for p_ in range(n - S, n):
+            page, slot = table[b, p_ // page_size], p_ % page_size
+            kva[page, slot] = g_kv[page, slot]
+    ref = O.absorb_attention_paged(x["q_nope"], x["q_pe"], kva, pea, x["wkv_b"], table, lens, page_size,
+                                   cfg.softmax_scale, cfg.v_head_dim)
+    check(outs[0], ref, TOL[dtype], f"fused paged append {dtype} page={page_size} S={S} {path}")
 
 
 # --------------------------------------------------------------------------------- naive route
