@@ -387,23 +387,22 @@ attn_kernel(AttnArgs a) {
     const int t0 = t_begin + j * kTile;
     if (kSparse && part < 8) {
       const int t = min(max(__builtin_amdgcn_readlane(src.cur, src.lo + wave * 8 + part), 0), end_pos - 1);
-      dma(src.kv, st + (wave * 8 + part) * (kC * 2),
-                        lane16 ^ uint32_t(kv_swz(8 * (wave & 1) + part) * 16), uint32_t(t) * uint32_t(a.kv_rb));
+      dma(src.kv, st + (wave * 8 + part) * (kC * 2), lane16 ^ uint32_t(kv_swz(8 * (wave & 1) + part) * 16),
+          uint32_t(t) * uint32_t(a.kv_rb));
     } else if (kSparse) {
-      dma(src.pe, st + kKvTileBytes + wave * 8 * (kR * 2),
-                        pe_voff + uint32_t(src.pidx) * uint32_t(a.pe_rb), 0);
+      dma(src.pe, st + kKvTileBytes + wave * 8 * (kR * 2), pe_voff + uint32_t(src.pidx) * uint32_t(a.pe_rb), 0);
     } else if (part < 8) {
       const int t = min(t0 + wave * 8 + part, src.tlast);  // wavefront-uniform
       // source chunk swz_chunk(lane, row) = lane ^ kv_swz(row), kv_swz(row) wavefront-uniform
-      dma(src.kv, st + (wave * 8 + part) * (kC * 2),
-                        lane16 ^ uint32_t(kv_swz(8 * (wave & 1) + part) * 16), uint32_t(t - src.tb) * uint32_t(a.kv_rb));
+      dma(src.kv, st + (wave * 8 + part) * (kC * 2), lane16 ^ uint32_t(kv_swz(8 * (wave & 1) + part) * 16),
+          uint32_t(t - src.tb) * uint32_t(a.kv_rb));
     } else {
       // rows from the tile's first one, or (a tile past the end) from the last needed one, so
       // that every offset is that of a row the workgroup may read
       const int tq = min(t0, src.tlast);
       const int tp = min(t0 + pe_row, src.tlast);
       dma(src.pe, st + kKvTileBytes + wave * 8 * (kR * 2), pe_voff + uint32_t(tp - tq) * uint32_t(a.pe_rb),
-                        uint32_t(tq - src.tb) * uint32_t(a.pe_rb));
+          uint32_t(tq - src.tb) * uint32_t(a.pe_rb));
     }
   };
   auto issue = [&](int j) __attribute__((always_inline)) {
