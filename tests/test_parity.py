@@ -231,6 +231,39 @@ def test_full_size_attention(gpu_lib, name):
     check(out, oracle_attn_full(cfg, x), TOL["bf16"], f"{name} all outputs")
 
 
+def test_full_size_fused_append(gpu_lib):
+    """dsv3_decode at full size as a serving step: each sequence's new token appended in the same call
+    (mla_absorb_attn_append).  Caches and output equal the two calls bit for bit, the written rows
+    match the oracle's append, and every output element matches the oracle's attention over the
+    appended caches."""
+    cfg = ATTN_CONFIGS["dsv3_decode"]
+    print(f"full-size fused append: B={cfg.batch} T={cfg.end_pos}", flush=True)
+    x = make_attn_inputs(cfg)
+    c_new, kp_new, w = _append_inputs(cfg, 1, 71)
+    t = to_dev(x, cfg)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(torch.bfloat16)
+    res = []
+    for fused in (True, False):
+        kv, pe = t["kv_cache"].clone(), t["pe_cache"].clone()
+        out = torch.full((cfg.batch, 1, cfg.n_heads, cfg.v_head_dim), float("nan"), dtype=torch.bfloat16, device="cuda")
+        if fused:
+            gpu_lib.absorb_attn(t["q_nope"], t["q_pe"], kv, pe, t["wkv_b"], cfg.end_pos, cfg.softmax_scale, out,
+                                append=(dev(c_new), dev(kp_new), dev(w), 1e-6))
+        else:
+            gpu_lib.cache_append(dev(c_new), dev(kp_new), dev(w), 1e-6, cfg.end_pos, kv, pe)
+            gpu_lib.absorb_attn(t["q_nope"], t["q_pe"], kv, pe, t["wkv_b"], cfg.end_pos, cfg.softmax_scale, out)
+        torch.cuda.synchronize()
+        res.append((out, kv, pe))
+    for a, b in zip(res[0], res[1]):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), "fused call differs from the two calls"
+    kv_o, pe_o = O.cache_append(c_new, kp_new, w, 1e-6, x["kv_cache"], x["pe_cache"], end_pos=cfg.end_pos)
+    g_new = res[0][1][:, cfg.end_pos - 1].float().cpu().numpy()
+    check(g_new.astype(np.float64), kv_o[:, cfg.end_pos - 1], TOL["bf16"], "full-size fused append: written rows")
+    x2 = dict(x, kv_cache=np.array(kv_o), pe_cache=pe_o)
+    x2["kv_cache"][:, cfg.end_pos - 1] = g_new
+    check(res[0][0], oracle_attn_full(cfg, x2), TOL["bf16"], "full-size fused append: all outputs")
+
+
 # --------------------------------------------------------------------------------- ragged batches
 
 def run_attn_ragged(lib, cfg, t, lens, path="auto", splits=0):
