@@ -1,7 +1,7 @@
 """GPU parity over a seeded sweep of shapes: batch, query length, head count, cache length and
 capacity, split count and per-sequence lengths drawn at random (fixed seeds), for contiguous
-caches, page pools, index lists and the naive path's append, each case through the matrix-core
-kernels and compared with the CPU oracle on every output element.
+caches, page pools, index lists, the naive path's append and the fused append-and-attend call, each
+case through the matrix-core kernels and compared with the CPU oracle on every output element.
 
 The fixed-shape tests pin the workloads and the edge cases one by one; this sweep covers the
 combinations between them (row blocks that straddle sequences, odd causal chunks, split counts
@@ -178,3 +178,57 @@ def test_plain_fp32_sweep(gpu_lib, seed):
     worst = float(np.abs(g - ref).max() / np.abs(ref).max())
     print(f"plain sweep {seed}: max rel err {worst:.3e}", flush=True)
     assert np.isfinite(g).all() and worst <= 1e-5, f"plain sweep {seed}: {worst:.3e}"
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_fused_append_sweep(gpu_lib, seed):
+    """mla_absorb_attn_append over seeded shapes: caches and output bit-equal to the stand-alone
+    append followed by the attention call, and the output within tolerance of the oracle's append
+    followed by absorb attention."""
+    cfg, splits, lens = draw_attn_case(100 + seed)
+    rng = np.random.default_rng(3000 + seed)
+    S = cfg.seqlen_q
+    print(f"fused append sweep {seed}: B={cfg.batch} S={S} H={cfg.n_heads} end_pos={cfg.end_pos} "
+          f"Tmax={cfg.cache_len} Bmax={cfg.cache_batch} splits={splits} lens={lens}", flush=True)
+    x = make_attn_inputs(cfg, seed=4000 + seed)
+    c_new = round_to_bf16(rng.normal(size=(cfg.batch, S, cfg.kv_lora_rank)).astype(np.float32))
+    kp_new = round_to_bf16(rng.normal(size=(cfg.batch, S, cfg.qk_rope_head_dim)).astype(np.float32))
+    w = round_to_bf16((1.0 + 0.14 * rng.normal(size=cfg.kv_lora_rank)).astype(np.float32))
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to("cuda").to(torch.bfloat16)
+    t = {k: dev(v) for k, v in x.items()}
+    seq_lens = None if lens is None else torch.tensor(lens, dtype=torch.int32, device="cuda")
+    res = []
+    for fused in (True, False):
+        kv, pe = t["kv_cache"].clone(), t["pe_cache"].clone()
+        out = torch.full((cfg.batch, S, cfg.n_heads, cfg.v_head_dim), float("nan"), dtype=torch.bfloat16,
+                         device="cuda")
+        if fused:
+            gpu_lib.absorb_attn(t["q_nope"], t["q_pe"], kv, pe, t["wkv_b"], cfg.end_pos, cfg.softmax_scale, out,
+                                num_splits=splits, path="mfma", seq_lens=seq_lens,
+                                append=(dev(c_new), dev(kp_new), dev(w), 1e-6))
+        else:
+            gpu_lib.cache_append(dev(c_new), dev(kp_new), dev(w), 1e-6, cfg.end_pos, kv, pe, seq_lens=seq_lens)
+            gpu_lib.absorb_attn(t["q_nope"], t["q_pe"], kv, pe, t["wkv_b"], cfg.end_pos, cfg.softmax_scale, out,
+                                num_splits=splits, path="mfma", seq_lens=seq_lens)
+        torch.cuda.synchronize()
+        res.append((out, kv, pe))
+    for a, b in zip(res[0], res[1]):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"sweep {seed}: fused differs from two calls"
+    # the oracle over the caches as the GPU wrote them (their new rows checked in the fixed tests)
+    kv_g = res[0][1].float().cpu().numpy().astype(np.float64)
+    pe_g = res[0][2].float().cpu().numpy().astype(np.float64)
+    if lens is None:
+        ref = O.absorb_attention(x["q_nope"], x["q_pe"], kv_g, pe_g, x["wkv_b"], cfg.end_pos, cfg.softmax_scale,
+                                 cfg.v_head_dim)
+    else:
+        ref = O.absorb_attention_ragged(x["q_nope"], x["q_pe"], kv_g, pe_g, x["wkv_b"], lens, cfg.softmax_scale,
+                                        cfg.v_head_dim)
+    check(res[0][0], ref, f"fused append sweep {seed}")
+    # and the written rows against the oracle's append
+    kv_o, _ = O.cache_append(c_new, kp_new, w, 1e-6, x["kv_cache"], x["pe_cache"], end_pos=cfg.end_pos,
+                             seq_lens=lens)
+    for b in range(cfg.batch):
+        n = cfg.end_pos if lens is None else min(max(lens[b], S), cfg.end_pos)
+        g_rows = kv_g[b, n - S:n]
+        o_rows = kv_o[b, n - S:n]
+        assert np.abs(g_rows - o_rows).max() <= TOL * np.abs(o_rows).max(), f"sweep {seed}: appended rows of {b}"
